@@ -1,0 +1,102 @@
+"""Ternary GEMV / GEMM / 2:4 GEMV definitions in float64.
+
+What the decode and prefill paths compute (mhpq.cn/news/1159370 §4.2: read
+the weight bits, expand the signs, multiply by the scale, then the matrix
+product; the activations are already rotated, zwxr.cn/news/303439 §3.4):
+
+    y'[m, n] = sum_g f16(scale[n, g]) * sum_{k in g} t[n, k] * x'[m, k]
+
+with x' the exact bf16 values handed to the kernel and t in {-1, 0, +1}.
+The vectorised forms dequantise and call numpy.matmul in float64; the
+brute-force forms are explicit Python loops for tiny shapes.
+"""
+
+import numpy as np
+
+from .numerics import bf16_bits_to_f64, f16_bits_to_f64
+from .quant import GROUP, dense_from_24, unpack_24, unpack_dense
+
+
+def _x(x_bf16_bits):
+    x = bf16_bits_to_f64(np.asarray(x_bf16_bits, dtype=np.uint16))
+    return x.reshape(1, -1) if x.ndim == 1 else x
+
+
+def dequant_dense(codes, scales, k):
+    """W~[n, k] = f16(scale[n, k // 128]) * t[n, k]."""
+    t = unpack_dense(codes, k).astype(np.float64)
+    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    return t * np.repeat(s, GROUP, axis=1)
+
+
+def gemv(x_bf16_bits, codes, scales, k):
+    """y'[m, n] for activations x'[m, k] (bf16 bits) against dense codes."""
+    return np.matmul(_x(x_bf16_bits), dequant_dense(codes, scales, k).T)
+
+
+# the prefill GEMM is the same contraction for M rows of activations
+gemm = gemv
+
+
+def dequant_24(meta, signs, scales, k):
+    idx0, idx1, neg0, neg1 = unpack_24(meta, signs, k)
+    t = dense_from_24(idx0, idx1, neg0, neg1).astype(np.float64)
+    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    return t * np.repeat(s, GROUP, axis=1)
+
+
+def gemv24(x_bf16_bits, meta, signs, scales, k):
+    """y'[m, n] = sum_g s[n, g] * sum_quads (+-x'[4q + idx0] +- x'[4q + idx1])."""
+    return np.matmul(_x(x_bf16_bits), dequant_24(meta, signs, scales, k).T)
+
+
+def gemv_bruteforce(x_bf16_bits, codes, scales, k):
+    """Loop form of gemv: decode each 2-bit field by hand and accumulate."""
+    x = _x(x_bf16_bits)
+    codes = np.asarray(codes, dtype=np.uint32)
+    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    m_rows, n_rows = x.shape[0], codes.shape[0]
+    y = np.zeros((m_rows, n_rows))
+    for m in range(m_rows):
+        for n in range(n_rows):
+            total = 0.0
+            for g in range(k // GROUP):
+                part = 0.0
+                for kk in range(g * GROUP, (g + 1) * GROUP):
+                    word = int(codes[n, kk // 16])
+                    r = kk % 16
+                    field = (word >> (2 * (r // 2) + 16 * (r % 2))) & 3
+                    if field == 1:
+                        part += x[m, kk]
+                    elif field == 3:
+                        part -= x[m, kk]
+                    elif field != 0:
+                        raise ValueError("invalid code")
+                total += float(s[n, g]) * part
+            y[m, n] = total
+    return y
+
+
+def gemv24_bruteforce(x_bf16_bits, meta, signs, scales, k):
+    """Loop form of gemv24: gather the two kept activations of every quad."""
+    x = _x(x_bf16_bits)
+    meta = np.asarray(meta, dtype=np.uint32)
+    signs = np.asarray(signs, dtype=np.uint32)
+    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    y = np.zeros((x.shape[0], meta.shape[0]))
+    for m in range(x.shape[0]):
+        for n in range(meta.shape[0]):
+            total = 0.0
+            for g in range(k // GROUP):
+                part = 0.0
+                for q in range(g * GROUP // 4, (g + 1) * GROUP // 4):
+                    nib = (int(meta[n, q // 8]) >> (4 * (q % 8))) & 0xF
+                    i0, i1 = nib & 3, nib >> 2
+                    sw = int(signs[n, q // 16])
+                    n0 = (sw >> (q % 16)) & 1
+                    n1 = (sw >> (16 + q % 16)) & 1
+                    part += (-1.0 if n0 else 1.0) * x[m, 4 * q + i0]
+                    part += (-1.0 if n1 else 1.0) * x[m, 4 * q + i1]
+                total += float(s[n, g]) * part
+            y[m, n] = total
+    return y

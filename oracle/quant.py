@@ -1,0 +1,218 @@
+"""Offline quantiser: absmean group scale, ternarisation and packing, dense and
+2:4, in float64.
+
+Definitions followed (readings of the pages are listed in the design doc):
+
+* Group scale: the mean absolute value of the 128 contiguous K-elements of one
+  row of one rotated 128x128 block (mhpq.cn/news/1159370 §1.1: take the group's
+  mean absolute value as the scale; §1.3: one fp16 scale per 128 elements).
+* Ternarise: divide by the scale, round, clip to {-1, 0, 1} (mhpq.cn §1.1).
+  Written as a threshold at half the scale with a strict comparison, as in the
+  sign(w) * (|w| > thr) step of dpshk.com/news/5289456 §3.2 step 5; a value at
+  exactly s/2 gives 0 (round-half-even agrees).  The comparison uses the
+  unrounded float64 scale; the stored scale is its fp16 rounding.
+* 2:4: of every 4 consecutive K-elements keep the 2 largest |w'| and ternarise
+  the survivors (mhpq.cn §1.2: prune with the 2:4 pattern, then ternarise what
+  remains).  Kept elements are nonzero, so each carries only a sign; the group
+  scale is the mean |w'| of the 64 kept elements of the group.
+* Storage: 2 bits per weight (mhpq.cn §3.1), as a sign bit and a magnitude bit
+  per weight (the sign/magnitude split of dpshk.com §2.2), pair-interleaved
+  inside each 32-bit word.
+
+Dense format (K a multiple of 128; rows contiguous):
+  codes[n][k // 16] uint32.  With r = k % 16 the 2-bit field of (n, k) starts at
+  bit 2 * (r // 2) + 16 * (r % 2): even k fill the low half-word, odd k the high
+  half-word, each in increasing k.  Field value: 0b00 -> 0, 0b01 -> +1,
+  0b11 -> -1 (bit 0 = nonzero, bit 1 = negative); 0b10 is invalid.
+  scales[n][k // 128] fp16 bits.
+2:4 format:
+  meta[n][q // 8] uint32 for quad q = k // 4: the nibble at bits 4 * (q % 8)
+  holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1 the kept positions.
+  signs[n][q // 16] uint32: bit q % 16 is set when the element at idx0 is
+  negative, bit 16 + q % 16 when the element at idx1 is.
+  scales as dense.
+"""
+
+import numpy as np
+
+from .hadamard import BLOCK, rotate_blocks
+from .numerics import f64_to_f16_bits
+
+GROUP = 128
+NEAR_REL = 1e-5
+
+FIELD_OF_T = {0: 0b00, 1: 0b01, -1: 0b11}
+
+
+def _check_w(w):
+    w = np.asarray(w, dtype=np.float64)
+    if w.ndim != 2 or w.shape[0] % BLOCK or w.shape[1] % BLOCK:
+        raise ValueError(f"weight shape {w.shape} must be multiples of {BLOCK}")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("weights must be finite")
+    return w
+
+
+def absmean_scales(wr):
+    """s[n, g] = mean over the 128 elements of group g of row n of |W'|."""
+    n, k = wr.shape
+    return np.abs(wr).reshape(n, k // GROUP, GROUP).mean(axis=2)
+
+
+def ternarize(wr, s):
+    """t = +1 where W' > s/2, -1 where W' < -s/2, else 0 (s per 128-group)."""
+    thr = np.repeat(s / 2.0, GROUP, axis=1)
+    return np.where(wr > thr, 1, np.where(wr < -thr, -1, 0)).astype(np.int8)
+
+
+def near_threshold(wr, s, rel=NEAR_REL):
+    """Elements whose |W'| is within rel * s/2 of the threshold s/2."""
+    thr = np.repeat(s / 2.0, GROUP, axis=1)
+    return np.abs(np.abs(wr) - thr) <= rel * thr
+
+
+def _field_pos(k):
+    r = np.asarray(k) % 16
+    return 2 * (r // 2) + 16 * (r % 2)
+
+
+def pack_dense(t):
+    """Pack ternary t[N, K] into codes[N, K/16] (uint32), format above."""
+    t = np.asarray(t)
+    n, k = t.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    field = np.zeros(t.shape, dtype=np.uint64)
+    field[t == 1] = FIELD_OF_T[1]
+    field[t == -1] = FIELD_OF_T[-1]
+    words = np.zeros((n, k // 16), dtype=np.uint64)
+    for r in range(16):
+        words |= field[:, r::16] << np.uint64(_field_pos(r))
+    return words.astype(np.uint32)
+
+
+def unpack_dense(codes, k):
+    """Inverse of pack_dense; raises on the invalid field 0b10."""
+    codes = np.asarray(codes, dtype=np.uint32).astype(np.uint64)
+    n = codes.shape[0]
+    if codes.shape[1] * 16 != k:
+        raise ValueError("codes shape does not match K")
+    t = np.zeros((n, k), dtype=np.int8)
+    for r in range(16):
+        f = (codes >> np.uint64(_field_pos(r))) & np.uint64(3)
+        if np.any(f == 0b10):
+            raise ValueError("invalid 2-bit code 0b10")
+        t[:, r::16] = np.where(f == 0b01, 1, np.where(f == 0b11, -1, 0))
+    return t
+
+
+def quantize_dense(w):
+    """Rotate 128x128 blocks, take absmean group scales, ternarise, pack.
+
+    Returns a dict with codes (uint32 [N, K/16]), scales (fp16 bits uint16
+    [N, K/128]) and the float64 intermediates wr (W'), s (unrounded scales) and
+    t (int8 ternary values)."""
+    w = _check_w(w)
+    wr = rotate_blocks(w)
+    s = absmean_scales(wr)
+    t = ternarize(wr, s)
+    return {"codes": pack_dense(t), "scales": f64_to_f16_bits(s), "wr": wr, "s": s, "t": t}
+
+
+# ---------------------------------------------------------------- 2:4 variant
+
+def select_24(wr):
+    """For every quad of 4 along K, the positions of the two largest |W'|
+    (ties go to the lower position); returns idx0 < idx1, each [N, K/4]."""
+    n, k = wr.shape
+    a = np.abs(wr).reshape(n, k // 4, 4)
+    order = np.argsort(-a, axis=2, kind="stable")
+    top = np.sort(order[:, :, :2], axis=2)
+    return top[:, :, 0].astype(np.int64), top[:, :, 1].astype(np.int64)
+
+
+def near_tie_24(wr, s, rel=NEAR_REL):
+    """Quads whose selection or signs are ambiguous at float rounding level:
+    the 2nd and 3rd largest |W'| are within rel of each other, or a kept
+    element has |W'| <= rel * s (its sign is then ill-defined)."""
+    n, k = wr.shape
+    a = np.sort(np.abs(wr).reshape(n, k // 4, 4), axis=2)[:, :, ::-1]
+    tie = np.abs(a[:, :, 1] - a[:, :, 2]) <= rel * np.maximum(a[:, :, 1], 1e-300)
+    sq = np.repeat(s, GROUP // 4, axis=1)
+    small = a[:, :, 1] <= rel * sq
+    return tie | small
+
+
+def quantize_24(w):
+    """Rotate, keep 2 of every 4 along K, absmean over the kept elements, pack.
+
+    Returns meta, signs, scales plus wr, s, idx0, idx1, neg0, neg1 and the
+    dense ternary equivalent t."""
+    w = _check_w(w)
+    wr = rotate_blocks(w)
+    n, k = wr.shape
+    idx0, idx1 = select_24(wr)
+    quads = wr.reshape(n, k // 4, 4)
+    v0 = np.take_along_axis(quads, idx0[:, :, None], axis=2)[:, :, 0]
+    v1 = np.take_along_axis(quads, idx1[:, :, None], axis=2)[:, :, 0]
+    kept_abs = (np.abs(v0) + np.abs(v1)).reshape(n, k // GROUP, GROUP // 4)
+    s = kept_abs.sum(axis=2) / (GROUP // 2)
+    neg0 = v0 < 0
+    neg1 = v1 < 0
+    meta, signs = pack_24(idx0, idx1, neg0, neg1)
+    t = dense_from_24(idx0, idx1, neg0, neg1)
+    return {"meta": meta, "signs": signs, "scales": f64_to_f16_bits(s), "wr": wr, "s": s,
+            "idx0": idx0, "idx1": idx1, "neg0": neg0, "neg1": neg1, "t": t}
+
+
+def pack_24(idx0, idx1, neg0, neg1):
+    idx0 = np.asarray(idx0, dtype=np.uint64)
+    idx1 = np.asarray(idx1, dtype=np.uint64)
+    n, nq = idx0.shape
+    if nq % 16:
+        raise ValueError("K/4 must be a multiple of 16")
+    if np.any(idx0 >= idx1) or np.any(idx1 > 3):
+        raise ValueError("need 0 <= idx0 < idx1 <= 3")
+    nib = idx0 | (idx1 << np.uint64(2))
+    meta = np.zeros((n, nq // 8), dtype=np.uint64)
+    for j in range(8):
+        meta |= nib[:, j::8] << np.uint64(4 * j)
+    n0 = np.asarray(neg0).astype(np.uint64)
+    n1 = np.asarray(neg1).astype(np.uint64)
+    signs = np.zeros((n, nq // 16), dtype=np.uint64)
+    for j in range(16):
+        signs |= n0[:, j::16] << np.uint64(j)
+        signs |= n1[:, j::16] << np.uint64(16 + j)
+    return meta.astype(np.uint32), signs.astype(np.uint32)
+
+
+def unpack_24(meta, signs, k):
+    meta = np.asarray(meta, dtype=np.uint32).astype(np.uint64)
+    signs = np.asarray(signs, dtype=np.uint32).astype(np.uint64)
+    n = meta.shape[0]
+    nq = k // 4
+    if meta.shape[1] * 8 != nq or signs.shape[1] * 16 != nq:
+        raise ValueError("meta/signs shape does not match K")
+    idx0 = np.zeros((n, nq), dtype=np.int64)
+    idx1 = np.zeros((n, nq), dtype=np.int64)
+    for j in range(8):
+        nib = (meta >> np.uint64(4 * j)) & np.uint64(0xF)
+        idx0[:, j::8] = (nib & np.uint64(3)).astype(np.int64)
+        idx1[:, j::8] = (nib >> np.uint64(2)).astype(np.int64)
+    if np.any(idx0 >= idx1):
+        raise ValueError("invalid 2:4 index nibble (need idx0 < idx1)")
+    neg0 = np.zeros((n, nq), dtype=bool)
+    neg1 = np.zeros((n, nq), dtype=bool)
+    for j in range(16):
+        neg0[:, j::16] = ((signs >> np.uint64(j)) & np.uint64(1)) == 1
+        neg1[:, j::16] = ((signs >> np.uint64(16 + j)) & np.uint64(1)) == 1
+    return idx0, idx1, neg0, neg1
+
+
+def dense_from_24(idx0, idx1, neg0, neg1):
+    """The ternary matrix a 2:4 encoding stands for (+-1 at kept positions)."""
+    n, nq = np.asarray(idx0).shape
+    t = np.zeros((n, nq, 4), dtype=np.int8)
+    np.put_along_axis(t, np.asarray(idx0)[:, :, None], np.where(neg0, -1, 1)[:, :, None].astype(np.int8), axis=2)
+    np.put_along_axis(t, np.asarray(idx1)[:, :, None], np.where(neg1, -1, 1)[:, :, None].astype(np.int8), axis=2)
+    return t.reshape(n, nq * 4)

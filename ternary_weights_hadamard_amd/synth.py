@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs shared by the tests and the benchmark.
+
+This module draws random numbers and formats them into the input buffers the
+library takes (fp32 weights, bf16 activation bits, packed code words drawn
+i.i.d. per field, fp16 scales).  It performs none of the method's arithmetic:
+no transform, no scale, no ternarisation.
+
+Workload shapes are those of a 27B-class layer: d_model = 5120, d_ff = 17408;
+Q, K, V, O are 5120 x 5120, up and gate 17408 x 5120, down 5120 x 17408 (rows x
+columns = out x in).
+"""
+
+import numpy as np
+
+D_MODEL = 5120
+D_FF = 17408
+
+# (name, N rows = out features, K columns = in features)
+LAYER_MATRICES = (
+    ("q", D_MODEL, D_MODEL),
+    ("k", D_MODEL, D_MODEL),
+    ("v", D_MODEL, D_MODEL),
+    ("o", D_MODEL, D_MODEL),
+    ("up", D_FF, D_MODEL),
+    ("gate", D_FF, D_MODEL),
+    ("down", D_MODEL, D_FF),
+)
+
+# 2-bit field values of the dense code format: 0 -> 0b00, +1 -> 0b01, -1 -> 0b11
+FIELD_ZERO, FIELD_POS, FIELD_NEG = 0b00, 0b01, 0b11
+# the six valid 2:4 index nibbles idx0 | idx1 << 2 with idx0 < idx1
+NIBBLES_24 = tuple(i0 | (i1 << 2) for i0 in range(4) for i1 in range(4) if i0 < i1)
+
+
+def f32_to_bf16_bits(x):
+    """float32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    nan = np.isnan(x)
+    out = rounded.astype(np.uint16)
+    out[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
+    return out
+
+
+def gaussian_bf16(shape, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+
+def single_layer_weights(n=1024, k=1024, seed=0, sigma=0.02, outlier_frac=0.001, outlier_mult=20.0):
+    """W ~ N(0, sigma^2) fp32 with round(outlier_frac * n * k) entries x outlier_mult."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(sigma)
+    count = int(round(outlier_frac * n * k))
+    idx = rng.choice(n * k, count, replace=False)
+    w.reshape(-1)[idx] *= np.float32(outlier_mult)
+    return w
+
+
+def stack_weights(n, k, seed, sigma=0.02, outlier_col_frac=0.01, nu=3.0):
+    """W ~ N(0, sigma^2) fp32 with heavy-tailed outlier input channels: a fraction
+    of the columns is replaced by sigma * Student-t(nu) draws."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(sigma)
+    ncol = max(1, int(round(outlier_col_frac * k)))
+    cols = rng.choice(k, ncol, replace=False)
+    w[:, cols] = (rng.standard_t(nu, size=(n, ncol)) * sigma).astype(np.float32)
+    return w
+
+
+def random_code_words(n, k, seed, p=(0.35, 0.30, 0.35)):
+    """Dense code words [n, k/16] uint32 whose 16 2-bit fields are drawn i.i.d.
+    with P(-1, 0, +1) = p.  Fields are independent, so no layout is assumed."""
+    rng = np.random.default_rng(seed)
+    fields = rng.choice(np.array([FIELD_NEG, FIELD_ZERO, FIELD_POS], dtype=np.uint32),
+                        size=(n, k // 16, 16), p=np.asarray(p) / np.sum(p))
+    shifts = (2 * np.arange(16, dtype=np.uint32))
+    return np.bitwise_or.reduce(fields << shifts, axis=2).astype(np.uint32)
+
+
+def random_scales_f16(n, k, seed, lo=0.005, hi=0.05):
+    """fp16 bit patterns [n, k/128] of U(lo, hi) draws."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(lo, hi, size=(n, k // 128)).astype(np.float16).view(np.uint16)
+
+
+def random_24(n, k, seed):
+    """2:4 planes: meta [n, k/32] with a uniform choice of the 6 index pairs per
+    quad, signs [n, k/64] with fair random bits."""
+    rng = np.random.default_rng(seed)
+    nib = rng.choice(np.array(NIBBLES_24, dtype=np.uint32), size=(n, k // 32, 8))
+    meta = np.bitwise_or.reduce(nib << (4 * np.arange(8, dtype=np.uint32)), axis=2).astype(np.uint32)
+    signs = rng.integers(0, 2 ** 32, size=(n, k // 64), dtype=np.uint64).astype(np.uint32)
+    return meta, signs
+
+
+def small_int_bf16(shape, seed, lim=8):
+    """bf16 bit patterns of integers in [-lim, lim] (exact in bf16)."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.integers(-lim, lim + 1, size=shape).astype(np.float32))

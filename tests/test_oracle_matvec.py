@@ -1,0 +1,116 @@
+"""Pins of the oracle GEMV / GEMM / 2:4 GEMV: brute-force loops, exact integer
+arithmetic done with Python ints, textbook special cases, and the 2:4 to dense
+expansion."""
+
+import numpy as np
+import pytest
+
+from oracle import matvec as mv
+from oracle import numerics as nu
+from oracle import quant as q
+from ternary_weights_hadamard_amd import synth
+
+
+def _t_from_codes(codes, k):
+    """Independent field decode for tests: walk the words bit by bit."""
+    n = codes.shape[0]
+    t = np.zeros((n, k), dtype=np.int64)
+    for row in range(n):
+        for kk in range(k):
+            w = int(codes[row, kk // 16])
+            r = kk % 16
+            pos = r if r % 2 == 0 else 15 + r
+            f = (w >> pos) & 3
+            t[row, kk] = {0: 0, 1: 1, 3: -1}[f]
+    return t
+
+
+@pytest.mark.parametrize("n,k,b", [(128, 128, 1), (128, 256, 3), (256, 128, 2)])
+def test_gemv_equals_bruteforce(n, k, b):
+    codes = synth.random_code_words(n, k, seed=n + k + b)
+    scales = synth.random_scales_f16(n, k, seed=7)
+    x = synth.gaussian_bf16((b, k), seed=11)
+    y = mv.gemv(x, codes, scales, k)
+    yb = mv.gemv_bruteforce(x, codes, scales, k)
+    assert y.shape == (b, n)
+    assert np.max(np.abs(y - yb)) <= 1e-12 * max(1.0, np.max(np.abs(yb)))
+
+
+def test_gemv_exact_integer_case():
+    # small-integer activations and power-of-two scales: every partial sum is an exact
+    # integer multiple of the scale, so the result is exact; check with Python ints.
+    n, k = 128, 256
+    codes = synth.random_code_words(n, k, seed=1)
+    x = synth.small_int_bf16((2, k), seed=2)
+    sc_exp = np.random.default_rng(3).integers(-6, 1, size=(n, k // 128))
+    scales = (2.0 ** sc_exp).astype(np.float16).view(np.uint16)
+    y = mv.gemv(x, codes, scales, k)
+    t = _t_from_codes(codes, k)
+    xi = nu.bf16_bits_to_f64(x).astype(np.int64)
+    for m in range(2):
+        for row in range(n):
+            acc = 0
+            for g in range(k // 128):
+                part = int(np.dot(t[row, g * 128:(g + 1) * 128], xi[m, g * 128:(g + 1) * 128]))
+                acc += part * 2.0 ** int(sc_exp[row, g])
+            assert y[m, row] == acc
+
+
+def test_all_plus_one_is_row_sum_and_one_hot_is_gather():
+    n, k = 128, 256
+    x = synth.gaussian_bf16((1, k), seed=5)
+    xv = nu.bf16_bits_to_f64(x)
+    one = np.float16(1.0).view(np.uint16)
+    ones = np.full((n, k // 128), one, dtype=np.uint16)
+    t = np.ones((n, k), dtype=np.int8)
+    y = mv.gemv(x, q.pack_dense(t), ones, k)
+    assert np.allclose(y, xv.sum(), rtol=1e-14, atol=1e-12)
+    # one nonzero per row at a chosen column, negative on odd rows
+    cols = np.random.default_rng(6).integers(0, k, size=n)
+    t = np.zeros((n, k), dtype=np.int8)
+    t[np.arange(n), cols] = np.where(np.arange(n) % 2 == 0, 1, -1)
+    y = mv.gemv(x, q.pack_dense(t), ones, k)
+    assert np.array_equal(y[0], np.where(np.arange(n) % 2 == 0, 1, -1) * xv[0, cols])
+
+
+def test_gemm_rows_equal_gemv_rows():
+    n, k = 256, 384
+    codes = synth.random_code_words(n, k, seed=8)
+    scales = synth.random_scales_f16(n, k, seed=9)
+    x = synth.gaussian_bf16((5, k), seed=10)
+    y = mv.gemm(x, codes, scales, k)
+    for m in range(5):
+        assert np.array_equal(y[m], mv.gemv(x[m], codes, scales, k)[0])
+
+
+def test_dequantised_matrix_matches_independent_decode():
+    n, k = 128, 256
+    codes = synth.random_code_words(n, k, seed=12)
+    scales = synth.random_scales_f16(n, k, seed=13)
+    wq = mv.dequant_dense(codes, scales, k)
+    s = scales.view(np.float16).astype(np.float64)
+    assert np.array_equal(wq, _t_from_codes(codes, k) * np.repeat(s, 128, axis=1))
+
+
+@pytest.mark.parametrize("n,k,b", [(128, 128, 1), (128, 256, 2)])
+def test_gemv24_equals_bruteforce_and_dense_expansion(n, k, b):
+    meta, signs = synth.random_24(n, k, seed=n + k)
+    scales = synth.random_scales_f16(n, k, seed=14)
+    x = synth.gaussian_bf16((b, k), seed=15)
+    y = mv.gemv24(x, meta, signs, scales, k)
+    yb = mv.gemv24_bruteforce(x, meta, signs, scales, k)
+    assert np.max(np.abs(y - yb)) <= 1e-12 * max(1.0, np.max(np.abs(yb)))
+    # the 2:4 encoding expanded to dense ternary codes gives the same product exactly
+    idx0, idx1, neg0, neg1 = q.unpack_24(meta, signs, k)
+    dense_codes = q.pack_dense(q.dense_from_24(idx0, idx1, neg0, neg1))
+    assert np.array_equal(mv.gemv(x, dense_codes, scales, k), y)
+    # exactly two nonzeros per quad
+    t = q.dense_from_24(idx0, idx1, neg0, neg1)
+    assert np.all(np.count_nonzero(t.reshape(n, k // 4, 4), axis=2) == 2)
+
+
+def test_random_codes_distribution():
+    codes = synth.random_code_words(256, 1024, seed=0)
+    t = q.unpack_dense(codes, 1024)
+    p = [np.mean(t == v) for v in (-1, 0, 1)]
+    assert np.allclose(p, (0.35, 0.30, 0.35), atol=0.005)

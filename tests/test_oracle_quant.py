@@ -1,0 +1,222 @@
+"""Pins of the oracle quantiser: closed-form blocks, the tie rule, hand-worked
+packing examples, Gaussian statistics in closed form, and brute force over
+every 2:4 pattern."""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+
+from oracle import hadamard as hd
+from oracle import quant as q
+
+H = scipy.linalg.hadamard(128).astype(np.float64)
+
+
+def _from_rotated(wr):
+    """W with rotate_blocks(W) == wr exactly, for dyadic wr with few bits:
+    W = H wr H / 128 per block (H H = 128 I)."""
+    w = np.empty_like(wr)
+    for a in range(0, wr.shape[0], 128):
+        for b in range(0, wr.shape[1], 128):
+            w[a:a + 128, b:b + 128] = H @ wr[a:a + 128, b:b + 128] @ H / 128
+    return w
+
+
+@pytest.mark.parametrize("a,b,k", [(0, 0, 0), (5, 9, 2), (127, 64, -3), (33, 100, 5)])
+@pytest.mark.parametrize("sign", [1, -1])
+def test_spike_block_is_lossless(a, b, k, sign):
+    # B = w e_a e_b^T  ->  W' = (w/128) h_a h_b^T, every |W'| = |w|/128 = s, codes all +-1
+    w = sign * 2.0 ** k
+    blk = np.zeros((128, 128))
+    blk[a, b] = w
+    r = q.quantize_dense(blk)
+    assert np.all(r["s"] == abs(w) / 128)
+    expect_t = np.sign(w) * np.outer(H[a], H[b])
+    assert np.array_equal(r["t"], expect_t.astype(np.int8))
+    # fp16 scale exact (a power of two) and reconstruction lossless
+    assert np.all(r["scales"] == np.float16(abs(w) / 128).view(np.uint16))
+    assert np.allclose(r["t"] * r["s"][:, :1], r["wr"], rtol=0, atol=0)
+
+
+def test_identity_block():
+    r = q.quantize_dense(np.eye(128))
+    assert np.all(r["s"] == 1.0 / 128)
+    assert np.array_equal(r["t"], np.eye(128, dtype=np.int8))
+
+
+def test_constant_and_zero_blocks():
+    r = q.quantize_dense(np.full((128, 128), 0.375))
+    # W' = 128 c e0 e0^T: row 0 has s = c with a single +1; other rows s = 0, codes 0
+    assert r["s"][0, 0] == 0.375 and np.all(r["s"][1:] == 0)
+    assert r["t"][0, 0] == 1 and np.count_nonzero(r["t"]) == 1
+    assert np.all(r["scales"][1:] == 0)
+    z = q.quantize_dense(np.zeros((128, 256)))
+    assert np.all(z["t"] == 0) and np.all(z["scales"] == 0) and np.all(z["codes"] == 0)
+
+
+def test_tie_at_half_scale_gives_zero():
+    # a rotated row of 48 x 1.0, 64 x 0.25, 16 x 0: s = (48 + 16)/128 = 0.5, s/2 = 0.25
+    wr = np.zeros((128, 128))
+    wr[0, :48] = 1.0
+    wr[0, 48:112] = 0.25
+    wr[1, :48] = -1.0
+    wr[1, 48:112] = -0.25
+    w = _from_rotated(wr)
+    r = q.quantize_dense(w)
+    assert np.array_equal(r["wr"], wr)
+    assert r["s"][0, 0] == 0.5 and r["s"][1, 0] == 0.5
+    assert np.all(r["t"][0, :48] == 1) and np.all(r["t"][0, 48:] == 0)
+    assert np.all(r["t"][1, :48] == -1) and np.all(r["t"][1, 48:] == 0)
+    assert np.all(q.near_threshold(r["wr"], r["s"])[0, 48:112])
+
+
+def test_threshold_is_half_the_absmean():
+    # group of 128 with values 0.1 .. 12.8: s = 6.45, threshold 3.225
+    wr = np.zeros((128, 128))
+    wr[0] = np.arange(1, 129) * 0.1
+    t = q.ternarize(wr, q.absmean_scales(wr))
+    assert np.all(t[0, :32] == 0) and np.all(t[0, 32:] == 1)  # 3.3 > 3.225 >= 3.2
+
+
+def test_blocks_quantise_independently():
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((256, 384)) * 0.02
+    full = q.quantize_dense(w)
+    part = q.quantize_dense(w[128:256, 256:384])
+    assert np.array_equal(full["t"][128:256, 256:384], part["t"])
+    assert np.array_equal(full["scales"][128:256, 2:3], part["scales"])
+
+
+def test_scales_are_numpy_float16_of_s():
+    rng = np.random.default_rng(3)
+    r = q.quantize_dense(rng.standard_normal((256, 256)) * 0.02)
+    assert np.array_equal(r["scales"], r["s"].astype(np.float16).view(np.uint16))
+
+
+def test_gaussian_statistics_closed_form():
+    # i.i.d. N(0, s^2) stays i.i.d. after the orthonormal block rotation.  With the
+    # absmean threshold a = sqrt(2/pi)/2 (in units of sigma):
+    #   P(t = 0) = erf(a / sqrt 2), P(+-1) = (1 - P0)/2,
+    #   weight NMSE = 1 - 2 s E|Z|1(|Z|>a) + s^2 P(|Z|>a), E|Z|1(|Z|>a) = 2 phi(a).
+    rng = np.random.default_rng(0)
+    r = q.quantize_dense(rng.standard_normal((1024, 1024)) * 0.02)
+    t = r["t"]
+    a = math.sqrt(2 / math.pi) / 2
+    p0 = scipy.special.erf(a / math.sqrt(2))
+    assert abs(np.mean(t == 0) - p0) < 0.005
+    assert abs(np.mean(t == 1) - (1 - p0) / 2) < 0.005
+    assert abs(np.mean(t == -1) - (1 - p0) / 2) < 0.005
+    s = math.sqrt(2 / math.pi)
+    phi = math.exp(-a * a / 2) / math.sqrt(2 * math.pi)
+    nmse = 1 - 2 * s * 2 * phi + s * s * (1 - p0)
+    rec = t * np.repeat(r["s"], 128, axis=1)
+    meas = np.sum((rec - r["wr"]) ** 2) / np.sum(r["wr"] ** 2)
+    assert abs(meas - nmse) < 0.01
+    # near-threshold elements are rare (expected ~6e-6 per element)
+    assert q.near_threshold(r["wr"], r["s"]).sum() < 60
+
+
+def test_dense_packing_hand_worked(golden_dir):
+    lines = [l.split() for l in open(os.path.join(golden_dir, "packing_dense.txt")) if l.strip() and not l.startswith("#")]
+    t = np.array([[int(v) for v in lines[0][1:]]], dtype=np.int8)
+    word = int(lines[1][1], 16)
+    assert q.pack_dense(t)[0, 0] == word
+    assert np.array_equal(q.unpack_dense(np.array([[word]], dtype=np.uint32), 16), t)
+
+
+@pytest.mark.parametrize("r", range(16))
+@pytest.mark.parametrize("val,field", [(1, 0b01), (-1, 0b11)])
+def test_dense_field_positions(r, val, field):
+    t = np.zeros((1, 16), dtype=np.int8)
+    t[0, r] = val
+    pos = r if r % 2 == 0 else 16 + (r - 1)
+    assert int(q.pack_dense(t)[0, 0]) == field << pos
+
+
+def test_pack_unpack_round_trip_and_invalid_field():
+    rng = np.random.default_rng(5)
+    t = rng.integers(-1, 2, size=(7, 256)).astype(np.int8)
+    codes = q.pack_dense(t)
+    assert codes.shape == (7, 16) and codes.dtype == np.uint32
+    assert np.array_equal(q.unpack_dense(codes, 256), t)
+    assert np.all(q.pack_dense(np.zeros((2, 32), dtype=np.int8)) == 0)
+    bad = np.array([[0b10]], dtype=np.uint32)
+    with pytest.raises(ValueError):
+        q.unpack_dense(bad, 16)
+
+
+def test_quantiser_rejects_bad_input():
+    with pytest.raises(ValueError):
+        q.quantize_dense(np.zeros((128, 200)))
+    w = np.zeros((128, 128))
+    w[3, 4] = np.nan
+    with pytest.raises(ValueError):
+        q.quantize_dense(w)
+
+
+# ------------------------------------------------------------------ 2:4
+
+def test_24_packing_hand_worked(golden_dir):
+    lines = [l for l in open(os.path.join(golden_dir, "packing_24.txt")) if l.strip() and not l.startswith("#")]
+    quads = [list(map(int, g.split())) for g in lines[0].split(None, 1)[1].split("|")]
+    quads += [[0, 1, 0, 0]] * 12
+    idx0 = np.array([[v[0] for v in quads]])
+    idx1 = np.array([[v[1] for v in quads]])
+    neg0 = np.array([[bool(v[2]) for v in quads]])
+    neg1 = np.array([[bool(v[3]) for v in quads]])
+    meta, signs = q.pack_24(idx0, idx1, neg0, neg1)
+    assert [int(v) for v in meta[0]] == [int(v, 16) for v in lines[1].split()[1:]]
+    assert int(signs[0, 0]) == int(lines[2].split()[1], 16)
+    t16 = [int(v) for v in lines[3].split()[1:]]
+    assert list(q.dense_from_24(idx0, idx1, neg0, neg1)[0, :16]) == t16
+    back = q.unpack_24(meta, signs, 64)
+    assert all(np.array_equal(a, b) for a, b in zip(back, (idx0, idx1, neg0, neg1)))
+
+
+def test_24_all_patterns_and_signs_brute_force():
+    # every quad pattern (6 index pairs x 4 sign pairs) with kept magnitudes 3, 2 and
+    # pruned 1, 0.5, laid out as a rotated block; quantize_24 must keep exactly them
+    combos = [(i0, i1, s0, s1) for i0, i1 in itertools.combinations(range(4), 2)
+              for s0 in (1, -1) for s1 in (1, -1)]
+    wr = np.zeros((128, 128))
+    for row in range(128):
+        for quad in range(32):
+            i0, i1, s0, s1 = combos[(row + 7 * quad) % len(combos)]
+            vals = [0.0] * 4
+            pruned = [p for p in range(4) if p not in (i0, i1)]
+            vals[i0], vals[i1] = s0 * 3.0, s1 * 2.0
+            vals[pruned[0]], vals[pruned[1]] = 1.0, -0.5
+            wr[row, 4 * quad:4 * quad + 4] = vals
+    r = q.quantize_24(_from_rotated(wr))
+    assert np.array_equal(r["wr"], wr)
+    for row in range(128):
+        for quad in range(32):
+            i0, i1, s0, s1 = combos[(row + 7 * quad) % len(combos)]
+            assert (r["idx0"][row, quad], r["idx1"][row, quad]) == (i0, i1)
+            assert (r["neg0"][row, quad], r["neg1"][row, quad]) == (s0 < 0, s1 < 0)
+    # scale = mean of the 64 kept magnitudes = (3 + 2) / 2
+    assert np.all(r["s"] == 2.5)
+    expect = np.zeros_like(wr)
+    for p in range(4):
+        cols = slice(p, None, 4)
+        kept = (r["idx0"] == p) | (r["idx1"] == p)
+        expect[:, cols] = np.where(kept, np.sign(wr[:, cols]), 0)
+    assert np.array_equal(r["t"], expect.astype(np.int8))
+
+
+def test_24_ties_keep_lower_positions():
+    wr = np.array([[1.0, 1.0, 1.0, 1.0], [0.5, 1.0, 1.0, 1.0], [1.0, 0.5, 1.0, 1.0], [0.0, 0.0, 0.0, 0.0]])
+    i0, i1 = q.select_24(wr)
+    assert [(int(a), int(b)) for a, b in zip(i0[:, 0], i1[:, 0])] == [(0, 1), (1, 2), (0, 2), (0, 1)]
+
+
+def test_24_rejects_invalid_nibble():
+    meta = np.array([[0x7, 0x4]], dtype=np.uint32)  # first nibble: idx0 = 3 >= idx1 = 1
+    with pytest.raises(ValueError):
+        q.unpack_24(meta, np.zeros((1, 1), dtype=np.uint32), 64)
