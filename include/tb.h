@@ -1,0 +1,173 @@
+/*
+ * tb.h - C ABI of libtb, inference with Hadamard-rotated ternary weights on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method (cited by page address and the page's own section numbers):
+ *   - Activations get a blockwise 128-point Walsh-Hadamard transform along K,
+ *     normalised by 1/sqrt(128) (xxqk.cn/news/652513 §2; dpshk.com/news/5289456
+ *     §2.1 and §2.3; mhpq.cn/news/1159370 §2.2).
+ *   - Weights are stored as {-1, 0, +1} codes with one fp16 scale per 128
+ *     consecutive K-elements (mhpq.cn/news/1159370 §1.1, §1.3, §3.1); an
+ *     optional 2:4 variant keeps two of every four (same page, §1.2).
+ *   - The offline quantiser applies H.W.H^T / 128 to every 128x128 block, takes
+ *     the group's mean absolute value as its scale and ternarises by dividing,
+ *     rounding and clipping (mhpq.cn §1.1; dpshk.com §3.2 steps 3-5).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, owned by the caller, contiguous
+ *     and row-major, with base addresses aligned to 16 bytes.  Nothing is
+ *     retained after return.
+ *   - `stream` is a hipStream_t passed as a plain pointer (NULL = the default
+ *     stream).  Work is enqueued on it asynchronously; the library never
+ *     synchronises, never allocates device memory and never prints.  Outputs
+ *     are valid once the stream has completed the call.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is enqueued and the status says why.  Validation touches no
+ *     GPU state, so it can be exercised on a machine without a GPU.
+ *   - Weight matrices are W[N][K] (out x in, y = W x); N and K must be positive
+ *     multiples of 128.  A batch dimension of 0 (rows, B, M) is a valid no-op.
+ *   - Calls are re-entrant and thread-safe; concurrent calls on different
+ *     streams are independent.
+ *
+ * Storage formats (bit exact, shared by the quantiser and the products):
+ *   Dense codes  uint32 codes[N][K/16].  For r = k % 16 the 2-bit field of
+ *                (n, k) starts at bit 2*(r/2) + 16*(r%2): even k fill the low
+ *                half-word and odd k the high half-word of word k/16.  Field:
+ *                0b00 = 0, 0b01 = +1, 0b11 = -1 (bit 0 nonzero, bit 1
+ *                negative); 0b10 never appears and reads as 0.
+ *   Scales       uint16 fp16 bits scales[N][K/128], the group's absmean,
+ *                rounded to nearest even.
+ *   2:4 meta     uint32 meta[N][K/32]: for quad q = k/4 the nibble at bits
+ *                4*(q%8) holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1,
+ *                the kept positions inside the quad.
+ *   2:4 signs    uint32 signs[N][K/64]: bit q%16 set when the element kept at
+ *                idx0 of quad q is negative, bit 16 + q%16 for idx1.
+ */
+#ifndef TB_H
+#define TB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TB_OK = 0,
+  TB_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  TB_ERR_SHAPE = 2,       /* N or K not a positive multiple of 128, bad batch   */
+  TB_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                   */
+  TB_ERR_DTYPE = 4,       /* unknown dtype enum value                           */
+  TB_ERR_FORMAT = 5,      /* unknown format, or a plane given/missing for it    */
+  TB_ERR_LAUNCH = 6,      /* the HIP runtime refused the launch                 */
+  TB_ERR_UNSUPPORTED = 7, /* valid request this build does not implement        */
+  TB_ERR_ALIAS = 8        /* input and output overlap where that is not allowed */
+} tb_status;
+
+typedef enum { TB_F32 = 0, TB_BF16 = 1 } tb_dtype;
+typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1 } tb_format;
+
+/* Bits OR-ed into the optional device error flag of tb_quantize_pack. */
+#define TB_EFLAG_NONFINITE 1u /* a non-finite weight was seen; its block's codes are unspecified */
+#define TB_EFLAG_SCALE_OVF 2u /* a group scale rounded to fp16 infinity (absmean >= 65520)      */
+
+/* Largest activation batch of the GEMV entry points. */
+#define TB_GEMV_MAX_BATCH 16
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* tb_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int tb_version(void);
+
+/*
+ * Sizes in bytes of the packed planes of an [N][K] matrix in format `fmt`
+ * (tb_format).  Dense: code_bytes = N*K/4, meta_bytes = 0.  2:4: code_bytes
+ * (the sign plane) = N*K/16, meta_bytes = N*K/8.  scale_bytes = N*K/64 for
+ * both.  Any output pointer may be NULL.  Host-only.
+ * Cites the 2-bit storage of mhpq.cn/news/1159370 §3.1 and the bit ledger of §1.3.
+ */
+tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
+                          size_t* scale_bytes);
+
+/*
+ * Blockwise 128-point orthonormal Walsh-Hadamard transform along K:
+ *   y[r][128b + i] = (1/sqrt(128)) * sum_j (-1)^popcount(i & j) * x[r][128b + j]
+ * (xxqk.cn/news/652513 §2: log2(n) rounds of (a+b, a-b) butterflies;
+ * dpshk.com/news/5289456 §2.1: H[i][j] = (-1)^popcount(i&j), 128-blocks;
+ * §2.3: scale 1/sqrt(block size)).  Used on activations before the products
+ * and, along N, to rotate an output back (the transform is its own inverse).
+ *   x      [rows][K] in x_dtype (TB_BF16 or TB_F32)
+ *   y      [rows][K] in y_dtype; bf16 output is rounded to nearest even.
+ *          y == x is allowed (in place) when the dtypes match; any other
+ *          overlap returns TB_ERR_ALIAS.
+ *   rows >= 0, K a positive multiple of 128.  Arithmetic is fp32.
+ */
+tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
+                     void* stream);
+
+/*
+ * Offline quantise and pack (mhpq.cn/news/1159370 §1.1-§1.3, §3.1;
+ * dpshk.com/news/5289456 §3.2 steps 3-5):
+ *   W'  = H B H^T / 128 for every 128x128 block B of W,
+ *   s   = mean |W'| over each 128-group (one row of one block),
+ *   t   = +1 if W' > s/2, -1 if W' < -s/2, else 0 (dense), written as codes,
+ *   scale = fp16(s).
+ * TB_FMT_24 first keeps, in every quad of 4 along K, the two largest |W'|
+ * (ties to the lower position), takes s over the 64 kept elements of each
+ * group and stores their signs (mhpq.cn §1.2).
+ *   W       fp32 [N][K]
+ *   codes   dense: [N][K/16] code words; 2:4: the sign plane [N][K/64]
+ *   meta    2:4: [N][K/32]; must be NULL for TB_FMT_DENSE (else TB_ERR_FORMAT)
+ *   scales  fp16 bits [N][K/128]
+ *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
+ *             (the caller zeroes it first).
+ * Arithmetic is fp32; the threshold uses the unrounded scale.
+ */
+tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes,
+                           uint32_t* meta, uint16_t* scales, int32_t* err_flag, void* stream);
+
+/*
+ * Decode GEMV with dense ternary weights (mhpq.cn/news/1159370 §4.2: read the
+ * weight bits, expand the signs, apply the scale, multiply):
+ *   y[b][n] = sum_g fp16(scales[n][g]) * sum_{k in g} t[n][k] * x[b][k]
+ *   x       bf16 bits [B][K], the already rotated activations
+ *   B       0 <= B <= TB_GEMV_MAX_BATCH (else TB_ERR_SHAPE)
+ *   codes, scales  dense format, [N][K/16] and [N][K/128]
+ *   y       fp32 [B][N]; must not overlap the inputs (TB_ERR_ALIAS)
+ * Products are exact, accumulation is fp32.
+ */
+tb_status tb_ternary_gemv(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                          int64_t N, int64_t K, float* y, void* stream);
+
+/*
+ * Decode GEMV with 2:4 ternary weights (mhpq.cn/news/1159370 §1.2):
+ *   y[b][n] = sum_g fp16(scales[n][g]) * sum_q (+-x[b][4q + idx0] +- x[b][4q + idx1])
+ *   meta [N][K/32], signs [N][K/64], scales [N][K/128] in the 2:4 format;
+ *   other arguments as tb_ternary_gemv.
+ */
+tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
+                            const uint16_t* scales, int64_t N, int64_t K, float* y, void* stream);
+
+/*
+ * Prefill GEMM with dense ternary weights, the same contraction as
+ * tb_ternary_gemv for M rows of activations:
+ *   y[m][n] = sum_g fp16(scales[n][g]) * sum_{k in g} t[n][k] * x[m][k]
+ *   x       bf16 bits [M][K], M >= 0 (any M; ragged tails are handled)
+ *   y       [M][N] in y_dtype: TB_BF16 (rounded to nearest even) or TB_F32;
+ *           must not overlap the inputs.
+ * The matrix cores take fp16 operands: each weight enters as the exact fp16
+ * value 2*t*scale and each activation as its fp16 value, which equals the
+ * bf16 value whenever 2^-14 <= |x| < 65504 or x = 0.  Smaller magnitudes are
+ * rounded (absolute error <= 2^-25); |x| >= 65520 becomes infinite and shows
+ * in y.  Accumulation is fp32.
+ */
+tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                          int64_t N, int64_t K, void* y, int y_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TB_H */

@@ -1,0 +1,120 @@
+// Blockwise 128-point orthonormal Walsh-Hadamard transform along K.
+//
+// xxqk.cn/news/652513 §2 computes the transform as log2(n) rounds of
+// (a + b, a - b) butterflies; dpshk.com/news/5289456 §2.3 normalises by
+// 1/sqrt(block size).  Here one 128-block lives in 16 consecutive lanes of a
+// wave, 8 contiguous elements per lane (one 16-byte bf16 load): the three
+// butterfly rounds over element bits 0-2 run inside a lane, the four over
+// element bits 3-6 pair lanes (lane ^ 1, 2, 4, 8) through DPP and ds_swizzle,
+// so nothing goes through LDS.  The kernel is HBM bound: 4 bytes per element
+// for bf16 in and out.
+#include "tb_common.h"
+#include "tb_launch.h"
+
+namespace tb {
+
+namespace {
+
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+
+template <int MASK>
+__device__ __forceinline__ void lane_stage(float (&v)[8], int sub) {
+  const bool upper = (sub & MASK) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float p = xor_lane<MASK>(v[e]);
+    v[e] = upper ? (p - v[e]) : (v[e] + p);
+  }
+}
+
+template <bool IN_BF16, bool OUT_BF16>
+__global__ void __launch_bounds__(256) fwht128_kernel(const void* __restrict__ x, void* __restrict__ y,
+                                                       int64_t nblocks) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t b = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); b - (threadIdx.x >> 4) < nblocks;
+       b += (int64_t)gridDim.x * 16) {
+    // every lane of the wave runs the cross-lane stages; lanes past the end carry zeros
+    const bool live = b < nblocks;
+    const int64_t base = b * kBlock + sub * 8;
+    float v[8];
+    if constexpr (IN_BF16) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (live) w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + base);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+      }
+    } else {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+      if (live) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + base);
+        a = p[0];
+        c = p[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = a[i];
+        v[4 + i] = c[i];
+      }
+    }
+    // element bits 0..2: inside the lane
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((e & h) == 0) {
+          float a = v[e], c = v[e + h];
+          v[e] = a + c;
+          v[e + h] = a - c;
+        }
+      }
+    }
+    // element bits 3..6: lane bits 0..3
+    lane_stage<1>(v, sub);
+    lane_stage<2>(v, sub);
+    lane_stage<4>(v, sub);
+    lane_stage<8>(v, sub);
+    if (!live) continue;
+    if constexpr (OUT_BF16) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = f32_to_bf16_rne(v[2 * i] * kInvSqrt128) | (f32_to_bf16_rne(v[2 * i + 1] * kInvSqrt128) << 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
+    } else {
+      f32x4 a, c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = v[i] * kInvSqrt128;
+        c[i] = v[4 + i] * kInvSqrt128;
+      }
+      f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + base);
+      p[0] = a;
+      p[1] = c;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
+                          hipStream_t stream) {
+  const int64_t nblocks = rows * (K / kBlock);
+  if (nblocks == 0) return hipSuccess;
+  int64_t groups = (nblocks + 15) / 16;
+  const int64_t cap = 1 << 20;
+  const unsigned grid = (unsigned)(groups < cap ? groups : cap);
+  const bool ib = x_dtype == TB_BF16, ob = y_dtype == TB_BF16;
+  if (ib && ob)
+    hipLaunchKernelGGL((fwht128_kernel<true, true>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
+  else if (ib && !ob)
+    hipLaunchKernelGGL((fwht128_kernel<true, false>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
+  else if (!ib && ob)
+    hipLaunchKernelGGL((fwht128_kernel<false, true>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
+  else
+    hipLaunchKernelGGL((fwht128_kernel<false, false>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace tb

@@ -1,0 +1,207 @@
+// Offline quantise/pack: per 128x128 block W' = H B H^T / 128, absmean scale
+// per 128-group (one row of a block), ternarise, pack.
+//
+// Method: mhpq.cn/news/1159370 §1.1 (scale = the group's mean absolute value;
+// divide, round, clip to {-1, 0, 1}), §1.2 (2:4: keep two of four, ternarise
+// the survivors), §1.3 (one fp16 scale per 128 elements), §3.1 (2 bits per
+// weight); dpshk.com/news/5289456 §2.1 and §3.2 (transform per 128x128 block,
+// then sign(w) * (|w| > thr)).
+//
+// One workgroup of 256 threads owns one block at a time:
+//   phase A  thread (column c, row half h) loads 64 rows of one column with
+//            coalesced 128-byte row segments and runs the column transform:
+//            6 butterfly rounds in registers, the 7th across lane ^ 32 with
+//            v_permlane32_swap; the block goes to LDS (fp32, 67.6 KB);
+//   phase B  thread (row r, column half h) reads 64 contiguous columns of its
+//            row with 16-byte LDS reads and runs the row transform the same
+//            way.  Each thread now holds 64 consecutive K-elements of one row:
+//            the group's |.| sum is an in-register sum plus one exchange, and
+//            the codes of 64 elements pack into four whole words.
+// The 1/128 of the 2D transform is a power of two; it is folded into the
+// threshold and the stored scale instead of being applied to every element.
+#include "tb_common.h"
+#include "tb_launch.h"
+
+namespace tb {
+
+namespace {
+
+constexpr int kLdsStride = kBlock + 4;  // floats per LDS row (bank spread for 16-byte reads)
+
+// In-register butterflies over the six low index bits of 64 values.
+__device__ __forceinline__ void fwht64_regs(float (&v)[64]) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+      if ((e & h) == 0) {
+        float a = v[e], c = v[e + h];
+        v[e] = a + c;
+        v[e + h] = a - c;
+      }
+    }
+  }
+}
+
+// Butterfly round over lane bit 5 (the 7th index bit): lanes 0-31 hold index
+// bit 6 = 0 and get own + partner, lanes 32-63 get partner - own.
+__device__ __forceinline__ void fwht_cross_halves(float (&v)[64], float sgn) {
+#pragma unroll
+  for (int e = 0; e < 64; ++e) {
+    float lo, hi;
+    swap_halves(v[e], lo, hi);
+    v[e] = lo + sgn * hi;
+  }
+}
+
+// 2-bit field position of K-offset r (0..15) inside a code word.
+__device__ __forceinline__ constexpr int field_pos(int r) { return 2 * (r >> 1) + 16 * (r & 1); }
+
+template <bool FMT24>
+__global__ void __launch_bounds__(256) quantize128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                           uint32_t* __restrict__ codes,
+                                                           uint32_t* __restrict__ meta,
+                                                           uint16_t* __restrict__ scales,
+                                                           int32_t* __restrict__ err_flag) {
+  __shared__ float lds[kBlock * kLdsStride];
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;      // lane bit 5
+  const int col = 32 * wv + (lane & 31);
+  const float sgn = half ? -1.f : 1.f;
+  const int64_t kblocks = K / kBlock;
+  const int64_t nblk = (N / kBlock) * kblocks;
+
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t n0 = (blk / kblocks) * kBlock;
+    const int64_t bk = blk % kblocks;
+    const int64_t k0 = bk * kBlock;
+    uint32_t flags = 0;
+
+    // ---- phase A: column transform (along N) ----
+    float v[64];
+    {
+      const float* src = W + (n0 + 64 * half) * K + k0 + col;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = __builtin_nontemporal_load(src + (int64_t)i * K);
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (!__builtin_isfinite(v[i])) flags |= TB_EFLAG_NONFINITE;
+    fwht64_regs(v);
+    fwht_cross_halves(v, sgn);
+    __syncthreads();  // previous block's phase B reads are done
+    {
+      // row r = 64*half + i; XOR-swizzle the column by row bit 6 to spread banks
+      const int pc = col ^ (half << 5);
+#pragma unroll
+      for (int i = 0; i < 64; ++i) lds[(64 * half + i) * kLdsStride + pc] = v[i];
+    }
+    __syncthreads();
+
+    // ---- phase B: row transform (along K) ----
+    const int row = 32 * wv + (lane & 31);
+    {
+      const int sw = ((row >> 6) & 1) << 5;
+      const float* rp = lds + row * kLdsStride;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + ((64 * half + 4 * q) ^ sw));
+        v[4 * q] = t4[0];
+        v[4 * q + 1] = t4[1];
+        v[4 * q + 2] = t4[2];
+        v[4 * q + 3] = t4[3];
+      }
+    }
+    fwht64_regs(v);
+    fwht_cross_halves(v, sgn);
+    // v[j] = T[row][64*half + j] with T = H B H^T (unnormalised: W' = T / 128)
+
+    const int64_t grow = n0 + row;
+    if constexpr (!FMT24) {
+      float asum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) asum += __builtin_fabsf(v[j]);
+      float lo, hi;
+      swap_halves(asum, lo, hi);
+      const float tsum = lo + hi;               // sum over the 128-group of |T|
+      const float thr = tsum * 0.00390625f;     // |W'| > s/2  <=>  |T| > sum|T| / 256
+      const float s = tsum * 6.103515625e-05f;  // s = sum|T| / 128 / 128
+      u32x4 words = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const uint32_t nz = __builtin_fabsf(v[j]) > thr ? 1u : 0u;
+        const uint32_t ng = (nz && v[j] < 0.f) ? 2u : 0u;
+        words[j >> 4] |= (nz | ng) << field_pos(j & 15);
+      }
+      *reinterpret_cast<u32x4*>(codes + grow * (K / 16) + k0 / 16 + 4 * half) = words;
+      if (half == 0) {
+        const uint32_t h16 = f32_to_f16_bits(s);
+        if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
+        scales[grow * kblocks + bk] = (uint16_t)h16;
+      }
+    } else {
+      // 2:4: in each quad keep the two largest |T|, ties to the lower position
+      float ksum = 0.f;
+      uint32_t nib[16];
+      uint32_t sbits = 0;
+#pragma unroll
+      for (int qd = 0; qd < 16; ++qd) {
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = __builtin_fabsf(v[4 * qd + e]);
+        bool keep[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int beaten = 0;
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            if (f != e) beaten += (a[f] > a[e] || (a[f] == a[e] && f < e)) ? 1 : 0;
+          keep[e] = beaten < 2;
+        }
+        // exactly two are kept: the first is at 0..2, the second at 1..3
+        const uint32_t i0 = keep[0] ? 0u : (keep[1] ? 1u : 2u);
+        const uint32_t i1 = keep[3] ? 3u : (keep[2] ? 2u : 1u);
+        const float v0 = keep[0] ? v[4 * qd] : (keep[1] ? v[4 * qd + 1] : v[4 * qd + 2]);
+        const float v1 = keep[3] ? v[4 * qd + 3] : (keep[2] ? v[4 * qd + 2] : v[4 * qd + 1]);
+        ksum += __builtin_fabsf(v0) + __builtin_fabsf(v1);
+        nib[qd] = i0 | (i1 << 2);
+        sbits |= (v0 < 0.f ? 1u : 0u) << qd;
+        sbits |= (v1 < 0.f ? 1u : 0u) << (16 + qd);
+      }
+      float lo, hi;
+      swap_halves(ksum, lo, hi);
+      const float s = (lo + hi) * 0.0001220703125f;  // mean over 64 kept of |T|/128
+      u32x2 mw = {0u, 0u};
+#pragma unroll
+      for (int qd = 0; qd < 16; ++qd) mw[qd >> 3] |= nib[qd] << (4 * (qd & 7));
+      *reinterpret_cast<u32x2*>(meta + grow * (K / 32) + k0 / 32 + 2 * half) = mw;
+      codes[grow * (K / 64) + k0 / 64 + half] = sbits;
+      if (half == 0) {
+        const uint32_t h16 = f32_to_f16_bits(s);
+        if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
+        scales[grow * kblocks + bk] = (uint16_t)h16;
+      }
+    }
+    wave_flag_or(err_flag, flags);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
+                              uint16_t* scales, int32_t* err_flag, hipStream_t stream) {
+  const int64_t nblk = (N / kBlock) * (K / kBlock);
+  const int64_t cap = 1 << 20;
+  const unsigned grid = (unsigned)(nblk < cap ? nblk : cap);
+  if (fmt == TB_FMT_24)
+    hipLaunchKernelGGL((quantize128_kernel<true>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta, scales,
+                       err_flag);
+  else
+    hipLaunchKernelGGL((quantize128_kernel<false>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta, scales,
+                       err_flag);
+  return hipGetLastError();
+}
+
+}  // namespace tb

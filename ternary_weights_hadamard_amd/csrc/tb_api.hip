@@ -1,0 +1,128 @@
+// C ABI of libtb: host-side argument validation, then one launch on the
+// caller's stream.  Validation makes no HIP call, so every error path can be
+// exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tb.h"
+#include "tb_launch.h"
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dims_ok(int64_t N, int64_t K) { return N > 0 && K > 0 && N % kGroup == 0 && K % kGroup == 0; }
+bool dtype_ok(int d) { return d == TB_F32 || d == TB_BF16; }
+size_t dtype_bytes(int d) { return d == TB_F32 ? 4 : 2; }
+
+// [a, a + na) and [b, b + nb) intersect (byte ranges)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+tb_status launched(hipError_t e) { return e == hipSuccess ? TB_OK : TB_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* tb_status_string(int status) {
+  switch (status) {
+    case TB_OK: return "TB_OK";
+    case TB_ERR_NULL: return "TB_ERR_NULL: a required pointer is NULL";
+    case TB_ERR_SHAPE: return "TB_ERR_SHAPE: N and K must be positive multiples of 128 and the batch in range";
+    case TB_ERR_ALIGN: return "TB_ERR_ALIGN: pointers must be 16-byte aligned";
+    case TB_ERR_DTYPE: return "TB_ERR_DTYPE: unknown dtype";
+    case TB_ERR_FORMAT: return "TB_ERR_FORMAT: unknown format or wrong planes for it";
+    case TB_ERR_LAUNCH: return "TB_ERR_LAUNCH: the HIP runtime refused the launch";
+    case TB_ERR_UNSUPPORTED: return "TB_ERR_UNSUPPORTED: not implemented";
+    case TB_ERR_ALIAS: return "TB_ERR_ALIAS: output overlaps an input";
+    default: return "unknown tb_status";
+  }
+}
+
+int tb_version(void) { return 100; }
+
+tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
+                          size_t* scale_bytes) {
+  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24) return TB_ERR_FORMAT;
+  if (!dims_ok(N, K)) return TB_ERR_SHAPE;
+  const size_t nk = (size_t)N * (size_t)K;
+  if (code_bytes) *code_bytes = fmt == TB_FMT_DENSE ? nk / 4 : nk / 16;
+  if (meta_bytes) *meta_bytes = fmt == TB_FMT_DENSE ? 0 : nk / 8;
+  if (scale_bytes) *scale_bytes = nk / 64;
+  return TB_OK;
+}
+
+tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return TB_ERR_DTYPE;
+  if (rows < 0 || K <= 0 || K % kGroup) return TB_ERR_SHAPE;
+  if (rows == 0) return TB_OK;
+  if (!x || !y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return TB_ERR_ALIGN;
+  const size_t n = (size_t)rows * (size_t)K;
+  if (x != y && overlap(x, n * dtype_bytes(x_dtype), y, n * dtype_bytes(y_dtype))) return TB_ERR_ALIAS;
+  if (x == y && x_dtype != y_dtype) return TB_ERR_ALIAS;
+  return launched(tb::launch_fwht128(x, x_dtype, y, y_dtype, rows, K, as_stream(stream)));
+}
+
+tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
+                           uint16_t* scales, int32_t* err_flag, void* stream) {
+  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24) return TB_ERR_FORMAT;
+  if (fmt == TB_FMT_DENSE && meta) return TB_ERR_FORMAT;
+  if (!dims_ok(N, K)) return TB_ERR_SHAPE;
+  if (!W || !codes || !scales || (fmt == TB_FMT_24 && !meta)) return TB_ERR_NULL;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(scales) || (meta && !aligned16(meta))) return TB_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(err_flag) & 3u) != 0) return TB_ERR_ALIGN;
+  const size_t nk = (size_t)N * (size_t)K;
+  const size_t cb = fmt == TB_FMT_DENSE ? nk / 4 : nk / 16, mb = fmt == TB_FMT_DENSE ? 0 : nk / 8, sb = nk / 64;
+  if (overlap(W, nk * 4, codes, cb) || overlap(W, nk * 4, scales, sb) || overlap(codes, cb, scales, sb) ||
+      (meta && (overlap(W, nk * 4, meta, mb) || overlap(meta, mb, codes, cb) || overlap(meta, mb, scales, sb))))
+    return TB_ERR_ALIAS;
+  return launched(tb::launch_quantize128(W, N, K, fmt, codes, meta, scales, err_flag, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemv(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
+                          int64_t K, float* y, void* stream) {
+  if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+  if (B == 0) return TB_OK;
+  if (!x || !codes || !scales || !y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return TB_ERR_ALIGN;
+  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)B * (size_t)N * 4;
+  if (overlap(y, yb, x, (size_t)B * K * 2) || overlap(y, yb, codes, nk / 4) || overlap(y, yb, scales, nk / 64))
+    return TB_ERR_ALIAS;
+  return launched(tb::launch_gemv_ternary(x, B, codes, scales, N, K, y, as_stream(stream)));
+}
+
+tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
+                            const uint16_t* scales, int64_t N, int64_t K, float* y, void* stream) {
+  if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+  if (B == 0) return TB_OK;
+  if (!x || !meta || !signs || !scales || !y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(meta) || !aligned16(signs) || !aligned16(scales) || !aligned16(y))
+    return TB_ERR_ALIGN;
+  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)B * (size_t)N * 4;
+  if (overlap(y, yb, x, (size_t)B * K * 2) || overlap(y, yb, meta, nk / 8) || overlap(y, yb, signs, nk / 16) ||
+      overlap(y, yb, scales, nk / 64))
+    return TB_ERR_ALIAS;
+  return launched(tb::launch_gemv_ternary24(x, B, meta, signs, scales, N, K, y, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
+                          int64_t K, void* y, int y_dtype, void* stream) {
+  if (!dtype_ok(y_dtype)) return TB_ERR_DTYPE;
+  if (!dims_ok(N, K) || M < 0 || M > (int64_t)65535 * 128) return TB_ERR_SHAPE;
+  if (M == 0) return TB_OK;
+  if (!x || !codes || !scales || !y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return TB_ERR_ALIGN;
+  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)M * (size_t)N * dtype_bytes(y_dtype);
+  if (overlap(y, yb, x, (size_t)M * K * 2) || overlap(y, yb, codes, nk / 4) || overlap(y, yb, scales, nk / 64))
+    return TB_ERR_ALIAS;
+  return launched(tb::launch_gemm_ternary(x, M, codes, scales, N, K, y, y_dtype, as_stream(stream)));
+}
+
+}  // extern "C"

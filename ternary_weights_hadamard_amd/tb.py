@@ -1,0 +1,169 @@
+"""Thin ctypes binding over libtb.so (the C ABI declared in include/tb.h).
+
+Argument marshalling only: tensors are device buffers (torch is used for
+device memory and streams), every step of the computation runs in the HIP
+kernels behind the C ABI.  There is no fallback: if the library is missing or
+a call fails, these functions raise.
+
+Dtypes on the Python side (bit patterns are what matter):
+  activations x      torch.bfloat16 (or int16/uint16 bit views)  [rows, K]
+  weights W          torch.float32 [N, K]
+  codes / meta / signs  torch.int32 (uint32 bit patterns)
+  scales             torch.float16 (fp16 bit patterns) [N, K/128]
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtb.so")
+
+TB_F32, TB_BF16 = 0, 1
+TB_FMT_DENSE, TB_FMT_24 = 0, 1
+TB_EFLAG_NONFINITE, TB_EFLAG_SCALE_OVF = 1, 2
+TB_GEMV_MAX_BATCH = 16
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+
+SIGNATURES = {
+    "tb_status_string": (ctypes.c_char_p, [_int]),
+    "tb_version": (_int, []),
+    "tb_packed_bytes": (_int, [_int, _i64, _i64, ctypes.POINTER(ctypes.c_size_t),
+                               ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "tb_fwht128": (_int, [_vp, _int, _vp, _int, _i64, _i64, _vp]),
+    "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
+    "tb_ternary_gemv": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "tb_ternary_gemm": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]),
+}
+
+
+class TBError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)}")
+
+
+def lib():
+    """Load libtb.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m ternary_weights_hadamard_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(code):
+    return lib().tb_status_string(int(code)).decode()
+
+
+def _check(code, where):
+    if code != 0:
+        raise TBError(code, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return TB_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return TB_BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("buffers must be contiguous device tensors")
+
+
+def tb_packed_bytes(fmt, n, k):
+    c, m, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().tb_packed_bytes(int(fmt), int(n), int(k), ctypes.byref(c), ctypes.byref(m), ctypes.byref(s)),
+           "tb_packed_bytes")
+    return c.value, m.value, s.value
+
+
+def tb_fwht128(x, y=None, out_dtype=None, stream=None):
+    """y[r, 128b + i] = sum_j H[i, j] / sqrt(128) * x[r, 128b + j]; y may be x."""
+    _dev(x)
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _dev(y)
+    rows = x.numel() // x.shape[-1] if x.numel() else 0
+    _check(lib().tb_fwht128(_p(x), _dt(x), _p(y), _dt(y), rows, x.shape[-1], _stream(stream)), "tb_fwht128")
+    return y
+
+
+def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, err_flag=None, stream=None):
+    """Quantise fp32 W [N, K]; returns (codes, meta, scales).  For TB_FMT_24 `codes` is the sign plane."""
+    _dev(w)
+    n, k = w.shape
+    dev = w.device
+    if codes is None:
+        codes = torch.empty((n, k // (16 if fmt == TB_FMT_DENSE else 64)), dtype=torch.int32, device=dev)
+    if meta is None and fmt == TB_FMT_24:
+        meta = torch.empty((n, k // 32), dtype=torch.int32, device=dev)
+    if scales is None:
+        scales = torch.empty((n, k // 128), dtype=torch.float16, device=dev)
+    _dev(codes, meta, scales, err_flag)
+    _check(lib().tb_quantize_pack(_p(w), n, k, int(fmt), _p(codes), _p(meta), _p(scales), _p(err_flag),
+                                  _stream(stream)), "tb_quantize_pack")
+    return codes, meta, scales
+
+
+def tb_ternary_gemv(x, codes, scales, y=None, stream=None):
+    """y[b, n] (fp32) = sum_g scale[n, g] * sum_k t[n, k] x[b, k]; x bf16 [B, K]."""
+    _dev(x, codes, scales)
+    b, k = x.shape
+    n = codes.shape[0]
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _dev(y)
+    _check(lib().tb_ternary_gemv(_p(x), b, _p(codes), _p(scales), n, k, _p(y), _stream(stream)), "tb_ternary_gemv")
+    return y
+
+
+def tb_ternary24_gemv(x, meta, signs, scales, y=None, stream=None):
+    _dev(x, meta, signs, scales)
+    b, k = x.shape
+    n = meta.shape[0]
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _dev(y)
+    _check(lib().tb_ternary24_gemv(_p(x), b, _p(meta), _p(signs), _p(scales), n, k, _p(y), _stream(stream)),
+           "tb_ternary24_gemv")
+    return y
+
+
+def tb_ternary_gemm(x, codes, scales, y=None, out_dtype=torch.bfloat16, stream=None):
+    """Y[m, n] = sum_g scale[n, g] * sum_k t[n, k] x[m, k]; x bf16 [M, K], Y bf16 or fp32."""
+    _dev(x, codes, scales)
+    m, k = x.shape
+    n = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _dev(y)
+    _check(lib().tb_ternary_gemm(_p(x), m, _p(codes), _p(scales), n, k, _p(y), _dt(y), _stream(stream)),
+           "tb_ternary_gemm")
+    return y

@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI: the built library loads, exports every entry point
+that include/tb.h declares, and rejects bad arguments on the host before any
+GPU work (no call here gets past validation, so no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_weights_hadamard_amd import tb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tb.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tb.LIB_PATH), reason="libtb.so not built")
+
+A = 0x10000  # 16-byte aligned fake device addresses (never dereferenced)
+B = 0x20000
+C = 0x30000
+D = 0x40000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(tb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"tb_fwht128", "tb_quantize_pack", "tb_ternary_gemv", "tb_ternary24_gemv", "tb_ternary_gemm"} <= set(names)
+    handle = ctypes.CDLL(tb.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(tb.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    L = tb.lib()
+    assert L.tb_version() >= 100
+    for code in range(9):
+        assert L.tb_status_string(code)
+    assert b"unknown" in L.tb_status_string(99)
+
+
+def test_packed_bytes():
+    assert tb.tb_packed_bytes(tb.TB_FMT_DENSE, 5120, 17408) == (5120 * 17408 // 4, 0, 5120 * 17408 // 64)
+    assert tb.tb_packed_bytes(tb.TB_FMT_24, 17408, 5120) == (17408 * 5120 // 16, 17408 * 5120 // 8, 17408 * 5120 // 64)
+    L = tb.lib()
+    assert L.tb_packed_bytes(7, 128, 128, None, None, None) == 5
+    assert L.tb_packed_bytes(0, 100, 128, None, None, None) == 2
+    assert L.tb_packed_bytes(0, 128, 0, None, None, None) == 2
+
+
+def _v(x):
+    return ctypes.c_void_p(x)
+
+
+def test_fwht_validation():
+    L = tb.lib()
+    s = None
+    assert L.tb_fwht128(_v(A), 5, _v(B), 1, 1, 128, s) == 4       # unknown dtype
+    assert L.tb_fwht128(_v(A), 1, _v(B), 1, 1, 100, s) == 2      # K not a multiple of 128
+    assert L.tb_fwht128(_v(A), 1, _v(B), 1, -1, 128, s) == 2     # negative rows
+    assert L.tb_fwht128(None, 1, _v(B), 1, 1, 128, s) == 1       # NULL
+    assert L.tb_fwht128(_v(MIS), 1, _v(B), 1, 1, 128, s) == 3    # misaligned
+    assert L.tb_fwht128(_v(A), 1, _v(A + 64), 1, 1, 128, s) == 8  # partial overlap
+    assert L.tb_fwht128(_v(A), 1, _v(A), 0, 1, 128, s) == 8      # in place with different dtypes
+    assert L.tb_fwht128(None, 1, None, 1, 0, 128, s) == 0        # empty batch is a no-op
+
+
+def test_quantize_validation():
+    L = tb.lib()
+    s = None
+    assert L.tb_quantize_pack(_v(A), 128, 128, 3, _v(B), None, _v(C), None, s) == 5   # bad format
+    assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(B), _v(D), _v(C), None, s) == 5  # meta given for dense
+    assert L.tb_quantize_pack(_v(A), 128, 128, 1, _v(B), None, _v(C), None, s) == 1   # meta missing for 2:4
+    assert L.tb_quantize_pack(_v(A), 130, 128, 0, _v(B), None, _v(C), None, s) == 2
+    assert L.tb_quantize_pack(_v(A), 128, 0, 0, _v(B), None, _v(C), None, s) == 2
+    assert L.tb_quantize_pack(None, 128, 128, 0, _v(B), None, _v(C), None, s) == 1
+    assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(MIS), None, _v(C), None, s) == 3
+    assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(B), None, _v(C), _v(D + 2), s) == 3  # flag misaligned
+    assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(A + 1024), None, _v(C), None, s) == 8  # codes inside W
+
+
+def test_gemv_validation():
+    L = tb.lib()
+    s = None
+    assert L.tb_ternary_gemv(_v(A), 17, _v(B), _v(C), 128, 128, _v(D), s) == 2   # B > 16
+    assert L.tb_ternary_gemv(_v(A), -1, _v(B), _v(C), 128, 128, _v(D), s) == 2
+    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 100, 128, _v(D), s) == 2
+    assert L.tb_ternary_gemv(_v(A), 1, None, _v(C), 128, 128, _v(D), s) == 1
+    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(MIS), s) == 3
+    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(B), s) == 8     # y over codes
+    assert L.tb_ternary_gemv(None, 0, None, None, 128, 128, None, s) == 0         # empty batch
+    assert L.tb_ternary24_gemv(_v(A), 1, _v(B), None, _v(C), 128, 128, _v(D), s) == 1
+    assert L.tb_ternary24_gemv(_v(A), 1, _v(B), _v(C), _v(D), 128, 384, _v(MIS), s) == 3
+    assert L.tb_ternary24_gemv(_v(A), 20, _v(B), _v(C), _v(D), 128, 384, _v(A), s) == 2
+
+
+def test_gemm_validation():
+    L = tb.lib()
+    s = None
+    assert L.tb_ternary_gemm(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 9, s) == 4   # bad dtype
+    assert L.tb_ternary_gemm(_v(A), -4, _v(B), _v(C), 128, 128, _v(D), 1, s) == 2
+    assert L.tb_ternary_gemm(_v(A), 4, _v(B), _v(C), 128, 200, _v(D), 1, s) == 2
+    assert L.tb_ternary_gemm(_v(A), 4, _v(B), None, 128, 128, _v(D), 1, s) == 1
+    assert L.tb_ternary_gemm(_v(MIS), 4, _v(B), _v(C), 128, 128, _v(D), 1, s) == 3
+    assert L.tb_ternary_gemm(_v(A), 4, _v(B), _v(C), 128, 128, _v(A), 0, s) == 8
+    assert L.tb_ternary_gemm(None, 0, None, None, 128, 128, None, 1, s) == 0
+
+
+def test_binding_raises_typed_error_on_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        tb.tb_fwht128(torch.zeros(1, 128, dtype=torch.bfloat16))

@@ -1,0 +1,79 @@
+"""GPU parity of tb_fwht128 against the oracle's blockwise transform."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, assert_close, bf16_dev, f32_dev, host_f64, host_u16, say
+from ternary_weights_hadamard_amd import synth, tb
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("rows,k", [(1, 128), (3, 384), (17, 1024), (64, 5120), (5, 17408)])
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
+def test_fwht_matches_oracle(rows, k, din, dout):
+    say(f"fwht rows={rows} K={k} {din}->{dout}")
+    xb = synth.gaussian_bf16((rows, k), seed=rows * 7 + k)
+    if din == "bf16":
+        xin = bf16_dev(xb)
+        xv = oracle.numerics.bf16_bits_to_f64(xb)
+    else:
+        xf = np.random.default_rng(k).standard_normal((rows, k)).astype(np.float32)
+        xin = f32_dev(xf)
+        xv = xf.astype(np.float64)
+    y = tb.tb_fwht128(xin, out_dtype=torch.bfloat16 if dout == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.hadamard.fwht_dense(xv)
+    assert_close(host_f64(y), ref, f"fwht {din}->{dout}")
+    if dout == "f32":
+        # fp32 arithmetic: far inside the bar
+        assert np.max(np.abs(host_f64(y) - ref)) <= 1e-5 * np.max(np.abs(ref))
+    else:
+        # bf16 output: within one bf16 rounding of the exact value
+        err = np.abs(host_f64(y) - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-30 + 1e-6 * np.max(np.abs(ref)))
+
+
+def test_fwht_in_place_and_special_vectors():
+    k = 256
+    x = np.zeros((4, k), dtype=np.float32)
+    x[0, 0] = 1.0        # spike -> every output +-1/sqrt(128)
+    x[1, 200] = -3.0
+    x[2, :128] = 0.5     # constant block -> DC only
+    x[3] = np.arange(k, dtype=np.float32)
+    t = f32_dev(x)
+    ptr = t.data_ptr()
+    out = tb.tb_fwht128(t, y=t)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == ptr
+    ref = oracle.hadamard.fwht_dense(x.astype(np.float64))
+    got = host_f64(t)
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+    assert np.allclose(np.abs(got[0, :128]), 1 / np.sqrt(128), rtol=1e-6)
+    assert np.all(got[0, 128:] == 0)
+    assert abs(got[2, 0] - 0.5 * np.sqrt(128)) < 1e-5 and np.max(np.abs(got[2, 1:])) < 1e-6
+    # applying the transform twice gives the input back (it is its own inverse)
+    tb.tb_fwht128(t, y=t)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(host_f64(t) - x)) <= 1e-5 * np.max(np.abs(x))
+
+
+def test_fwht_bf16_in_place_and_canaries():
+    k = 384
+    xb = synth.gaussian_bf16((9, k), seed=3)
+    buf = torch.full((9 * k + 64,), -7.0, dtype=torch.bfloat16, device=DEV)
+    view = buf[32:32 + 9 * k].view(9, k)
+    view.copy_(bf16_dev(xb))
+    tb.tb_fwht128(view, y=view)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:32] == -7.0) and torch.all(buf[32 + 9 * k:] == -7.0)
+    ref = oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(xb))
+    assert_close(host_f64(view), ref, "fwht bf16 in place")
+
+
+def test_fwht_empty_batch_is_noop():
+    t = torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV)
+    tb.tb_fwht128(t)
+    torch.cuda.synchronize()

@@ -1,0 +1,70 @@
+"""GPU parity of tb_ternary_gemm against the oracle (and against the GEMV)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, assert_close, bf16_dev, f16_dev, host_f64, say, u32_dev
+from ternary_weights_hadamard_amd import synth, tb
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (7, 256, 384), (128, 128, 1024), (300, 384, 640), (257, 256, 256)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_gemm_small_matches_oracle(m, n, k, out):
+    say(f"gemm M={m} N={n} K={k} {out}")
+    codes = synth.random_code_words(n, k, seed=m + n)
+    scales = synth.random_scales_f16(n, k, seed=k)
+    x = synth.gaussian_bf16((m, k), seed=m)
+    y = tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(scales),
+                           out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matvec.gemm(x, codes, scales, k)
+    assert_close(host_f64(y), ref, f"gemm {m}x{n}x{k} {out}")
+
+
+@pytest.mark.parametrize("k,n", [(5120, 17408), (17408, 5120)])
+def test_gemm_full_size_sampled(k, n):
+    m = 2048
+    say(f"gemm full M={m} K={k} N={n}")
+    codes = synth.random_code_words(n, k, seed=40 if k == 5120 else 41)
+    scales = synth.random_scales_f16(n, k, seed=43)
+    x = synth.gaussian_bf16((m, k), seed=42)
+    for out in (torch.bfloat16, torch.float32):
+        y = host_f64(tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(scales), out_dtype=out))
+        rs = np.sort(np.random.default_rng(5).choice(m, 64, replace=False))
+        cs = np.sort(np.random.default_rng(6).choice(n, 96, replace=False))
+        ref = oracle.matvec.gemm(x[rs], codes[cs], scales[cs], k)
+        assert_close(y[np.ix_(rs, cs)], ref, f"gemm {m}x{n}x{k} {out} (64x96 sampled)")
+        del y
+
+
+def test_gemm_exact_small_integers_and_gemv_agreement():
+    m, n, k = 33, 256, 1024
+    codes = synth.random_code_words(n, k, seed=50)
+    x = synth.small_int_bf16((m, k), seed=51)
+    sc = (2.0 ** np.random.default_rng(52).integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    y = tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(sc), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
+    # rows 0..7 through the GEMV give the same exact values
+    yv = tb.tb_ternary_gemv(bf16_dev(x[:8]), u32_dev(codes), f16_dev(sc))
+    torch.cuda.synchronize()
+    assert np.array_equal(yv.cpu().numpy(), y.cpu().numpy()[:8])
+
+
+def test_gemm_canaries_and_empty():
+    m, n, k = 130, 128, 256
+    codes = synth.random_code_words(n, k, seed=60)
+    scales = synth.random_scales_f16(n, k, seed=61)
+    x = synth.gaussian_bf16((m, k), seed=62)
+    buf = torch.full((m * n + 256,), -9.0, dtype=torch.bfloat16, device=DEV)
+    y = buf[128:128 + m * n].view(m, n)
+    tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(scales), y=y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:128] == -9.0) and torch.all(buf[128 + m * n:] == -9.0)
+    assert_close(host_f64(y), oracle.matvec.gemm(x, codes, scales, k), "gemm canary run")
+    e = tb.tb_ternary_gemm(torch.empty((0, k), dtype=torch.bfloat16, device=DEV), u32_dev(codes), f16_dev(scales))
+    assert e.shape == (0, n)

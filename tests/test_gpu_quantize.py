@@ -1,0 +1,110 @@
+"""GPU parity of tb_quantize_pack (dense and 2:4) against the oracle."""
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from gpu_util import DEV, check_dense_codes, f32_dev, host_u16, host_u32, say
+from ternary_weights_hadamard_amd import synth, tb
+
+pytestmark = pytest.mark.gpu
+
+H = scipy.linalg.hadamard(128).astype(np.float64)
+
+
+def _quant(w, fmt=tb.TB_FMT_DENSE, flag=None):
+    codes, meta, scales = tb.tb_quantize_pack(f32_dev(w), fmt=fmt, err_flag=flag)
+    torch.cuda.synchronize()
+    return codes, meta, scales
+
+
+def test_single_layer_1024_seed0():
+    # 1024 x 1024, N(0, 0.02^2) with 0.1 % outliers x20, seed 0
+    w = synth.single_layer_weights(1024, 1024, seed=0)
+    say("quantize 1024x1024 seed 0")
+    codes, _, scales = _quant(w)
+    ref = oracle.quant.quantize_dense(w.astype(np.float64))
+    check_dense_codes(codes, scales, ref, 1024, "1024^2")
+
+
+@pytest.mark.parametrize("n,k,seed", [(128, 128, 1), (256, 384, 2), (384, 1280, 3), (640, 256, 4)])
+def test_ragged_block_grids(n, k, seed):
+    w = synth.stack_weights(n, k, seed=seed)
+    say(f"quantize {n}x{k} seed {seed}")
+    codes, _, scales = _quant(w)
+    check_dense_codes(codes, scales, oracle.quant.quantize_dense(w.astype(np.float64)), k, f"{n}x{k}")
+
+
+def test_closed_form_blocks():
+    w = np.zeros((256, 512), dtype=np.float32)
+    w[3, 9] = 4.0                    # spike in block (0,0): lossless, all codes +-1
+    w[128:256, 128:256] = np.eye(128, dtype=np.float32)  # identity block
+    w[:128, 256:384] = 0.375         # constant block
+    # block (1, 3) stays zero
+    codes, _, scales = _quant(w)
+    ref = oracle.quant.quantize_dense(w.astype(np.float64))
+    check_dense_codes(codes, scales, ref, 512, "closed forms")
+    t = oracle.quant.unpack_dense(host_u32(codes), 512)
+    assert np.array_equal(t, ref["t"])
+    s = host_u16(scales)
+    assert np.all(s[:128, 0] == np.float16(4.0 / 128).view(np.uint16))
+    assert np.all(s[128:, 1] == np.float16(1.0 / 128).view(np.uint16))
+    assert s[0, 2] == np.float16(0.375).view(np.uint16) and np.all(s[1:128, 2] == 0)
+    assert np.all(s[128:, 3] == 0) and np.all(host_u32(codes)[128:, 24:32] == 0)
+
+
+def test_tie_at_half_scale():
+    wr = np.zeros((128, 128))
+    wr[0, :48] = 1.0
+    wr[0, 48:112] = 0.25
+    w = (H @ wr @ H / 128).astype(np.float32)
+    codes, _, scales = _quant(w)
+    t = oracle.quant.unpack_dense(host_u32(codes), 128)
+    assert np.all(t[0, :48] == 1) and np.all(t[0, 48:] == 0)
+    assert host_u16(scales)[0, 0] == np.float16(0.5).view(np.uint16)
+
+
+def test_error_flags():
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    w = np.zeros((128, 256), dtype=np.float32)
+    w[5, 200] = np.nan
+    _quant(w, flag=flag)
+    assert int(flag.item()) & tb.TB_EFLAG_NONFINITE
+    flag.zero_()
+    w = np.full((128, 128), 1.0e5, dtype=np.float32)  # row 0 scale = 1e5 > fp16 max
+    _quant(w, flag=flag)
+    assert int(flag.item()) & tb.TB_EFLAG_SCALE_OVF
+    flag.zero_()
+    _quant(synth.stack_weights(128, 128, seed=5), flag=flag)
+    assert int(flag.item()) == 0
+
+
+def test_output_canaries():
+    n, k = 256, 256
+    w = synth.stack_weights(n, k, seed=6)
+    cb = torch.full((n * k // 16 + 8,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    sb = torch.full((n * k // 128 + 16,), -3.0, dtype=torch.float16, device=DEV)
+    codes = cb[4:4 + n * k // 16].view(n, k // 16)
+    scales = sb[8:8 + n * k // 128].view(n, k // 128)
+    tb.tb_quantize_pack(f32_dev(w), codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    assert torch.all(cb[:4] == 0x5A5A5A5A) and torch.all(cb[4 + n * k // 16:] == 0x5A5A5A5A)
+    assert torch.all(sb[:8] == -3.0) and torch.all(sb[8 + n * k // 128:] == -3.0)
+    check_dense_codes(codes, scales, oracle.quant.quantize_dense(w.astype(np.float64)), k, "canary run")
+
+
+@pytest.mark.parametrize("n,k,seed", [(128, 128, 11), (256, 512, 12), (1024, 1024, 0)])
+def test_24_matches_oracle(n, k, seed):
+    w = synth.single_layer_weights(n, k, seed=seed) if seed == 0 else synth.stack_weights(n, k, seed=seed)
+    say(f"quantize 2:4 {n}x{k}")
+    signs, meta, scales = _quant(w, fmt=tb.TB_FMT_24)
+    ref = oracle.quant.quantize_24(w.astype(np.float64))
+    i0, i1, n0, n1 = oracle.quant.unpack_24(host_u32(meta), host_u32(signs), k)
+    tie = oracle.quant.near_tie_24(ref["wr"], ref["s"])
+    bad = ((i0 != ref["idx0"]) | (i1 != ref["idx1"]) | (n0 != ref["neg0"]) | (n1 != ref["neg1"])) & ~tie
+    say(f"  2:4 {n}x{k}: {int(tie.sum())} near-tie quads, {int(bad.sum())} mismatches outside them")
+    assert not bad.any()
+    ulp = np.abs(host_u16(scales).astype(np.int64) - ref["scales"].astype(np.int64))
+    assert ulp.max() <= 1
