@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hadamard-rotated ternary-weight path on one MI355X.
+
+Timed step (the value): one decode token through a 64-layer 27B-shaped stack
+(d_model 5120, d_ff 17408) at batch 1: for every layer and each fused
+projection (QKV 15360x5120, O 5120x5120, gate/up 34816x5120, down
+5120x17408) the activations are rotated (tb_fwht128), multiplied by the packed
+ternary weights (tb_ternary_gemv) and the output is rotated back
+(tb_fwht128 along N).  All 6.33 GB of packed weights are resident in HBM and
+each is read once per step, far beyond the 256 MB last-level cache.  The step
+is captured once in a HIP graph and replayed.
+value = packed weight bytes (codes + scales) streamed per step / step time.
+
+Also measured in the same run, each over its own synthetic input, and
+reported under "extra": the same decode step at batch 8, the 2:4 GEMV
+(17408x5120, batch 1), the prefill GEMM (M = 2048, both FFN shapes), the
+activation FWHT at prefill size, and the offline quantiser over one layer.
+The CPU oracle is timed on a bounded sample of the decode workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_MFMA_TFLOPS = 2500.0    # dense fp16 / bf16 matrix cores
+D, F = 5120, 17408
+FUSED = (("qkv", 3 * D, D), ("o", D, D), ("gate_up", 2 * F, D), ("down", D, F))
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(n, k, b):
+    """Algorithmic bytes of one GEMV launch: codes + scales + activations + output."""
+    return n * k // 4 + n * k // 64 + 2 * b * k + 4 * b * n
+
+
+def packed_bytes(n, k):
+    return n * k // 4 + n * k // 64
+
+
+class DecodeStack:
+    def __init__(self, layers, batch, gen, dev):
+        import torch
+
+        from ternary_weights_hadamard_amd import synth
+
+        self.layers, self.batch = layers, batch
+        self.w = []
+        for li in range(layers):
+            self.w.append([(synth.torch_code_words(n, k, gen, dev), synth.torch_scales_f16(n, k, gen, dev), n, k)
+                           for _, n, k in FUSED])
+            if li % 16 == 15:
+                log(f"  generated {li + 1}/{layers} layers")
+        self.make_acts(batch, gen, dev)
+
+    def make_acts(self, batch, gen, dev):
+        import torch
+
+        from ternary_weights_hadamard_amd import synth
+
+        self.batch = batch
+        self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
+        self.xr = [torch.empty((batch, k), dtype=torch.bfloat16, device=dev) for _, n, k in FUSED]
+        self.yr = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+        self.y = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+
+    def step(self):
+        from ternary_weights_hadamard_amd import tb
+
+        for layer in self.w:
+            for j, (codes, scales, n, k) in enumerate(layer):
+                tb.tb_fwht128(self.x[j], y=self.xr[j])
+                tb.tb_ternary_gemv(self.xr[j], codes, scales, y=self.yr[j])
+                tb.tb_fwht128(self.yr[j], y=self.y[j])
+
+    def packed_bytes(self):
+        return sum(packed_bytes(n, k) for layer in self.w for _, _, n, k in layer)
+
+    def gemv_event_times(self, passes=1):
+        """Per-launch GEMV durations (ms) from HIP events bracketing each launch
+        on the stream it runs on; returns (total bytes, total ms, launches)."""
+        import torch
+
+        from ternary_weights_hadamard_amd import tb
+
+        pairs, nbytes = [], 0
+        for _ in range(passes):
+            for layer in self.w:
+                for j, (codes, scales, n, k) in enumerate(layer):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    tb.tb_ternary_gemv(self.xr[j], codes, scales, y=self.yr[j])
+                    b.record()
+                    pairs.append((a, b))
+                    nbytes += gemv_bytes(n, k, self.batch)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in pairs)
+        return nbytes, ms, len(pairs)
+
+
+def time_graph(fn, steps, warmup):
+    """Capture fn() in a HIP graph, replay `warmup` times untimed, then time
+    exactly `steps` replays bracketed by synchronisations; returns ms total."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager pass (first-touch, library load)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3
+    return t0.elapsed_time(t1), wall, g
+
+
+def time_eager(fn, iters):
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def extra_phases(gen, dev, quick):
+    """Timings of the other rows of the path, each on its own synthetic input."""
+    import torch
+
+    from ternary_weights_hadamard_amd import synth, tb
+
+    out = {}
+    # prefill GEMM, M = 2048, both FFN shapes (bf16 out)
+    m = 2048
+    gemm = {}
+    for k, n in ((D, F), (F, D)):
+        codes = synth.torch_code_words(n, k, gen, dev)
+        scales = synth.torch_scales_f16(n, k, gen, dev)
+        x = synth.torch_gaussian_bf16((m, k), gen, dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ms = time_eager(lambda: tb.tb_ternary_gemm(x, codes, scales, y=y), 3 if quick else 10)
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        gemm[f"{k}x{n}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS, 4)}
+        log(f"  prefill GEMM M={m} K={k} N={n}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        del codes, scales, x, y
+    out["prefill_gemm"] = {"workload": "M=2048, (K,N) = (5120,17408) and (17408,5120), bf16 out", "peak_tflops": PEAK_MFMA_TFLOPS, **gemm}
+
+    # 2:4 GEMV, 17408 x 5120, batch 1, rotated over >= 1 GB of weight copies
+    n, k = F, D
+    copies = 64
+    planes = [synth.torch_24(n, k, gen, dev) + (synth.torch_scales_f16(n, k, gen, dev),) for _ in range(copies)]
+    x = synth.torch_gaussian_bf16((1, k), gen, dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+    def run24():
+        for meta, signs, sc in planes:
+            tb.tb_ternary24_gemv(x, meta, signs, sc, y=y)
+
+    ms = time_eager(run24, 2 if quick else 5) / copies
+    b24 = n * k // 8 + n * k // 16 + n * k // 64 + 2 * k + 4 * n
+    out["gemv24"] = {"workload": "17408x5120 2:4, batch 1, 64 weight copies (1.16 GB) rotated",
+                     "us_per_launch": round(ms * 1e3, 2), "gbs": round(b24 / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(b24 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "note": "eager launches back to back; time includes launch gaps"}
+    log(f"  2:4 GEMV: {ms * 1e3:.2f} us/launch, {out['gemv24']['gbs']} GB/s")
+    del planes
+
+    # activation FWHT at prefill size: 2048 x 17408 bf16 -> bf16
+    xa = synth.torch_gaussian_bf16((2048, F), gen, dev)
+    ya = torch.empty_like(xa)
+    ms = time_eager(lambda: tb.tb_fwht128(xa, y=ya), 5 if quick else 20)
+    fb = 2 * 2 * 2048 * F
+    out["fwht128"] = {"workload": "2048x17408 bf16 -> bf16", "us": round(ms * 1e3, 2),
+                      "gbs": round(fb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"  FWHT 2048x17408: {ms * 1e3:.1f} us, {out['fwht128']['gbs']} GB/s")
+    del xa, ya
+
+    # offline quantiser over one 27B layer (7 matrices, 372M fp32 weights)
+    mats = [("q", D, D), ("k", D, D), ("v", D, D), ("o", D, D), ("up", F, D), ("gate", F, D), ("down", D, F)]
+    ws, outs = [], []
+    for _, n, k in mats:
+        w = torch.randn((n, k), generator=gen, device=dev) * 0.02
+        ws.append(w)
+        outs.append((torch.empty((n, k // 16), dtype=torch.int32, device=dev),
+                     torch.empty((n, k // 128), dtype=torch.float16, device=dev)))
+
+    def runq():
+        for w, (c, s) in zip(ws, outs):
+            tb.tb_quantize_pack(w, codes=c, scales=s)
+
+    ms = time_eager(runq, 2 if quick else 5)
+    nw = sum(n * k for _, n, k in mats)
+    qb = nw * 4 + nw // 4 + nw // 64
+    out["quantize"] = {"workload": "one 27B layer, 7 matrices, 372,244,480 fp32 weights", "ms_per_layer": round(ms, 3),
+                       "gbs": round(qb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(qb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "projected_64_layer_ms": round(64 * ms, 1)}
+    log(f"  quantise one layer: {ms:.3f} ms, {out['quantize']['gbs']} GB/s")
+    del ws, outs
+    return out
+
+
+def cpu_baseline(stack, max_seconds=30.0):
+    """Time the CPU oracle's GEMV on layer 0's fused matrices at batch 1, with one
+    BLAS thread, until about max_seconds of work; report packed-weight GB/s."""
+    import numpy as np
+    import torch
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+
+    import contextlib
+
+    x = stack.x  # same activation tensors the GPU used
+    done_bytes, t_total, names = 0, 0.0, []
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        for j, (codes, scales, n, k) in enumerate(stack.w[0]):
+            c = codes.cpu().numpy().view(np.uint32)
+            s = scales.cpu().view(torch.int16).numpy().view(np.uint16)
+            xb = x[j][:1].cpu().view(torch.int16).numpy().view(np.uint16)
+            xr = oracle.numerics.f64_to_bf16_bits(oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(xb)))
+            t0 = time.perf_counter()
+            oracle.matvec.gemv(xr, c, s, k)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            done_bytes += packed_bytes(n, k)
+            names.append(FUSED[j][0])
+            log(f"  oracle GEMV {FUSED[j][0]} {n}x{k}: {dt:.2f} s")
+            if t_total > max_seconds:
+                break
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle GEMV (dequantise + matmul), batch 1, layer 0 matrices {'/'.join(names)} "
+                      f"({done_bytes / 1e6:.1f} MB packed), one thread, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra phases")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="fewer iterations in the extra phases")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
+              "would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ternary_weights_hadamard_amd import tb
+
+    tb.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(29)
+
+    log(f"building {args.layers}-layer stack (batch {args.batch}) on {torch.cuda.get_device_name(0)}")
+    stack = DecodeStack(args.layers, args.batch, gen, dev)
+    step_bytes = stack.packed_bytes()
+    log(f"packed weights per step: {step_bytes / 1e9:.3f} GB")
+
+    torch.cuda.synchronize()
+    ms_total, wall_ms, graph = time_graph(stack.step, args.steps, args.warmup)
+    ms_step = ms_total / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"decode step: {ms_step:.4f} ms ({value:.1f} GB/s packed); wall {wall_ms / args.steps:.4f} ms/step")
+    del graph
+
+    # dominant kernel: the GEMV, per-launch durations from events on its stream
+    gb, gms, nl = stack.gemv_event_times(passes=1)
+    achieved = gb / (gms * 1e-3) / 1e9
+    log(f"GEMV: {nl} launches, avg {gms / nl * 1e3:.2f} us, {achieved:.1f} GB/s algorithmic")
+
+    extra = {"step_wall_ms": round(wall_ms / args.steps, 4),
+             "gemv_avg_launch_us": round(gms / nl * 1e3, 3), "gemv_launches_per_step": nl}
+    # batch 8 decode
+    if not args.no_extra:
+        stack.make_acts(8, gen, dev)
+        ms8, _, g8 = time_graph(stack.step, max(3, args.steps // 2), 2)
+        del g8
+        ms8 /= max(3, args.steps // 2)
+        gb8, gms8, nl8 = stack.gemv_event_times(passes=1)
+        extra["decode_batch8"] = {"ms_per_step": round(ms8, 4), "gbs_packed": round(step_bytes / (ms8 * 1e-3) / 1e9, 1),
+                                  "gemv_gbs_algorithmic": round(gb8 / (gms8 * 1e-3) / 1e9, 1),
+                                  "gemv_frac_of_hbm_peak": round(gb8 / (gms8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"decode batch 8: {ms8:.4f} ms/step, GEMV {extra['decode_batch8']['gemv_gbs_algorithmic']} GB/s")
+        stack.make_acts(args.batch, gen, dev)
+        extra.update(extra_phases(gen, dev, args.quick))
+
+    result = {
+        "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode GEMV, {args.layers}-layer 27B-shaped stack (d_model 5120, d_ff 17408; fused QKV, O, "
+                               f"gate/up, down), batch {args.batch}, FWHT128 in and out, HIP graph",
+                   "layers": args.layers, "batch": args.batch, "packed_bytes_per_step": step_bytes,
+                   "code_distribution": "P(-1,0,+1) = (0.35, 0.30, 0.35)", "scales": "U(0.005, 0.05) fp16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "gemv_ternary_kernel", "bytes_per_launch": "N*K/4 + N*K/64 + 2*B*K + 4*B*N"},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(stack)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -99,3 +99,42 @@ def small_int_bf16(shape, seed, lim=8):
     """bf16 bit patterns of integers in [-lim, lim] (exact in bf16)."""
     rng = np.random.default_rng(seed)
     return f32_to_bf16_bits(rng.integers(-lim, lim + 1, size=shape).astype(np.float32))
+
+
+# ---------------------------------------------------------------- device-side
+# Generators for benchmark-sized inputs, drawn on the GPU with torch (same
+# distributions as above; not bit-identical to the numpy streams).
+
+def torch_code_words(n, k, gen, device, p=(0.35, 0.30, 0.35)):
+    """[n, k/16] int32 code words, 2-bit fields i.i.d. with P(-1, 0, +1) = p."""
+    import torch
+
+    u = torch.rand((n, k // 16, 16), generator=gen, device=device)
+    f = torch.where(u < p[0], FIELD_NEG, torch.where(u < p[0] + p[1], FIELD_ZERO, FIELD_POS)).to(torch.int64)
+    del u
+    shifts = 2 * torch.arange(16, device=device, dtype=torch.int64)
+    w = (f << shifts).sum(dim=-1)
+    return w.to(torch.int32)
+
+
+def torch_scales_f16(n, k, gen, device, lo=0.005, hi=0.05):
+    import torch
+
+    return (lo + (hi - lo) * torch.rand((n, k // 128), generator=gen, device=device)).to(torch.float16)
+
+
+def torch_gaussian_bf16(shape, gen, device, scale=1.0):
+    import torch
+
+    return (torch.randn(shape, generator=gen, device=device) * scale).to(torch.bfloat16)
+
+
+def torch_24(n, k, gen, device):
+    """2:4 planes (meta [n, k/32], signs [n, k/64]) as int32, uniform index pairs and signs."""
+    import torch
+
+    nib = torch.tensor(NIBBLES_24, dtype=torch.int64, device=device)
+    sel = torch.randint(0, 6, (n, k // 32, 8), generator=gen, device=device)
+    meta = (nib[sel] << (4 * torch.arange(8, device=device, dtype=torch.int64))).sum(-1).to(torch.int32)
+    signs = torch.randint(-2 ** 31, 2 ** 31, (n, k // 64), generator=gen, device=device, dtype=torch.int64)
+    return meta, signs.to(torch.int32)

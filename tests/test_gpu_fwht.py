@@ -26,7 +26,7 @@ def test_fwht_matches_oracle(rows, k, din, dout):
     y = tb.tb_fwht128(xin, out_dtype=torch.bfloat16 if dout == "bf16" else torch.float32)
     torch.cuda.synchronize()
     ref = oracle.hadamard.fwht_dense(xv)
-    assert_close(host_f64(y), ref, f"fwht {din}->{dout}")
+    assert_close(host_f64(y), ref, f"fwht {din}->{dout}", out_bf16=dout == "bf16")
     if dout == "f32":
         # fp32 arithmetic: far inside the bar
         assert np.max(np.abs(host_f64(y) - ref)) <= 1e-5 * np.max(np.abs(ref))
@@ -70,7 +70,7 @@ def test_fwht_bf16_in_place_and_canaries():
     torch.cuda.synchronize()
     assert torch.all(buf[:32] == -7.0) and torch.all(buf[32 + 9 * k:] == -7.0)
     ref = oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(xb))
-    assert_close(host_f64(view), ref, "fwht bf16 in place")
+    assert_close(host_f64(view), ref, "fwht bf16 in place", out_bf16=True)
 
 
 def test_fwht_empty_batch_is_noop():

@@ -22,7 +22,7 @@ def test_gemm_small_matches_oracle(m, n, k, out):
                            out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
     torch.cuda.synchronize()
     ref = oracle.matvec.gemm(x, codes, scales, k)
-    assert_close(host_f64(y), ref, f"gemm {m}x{n}x{k} {out}")
+    assert_close(host_f64(y), ref, f"gemm {m}x{n}x{k} {out}", out_bf16=out == "bf16")
 
 
 @pytest.mark.parametrize("k,n", [(5120, 17408), (17408, 5120)])
@@ -37,7 +37,8 @@ def test_gemm_full_size_sampled(k, n):
         rs = np.sort(np.random.default_rng(5).choice(m, 64, replace=False))
         cs = np.sort(np.random.default_rng(6).choice(n, 96, replace=False))
         ref = oracle.matvec.gemm(x[rs], codes[cs], scales[cs], k)
-        assert_close(y[np.ix_(rs, cs)], ref, f"gemm {m}x{n}x{k} {out} (64x96 sampled)")
+        assert_close(y[np.ix_(rs, cs)], ref, f"gemm {m}x{n}x{k} {out} (64x96 sampled)",
+                     out_bf16=out == torch.bfloat16)
         del y
 
 
@@ -65,6 +66,6 @@ def test_gemm_canaries_and_empty():
     tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(scales), y=y)
     torch.cuda.synchronize()
     assert torch.all(buf[:128] == -9.0) and torch.all(buf[128 + m * n:] == -9.0)
-    assert_close(host_f64(y), oracle.matvec.gemm(x, codes, scales, k), "gemm canary run")
+    assert_close(host_f64(y), oracle.matvec.gemm(x, codes, scales, k), "gemm canary run", out_bf16=True)
     e = tb.tb_ternary_gemm(torch.empty((0, k), dtype=torch.bfloat16, device=DEV), u32_dev(codes), f16_dev(scales))
     assert e.shape == (0, n)
