@@ -55,7 +55,7 @@ def gemv_bruteforce(x_bf16_bits, codes, scales, k):
     x = _x(x_bf16_bits)
     codes = np.asarray(codes, dtype=np.uint32)
     s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
-    m_rows, n_rows = x.shape[0], codes.shape[0]
+    m_rows, n_rows = x.shape[0], codes.shape[0] * 16
     y = np.zeros((m_rows, n_rows))
     for m in range(m_rows):
         for n in range(n_rows):
@@ -63,9 +63,11 @@ def gemv_bruteforce(x_bf16_bits, codes, scales, k):
             for g in range(k // GROUP):
                 part = 0.0
                 for kk in range(g * GROUP, (g + 1) * GROUP):
-                    word = int(codes[n, kk // 16])
-                    r = kk % 16
-                    field = (word >> (2 * (r // 2) + 16 * (r % 2))) & 3
+                    c = kk % GROUP
+                    lane = 16 * (c // 32) + n % 16
+                    word = int(codes[n // 16, g, 2 * lane + (c % 32) // 16])
+                    r = c % 16
+                    field = (word >> (4 * (r % 8) + (2 if r < 8 else 0))) & 3
                     if field == 1:
                         part += x[m, kk]
                     elif field == 3:

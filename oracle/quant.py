@@ -16,14 +16,19 @@ Definitions followed (readings of the pages are listed in the design doc):
   remains).  Kept elements are nonzero, so each carries only a sign; the group
   scale is the mean |w'| of the 64 kept elements of the group.
 * Storage: 2 bits per weight (mhpq.cn §3.1), as a sign bit and a magnitude bit
-  per weight (the sign/magnitude split of dpshk.com §2.2), pair-interleaved
-  inside each 32-bit word.
+  per weight (the sign/magnitude split of dpshk.com §2.2).  The arrangement of
+  the fields inside the words is this implementation's choice: 16-row x
+  128-column tiles whose word order matches the operand layout of the matrix
+  instruction that consumes them.
 
-Dense format (K a multiple of 128; rows contiguous):
-  codes[n][k // 16] uint32.  With r = k % 16 the 2-bit field of (n, k) starts at
-  bit 2 * (r // 2) + 16 * (r % 2): even k fill the low half-word, odd k the high
-  half-word, each in increasing k.  Field value: 0b00 -> 0, 0b01 -> +1,
-  0b11 -> -1 (bit 0 = nonzero, bit 1 = negative); 0b10 is invalid.
+Dense format (N a multiple of 16, K a multiple of 128):
+  codes[N / 16][K / 128][128] uint32.  Tile (nb, g) covers rows 16 nb .. 16 nb + 15
+  and columns 128 g .. 128 g + 127.  With l = 16 q + i (i = row in the tile,
+  q = 0..3) and h = 0, 1, word 2 l + h of the tile holds row 16 nb + i, columns
+  128 g + 32 q + 16 h + r for r = 0..15; the 2-bit field of r starts at bit
+  4 (r mod 8) + 2 - 2 floor(r / 8), so fields r < 8 sit in bits 2-3 of nibble r
+  and fields r >= 8 in bits 0-1 of nibble r - 8.  Field value: 0b00 -> 0,
+  0b01 -> +1, 0b11 -> -1 (bit 0 = nonzero, bit 1 = negative); 0b10 is invalid.
   scales[n][k // 128] fp16 bits.
 2:4 format:
   meta[n][q // 8] uint32 for quad q = k // 4: the nibble at bits 4 * (q % 8)
@@ -71,45 +76,54 @@ def near_threshold(wr, s, rel=NEAR_REL):
     return np.abs(np.abs(wr) - thr) <= rel * thr
 
 
-def _field_pos(k):
-    r = np.asarray(k) % 16
-    return 2 * (r // 2) + 16 * (r % 2)
+def dense_location(n, k):
+    """Tile index (nb, g), word index in the tile and bit position of the 2-bit
+    field of element (n, k) of the dense format (arrays broadcast)."""
+    n = np.asarray(n)
+    k = np.asarray(k)
+    i, nb = n % 16, n // 16
+    g, kk = k // GROUP, k % GROUP
+    q, h, r = kk // 32, (kk % 32) // 16, kk % 16
+    word = 2 * (16 * q + i) + h
+    bit = 4 * (r % 8) + 2 - 2 * (r // 8)
+    return nb, g, word, bit
 
 
 def pack_dense(t):
-    """Pack ternary t[N, K] into codes[N, K/16] (uint32), format above."""
+    """Pack ternary t[N, K] into codes[N/16, K/128, 128] (uint32), format above."""
     t = np.asarray(t)
     n, k = t.shape
-    if k % 16:
-        raise ValueError("K must be a multiple of 16")
+    if n % 16 or k % GROUP:
+        raise ValueError("N must be a multiple of 16 and K of 128")
     field = np.zeros(t.shape, dtype=np.uint64)
     field[t == 1] = FIELD_OF_T[1]
     field[t == -1] = FIELD_OF_T[-1]
-    words = np.zeros((n, k // 16), dtype=np.uint64)
-    for r in range(16):
-        words |= field[:, r::16] << np.uint64(_field_pos(r))
+    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    nb, g, word, bit = dense_location(nn, kk)
+    words = np.zeros((n // 16, k // GROUP, 128), dtype=np.uint64)
+    # every (tile, word, bit) is hit by exactly one element, so add == or
+    np.add.at(words, (nb, g, word), field << bit.astype(np.uint64))
     return words.astype(np.uint32)
 
 
 def unpack_dense(codes, k):
     """Inverse of pack_dense; raises on the invalid field 0b10."""
     codes = np.asarray(codes, dtype=np.uint32).astype(np.uint64)
-    n = codes.shape[0]
-    if codes.shape[1] * 16 != k:
+    if codes.ndim != 3 or codes.shape[1] * GROUP != k or codes.shape[2] != 128:
         raise ValueError("codes shape does not match K")
-    t = np.zeros((n, k), dtype=np.int8)
-    for r in range(16):
-        f = (codes >> np.uint64(_field_pos(r))) & np.uint64(3)
-        if np.any(f == 0b10):
-            raise ValueError("invalid 2-bit code 0b10")
-        t[:, r::16] = np.where(f == 0b01, 1, np.where(f == 0b11, -1, 0))
-    return t
+    n = codes.shape[0] * 16
+    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    nb, g, word, bit = dense_location(nn, kk)
+    f = (codes[nb, g, word] >> bit.astype(np.uint64)) & np.uint64(3)
+    if np.any(f == 0b10):
+        raise ValueError("invalid 2-bit code 0b10")
+    return np.where(f == 0b01, 1, np.where(f == 0b11, -1, 0)).astype(np.int8)
 
 
 def quantize_dense(w):
     """Rotate 128x128 blocks, take absmean group scales, ternarise, pack.
 
-    Returns a dict with codes (uint32 [N, K/16]), scales (fp16 bits uint16
+    Returns a dict with codes (uint32 [N/16, K/128, 128]), scales (fp16 bits uint16
     [N, K/128]) and the float64 intermediates wr (W'), s (unrounded scales) and
     t (int8 ternary values)."""
     w = _check_w(w)

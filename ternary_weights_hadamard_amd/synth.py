@@ -70,13 +70,15 @@ def stack_weights(n, k, seed, sigma=0.02, outlier_col_frac=0.01, nu=3.0):
 
 
 def random_code_words(n, k, seed, p=(0.35, 0.30, 0.35)):
-    """Dense code words [n, k/16] uint32 whose 16 2-bit fields are drawn i.i.d.
-    with P(-1, 0, +1) = p.  Fields are independent, so no layout is assumed."""
+    """Dense code words [n/16, k/128, 128] uint32 (the tiled shape of the dense
+    format) whose 2-bit fields are drawn i.i.d. with P(-1, 0, +1) = p.  Every
+    field is independent, so no assignment of fields to elements is assumed."""
     rng = np.random.default_rng(seed)
     fields = rng.choice(np.array([FIELD_NEG, FIELD_ZERO, FIELD_POS], dtype=np.uint32),
-                        size=(n, k // 16, 16), p=np.asarray(p) / np.sum(p))
+                        size=(n * k // 16, 16), p=np.asarray(p) / np.sum(p))
     shifts = (2 * np.arange(16, dtype=np.uint32))
-    return np.bitwise_or.reduce(fields << shifts, axis=2).astype(np.uint32)
+    words = np.bitwise_or.reduce(fields << shifts, axis=1).astype(np.uint32)
+    return words.reshape(n // 16, k // 128, 128)
 
 
 def random_scales_f16(n, k, seed, lo=0.005, hi=0.05):
@@ -106,10 +108,10 @@ def small_int_bf16(shape, seed, lim=8):
 # distributions as above; not bit-identical to the numpy streams).
 
 def torch_code_words(n, k, gen, device, p=(0.35, 0.30, 0.35)):
-    """[n, k/16] int32 code words, 2-bit fields i.i.d. with P(-1, 0, +1) = p."""
+    """[n/16, k/128, 128] int32 code words, 2-bit fields i.i.d. with P(-1, 0, +1) = p."""
     import torch
 
-    u = torch.rand((n, k // 16, 16), generator=gen, device=device)
+    u = torch.rand((n // 16, k // 128, 128, 16), generator=gen, device=device)
     f = torch.where(u < p[0], FIELD_NEG, torch.where(u < p[0] + p[1], FIELD_ZERO, FIELD_POS)).to(torch.int64)
     del u
     shifts = 2 * torch.arange(16, device=device, dtype=torch.int64)

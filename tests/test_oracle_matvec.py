@@ -12,16 +12,22 @@ from ternary_weights_hadamard_amd import synth
 
 
 def _t_from_codes(codes, k):
-    """Independent field decode for tests: walk the words bit by bit."""
-    n = codes.shape[0]
+    """Independent field decode for tests: walk every tile word nibble by nibble.
+    Nibble p of word 2l + h (l = 16q + i) carries column 32q + 16h + p in its
+    bits 2-3 and column 32q + 16h + 8 + p in its bits 0-1."""
+    n = codes.shape[0] * 16
     t = np.zeros((n, k), dtype=np.int64)
-    for row in range(n):
-        for kk in range(k):
-            w = int(codes[row, kk // 16])
-            r = kk % 16
-            pos = r if r % 2 == 0 else 15 + r
-            f = (w >> pos) & 3
-            t[row, kk] = {0: 0, 1: 1, 3: -1}[f]
+    for nb in range(codes.shape[0]):
+        for g in range(codes.shape[1]):
+            for word in range(128):
+                w = int(codes[nb, g, word])
+                lane, h = divmod(word, 2)
+                q_, i = divmod(lane, 16)
+                for p in range(8):
+                    nib = (w >> (4 * p)) & 0xF
+                    base = 128 * g + 32 * q_ + 16 * h
+                    t[16 * nb + i, base + p] = {0: 0, 1: 1, 3: -1}[nib >> 2]
+                    t[16 * nb + i, base + 8 + p] = {0: 0, 1: 1, 3: -1}[nib & 3]
     return t
 
 

@@ -122,33 +122,64 @@ def test_gaussian_statistics_closed_form():
     assert q.near_threshold(r["wr"], r["s"]).sum() < 60
 
 
+def _golden_lines(golden_dir):
+    return [l.split() for l in open(os.path.join(golden_dir, "packing_dense.txt")) if l.strip() and not l.startswith("#")]
+
+
 def test_dense_packing_hand_worked(golden_dir):
-    lines = [l.split() for l in open(os.path.join(golden_dir, "packing_dense.txt")) if l.strip() and not l.startswith("#")]
-    t = np.array([[int(v) for v in lines[0][1:]]], dtype=np.int8)
+    lines = _golden_lines(golden_dir)
+    t = np.zeros((16, 128), dtype=np.int8)
+    t[0, :16] = [int(v) for v in lines[0][1:]]
     word = int(lines[1][1], 16)
-    assert q.pack_dense(t)[0, 0] == word
-    assert np.array_equal(q.unpack_dense(np.array([[word]], dtype=np.uint32), 16), t)
+    codes = q.pack_dense(t)
+    assert codes.shape == (1, 1, 128)
+    assert codes[0, 0, 0] == word and np.all(codes[0, 0, 1:] == 0)
+    assert np.array_equal(q.unpack_dense(codes, 128), t)
+
+
+def test_dense_packing_tile_position(golden_dir):
+    f = _golden_lines(golden_dir)[2]
+    n, k, val = int(f[1]), int(f[2]), int(f[3])
+    nb, g, word, value = int(f[5]), int(f[6]), int(f[8]), int(f[10], 16)
+    t = np.zeros((32, 256), dtype=np.int8)
+    t[n, k] = val
+    codes = q.pack_dense(t)
+    expect = np.zeros_like(codes)
+    expect[nb, g, word] = value
+    assert np.array_equal(codes, expect)
 
 
 @pytest.mark.parametrize("r", range(16))
 @pytest.mark.parametrize("val,field", [(1, 0b01), (-1, 0b11)])
 def test_dense_field_positions(r, val, field):
-    t = np.zeros((1, 16), dtype=np.int8)
+    # r < 8: bits 2-3 of nibble r; r >= 8: bits 0-1 of nibble r - 8
+    t = np.zeros((16, 128), dtype=np.int8)
     t[0, r] = val
-    pos = r if r % 2 == 0 else 16 + (r - 1)
-    assert int(q.pack_dense(t)[0, 0]) == field << pos
+    pos = 4 * r + 2 if r < 8 else 4 * (r - 8)
+    assert int(q.pack_dense(t)[0, 0, 0]) == field << pos
+
+
+def test_dense_every_slot_used_once():
+    # the map (n, k) -> (tile, word, bit) is a bijection onto all 2-bit slots
+    n, k = 32, 256
+    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    nb, g, word, bit = q.dense_location(nn, kk)
+    slot = ((nb * (k // 128) + g) * 128 + word) * 16 + bit // 2
+    assert np.all(bit % 2 == 0)
+    assert np.array_equal(np.sort(slot.ravel()), np.arange(n * k))
 
 
 def test_pack_unpack_round_trip_and_invalid_field():
     rng = np.random.default_rng(5)
-    t = rng.integers(-1, 2, size=(7, 256)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(48, 256)).astype(np.int8)
     codes = q.pack_dense(t)
-    assert codes.shape == (7, 16) and codes.dtype == np.uint32
+    assert codes.shape == (3, 2, 128) and codes.dtype == np.uint32
     assert np.array_equal(q.unpack_dense(codes, 256), t)
-    assert np.all(q.pack_dense(np.zeros((2, 32), dtype=np.int8)) == 0)
-    bad = np.array([[0b10]], dtype=np.uint32)
+    assert np.all(q.pack_dense(np.zeros((16, 128), dtype=np.int8)) == 0)
+    bad = np.zeros((1, 1, 128), dtype=np.uint32)
+    bad[0, 0, 7] = 0b10 << 8
     with pytest.raises(ValueError):
-        q.unpack_dense(bad, 16)
+        q.unpack_dense(bad, 128)
 
 
 def test_quantiser_rejects_bad_input():
