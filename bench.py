@@ -4,9 +4,9 @@
 Timed step (the value): one decode token through a 64-layer 27B-shaped stack
 (d_model 5120, d_ff 17408) at batch 1: for every layer and each fused
 projection (QKV 15360x5120, O 5120x5120, gate/up 34816x5120, down
-5120x17408) the activations are rotated (tb_fwht128), multiplied by the packed
-ternary weights (tb_ternary_gemv) and the output is rotated back
-(tb_fwht128 along N).  All 6.33 GB of packed weights are resident in HBM and
+5120x17408) the activations are rotated and encoded as the GEMV operand
+(tb_fwht128 with the act8 output), multiplied by the packed ternary weights
+(tb_ternary_gemv) and the output is rotated back (tb_fwht128 along N).  All 6.33 GB of packed weights are resident in HBM and
 each is read once per step, far beyond the 256 MB last-level cache.  The step
 is captured once in a HIP graph and replayed.
 value = packed weight bytes (codes + scales) streamed per step / step time.
@@ -67,9 +67,11 @@ class DecodeStack:
 
         from ternary_weights_hadamard_amd import synth
 
+        from ternary_weights_hadamard_amd import tb
+
         self.batch = batch
         self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
-        self.xr = [torch.empty((batch, k), dtype=torch.bfloat16, device=dev) for _, n, k in FUSED]
+        self.act = [torch.empty(tb.tb_act8_bytes(batch, k), dtype=torch.uint8, device=dev) for _, n, k in FUSED]
         self.yr = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
         self.y = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
 
@@ -78,8 +80,8 @@ class DecodeStack:
 
         for layer in self.w:
             for j, (codes, scales, n, k) in enumerate(layer):
-                tb.tb_fwht128(self.x[j], y=self.xr[j])
-                tb.tb_ternary_gemv(self.xr[j], codes, scales, y=self.yr[j])
+                tb.tb_fwht128(self.x[j], y=self.act[j])
+                tb.tb_ternary_gemv(self.act[j], codes, scales, self.batch, y=self.yr[j])
                 tb.tb_fwht128(self.yr[j], y=self.y[j])
 
     def packed_bytes(self):
@@ -99,7 +101,7 @@ class DecodeStack:
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record()
-                    tb.tb_ternary_gemv(self.xr[j], codes, scales, y=self.yr[j])
+                    tb.tb_ternary_gemv(self.act[j], codes, scales, self.batch, y=self.yr[j])
                     b.record()
                     pairs.append((a, b))
                     nbytes += gemv_bytes(n, k, self.batch)
@@ -210,7 +212,7 @@ def extra_phases(gen, dev, quick):
     for _, n, k in mats:
         w = torch.randn((n, k), generator=gen, device=dev) * 0.02
         ws.append(w)
-        outs.append((torch.empty((n, k // 16), dtype=torch.int32, device=dev),
+        outs.append((torch.empty((n // 16, k // 128, 128), dtype=torch.int32, device=dev),
                      torch.empty((n, k // 128), dtype=torch.float16, device=dev)))
 
     def runq():

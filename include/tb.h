@@ -30,11 +30,16 @@
  *     streams are independent.
  *
  * Storage formats (bit exact, shared by the quantiser and the products):
- *   Dense codes  uint32 codes[N][K/16].  For r = k % 16 the 2-bit field of
- *                (n, k) starts at bit 2*(r/2) + 16*(r%2): even k fill the low
- *                half-word and odd k the high half-word of word k/16.  Field:
- *                0b00 = 0, 0b01 = +1, 0b11 = -1 (bit 0 nonzero, bit 1
- *                negative); 0b10 never appears and reads as 0.
+ *   Dense codes  uint32 codes[N/16][K/128][128], one 128-word tile per 16 rows
+ *                x 128 columns.  In tile (nb, g), word 2l + h (l = 16q + i,
+ *                q = 0..3, h = 0..1) holds row 16nb + i, columns
+ *                128g + 32q + 16h + r for r = 0..15, the 2-bit field of r at
+ *                bit 4*(r%8) + 2 - 2*(r/8).  Field: 0b00 = 0, 0b01 = +1,
+ *                0b11 = -1 (bit 0 nonzero, bit 1 negative); 0b10 never
+ *                appears.  (Two bits per weight: mhpq.cn/news/1159370 §3.1;
+ *                the arrangement is this library's, chosen so that two AND
+ *                masks turn a word into the fp4 operand of the gfx950
+ *                block-scaled matrix instruction.)
  *   Scales       uint16 fp16 bits scales[N][K/128], the group's absmean,
  *                rounded to nearest even.
  *   2:4 meta     uint32 meta[N][K/32]: for quad q = k/4 the nibble at bits
@@ -65,12 +70,29 @@ typedef enum {
   TB_ERR_ALIAS = 8        /* input and output overlap where that is not allowed */
 } tb_status;
 
-typedef enum { TB_F32 = 0, TB_BF16 = 1 } tb_dtype;
+typedef enum { TB_F32 = 0, TB_BF16 = 1, TB_ACT8 = 2 } tb_dtype;
 typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1 } tb_format;
 
 /* Bits OR-ed into the optional device error flag of tb_quantize_pack. */
 #define TB_EFLAG_NONFINITE 1u /* a non-finite weight was seen; its block's codes are unspecified */
 #define TB_EFLAG_SCALE_OVF 2u /* a group scale rounded to fp16 infinity (absmean >= 65520)      */
+
+/*
+ * TB_ACT8 is the activation operand of tb_ternary_gemv, for B rows of K
+ * activations, in one buffer of tb_act8_bytes(B, K) = 4*B*K + B*K/8 bytes.
+ * Every bf16 activation is stored exactly as the sum of four e4m3 values on
+ * four sub-rows (two magnitude levels x high and low significand halves) with
+ * one E8M0 scale per 32 K-elements and sub-row:
+ *   values  uint8 [B][K/128][4 sub-rows][4 q][32]: bytes 0-15 of q are
+ *           K 128g + 16q + (0..15), bytes 16-31 are K 128g + 64 + 16q + (0..15);
+ *   scales  uint8 at byte offset 4*B*K: [B][K/128][4 sub-rows][4 blocks],
+ *           block q = K 128g + 32q .. +31; 0xFF marks a block holding a
+ *           non-finite activation (the product rows then come out NaN).
+ * Sub-rows 0/1 take the elements within 10 binades of their block's largest,
+ * sub-rows 2/3 those within 10 binades of the largest of the rest.  Elements
+ * below both, and bf16 subnormals, are read as zero: each such element is
+ * below 2^-20 of its block's largest magnitude.
+ */
 
 /* Largest activation batch of the GEMV entry points. */
 #define TB_GEMV_MAX_BATCH 16
@@ -100,6 +122,9 @@ tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, siz
  * and, along N, to rotate an output back (the transform is its own inverse).
  *   x      [rows][K] in x_dtype (TB_BF16 or TB_F32)
  *   y      [rows][K] in y_dtype; bf16 output is rounded to nearest even.
+ *          TB_ACT8 writes the rounded bf16 result as the activation operand of
+ *          tb_ternary_gemv (tb_act8_bytes(rows, K) bytes), which fuses the
+ *          rotation of the activations with their encoding.
  *          y == x is allowed (in place) when the dtypes match; any other
  *          overlap returns TB_ERR_ALIAS.
  *   rows >= 0, K a positive multiple of 128.  Arithmetic is fp32.
@@ -132,20 +157,38 @@ tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32
  * Decode GEMV with dense ternary weights (mhpq.cn/news/1159370 §4.2: read the
  * weight bits, expand the signs, apply the scale, multiply):
  *   y[b][n] = sum_g fp16(scales[n][g]) * sum_{k in g} t[n][k] * x[b][k]
- *   x       bf16 bits [B][K], the already rotated activations
+ *   act     the already rotated activations x [B][K] in the TB_ACT8 operand
+ *           format (tb_act8_prep, or tb_fwht128 with y_dtype TB_ACT8)
  *   B       0 <= B <= TB_GEMV_MAX_BATCH (else TB_ERR_SHAPE)
- *   codes, scales  dense format, [N][K/16] and [N][K/128]
+ *   codes, scales  dense format, [N/16][K/128][128] and [N][K/128]
  *   y       fp32 [B][N]; must not overlap the inputs (TB_ERR_ALIAS)
- * Products are exact, accumulation is fp32.
+ * The products are exact; each 32-element block's products are summed
+ * exactly inside the matrix instruction, blocks, sub-rows and groups are
+ * accumulated in fp32.
  */
-tb_status tb_ternary_gemv(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales,
+tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, float* y, void* stream);
+
+/*
+ * Bytes of the TB_ACT8 activation operand for B rows of K activations:
+ * 4*B*K + B*K/8.  Host-only; 0 when K is not a positive multiple of 128 or
+ * B < 0.
+ */
+size_t tb_act8_bytes(int64_t B, int64_t K);
+
+/*
+ * Encode bf16 activations x[B][K] (already rotated) as the TB_ACT8 operand of
+ * tb_ternary_gemv, without transforming them.  B >= 0 (0 is a no-op), K a
+ * positive multiple of 128; act must not overlap x.
+ */
+tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, void* stream);
 
 /*
  * Decode GEMV with 2:4 ternary weights (mhpq.cn/news/1159370 §1.2):
  *   y[b][n] = sum_g fp16(scales[n][g]) * sum_q (+-x[b][4q + idx0] +- x[b][4q + idx1])
+ *   x       bf16 bits [B][K], the already rotated activations
  *   meta [N][K/32], signs [N][K/64], scales [N][K/128] in the 2:4 format;
- *   other arguments as tb_ternary_gemv.
+ *   B and y as tb_ternary_gemv.  Products are exact, accumulation is fp32.
  */
 tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                             const uint16_t* scales, int64_t N, int64_t K, float* y, void* stream);

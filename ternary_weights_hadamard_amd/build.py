@@ -3,13 +3,20 @@
 Usage: python -m ternary_weights_hadamard_amd.build  (or call build()).
 Every HIP source is compiled with packed-fp32 instructions disabled and the
 objects are linked into ternary_weights_hadamard_amd/libtb.so.
+
+Sources that use the block-scaled matrix instruction are also compiled to
+assembly and checked: its destination must not overlap its A or B source
+registers.  The instruction reads its sources over several passes and the
+compiler does not always keep the destination apart (an overlapping
+destination gives wrong sums), so such a build is rejected.
 """
 
 import concurrent.futures
 import os
-import shutil
+import re
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -54,12 +61,58 @@ def _compile(src, objdir):
     return obj
 
 
+_SCALED_MFMA = "v_mfma_scale_f32_16x16x128_f8f6f4"
+_REG = re.compile(r"^([va])(?:\[(\d+):(\d+)\]|(\d+))$")
+
+
+def _reg_range(tok):
+    m = _REG.match(tok.strip())
+    if not m:
+        return None
+    lo = int(m.group(2) if m.group(2) is not None else m.group(4))
+    hi = int(m.group(3) if m.group(3) is not None else m.group(4))
+    return m.group(1), lo, hi
+
+
+def check_scaled_mfma_operands(asm_text, where):
+    """Raise if a block-scaled MFMA writes registers it also reads as A or B."""
+    n = 0
+    for line in asm_text.splitlines():
+        line = line.split(";")[0].strip()
+        if not line.startswith(_SCALED_MFMA):
+            continue
+        n += 1
+        ops = [o.strip() for o in line[len(_SCALED_MFMA):].split(",")]
+        dst, a, b = (_reg_range(o) for o in ops[:3])
+        if dst is None:
+            raise RuntimeError(f"{where}: cannot parse {line!r}")
+        for src in (a, b):
+            if src and src[0] == dst[0] and src[1] <= dst[2] and dst[1] <= src[2]:
+                raise RuntimeError(f"{where}: scaled MFMA destination overlaps a source: {line!r}")
+    return n
+
+
+def _check_asm(src):
+    with open(src) as f:
+        if "mfma_scale" not in f.read():
+            return 0
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [HIPCC, *CFLAGS, "--cuda-device-only", "-S", src, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n{_filter(r.stderr)}")
+        with open(out) as f:
+            return check_scaled_mfma_operands(f.read(), os.path.basename(src))
+
+
 def build(verbose=True):
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     srcs = _sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, objdir), srcs))
+        checked = sum(ex.map(_check_asm, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,7 +120,7 @@ def build(verbose=True):
         raise RuntimeError(f"link failed:\n{_filter(r.stderr)}")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources ({checked} scaled MFMAs checked)")
     return LIB
 
 

@@ -8,6 +8,11 @@
 // element bits 3-6 pair lanes (lane ^ 1, 2, 4, 8) through DPP and ds_swizzle,
 // so nothing goes through LDS.  The kernel is HBM bound: 4 bytes per element
 // for bf16 in and out.
+//
+// With the act8 output the rounded bf16 result is re-encoded in the same pass
+// as the dense GEMV's activation operand (act8.h); the same kernel without the
+// transform re-encodes bf16 activations as they are.
+#include "act8.h"
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -27,7 +32,9 @@ __device__ __forceinline__ void lane_stage(float (&v)[8], int sub) {
   }
 }
 
-template <bool IN_BF16, bool OUT_BF16>
+enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutAct8 = 2 };
+
+template <bool IN_BF16, int OUT, bool XFORM>
 __global__ void __launch_bounds__(256) fwht128_kernel(const void* __restrict__ x, void* __restrict__ y,
                                                        int64_t nblocks) {
   const int sub = threadIdx.x & 15;
@@ -58,36 +65,50 @@ __global__ void __launch_bounds__(256) fwht128_kernel(const void* __restrict__ x
         v[4 + i] = c[i];
       }
     }
-    // element bits 0..2: inside the lane
+    float sc = 1.0f;
+    if constexpr (XFORM) {
+      // element bits 0..2: inside the lane
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+      for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if ((e & h) == 0) {
-          float a = v[e], c = v[e + h];
-          v[e] = a + c;
-          v[e + h] = a - c;
+        for (int e = 0; e < 8; ++e) {
+          if ((e & h) == 0) {
+            float a = v[e], c = v[e + h];
+            v[e] = a + c;
+            v[e + h] = a - c;
+          }
         }
       }
+      // element bits 3..6: lane bits 0..3
+      lane_stage<1>(v, sub);
+      lane_stage<2>(v, sub);
+      lane_stage<4>(v, sub);
+      lane_stage<8>(v, sub);
+      sc = kInvSqrt128;
     }
-    // element bits 3..6: lane bits 0..3
-    lane_stage<1>(v, sub);
-    lane_stage<2>(v, sub);
-    lane_stage<4>(v, sub);
-    lane_stage<8>(v, sub);
+    if constexpr (OUT == kOutAct8) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e] * sc);
+      // act8 buffer: values of block b at b * 512, scales at 4 * elements + b * 16
+      uint8_t* act = static_cast<uint8_t*>(y);
+      const int64_t bb = live ? b : 0;
+      act8_encode_store(h, sub, act + bb * 512, act + nblocks * 512 + bb * 16, live);
+      continue;
+    }
     if (!live) continue;
-    if constexpr (OUT_BF16) {
+    if constexpr (OUT == kOutBF16) {
       u32x4 w;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        w[i] = f32_to_bf16_rne(v[2 * i] * kInvSqrt128) | (f32_to_bf16_rne(v[2 * i + 1] * kInvSqrt128) << 16);
+        w[i] = f32_to_bf16_rne(v[2 * i] * sc) | (f32_to_bf16_rne(v[2 * i + 1] * sc) << 16);
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
     } else {
       f32x4 a, c;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = v[i] * kInvSqrt128;
-        c[i] = v[4 + i] * kInvSqrt128;
+        a[i] = v[i] * sc;
+        c[i] = v[4 + i] * sc;
       }
       f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + base);
       p[0] = a;
@@ -96,25 +117,36 @@ __global__ void __launch_bounds__(256) fwht128_kernel(const void* __restrict__ x
   }
 }
 
-}  // namespace
-
-hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
-                          hipStream_t stream) {
-  const int64_t nblocks = rows * (K / kBlock);
+template <bool XFORM>
+hipError_t launch_blocks(const void* x, int x_dtype, void* y, int y_dtype, int64_t nblocks, hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;
   int64_t groups = (nblocks + 15) / 16;
   const int64_t cap = 1 << 20;
   const unsigned grid = (unsigned)(groups < cap ? groups : cap);
-  const bool ib = x_dtype == TB_BF16, ob = y_dtype == TB_BF16;
-  if (ib && ob)
-    hipLaunchKernelGGL((fwht128_kernel<true, true>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
-  else if (ib && !ob)
-    hipLaunchKernelGGL((fwht128_kernel<true, false>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
-  else if (!ib && ob)
-    hipLaunchKernelGGL((fwht128_kernel<false, true>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
-  else
-    hipLaunchKernelGGL((fwht128_kernel<false, false>), dim3(grid), dim3(256), 0, stream, x, y, nblocks);
+  const dim3 g(grid), blk(256);
+  const bool ib = x_dtype == TB_BF16;
+  if (y_dtype == TB_ACT8) {
+    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutAct8, XFORM>), g, blk, 0, stream, x, y, nblocks);
+    else hipLaunchKernelGGL((fwht128_kernel<false, kOutAct8, XFORM>), g, blk, 0, stream, x, y, nblocks);
+  } else if (y_dtype == TB_BF16) {
+    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutBF16, XFORM>), g, blk, 0, stream, x, y, nblocks);
+    else hipLaunchKernelGGL((fwht128_kernel<false, kOutBF16, XFORM>), g, blk, 0, stream, x, y, nblocks);
+  } else {
+    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutF32, XFORM>), g, blk, 0, stream, x, y, nblocks);
+    else hipLaunchKernelGGL((fwht128_kernel<false, kOutF32, XFORM>), g, blk, 0, stream, x, y, nblocks);
+  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
+                          hipStream_t stream) {
+  return launch_blocks<true>(x, x_dtype, y, y_dtype, rows * (K / kBlock), stream);
+}
+
+hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream) {
+  return launch_blocks<false>(x, TB_BF16, act, TB_ACT8, rows * (K / kBlock), stream);
 }
 
 }  // namespace tb

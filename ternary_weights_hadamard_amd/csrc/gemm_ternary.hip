@@ -8,9 +8,13 @@
 // exponent), the activations enter as fp16 (bf16 -> fp16 is exact for
 // 2^-14 <= |x| < 65504), and the fp32 accumulator runs over all of K.  The
 // result is halved on the way out.
-// Decode: (word << (14 - 2f)) & 0xC000C000 gives the fp16 pair (2t, 2t') of
-// field f (bit 14 alone is the exponent of 2.0 in fp16 too), and one packed
-// fp16 multiply by (s, s) makes (2ts, 2t's).
+// Decode: a dense code word holds column c's field in nibble c % 8, bits 2-3
+// for c < 8 and bits 0-1 for c >= 8.  Shifting the word left by 4, 6 and 2
+// puts the fields of columns 2p, 8 + 2p and 9 + 2p at bits 6-7 of byte p (the
+// field of column 2p + 1 is there already); one v_perm_b32 moves two such
+// bytes to bytes 1 and 3 and the mask 0xC000C000 leaves the fp16 pair
+// (2t, 2t') - bit 14 alone is the exponent of 2.0 in fp16.  One packed fp16
+// multiply by (s, s) makes (2ts, 2t's).
 // Tiling (first version): 128 x 128 output tile per workgroup of 4 waves, each
 // wave 64 x 64 with v_mfma_f32_16x16x32_f16; K steps of 64 staged through LDS
 // (fp16, double buffered, rows padded to spread banks).  Each K step reads the
@@ -26,6 +30,17 @@ namespace {
 constexpr int BM = 128, BN = 128, KT = 64;
 constexpr int LDS_ROW = KT + 8;  // fp16 elements per LDS row (144 bytes)
 constexpr int TILE_ELEMS = BM * LDS_ROW;
+
+// fp16 pairs (2t, 2t') of the 16 columns of a dense code word, in column order.
+__device__ __forceinline__ void decode_word_f16(uint32_t w, uint32_t (&out)[8]) {
+  const uint32_t t4 = w << 4, t6 = w << 6, t2 = w << 2;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t sel = 0x0Cu | ((uint32_t)p << 8) | (0x0Cu << 16) | ((uint32_t)(4 + p) << 24);
+    out[p] = __builtin_amdgcn_perm(w, t4, sel) & 0xC000C000u;       // columns 2p, 2p + 1
+    out[4 + p] = __builtin_amdgcn_perm(t2, t6, sel) & 0xC000C000u;   // columns 8 + 2p, 9 + 2p
+  }
+}
 
 __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
   const float lo = bf16_to_f32(w & 0xffffu);
@@ -47,7 +62,6 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t G = K / kBlock;
-  const int64_t wpr = K / 16;
   const int nsteps = (int)(K / KT);
 
   // global -> register staging assignment
@@ -55,9 +69,10 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const int xr = tid >> 1, xk = (tid & 1) * 32;
   const bool xvalid = m0 + xr < M;
   const uint16_t* xsrc = x + (m0 + xr) * K + xk;
-  // W: 128 rows x 64 k = 4 words per row; thread -> row tid/2, 2 words at (tid&1)*2
+  // W: 128 rows x 64 k; thread -> row tid/2, the 32 columns of lane group
+  // (k0 % 128) / 32 + (tid & 1) of the row's tile: two consecutive words
   const int wr = tid >> 1, wk = (tid & 1) * 32;
-  const uint32_t* wsrc = codes + (n0 + wr) * wpr + (tid & 1) * 2;
+  const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
   const uint16_t* ssrc = scales + (n0 + wr) * G;
 
   u32x4 xs[4];
@@ -73,7 +88,7 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < 4; ++i) xs[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    cs = *reinterpret_cast<const u32x2*>(wsrc + k0 / 16);
+    cs = *reinterpret_cast<const u32x2*>(wsrc + (k0 / kBlock) * 128 + 64 * ((k0 % kBlock) / 64));
     ss = ssrc[k0 / kBlock];
   };
   auto lstore = [&](int stage) {
@@ -92,12 +107,12 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
     uint16_t* wd = &lds[stage][1][wr * LDS_ROW + wk];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t w = cs[j];
+      uint32_t bits[8];
+      decode_word_f16(cs[j], bits);
       u32x4 o0, o1;
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
-        const uint32_t bits = (w << (14 - 2 * f)) & 0xC000C000u;
-        const f16x2 v = __builtin_bit_cast(f16x2, bits) * s2;
+        const f16x2 v = __builtin_bit_cast(f16x2, bits[f]) * s2;
         if (f < 4) o0[f] = __builtin_bit_cast(uint32_t, v);
         else o1[f - 4] = __builtin_bit_cast(uint32_t, v);
       }

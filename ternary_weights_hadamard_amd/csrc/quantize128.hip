@@ -16,7 +16,8 @@
 //            row with 16-byte LDS reads and runs the row transform the same
 //            way.  Each thread now holds 64 consecutive K-elements of one row:
 //            the group's |.| sum is an in-register sum plus one exchange, and
-//            the codes of 64 elements pack into four whole words.
+//            the codes of 64 elements pack into four whole words (two word
+//            pairs of the row's 16 x 128 tile).
 // The 1/128 of the 2D transform is a power of two; it is folded into the
 // threshold and the stored scale instead of being applied to every element.
 #include "tb_common.h"
@@ -54,8 +55,9 @@ __device__ __forceinline__ void fwht_cross_halves(float (&v)[64], float sgn) {
   }
 }
 
-// 2-bit field position of K-offset r (0..15) inside a code word.
-__device__ __forceinline__ constexpr int field_pos(int r) { return 2 * (r >> 1) + 16 * (r & 1); }
+// 2-bit field position of column offset r (0..15) inside a dense code word:
+// r < 8 in bits 2-3 of nibble r, r >= 8 in bits 0-1 of nibble r - 8.
+__device__ __forceinline__ constexpr int field_pos(int r) { return 4 * (r & 7) + 2 - 2 * (r >> 3); }
 
 template <bool FMT24>
 __global__ void __launch_bounds__(256) quantize128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
@@ -135,7 +137,10 @@ __global__ void __launch_bounds__(256) quantize128_kernel(const float* __restric
         const uint32_t ng = (nz && v[j] < 0.f) ? 2u : 0u;
         words[j >> 4] |= (nz | ng) << field_pos(j & 15);
       }
-      *reinterpret_cast<u32x4*>(codes + grow * (K / 16) + k0 / 16 + 4 * half) = words;
+      // columns 64 half + j of group bk: word pairs of lane groups 2 half and 2 half + 1
+      uint32_t* tile = codes + ((grow >> 4) * kblocks + bk) * 128 + 2 * (grow & 15);
+      *reinterpret_cast<u32x2*>(tile + 64 * half) = u32x2{words[0], words[1]};
+      *reinterpret_cast<u32x2*>(tile + 64 * half + 32) = u32x2{words[2], words[3]};
       if (half == 0) {
         const uint32_t h16 = f32_to_f16_bits(s);
         if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;

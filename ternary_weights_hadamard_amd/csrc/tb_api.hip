@@ -15,6 +15,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dims_ok(int64_t N, int64_t K) { return N > 0 && K > 0 && N % kGroup == 0 && K % kGroup == 0; }
 bool dtype_ok(int d) { return d == TB_F32 || d == TB_BF16; }
 size_t dtype_bytes(int d) { return d == TB_F32 ? 4 : 2; }
+// bytes of the act8 operand of `elems` activations (4 per element + 1/8 of scales)
+size_t act8_bytes(size_t elems) { return elems * 4 + elems / 8; }
 
 // [a, a + na) and [b, b + nb) intersect (byte ranges)
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -45,7 +47,12 @@ const char* tb_status_string(int status) {
   }
 }
 
-int tb_version(void) { return 100; }
+int tb_version(void) { return 101; }
+
+size_t tb_act8_bytes(int64_t B, int64_t K) {
+  if (B < 0 || K <= 0 || K % kGroup) return 0;
+  return act8_bytes((size_t)B * (size_t)K);
+}
 
 tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
                           size_t* scale_bytes) {
@@ -59,14 +66,15 @@ tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, siz
 }
 
 tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K, void* stream) {
-  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return TB_ERR_DTYPE;
+  if (!dtype_ok(x_dtype) || !(dtype_ok(y_dtype) || y_dtype == TB_ACT8)) return TB_ERR_DTYPE;
   if (rows < 0 || K <= 0 || K % kGroup) return TB_ERR_SHAPE;
   if (rows == 0) return TB_OK;
   if (!x || !y) return TB_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return TB_ERR_ALIGN;
   const size_t n = (size_t)rows * (size_t)K;
-  if (x != y && overlap(x, n * dtype_bytes(x_dtype), y, n * dtype_bytes(y_dtype))) return TB_ERR_ALIAS;
+  const size_t yb = y_dtype == TB_ACT8 ? act8_bytes(n) : n * dtype_bytes(y_dtype);
   if (x == y && x_dtype != y_dtype) return TB_ERR_ALIAS;
+  if (x != y && overlap(x, n * dtype_bytes(x_dtype), y, yb)) return TB_ERR_ALIAS;
   return launched(tb::launch_fwht128(x, x_dtype, y, y_dtype, rows, K, as_stream(stream)));
 }
 
@@ -86,16 +94,27 @@ tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32
   return launched(tb::launch_quantize128(W, N, K, fmt, codes, meta, scales, err_flag, as_stream(stream)));
 }
 
-tb_status tb_ternary_gemv(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
+tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, void* stream) {
+  if (B < 0 || K <= 0 || K % kGroup) return TB_ERR_SHAPE;
+  if (B == 0) return TB_OK;
+  if (!x || !act) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(act)) return TB_ERR_ALIGN;
+  const size_t n = (size_t)B * (size_t)K;
+  if (overlap(x, n * 2, act, act8_bytes(n))) return TB_ERR_ALIAS;
+  return launched(tb::launch_act8_prep(x, B, K, act, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
                           int64_t K, float* y, void* stream) {
   if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
   if (B == 0) return TB_OK;
-  if (!x || !codes || !scales || !y) return TB_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return TB_ERR_ALIGN;
+  if (!act || !codes || !scales || !y) return TB_ERR_NULL;
+  if (!aligned16(act) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return TB_ERR_ALIGN;
   const size_t nk = (size_t)N * (size_t)K, yb = (size_t)B * (size_t)N * 4;
-  if (overlap(y, yb, x, (size_t)B * K * 2) || overlap(y, yb, codes, nk / 4) || overlap(y, yb, scales, nk / 64))
+  if (overlap(y, yb, act, act8_bytes((size_t)B * K)) || overlap(y, yb, codes, nk / 4) ||
+      overlap(y, yb, scales, nk / 64))
     return TB_ERR_ALIAS;
-  return launched(tb::launch_gemv_ternary(x, B, codes, scales, N, K, y, as_stream(stream)));
+  return launched(tb::launch_gemv_ternary(act, B, codes, scales, N, K, y, as_stream(stream)));
 }
 
 tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,

@@ -7,8 +7,11 @@ a call fails, these functions raise.
 
 Dtypes on the Python side (bit patterns are what matter):
   activations x      torch.bfloat16 (or int16/uint16 bit views)  [rows, K]
+  act8 operand       torch.uint8, flat, tb_act8_bytes(B, K) bytes
   weights W          torch.float32 [N, K]
-  codes / meta / signs  torch.int32 (uint32 bit patterns)
+  codes              torch.int32 (uint32 bit patterns): dense [N/16, K/128, 128],
+                     2:4 sign plane [N, K/64]
+  meta               torch.int32 [N, K/32]
   scales             torch.float16 (fp16 bit patterns) [N, K/128]
 """
 
@@ -19,7 +22,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtb.so")
 
-TB_F32, TB_BF16 = 0, 1
+TB_F32, TB_BF16, TB_ACT8 = 0, 1, 2
 TB_FMT_DENSE, TB_FMT_24 = 0, 1
 TB_EFLAG_NONFINITE, TB_EFLAG_SCALE_OVF = 1, 2
 TB_GEMV_MAX_BATCH = 16
@@ -38,6 +41,8 @@ SIGNATURES = {
     "tb_fwht128": (_int, [_vp, _int, _vp, _int, _i64, _i64, _vp]),
     "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "tb_ternary_gemv": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "tb_act8_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "tb_act8_prep": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "tb_ternary_gemm": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]),
 }
@@ -86,6 +91,8 @@ def _stream(stream):
 def _dt(t):
     if t.dtype == torch.float32:
         return TB_F32
+    if t.dtype == torch.uint8:
+        return TB_ACT8
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return TB_BF16
     raise TypeError(f"unsupported activation dtype {t.dtype}")
@@ -104,13 +111,21 @@ def tb_packed_bytes(fmt, n, k):
     return c.value, m.value, s.value
 
 
+def tb_act8_bytes(b, k):
+    return int(lib().tb_act8_bytes(int(b), int(k)))
+
+
 def tb_fwht128(x, y=None, out_dtype=None, stream=None):
-    """y[r, 128b + i] = sum_j H[i, j] / sqrt(128) * x[r, 128b + j]; y may be x."""
+    """y[r, 128b + i] = sum_j H[i, j] / sqrt(128) * x[r, 128b + j]; y may be x.
+    out_dtype torch.uint8 (or a uint8 y) writes the act8 GEMV operand instead."""
     _dev(x)
-    if y is None:
-        y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    _dev(y)
     rows = x.numel() // x.shape[-1] if x.numel() else 0
+    if y is None:
+        if out_dtype == torch.uint8:
+            y = torch.empty(tb_act8_bytes(rows, x.shape[-1]), dtype=torch.uint8, device=x.device)
+        else:
+            y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _dev(y)
     _check(lib().tb_fwht128(_p(x), _dt(x), _p(y), _dt(y), rows, x.shape[-1], _stream(stream)), "tb_fwht128")
     return y
 
@@ -121,7 +136,8 @@ def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, er
     n, k = w.shape
     dev = w.device
     if codes is None:
-        codes = torch.empty((n, k // (16 if fmt == TB_FMT_DENSE else 64)), dtype=torch.int32, device=dev)
+        shape = (n // 16, k // 128, 128) if fmt == TB_FMT_DENSE else (n, k // 64)
+        codes = torch.empty(shape, dtype=torch.int32, device=dev)
     if meta is None and fmt == TB_FMT_24:
         meta = torch.empty((n, k // 32), dtype=torch.int32, device=dev)
     if scales is None:
@@ -132,15 +148,28 @@ def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, er
     return codes, meta, scales
 
 
-def tb_ternary_gemv(x, codes, scales, y=None, stream=None):
-    """y[b, n] (fp32) = sum_g scale[n, g] * sum_k t[n, k] x[b, k]; x bf16 [B, K]."""
-    _dev(x, codes, scales)
+def tb_act8_prep(x, act=None, stream=None):
+    """Encode bf16 activations x [B, K] as the act8 operand of tb_ternary_gemv."""
+    _dev(x)
     b, k = x.shape
-    n = codes.shape[0]
+    if act is None:
+        act = torch.empty(max(tb_act8_bytes(b, k), 1), dtype=torch.uint8, device=x.device)
+    _dev(act)
+    _check(lib().tb_act8_prep(_p(x), b, k, _p(act), _stream(stream)), "tb_act8_prep")
+    return act
+
+
+def tb_ternary_gemv(act, codes, scales, batch, y=None, stream=None):
+    """y[b, n] (fp32) = sum_g scale[n, g] * sum_k t[n, k] x[b, k] for `batch`
+    rows of activations given as the act8 operand `act`."""
+    _dev(act, codes, scales)
+    n, g = scales.shape
+    k = g * 128
     if y is None:
-        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+        y = torch.empty((batch, n), dtype=torch.float32, device=act.device)
     _dev(y)
-    _check(lib().tb_ternary_gemv(_p(x), b, _p(codes), _p(scales), n, k, _p(y), _stream(stream)), "tb_ternary_gemv")
+    _check(lib().tb_ternary_gemv(_p(act), int(batch), _p(codes), _p(scales), n, k, _p(y), _stream(stream)),
+           "tb_ternary_gemv")
     return y
 
 
@@ -160,7 +189,7 @@ def tb_ternary_gemm(x, codes, scales, y=None, out_dtype=torch.bfloat16, stream=N
     """Y[m, n] = sum_g scale[n, g] * sum_k t[n, k] x[m, k]; x bf16 [M, K], Y bf16 or fp32."""
     _dev(x, codes, scales)
     m, k = x.shape
-    n = codes.shape[0]
+    n = scales.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
     _dev(y)

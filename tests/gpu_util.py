@@ -87,3 +87,52 @@ def check_dense_codes(codes_gpu, scales_gpu, ref, k, what):
     assert not outside.any(), f"{what}: {int(outside.sum())} code mismatches outside the threshold band"
     assert ulp.max(initial=0) <= 1, f"{what}: scale differs by {ulp.max()} ulp"
     return int(near.sum()), int((mism & near).sum())
+
+
+# ---------------------------------------------------------------- act8 operand
+# Test-side reading of the act8 format (the activation operand of the dense
+# GEMV, defined in include/tb.h): four e4m3 sub-rows with E8M0 block scales.
+
+def e4m3_to_f64(b):
+    b = np.asarray(b, dtype=np.int64)
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    v = np.where(e > 0, np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)), np.ldexp(m / 8.0, -6))
+    v = np.where((b & 0x7F) == 0x7F, np.nan, v)
+    return np.where(s > 0, -v, v)
+
+
+def act8_decode(buf, b, k):
+    """x[b, k] as the sum of the four sub-rows of an act8 buffer (float64)."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    g = k // 128
+    vals = buf[:4 * b * k].reshape(b, g, 4, 4, 32).astype(np.int64)  # [b][g][sub][q][byte]
+    scl = buf[4 * b * k:4 * b * k + b * k // 8].reshape(b, g, 4, 4).astype(np.int64)  # [b][g][sub][block]
+    x = np.zeros((b, k))
+    for q in range(4):
+        for half in range(2):
+            kl = 64 * half + 16 * q + np.arange(16)           # K within the group
+            v = e4m3_to_f64(vals[:, :, :, q, 16 * half:16 * half + 16])  # [b][g][sub][16]
+            sc = scl[:, :, :, (kl // 32)]                       # [b][g][sub][16]
+            fac = np.where(sc == 0xFF, np.nan, np.ldexp(1.0, (sc - 127)))
+            part = np.sum(v * fac, axis=2)                      # [b][g][16]
+            cols = (128 * np.arange(g)[:, None] + kl[None, :])  # [g][16]
+            x[:, cols] += part
+    return x
+
+
+def act8_kept(x_bits):
+    """bf16 bits of what act8 represents: the element itself when its exponent is
+    within 10 of its 32-block's largest (level 0) or within 10 of the largest of
+    the rest (level 1), else 0; bf16 subnormals become 0."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    out = x.copy()
+    b, k = x.shape
+    e = ((x >> 7) & 0xFF).astype(np.int64).reshape(b, k // 32, 32)
+    fin = (e > 0) & (e < 255)
+    m0 = np.max(np.where(e < 255, e, 0), axis=2, keepdims=True)
+    rest = fin & (e + 10 < m0)
+    m1 = np.max(np.where(rest, e, 0), axis=2, keepdims=True)
+    keep = fin & ((e + 10 >= m0) | (rest & (e + 10 >= m1) & (m1 > 0)))
+    keep = keep | (e == 255)
+    out[~keep.reshape(b, k)] = 0
+    return out

@@ -68,6 +68,26 @@ def test_fwht_validation():
     assert L.tb_fwht128(_v(A), 1, _v(A + 64), 1, 1, 128, s) == 8  # partial overlap
     assert L.tb_fwht128(_v(A), 1, _v(A), 0, 1, 128, s) == 8      # in place with different dtypes
     assert L.tb_fwht128(None, 1, None, 1, 0, 128, s) == 0        # empty batch is a no-op
+    assert L.tb_fwht128(_v(A), 2, _v(B), 1, 1, 128, s) == 4      # act8 is an output-only dtype
+    # act8 output: 4.125 bytes per element, so a y starting 512 bytes after a
+    # 256-byte bf16 x does not overlap it, one starting inside x does
+    assert L.tb_fwht128(_v(A), 1, _v(A + 128), 2, 1, 128, s) == 8
+    assert L.tb_fwht128(_v(A), 2, _v(A), 2, 1, 128, s) == 4
+
+
+def test_act8_bytes_and_prep_validation():
+    L = tb.lib()
+    s = None
+    assert tb.tb_act8_bytes(1, 5120) == 4 * 5120 + 5120 // 8
+    assert tb.tb_act8_bytes(3, 128) == 3 * (4 * 128 + 16)
+    assert tb.tb_act8_bytes(0, 128) == 0
+    assert tb.tb_act8_bytes(1, 100) == 0 and tb.tb_act8_bytes(-1, 128) == 0
+    assert L.tb_act8_prep(_v(A), 1, 100, _v(B), s) == 2
+    assert L.tb_act8_prep(_v(A), -1, 128, _v(B), s) == 2
+    assert L.tb_act8_prep(None, 1, 128, _v(B), s) == 1
+    assert L.tb_act8_prep(_v(A), 1, 128, _v(MIS), s) == 3
+    assert L.tb_act8_prep(_v(A), 1, 128, _v(A + 16), s) == 8    # act over x
+    assert L.tb_act8_prep(None, 0, 128, None, s) == 0           # empty batch
 
 
 def test_quantize_validation():
@@ -93,6 +113,7 @@ def test_gemv_validation():
     assert L.tb_ternary_gemv(_v(A), 1, None, _v(C), 128, 128, _v(D), s) == 1
     assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(MIS), s) == 3
     assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(B), s) == 8     # y over codes
+    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(A + 512), s) == 8  # y over act8 (528 bytes)
     assert L.tb_ternary_gemv(None, 0, None, None, 128, 128, None, s) == 0         # empty batch
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), None, _v(C), 128, 128, _v(D), s) == 1
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), _v(C), _v(D), 128, 384, _v(MIS), s) == 3

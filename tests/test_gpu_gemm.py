@@ -35,9 +35,10 @@ def test_gemm_full_size_sampled(k, n):
     for out in (torch.bfloat16, torch.float32):
         y = host_f64(tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(scales), out_dtype=out))
         rs = np.sort(np.random.default_rng(5).choice(m, 64, replace=False))
-        cs = np.sort(np.random.default_rng(6).choice(n, 96, replace=False))
-        ref = oracle.matvec.gemm(x[rs], codes[cs], scales[cs], k)
-        assert_close(y[np.ix_(rs, cs)], ref, f"gemm {m}x{n}x{k} {out} (64x96 sampled)",
+        tiles = np.sort(np.random.default_rng(6).choice(n // 16, 6, replace=False))
+        cs = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+        ref = oracle.matvec.gemm(x[rs], codes[tiles], scales[cs], k)
+        assert_close(y[np.ix_(rs, cs)], ref, f"gemm {m}x{n}x{k} {out} (64 rows x 6 tiles sampled)",
                      out_bf16=out == torch.bfloat16)
         del y
 
@@ -51,7 +52,7 @@ def test_gemm_exact_small_integers_and_gemv_agreement():
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
     # rows 0..7 through the GEMV give the same exact values
-    yv = tb.tb_ternary_gemv(bf16_dev(x[:8]), u32_dev(codes), f16_dev(sc))
+    yv = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x[:8])), u32_dev(codes), f16_dev(sc), 8)
     torch.cuda.synchronize()
     assert np.array_equal(yv.cpu().numpy(), y.cpu().numpy()[:8])
 

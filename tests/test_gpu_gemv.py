@@ -1,11 +1,12 @@
-"""GPU parity of tb_ternary_gemv and tb_ternary24_gemv against the oracle."""
+"""GPU parity of tb_act8_prep + tb_ternary_gemv and of tb_ternary24_gemv
+against the oracle."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import DEV, assert_close, bf16_dev, f16_dev, say, u32_dev
+from gpu_util import (DEV, act8_decode, act8_kept, assert_close, bf16_dev, f16_dev, say, u32_dev)
 from ternary_weights_hadamard_amd import synth, tb
 
 pytestmark = pytest.mark.gpu
@@ -18,28 +19,36 @@ def _dense_inputs(n, k, b, seed):
     return codes, scales, x
 
 
+def _gemv(x_bits, codes, scales):
+    act = tb.tb_act8_prep(bf16_dev(x_bits))
+    y = tb.tb_ternary_gemv(act, u32_dev(codes), f16_dev(scales), x_bits.shape[0])
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
 @pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (1024, 1024), (384, 2176)])
 @pytest.mark.parametrize("b", [1, 2, 5, 8, 16])
 def test_gemv_small_matches_oracle(n, k, b):
     say(f"gemv N={n} K={k} B={b}")
     codes, scales, x = _dense_inputs(n, k, b, seed=n + k + b)
-    y = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(codes), f16_dev(scales))
-    torch.cuda.synchronize()
+    y = _gemv(x, codes, scales)
     ref = oracle.matvec.gemv(x, codes, scales, k)
-    assert_close(y.cpu().numpy(), ref, f"gemv {n}x{k} B={b}")
-    # fp32 accumulation of exact products: far inside the bar
-    assert np.max(np.abs(y.cpu().numpy() - ref)) <= 1e-5 * np.max(np.abs(ref))
+    assert_close(y, ref, f"gemv {n}x{k} B={b}")
+    # exact products, fp32 accumulation: far inside the bar
+    assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("n,k", [(5120, 5120), (17408, 5120), (5120, 17408)])
-@pytest.mark.parametrize("b", [1, 8])
-def test_gemv_full_size_sampled_rows(n, k, b):
+@pytest.mark.parametrize("n,k", [(5120, 5120), (17408, 5120), (5120, 17408), (15360, 5120)])
+@pytest.mark.parametrize("b", [1, 4, 8])
+def test_gemv_full_size_sampled_tiles(n, k, b):
     say(f"gemv full N={n} K={k} B={b}")
     codes, scales, x = _dense_inputs(n, k, b, seed=20 + b)
-    y = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(codes), f16_dev(scales)).cpu().numpy()
-    rows = np.sort(np.random.default_rng(1).choice(n, 256, replace=False))
-    ref = oracle.matvec.gemv(x, codes[rows], scales[rows], k)
-    assert_close(y[:, rows], ref, f"gemv {n}x{k} B={b} (256 sampled rows)")
+    y = _gemv(x, codes, scales)
+    tiles = np.sort(np.random.default_rng(1).choice(n // 16, 16, replace=False))
+    rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+    ref = oracle.matvec.gemv(x, codes[tiles], scales[rows], k)
+    assert_close(y[:, rows], ref, f"gemv {n}x{k} B={b} (16 sampled tiles)")
+    assert np.max(np.abs(y[:, rows] - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
 @pytest.mark.parametrize("b", [1, 3, 16])
@@ -49,10 +58,9 @@ def test_gemv_exact_small_integers(b):
     codes = synth.random_code_words(n, k, seed=5)
     x = synth.small_int_bf16((b, k), seed=6)
     sc = (2.0 ** np.random.default_rng(7).integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
-    y = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(codes), f16_dev(sc))
-    torch.cuda.synchronize()
+    y = _gemv(x, codes, sc)
     ref = oracle.matvec.gemv(x, codes, sc, k)
-    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    assert np.array_equal(y, ref)
 
 
 def test_gemv_special_patterns():
@@ -61,36 +69,111 @@ def test_gemv_special_patterns():
     xv = oracle.numerics.bf16_bits_to_f64(x)
     ones_scale = np.full((n, k // 128), np.float16(1.0).view(np.uint16), dtype=np.uint16)
     t = np.ones((n, k), dtype=np.int8)
-    y = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(oracle.quant.pack_dense(t)), f16_dev(ones_scale))
-    torch.cuda.synchronize()
-    assert np.allclose(y.cpu().numpy(), xv.sum(), rtol=1e-5)
+    y = _gemv(x, oracle.quant.pack_dense(t), ones_scale)
+    assert np.allclose(y, xv.sum(), rtol=1e-5)
     cols = np.random.default_rng(2).integers(0, k, size=n)
     t = np.zeros((n, k), dtype=np.int8)
     t[np.arange(n), cols] = -1
-    y = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(oracle.quant.pack_dense(t)), f16_dev(ones_scale))
-    torch.cuda.synchronize()
-    assert np.array_equal(y.cpu().numpy()[0], -xv[0, cols])
+    y = _gemv(x, oracle.quant.pack_dense(t), ones_scale)
+    assert np.array_equal(y[0], -xv[0, cols])
     t = np.zeros((n, k), dtype=np.int8)
-    y = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(oracle.quant.pack_dense(t)), f16_dev(ones_scale))
-    torch.cuda.synchronize()
-    assert np.all(y.cpu().numpy() == 0)
+    y = _gemv(x, oracle.quant.pack_dense(t), ones_scale)
+    assert np.all(y == 0)
 
 
 def test_gemv_canaries_and_empty_batch():
     n, k, b = 384, 640, 3
     codes, scales, x = _dense_inputs(n, k, b, seed=31)
-    buf = torch.full((b * n + 128,), 12345.0, dtype=torch.float32, device=DEV)
-    y = buf[64:64 + b * n].view(b, n)
-    tb.tb_ternary_gemv(bf16_dev(x), u32_dev(codes), f16_dev(scales), y=y)
+    act = tb.tb_act8_prep(bf16_dev(x))
+    y = torch.full((b + 1, n), 7.0, dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv(act, u32_dev(codes), f16_dev(scales), b, y=y[:b])
     torch.cuda.synchronize()
-    assert torch.all(buf[:64] == 12345.0) and torch.all(buf[64 + b * n:] == 12345.0)
-    assert_close(y.cpu().numpy(), oracle.matvec.gemv(x, codes, scales, k), "gemv canary run")
-    e = torch.empty((0, k), dtype=torch.bfloat16, device=DEV)
-    out = tb.tb_ternary_gemv(e, u32_dev(codes), f16_dev(scales))
+    assert torch.all(y[b] == 7.0), "GEMV wrote past its output"
+    assert_close(y[:b].cpu().numpy(), oracle.matvec.gemv(x, codes, scales, k), "gemv canary run")
+    out = tb.tb_ternary_gemv(act, u32_dev(codes), f16_dev(scales), 0)
     assert out.shape == (0, n)
 
 
-# ------------------------------------------------------------------ 2:4
+# ---------------------------------------------------------------- act8 operand
+
+def _act8_host(x_bits):
+    b, k = x_bits.shape
+    act = tb.tb_act8_prep(bf16_dev(x_bits))
+    torch.cuda.synchronize()
+    buf = act.cpu().numpy()
+    assert buf.size == tb.tb_act8_bytes(b, k)
+    return buf
+
+
+@pytest.mark.parametrize("b,k", [(1, 128), (3, 640), (16, 5120)])
+def test_act8_reconstructs_gaussian_activations_exactly(b, k):
+    x = synth.gaussian_bf16((b, k), seed=b + k)
+    rec = act8_decode(_act8_host(x), b, k)
+    assert np.array_equal(rec, oracle.numerics.bf16_bits_to_f64(x))
+
+
+def _wide_range_bf16(b, k, seed, span=60):
+    """bf16 values with exponents spread uniformly over `span` binades, random
+    signs, some exact zeros and subnormals."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(127 - span // 2, 127 + span // 2, size=(b, k))
+    m = rng.integers(0, 128, size=(b, k))
+    s = rng.integers(0, 2, size=(b, k))
+    bits = ((s << 15) | (e << 7) | m).astype(np.uint16)
+    bits[rng.random((b, k)) < 0.02] = 0
+    sub = rng.random((b, k)) < 0.01
+    bits[sub] = rng.integers(1, 128, size=int(sub.sum())).astype(np.uint16)  # subnormals
+    return bits
+
+
+def test_act8_wide_range_keeps_what_the_format_promises():
+    b, k = 2, 2048
+    x = _wide_range_bf16(b, k, seed=3)
+    rec = act8_decode(_act8_host(x), b, k)
+    kept = act8_kept(x)
+    assert np.array_equal(rec, oracle.numerics.bf16_bits_to_f64(kept))
+    # what is dropped is below 2^-20 of its block's largest magnitude
+    xv = np.abs(oracle.numerics.bf16_bits_to_f64(x)).reshape(b, k // 32, 32)
+    dropped = (kept != x).reshape(b, k // 32, 32)
+    blockmax = xv.max(axis=2, keepdims=True)
+    assert np.all(np.where(dropped, xv, 0.0) < 2.0 ** -20 * blockmax)
+    say(f"  act8 wide range: {int(dropped.sum())} of {b * k} elements below the kept range")
+
+
+def test_gemv_wide_range_activations_exact_on_kept_values():
+    n, k, b = 512, 2048, 3
+    codes = synth.random_code_words(n, k, seed=41)
+    scales = synth.random_scales_f16(n, k, seed=42)
+    x = _wide_range_bf16(b, k, seed=43, span=40)
+    y = _gemv(x, codes, scales)
+    ref = oracle.matvec.gemv(act8_kept(x), codes, scales, k)
+    assert_close(y, ref, "gemv wide-range activations (oracle on kept values)")
+    assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_gemv_nonfinite_activation_poisons_only_its_batch_row():
+    n, k, b = 256, 512, 3
+    codes, scales, x = _dense_inputs(n, k, b, seed=51)
+    x = x.copy()
+    x[1, 200] = 0x7F80  # +inf
+    y = _gemv(x, codes, scales)
+    assert np.all(np.isnan(y[1])), "a non-finite activation must make its output row non-finite"
+    ref = oracle.matvec.gemv(x[[0, 2]], codes, scales, k)
+    assert_close(y[[0, 2]], ref, "gemv rows next to a non-finite row")
+
+
+def test_act8_from_fwht_equals_prep_of_rotated_bf16():
+    b, k = 5, 1152
+    x = synth.gaussian_bf16((b, k), seed=61)
+    xd = bf16_dev(x)
+    fused = tb.tb_fwht128(xd, out_dtype=torch.uint8)
+    rotated = tb.tb_fwht128(xd)
+    prep = tb.tb_act8_prep(rotated)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, prep)
+
+
+# ---------------------------------------------------------------- 2:4
 
 @pytest.mark.parametrize("n,k,b", [(128, 128, 1), (256, 384, 1), (1024, 1024, 1), (256, 640, 4), (128, 256, 16)])
 def test_gemv24_small_matches_oracle(n, k, b):
@@ -125,7 +208,7 @@ def test_gemv24_exact_and_dense_equivalence():
     y24 = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(sc))
     i0, i1, n0, n1 = oracle.quant.unpack_24(meta, signs, k)
     dense = oracle.quant.pack_dense(oracle.quant.dense_from_24(i0, i1, n0, n1))
-    yd = tb.tb_ternary_gemv(bf16_dev(x), u32_dev(dense), f16_dev(sc))
+    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(sc), x.shape[0])
     torch.cuda.synchronize()
     ref = oracle.matvec.gemv24(x, meta, signs, sc, k)
     assert np.array_equal(y24.cpu().numpy().astype(np.float64), ref)

@@ -21,7 +21,8 @@ def test_single_layer_pipeline_1024():
     say("pipeline 1024^2")
     codes, _, scales = tb.tb_quantize_pack(f32_dev(w))
     xr = tb.tb_fwht128(bf16_dev(x))
-    yr = tb.tb_ternary_gemv(xr, codes, scales)
+    act = tb.tb_fwht128(bf16_dev(x), out_dtype=torch.uint8)  # rotation fused with the operand encoding
+    yr = tb.tb_ternary_gemv(act, codes, scales, 1)
     y = tb.tb_fwht128(yr)
     torch.cuda.synchronize()
 
@@ -48,7 +49,7 @@ def test_gemm_prefill_of_quantised_layer():
     codes, _, scales = tb.tb_quantize_pack(f32_dev(w))
     xr = tb.tb_fwht128(bf16_dev(x))
     y = tb.tb_ternary_gemm(xr, codes, scales, out_dtype=torch.float32)
-    yv = tb.tb_ternary_gemv(xr[:16].contiguous(), codes, scales)
+    yv = tb.tb_ternary_gemv(tb.tb_act8_prep(xr[:16].contiguous()), codes, scales, 16)
     torch.cuda.synchronize()
     ref = oracle.quant.quantize_dense(w.astype(np.float64))
     check_dense_codes(codes, scales, ref, k, "prefill codes")

@@ -86,7 +86,7 @@ def test_output_canaries():
     w = synth.stack_weights(n, k, seed=6)
     cb = torch.full((n * k // 16 + 8,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
     sb = torch.full((n * k // 128 + 16,), -3.0, dtype=torch.float16, device=DEV)
-    codes = cb[4:4 + n * k // 16].view(n, k // 16)
+    codes = cb[4:4 + n * k // 16].view(n // 16, k // 128, 128)
     scales = sb[8:8 + n * k // 128].view(n, k // 128)
     tb.tb_quantize_pack(f32_dev(w), codes=codes, scales=scales)
     torch.cuda.synchronize()
