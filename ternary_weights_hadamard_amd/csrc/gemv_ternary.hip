@@ -3,8 +3,8 @@
 // (mhpq.cn/news/1159370 §4.2: read the weight bits, expand, scale, multiply).
 //
 // HBM bound: every weight is streamed once at 2 bits plus 1/8 bit of scale,
-// so the kernel is built to spend as little vector-ALU work per weight as
-// possible and to keep many code loads in flight.
+// so the kernel spends as little vector-ALU work per weight as possible and
+// keeps as many code loads in flight as the registers allow.
 //   * The contraction runs on v_mfma_scale_f32_16x16x128_f8f6f4: the weights
 //     are its fp4 operand (one 16-row x 128-column tile per instruction), the
 //     activations its e4m3 operand with E8M0 block scales (act8.h: each bf16
@@ -16,11 +16,14 @@
 //   * Lane (i, q) holds output rows 4q .. 4q + 3 of column i: the four sub-rows
 //     of batch row 4m + q.  Their sum times f16(scale) / 2 is the group's
 //     contribution.
-// Work split: a wave owns one 16-row tile and a contiguous range of groups;
-// four waves per workgroup cover 4 / KS tiles x KS group ranges, and split
-// ranges are added through LDS.  Each wave keeps kPrefetch groups of codes and
-// scales in flight and loads the activation operand two groups ahead (it is
-// read by every wave and stays in cache).
+// Work split: a wave owns one 16-row tile and a slice of at most CH groups of
+// K; it issues every load of its slice (activations, codes and scales, group
+// by group) before the first instruction that needs one, so all of them are in
+// flight at once and the in-order load counter never makes a far load wait for
+// a near one.  The KS slices of a tile are the waves of one workgroup and are
+// added through LDS in a fixed order (the result does not depend on timing).
+#include <algorithm>
+
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -31,112 +34,105 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-constexpr int kPrefetch = 8;
-constexpr int kWaves = 4;
+constexpr int kMaxSlices = 16;  // waves per workgroup
 
+// groups per wave and chunk: a group costs 9 * NB4 + 3 registers, and a
+// workgroup of up to 16 waves leaves 128 per lane
 template <int NB4>
-struct ActFrag {
-  i32x8 v[NB4];
-  int s[NB4];
+struct Chunk {
+  static constexpr int value = NB4 == 1 ? 9 : NB4 == 2 ? 4 : NB4 == 3 ? 3 : 2;
 };
 
-template <int NB4>
-__global__ void __launch_bounds__(256) gemv_ternary_kernel(const uint8_t* __restrict__ act, int B,
-                                                            const uint32_t* __restrict__ codes,
-                                                            const uint16_t* __restrict__ scales, int64_t N,
-                                                            int64_t K, float* __restrict__ y, int KS) {
-  __shared__ float red[kWaves][NB4][64];
+template <int NB4, int CH>
+__global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint8_t* __restrict__ act, int B,
+                                                                        const uint32_t* __restrict__ codes,
+                                                                        const uint16_t* __restrict__ scales,
+                                                                        int64_t N, int64_t K,
+                                                                        float* __restrict__ y, int KS) {
+  __shared__ float red[kMaxSlices][NB4][64];
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, q = lane >> 4;
-  const int ks = wv % KS;
-  const int64_t nb = (int64_t)blockIdx.x * (kWaves / KS) + wv / KS;
-  const bool live = nb < N / 16;
+  const int64_t nb = blockIdx.x;
   const int G = (int)(K / kBlock);
   const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
+
+  // activation operand rows of this lane: batch 4m + i/4, sub-row i % 4
+  const uint8_t* av_base[NB4];
+  const uint8_t* as_base[NB4];
+  bool arow[NB4];
+#pragma unroll
+  for (int m = 0; m < NB4; ++m) {
+    const int b = 4 * m + (i >> 2);
+    arow[m] = b < B;
+    const size_t row = (size_t)(arow[m] ? b : 0) * G;
+    av_base[m] = act + (row * 16 + (i & 3) * 4 + q) * 32;
+    as_base[m] = act + (size_t)4 * B * K + row * 16 + (i & 3) * 4 + q;
+  }
+  const uint32_t* cp = codes + (size_t)nb * G * 128 + 2 * lane;
+  const uint16_t* sp = scales + (size_t)(16 * nb + i) * G;
 
   float acc[NB4];
 #pragma unroll
   for (int m = 0; m < NB4; ++m) acc[m] = 0.f;
 
-  if (live && gb < ge) {
-    const uint32_t* cp = codes + (size_t)nb * G * 128 + 2 * lane;
-    const uint16_t* sp = scales + (size_t)(16 * nb + i) * G;
-    // activation operand rows of this lane: batch 4m + i/4, sub-row i % 4
-    const uint8_t* av_base[NB4];
-    const uint8_t* as_base[NB4];
-    bool arow[NB4];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int c = gb; c < ge; c += CH) {
+    const int n = min(CH, ge - c);
+    i32x8 av[CH][NB4];
+    int as[CH][NB4];
+    u32x2 cw[CH];
+    uint32_t sw[CH];
+    // every load of the chunk first (slots past the slice repeat its last group;
+    // the loops stay free of early exits so the arrays live in registers)
 #pragma unroll
-    for (int m = 0; m < NB4; ++m) {
-      const int b = 4 * m + (i >> 2);
-      arow[m] = b < B;
-      const size_t row = (size_t)(arow[m] ? b : 0) * G;
-      av_base[m] = act + (row * 16 + (i & 3) * 4 + q) * 32;
-      as_base[m] = act + (size_t)4 * B * K + row * 16 + (i & 3) * 4 + q;
-    }
-    auto load_act = [&](int g, ActFrag<NB4>& f) {
+    for (int j = 0; j < CH; ++j) {
+      const int g = min(c + j, ge - 1);
+      cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)g * 128);
+      sw[j] = sp[g];
 #pragma unroll
       for (int m = 0; m < NB4; ++m) {
         if (arow[m]) {
           const u32x4* p = reinterpret_cast<const u32x4*>(av_base[m] + (size_t)g * 512);
           const u32x4 lo = p[0], hi = p[1];
-          f.v[m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          f.s[m] = as_base[m][(size_t)g * 16];
+          av[j][m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          as[j][m] = as_base[m][(size_t)g * 16];
         } else {
-          f.v[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-          f.s[m] = 127;
+          av[j][m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          as[j][m] = 127;
         }
       }
-    };
-
-    u32x2 cr[kPrefetch];
-    uint32_t sr[kPrefetch];
-#pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) {
-      const int g = min(gb + p, ge - 1);
-      cr[p] = *reinterpret_cast<const u32x2*>(cp + (size_t)g * 128);
-      sr[p] = sp[g];
     }
-    ActFrag<NB4> fa[2];
-    load_act(gb, fa[0]);
-    load_act(min(gb + 1, ge - 1), fa[1]);
-
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int g0 = gb; g0 < ge; g0 += kPrefetch) {
 #pragma unroll
-      for (int p = 0; p < kPrefetch; ++p) {
-        const int g = g0 + p;
-        if (g >= ge) break;
-        ActFrag<NB4>& f = fa[p & 1];
-        const uint32_t w0 = cr[p][0], w1 = cr[p][1];
-        const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
-                          (int)((w1 << 2) & 0xCCCCCCCCu)};
-        const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};
-        const float s = f16_bits_to_f32(sr[p]) * 0.5f;
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t w0 = cw[j][0], w1 = cw[j][1];
+      const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
+                        (int)((w1 << 2) & 0xCCCCCCCCu)};
+      const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
+      const float s = f16_bits_to_f32(sw[j]) * 0.5f;
 #pragma unroll
-        for (int m = 0; m < NB4; ++m) {
-          const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.v[m], b8, zero, 0, 4, 0, f.s[m], 0, 127);
-          acc[m] = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc[m]);
-        }
-        // refill: codes kPrefetch groups ahead, activations two ahead (clamped to the range)
-        const int gn = min(g + kPrefetch, ge - 1);
-        cr[p] = *reinterpret_cast<const u32x2*>(cp + (size_t)gn * 128);
-        sr[p] = sp[gn];
-        load_act(min(g + 2, ge - 1), f);
+      for (int m = 0; m < NB4; ++m) {
+        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[j][m], b8, zero, 0, 4, 0, as[j][m], 0, 127);
+        // keep both sources live past the instruction: its destination must not
+        // reuse their registers (it reads them over several passes)
+        keep_in_vgprs(av[j][m]);
+        keep_in_vgprs(bw);
+        const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc[m]);
+        acc[m] = j < n ? a : acc[m];  // slots past the slice (a repeated group) add nothing
       }
     }
   }
 
   if (KS > 1) {
 #pragma unroll
-    for (int m = 0; m < NB4; ++m) red[wv][m][lane] = acc[m];
+    for (int m = 0; m < NB4; ++m) red[ks][m][lane] = acc[m];
     __syncthreads();
     if (ks != 0) return;
 #pragma unroll
     for (int m = 0; m < NB4; ++m)
-      for (int w = 1; w < KS; ++w) acc[m] += red[wv + w][m][lane];
+      for (int w = 1; w < KS; ++w) acc[m] += red[w][m][lane];
   }
-  if (!live) return;
 #pragma unroll
   for (int m = 0; m < NB4; ++m) {
     const int b = 4 * m + q;
@@ -144,23 +140,161 @@ __global__ void __launch_bounds__(256) gemv_ternary_kernel(const uint8_t* __rest
   }
 }
 
+
+// Staged path (B <= 4, the activation slices of a workgroup fit in LDS).  Per
+// wave: the activation operand of its slice is copied into a private LDS area
+// with whole-wave 16-byte loads (one load moves two groups of one batch row),
+// the weight scales come in with one load per four groups (lane (i, q) fetches
+// group 4r + q of row i) and are handed to the other lanes with ds_bpermute,
+// and the codes with one load per group.  That is about CH + CH/2 + CH/4 + 1
+// loads for CH groups instead of 5 CH, which matters because the number of
+// loads a wave can keep in flight, not their size, bounds this kernel.
+constexpr int kStageBytes = 528;  // act8 bytes per group and batch row (512 values + 16 scales)
+
+template <int CH>
+__global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(const uint8_t* __restrict__ act, int B,
+                                                                       const uint32_t* __restrict__ codes,
+                                                                       const uint16_t* __restrict__ scales,
+                                                                       int64_t N, int64_t K,
+                                                                       float* __restrict__ y, int KS) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, q = lane >> 4;
+  const int64_t nb = blockIdx.x;
+  const int G = (int)(K / kBlock);
+  const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
+  const int n = ge - gb;  // 1 .. CH groups in this slice
+  constexpr int kPairs = (CH + 1) / 2;
+  constexpr int kScaleRegs = (CH + 3) / 4;
+  unsigned char* st = smem + (size_t)ks * B * CH * kStageBytes;  // [B][CH][512] values, then [B][CH][16] scales
+  unsigned char* st_sc = st + (size_t)B * CH * 512;
+  float* red = reinterpret_cast<float*>(smem + (size_t)KS * B * CH * kStageBytes);
+
+  // 1. activation slice (issued first: it is waited for first)
+  u32x4 av_st[4][kPairs];
+  u32x4 as_st[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const unsigned char* src = act + ((size_t)b * G + gb) * 512;
+#pragma unroll
+    for (int t = 0; t < kPairs; ++t) {
+      const int off = t * 1024 + lane * 16;
+      if (b < B && off < n * 512) av_st[b][t] = *reinterpret_cast<const u32x4*>(src + off);
+    }
+    if (b < B && lane < n)
+      as_st[b] = *reinterpret_cast<const u32x4*>(act + (size_t)4 * B * K + ((size_t)b * G + gb + lane) * 16);
+  }
+  // 2. codes, one 8-byte load per lane and group (slots past the slice repeat its last group)
+  const uint32_t* cp = codes + (size_t)nb * G * 128 + 2 * lane;
+  u32x2 cw[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128);
+  // 3. weight scales: lane (i, q) holds row i's scale of groups gb + 4r + q
+  const uint16_t* sp = scales + (size_t)(16 * nb + i) * G;
+  uint32_t sr[kScaleRegs];
+#pragma unroll
+  for (int r = 0; r < kScaleRegs; ++r) sr[r] = sp[min(gb + 4 * r + q, ge - 1)];
+  // 4. activation slice into this wave's LDS area (read back by other lanes of
+  //    the same wave only; LDS operations of a wave complete in order)
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int t = 0; t < kPairs; ++t) {
+      const int off = t * 1024 + lane * 16;
+      if (b < B && off < n * 512) *reinterpret_cast<u32x4*>(st + (size_t)b * CH * 512 + off) = av_st[b][t];
+    }
+    if (b < B && lane < n) *reinterpret_cast<u32x4*>(st_sc + ((size_t)b * CH + lane) * 16) = as_st[b];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 5. the products: lane (i, q) feeds A rows of batch i / 4, sub-row i % 4.
+  //    Rows of batches >= B only reach output rows that are never stored, so
+  //    those lanes read the last batch row instead of branching.
+  const int bp = min(i >> 2, B - 1);
+  const unsigned char* a_src = st + (size_t)bp * CH * 512 + ((i & 3) * 4 + q) * 32;
+  const unsigned char* a_sc = st_sc + (size_t)bp * CH * 16 + (i & 3) * 4 + q;
+  float acc = 0.f;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(a_src + j * 512);
+    const u32x4 lo = p[0], hi = p[1];
+    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const int as = a_sc[j * 16];
+    const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * (j & 3)) * 4, (int)sr[j >> 2]);
+    const float s = f16_bits_to_f32((uint32_t)sbits & 0xFFFFu) * 0.5f;
+    const uint32_t w0 = cw[j][0], w1 = cw[j][1];
+    const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
+                      (int)((w1 << 2) & 0xCCCCCCCCu)};
+    const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
+    const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, zero, 0, 4, 0, as, 0, 127);
+    keep_in_vgprs(av);
+    keep_in_vgprs(bw);
+    const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc);
+    acc = j < n ? a : acc;  // slots past the slice add nothing
+  }
+
+  if (KS > 1) {
+    red[ks * 64 + lane] = acc;
+    __syncthreads();
+    if (ks != 0) return;
+    for (int w = 1; w < KS; ++w) acc += red[w * 64 + lane];
+  }
+  if (q < B) y[(size_t)q * N + 16 * nb + i] = acc;
+}
+
+constexpr int kStagedCH = 10;
+constexpr size_t kStagedMaxLds = 96 * 1024;
+
+size_t staged_lds(int64_t B, int ks) { return (size_t)ks * B * kStagedCH * kStageBytes + (size_t)ks * 64 * 4; }
+
+int slices(int64_t K, int ch) {
+  const int64_t G = K / kBlock;
+  return (int)std::min<int64_t>(kMaxSlices, (G + ch - 1) / ch);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_ternary(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, float* y, hipStream_t stream) {
-  const int64_t tiles = N / 16, G = K / kBlock;
-  // split K over up to 4 waves while the tiles alone give fewer than 2048
-  // waves, keeping at least 4 groups per wave
-  int ks = 1;
-  while (ks < kWaves && tiles * ks < 2048 && G >= 8 * ks) ks *= 2;
-  const int64_t per_block = kWaves / ks;
-  const dim3 grid((unsigned)((tiles + per_block - 1) / per_block)), block(64 * kWaves);
-  const int nb4 = (int)((B + 3) / 4);
-  switch (nb4) {
-    case 1: hipLaunchKernelGGL(gemv_ternary_kernel<1>, grid, block, 0, stream, act, (int)B, codes, scales, N, K, y, ks); break;
-    case 2: hipLaunchKernelGGL(gemv_ternary_kernel<2>, grid, block, 0, stream, act, (int)B, codes, scales, N, K, y, ks); break;
-    case 3: hipLaunchKernelGGL(gemv_ternary_kernel<3>, grid, block, 0, stream, act, (int)B, codes, scales, N, K, y, ks); break;
-    default: hipLaunchKernelGGL(gemv_ternary_kernel<4>, grid, block, 0, stream, act, (int)B, codes, scales, N, K, y, ks); break;
+  const dim3 grid((unsigned)(N / 16));
+  const int b = (int)B;
+  if (B <= 4 && (K / kBlock + kStagedCH - 1) / kStagedCH <= kMaxSlices) {
+    const int ks = slices(K, kStagedCH);
+    const size_t lds = staged_lds(B, ks);
+    if (lds <= kStagedMaxLds) {
+      hipLaunchKernelGGL((gemv_staged_kernel<kStagedCH>), grid, dim3(64 * ks), lds, stream, act, b, codes, scales, N,
+                         K, y, ks);
+      return hipGetLastError();
+    }
+  }
+  switch ((B + 3) / 4) {
+    case 1: {
+      const int ks = slices(K, Chunk<1>::value);
+      hipLaunchKernelGGL((gemv_direct_kernel<1, Chunk<1>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
+                         scales, N, K, y, ks);
+      break;
+    }
+    case 2: {
+      const int ks = slices(K, Chunk<2>::value);
+      hipLaunchKernelGGL((gemv_direct_kernel<2, Chunk<2>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
+                         scales, N, K, y, ks);
+      break;
+    }
+    case 3: {
+      const int ks = slices(K, Chunk<3>::value);
+      hipLaunchKernelGGL((gemv_direct_kernel<3, Chunk<3>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
+                         scales, N, K, y, ks);
+      break;
+    }
+    default: {
+      const int ks = slices(K, Chunk<4>::value);
+      hipLaunchKernelGGL((gemv_direct_kernel<4, Chunk<4>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
+                         scales, N, K, y, ks);
+      break;
+    }
   }
   return hipGetLastError();
 }

@@ -69,6 +69,18 @@ __device__ __forceinline__ float xor_lane(float v) {
   return __int_as_float(r);
 }
 
+// Make the compiler keep `v` in vector registers up to this point.  The asm
+// exists only in the device pass: the host pass cannot parse the "v"
+// constraint and would drop the kernel's launch stub.
+template <typename T>
+__device__ __forceinline__ void keep_in_vgprs(const T& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(v));
+#else
+  (void)v;
+#endif
+}
+
 // Atomically OR `bits` into *flag once per wave (lanes with a nonzero `bits`).
 __device__ __forceinline__ void wave_flag_or(int32_t* flag, uint32_t bits) {
   if (flag == nullptr) return;
