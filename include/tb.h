@@ -54,6 +54,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Symbols of the C ABI; everything else in the library is hidden. */
+#define TB_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -97,11 +100,34 @@ typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1 } tb_format;
 /* Largest activation batch of the GEMV entry points. */
 #define TB_GEMV_MAX_BATCH 16
 
+/* Most segments one grouped call (tb_fwht128_multi, tb_ternary_gemv_multi) takes. */
+#define TB_MAX_SEGMENTS 8
+
+/* One array of a grouped tb_fwht128_multi call: arguments as in tb_fwht128. */
+typedef struct {
+  const void* x;
+  void* y;
+  int64_t rows;
+  int64_t K;
+} tb_fwht_segment;
+
+/* One product of a grouped tb_ternary_gemv_multi call: arguments as in
+ * tb_ternary_gemv. */
+typedef struct {
+  const uint8_t* act;
+  int64_t B;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  int64_t N;
+  int64_t K;
+  float* y;
+} tb_gemv_segment;
+
 /* Human-readable name of a status code (static storage, never NULL). */
-const char* tb_status_string(int status);
+TB_API const char* tb_status_string(int status);
 
 /* Library version: major * 10000 + minor * 100 + patch. */
-int tb_version(void);
+TB_API int tb_version(void);
 
 /*
  * Sizes in bytes of the packed planes of an [N][K] matrix in format `fmt`
@@ -110,7 +136,7 @@ int tb_version(void);
  * both.  Any output pointer may be NULL.  Host-only.
  * Cites the 2-bit storage of mhpq.cn/news/1159370 §3.1 and the bit ledger of §1.3.
  */
-tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
+TB_API tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
                           size_t* scale_bytes);
 
 /*
@@ -129,8 +155,18 @@ tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, siz
  *          overlap returns TB_ERR_ALIAS.
  *   rows >= 0, K a positive multiple of 128.  Arithmetic is fp32.
  */
-tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
+TB_API tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
                      void* stream);
+
+/*
+ * tb_fwht128 over up to TB_MAX_SEGMENTS independent arrays in one launch (the
+ * activations of several projections, or their outputs); same transform and
+ * rules per segment, one x_dtype / y_dtype for all.  `segs` is a host array
+ * read during the call.  Segments must not overlap one another except a
+ * segment rotating in place.  count == 0 is a no-op; count outside
+ * [0, TB_MAX_SEGMENTS] returns TB_ERR_SHAPE.
+ */
+TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype, void* stream);
 
 /*
  * Offline quantise and pack (mhpq.cn/news/1159370 §1.1-§1.3, §3.1;
@@ -150,7 +186,7 @@ tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t r
  *             (the caller zeroes it first).
  * Arithmetic is fp32; the threshold uses the unrounded scale.
  */
-tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes,
+TB_API tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes,
                            uint32_t* meta, uint16_t* scales, int32_t* err_flag, void* stream);
 
 /*
@@ -166,22 +202,32 @@ tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32
  * exactly inside the matrix instruction, blocks, sub-rows and groups are
  * accumulated in fp32.
  */
-tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
+TB_API tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, float* y, void* stream);
+
+/*
+ * tb_ternary_gemv over up to TB_MAX_SEGMENTS independent products in one
+ * launch (e.g. the projections of a layer, so that small matrices do not leave
+ * the GPU idle); each segment is validated and computed as tb_ternary_gemv.
+ * `segs` is a host array read during the call; no segment's y may overlap any
+ * segment's inputs or another y.  count == 0 is a no-op; count outside
+ * [0, TB_MAX_SEGMENTS] returns TB_ERR_SHAPE.
+ */
+TB_API tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* stream);
 
 /*
  * Bytes of the TB_ACT8 activation operand for B rows of K activations:
  * 4*B*K + B*K/8.  Host-only; 0 when K is not a positive multiple of 128 or
  * B < 0.
  */
-size_t tb_act8_bytes(int64_t B, int64_t K);
+TB_API size_t tb_act8_bytes(int64_t B, int64_t K);
 
 /*
  * Encode bf16 activations x[B][K] (already rotated) as the TB_ACT8 operand of
  * tb_ternary_gemv, without transforming them.  B >= 0 (0 is a no-op), K a
  * positive multiple of 128; act must not overlap x.
  */
-tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, void* stream);
+TB_API tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, void* stream);
 
 /*
  * Decode GEMV with 2:4 ternary weights (mhpq.cn/news/1159370 §1.2):
@@ -190,7 +236,7 @@ tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, vo
  *   meta [N][K/32], signs [N][K/64], scales [N][K/128] in the 2:4 format;
  *   B and y as tb_ternary_gemv.  Products are exact, accumulation is fp32.
  */
-tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
+TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                             const uint16_t* scales, int64_t N, int64_t K, float* y, void* stream);
 
 /*
@@ -206,7 +252,7 @@ tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, 
  * rounded (absolute error <= 2^-25); |x| >= 65520 becomes infinite and shows
  * in y.  Accumulation is fp32.
  */
-tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, void* y, int y_dtype, void* stream);
 
 #ifdef __cplusplus

@@ -32,6 +32,7 @@ CFLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
+    "-fvisibility=hidden",
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -34,14 +34,40 @@ __device__ __forceinline__ void lane_stage(float (&v)[8], int sub) {
 
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutAct8 = 2 };
 
+// A launch covers up to TB_MAX_SEGMENTS independent arrays (segments); the
+// 128-blocks are numbered across them and each 16-lane group finds the
+// segment of its block.
+struct FwhtSeg {
+  const void* x;
+  void* y;
+  int64_t nblocks, begin;
+};
+
+struct FwhtSegs {
+  FwhtSeg s[TB_MAX_SEGMENTS];
+  int count;
+  int64_t total;
+};
+
 template <bool IN_BF16, int OUT, bool XFORM>
-__global__ void __launch_bounds__(256) fwht128_kernel(const void* __restrict__ x, void* __restrict__ y,
-                                                       int64_t nblocks) {
+__global__ void __launch_bounds__(256) fwht128_kernel(FwhtSegs segs) {
   const int sub = threadIdx.x & 15;
-  for (int64_t b = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); b - (threadIdx.x >> 4) < nblocks;
-       b += (int64_t)gridDim.x * 16) {
+  for (int64_t bf = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); bf - (threadIdx.x >> 4) < segs.total;
+       bf += (int64_t)gridDim.x * 16) {
     // every lane of the wave runs the cross-lane stages; lanes past the end carry zeros
-    const bool live = b < nblocks;
+    const bool live = bf < segs.total;
+    const void* x = segs.s[0].x;
+    void* y = segs.s[0].y;
+    int64_t nblocks = segs.s[0].nblocks, begin = 0;
+#pragma unroll
+    for (int t = 1; t < TB_MAX_SEGMENTS; ++t) {
+      const bool take = t < segs.count && bf >= segs.s[t].begin;
+      x = take ? segs.s[t].x : x;
+      y = take ? segs.s[t].y : y;
+      nblocks = take ? segs.s[t].nblocks : nblocks;
+      begin = take ? segs.s[t].begin : begin;
+    }
+    const int64_t b = bf - begin;  // block inside its segment
     const int64_t base = b * kBlock + sub * 8;
     float v[8];
     if constexpr (IN_BF16) {
@@ -118,35 +144,57 @@ __global__ void __launch_bounds__(256) fwht128_kernel(const void* __restrict__ x
 }
 
 template <bool XFORM>
-hipError_t launch_blocks(const void* x, int x_dtype, void* y, int y_dtype, int64_t nblocks, hipStream_t stream) {
-  if (nblocks == 0) return hipSuccess;
-  int64_t groups = (nblocks + 15) / 16;
+hipError_t launch_segments(const FwhtSegs& segs, int x_dtype, int y_dtype, hipStream_t stream) {
+  if (segs.total == 0) return hipSuccess;
+  int64_t groups = (segs.total + 15) / 16;
   const int64_t cap = 1 << 20;
   const unsigned grid = (unsigned)(groups < cap ? groups : cap);
   const dim3 g(grid), blk(256);
   const bool ib = x_dtype == TB_BF16;
   if (y_dtype == TB_ACT8) {
-    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutAct8, XFORM>), g, blk, 0, stream, x, y, nblocks);
-    else hipLaunchKernelGGL((fwht128_kernel<false, kOutAct8, XFORM>), g, blk, 0, stream, x, y, nblocks);
+    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutAct8, XFORM>), g, blk, 0, stream, segs);
+    else hipLaunchKernelGGL((fwht128_kernel<false, kOutAct8, XFORM>), g, blk, 0, stream, segs);
   } else if (y_dtype == TB_BF16) {
-    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutBF16, XFORM>), g, blk, 0, stream, x, y, nblocks);
-    else hipLaunchKernelGGL((fwht128_kernel<false, kOutBF16, XFORM>), g, blk, 0, stream, x, y, nblocks);
+    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutBF16, XFORM>), g, blk, 0, stream, segs);
+    else hipLaunchKernelGGL((fwht128_kernel<false, kOutBF16, XFORM>), g, blk, 0, stream, segs);
   } else {
-    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutF32, XFORM>), g, blk, 0, stream, x, y, nblocks);
-    else hipLaunchKernelGGL((fwht128_kernel<false, kOutF32, XFORM>), g, blk, 0, stream, x, y, nblocks);
+    if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutF32, XFORM>), g, blk, 0, stream, segs);
+    else hipLaunchKernelGGL((fwht128_kernel<false, kOutF32, XFORM>), g, blk, 0, stream, segs);
   }
   return hipGetLastError();
+}
+
+FwhtSegs one_segment(const void* x, void* y, int64_t nblocks) {
+  FwhtSegs s{};
+  s.s[0] = FwhtSeg{x, y, nblocks, 0};
+  s.count = 1;
+  s.total = nblocks;
+  return s;
 }
 
 }  // namespace
 
 hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
                           hipStream_t stream) {
-  return launch_blocks<true>(x, x_dtype, y, y_dtype, rows * (K / kBlock), stream);
+  return launch_segments<true>(one_segment(x, y, rows * (K / kBlock)), x_dtype, y_dtype, stream);
+}
+
+hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype,
+                                hipStream_t stream) {
+  FwhtSegs s{};
+  int64_t total = 0;
+  for (int c = 0; c < count; ++c) {
+    const int64_t nb = segs[c].rows * (segs[c].K / kBlock);
+    s.s[c] = FwhtSeg{segs[c].x, segs[c].y, nb, total};
+    total += nb;
+  }
+  s.count = count;
+  s.total = total;
+  return launch_segments<true>(s, x_dtype, y_dtype, stream);
 }
 
 hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream) {
-  return launch_blocks<false>(x, TB_BF16, act, TB_ACT8, rows * (K / kBlock), stream);
+  return launch_segments<false>(one_segment(x, act, rows * (K / kBlock)), TB_BF16, TB_ACT8, stream);
 }
 
 }  // namespace tb

@@ -35,6 +35,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kMaxSlices = 16;  // waves per workgroup
+constexpr int kMaxSegs = TB_MAX_SEGMENTS;
 
 // groups per wave and chunk: a group costs 9 * NB4 + 3 registers, and a
 // workgroup of up to 16 waves leaves 128 per lane
@@ -149,127 +150,216 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint
 // and the codes with one load per group.  That is about CH + CH/2 + CH/4 + 1
 // loads for CH groups instead of 5 CH, which matters because the number of
 // loads a wave can keep in flight, not their size, bounds this kernel.
+//
+// One launch can carry up to kMaxSegs independent products (segments), e.g.
+// the projections of one layer: workgroups are numbered across segments and
+// each finds its own.  A segment splits K over ks waves (a power of two); a
+// workgroup of `waves` waves covers waves / ks tiles of it.
 constexpr int kStageBytes = 528;  // act8 bytes per group and batch row (512 values + 16 scales)
+constexpr size_t kStagedMaxLds = 96 * 1024;
+// groups per wave: 10 for one batch row, 8 when up to four rows are staged
+// (the staging registers grow with the rows)
+constexpr int staged_ch(int bmax) { return bmax == 1 ? 10 : 8; }
 
-template <int CH>
-__global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(const uint8_t* __restrict__ act, int B,
-                                                                       const uint32_t* __restrict__ codes,
-                                                                       const uint16_t* __restrict__ scales,
-                                                                       int64_t N, int64_t K,
-                                                                       float* __restrict__ y, int KS) {
+struct StagedSeg {
+  const uint8_t* act;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  float* y;
+  int64_t N, K;
+  int B, ks, wg_begin, pad;
+};
+
+struct StagedSegs {
+  StagedSeg s[kMaxSegs];
+  int count, bmax;
+};
+
+// the segment of this workgroup, selected field by field (the index is
+// uniform, so these are scalar selects on kernel arguments)
+__device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) {
+  const int wg = (int)blockIdx.x;
+  StagedSeg r = a.s[0];
+#pragma unroll
+  for (int t = 1; t < kMaxSegs; ++t) {
+    const bool take = t < a.count && wg >= a.s[t].wg_begin;
+    r.act = take ? a.s[t].act : r.act;
+    r.codes = take ? a.s[t].codes : r.codes;
+    r.scales = take ? a.s[t].scales : r.scales;
+    r.y = take ? a.s[t].y : r.y;
+    r.N = take ? a.s[t].N : r.N;
+    r.K = take ? a.s[t].K : r.K;
+    r.B = take ? a.s[t].B : r.B;
+    r.ks = take ? a.s[t].ks : r.ks;
+    r.wg_begin = take ? a.s[t].wg_begin : r.wg_begin;
+  }
+  return r;
+}
+
+template <int CH, int BMAX>
+__global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs segs) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const StagedSeg sg = pick_segment(segs);
+  const uint8_t* __restrict__ act = sg.act;
+  const int B = sg.B, KS = sg.ks;
+  const int64_t N = sg.N, K = sg.K;
+  const int waves = (int)(blockDim.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = w % KS;
   const int i = lane & 15, q = lane >> 4;
-  const int64_t nb = blockIdx.x;
+  const int64_t nb = (int64_t)(blockIdx.x - sg.wg_begin) * (waves / KS) + w / KS;
+  const bool live = nb < N / 16;
   const int G = (int)(K / kBlock);
   const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
   const int n = ge - gb;  // 1 .. CH groups in this slice
   constexpr int kPairs = (CH + 1) / 2;
   constexpr int kScaleRegs = (CH + 3) / 4;
-  unsigned char* st = smem + (size_t)ks * B * CH * kStageBytes;  // [B][CH][512] values, then [B][CH][16] scales
+  const size_t region = (size_t)segs.bmax * CH * kStageBytes;
+  unsigned char* st = smem + (size_t)w * region;  // [B][CH][512] values, then [B][CH][16] scales
   unsigned char* st_sc = st + (size_t)B * CH * 512;
-  float* red = reinterpret_cast<float*>(smem + (size_t)KS * B * CH * kStageBytes);
+  float* red = reinterpret_cast<float*>(smem + (size_t)waves * region);
 
-  // 1. activation slice (issued first: it is waited for first)
-  u32x4 av_st[4][kPairs];
-  u32x4 as_st[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const unsigned char* src = act + ((size_t)b * G + gb) * 512;
-#pragma unroll
-    for (int t = 0; t < kPairs; ++t) {
-      const int off = t * 1024 + lane * 16;
-      if (b < B && off < n * 512) av_st[b][t] = *reinterpret_cast<const u32x4*>(src + off);
-    }
-    if (b < B && lane < n)
-      as_st[b] = *reinterpret_cast<const u32x4*>(act + (size_t)4 * B * K + ((size_t)b * G + gb + lane) * 16);
-  }
-  // 2. codes, one 8-byte load per lane and group (slots past the slice repeat its last group)
-  const uint32_t* cp = codes + (size_t)nb * G * 128 + 2 * lane;
-  u32x2 cw[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128);
-  // 3. weight scales: lane (i, q) holds row i's scale of groups gb + 4r + q
-  const uint16_t* sp = scales + (size_t)(16 * nb + i) * G;
-  uint32_t sr[kScaleRegs];
-#pragma unroll
-  for (int r = 0; r < kScaleRegs; ++r) sr[r] = sp[min(gb + 4 * r + q, ge - 1)];
-  // 4. activation slice into this wave's LDS area (read back by other lanes of
-  //    the same wave only; LDS operations of a wave complete in order)
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-#pragma unroll
-    for (int t = 0; t < kPairs; ++t) {
-      const int off = t * 1024 + lane * 16;
-      if (b < B && off < n * 512) *reinterpret_cast<u32x4*>(st + (size_t)b * CH * 512 + off) = av_st[b][t];
-    }
-    if (b < B && lane < n) *reinterpret_cast<u32x4*>(st_sc + ((size_t)b * CH + lane) * 16) = as_st[b];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // 5. the products: lane (i, q) feeds A rows of batch i / 4, sub-row i % 4.
-  //    Rows of batches >= B only reach output rows that are never stored, so
-  //    those lanes read the last batch row instead of branching.
-  const int bp = min(i >> 2, B - 1);
-  const unsigned char* a_src = st + (size_t)bp * CH * 512 + ((i & 3) * 4 + q) * 32;
-  const unsigned char* a_sc = st_sc + (size_t)bp * CH * 16 + (i & 3) * 4 + q;
   float acc = 0.f;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    // 1. activation slice (issued first: it is waited for first)
+    u32x4 av_st[BMAX][kPairs];
+    u32x4 as_st[BMAX];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(a_src + j * 512);
-    const u32x4 lo = p[0], hi = p[1];
-    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    const int as = a_sc[j * 16];
-    const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * (j & 3)) * 4, (int)sr[j >> 2]);
-    const float s = f16_bits_to_f32((uint32_t)sbits & 0xFFFFu) * 0.5f;
-    const uint32_t w0 = cw[j][0], w1 = cw[j][1];
-    const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
-                      (int)((w1 << 2) & 0xCCCCCCCCu)};
-    const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
-    const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, zero, 0, 4, 0, as, 0, 127);
-    keep_in_vgprs(av);
-    keep_in_vgprs(bw);
-    const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc);
-    acc = j < n ? a : acc;  // slots past the slice add nothing
+    for (int b = 0; b < BMAX; ++b) {
+      const unsigned char* src = act + ((size_t)b * G + gb) * 512;
+#pragma unroll
+      for (int t = 0; t < kPairs; ++t) {
+        const int off = t * 1024 + lane * 16;
+        if (b < B && off < n * 512) av_st[b][t] = *reinterpret_cast<const u32x4*>(src + off);
+      }
+      if (b < B && lane < n)
+        as_st[b] = *reinterpret_cast<const u32x4*>(act + (size_t)4 * B * K + ((size_t)b * G + gb + lane) * 16);
+    }
+    // 2. codes, one 8-byte load per lane and group (slots past the slice repeat its last group)
+    const uint32_t* cp = sg.codes + (size_t)nb * G * 128 + 2 * lane;
+    u32x2 cw[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128);
+    // 3. weight scales: lane (i, q) holds row i's scale of groups gb + 4r + q
+    const uint16_t* sp = sg.scales + (size_t)(16 * nb + i) * G;
+    uint32_t sr[kScaleRegs];
+#pragma unroll
+    for (int r = 0; r < kScaleRegs; ++r) sr[r] = sp[min(gb + 4 * r + q, ge - 1)];
+    // 4. activation slice into this wave's LDS area (read back by other lanes of
+    //    the same wave only; LDS operations of a wave complete in order)
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+#pragma unroll
+      for (int t = 0; t < kPairs; ++t) {
+        const int off = t * 1024 + lane * 16;
+        if (b < B && off < n * 512) *reinterpret_cast<u32x4*>(st + (size_t)b * CH * 512 + off) = av_st[b][t];
+      }
+      if (b < B && lane < n) *reinterpret_cast<u32x4*>(st_sc + ((size_t)b * CH + lane) * 16) = as_st[b];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // 5. the products: lane (i, q) feeds A rows of batch i / 4, sub-row i % 4.
+    //    Rows of batches >= B only reach output rows that are never stored, so
+    //    those lanes read the last batch row instead of branching.
+    const int bp = min(i >> 2, B - 1);
+    const unsigned char* a_src = st + (size_t)bp * CH * 512 + ((i & 3) * 4 + q) * 32;
+    const unsigned char* a_sc = st_sc + (size_t)bp * CH * 16 + (i & 3) * 4 + q;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(a_src + j * 512);
+      const u32x4 lo = p[0], hi = p[1];
+      const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const int as = a_sc[j * 16];
+      const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * (j & 3)) * 4, (int)sr[j >> 2]);
+      const float s = f16_bits_to_f32((uint32_t)sbits & 0xFFFFu) * 0.5f;
+      const uint32_t w0 = cw[j][0], w1 = cw[j][1];
+      const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
+                        (int)((w1 << 2) & 0xCCCCCCCCu)};
+      const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
+      const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, zero, 0, 4, 0, as, 0, 127);
+      keep_in_vgprs(av);
+      keep_in_vgprs(bw);
+      const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc);
+      acc = j < n ? a : acc;  // slots past the slice add nothing
+    }
   }
 
   if (KS > 1) {
-    red[ks * 64 + lane] = acc;
+    red[w * 64 + lane] = acc;
     __syncthreads();
     if (ks != 0) return;
-    for (int w = 1; w < KS; ++w) acc += red[w * 64 + lane];
+    for (int u = 1; u < KS; ++u) acc += red[(w + u) * 64 + lane];
   }
-  if (q < B) y[(size_t)q * N + 16 * nb + i] = acc;
+  if (live && q < B) sg.y[(size_t)q * N + 16 * nb + i] = acc;
 }
-
-constexpr int kStagedCH = 10;
-constexpr size_t kStagedMaxLds = 96 * 1024;
-
-size_t staged_lds(int64_t B, int ks) { return (size_t)ks * B * kStagedCH * kStageBytes + (size_t)ks * 64 * 4; }
 
 int slices(int64_t K, int ch) {
   const int64_t G = K / kBlock;
   return (int)std::min<int64_t>(kMaxSlices, (G + ch - 1) / ch);
 }
 
+// K slices of a staged segment: the smallest power of two giving at most ch
+// groups per wave, or 0 when even kMaxSlices waves are too few
+int staged_slices(int64_t K, int ch) {
+  const int64_t G = K / kBlock;
+  for (int ks = 1; ks <= kMaxSlices; ks *= 2)
+    if (G <= (int64_t)ks * ch) return ks;
+  return 0;
+}
+
 }  // namespace
 
-hipError_t launch_gemv_ternary(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                               int64_t N, int64_t K, float* y, hipStream_t stream) {
+hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream) {
+  // one grouped launch when every segment fits the staged path together, else
+  // each segment on its own exactly as a single call would run it (so a
+  // segment's result never depends on what it was grouped with)
+  StagedSegs st{};
+  bool staged = count <= kMaxSegs;
+  int bmax = 1;
+  for (int c = 0; c < count; ++c) bmax = std::max(bmax, (int)segs[c].B);
+  const int ch = staged_ch(bmax);
+  int waves = 1, wg = 0;
+  for (int c = 0; c < count && staged; ++c) {
+    const int ks = staged_slices(segs[c].K, ch);
+    if (segs[c].B > 4 || ks == 0) staged = false;
+    waves = std::max(waves, ks);
+  }
+  const size_t lds = (size_t)waves * bmax * ch * kStageBytes + (size_t)waves * 64 * sizeof(float);
+  if (staged && lds <= kStagedMaxLds) {
+    for (int c = 0; c < count; ++c) {
+      const int ks = staged_slices(segs[c].K, ch);
+      const int64_t tiles = segs[c].N / 16, per_wg = waves / ks;
+      st.s[c] = StagedSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
+                          (int)segs[c].B, ks, wg, 0};
+      wg += (int)((tiles + per_wg - 1) / per_wg);
+    }
+    st.count = count;
+    st.bmax = bmax;
+    // batch 1 gets its own instantiation: four rows of staging registers would
+    // halve the waves a SIMD can hold
+    if (bmax == 1)
+      hipLaunchKernelGGL((gemv_staged_kernel<staged_ch(1), 1>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
+    else
+      hipLaunchKernelGGL((gemv_staged_kernel<staged_ch(4), 4>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
+    return hipGetLastError();
+  }
+  if (count == 1)
+    return launch_gemv_direct(segs[0].act, segs[0].B, segs[0].codes, segs[0].scales, segs[0].N, segs[0].K,
+                              segs[0].y, stream);
+  for (int c = 0; c < count; ++c) {
+    const hipError_t e = launch_gemv_multi(segs + c, 1, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemv_direct(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                              int64_t N, int64_t K, float* y, hipStream_t stream) {
   const dim3 grid((unsigned)(N / 16));
   const int b = (int)B;
-  if (B <= 4 && (K / kBlock + kStagedCH - 1) / kStagedCH <= kMaxSlices) {
-    const int ks = slices(K, kStagedCH);
-    const size_t lds = staged_lds(B, ks);
-    if (lds <= kStagedMaxLds) {
-      hipLaunchKernelGGL((gemv_staged_kernel<kStagedCH>), grid, dim3(64 * ks), lds, stream, act, b, codes, scales, N,
-                         K, y, ks);
-      return hipGetLastError();
-    }
-  }
   switch ((B + 3) / 4) {
     case 1: {
       const int ks = slices(K, Chunk<1>::value);
@@ -297,6 +387,12 @@ hipError_t launch_gemv_ternary(const uint8_t* act, int64_t B, const uint32_t* co
     }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_ternary(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                               int64_t N, int64_t K, float* y, hipStream_t stream) {
+  const GemvSegment seg{act, B, codes, scales, N, K, y};
+  return launch_gemv_multi(&seg, 1, stream);
 }
 
 }  // namespace tb

@@ -28,6 +28,37 @@ tb_status launched(hipError_t e) { return e == hipSuccess ? TB_OK : TB_ERR_LAUNC
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// byte sizes of one FWHT segment's input and output
+size_t fwht_in_bytes(int64_t rows, int64_t K, int x_dtype) { return (size_t)rows * (size_t)K * dtype_bytes(x_dtype); }
+size_t fwht_out_bytes(int64_t rows, int64_t K, int y_dtype) {
+  const size_t n = (size_t)rows * (size_t)K;
+  return y_dtype == TB_ACT8 ? act8_bytes(n) : n * dtype_bytes(y_dtype);
+}
+
+tb_status check_fwht(const void* x, int x_dtype, const void* y, int y_dtype, int64_t rows, int64_t K) {
+  if (!dtype_ok(x_dtype) || !(dtype_ok(y_dtype) || y_dtype == TB_ACT8)) return TB_ERR_DTYPE;
+  if (rows < 0 || K <= 0 || K % kGroup) return TB_ERR_SHAPE;
+  if (rows == 0) return TB_OK;
+  if (!x || !y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return TB_ERR_ALIGN;
+  if (x == y && x_dtype != y_dtype) return TB_ERR_ALIAS;
+  if (x != y && overlap(x, fwht_in_bytes(rows, K, x_dtype), y, fwht_out_bytes(rows, K, y_dtype))) return TB_ERR_ALIAS;
+  return TB_OK;
+}
+
+tb_status check_gemv(const tb_gemv_segment& g) {
+  if (!dims_ok(g.N, g.K) || g.B < 0 || g.B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+  if (g.B == 0) return TB_OK;
+  if (!g.act || !g.codes || !g.scales || !g.y) return TB_ERR_NULL;
+  if (!aligned16(g.act) || !aligned16(g.codes) || !aligned16(g.scales) || !aligned16(g.y)) return TB_ERR_ALIGN;
+  const size_t nk = (size_t)g.N * (size_t)g.K, yb = (size_t)g.B * (size_t)g.N * 4;
+  if (overlap(g.y, yb, g.act, act8_bytes((size_t)g.B * g.K)) || overlap(g.y, yb, g.codes, nk / 4) ||
+      overlap(g.y, yb, g.scales, nk / 64))
+    return TB_ERR_ALIAS;
+  return TB_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -66,16 +97,33 @@ tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, siz
 }
 
 tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K, void* stream) {
-  if (!dtype_ok(x_dtype) || !(dtype_ok(y_dtype) || y_dtype == TB_ACT8)) return TB_ERR_DTYPE;
-  if (rows < 0 || K <= 0 || K % kGroup) return TB_ERR_SHAPE;
-  if (rows == 0) return TB_OK;
-  if (!x || !y) return TB_ERR_NULL;
-  if (!aligned16(x) || !aligned16(y)) return TB_ERR_ALIGN;
-  const size_t n = (size_t)rows * (size_t)K;
-  const size_t yb = y_dtype == TB_ACT8 ? act8_bytes(n) : n * dtype_bytes(y_dtype);
-  if (x == y && x_dtype != y_dtype) return TB_ERR_ALIAS;
-  if (x != y && overlap(x, n * dtype_bytes(x_dtype), y, yb)) return TB_ERR_ALIAS;
+  const tb_status st = check_fwht(x, x_dtype, y, y_dtype, rows, K);
+  if (st != TB_OK || rows == 0) return st;
   return launched(tb::launch_fwht128(x, x_dtype, y, y_dtype, rows, K, as_stream(stream)));
+}
+
+tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype, void* stream) {
+  if (count < 0 || count > TB_MAX_SEGMENTS) return TB_ERR_SHAPE;
+  if (!dtype_ok(x_dtype) || !(dtype_ok(y_dtype) || y_dtype == TB_ACT8)) return TB_ERR_DTYPE;
+  if (count == 0) return TB_OK;
+  if (!segs) return TB_ERR_NULL;
+  tb_fwht_segment live[TB_MAX_SEGMENTS];
+  int n = 0;
+  for (int c = 0; c < count; ++c) {
+    const tb_fwht_segment& a = segs[c];
+    const tb_status st = check_fwht(a.x, x_dtype, a.y, y_dtype, a.rows, a.K);
+    if (st != TB_OK) return st;
+    for (int d = 0; d < c; ++d) {
+      const tb_fwht_segment& b = segs[d];
+      if (a.rows == 0 || b.rows == 0) continue;
+      const size_t ai = fwht_in_bytes(a.rows, a.K, x_dtype), ao = fwht_out_bytes(a.rows, a.K, y_dtype);
+      const size_t bi = fwht_in_bytes(b.rows, b.K, x_dtype), bo = fwht_out_bytes(b.rows, b.K, y_dtype);
+      if (overlap(a.y, ao, b.y, bo) || overlap(a.y, ao, b.x, bi) || overlap(b.y, bo, a.x, ai)) return TB_ERR_ALIAS;
+    }
+    if (a.rows > 0) live[n++] = a;
+  }
+  if (n == 0) return TB_OK;
+  return launched(tb::launch_fwht128_multi(live, n, x_dtype, y_dtype, as_stream(stream)));
 }
 
 tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
@@ -106,15 +154,36 @@ tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, vo
 
 tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
                           int64_t K, float* y, void* stream) {
-  if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
-  if (B == 0) return TB_OK;
-  if (!act || !codes || !scales || !y) return TB_ERR_NULL;
-  if (!aligned16(act) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return TB_ERR_ALIGN;
-  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)B * (size_t)N * 4;
-  if (overlap(y, yb, act, act8_bytes((size_t)B * K)) || overlap(y, yb, codes, nk / 4) ||
-      overlap(y, yb, scales, nk / 64))
-    return TB_ERR_ALIAS;
+  const tb_gemv_segment g{act, B, codes, scales, N, K, y};
+  const tb_status st = check_gemv(g);
+  if (st != TB_OK || B == 0) return st;
   return launched(tb::launch_gemv_ternary(act, B, codes, scales, N, K, y, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* stream) {
+  if (count < 0 || count > TB_MAX_SEGMENTS) return TB_ERR_SHAPE;
+  if (count == 0) return TB_OK;
+  if (!segs) return TB_ERR_NULL;
+  tb_gemv_segment live[TB_MAX_SEGMENTS];
+  int n = 0;
+  for (int c = 0; c < count; ++c) {
+    const tb_gemv_segment& a = segs[c];
+    const tb_status st = check_gemv(a);
+    if (st != TB_OK) return st;
+    if (a.B == 0) continue;
+    const size_t ay = (size_t)a.B * (size_t)a.N * 4;
+    for (int d = 0; d < count; ++d) {
+      const tb_gemv_segment& b = segs[d];
+      if (d == c || b.B == 0) continue;
+      const size_t nk = (size_t)b.N * (size_t)b.K;
+      if (overlap(a.y, ay, b.act, act8_bytes((size_t)b.B * b.K)) || overlap(a.y, ay, b.codes, nk / 4) ||
+          overlap(a.y, ay, b.scales, nk / 64) || (d < c && overlap(a.y, ay, b.y, (size_t)b.B * (size_t)b.N * 4)))
+        return TB_ERR_ALIAS;
+    }
+    live[n++] = a;
+  }
+  if (n == 0) return TB_OK;
+  return launched(tb::launch_gemv_multi(live, n, as_stream(stream)));
 }
 
 tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,

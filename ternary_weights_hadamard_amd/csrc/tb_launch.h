@@ -5,15 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tb.h"
+
 namespace tb {
 
 hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
                           hipStream_t stream);
+hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype,
+                                hipStream_t stream);
 hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
                               uint16_t* scales, int32_t* err_flag, hipStream_t stream);
 hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream);
+typedef tb_gemv_segment GemvSegment;
 hipError_t launch_gemv_ternary(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, float* y, hipStream_t stream);
+hipError_t launch_gemv_direct(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                              int64_t N, int64_t K, float* y, hipStream_t stream);
+hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream);
 hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                                  const uint16_t* scales, int64_t N, int64_t K, float* y, hipStream_t stream);
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

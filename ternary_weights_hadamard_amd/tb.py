@@ -26,6 +26,7 @@ TB_F32, TB_BF16, TB_ACT8 = 0, 1, 2
 TB_FMT_DENSE, TB_FMT_24 = 0, 1
 TB_EFLAG_NONFINITE, TB_EFLAG_SCALE_OVF = 1, 2
 TB_GEMV_MAX_BATCH = 16
+TB_MAX_SEGMENTS = 8
 
 _lib = None
 
@@ -33,12 +34,23 @@ _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _int = ctypes.c_int
 
+class FwhtSegment(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("rows", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class GemvSegment(ctypes.Structure):
+    _fields_ = [("act", ctypes.c_void_p), ("B", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
 SIGNATURES = {
     "tb_status_string": (ctypes.c_char_p, [_int]),
     "tb_version": (_int, []),
     "tb_packed_bytes": (_int, [_int, _i64, _i64, ctypes.POINTER(ctypes.c_size_t),
                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "tb_fwht128": (_int, [_vp, _int, _vp, _int, _i64, _i64, _vp]),
+    "tb_fwht128_multi": (_int, [ctypes.POINTER(FwhtSegment), _int, _int, _int, _vp]),
+    "tb_ternary_gemv_multi": (_int, [ctypes.POINTER(GemvSegment), _int, _vp]),
     "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "tb_ternary_gemv": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
     "tb_act8_bytes": (ctypes.c_size_t, [_i64, _i64]),
@@ -130,6 +142,21 @@ def tb_fwht128(x, y=None, out_dtype=None, stream=None):
     return y
 
 
+def tb_fwht128_multi(pairs, stream=None):
+    """One launch rotating several arrays: pairs = [(x, y), ...] with a common
+    input dtype and a common output dtype (a uint8 y means the act8 operand)."""
+    if not pairs:
+        return
+    for x, y in pairs:
+        _dev(x, y)
+    arr = (FwhtSegment * len(pairs))()
+    for c, (x, y) in enumerate(pairs):
+        rows = x.numel() // x.shape[-1] if x.numel() else 0
+        arr[c] = FwhtSegment(x.data_ptr(), y.data_ptr(), rows, x.shape[-1])
+    _check(lib().tb_fwht128_multi(arr, len(pairs), _dt(pairs[0][0]), _dt(pairs[0][1]), _stream(stream)),
+           "tb_fwht128_multi")
+
+
 def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, err_flag=None, stream=None):
     """Quantise fp32 W [N, K]; returns (codes, meta, scales).  For TB_FMT_24 `codes` is the sign plane."""
     _dev(w)
@@ -171,6 +198,18 @@ def tb_ternary_gemv(act, codes, scales, batch, y=None, stream=None):
     _check(lib().tb_ternary_gemv(_p(act), int(batch), _p(codes), _p(scales), n, k, _p(y), _stream(stream)),
            "tb_ternary_gemv")
     return y
+
+
+def tb_ternary_gemv_multi(segments, stream=None):
+    """One launch of several GEMVs: segments = [(act, codes, scales, batch, y), ...]."""
+    if not segments:
+        return
+    arr = (GemvSegment * len(segments))()
+    for c, (act, codes, scales, batch, y) in enumerate(segments):
+        _dev(act, codes, scales, y)
+        n, g = scales.shape
+        arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n, g * 128, y.data_ptr())
+    _check(lib().tb_ternary_gemv_multi(arr, len(segments), _stream(stream)), "tb_ternary_gemv_multi")
 
 
 def tb_ternary24_gemv(x, meta, signs, scales, y=None, stream=None):

@@ -120,6 +120,34 @@ def test_gemv_validation():
     assert L.tb_ternary24_gemv(_v(A), 20, _v(B), _v(C), _v(D), 128, 384, _v(A), s) == 2
 
 
+def test_grouped_validation():
+    L = tb.lib()
+    s = None
+    F, Gs = tb.FwhtSegment, tb.GemvSegment
+    fw = (F * 2)(F(A, B, 1, 128), F(C, D, 1, 128))
+    assert L.tb_fwht128_multi(fw, 9, 1, 1, s) == 2                 # more than TB_MAX_SEGMENTS
+    assert L.tb_fwht128_multi(fw, -1, 1, 1, s) == 2
+    assert L.tb_fwht128_multi(fw, 0, 1, 1, s) == 0                 # empty group
+    assert L.tb_fwht128_multi(None, 2, 1, 1, s) == 1
+    assert L.tb_fwht128_multi(fw, 2, 7, 1, s) == 4
+    bad = (F * 2)(F(A, B, 1, 128), F(C, D, 1, 100))
+    assert L.tb_fwht128_multi(bad, 2, 1, 1, s) == 2                # one bad segment fails the call
+    clash = (F * 2)(F(A, B, 1, 128), F(C, B + 64, 1, 128))
+    assert L.tb_fwht128_multi(clash, 2, 1, 1, s) == 8              # outputs overlap each other
+    reads = (F * 2)(F(A, B, 1, 128), F(B, D, 1, 128))
+    assert L.tb_fwht128_multi(reads, 2, 1, 1, s) == 8              # one writes what another reads
+    gv = (Gs * 2)(Gs(A, 1, B, C, 128, 128, D), Gs(A, 1, B, C, 128, 128, D + 4096))
+    assert L.tb_ternary_gemv_multi(gv, 9, s) == 2
+    assert L.tb_ternary_gemv_multi(gv, 0, s) == 0
+    assert L.tb_ternary_gemv_multi(None, 1, s) == 1
+    same_y = (Gs * 2)(Gs(A, 1, B, C, 128, 128, D), Gs(A, 1, B, C, 128, 128, D))
+    assert L.tb_ternary_gemv_multi(same_y, 2, s) == 8              # two products into one y
+    y_over_in = (Gs * 2)(Gs(A, 1, B, C, 128, 128, D), Gs(D, 1, B, C, 128, 128, D + 4096))
+    assert L.tb_ternary_gemv_multi(y_over_in, 2, s) == 8           # a y is another's act
+    shape = (Gs * 1)(Gs(A, 17, B, C, 128, 128, D))
+    assert L.tb_ternary_gemv_multi(shape, 1, s) == 2
+
+
 def test_gemm_validation():
     L = tb.lib()
     s = None

@@ -213,3 +213,42 @@ def test_gemv24_exact_and_dense_equivalence():
     ref = oracle.matvec.gemv24(x, meta, signs, sc, k)
     assert np.array_equal(y24.cpu().numpy().astype(np.float64), ref)
     assert np.array_equal(yd.cpu().numpy(), y24.cpu().numpy())
+
+
+# ---------------------------------------------------------------- grouped launches
+
+@pytest.mark.parametrize("b", [1, 3])
+def test_grouped_fwht_and_gemv_equal_single_calls(b):
+    # shapes with different K-slice counts in one launch (G = 40, 5, 17, 136)
+    shapes = [(1920, 5120), (640, 640), (768, 2176), (128, 17408)]
+    say(f"grouped fwht + gemv, B={b}")
+    xs, segs, singles = [], [], []
+    for c, (n, k) in enumerate(shapes):
+        codes = synth.random_code_words(n, k, seed=70 + c)
+        scales = synth.random_scales_f16(n, k, seed=80 + c)
+        x = synth.gaussian_bf16((b, k), seed=90 + c)
+        xs.append((bf16_dev(x), u32_dev(codes), f16_dev(scales), x, codes, scales))
+    acts = [torch.empty(tb.tb_act8_bytes(b, x.shape[1]), dtype=torch.uint8, device=DEV) for _, _, _, x, _, _ in xs]
+    tb.tb_fwht128_multi([(xd, a) for (xd, *_), a in zip(xs, acts)])
+    ys = [torch.empty((b, n), dtype=torch.float32, device=DEV) for n, _ in shapes]
+    tb.tb_ternary_gemv_multi([(a, cd, sc, b, y) for a, (_, cd, sc, *_), y in zip(acts, xs, ys)])
+    torch.cuda.synchronize()
+    for c, ((xd, cd, sc, x, codes, scales), a, y) in enumerate(zip(xs, acts, ys)):
+        a1 = tb.tb_fwht128(xd, out_dtype=torch.uint8)
+        y1 = tb.tb_ternary_gemv(a1, cd, sc, b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, a1), f"segment {c}: grouped rotation differs from the single call"
+        assert torch.equal(y, y1), f"segment {c}: grouped GEMV differs from the single call"
+        k = x.shape[1]
+        xr = oracle.numerics.f64_to_bf16_bits(oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(x)))
+        assert_close(y.cpu().numpy(), oracle.matvec.gemv(xr, codes, scales, k), f"grouped segment {c} vs oracle")
+
+
+def test_grouped_output_rotation_f32():
+    shapes = [(2, 384), (2, 17408), (2, 1024)]
+    xs = [torch.randn(s, dtype=torch.float32, device=DEV) for s in shapes]
+    ys = [torch.empty_like(x) for x in xs]
+    tb.tb_fwht128_multi(list(zip(xs, ys)))
+    torch.cuda.synchronize()
+    for x, y in zip(xs, ys):
+        assert torch.equal(y, tb.tb_fwht128(x))
