@@ -48,7 +48,7 @@ def packed_bytes(n, k):
 
 
 class DecodeStack:
-    def __init__(self, layers, batch, gen, dev, grouping="layer"):
+    def __init__(self, layers, batch, gen, dev, grouping="split"):
         import torch
 
         from ternary_weights_hadamard_amd import synth
@@ -84,6 +84,9 @@ class DecodeStack:
         segs = [(self.act[j], codes, scales, self.batch, self.yr[j]) for j, (codes, scales, n, k) in enumerate(layer)]
         if self.grouping == "layer":
             tb.tb_ternary_gemv_multi(segs)
+        elif self.grouping == "none":
+            for sg in segs:
+                tb.tb_ternary_gemv_multi([sg])
         else:
             tb.tb_ternary_gemv_multi([s for s, (_, _, _, k) in zip(segs, layer) if k == D])
             tb.tb_ternary_gemv_multi([s for s, (_, _, _, k) in zip(segs, layer) if k != D])
@@ -115,7 +118,7 @@ class DecodeStack:
         launches per step)."""
         ms, _, g = time_graph(self.gemv_only, replays, 1)
         del g
-        per_layer = 1 if self.grouping == "layer" else 2
+        per_layer = {"layer": 1, "split": 2, "none": 4}[self.grouping]
         nl = per_layer * len(self.w)
         per_launch_bytes = sum(gemv_bytes(n, k, self.batch) for _, _, n, k in self.w[0]) / per_layer
         return per_launch_bytes, ms / (replays * nl), nl
@@ -288,8 +291,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the extra phases")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="fewer iterations in the extra phases")
-    ap.add_argument("--grouping", choices=("layer", "split"), default="layer",
-                    help="GEMV launches per layer: one over all four matrices, or two")
+    ap.add_argument("--grouping", choices=("layer", "split", "none"), default="split",
+                    help="GEMV launches per layer: one over all four matrices, two (d_model-input ones, then down), or one per matrix")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -158,8 +158,12 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint
 constexpr int kStageBytes = 528;  // act8 bytes per group and batch row (512 values + 16 scales)
 constexpr size_t kStagedMaxLds = 96 * 1024;
 // groups per wave: 10 for one batch row, 8 when up to four rows are staged
-// (the staging registers grow with the rows)
+// (the staging registers grow with the rows).  A batch-1 group whose longest
+// K would need more than 8 waves per tile takes 18 groups per wave instead:
+// 8-wave workgroups of at most 76 KB LDS, two per CU, rather than 16-wave
+// ones that fit only once per CU.
 constexpr int staged_ch(int bmax) { return bmax == 1 ? 10 : 8; }
+constexpr int kLongCH = 18;
 
 struct StagedSeg {
   const uint8_t* act;
@@ -312,25 +316,35 @@ int staged_slices(int64_t K, int ch) {
 
 }  // namespace
 
+// Groups per wave of one segment, a function of its own K and B only, so that
+// a segment is cut into the same K slices (and summed in the same order)
+// whatever it is launched with.
+int segment_ch(int64_t K, int64_t B) {
+  if (B > 1) return staged_ch(4);
+  const int ks = staged_slices(K, staged_ch(1));
+  return ks != 0 && ks <= 8 ? staged_ch(1) : kLongCH;
+}
+
 hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream) {
   // one grouped launch when every segment fits the staged path together, else
-  // each segment on its own exactly as a single call would run it (so a
-  // segment's result never depends on what it was grouped with)
+  // each segment on its own exactly as a single call would run it
   StagedSegs st{};
   bool staged = count <= kMaxSegs;
-  int bmax = 1;
-  for (int c = 0; c < count; ++c) bmax = std::max(bmax, (int)segs[c].B);
-  const int ch = staged_ch(bmax);
-  int waves = 1, wg = 0;
+  int bmax = 1, ch = 1, waves = 1, wg = 0;
   for (int c = 0; c < count && staged; ++c) {
-    const int ks = staged_slices(segs[c].K, ch);
+    const int sc = segment_ch(segs[c].K, segs[c].B);
+    const int ks = staged_slices(segs[c].K, sc);
     if (segs[c].B > 4 || ks == 0) staged = false;
+    bmax = std::max(bmax, (int)segs[c].B);
+    ch = std::max(ch, sc);
     waves = std::max(waves, ks);
   }
+  // kernels exist for (10, 1), (18, 1) and (8, up to 4 rows)
+  if (bmax > 1 && ch != staged_ch(4)) staged = false;
   const size_t lds = (size_t)waves * bmax * ch * kStageBytes + (size_t)waves * 64 * sizeof(float);
   if (staged && lds <= kStagedMaxLds) {
     for (int c = 0; c < count; ++c) {
-      const int ks = staged_slices(segs[c].K, ch);
+      const int ks = staged_slices(segs[c].K, segment_ch(segs[c].K, segs[c].B));
       const int64_t tiles = segs[c].N / 16, per_wg = waves / ks;
       st.s[c] = StagedSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
                           (int)segs[c].B, ks, wg, 0};
@@ -338,9 +352,9 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
     }
     st.count = count;
     st.bmax = bmax;
-    // batch 1 gets its own instantiation: four rows of staging registers would
-    // halve the waves a SIMD can hold
-    if (bmax == 1)
+    if (bmax == 1 && ch == kLongCH)
+      hipLaunchKernelGGL((gemv_staged_kernel<kLongCH, 1>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
+    else if (bmax == 1)
       hipLaunchKernelGGL((gemv_staged_kernel<staged_ch(1), 1>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
     else
       hipLaunchKernelGGL((gemv_staged_kernel<staged_ch(4), 4>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
