@@ -38,6 +38,39 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+GEMV_SOURCES = ("ternary_weights_hadamard_amd/csrc/gemv_ternary.hip", "ternary_weights_hadamard_amd/csrc/tb_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_batch1_hbm_traffic.txt")
+CALIB_BYTES = 256 << 20  # plain copy used to calibrate the byte counters
+
+
+def gemv_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per GEMV launch from the committed counter summary, or None when
+    it is missing or was taken on other GEMV sources than the current ones."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("gemv_source_hash") != gemv_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def gemv_bytes(n, k, b):
     """Algorithmic bytes of one GEMV launch: codes + scales + activations + output."""
     return n * k // 4 + n * k // 64 + 2 * b * k + 4 * b * n
@@ -103,6 +136,17 @@ class DecodeStack:
             tb.tb_fwht128_multi(rot_in)
             self.gemv_calls(layer)
             tb.tb_fwht128_multi(rot_out)
+
+    def step_sequential(self):
+        """The same work in the order a decoder layer imposes: every projection's
+        rotation, GEMV and back-rotation one after the other, one launch each."""
+        from ternary_weights_hadamard_amd import tb
+
+        for layer in self.w:
+            for j, (codes, scales, n, k) in enumerate(layer):
+                tb.tb_fwht128(self.x[j], y=self.act[j])
+                tb.tb_ternary_gemv(self.act[j], codes, scales, self.batch, y=self.yr[j])
+                tb.tb_fwht128(self.yr[j], y=self.y[j])
 
     def gemv_only(self):
         for layer in self.w:
@@ -244,6 +288,98 @@ def extra_phases(gen, dev, quick):
     return out
 
 
+def profile_pass(dev):
+    """Short run for the counter passes: a 4-layer stack (weights beyond the
+    256 MB last-level cache), every layer's grouped GEMV launches 3 times round
+    robin, then a plain copy of CALIB_BYTES for the counter calibration."""
+    import torch
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    stack = DecodeStack(4, 1, gen, dev, "split")
+    stack.step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        stack.gemv_only()
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    per_launch = sum(gemv_bytes(n, k, 1) for _, _, n, k in stack.w[0]) / 2
+    print(json.dumps({"profile_pass": True, "gemv_launches": 3 * 2 * 4, "algorithmic_bytes_per_launch": per_launch,
+                      "calibration_copy_bytes": CALIB_BYTES}), flush=True)
+
+
+def summarize_counters(fetch_dir, write_dir, out_path, commands):
+    """Turn the FETCH_SIZE and WRITE_SIZE passes of profile_pass into HBM bytes
+    per GEMV launch: each counter is scaled by what it reads for the copy of
+    CALIB_BYTES (copy read = CALIB_BYTES, copy write = CALIB_BYTES)."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        per = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (r.get("Dispatch_Id"), r.get("Kernel_Name", ""))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return per
+
+    def split(per):
+        gemv = [v for (_, name), v in per.items() if "gemv_staged_kernel" in name]
+        copy = [v for (_, name), v in per.items() if "copy" in name.lower() and "tb::" not in name]
+        copy = sorted(copy)[-3:]  # the three calibration copies are the largest copy dispatches
+        return gemv, copy
+
+    fg, fc = split(load(fetch_dir, "FETCH_SIZE"))
+    wg, wc = split(load(write_dir, "WRITE_SIZE"))
+    kib = 1024.0
+    f_scale = CALIB_BYTES / (sum(fc) / len(fc) * kib)
+    w_scale = CALIB_BYTES / (sum(wc) / len(wc) * kib)
+    fetch = sum(fg) / len(fg) * kib * f_scale
+    write = sum(wg) / len(wg) * kib * w_scale
+    lines = ["# HBM traffic of the grouped decode GEMV (batch 1, 27B-shaped layers, split grouping:",
+             "# [QKV 15360x5120, O 5120x5120, gate/up 34816x5120] and [down 5120x17408] per layer)",
+             "# from two rocprofv3 counter passes over `python3 bench.py --profile-pass`:"]
+    lines += [f"#   {c}" for c in commands]
+    lines += ["# Counters are KiB per dispatch; each is scaled by what it reads for a plain",
+              f"# {CALIB_BYTES >> 20} MiB device copy (torch copy_, read and written once).",
+              f"gemv_dispatches_fetch = {len(fg)}", f"gemv_dispatches_write = {len(wg)}",
+              f"fetch_calibration_factor = {f_scale:.4f}", f"write_calibration_factor = {w_scale:.4f}",
+              f"fetch_bytes_per_launch = {fetch:.0f}", f"write_bytes_per_launch = {write:.0f}",
+              f"hbm_bytes_per_launch = {fetch + write:.0f}",
+              f"gemv_source_hash = {gemv_source_hash()}"]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_kernel_stats(stats_csv, out_path, command):
+    """Short text summary of a rocprofv3 --stats kernel table: the library's
+    kernels with calls, average and total duration."""
+    import csv
+
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "tb::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["# rocprofv3 kernel statistics of the decode-step benchmark on one MI355X (libtb kernels only;",
+             "# the input generation outside the timed region is left out)", f"#   {command}",
+             "# kernel | calls | average us | total us | share of libtb kernel time", ""]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        short = r["Name"].replace("void tb::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / total * 100:.1f}%")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(stack, max_seconds=30.0):
     """Time the CPU oracle's GEMV on layer 0's fused matrices at batch 1, with one
     BLAS thread, until about max_seconds of work; report packed-weight GB/s."""
@@ -293,7 +429,25 @@ def main():
     ap.add_argument("--quick", action="store_true", help="fewer iterations in the extra phases")
     ap.add_argument("--grouping", choices=("layer", "split", "none"), default="split",
                     help="GEMV launches per layer: one over all four matrices, two (d_model-input ones, then down), or one per matrix")
+    ap.add_argument("--profile-pass", action="store_true", help="short run for rocprofv3 counter passes")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
+    ap.add_argument("--summarize-kernel-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="write a text summary of a rocprofv3 --stats kernel table")
     args = ap.parse_args()
+
+    if args.summarize_kernel_stats:
+        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+               "python3 bench.py --steps 5 --warmup 1 --no-extra --no-cpu-baseline")
+        summarize_kernel_stats(args.summarize_kernel_stats[0], args.summarize_kernel_stats[1], cmd)
+        return
+
+    if args.summarize_counters:
+        cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 bench.py --profile-pass",
+                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 bench.py --profile-pass",
+                "python3 bench.py --summarize-counters <fetch_dir> <write_dir>"]
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], TRAFFIC_FILE, cmds)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
@@ -308,6 +462,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_pass:
+        profile_pass(dev)
+        return
     gen = torch.Generator(device=dev)
     gen.manual_seed(29)
 
@@ -331,6 +488,16 @@ def main():
 
     extra = {"step_wall_ms": round(wall_ms / args.steps, 4),
              "gemv_avg_launch_us": round(gms * 1e3, 3), "gemv_launches_per_step": nl}
+    # the same step with a decoder layer's ordering (no grouping across projections)
+    if not args.no_extra:
+        ms_seq, _, gs = time_graph(stack.step_sequential, max(3, args.steps // 2), 2)
+        del gs
+        ms_seq /= max(3, args.steps // 2)
+        extra["decode_sequential"] = {"ms_per_step": round(ms_seq, 4),
+                                      "gbs_packed": round(step_bytes / (ms_seq * 1e-3) / 1e9, 1),
+                                      "note": "each projection rotated, multiplied and rotated back in order, "
+                                              "12 launches per layer"}
+        log(f"decode step, sequential order: {ms_seq:.4f} ms ({step_bytes / (ms_seq * 1e-3) / 1e9:.1f} GB/s)")
     # batch 8 decode
     if not args.no_extra:
         stack.make_acts(8, gen, dev)
@@ -345,6 +512,7 @@ def main():
         stack.make_acts(args.batch, gen, dev)
         extra.update(extra_phases(gen, dev, args.quick))
 
+    traffic = recorded_traffic()
     result = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)",
         "value": round(value, 2),
@@ -363,7 +531,8 @@ def main():
                    "layers": args.layers, "batch": args.batch, "packed_bytes_per_step": step_bytes,
                    "code_distribution": "P(-1,0,+1) = (0.35, 0.30, 0.35)", "scales": "U(0.005, 0.05) fp16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None or args.batch != 1 else round(traffic),
                      "kernel": "gemv_staged_kernel (one grouped launch per layer: QKV, O, gate/up, down)",
                      "bytes_per_launch": "sum over the 4 matrices of N*K/4 + N*K/64 + 2*B*K + 4*B*N"},
         "extra": extra,
