@@ -42,17 +42,50 @@ __device__ __forceinline__ int quad_max(int v) {
   return v;
 }
 
+// One level's two sub-rows for the 8 values f[e] of a lane: every element
+// `in` the level is split into its sign and top four significant bits (hi)
+// and the rest (lo = f - hi), both exact in fp32; each part is scaled by a
+// power of two so that the level's largest exponent ml lands at e4m3 exponent
+// 7 (hi) or 3 (lo) and converted by the hardware.  Every scaled part is a
+// normal e4m3 number (hi has 4 significant bits and an exponent within 10
+// binades below 7; lo has at most 4 significant bits no lower than 2^-6), so
+// the conversion is exact whatever its rounding.  s_hi / s_lo are the E8M0
+// codes of the two sub-rows.
+__device__ __forceinline__ void act8_level(const float (&f)[8], const bool (&in)[8], int ml, uint32_t (&hi_w)[2],
+                                           uint32_t (&lo_w)[2], uint32_t& s_hi, uint32_t& s_lo) {
+  const int shi = ml == 0 ? 127 : max(ml - 7, 0);
+  const int slo = ml == 0 ? 127 : max(ml - 11, 0);
+  s_hi = (uint32_t)shi;
+  s_lo = (uint32_t)slo;
+  float ph[8], pl[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float top = __uint_as_float(__float_as_uint(f[e]) & 0xFFF00000u);
+    ph[e] = __builtin_ldexpf(in[e] ? top : 0.f, 127 - shi);
+    pl[e] = __builtin_ldexpf(in[e] ? f[e] - top : 0.f, 127 - slo);
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(ph[4 * w], ph[4 * w + 1], 0, false);
+    hi_w[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ph[4 * w + 2], ph[4 * w + 3], h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32(pl[4 * w], pl[4 * w + 1], 0, false);
+    lo_w[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pl[4 * w + 2], pl[4 * w + 3], l, true);
+  }
+}
+
 // Encode the 8 bf16 values h[e] (K = 128 g + 8 sub + e) held by lane `sub`
-// (0..15) of a 128-element group and store them.  `vals` points at the group's
-// 512 value bytes, `scl` at its 16 scale bytes.  All 16 lanes of the group must
-// call this together (quad reductions); `store` false skips the writes.
-__device__ __forceinline__ void act8_encode_store(const uint32_t (&h)[8], int sub, uint8_t* vals, uint8_t* scl,
-                                                  bool store) {
+// (0..15) of a 128-element group: word[j] are the lane's 8 bytes of sub-row j,
+// sc[j] the E8M0 scale of sub-row j for the lane's 32-element block.  All 16
+// lanes of the group must call this together (quad reductions).
+__device__ __forceinline__ void act8_encode(const uint32_t (&h)[8], uint32_t (&word)[kActSub][2],
+                                            uint32_t (&sc)[kActSub]) {
   int ex[8];
+  float f[8];
   int m0 = 0, nonfinite = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     ex[e] = (int)((h[e] >> 7) & 0xFFu);
+    f[e] = __uint_as_float(h[e] << 16);
     if (ex[e] == 255) nonfinite = 1;
     else m0 = max(m0, ex[e]);
   }
@@ -64,32 +97,17 @@ __device__ __forceinline__ void act8_encode_store(const uint32_t (&h)[8], int su
     if (ex[e] > 0 && ex[e] + 10 < m0) m1 = max(m1, ex[e]);
   m1 = quad_max(m1);
 
-  uint32_t word[kActSub][2];
-  uint32_t sc[kActSub];
+  bool in[8];
 #pragma unroll
-  for (int lv = 0; lv < 2; ++lv) {
-    const int ml = lv == 0 ? m0 : m1;
-    const int s_hi = ml == 0 ? 127 : max(ml - 7, 0);
-    const int s_lo = ml == 0 ? 127 : max(ml - 11, 0);
-    sc[2 * lv] = (uint32_t)s_hi;
-    sc[2 * lv + 1] = (uint32_t)s_lo;
-    word[2 * lv][0] = word[2 * lv][1] = 0u;
-    word[2 * lv + 1][0] = word[2 * lv + 1][1] = 0u;
+  for (int e = 0; e < 8; ++e) in[e] = ex[e] > 0 && ex[e] < 255 && ex[e] + 10 >= m0;
+  act8_level(f, in, m0, word[0], word[1], sc[0], sc[1]);
+  if (m1 != 0) {  // some element lies more than 10 binades below the block's largest
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int x = ex[e];
-      const bool in = ml > 0 && x > 0 && x < 255 && x + 10 >= ml && (lv == 0 || x + 10 < m0);
-      const uint32_t sgn = (h[e] >> 8) & 0x80u;
-      const int ehi = x - s_hi + 7;
-      uint32_t bhi = 0u, blo = 0u;
-      if (in && ehi >= 1) bhi = sgn | ((uint32_t)ehi << 3) | ((h[e] >> 4) & 7u);
-      const uint32_t m4 = h[e] & 0xFu;
-      const int p = 31 - __builtin_clz(m4 | 1u);  // leading bit of m4 (0 when m4 <= 1)
-      const int elo = x + p - s_lo;
-      if (in && m4 != 0u && elo >= 1) blo = sgn | ((uint32_t)elo << 3) | ((m4 << (3 - p)) & 7u);
-      word[2 * lv][e >> 2] |= bhi << (8 * (e & 3));
-      word[2 * lv + 1][e >> 2] |= blo << (8 * (e & 3));
-    }
+    for (int e = 0; e < 8; ++e) in[e] = ex[e] > 0 && ex[e] + 10 < m0 && ex[e] + 10 >= m1;
+    act8_level(f, in, m1, word[2], word[3], sc[2], sc[3]);
+  } else {
+    word[2][0] = word[2][1] = word[3][0] = word[3][1] = 0u;
+    sc[2] = sc[3] = 127u;
   }
   if (nonfinite) {
 #pragma unroll
@@ -97,10 +115,24 @@ __device__ __forceinline__ void act8_encode_store(const uint32_t (&h)[8], int su
       if (ex[e] == 255) word[0][e >> 2] = (word[0][e >> 2] & ~(0xFFu << (8 * (e & 3)))) | (0x7Fu << (8 * (e & 3)));
     sc[0] = 0xFFu;
   }
-  if (!store) return;
-  // K 128 g + 8 sub .. +7 is 16-chunk c = sub / 2: lane group c % 4, half c / 4
+}
+
+// Byte offset of lane `sub`'s 8 values inside a sub-row of 128 bytes: K
+// 128 g + 8 sub .. +7 is 16-chunk c = sub / 2, i.e. lane group c % 4, half c / 4.
+__device__ __forceinline__ int act8_lane_offset(int sub) {
   const int c = sub >> 1;
-  const int off = (c & 3) * 32 + (c >> 2) * 16 + (sub & 1) * 8;
+  return (c & 3) * 32 + (c >> 2) * 16 + (sub & 1) * 8;
+}
+
+// act8_encode, then store the group: `vals` points at its 512 value bytes,
+// `scl` at its 16 scale bytes; `store` false skips the writes.
+__device__ __forceinline__ void act8_encode_store(const uint32_t (&h)[8], int sub, uint8_t* vals, uint8_t* scl,
+                                                  bool store) {
+  uint32_t word[kActSub][2];
+  uint32_t sc[kActSub];
+  act8_encode(h, word, sc);
+  if (!store) return;
+  const int off = act8_lane_offset(sub);
 #pragma unroll
   for (int j = 0; j < kActSub; ++j)
     *reinterpret_cast<u32x2*>(vals + j * 128 + off) = u32x2{word[j][0], word[j][1]};

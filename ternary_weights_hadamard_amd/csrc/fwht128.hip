@@ -2,35 +2,22 @@
 //
 // xxqk.cn/news/652513 §2 computes the transform as log2(n) rounds of
 // (a + b, a - b) butterflies; dpshk.com/news/5289456 §2.3 normalises by
-// 1/sqrt(block size).  Here one 128-block lives in 16 consecutive lanes of a
-// wave, 8 contiguous elements per lane (one 16-byte bf16 load): the three
-// butterfly rounds over element bits 0-2 run inside a lane, the four over
-// element bits 3-6 pair lanes (lane ^ 1, 2, 4, 8) through DPP and ds_swizzle,
-// so nothing goes through LDS.  The kernel is HBM bound: 4 bytes per element
-// for bf16 in and out.
+// 1/sqrt(block size).  One 128-block lives in 16 consecutive lanes of a wave,
+// 8 contiguous elements per lane (one 16-byte bf16 load), and the butterflies
+// run in registers (fwht_lanes.h).  The kernel is HBM bound: 4 bytes per
+// element for bf16 in and out.
 //
 // With the act8 output the rounded bf16 result is re-encoded in the same pass
 // as the dense GEMV's activation operand (act8.h); the same kernel without the
 // transform re-encodes bf16 activations as they are.
 #include "act8.h"
+#include "fwht_lanes.h"
 #include "tb_common.h"
 #include "tb_launch.h"
 
 namespace tb {
 
 namespace {
-
-constexpr float kInvSqrt128 = 0.08838834764831845f;
-
-template <int MASK>
-__device__ __forceinline__ void lane_stage(float (&v)[8], int sub) {
-  const bool upper = (sub & MASK) != 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float p = xor_lane<MASK>(v[e]);
-    v[e] = upper ? (p - v[e]) : (v[e] + p);
-  }
-}
 
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutAct8 = 2 };
 
@@ -93,23 +80,7 @@ __global__ void __launch_bounds__(256) fwht128_kernel(FwhtSegs segs) {
     }
     float sc = 1.0f;
     if constexpr (XFORM) {
-      // element bits 0..2: inside the lane
-#pragma unroll
-      for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if ((e & h) == 0) {
-            float a = v[e], c = v[e + h];
-            v[e] = a + c;
-            v[e + h] = a - c;
-          }
-        }
-      }
-      // element bits 3..6: lane bits 0..3
-      lane_stage<1>(v, sub);
-      lane_stage<2>(v, sub);
-      lane_stage<4>(v, sub);
-      lane_stage<8>(v, sub);
+      fwht128_lanes(v, sub);
       sc = kInvSqrt128;
     }
     if constexpr (OUT == kOutAct8) {

@@ -115,10 +115,9 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint
 #pragma unroll
       for (int m = 0; m < NB4; ++m) {
         const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[j][m], b8, zero, 0, 4, 0, as[j][m], 0, 127);
-        // keep both sources live past the instruction: its destination must not
-        // reuse their registers (it reads them over several passes)
-        keep_in_vgprs(av[j][m]);
-        keep_in_vgprs(bw);
+        // the destination must not reuse the sources' registers (the
+        // instruction reads them over several passes)
+        keep_sources_past(d, av[j][m], bw);
         const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc[m]);
         acc[m] = j < n ? a : acc[m];  // slots past the slice (a repeated group) add nothing
       }
@@ -284,8 +283,7 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
                         (int)((w1 << 2) & 0xCCCCCCCCu)};
       const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
       const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, zero, 0, 4, 0, as, 0, 127);
-      keep_in_vgprs(av);
-      keep_in_vgprs(bw);
+      keep_sources_past(d, av, bw);  // the destination must not reuse the sources' registers
       const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc);
       acc = j < n ? a : acc;  // slots past the slice add nothing
     }

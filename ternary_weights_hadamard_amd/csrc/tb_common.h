@@ -69,15 +69,20 @@ __device__ __forceinline__ float xor_lane(float v) {
   return __int_as_float(r);
 }
 
-// Make the compiler keep `v` in vector registers up to this point.  The asm
-// exists only in the device pass: the host pass cannot parse the "v"
-// constraint and would drop the kernel's launch stub.
-template <typename T>
-__device__ __forceinline__ void keep_in_vgprs(const T& v) {
+// Keep the sources `a` and `b` of an instruction that produced `d` in vector
+// registers until after it: the asm reads all three, so it cannot be placed
+// before the instruction, and the sources stay live across it (their
+// registers cannot be reused for `d`).  The asm exists only in the device
+// pass: the host pass cannot parse the "v" constraint and would drop the
+// kernel's launch stub.
+template <typename D, typename A, typename B>
+__device__ __forceinline__ void keep_sources_past(const D& d, const A& a, const B& b) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" ::"v"(v));
+  asm volatile("" ::"v"(d), "v"(a), "v"(b));
 #else
-  (void)v;
+  (void)d;
+  (void)a;
+  (void)b;
 #endif
 }
 
