@@ -246,11 +246,10 @@ TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t*
  *   x       bf16 bits [M][K], M >= 0 (any M; ragged tails are handled)
  *   y       [M][N] in y_dtype: TB_BF16 (rounded to nearest even) or TB_F32;
  *           must not overlap the inputs.
- * The matrix cores take fp16 operands: each weight enters as the exact fp16
- * value 2*t*scale and each activation as its fp16 value, which equals the
- * bf16 value whenever 2^-14 <= |x| < 65504 or x = 0.  Smaller magnitudes are
- * rounded (absolute error <= 2^-25); |x| >= 65520 becomes infinite and shows
- * in y.  Accumulation is fp32.
+ * The matrix cores take the activations as the bf16 values they are and each
+ * weight as the exact bf16 value 2t; every product is exact.  Each 128-K
+ * group's products are summed in fp32 and added to the result times the
+ * group's scale; the result is halved on the way out.
  */
 TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, void* y, int y_dtype, void* stream);

@@ -1,25 +1,24 @@
 // Prefill GEMM with dense ternary weights, the decode contraction for M rows:
 //   y[m][n] = sum_g f16(scale[n][g]) * sum_{k in g} t[n][k] * x[m][k]
 //
-// The one dense contraction of the path, so it runs on the matrix cores.  The
-// group scale changes every 128 K, and applying it to fp32 partial sums would
-// double the accumulator registers; instead each weight enters the MFMA as the
-// fp16 value 2 t s, which is exact (s is fp16; doubling only moves the
-// exponent), the activations enter as fp16 (bf16 -> fp16 is exact for
-// 2^-14 <= |x| < 65504), and the fp32 accumulator runs over all of K.  The
-// result is halved on the way out.
+// The one dense contraction of the path, so it runs on the matrix cores, with
+// bf16 operands: the activations go to LDS as they are (no conversion) and
+// each weight enters as the bf16 value 2t (exact).  A 128-K group's products
+// accumulate in fp32 registers of their own; at the end of the group they are
+// added to the result accumulators times the group's fp16 scale (one FMA per
+// accumulator, the scale taken straight from fp16).  The result is halved on
+// the way out.
 // Decode: a dense code word holds column c's field in nibble c % 8, bits 2-3
 // for c < 8 and bits 0-1 for c >= 8.  Shifting the word left by 4, 6 and 2
 // puts the fields of columns 2p, 8 + 2p and 9 + 2p at bits 6-7 of byte p (the
 // field of column 2p + 1 is there already); one v_perm_b32 moves two such
-// bytes to bytes 1 and 3 and the mask 0xC000C000 leaves the fp16 pair
-// (2t, 2t') - bit 14 alone is the exponent of 2.0 in fp16.  One packed fp16
-// multiply by (s, s) makes (2ts, 2t's).
-// Tiling (first version): 128 x 128 output tile per workgroup of 4 waves, each
-// wave 64 x 64 with v_mfma_f32_16x16x32_f16; K steps of 64 staged through LDS
-// (fp16, double buffered, rows padded to spread banks).  Each K step reads the
-// codes of 128 rows once (8 bytes per thread) and decodes them once for all
-// 128 activation rows of the tile.
+// bytes to bytes 1 and 3 and the mask 0xC000C000 leaves the bf16 pair
+// (2t, 2t') - bit 14 alone is the exponent of 2.0.
+// Tiling: 128 x 128 output tile per workgroup of 4 waves, each wave 64 x 64
+// with v_mfma_f32_16x16x32_bf16; K steps of 64 staged through LDS (double
+// buffered, rows padded to spread banks), two steps per scale group.  Each K
+// step reads the codes of 128 rows once (8 bytes per thread) and decodes them
+// once for all 128 activation rows of the tile.
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -28,11 +27,11 @@ namespace tb {
 namespace {
 
 constexpr int BM = 128, BN = 128, KT = 64;
-constexpr int LDS_ROW = KT + 8;  // fp16 elements per LDS row (144 bytes)
+constexpr int LDS_ROW = KT + 8;  // bf16 elements per LDS row (144 bytes)
 constexpr int TILE_ELEMS = BM * LDS_ROW;
 
-// fp16 pairs (2t, 2t') of the 16 columns of a dense code word, in column order.
-__device__ __forceinline__ void decode_word_f16(uint32_t w, uint32_t (&out)[8]) {
+// bf16 pairs (2t, 2t') of the 16 columns of a dense code word, in column order.
+__device__ __forceinline__ void decode_word_bf16(uint32_t w, uint32_t (&out)[8]) {
   const uint32_t t4 = w << 4, t6 = w << 6, t2 = w << 2;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -42,18 +41,13 @@ __device__ __forceinline__ void decode_word_f16(uint32_t w, uint32_t (&out)[8]) 
   }
 }
 
-__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
-  const float lo = bf16_to_f32(w & 0xffffu);
-  const float hi = bf16_to_f32(w >> 16);
-  return f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
-}
-
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                            const uint32_t* __restrict__ codes,
                                                            const uint16_t* __restrict__ scales, int64_t N,
                                                            int64_t K, void* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE_ELEMS];  // [stage][X | W][row][k]
+  __shared__ uint16_t lds_s[2][BN];                                         // [stage][weight row] fp16 scale
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -62,7 +56,7 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t G = K / kBlock;
-  const int nsteps = (int)(K / KT);
+  const int nsteps = (int)(K / KT);  // even: K is a multiple of 128
 
   // global -> register staging assignment
   // X: 128 rows x 64 k bf16 = 128 B per row; thread -> row tid/2, 32 k (64 B) at (tid&1)*32
@@ -92,62 +86,72 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
     ss = ssrc[k0 / kBlock];
   };
   auto lstore = [&](int stage) {
-    // X: convert bf16 -> fp16 and store 32 elements of row xr
+    // X: 32 bf16 of row xr, as they are
     uint16_t* xd = &lds[stage][0][xr * LDS_ROW + xk];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = bf16pair_to_f16pair(xs[i][j]);
-      *reinterpret_cast<u32x4*>(xd + 8 * i) = o;
-    }
-    // W: decode 32 k of row wr into fp16 2*t*s, pairs (k, k+1)
-    const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)ss);
-    const f16x2 s2 = {sh, sh};
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xd + 8 * i) = xs[i];
+    // W: decode 32 k of row wr into bf16 2t, pairs (k, k+1)
     uint16_t* wd = &lds[stage][1][wr * LDS_ROW + wk];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t bits[8];
-      decode_word_f16(cs[j], bits);
-      u32x4 o0, o1;
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const f16x2 v = __builtin_bit_cast(f16x2, bits[f]) * s2;
-        if (f < 4) o0[f] = __builtin_bit_cast(uint32_t, v);
-        else o1[f - 4] = __builtin_bit_cast(uint32_t, v);
-      }
-      *reinterpret_cast<u32x4*>(wd + 16 * j) = o0;
-      *reinterpret_cast<u32x4*>(wd + 16 * j + 8) = o1;
+      decode_word_bf16(cs[j], bits);
+      *reinterpret_cast<u32x4*>(wd + 16 * j) = u32x4{bits[0], bits[1], bits[2], bits[3]};
+      *reinterpret_cast<u32x4*>(wd + 16 * j + 8) = u32x4{bits[4], bits[5], bits[6], bits[7]};
     }
+    if ((tid & 1) == 0) lds_s[stage][wr] = (uint16_t)ss;
   };
 
-  f32x4 acc[4][4];
+  // acc: the result; accg: the current scale group's products
+  f32x4 acc[4][4], accg[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // the MFMAs of one K step from LDS stage `st`; FIRST starts the group
+  auto mfma_step = [&](int st, bool first) {
+#pragma unroll
+    for (int kk = 0; kk < KT; kk += 32) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&lds[st][0][(wm + 16 * i + li) * LDS_ROW + kk + 8 * q]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&lds[st][1][(wn + 16 * j + li) * LDS_ROW + kk + 8 * q]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], (first && kk == 0) ? zero : accg[i][j], 0,
+                                                                 0, 0);
+    }
+  };
 
   gload(0);
   lstore(0);
   __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    if (step + 1 < nsteps) gload(step + 1);
+  for (int step = 0; step < nsteps; step += 2) {
+    // first step of the group: stage 0, while step + 1 comes in
+    gload(step + 1);
+    mfma_step(0, true);
+    lstore(1);
+    __syncthreads();
+    // second step: stage 1, while the next group's first step comes in
+    if (step + 2 < nsteps) gload(step + 2);
+    mfma_step(1, false);
+    // fold the group: lane's column n = n0 + wn + 16 j + li
 #pragma unroll
-    for (int kk = 0; kk < KT; kk += 32) {
-      f16x8 a[4], b[4];
+    for (int j = 0; j < 4; ++j) {
+      const float sc = (float)__builtin_bit_cast(_Float16, lds_s[1][wn + 16 * j + li]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const f16x8*>(&lds[cur][0][(wm + 16 * i + li) * LDS_ROW + kk + 8 * q]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const f16x8*>(&lds[cur][1][(wn + 16 * j + li) * LDS_ROW + kk + 8 * q]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(accg[i][j][r], sc, acc[i][j][r]);
     }
-    if (step + 1 < nsteps) lstore(cur ^ 1);
+    if (step + 2 < nsteps) lstore(0);
     __syncthreads();
   }
 

@@ -57,6 +57,24 @@ def test_gemm_exact_small_integers_and_gemv_agreement():
     assert np.array_equal(yv.cpu().numpy(), y.cpu().numpy()[:8])
 
 
+def test_gemm_tiny_and_wide_range_activations_exact():
+    # bf16 activations far below the fp16 range (down to 2^-100) and up to
+    # 2^20, times power-of-two scales: every product and every sum here is an
+    # exact fp32 value, so the result must equal the oracle's exactly
+    m, n, k = 40, 128, 512
+    rng = np.random.default_rng(61)
+    codes = synth.random_code_words(n, k, seed=60)
+    e = rng.integers(-100, 20, size=(m, 1))          # one binade per row keeps the sums exact
+    mant = rng.integers(-8, 9, size=(m, k))
+    xv = mant.astype(np.float64) * np.exp2(e.astype(np.float64))
+    x = oracle.numerics.f64_to_bf16_bits(xv)
+    assert np.array_equal(oracle.numerics.bf16_bits_to_f64(x), xv)
+    sc = (2.0 ** rng.integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    y = tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(sc), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
+
+
 def test_gemm_canaries_and_empty():
     m, n, k = 130, 128, 256
     codes = synth.random_code_words(n, k, seed=60)
