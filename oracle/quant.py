@@ -11,6 +11,15 @@ Definitions followed (readings of the pages are listed in the design doc):
   sign(w) * (|w| > thr) step of dpshk.com/news/5289456 §3.2 step 5; a value at
   exactly s/2 gives 0 (round-half-even agrees).  The comparison uses the
   unrounded float64 scale; the stored scale is its fp16 rounding.
+* Error-minimising variant: for each group choose the threshold theta and
+  scale s that minimise ||w' - s t||^2 with t = sign(w') [|w'| >= theta]
+  (a threshold-shaped ternarisation, dpshk.com/news/5289456 §3.2 steps 4-5;
+  the threshold as the accuracy-critical choice, xxqk.cn/news/652513 §4).
+  For a kept set of j elements with magnitude sum S the best scale is S / j
+  and the error is sum w'^2 - S^2 / j, so theta is the group magnitude that
+  maximises S^2 / j over the kept sets {|w'| >= theta}.  The 0.38-quantile
+  threshold of dpshk.com §3.2 step 4 is one member of this family (it keeps
+  the largest 79 of 128).  Ties in S^2 / j go to the larger theta.
 * 2:4: of every 4 consecutive K-elements keep the 2 largest |w'| and ternarise
   the survivors (mhpq.cn §1.2: prune with the 2:4 pattern, then ternarise what
   remains).  Kept elements are nonzero, so each carries only a sign; the group
@@ -131,6 +140,76 @@ def quantize_dense(w):
     s = absmean_scales(wr)
     t = ternarize(wr, s)
     return {"codes": pack_dense(t), "scales": f64_to_f16_bits(s), "wr": wr, "s": s, "t": t}
+
+
+# ---------------------------------------------------------------- error-minimising variant
+
+def mse_threshold(a):
+    """For magnitudes a[..., n] (float64, >= 0) of groups along the last axis:
+    the threshold theta (one of the group's magnitudes) maximising S^2 / j over
+    the kept sets {k : a_k >= theta}, j = their count and S their sum; among
+    equal objectives the larger theta.  Returns (theta, j, S)."""
+    a = np.asarray(a, dtype=np.float64)
+    d = -np.sort(-a, axis=-1)                     # descending magnitudes
+    n = d.shape[-1]
+    S = np.cumsum(d, axis=-1)                     # S[j-1]: sum of the j largest
+    j = np.arange(1, n + 1, dtype=np.float64)
+    obj = S * S / j
+    # a kept set {a >= theta} holds every copy of theta: only the last of a
+    # run of equal magnitudes is a candidate
+    last = np.ones(d.shape, dtype=bool)
+    last[..., :-1] = d[..., :-1] > d[..., 1:]
+    obj = np.where(last, obj, -np.inf)
+    # argmax takes the first maximum, i.e. the smallest j: the larger theta
+    best = np.argmax(obj, axis=-1)
+    take = lambda arr: np.take_along_axis(arr, best[..., None], axis=-1)[..., 0]
+    return take(d), best + 1, take(S)
+
+
+def mse_objective_gap(a):
+    """Relative gap between the best and the second-best objective S^2 / j over
+    distinct thresholds of each group (0 when the group has one distinct
+    magnitude)."""
+    a = np.asarray(a, dtype=np.float64)
+    d = -np.sort(-a, axis=-1)
+    n = d.shape[-1]
+    S = np.cumsum(d, axis=-1)
+    obj = S * S / np.arange(1, n + 1, dtype=np.float64)
+    last = np.ones(d.shape, dtype=bool)
+    last[..., :-1] = d[..., :-1] > d[..., 1:]
+    obj = np.sort(np.where(last, obj, -np.inf), axis=-1)
+    top, second = obj[..., -1], obj[..., -2]
+    gap = np.where(np.isfinite(second), (top - second) / np.maximum(top, 1e-300), np.inf)
+    return np.where(top > 0, gap, np.inf)
+
+
+def quantize_dense_mse(w):
+    """Rotate 128x128 blocks; per group the error-minimising threshold and scale
+    (mse_threshold); t = sign(W') [|W'| >= theta]; pack as the dense format.
+
+    Returns codes, scales (fp16 bits), and wr, s (unrounded scales), theta, t."""
+    w = _check_w(w)
+    wr = rotate_blocks(w)
+    n, k = wr.shape
+    a = np.abs(wr).reshape(n, k // GROUP, GROUP)
+    theta, j, S = mse_threshold(a)
+    s = S / j
+    keep = a >= theta[..., None]
+    t = (np.sign(wr) * keep.reshape(n, k)).astype(np.int8)
+    return {"codes": pack_dense(t), "scales": f64_to_f16_bits(s), "wr": wr, "s": s, "theta": theta, "t": t}
+
+
+def near_threshold_mse(wr, theta, rel=NEAR_REL):
+    """Elements whose |W'| is within rel * theta of their group's threshold."""
+    thr = np.repeat(theta, GROUP, axis=1)
+    return np.abs(np.abs(wr) - thr) <= rel * thr
+
+
+def near_tie_mse(wr, rel=NEAR_REL):
+    """Groups [N, K/128] whose best and second-best objective differ by at most
+    rel (relative): float rounding may pick either threshold."""
+    n, k = wr.shape
+    return mse_objective_gap(np.abs(wr).reshape(n, k // GROUP, GROUP)) <= rel
 
 
 # ---------------------------------------------------------------- 2:4 variant

@@ -251,3 +251,83 @@ def test_24_rejects_invalid_nibble():
     meta = np.array([[0x7, 0x4]], dtype=np.uint32)  # first nibble: idx0 = 3 >= idx1 = 1
     with pytest.raises(ValueError):
         q.unpack_24(meta, np.zeros((1, 1), dtype=np.uint32), 64)
+
+
+# ---------------------------------------------------------------- error-minimising variant
+
+def _brute_force_min_error(w):
+    """Smallest ||w - s t||^2 over every ternary t in {-1, 0, 1}^n with its best
+    scale s = <w, t> / <t, t> (t = 0 leaves ||w||^2); returns (error, t)."""
+    n = w.size
+    best, best_t = float(np.sum(w * w)), np.zeros(n, dtype=np.int8)
+    for code in range(1, 3 ** n):
+        t = np.array([(code // 3 ** i) % 3 - 1 for i in range(n)], dtype=np.float64)
+        tt = float(t @ t)
+        if tt == 0:
+            continue
+        s = float(w @ t) / tt
+        err = float(np.sum((w - s * t) ** 2))
+        if err < best - 1e-12:
+            best, best_t = err, t.astype(np.int8)
+    return best, best_t
+
+
+@pytest.mark.parametrize("n", [4, 6, 8])
+def test_mse_threshold_matches_brute_force_over_all_ternary_vectors(n):
+    rng = np.random.default_rng(100 + n)
+    for _ in range(6):
+        w = rng.normal(size=n)
+        err_bf, t_bf = _brute_force_min_error(w)
+        theta, j, S = q.mse_threshold(np.abs(w))
+        err = float(np.sum(w * w) - S * S / j)
+        assert abs(err - err_bf) <= 1e-12 * max(1.0, err_bf)
+        t = (np.sign(w) * (np.abs(w) >= theta)).astype(np.int8)
+        # (s, t) and (-s, -t) are the same approximation; the oracle's s is >= 0
+        assert np.array_equal(t, t_bf) or np.array_equal(t, -t_bf)
+        assert int(np.count_nonzero(t)) == int(j)
+
+
+def test_mse_threshold_hand_worked_groups():
+    # a = [2, 2, 1, 1, 0]: theta 2 -> 4^2/2 = 8; theta 1 -> 6^2/4 = 9; theta 0 -> 6^2/5 = 7.2
+    theta, j, S = q.mse_threshold(np.array([2.0, 1.0, 0.0, 2.0, 1.0]))
+    assert (theta, j, S) == (1.0, 4, 6.0)
+    # a = [3, 1, 1, 1]: theta 3 -> 9/1 = 9 and theta 1 -> 6^2/4 = 9 tie: the larger threshold
+    theta, j, S = q.mse_threshold(np.array([1.0, 3.0, 1.0, 1.0]))
+    assert (theta, j, S) == (3.0, 1, 3.0)
+    # equal magnitudes are kept or dropped together
+    theta, j, S = q.mse_threshold(np.array([5.0, 1.0, 1.0, 1.0, 1.0, 1.0]))
+    assert theta == 5.0 and j == 1   # 25 / 1 > 100 / 6
+    theta, j, S = q.mse_threshold(np.array([2.0, 1.0, 1.0, 1.0, 1.0, 1.0]))
+    assert theta == 1.0 and j == 6   # 49 / 6 > 4 / 1
+    # an all-zero group keeps nothing of value: t = 0, s = 0
+    theta, j, S = q.mse_threshold(np.zeros(8))
+    assert theta == 0.0 and S == 0.0
+
+
+def test_mse_rule_never_loses_to_the_absmean_rule_or_the_quantile_rule():
+    # the absmean rule and the 0.38-quantile rule (largest 79 of 128, best
+    # scale) are threshold-shaped ternarisations, so their error cannot be
+    # below the minimum over all thresholds and scales
+    rng = np.random.default_rng(7)
+    w = rng.standard_t(3, size=(128, 512)) * 0.02
+    r = q.quantize_dense_mse(w)
+    wr = r["wr"]
+    n, k = wr.shape
+    g = lambda x: x.reshape(n, k // 128, 128)
+    err_mse = np.sum(g((wr - np.repeat(r["s"], 128, axis=1) * r["t"]) ** 2), axis=2)
+    ra = q.quantize_dense(w)
+    err_abs = np.sum(g((wr - np.repeat(ra["s"], 128, axis=1) * ra["t"]) ** 2), axis=2)
+    assert np.all(err_mse <= err_abs * (1 + 1e-12))
+    d = -np.sort(-np.abs(g(wr)), axis=2)
+    s79 = d[:, :, :79].sum(axis=2)
+    err_q = np.sum(g(wr) ** 2, axis=2) - s79 ** 2 / 79
+    assert np.all(err_mse <= err_q * (1 + 1e-12))
+    assert np.mean(err_mse) < np.mean(err_abs)
+
+
+def test_mse_near_tie_groups_are_a_small_minority():
+    rng = np.random.default_rng(8)
+    w = rng.normal(size=(512, 512)) * 0.02
+    wr = q.quantize_dense_mse(w)["wr"]
+    frac = q.near_tie_mse(wr).mean()
+    assert frac < 0.1
