@@ -14,7 +14,8 @@ value = packed weight bytes (codes + scales) streamed per step / step time.
 Also measured in the same run, each over its own synthetic input, and
 reported under "extra": the same decode step at batch 8, the 2:4 GEMV
 (17408x5120, batch 1), the prefill GEMM (M = 2048, both FFN shapes), the
-activation FWHT at prefill size, and the offline quantiser over one layer.
+activation FWHT at prefill size, and the offline quantiser over one layer
+(absmean rule and the error-minimising rule).
 The CPU oracle is timed on a bounded sample of the decode workload.
 """
 
@@ -284,6 +285,16 @@ def extra_phases(gen, dev, quick):
                        "gbs": round(qb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(qb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "projected_64_layer_ms": round(64 * ms, 1)}
     log(f"  quantise one layer: {ms:.3f} ms, {out['quantize']['gbs']} GB/s")
+
+    def runq_minerr():
+        for w, (c, s) in zip(ws, outs):
+            tb.tb_quantize_pack(w, fmt=tb.TB_FMT_DENSE_MINERR, codes=c, scales=s)
+
+    ms = time_eager(runq_minerr, 1 if quick else 2)
+    out["quantize_minerr"] = {"workload": "one 27B layer, error-minimising threshold and scale per group",
+                              "ms_per_layer": round(ms, 3), "gbs": round(qb / (ms * 1e-3) / 1e9, 1),
+                              "note": "every group magnitude tried as the threshold (128 x 128 compares per group)"}
+    log(f"  quantise one layer, min-error rule: {ms:.3f} ms")
     del ws, outs
     return out
 

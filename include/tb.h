@@ -74,7 +74,9 @@ typedef enum {
 } tb_status;
 
 typedef enum { TB_F32 = 0, TB_BF16 = 1, TB_ACT8 = 2 } tb_dtype;
-typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1 } tb_format;
+/* Quantiser rules and storage formats.  TB_FMT_DENSE_MINERR stores the dense
+ * format; only the threshold and scale rule differ (tb_quantize_pack). */
+typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2 } tb_format;
 
 /* Bits OR-ed into the optional device error flag of tb_quantize_pack. */
 #define TB_EFLAG_NONFINITE 1u /* a non-finite weight was seen; its block's codes are unspecified */
@@ -131,7 +133,7 @@ TB_API int tb_version(void);
 
 /*
  * Sizes in bytes of the packed planes of an [N][K] matrix in format `fmt`
- * (tb_format).  Dense: code_bytes = N*K/4, meta_bytes = 0.  2:4: code_bytes
+ * (tb_format).  Dense (both rules): code_bytes = N*K/4, meta_bytes = 0.  2:4: code_bytes
  * (the sign plane) = N*K/16, meta_bytes = N*K/8.  scale_bytes = N*K/64 for
  * both.  Any output pointer may be NULL.  Host-only.
  * Cites the 2-bit storage of mhpq.cn/news/1159370 §3.1 and the bit ledger of §1.3.
@@ -178,13 +180,20 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_
  * TB_FMT_24 first keeps, in every quad of 4 along K, the two largest |W'|
  * (ties to the lower position), takes s over the 64 kept elements of each
  * group and stores their signs (mhpq.cn §1.2).
+ * TB_FMT_DENSE_MINERR (dense storage) chooses each group's threshold and
+ * scale to minimise ||W' - s t||^2 (the threshold as the accuracy-critical
+ * knob, xxqk.cn/news/652513 §4): over the group's magnitudes theta, the kept
+ * set {|W'| >= theta} with the largest S^2 / j (S the sum of its magnitudes,
+ * j its size), t = sign(W') on it, s = S / j; ties go to the larger theta.
+ * The 0.38-quantile threshold of dpshk.com §3.2 step 4 is one of the
+ * candidates (it keeps the largest 79 of 128).
  *   W       fp32 [N][K]
  *   codes   dense: [N][K/16] code words; 2:4: the sign plane [N][K/64]
- *   meta    2:4: [N][K/32]; must be NULL for TB_FMT_DENSE (else TB_ERR_FORMAT)
+ *   meta    2:4: [N][K/32]; must be NULL for the dense formats (else TB_ERR_FORMAT)
  *   scales  fp16 bits [N][K/128]
  *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
  *             (the caller zeroes it first).
- * Arithmetic is fp32; the threshold uses the unrounded scale.
+ * Arithmetic is fp32; the absmean threshold uses the unrounded scale.
  */
 TB_API tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes,
                            uint32_t* meta, uint16_t* scales, int32_t* err_flag, void* stream);

@@ -1,5 +1,9 @@
-// Offline quantise/pack: per 128x128 block W' = H B H^T / 128, absmean scale
-// per 128-group (one row of a block), ternarise, pack.
+// Offline quantise/pack: per 128x128 block W' = H B H^T / 128, a scale and a
+// threshold per 128-group (one row of a block), ternarise, pack.  Rules: the
+// absmean scale with threshold s/2 (dense, 2:4), or the error-minimising
+// threshold and scale (dense): over the group's magnitudes theta, the kept set
+// {|w'| >= theta} with the largest S^2 / j (S its magnitude sum, j its size),
+// scale S / j, which minimises ||w' - s t||^2; ties to the larger theta.
 //
 // Method: mhpq.cn/news/1159370 §1.1 (scale = the group's mean absolute value;
 // divide, round, clip to {-1, 0, 1}), §1.2 (2:4: keep two of four, ternarise
@@ -20,6 +24,9 @@
 //            pairs of the row's 16 x 128 tile).
 // The 1/128 of the 2D transform is a power of two; it is folded into the
 // threshold and the stored scale instead of being applied to every element.
+// The error-minimising rule evaluates every magnitude of the group as a
+// threshold: lane pair (l, l ^ 32) holds the group, exchanges one candidate of
+// each lane per step and adds both lanes' kept counts and sums.
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -59,7 +66,9 @@ __device__ __forceinline__ void fwht_cross_halves(float (&v)[64], float sgn) {
 // r < 8 in bits 2-3 of nibble r, r >= 8 in bits 0-1 of nibble r - 8.
 __device__ __forceinline__ constexpr int field_pos(int r) { return 4 * (r & 7) + 2 - 2 * (r >> 3); }
 
-template <bool FMT24>
+enum Rule { kAbsmean = 0, kTwoFour = 1, kMinError = 2 };
+
+template <int RULE>
 __global__ void __launch_bounds__(256) quantize128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                                            uint32_t* __restrict__ codes,
                                                            uint32_t* __restrict__ meta,
@@ -121,7 +130,58 @@ __global__ void __launch_bounds__(256) quantize128_kernel(const float* __restric
     // v[j] = T[row][64*half + j] with T = H B H^T (unnormalised: W' = T / 128)
 
     const int64_t grow = n0 + row;
-    if constexpr (!FMT24) {
+    if constexpr (RULE == kMinError) {
+      // every magnitude of the group is a candidate threshold; per step each
+      // lane of the pair offers one, both lanes count and sum their own
+      // magnitudes >= each candidate, and the pair adds its halves
+      float best_e = -1.f, best_th = 0.f, best_s = 0.f, best_j = 1.f;
+#pragma unroll 1
+      for (int i = 0; i < 64; ++i) {
+        // candidate i of this lane, picked with selects (an indexed read would
+        // move v to scratch memory)
+        float cand = 0.f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) cand = e == i ? v[e] : cand;
+        float th_lo, th_hi;
+        swap_halves(__builtin_fabsf(cand), th_lo, th_hi);
+        float c_lo = 0.f, s_lo = 0.f, c_hi = 0.f, s_hi = 0.f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+          const float x = __builtin_fabsf(v[e]);
+          const bool g_lo = x >= th_lo, g_hi = x >= th_hi;
+          c_lo += g_lo ? 1.f : 0.f;
+          s_lo += g_lo ? x : 0.f;
+          c_hi += g_hi ? 1.f : 0.f;
+          s_hi += g_hi ? x : 0.f;
+        }
+        // totals over the pair (the same two terms in both lanes, so the same sums)
+        float a0, a1, b0, b1, d0, d1, f0, f1;
+        swap_halves(c_lo, a0, a1);
+        swap_halves(s_lo, b0, b1);
+        swap_halves(c_hi, d0, d1);
+        swap_halves(s_hi, f0, f1);
+        const float cl = a0 + a1, sl = b0 + b1, ch = d0 + d1, sh = f0 + f1;
+        const float el = sl * sl / cl, eh = sh * sh / ch;
+        if (el > best_e || (el == best_e && th_lo > best_th)) { best_e = el; best_th = th_lo; best_s = sl; best_j = cl; }
+        if (eh > best_e || (eh == best_e && th_hi > best_th)) { best_e = eh; best_th = th_hi; best_s = sh; best_j = ch; }
+      }
+      const float s = best_s / best_j * 0.0078125f;  // mean kept |T| / 128
+      u32x4 words = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const uint32_t nz = (__builtin_fabsf(v[j]) >= best_th && v[j] != 0.f) ? 1u : 0u;
+        const uint32_t ng = (nz && v[j] < 0.f) ? 2u : 0u;
+        words[j >> 4] |= (nz | ng) << field_pos(j & 15);
+      }
+      uint32_t* tile = codes + ((grow >> 4) * kblocks + bk) * 128 + 2 * (grow & 15);
+      *reinterpret_cast<u32x2*>(tile + 64 * half) = u32x2{words[0], words[1]};
+      *reinterpret_cast<u32x2*>(tile + 64 * half + 32) = u32x2{words[2], words[3]};
+      if (half == 0) {
+        const uint32_t h16 = f32_to_f16_bits(s);
+        if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
+        scales[grow * kblocks + bk] = (uint16_t)h16;
+      }
+    } else if constexpr (RULE == kAbsmean) {
       float asum = 0.f;
 #pragma unroll
       for (int j = 0; j < 64; ++j) asum += __builtin_fabsf(v[j]);
@@ -201,11 +261,14 @@ hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uin
   const int64_t cap = 1 << 20;
   const unsigned grid = (unsigned)(nblk < cap ? nblk : cap);
   if (fmt == TB_FMT_24)
-    hipLaunchKernelGGL((quantize128_kernel<true>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta, scales,
-                       err_flag);
+    hipLaunchKernelGGL((quantize128_kernel<kTwoFour>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,
+                       scales, err_flag);
+  else if (fmt == TB_FMT_DENSE_MINERR)
+    hipLaunchKernelGGL((quantize128_kernel<kMinError>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,
+                       scales, err_flag);
   else
-    hipLaunchKernelGGL((quantize128_kernel<false>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta, scales,
-                       err_flag);
+    hipLaunchKernelGGL((quantize128_kernel<kAbsmean>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,
+                       scales, err_flag);
   return hipGetLastError();
 }
 

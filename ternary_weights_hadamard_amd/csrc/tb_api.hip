@@ -87,7 +87,8 @@ size_t tb_act8_bytes(int64_t B, int64_t K) {
 
 tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
                           size_t* scale_bytes) {
-  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24) return TB_ERR_FORMAT;
+  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR) return TB_ERR_FORMAT;
+  if (fmt == TB_FMT_DENSE_MINERR) fmt = TB_FMT_DENSE;
   if (!dims_ok(N, K)) return TB_ERR_SHAPE;
   const size_t nk = (size_t)N * (size_t)K;
   if (code_bytes) *code_bytes = fmt == TB_FMT_DENSE ? nk / 4 : nk / 16;
@@ -128,14 +129,15 @@ tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, 
 
 tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
                            uint16_t* scales, int32_t* err_flag, void* stream) {
-  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24) return TB_ERR_FORMAT;
-  if (fmt == TB_FMT_DENSE && meta) return TB_ERR_FORMAT;
+  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR) return TB_ERR_FORMAT;
+  if (fmt != TB_FMT_24 && meta) return TB_ERR_FORMAT;
   if (!dims_ok(N, K)) return TB_ERR_SHAPE;
   if (!W || !codes || !scales || (fmt == TB_FMT_24 && !meta)) return TB_ERR_NULL;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(scales) || (meta && !aligned16(meta))) return TB_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(err_flag) & 3u) != 0) return TB_ERR_ALIGN;
   const size_t nk = (size_t)N * (size_t)K;
-  const size_t cb = fmt == TB_FMT_DENSE ? nk / 4 : nk / 16, mb = fmt == TB_FMT_DENSE ? 0 : nk / 8, sb = nk / 64;
+  const bool dense = fmt != TB_FMT_24;
+  const size_t cb = dense ? nk / 4 : nk / 16, mb = dense ? 0 : nk / 8, sb = nk / 64;
   if (overlap(W, nk * 4, codes, cb) || overlap(W, nk * 4, scales, sb) || overlap(codes, cb, scales, sb) ||
       (meta && (overlap(W, nk * 4, meta, mb) || overlap(meta, mb, codes, cb) || overlap(meta, mb, scales, sb))))
     return TB_ERR_ALIAS;

@@ -23,7 +23,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtb.so")
 
 TB_F32, TB_BF16, TB_ACT8 = 0, 1, 2
-TB_FMT_DENSE, TB_FMT_24 = 0, 1
+TB_FMT_DENSE, TB_FMT_24, TB_FMT_DENSE_MINERR = 0, 1, 2
 TB_EFLAG_NONFINITE, TB_EFLAG_SCALE_OVF = 1, 2
 TB_GEMV_MAX_BATCH = 16
 TB_MAX_SEGMENTS = 8
@@ -163,7 +163,7 @@ def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, er
     n, k = w.shape
     dev = w.device
     if codes is None:
-        shape = (n // 16, k // 128, 128) if fmt == TB_FMT_DENSE else (n, k // 64)
+        shape = (n // 16, k // 128, 128) if fmt != TB_FMT_24 else (n, k // 64)
         codes = torch.empty(shape, dtype=torch.int32, device=dev)
     if meta is None and fmt == TB_FMT_24:
         meta = torch.empty((n, k // 32), dtype=torch.int32, device=dev)

@@ -108,3 +108,76 @@ def test_24_matches_oracle(n, k, seed):
     assert not bad.any()
     ulp = np.abs(host_u16(scales).astype(np.int64) - ref["scales"].astype(np.int64))
     assert ulp.max() <= 1
+
+
+# ---------------------------------------------------------------- error-minimising rule
+
+def _check_minerr(codes, scales, w, what):
+    """Codes and scales of TB_FMT_DENSE_MINERR against the oracle.  Groups whose
+    best and second-best thresholds are within float rounding (near ties) may
+    take either: for them the GPU's kept set must be threshold-shaped and its
+    float64 objective within 1e-5 of the best.  Elsewhere codes are bit-exact
+    except elements within 1e-5 of the threshold; scales equal or 1 ulp."""
+    ref = oracle.quant.quantize_dense_mse(w.astype(np.float64))
+    n, k = w.shape
+    wr = ref["wr"]
+    t_gpu = oracle.quant.unpack_dense(host_u32(codes), k)
+    tie = oracle.quant.near_tie_mse(wr)                                # [n, k/128]
+    near = oracle.quant.near_threshold_mse(wr, ref["theta"])           # [n, k]
+    tie_el = np.repeat(tie, 128, axis=1)
+    bad = (t_gpu != ref["t"]) & ~near & ~tie_el
+    # every kept element's sign agrees with W'
+    assert np.all((t_gpu == 0) | (np.sign(wr) == t_gpu) | (np.abs(wr) <= 1e-12)), f"{what}: sign of a kept element"
+    # near-tie groups: threshold-shaped and near-optimal
+    a = np.abs(wr).reshape(n, k // 128, 128)
+    kept = (t_gpu != 0).reshape(n, k // 128, 128)
+    j = kept.sum(axis=2)
+    S = np.where(kept, a, 0).sum(axis=2)
+    obj = np.where(j > 0, S * S / np.maximum(j, 1), 0.0)
+    _, jb, Sb = oracle.quant.mse_threshold(a)
+    best = Sb * Sb / jb
+    lo_kept = np.where(kept, a, np.inf).min(axis=2)
+    hi_drop = np.where(~kept & (a > 0), a, 0).max(axis=2)
+    shaped = lo_kept >= hi_drop * (1 - 1e-5)
+    near_opt = obj >= best * (1 - 1e-5)
+    sg = host_u16(scales).astype(np.int64)
+    sr = ref["scales"].astype(np.int64)
+    s_ok = np.abs(sg - sr) <= 1
+    # in near-tie groups the scale belongs to the GPU's own kept set
+    own = oracle.numerics.f64_to_f16_bits(np.where(j > 0, S / np.maximum(j, 1), 0.0)).astype(np.int64)
+    s_ok_tie = np.abs(sg - own) <= 1
+    say(f"  {what}: {int(tie.sum())} near-tie groups of {tie.size}, {int(near.sum())} near-threshold elements, "
+        f"{int(bad.sum())} mismatches elsewhere")
+    assert not bad.any(), f"{what}: {int(bad.sum())} code mismatches outside near ties and the threshold band"
+    assert np.all(shaped | (j == 0)), f"{what}: a kept set that is not threshold-shaped"
+    assert np.all(near_opt[tie]), f"{what}: a near-tie group more than 1e-5 from the best objective"
+    assert np.all(s_ok[~tie]) and np.all(s_ok_tie[tie]), f"{what}: scale beyond 1 ulp"
+    return ref
+
+
+@pytest.mark.parametrize("n,k,seed", [(128, 128, 11), (256, 384, 12), (1024, 1024, 0), (384, 1280, 13)])
+def test_minerr_matches_oracle(n, k, seed):
+    w = synth.single_layer_weights(n, k, seed=seed) if seed == 0 else synth.stack_weights(n, k, seed=seed)
+    say(f"quantize min-error {n}x{k} seed {seed}")
+    codes, meta, scales = _quant(w, fmt=tb.TB_FMT_DENSE_MINERR)
+    assert meta is None
+    _check_minerr(codes, scales, w, f"min-error {n}x{k}")
+
+
+def test_minerr_closed_forms_and_lower_error_than_absmean():
+    w = synth.stack_weights(256, 512, seed=21)
+    w[:128, :128] = 0.0                                   # all-zero block: codes 0, scale 0
+    w[5, 130] = 3.0                                       # a spike: lossless
+    codes, _, scales = _quant(w, fmt=tb.TB_FMT_DENSE_MINERR)
+    ref = _check_minerr(codes, scales, w, "min-error closed forms")
+    s = host_u16(scales)
+    assert np.all(s[:128, 0] == 0) and np.all(host_u32(codes)[:8, 0] == 0)
+    # reconstruction error in the rotated domain: never above the absmean rule's
+    ca, _, sa = _quant(w)
+    wr = ref["wr"]
+    f16 = lambda b: b.view(np.float16).astype(np.float64)
+    err = lambda t, sc: np.sum((wr - np.repeat(f16(host_u16(sc)), 128, axis=1) * t) ** 2)
+    e_min = err(oracle.quant.unpack_dense(host_u32(codes), 512), scales)
+    e_abs = err(oracle.quant.unpack_dense(host_u32(ca), 512), sa)
+    say(f"  squared error: min-error rule {e_min:.4e}, absmean rule {e_abs:.4e}")
+    assert e_min < e_abs
