@@ -22,9 +22,10 @@ Modules
 ``numerics``  fp16 / bf16 round-to-nearest-even by integer bit operations.
 ``hadamard``  H by the bit rule and by Sylvester's recursion; blockwise FWHT128
               (dense matmul and butterfly forms); the 2D block rotation.
-``quant``     absmean group scale, ternarisation, dense and 2:4 packing.
-``matvec``    the ternary GEMV / GEMM / 2:4 GEMV definitions (dequantise,
-              then a float64 matmul) and brute-force loop versions.
+``quant``     absmean group scale, ternarisation, dense and 2:4 packing; the
+              error-minimising threshold rule; the residual second plane.
+``matvec``    the ternary GEMV / GEMM / 2:4 GEMV / two-plane GEMV definitions
+              (dequantise, then a float64 matmul) and brute-force loop versions.
 ``bits``      bits-per-weight ledger and packed buffer sizes.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``

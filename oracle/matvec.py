@@ -14,7 +14,7 @@ brute-force forms are explicit Python loops for tiny shapes.
 import numpy as np
 
 from .numerics import bf16_bits_to_f64, f16_bits_to_f64
-from .quant import GROUP, dense_from_24, unpack_24, unpack_dense
+from .quant import GROUP, dense_from_24, split_planes, unpack_24, unpack_dense
 
 
 def _x(x_bf16_bits):
@@ -36,6 +36,20 @@ def gemv(x_bf16_bits, codes, scales, k):
 
 # the prefill GEMM is the same contraction for M rows of activations
 gemm = gemv
+
+
+def dequant_residual(codes, scales, k):
+    """W~[n, k] = f16(s1[n, g]) t1[n, k] + f16(s2[n, g]) t2[n, k] for the
+    two-plane format (groups of the planes interleaved, quant.interleave_planes)."""
+    c1, c2 = split_planes(codes)
+    s1, s2 = split_planes(scales)
+    return dequant_dense(c1, s1, k) + dequant_dense(c2, s2, k)
+
+
+def gemv_residual(x_bf16_bits, codes, scales, k):
+    """y'[m, n] = sum_g sum_p f16(s_p[n, g]) sum_{k in g} t_p[n, k] x'[m, k] over
+    both planes p of the two-plane format."""
+    return np.matmul(_x(x_bf16_bits), dequant_residual(codes, scales, k).T)
 
 
 def dequant_24(meta, signs, scales, k):

@@ -20,6 +20,9 @@ Definitions followed (readings of the pages are listed in the design doc):
   maximises S^2 / j over the kept sets {|w'| >= theta}.  The 0.38-quantile
   threshold of dpshk.com §3.2 step 4 is one member of this family (it keeps
   the largest 79 of 128).  Ties in S^2 / j go to the larger theta.
+* Residual plane: the part of W' the first ternary plane misses, W' minus its
+  fp16 scale times t, is ternarised again by the absmean rule (the residual
+  calibration of xxqk.cn/news/652513 §3), giving W' ~ s1 t1 + s2 t2.
 * 2:4: of every 4 consecutive K-elements keep the 2 largest |w'| and ternarise
   the survivors (mhpq.cn §1.2: prune with the 2:4 pattern, then ternarise what
   remains).  Kept elements are nonzero, so each carries only a sign; the group
@@ -39,6 +42,9 @@ Dense format (N a multiple of 16, K a multiple of 128):
   and fields r >= 8 in bits 0-1 of nibble r - 8.  Field value: 0b00 -> 0,
   0b01 -> +1, 0b11 -> -1 (bit 0 = nonzero, bit 1 = negative); 0b10 is invalid.
   scales[n][k // 128] fp16 bits.
+Residual (two-plane) format: the dense format of both planes with their
+  groups interleaved along K (interleave_planes), codes [N/16][2 K/128][128] and
+  scales [N][2 K/128].
 2:4 format:
   meta[n][q // 8] uint32 for quad q = k // 4: the nibble at bits 4 * (q % 8)
   holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1 the kept positions.
@@ -50,7 +56,7 @@ Dense format (N a multiple of 16, K a multiple of 128):
 import numpy as np
 
 from .hadamard import BLOCK, rotate_blocks
-from .numerics import f64_to_f16_bits
+from .numerics import f16_bits_to_f64, f64_to_f16_bits
 
 GROUP = 128
 NEAR_REL = 1e-5
@@ -210,6 +216,55 @@ def near_tie_mse(wr, rel=NEAR_REL):
     rel (relative): float rounding may pick either threshold."""
     n, k = wr.shape
     return mse_objective_gap(np.abs(wr).reshape(n, k // GROUP, GROUP)) <= rel
+
+
+# ---------------------------------------------------------------- residual second plane
+
+def interleave_planes(a, b):
+    """Per-group interleave of two planes along the group axis (axis 1): the
+    result's group 2 g is a's group g and group 2 g + 1 is b's.  Works for
+    codes [N/16, G, 128] and for scales [N, G]."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.shape != b.shape:
+        raise ValueError("planes differ in shape")
+    return np.stack([a, b], axis=2).reshape(a.shape[0], 2 * a.shape[1], *a.shape[2:])
+
+
+def split_planes(x):
+    """Inverse of interleave_planes: (plane 1, plane 2)."""
+    x = np.asarray(x)
+    return x[:, 0::2], x[:, 1::2]
+
+
+def quantize_dense_residual(w):
+    """Two ternary planes, W' ~ f16(s1) t1 + f16(s2) t2: the residual
+    calibration of xxqk.cn/news/652513 §3, which stores the difference between
+    the rotated coefficients and their ternary approximation and ternarises it
+    once more.
+
+    Plane 1 is quantize_dense's absmean rule.  The residual is taken against
+    what the product will apply, the stored fp16 scale:
+        d = W' - f16(s1) t1,
+    and stays in the rotated basis, so both planes multiply the same rotated
+    activations.  Plane 2 is the absmean rule applied to d: s2 = mean |d| per
+    group, t2 = +-1 where |d| > s2 / 2, fp16 scale.
+
+    Storage (interleave_planes): codes [N/16][2 K/128][128] and scales
+    [N][2 K/128], where group 2 g + p holds plane p's group g (p = 0 first).
+
+    Returns codes, scales, and wr, s1, t1, d, s2, t2 (float64 / int8)."""
+    w = _check_w(w)
+    wr = rotate_blocks(w)
+    s1 = absmean_scales(wr)
+    t1 = ternarize(wr, s1)
+    sc1 = f64_to_f16_bits(s1)
+    d = wr - t1 * np.repeat(f16_bits_to_f64(sc1), GROUP, axis=1)
+    s2 = absmean_scales(d)
+    t2 = ternarize(d, s2)
+    sc2 = f64_to_f16_bits(s2)
+    return {"codes": interleave_planes(pack_dense(t1), pack_dense(t2)), "scales": interleave_planes(sc1, sc2),
+            "wr": wr, "s1": s1, "t1": t1, "d": d, "s2": s2, "t2": t2}
 
 
 # ---------------------------------------------------------------- 2:4 variant

@@ -120,3 +120,29 @@ def test_random_codes_distribution():
     t = q.unpack_dense(codes, 1024)
     p = [np.mean(t == v) for v in (-1, 0, 1)]
     assert np.allclose(p, (0.35, 0.30, 0.35), atol=0.005)
+
+
+def test_gemv_residual_two_plane_cases():
+    # exact two-plane rows (golden residual example): W' = s1 t1 + s2 t2 with
+    # s1 = 0.75, s2 = 0.25 and t1 = +1, t2 = +1 / -1 gives W' = 1 / 0.5; the
+    # product over both planes must then be W' x, computed without the codes
+    rng = np.random.default_rng(8)
+    n, k = 32, 256
+    wr = np.where(rng.random((n, k)) < 0.5, 1.0, 0.5) * np.where(rng.random((n, 1)) < 0.5, 1.0, -1.0)
+    t1 = np.sign(wr).astype(np.int8)
+    t2 = np.where(np.abs(wr) == 1.0, 1, -1).astype(np.int8) * t1
+    s1 = np.full((n, k // 128), np.float16(0.75)).view(np.uint16)
+    s2 = np.full((n, k // 128), np.float16(0.25)).view(np.uint16)
+    codes = q.interleave_planes(q.pack_dense(t1), q.pack_dense(t2))
+    scales = q.interleave_planes(s1, s2)
+    x = nu.f64_to_bf16_bits(rng.standard_normal((3, k)))
+    xf = nu.bf16_bits_to_f64(x)
+    assert np.array_equal(mv.gemv_residual(x, codes, scales, k), xf @ wr.T)
+    # a zero second plane leaves the one-plane product
+    z = q.interleave_planes(q.pack_dense(t1), q.pack_dense(np.zeros_like(t1)))
+    zs = q.interleave_planes(s1, np.zeros_like(s2))
+    assert np.array_equal(mv.gemv_residual(x, z, zs, k), mv.gemv(x, q.pack_dense(t1), s1, k))
+    # the planes add: swapping them changes nothing
+    sw = q.interleave_planes(q.pack_dense(t2), q.pack_dense(t1))
+    ss = q.interleave_planes(s2, s1)
+    assert np.allclose(mv.gemv_residual(x, sw, ss, k), xf @ wr.T, rtol=0, atol=1e-12)

@@ -331,3 +331,83 @@ def test_mse_near_tie_groups_are_a_small_minority():
     wr = q.quantize_dense_mse(w)["wr"]
     frac = q.near_tie_mse(wr).mean()
     assert frac < 0.1
+
+
+# ---------------------------------------------------------------- residual second plane
+
+def _runs(text):
+    out = []
+    for run in text.split():
+        v, n = run.split("x")
+        out += [float(v)] * int(n)
+    assert len(out) == 128, text
+    return np.array(out)
+
+
+def _residual_golden(golden_dir):
+    rows = []
+    for line in open(os.path.join(golden_dir, "residual_plane.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, wr, s1, t1, s2, t2, err = [f.strip() for f in line.split("|")]
+            rows.append((name, _runs(wr), float(s1), _runs(t1), float(s2), _runs(t2), float(err)))
+    return rows
+
+
+def test_residual_plane_hand_worked(golden_dir):
+    types = _residual_golden(golden_dir)
+    wr = np.stack([types[r % len(types)][1] for r in range(128)])
+    wr = np.concatenate([wr, wr[::-1]], axis=0)  # 256 rows: two 128-row blocks
+    r = q.quantize_dense_residual(_from_rotated(wr))
+    assert np.array_equal(r["wr"], wr)
+    for row in range(wr.shape[0]):
+        name, _, s1, t1, s2, t2, err = types[(row if row < 128 else 255 - row) % len(types)]
+        # the fixture's scales are the stored fp16 values
+        assert float(np.float16(r["s1"][row, 0])) == s1, name
+        assert np.array_equal(r["t1"][row], t1), name
+        assert float(np.float16(r["s2"][row, 0])) == s2, name
+        assert np.array_equal(r["t2"][row], t2), name
+        recon = s1 * t1 + s2 * t2
+        assert np.sum((wr[row] - recon) ** 2) == err, name
+    # the packed planes and scales say the same
+    c1, c2 = q.split_planes(r["codes"])
+    sc1, sc2 = q.split_planes(r["scales"])
+    assert np.array_equal(q.unpack_dense(c1, 128), r["t1"])
+    assert np.array_equal(q.unpack_dense(c2, 128), r["t2"])
+    want_s1 = np.array([types[(row if row < 128 else 255 - row) % len(types)][2] for row in range(256)])
+    want_s2 = np.array([types[(row if row < 128 else 255 - row) % len(types)][4] for row in range(256)])
+    assert np.array_equal(sc1[:, 0], want_s1.astype(np.float16).view(np.uint16))
+    assert np.array_equal(sc2[:, 0], want_s2.astype(np.float16).view(np.uint16))
+
+
+def test_residual_interleave_layout():
+    # group 2g of the interleaved format is plane 1's group g, 2g + 1 plane 2's
+    a = np.arange(2 * 3 * 4).reshape(2, 3, 4)
+    b = 100 + a
+    x = q.interleave_planes(a, b)
+    assert x.shape == (2, 6, 4)
+    for g in range(3):
+        assert np.array_equal(x[:, 2 * g], a[:, g]) and np.array_equal(x[:, 2 * g + 1], b[:, g])
+    p1, p2 = q.split_planes(x)
+    assert np.array_equal(p1, a) and np.array_equal(p2, b)
+    s = q.interleave_planes(np.array([[1, 2]]), np.array([[7, 8]]))
+    assert s.tolist() == [[1, 7, 2, 8]]
+
+
+def test_residual_plane_lowers_the_error_and_keeps_plane_one():
+    rng = np.random.default_rng(41)
+    w = rng.standard_normal((256, 384)) * 0.02
+    r = q.quantize_dense_residual(w)
+    one = q.quantize_dense(w)
+    # plane 1 is exactly the one-plane quantiser
+    assert np.array_equal(r["t1"], one["t"]) and np.array_equal(q.split_planes(r["scales"])[0], one["scales"])
+    s1 = np.repeat(q.split_planes(r["scales"])[0].view(np.float16).astype(np.float64), 128, axis=1)
+    s2 = np.repeat(q.split_planes(r["scales"])[1].view(np.float16).astype(np.float64), 128, axis=1)
+    e1 = ((r["wr"] - s1 * r["t1"]) ** 2).reshape(256, 3, 128).sum(axis=2)
+    e2 = ((r["wr"] - s1 * r["t1"] - s2 * r["t2"]) ** 2).reshape(256, 3, 128).sum(axis=2)
+    # per group: -2 s2 sum_kept |d| + s2^2 j < 0 since every kept |d| > s2 / 2
+    # (up to the fp16 rounding of s2, relative 2^-11)
+    assert np.all(e2 < e1 * (1 + 1e-3))
+    assert np.sum(e2) < 0.5 * np.sum(e1)
+    # the residual of a Gaussian group is again spread out: plane 2 keeps most
+    # elements (|d| > mean |d| / 2)
+    assert 0.5 < np.mean(r["t2"] != 0) < 0.9
