@@ -75,8 +75,10 @@ typedef enum {
 
 typedef enum { TB_F32 = 0, TB_BF16 = 1, TB_ACT8 = 2 } tb_dtype;
 /* Quantiser rules and storage formats.  TB_FMT_DENSE_MINERR stores the dense
- * format; only the threshold and scale rule differ (tb_quantize_pack). */
-typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2 } tb_format;
+ * format; only the threshold and scale rule differ (tb_quantize_pack).
+ * TB_FMT_DENSE_RESID stores two dense planes with their 128-groups
+ * interleaved along K (the two-plane format, see tb_quantize_pack). */
+typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_DENSE_RESID = 3 } tb_format;
 
 /* Bits OR-ed into the optional device error flag of tb_quantize_pack. */
 #define TB_EFLAG_NONFINITE 1u /* a non-finite weight was seen; its block's codes are unspecified */
@@ -114,7 +116,9 @@ typedef struct {
 } tb_fwht_segment;
 
 /* One product of a grouped tb_ternary_gemv_multi call: arguments as in
- * tb_ternary_gemv. */
+ * tb_ternary_gemv.  `planes` is 1 for the one-plane dense formats (0 is read
+ * as 1) and 2 for two-plane codes and scales (TB_FMT_DENSE_RESID, as
+ * tb_ternary_gemv_resid takes them); anything else returns TB_ERR_FORMAT. */
 typedef struct {
   const uint8_t* act;
   int64_t B;
@@ -123,6 +127,7 @@ typedef struct {
   int64_t N;
   int64_t K;
   float* y;
+  int64_t planes;
 } tb_gemv_segment;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -135,7 +140,8 @@ TB_API int tb_version(void);
  * Sizes in bytes of the packed planes of an [N][K] matrix in format `fmt`
  * (tb_format).  Dense (both rules): code_bytes = N*K/4, meta_bytes = 0.  2:4: code_bytes
  * (the sign plane) = N*K/16, meta_bytes = N*K/8.  scale_bytes = N*K/64 for
- * both.  Any output pointer may be NULL.  Host-only.
+ * both.  Two-plane (TB_FMT_DENSE_RESID): code_bytes = N*K/2, meta_bytes = 0,
+ * scale_bytes = N*K/32.  Any output pointer may be NULL.  Host-only.
  * Cites the 2-bit storage of mhpq.cn/news/1159370 §3.1 and the bit ledger of §1.3.
  */
 TB_API tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
@@ -187,10 +193,18 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_
  * j its size), t = sign(W') on it, s = S / j; ties go to the larger theta.
  * The 0.38-quantile threshold of dpshk.com §3.2 step 4 is one of the
  * candidates (it keeps the largest 79 of 128).
+ * TB_FMT_DENSE_RESID adds a second ternary plane for what the first misses
+ * (the residual calibration of xxqk.cn/news/652513 §3): plane 1 is the
+ * absmean rule above; the residual d = W' - fp16(s1) t1 (against the stored
+ * scale, in the rotated basis) is ternarised by the same rule, giving
+ * W' ~ fp16(s1) t1 + fp16(s2) t2.  Storage: the dense format of both planes
+ * with their groups interleaved, codes [N/16][2K/128][128] and scales
+ * [N][2K/128], where group 2g + p is plane p's group g.
  *   W       fp32 [N][K]
- *   codes   dense: [N][K/16] code words; 2:4: the sign plane [N][K/64]
+ *   codes   dense: [N][K/16] code words; two-plane: [N][K/8]; 2:4: the sign
+ *           plane [N][K/64]
  *   meta    2:4: [N][K/32]; must be NULL for the dense formats (else TB_ERR_FORMAT)
- *   scales  fp16 bits [N][K/128]
+ *   scales  fp16 bits [N][K/128]; two-plane: [N][2K/128]
  *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
  *             (the caller zeroes it first).
  * Arithmetic is fp32; the absmean threshold uses the unrounded scale.
@@ -223,6 +237,18 @@ TB_API tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* 
  * [0, TB_MAX_SEGMENTS] returns TB_ERR_SHAPE.
  */
 TB_API tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* stream);
+
+/*
+ * Decode GEMV with two-plane dense ternary weights (TB_FMT_DENSE_RESID, the
+ * residual calibration of xxqk.cn/news/652513 §3):
+ *   y[b][n] = sum_g sum_p fp16(s_p[n][g]) * sum_{k in g} t_p[n][k] * x[b][k]
+ *   codes   [N/16][2K/128][128], scales [N][2K/128]: group 2g + p is plane
+ *           p's group g (as tb_quantize_pack writes them)
+ *   act, B, y and the error rules as tb_ternary_gemv; K is the activation
+ *   length.  Both planes' products are exact and accumulated in fp32.
+ */
+TB_API tb_status tb_ternary_gemv_resid(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                                int64_t N, int64_t K, float* y, void* stream);
 
 /*
  * Bytes of the TB_ACT8 activation operand for B rows of K activations:

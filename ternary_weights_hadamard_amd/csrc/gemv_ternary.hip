@@ -48,14 +48,15 @@ template <int NB4, int CH>
 __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint8_t* __restrict__ act, int B,
                                                                         const uint32_t* __restrict__ codes,
                                                                         const uint16_t* __restrict__ scales,
-                                                                        int64_t N, int64_t K,
+                                                                        int64_t N, int64_t K, int P,
                                                                         float* __restrict__ y, int KS) {
   __shared__ float red[kMaxSlices][NB4][64];
   const int lane = threadIdx.x & 63;
   const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, q = lane >> 4;
   const int64_t nb = blockIdx.x;
-  const int G = (int)(K / kBlock);
+  const int GA = (int)(K / kBlock);  // activation groups per row
+  const int G = GA * P;              // code and scale groups per row (P planes)
   const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
 
   // activation operand rows of this lane: batch 4m + i/4, sub-row i % 4
@@ -66,7 +67,7 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint
   for (int m = 0; m < NB4; ++m) {
     const int b = 4 * m + (i >> 2);
     arow[m] = b < B;
-    const size_t row = (size_t)(arow[m] ? b : 0) * G;
+    const size_t row = (size_t)(arow[m] ? b : 0) * GA;
     av_base[m] = act + (row * 16 + (i & 3) * 4 + q) * 32;
     as_base[m] = act + (size_t)4 * B * K + row * 16 + (i & 3) * 4 + q;
   }
@@ -89,16 +90,17 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int g = min(c + j, ge - 1);
+      const int ga = P == 1 ? g : g >> 1;  // the activation group of code group g
       cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)g * 128);
       sw[j] = sp[g];
 #pragma unroll
       for (int m = 0; m < NB4; ++m) {
         if (arow[m]) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(av_base[m] + (size_t)g * 512);
+          const u32x4* p = reinterpret_cast<const u32x4*>(av_base[m] + (size_t)ga * 512);
           const u32x4 lo = p[0], hi = p[1];
           av[j][m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          as[j][m] = as_base[m][(size_t)g * 16];
+          as[j][m] = as_base[m][(size_t)ga * 16];
         } else {
           av[j][m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
           as[j][m] = 127;
@@ -176,6 +178,7 @@ struct StagedSeg {
 struct StagedSegs {
   StagedSeg s[kMaxSegs];
   int count, bmax;
+  int stage_groups;  // activation groups staged per wave and batch row (two planes)
 };
 
 // the segment of this workgroup, selected field by field (the index is
@@ -199,7 +202,8 @@ __device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) {
   return r;
 }
 
-template <int CH, int BMAX>
+// P code planes per segment (1, or 2 with the planes' groups interleaved)
+template <int CH, int BMAX, int P>
 __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs segs) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const StagedSeg sg = pick_segment(segs);
@@ -213,14 +217,18 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
   const int i = lane & 15, q = lane >> 4;
   const int64_t nb = (int64_t)(blockIdx.x - sg.wg_begin) * (waves / KS) + w / KS;
   const bool live = nb < N / 16;
-  const int G = (int)(K / kBlock);
+  const int GA = (int)(K / kBlock);  // activation groups per row
+  const int G = GA * P;              // code and scale groups per row
   const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
-  const int n = ge - gb;  // 1 .. CH groups in this slice
+  const int n = ge - gb;  // 1 .. CH code groups in this slice
+  // activation groups of the slice: code group g multiplies activation group g / P
+  const int ab = gb / P, na = (ge - 1) / P - ab + 1;
   constexpr int kPairs = (CH + 1) / 2;
   constexpr int kScaleRegs = (CH + 3) / 4;
-  const size_t region = (size_t)segs.bmax * CH * kStageBytes;
-  unsigned char* st = smem + (size_t)w * region;  // [B][CH][512] values, then [B][CH][16] scales
-  unsigned char* st_sc = st + (size_t)B * CH * 512;
+  const int SG = P == 1 ? CH : segs.stage_groups;  // >= na
+  const size_t region = (size_t)segs.bmax * SG * kStageBytes;
+  unsigned char* st = smem + (size_t)w * region;  // [B][SG][512] values, then [B][SG][16] scales
+  unsigned char* st_sc = st + (size_t)B * SG * 512;
   float* red = reinterpret_cast<float*>(smem + (size_t)waves * region);
 
   float acc = 0.f;
@@ -230,14 +238,14 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
     u32x4 as_st[BMAX];
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) {
-      const unsigned char* src = act + ((size_t)b * G + gb) * 512;
+      const unsigned char* src = act + ((size_t)b * GA + ab) * 512;
 #pragma unroll
       for (int t = 0; t < kPairs; ++t) {
         const int off = t * 1024 + lane * 16;
-        if (b < B && off < n * 512) av_st[b][t] = *reinterpret_cast<const u32x4*>(src + off);
+        if (b < B && off < na * 512) av_st[b][t] = *reinterpret_cast<const u32x4*>(src + off);
       }
-      if (b < B && lane < n)
-        as_st[b] = *reinterpret_cast<const u32x4*>(act + (size_t)4 * B * K + ((size_t)b * G + gb + lane) * 16);
+      if (b < B && lane < na)
+        as_st[b] = *reinterpret_cast<const u32x4*>(act + (size_t)4 * B * K + ((size_t)b * GA + ab + lane) * 16);
     }
     // 2. codes, one 8-byte load per lane and group (slots past the slice repeat its last group)
     const uint32_t* cp = sg.codes + (size_t)nb * G * 128 + 2 * lane;
@@ -256,9 +264,9 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
 #pragma unroll
       for (int t = 0; t < kPairs; ++t) {
         const int off = t * 1024 + lane * 16;
-        if (b < B && off < n * 512) *reinterpret_cast<u32x4*>(st + (size_t)b * CH * 512 + off) = av_st[b][t];
+        if (b < B && off < na * 512) *reinterpret_cast<u32x4*>(st + (size_t)b * SG * 512 + off) = av_st[b][t];
       }
-      if (b < B && lane < n) *reinterpret_cast<u32x4*>(st_sc + ((size_t)b * CH + lane) * 16) = as_st[b];
+      if (b < B && lane < na) *reinterpret_cast<u32x4*>(st_sc + ((size_t)b * SG + lane) * 16) = as_st[b];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -267,15 +275,17 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
     //    Rows of batches >= B only reach output rows that are never stored, so
     //    those lanes read the last batch row instead of branching.
     const int bp = min(i >> 2, B - 1);
-    const unsigned char* a_src = st + (size_t)bp * CH * 512 + ((i & 3) * 4 + q) * 32;
-    const unsigned char* a_sc = st_sc + (size_t)bp * CH * 16 + (i & 3) * 4 + q;
+    const unsigned char* a_src = st + (size_t)bp * SG * 512 + ((i & 3) * 4 + q) * 32;
+    const unsigned char* a_sc = st_sc + (size_t)bp * SG * 16 + (i & 3) * 4 + q;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(a_src + j * 512);
+      // staged activation group of slot j (slots past the slice repeat the last one)
+      const int aj = P == 1 ? j : (min(gb + j, ge - 1) >> 1) - ab;
+      const u32x4* p = reinterpret_cast<const u32x4*>(a_src + aj * 512);
       const u32x4 lo = p[0], hi = p[1];
       const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int as = a_sc[j * 16];
+      const int as = a_sc[aj * 16];
       const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * (j & 3)) * 4, (int)sr[j >> 2]);
       const float s = f16_bits_to_f32((uint32_t)sbits & 0xFFFFu) * 0.5f;
       const uint32_t w0 = cw[j][0], w1 = cw[j][1];
@@ -314,9 +324,9 @@ int staged_slices(int64_t K, int ch) {
 
 }  // namespace
 
-// Groups per wave of one segment, a function of its own K and B only, so that
-// a segment is cut into the same K slices (and summed in the same order)
-// whatever it is launched with.
+// Groups per wave of one segment, a function of its own code length K (all
+// planes) and B only, so that a segment is cut into the same K slices (and
+// summed in the same order) whatever it is launched with.
 int segment_ch(int64_t K, int64_t B) {
   if (B > 1) return staged_ch(4);
   const int ks = staged_slices(K, staged_ch(1));
@@ -329,20 +339,27 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
   StagedSegs st{};
   bool staged = count <= kMaxSegs;
   int bmax = 1, ch = 1, waves = 1, wg = 0;
+  const int64_t planes = count > 0 ? segs[0].planes : 1;
   for (int c = 0; c < count && staged; ++c) {
-    const int sc = segment_ch(segs[c].K, segs[c].B);
-    const int ks = staged_slices(segs[c].K, sc);
+    const int64_t kc = segs[c].K * segs[c].planes;  // code groups x 128
+    const int sc = segment_ch(kc, segs[c].B);
+    const int ks = staged_slices(kc, sc);
     if (segs[c].B > 4 || ks == 0) staged = false;
     bmax = std::max(bmax, (int)segs[c].B);
     ch = std::max(ch, sc);
     waves = std::max(waves, ks);
+    if (segs[c].planes != planes) staged = false;  // one plane count per grouped launch
   }
   // kernels exist for (10, 1), (18, 1) and (8, up to 4 rows)
   if (bmax > 1 && ch != staged_ch(4)) staged = false;
-  const size_t lds = (size_t)waves * bmax * ch * kStageBytes + (size_t)waves * 64 * sizeof(float);
+  // a slice of at most ch code groups spans at most ch activation groups with
+  // one plane, ch / 2 + 1 with two
+  const int stage_groups = planes == 1 ? ch : ch / 2 + 1;
+  const size_t lds = (size_t)waves * bmax * stage_groups * kStageBytes + (size_t)waves * 64 * sizeof(float);
   if (staged && lds <= kStagedMaxLds) {
     for (int c = 0; c < count; ++c) {
-      const int ks = staged_slices(segs[c].K, segment_ch(segs[c].K, segs[c].B));
+      const int64_t kc = segs[c].K * segs[c].planes;
+      const int ks = staged_slices(kc, segment_ch(kc, segs[c].B));
       const int64_t tiles = segs[c].N / 16, per_wg = waves / ks;
       st.s[c] = StagedSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
                           (int)segs[c].B, ks, wg, 0};
@@ -350,17 +367,30 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
     }
     st.count = count;
     st.bmax = bmax;
-    if (bmax == 1 && ch == kLongCH)
-      hipLaunchKernelGGL((gemv_staged_kernel<kLongCH, 1>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
-    else if (bmax == 1)
-      hipLaunchKernelGGL((gemv_staged_kernel<staged_ch(1), 1>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
-    else
-      hipLaunchKernelGGL((gemv_staged_kernel<staged_ch(4), 4>), dim3((unsigned)wg), dim3(64 * waves), lds, stream, st);
+    st.stage_groups = stage_groups;
+    const dim3 grid((unsigned)wg), block(64 * waves);
+#define TB_STAGED(CH_, BMAX_, P_) hipLaunchKernelGGL((gemv_staged_kernel<CH_, BMAX_, P_>), grid, block, lds, stream, st)
+    if (planes == 1) {
+      if (bmax == 1 && ch == kLongCH)
+        TB_STAGED(kLongCH, 1, 1);
+      else if (bmax == 1)
+        TB_STAGED(staged_ch(1), 1, 1);
+      else
+        TB_STAGED(staged_ch(4), 4, 1);
+    } else {
+      if (bmax == 1 && ch == kLongCH)
+        TB_STAGED(kLongCH, 1, 2);
+      else if (bmax == 1)
+        TB_STAGED(staged_ch(1), 1, 2);
+      else
+        TB_STAGED(staged_ch(4), 4, 2);
+    }
+#undef TB_STAGED
     return hipGetLastError();
   }
   if (count == 1)
     return launch_gemv_direct(segs[0].act, segs[0].B, segs[0].codes, segs[0].scales, segs[0].N, segs[0].K,
-                              segs[0].y, stream);
+                              (int)segs[0].planes, segs[0].y, stream);
   for (int c = 0; c < count; ++c) {
     const hipError_t e = launch_gemv_multi(segs + c, 1, stream);
     if (e != hipSuccess) return e;
@@ -369,42 +399,37 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
 }
 
 hipError_t launch_gemv_direct(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                              int64_t N, int64_t K, float* y, hipStream_t stream) {
+                              int64_t N, int64_t K, int planes, float* y, hipStream_t stream) {
   const dim3 grid((unsigned)(N / 16));
   const int b = (int)B;
   switch ((B + 3) / 4) {
     case 1: {
-      const int ks = slices(K, Chunk<1>::value);
+      const int ks = slices(K * planes, Chunk<1>::value);
       hipLaunchKernelGGL((gemv_direct_kernel<1, Chunk<1>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, y, ks);
+                         scales, N, K, planes, y, ks);
       break;
     }
     case 2: {
-      const int ks = slices(K, Chunk<2>::value);
+      const int ks = slices(K * planes, Chunk<2>::value);
       hipLaunchKernelGGL((gemv_direct_kernel<2, Chunk<2>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, y, ks);
+                         scales, N, K, planes, y, ks);
       break;
     }
     case 3: {
-      const int ks = slices(K, Chunk<3>::value);
+      const int ks = slices(K * planes, Chunk<3>::value);
       hipLaunchKernelGGL((gemv_direct_kernel<3, Chunk<3>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, y, ks);
+                         scales, N, K, planes, y, ks);
       break;
     }
     default: {
-      const int ks = slices(K, Chunk<4>::value);
+      const int ks = slices(K * planes, Chunk<4>::value);
       hipLaunchKernelGGL((gemv_direct_kernel<4, Chunk<4>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, y, ks);
+                         scales, N, K, planes, y, ks);
       break;
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_ternary(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                               int64_t N, int64_t K, float* y, hipStream_t stream) {
-  const GemvSegment seg{act, B, codes, scales, N, K, y};
-  return launch_gemv_multi(&seg, 1, stream);
-}
 
 }  // namespace tb

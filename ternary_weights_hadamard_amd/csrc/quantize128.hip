@@ -24,6 +24,9 @@
 //            pairs of the row's 16 x 128 tile).
 // The 1/128 of the 2D transform is a power of two; it is folded into the
 // threshold and the stored scale instead of being applied to every element.
+// The two-plane format ternarises the group once, subtracts the stored scale
+// times the codes (the residual calibration of xxqk.cn/news/652513 §3) and
+// ternarises that residual by the same rule into the next group slot.
 // The error-minimising rule evaluates every magnitude of the group as a
 // threshold: lane pair (l, l ^ 32) holds the group, exchanges one candidate of
 // each lane per step and adds both lanes' kept counts and sums.
@@ -66,7 +69,7 @@ __device__ __forceinline__ void fwht_cross_halves(float (&v)[64], float sgn) {
 // r < 8 in bits 2-3 of nibble r, r >= 8 in bits 0-1 of nibble r - 8.
 __device__ __forceinline__ constexpr int field_pos(int r) { return 4 * (r & 7) + 2 - 2 * (r >> 3); }
 
-enum Rule { kAbsmean = 0, kTwoFour = 1, kMinError = 2 };
+enum Rule { kAbsmean = 0, kTwoFour = 1, kMinError = 2, kResidual = 3 };
 
 template <int RULE>
 __global__ void __launch_bounds__(256) quantize128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
@@ -181,30 +184,45 @@ __global__ void __launch_bounds__(256) quantize128_kernel(const float* __restric
         if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
         scales[grow * kblocks + bk] = (uint16_t)h16;
       }
-    } else if constexpr (RULE == kAbsmean) {
-      float asum = 0.f;
+    } else if constexpr (RULE == kAbsmean || RULE == kResidual) {
+      // one plane, or two with their groups interleaved (group 2 bk + p)
+      constexpr int kPlanes = RULE == kResidual ? 2 : 1;
 #pragma unroll
-      for (int j = 0; j < 64; ++j) asum += __builtin_fabsf(v[j]);
-      float lo, hi;
-      swap_halves(asum, lo, hi);
-      const float tsum = lo + hi;               // sum over the 128-group of |T|
-      const float thr = tsum * 0.00390625f;     // |W'| > s/2  <=>  |T| > sum|T| / 256
-      const float s = tsum * 6.103515625e-05f;  // s = sum|T| / 128 / 128
-      u32x4 words = {0u, 0u, 0u, 0u};
+      for (int p = 0; p < kPlanes; ++p) {
+        float asum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const uint32_t nz = __builtin_fabsf(v[j]) > thr ? 1u : 0u;
-        const uint32_t ng = (nz && v[j] < 0.f) ? 2u : 0u;
-        words[j >> 4] |= (nz | ng) << field_pos(j & 15);
-      }
-      // columns 64 half + j of group bk: word pairs of lane groups 2 half and 2 half + 1
-      uint32_t* tile = codes + ((grow >> 4) * kblocks + bk) * 128 + 2 * (grow & 15);
-      *reinterpret_cast<u32x2*>(tile + 64 * half) = u32x2{words[0], words[1]};
-      *reinterpret_cast<u32x2*>(tile + 64 * half + 32) = u32x2{words[2], words[3]};
-      if (half == 0) {
+        for (int j = 0; j < 64; ++j) asum += __builtin_fabsf(v[j]);
+        float lo, hi;
+        swap_halves(asum, lo, hi);
+        const float tsum = lo + hi;               // sum over the 128-group of |T|
+        const float thr = tsum * 0.00390625f;     // |W'| > s/2  <=>  |T| > sum|T| / 256
+        const float s = tsum * 6.103515625e-05f;  // s = sum|T| / 128 / 128
+        u32x4 words = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+          const uint32_t nz = __builtin_fabsf(v[j]) > thr ? 1u : 0u;
+          const uint32_t ng = (nz && v[j] < 0.f) ? 2u : 0u;
+          words[j >> 4] |= (nz | ng) << field_pos(j & 15);
+        }
+        // columns 64 half + j of group bk: word pairs of lane groups 2 half and 2 half + 1
+        const int64_t gcol = kPlanes * bk + p;
+        uint32_t* tile = codes + ((grow >> 4) * kPlanes * kblocks + gcol) * 128 + 2 * (grow & 15);
+        *reinterpret_cast<u32x2*>(tile + 64 * half) = u32x2{words[0], words[1]};
+        *reinterpret_cast<u32x2*>(tile + 64 * half + 32) = u32x2{words[2], words[3]};
         const uint32_t h16 = f32_to_f16_bits(s);
-        if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
-        scales[grow * kblocks + bk] = (uint16_t)h16;
+        if (half == 0) {
+          if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
+          scales[grow * kPlanes * kblocks + gcol] = (uint16_t)h16;
+        }
+        if (p + 1 < kPlanes) {
+          // the residual against the stored scale, in units of T: T - 128 f16(s) t
+          const float s128 = f16_bits_to_f32(h16) * 128.f;
+#pragma unroll
+          for (int j = 0; j < 64; ++j) {
+            const float a = __builtin_fabsf(v[j]) > thr ? s128 : 0.f;
+            v[j] = v[j] < 0.f ? v[j] + a : v[j] - a;
+          }
+        }
       }
     } else {
       // 2:4: in each quad keep the two largest |T|, ties to the lower position
@@ -265,6 +283,9 @@ hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uin
                        scales, err_flag);
   else if (fmt == TB_FMT_DENSE_MINERR)
     hipLaunchKernelGGL((quantize128_kernel<kMinError>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,
+                       scales, err_flag);
+  else if (fmt == TB_FMT_DENSE_RESID)
+    hipLaunchKernelGGL((quantize128_kernel<kResidual>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,
                        scales, err_flag);
   else
     hipLaunchKernelGGL((quantize128_kernel<kAbsmean>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,

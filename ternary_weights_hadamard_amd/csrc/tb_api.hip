@@ -46,14 +46,22 @@ tb_status check_fwht(const void* x, int x_dtype, const void* y, int y_dtype, int
   return TB_OK;
 }
 
+// code planes of a GEMV segment (0 is read as 1), or 0 when invalid
+int64_t gemv_planes(const tb_gemv_segment& g) { return g.planes == 0 ? 1 : (g.planes == 1 || g.planes == 2) ? g.planes : 0; }
+
+// bytes of a GEMV segment's codes and scales (all planes)
+size_t gemv_code_bytes(const tb_gemv_segment& g) { return (size_t)gemv_planes(g) * (size_t)g.N * (size_t)g.K / 4; }
+size_t gemv_scale_bytes(const tb_gemv_segment& g) { return (size_t)gemv_planes(g) * (size_t)g.N * (size_t)g.K / 64; }
+
 tb_status check_gemv(const tb_gemv_segment& g) {
+  if (gemv_planes(g) == 0) return TB_ERR_FORMAT;
   if (!dims_ok(g.N, g.K) || g.B < 0 || g.B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
   if (g.B == 0) return TB_OK;
   if (!g.act || !g.codes || !g.scales || !g.y) return TB_ERR_NULL;
   if (!aligned16(g.act) || !aligned16(g.codes) || !aligned16(g.scales) || !aligned16(g.y)) return TB_ERR_ALIGN;
-  const size_t nk = (size_t)g.N * (size_t)g.K, yb = (size_t)g.B * (size_t)g.N * 4;
-  if (overlap(g.y, yb, g.act, act8_bytes((size_t)g.B * g.K)) || overlap(g.y, yb, g.codes, nk / 4) ||
-      overlap(g.y, yb, g.scales, nk / 64))
+  const size_t yb = (size_t)g.B * (size_t)g.N * 4;
+  if (overlap(g.y, yb, g.act, act8_bytes((size_t)g.B * g.K)) || overlap(g.y, yb, g.codes, gemv_code_bytes(g)) ||
+      overlap(g.y, yb, g.scales, gemv_scale_bytes(g)))
     return TB_ERR_ALIAS;
   return TB_OK;
 }
@@ -78,7 +86,7 @@ const char* tb_status_string(int status) {
   }
 }
 
-int tb_version(void) { return 101; }
+int tb_version(void) { return 102; }
 
 size_t tb_act8_bytes(int64_t B, int64_t K) {
   if (B < 0 || K <= 0 || K % kGroup) return 0;
@@ -87,13 +95,13 @@ size_t tb_act8_bytes(int64_t B, int64_t K) {
 
 tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
                           size_t* scale_bytes) {
-  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR) return TB_ERR_FORMAT;
-  if (fmt == TB_FMT_DENSE_MINERR) fmt = TB_FMT_DENSE;
+  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR && fmt != TB_FMT_DENSE_RESID)
+    return TB_ERR_FORMAT;
   if (!dims_ok(N, K)) return TB_ERR_SHAPE;
-  const size_t nk = (size_t)N * (size_t)K;
-  if (code_bytes) *code_bytes = fmt == TB_FMT_DENSE ? nk / 4 : nk / 16;
-  if (meta_bytes) *meta_bytes = fmt == TB_FMT_DENSE ? 0 : nk / 8;
-  if (scale_bytes) *scale_bytes = nk / 64;
+  const size_t nk = (size_t)N * (size_t)K, planes = fmt == TB_FMT_DENSE_RESID ? 2 : 1;
+  if (code_bytes) *code_bytes = fmt == TB_FMT_24 ? nk / 16 : planes * nk / 4;
+  if (meta_bytes) *meta_bytes = fmt == TB_FMT_24 ? nk / 8 : 0;
+  if (scale_bytes) *scale_bytes = planes * nk / 64;
   return TB_OK;
 }
 
@@ -129,7 +137,8 @@ tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, 
 
 tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
                            uint16_t* scales, int32_t* err_flag, void* stream) {
-  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR) return TB_ERR_FORMAT;
+  if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR && fmt != TB_FMT_DENSE_RESID)
+    return TB_ERR_FORMAT;
   if (fmt != TB_FMT_24 && meta) return TB_ERR_FORMAT;
   if (!dims_ok(N, K)) return TB_ERR_SHAPE;
   if (!W || !codes || !scales || (fmt == TB_FMT_24 && !meta)) return TB_ERR_NULL;
@@ -137,7 +146,8 @@ tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32
   if ((reinterpret_cast<uintptr_t>(err_flag) & 3u) != 0) return TB_ERR_ALIGN;
   const size_t nk = (size_t)N * (size_t)K;
   const bool dense = fmt != TB_FMT_24;
-  const size_t cb = dense ? nk / 4 : nk / 16, mb = dense ? 0 : nk / 8, sb = nk / 64;
+  const size_t planes = fmt == TB_FMT_DENSE_RESID ? 2 : 1;
+  const size_t cb = dense ? planes * nk / 4 : nk / 16, mb = dense ? 0 : nk / 8, sb = planes * nk / 64;
   if (overlap(W, nk * 4, codes, cb) || overlap(W, nk * 4, scales, sb) || overlap(codes, cb, scales, sb) ||
       (meta && (overlap(W, nk * 4, meta, mb) || overlap(meta, mb, codes, cb) || overlap(meta, mb, scales, sb))))
     return TB_ERR_ALIAS;
@@ -156,10 +166,18 @@ tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, vo
 
 tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
                           int64_t K, float* y, void* stream) {
-  const tb_gemv_segment g{act, B, codes, scales, N, K, y};
+  const tb_gemv_segment g{act, B, codes, scales, N, K, y, 1};
   const tb_status st = check_gemv(g);
   if (st != TB_OK || B == 0) return st;
-  return launched(tb::launch_gemv_ternary(act, B, codes, scales, N, K, y, as_stream(stream)));
+  return launched(tb::launch_gemv_multi(&g, 1, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemv_resid(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                                int64_t N, int64_t K, float* y, void* stream) {
+  const tb_gemv_segment g{act, B, codes, scales, N, K, y, 2};
+  const tb_status st = check_gemv(g);
+  if (st != TB_OK || B == 0) return st;
+  return launched(tb::launch_gemv_multi(&g, 1, as_stream(stream)));
 }
 
 tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* stream) {
@@ -177,12 +195,13 @@ tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* st
     for (int d = 0; d < count; ++d) {
       const tb_gemv_segment& b = segs[d];
       if (d == c || b.B == 0) continue;
-      const size_t nk = (size_t)b.N * (size_t)b.K;
-      if (overlap(a.y, ay, b.act, act8_bytes((size_t)b.B * b.K)) || overlap(a.y, ay, b.codes, nk / 4) ||
-          overlap(a.y, ay, b.scales, nk / 64) || (d < c && overlap(a.y, ay, b.y, (size_t)b.B * (size_t)b.N * 4)))
+      if (overlap(a.y, ay, b.act, act8_bytes((size_t)b.B * b.K)) || overlap(a.y, ay, b.codes, gemv_code_bytes(b)) ||
+          overlap(a.y, ay, b.scales, gemv_scale_bytes(b)) ||
+          (d < c && overlap(a.y, ay, b.y, (size_t)b.B * (size_t)b.N * 4)))
         return TB_ERR_ALIAS;
     }
-    live[n++] = a;
+    live[n] = a;
+    live[n++].planes = gemv_planes(a);
   }
   if (n == 0) return TB_OK;
   return launched(tb::launch_gemv_multi(live, n, as_stream(stream)));

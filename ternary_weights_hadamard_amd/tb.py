@@ -23,7 +23,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtb.so")
 
 TB_F32, TB_BF16, TB_ACT8 = 0, 1, 2
-TB_FMT_DENSE, TB_FMT_24, TB_FMT_DENSE_MINERR = 0, 1, 2
+TB_FMT_DENSE, TB_FMT_24, TB_FMT_DENSE_MINERR, TB_FMT_DENSE_RESID = 0, 1, 2, 3
 TB_EFLAG_NONFINITE, TB_EFLAG_SCALE_OVF = 1, 2
 TB_GEMV_MAX_BATCH = 16
 TB_MAX_SEGMENTS = 8
@@ -40,7 +40,8 @@ class FwhtSegment(ctypes.Structure):
 
 class GemvSegment(ctypes.Structure):
     _fields_ = [("act", ctypes.c_void_p), ("B", ctypes.c_int64), ("codes", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("planes", ctypes.c_int64)]
 
 
 SIGNATURES = {
@@ -53,6 +54,7 @@ SIGNATURES = {
     "tb_ternary_gemv_multi": (_int, [ctypes.POINTER(GemvSegment), _int, _vp]),
     "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "tb_ternary_gemv": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "tb_ternary_gemv_resid": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
     "tb_act8_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "tb_act8_prep": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
@@ -158,17 +160,19 @@ def tb_fwht128_multi(pairs, stream=None):
 
 
 def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, err_flag=None, stream=None):
-    """Quantise fp32 W [N, K]; returns (codes, meta, scales).  For TB_FMT_24 `codes` is the sign plane."""
+    """Quantise fp32 W [N, K]; returns (codes, meta, scales).  For TB_FMT_24 `codes` is the sign plane;
+    for TB_FMT_DENSE_RESID codes and scales hold both planes, groups interleaved."""
     _dev(w)
     n, k = w.shape
     dev = w.device
+    planes = 2 if fmt == TB_FMT_DENSE_RESID else 1
     if codes is None:
-        shape = (n // 16, k // 128, 128) if fmt != TB_FMT_24 else (n, k // 64)
+        shape = (n // 16, planes * k // 128, 128) if fmt != TB_FMT_24 else (n, k // 64)
         codes = torch.empty(shape, dtype=torch.int32, device=dev)
     if meta is None and fmt == TB_FMT_24:
         meta = torch.empty((n, k // 32), dtype=torch.int32, device=dev)
     if scales is None:
-        scales = torch.empty((n, k // 128), dtype=torch.float16, device=dev)
+        scales = torch.empty((n, planes * k // 128), dtype=torch.float16, device=dev)
     _dev(codes, meta, scales, err_flag)
     _check(lib().tb_quantize_pack(_p(w), n, k, int(fmt), _p(codes), _p(meta), _p(scales), _p(err_flag),
                                   _stream(stream)), "tb_quantize_pack")
@@ -200,15 +204,33 @@ def tb_ternary_gemv(act, codes, scales, batch, y=None, stream=None):
     return y
 
 
+def tb_ternary_gemv_resid(act, codes, scales, batch, y=None, stream=None):
+    """tb_ternary_gemv over two-plane weights (TB_FMT_DENSE_RESID): codes
+    [N/16, 2K/128, 128], scales [N, 2K/128], groups of the planes interleaved."""
+    _dev(act, codes, scales)
+    n, g2 = scales.shape
+    k = g2 // 2 * 128
+    if y is None:
+        y = torch.empty((batch, n), dtype=torch.float32, device=act.device)
+    _dev(y)
+    _check(lib().tb_ternary_gemv_resid(_p(act), int(batch), _p(codes), _p(scales), n, k, _p(y), _stream(stream)),
+           "tb_ternary_gemv_resid")
+    return y
+
+
 def tb_ternary_gemv_multi(segments, stream=None):
-    """One launch of several GEMVs: segments = [(act, codes, scales, batch, y), ...]."""
+    """One launch of several GEMVs: segments = [(act, codes, scales, batch, y[, planes]), ...];
+    planes is 1 (default) or 2 for two-plane weights."""
     if not segments:
         return
     arr = (GemvSegment * len(segments))()
-    for c, (act, codes, scales, batch, y) in enumerate(segments):
+    for c, seg in enumerate(segments):
+        act, codes, scales, batch, y = seg[:5]
+        planes = int(seg[5]) if len(seg) > 5 else 1
         _dev(act, codes, scales, y)
         n, g = scales.shape
-        arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n, g * 128, y.data_ptr())
+        arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n,
+                             g // max(planes, 1) * 128, y.data_ptr(), planes)
     _check(lib().tb_ternary_gemv_multi(arr, len(segments), _stream(stream)), "tb_ternary_gemv_multi")
 
 

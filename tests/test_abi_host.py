@@ -47,6 +47,8 @@ def test_status_strings_and_version():
 def test_packed_bytes():
     assert tb.tb_packed_bytes(tb.TB_FMT_DENSE, 5120, 17408) == (5120 * 17408 // 4, 0, 5120 * 17408 // 64)
     assert tb.tb_packed_bytes(tb.TB_FMT_24, 17408, 5120) == (17408 * 5120 // 16, 17408 * 5120 // 8, 17408 * 5120 // 64)
+    assert tb.tb_packed_bytes(tb.TB_FMT_DENSE_MINERR, 256, 384) == tb.tb_packed_bytes(tb.TB_FMT_DENSE, 256, 384)
+    assert tb.tb_packed_bytes(tb.TB_FMT_DENSE_RESID, 5120, 5120) == (5120 * 5120 // 2, 0, 5120 * 5120 // 32)
     L = tb.lib()
     assert L.tb_packed_bytes(7, 128, 128, None, None, None) == 5
     assert L.tb_packed_bytes(0, 100, 128, None, None, None) == 2
@@ -93,7 +95,11 @@ def test_act8_bytes_and_prep_validation():
 def test_quantize_validation():
     L = tb.lib()
     s = None
-    assert L.tb_quantize_pack(_v(A), 128, 128, 3, _v(B), None, _v(C), None, s) == 5   # bad format
+    assert L.tb_quantize_pack(_v(A), 128, 128, 4, _v(B), None, _v(C), None, s) == 5   # bad format
+    assert L.tb_quantize_pack(_v(A), 128, 128, 3, _v(B), _v(D), _v(C), None, s) == 5  # meta given for two planes
+    # two planes: codes take 8 KB for 128 x 128, so scales 4 KB after them overlap
+    # (one plane would end there; that case is not called: it would launch)
+    assert L.tb_quantize_pack(_v(A), 128, 128, 3, _v(B), None, _v(B + 4096), None, s) == 8
     assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(B), _v(D), _v(C), None, s) == 5  # meta given for dense
     assert L.tb_quantize_pack(_v(A), 128, 128, 1, _v(B), None, _v(C), None, s) == 1   # meta missing for 2:4
     assert L.tb_quantize_pack(_v(A), 130, 128, 0, _v(B), None, _v(C), None, s) == 2
@@ -102,6 +108,26 @@ def test_quantize_validation():
     assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(MIS), None, _v(C), None, s) == 3
     assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(B), None, _v(C), _v(D + 2), s) == 3  # flag misaligned
     assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(A + 1024), None, _v(C), None, s) == 8  # codes inside W
+
+
+def test_gemv_resid_validation():
+    L = tb.lib()
+    s = None
+    assert L.tb_ternary_gemv_resid(_v(A), 17, _v(B), _v(C), 128, 128, _v(D), s) == 2
+    assert L.tb_ternary_gemv_resid(_v(A), 1, None, _v(C), 128, 128, _v(D), s) == 1
+    assert L.tb_ternary_gemv_resid(_v(A), 1, _v(B), _v(C), 128, 128, _v(MIS), s) == 3
+    assert L.tb_ternary_gemv_resid(None, 0, None, None, 128, 128, None, s) == 0
+    # y right after one plane's codes (4 KB) overlaps the second plane; after
+    # one plane's scales (256 B) overlaps the second plane's scales
+    assert L.tb_ternary_gemv_resid(_v(A), 1, _v(B), _v(C), 128, 128, _v(B + 4096), s) == 8
+    assert L.tb_ternary_gemv_resid(_v(A), 1, _v(B), _v(C), 128, 128, _v(C + 256), s) == 8
+    Gs = tb.GemvSegment
+    bad_planes = (Gs * 1)(Gs(A, 1, B, C, 128, 128, D, 3))
+    assert L.tb_ternary_gemv_multi(bad_planes, 1, s) == 5
+    neg_planes = (Gs * 1)(Gs(A, 1, B, C, 128, 128, D, -1))
+    assert L.tb_ternary_gemv_multi(neg_planes, 1, s) == 5
+    two = (Gs * 2)(Gs(A, 1, B, C, 128, 128, D, 2), Gs(A, 1, B, C, 128, 128, B + 4096, 1))
+    assert L.tb_ternary_gemv_multi(two, 2, s) == 8                 # a y inside another's second plane
 
 
 def test_gemv_validation():

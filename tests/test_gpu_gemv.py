@@ -252,3 +252,102 @@ def test_grouped_output_rotation_f32():
     torch.cuda.synchronize()
     for x, y in zip(xs, ys):
         assert torch.equal(y, tb.tb_fwht128(x))
+
+
+# ---------------------------------------------------------------- two-plane weights
+
+def _gemv_resid(x_bits, codes, scales):
+    act = tb.tb_act8_prep(bf16_dev(x_bits))
+    y = tb.tb_ternary_gemv_resid(act, u32_dev(codes), f16_dev(scales), x_bits.shape[0])
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def _resid_inputs(n, k, b, seed):
+    # both planes' codes and scales, groups interleaved: the dense format of [n, 2k]
+    codes = synth.random_code_words(n, 2 * k, seed=seed)
+    scales = synth.random_scales_f16(n, 2 * k, seed=seed + 1)
+    x = synth.gaussian_bf16((b, k), seed=seed + 2)
+    return codes, scales, x
+
+
+@pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (1024, 1024), (384, 2176)])
+@pytest.mark.parametrize("b", [1, 3, 5, 16])
+def test_gemv_resid_small_matches_oracle(n, k, b):
+    say(f"two-plane gemv N={n} K={k} B={b}")
+    codes, scales, x = _resid_inputs(n, k, b, seed=3 * n + k + b)
+    y = _gemv_resid(x, codes, scales)
+    ref = oracle.matvec.gemv_residual(x, codes, scales, k)
+    assert_close(y, ref, f"two-plane gemv {n}x{k} B={b}")
+    assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("n,k", [(5120, 5120), (17408, 5120), (5120, 17408)])
+@pytest.mark.parametrize("b", [1, 8])
+def test_gemv_resid_full_size_sampled_tiles(n, k, b):
+    say(f"two-plane gemv full N={n} K={k} B={b}")
+    codes, scales, x = _resid_inputs(n, k, b, seed=40 + b)
+    y = _gemv_resid(x, codes, scales)
+    tiles = np.sort(np.random.default_rng(2).choice(n // 16, 12, replace=False))
+    rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+    ref = oracle.matvec.gemv_residual(x, codes[tiles], scales[rows], k)
+    assert_close(y[:, rows], ref, f"two-plane gemv {n}x{k} B={b} (12 sampled tiles)")
+    assert np.max(np.abs(y[:, rows] - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("b", [1, 4, 9])
+def test_gemv_resid_exact_small_integers(b):
+    n, k = 256, 1280
+    codes = synth.random_code_words(n, 2 * k, seed=15)
+    x = synth.small_int_bf16((b, k), seed=16)
+    sc = (2.0 ** np.random.default_rng(17).integers(-6, 2, size=(n, 2 * k // 128))).astype(np.float16).view(np.uint16)
+    y = _gemv_resid(x, codes, sc)
+    assert np.array_equal(y, oracle.matvec.gemv_residual(x, codes, sc, k))
+
+
+def test_gemv_resid_of_quantised_weights():
+    # quantiser -> two-plane GEMV: closer to W' x' than the one-plane product
+    n, k = 512, 1024
+    w = synth.stack_weights(n, k, seed=44)
+    x = synth.gaussian_bf16((2, k), seed=45)
+    c2, _, s2 = tb.tb_quantize_pack(torch.from_numpy(w).to(DEV), fmt=tb.TB_FMT_DENSE_RESID)
+    c1, _, s1 = tb.tb_quantize_pack(torch.from_numpy(w).to(DEV))
+    act = tb.tb_act8_prep(bf16_dev(x))
+    y2 = tb.tb_ternary_gemv_resid(act, c2, s2, 2)
+    y1 = tb.tb_ternary_gemv(act, c1, s1, 2)
+    torch.cuda.synchronize()
+    exact = oracle.numerics.bf16_bits_to_f64(x) @ oracle.hadamard.rotate_blocks(w.astype(np.float64)).T
+    e1 = np.linalg.norm(y1.cpu().numpy() - exact)
+    e2 = np.linalg.norm(y2.cpu().numpy() - exact)
+    say(f"  |y - W'x|: one plane {e1:.4e}, two planes {e2:.4e}")
+    assert e2 < 0.75 * e1
+    # and it is the oracle's product over the GPU's own planes
+    assert_close(y2.cpu().numpy(), oracle.matvec.gemv_residual(x, c2.cpu().numpy().view(np.uint32),
+                                                               s2.cpu().numpy().view(np.uint16), k), "quantised two-plane")
+
+
+@pytest.mark.parametrize("b", [1, 3, 6])
+def test_grouped_two_plane_and_mixed_equal_single_calls(b):
+    # all two-plane, then one- and two-plane segments mixed in one call
+    shapes = [(1920, 5120, 2), (640, 640, 2), (768, 2176, 2), (256, 17408, 2)]
+    mixed = [(1920, 5120, 1), (640, 640, 2), (768, 2176, 1), (256, 17408, 2)]
+    for case, spec in (("two-plane", shapes), ("mixed", mixed)):
+        say(f"grouped {case} gemv, B={b}")
+        segs, singles = [], []
+        for c, (n, k, p) in enumerate(spec):
+            codes = synth.random_code_words(n, p * k, seed=170 + c)
+            scales = synth.random_scales_f16(n, p * k, seed=180 + c)
+            x = synth.gaussian_bf16((b, k), seed=190 + c)
+            act = tb.tb_act8_prep(bf16_dev(x))
+            cd, sc = u32_dev(codes), f16_dev(scales)
+            y = torch.empty((b, n), dtype=torch.float32, device=DEV)
+            segs.append((act, cd, sc, b, y, p))
+            singles.append((x, codes, scales, k, p))
+        tb.tb_ternary_gemv_multi(segs)
+        torch.cuda.synchronize()
+        for c, ((act, cd, sc, _, y, p), (x, codes, scales, k, _)) in enumerate(zip(segs, singles)):
+            y1 = tb.tb_ternary_gemv_resid(act, cd, sc, b) if p == 2 else tb.tb_ternary_gemv(act, cd, sc, b)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y1), f"{case} segment {c}: grouped differs from the single call"
+            ref = (oracle.matvec.gemv_residual if p == 2 else oracle.matvec.gemv)(x, codes, scales, k)
+            assert_close(y.cpu().numpy(), ref, f"{case} segment {c} vs oracle")

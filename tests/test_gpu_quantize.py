@@ -181,3 +181,90 @@ def test_minerr_closed_forms_and_lower_error_than_absmean():
     e_abs = err(oracle.quant.unpack_dense(host_u32(ca), 512), sa)
     say(f"  squared error: min-error rule {e_min:.4e}, absmean rule {e_abs:.4e}")
     assert e_min < e_abs
+
+
+# ---------------------------------------------------------------- residual second plane
+
+def _f16(b):
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _check_resid(codes, scales, w, what):
+    """Codes and scales of TB_FMT_DENSE_RESID against the oracle.  Plane 1 as the
+    one-plane rule.  Plane 2 is bit-exact (outside its own threshold band) in
+    groups where the GPU's plane 1 equals the oracle's; where plane 1 took the
+    other side of a near-threshold element or the other fp16 rounding of s1,
+    plane 2 must be the absmean rule applied to the GPU's own residual."""
+    ref = oracle.quant.quantize_dense_residual(w.astype(np.float64))
+    n, k = w.shape
+    g = k // 128
+    c1, c2 = oracle.quant.split_planes(host_u32(codes))
+    sc1, sc2 = (p.astype(np.int64) for p in oracle.quant.split_planes(host_u16(scales)))
+    r1, r2 = (p.astype(np.int64) for p in oracle.quant.split_planes(ref["scales"]))
+    t1 = oracle.quant.unpack_dense(c1, k)
+    t2 = oracle.quant.unpack_dense(c2, k)
+    wr = ref["wr"]
+    near1 = oracle.quant.near_threshold(wr, ref["s1"])
+    assert not ((t1 != ref["t1"]) & ~near1).any(), f"{what}: plane-1 code mismatch outside the band"
+    assert np.abs(sc1 - r1).max(initial=0) <= 1, f"{what}: plane-1 scale beyond 1 ulp"
+    same = (t1 == ref["t1"]).reshape(n, g, 128).all(axis=2) & (sc1 == r1)
+    same_el = np.repeat(same, 128, axis=1)
+    near2 = oracle.quant.near_threshold(ref["d"], ref["s2"])
+    bad2 = (t2 != ref["t2"]) & ~near2 & same_el
+    assert not bad2.any(), f"{what}: {int(bad2.sum())} plane-2 code mismatches outside the band"
+    assert np.abs(sc2 - r2)[same].max(initial=0) <= 1, f"{what}: plane-2 scale beyond 1 ulp"
+    # the other groups: the absmean rule on the GPU's own residual (test-side)
+    d_own = wr - np.repeat(_f16(sc1), 128, axis=1) * t1
+    s2_own = np.abs(d_own).reshape(n, g, 128).mean(axis=2)
+    thr = np.repeat(s2_own / 2, 128, axis=1)
+    t2_own = np.where(d_own > thr, 1, np.where(d_own < -thr, -1, 0))
+    band = np.abs(np.abs(d_own) - thr) <= 1e-5 * thr
+    other = ~same_el
+    assert not ((t2 != t2_own) & ~band & other).any(), f"{what}: plane 2 is not the rule on the GPU's own residual"
+    own16 = oracle.numerics.f64_to_f16_bits(s2_own).astype(np.int64)
+    assert np.abs(sc2 - own16)[~same].max(initial=0) <= 1
+    say(f"  {what}: {int(near1.sum())} plane-1 near-threshold elements, {int((~same).sum())} of {same.size} "
+        f"groups with another plane 1, {int((near2 & same_el).sum())} plane-2 near-threshold elements")
+    return ref, t1, t2, sc1, sc2
+
+
+@pytest.mark.parametrize("n,k,seed", [(128, 128, 31), (256, 384, 32), (1024, 1024, 0), (384, 1280, 33)])
+def test_resid_matches_oracle(n, k, seed):
+    w = synth.single_layer_weights(n, k, seed=seed) if seed == 0 else synth.stack_weights(n, k, seed=seed)
+    say(f"quantize two-plane {n}x{k} seed {seed}")
+    codes, meta, scales = _quant(w, fmt=tb.TB_FMT_DENSE_RESID)
+    assert meta is None and tuple(codes.shape) == (n // 16, 2 * k // 128, 128) and tuple(scales.shape) == (n, 2 * k // 128)
+    _, t1, t2, sc1, sc2 = _check_resid(codes, scales, w, f"two-plane {n}x{k}")
+    # plane 1 is the one-plane format, word for word
+    c_one, _, s_one = _quant(w)
+    assert np.array_equal(oracle.quant.split_planes(host_u32(codes))[0], host_u32(c_one))
+    assert np.array_equal(oracle.quant.split_planes(host_u16(scales))[0], host_u16(s_one))
+
+
+def test_resid_closed_forms_and_error():
+    # the hand-worked rows of the oracle's residual fixture, as a rotated block
+    wr = np.zeros((256, 256))
+    wr[0, :64], wr[0, 64:128] = 1.0, 0.5            # exact two-level row: lossless
+    wr[1, :64], wr[1, 64:128] = 1.0, 0.25           # s1 0.625, s2 0.3125
+    wr[2, :32], wr[2, 32:128] = -0.5, 0.5           # already ternary: plane 2 zero
+    wr[3, :128] = 1.0006103515625                   # fp16 rounding of s1 decides plane 2
+    wr[128:, 128:] = np.random.default_rng(5).standard_normal((128, 128)) * 0.02 * 128
+    w = np.zeros_like(wr)
+    for a in (0, 128):
+        for b in (0, 128):
+            w[a:a + 128, b:b + 128] = H @ wr[a:a + 128, b:b + 128] @ H / 128
+    codes, _, scales = _quant(w.astype(np.float32), fmt=tb.TB_FMT_DENSE_RESID)
+    ref, t1, t2, sc1, sc2 = _check_resid(codes, scales, w.astype(np.float32), "two-plane closed forms")
+    s1, s2 = _f16(sc1), _f16(sc2)
+    assert s1[0, 0] == 0.75 and s2[0, 0] == 0.25 and np.all(t2[0, :64] == 1) and np.all(t2[0, 64:128] == -1)
+    assert s1[1, 0] == 0.625 and s2[1, 0] == 0.3125 and np.all(t2[1, :128] == 1)
+    assert s2[2, 0] == 0 and np.all(t2[2, :128] == 0)
+    assert s1[3, 0] == 1.0009765625 and s2[3, 0] == 0.0003662109375 and np.all(t2[3, :128] == -1)
+    assert np.all(sc1[4:128, 0] == 0) and np.all(sc2[4:128, 0] == 0) and np.all(t2[4:128, :128] == 0)
+    # the second plane lowers the error of every Gaussian group
+    rec1 = np.repeat(s1, 128, axis=1) * t1
+    rec2 = rec1 + np.repeat(s2, 128, axis=1) * t2
+    e1 = ((ref["wr"] - rec1) ** 2).reshape(256, 2, 128).sum(axis=2)[128:, 1]
+    e2 = ((ref["wr"] - rec2) ** 2).reshape(256, 2, 128).sum(axis=2)[128:, 1]
+    say(f"  squared error of the Gaussian block: one plane {e1.sum():.4e}, two planes {e2.sum():.4e}")
+    assert np.all(e2 < e1)
