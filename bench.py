@@ -72,9 +72,9 @@ def recorded_traffic():
         return None
 
 
-def gemv_bytes(n, k, b):
-    """Algorithmic bytes of one GEMV launch: codes + scales + activations + output."""
-    return n * k // 4 + n * k // 64 + 2 * b * k + 4 * b * n
+def gemv_bytes(n, k, b, planes=1):
+    """Algorithmic bytes of one GEMV launch: codes + scales (per plane) + activations + output."""
+    return planes * (n * k // 4 + n * k // 64) + 2 * b * k + 4 * b * n
 
 
 def packed_bytes(n, k):
@@ -82,16 +82,17 @@ def packed_bytes(n, k):
 
 
 class DecodeStack:
-    def __init__(self, layers, batch, gen, dev, grouping="split"):
+    def __init__(self, layers, batch, gen, dev, grouping="split", planes=1):
         import torch
 
         from ternary_weights_hadamard_amd import synth
 
-        self.layers, self.batch, self.grouping = layers, batch, grouping
+        self.layers, self.batch, self.grouping, self.planes = layers, batch, grouping, planes
         self.w = []
+        # two-plane weights are the dense format of [n, 2k] (the planes' groups interleaved)
         for li in range(layers):
-            self.w.append([(synth.torch_code_words(n, k, gen, dev), synth.torch_scales_f16(n, k, gen, dev), n, k)
-                           for _, n, k in FUSED])
+            self.w.append([(synth.torch_code_words(n, planes * k, gen, dev),
+                            synth.torch_scales_f16(n, planes * k, gen, dev), n, k) for _, n, k in FUSED])
             if li % 16 == 15:
                 log(f"  generated {li + 1}/{layers} layers")
         self.make_acts(batch, gen, dev)
@@ -115,7 +116,8 @@ class DecodeStack:
         projection on its own ("split")."""
         from ternary_weights_hadamard_amd import tb
 
-        segs = [(self.act[j], codes, scales, self.batch, self.yr[j]) for j, (codes, scales, n, k) in enumerate(layer)]
+        segs = [(self.act[j], codes, scales, self.batch, self.yr[j], self.planes)
+                for j, (codes, scales, n, k) in enumerate(layer)]
         if self.grouping == "layer":
             tb.tb_ternary_gemv_multi(segs)
         elif self.grouping == "none":
@@ -154,7 +156,7 @@ class DecodeStack:
             self.gemv_calls(layer)
 
     def packed_bytes(self):
-        return sum(packed_bytes(n, k) for layer in self.w for _, _, n, k in layer)
+        return self.planes * sum(packed_bytes(n, k) for layer in self.w for _, _, n, k in layer)
 
     def gemv_times(self, replays=5):
         """The grouped GEMV launches of one step (one per layer) captured in a
@@ -165,7 +167,7 @@ class DecodeStack:
         del g
         per_layer = {"layer": 1, "split": 2, "none": 4}[self.grouping]
         nl = per_layer * len(self.w)
-        per_launch_bytes = sum(gemv_bytes(n, k, self.batch) for _, _, n, k in self.w[0]) / per_layer
+        per_launch_bytes = sum(gemv_bytes(n, k, self.batch, self.planes) for _, _, n, k in self.w[0]) / per_layer
         return per_launch_bytes, ms / (replays * nl), nl
 
 
@@ -521,6 +523,20 @@ def main():
                                   "gemv_frac_of_hbm_peak": round(gb8 / (gms8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"decode batch 8: {ms8:.4f} ms/step, GEMV {extra['decode_batch8']['gemv_gbs_algorithmic']} GB/s")
         stack.make_acts(args.batch, gen, dev)
+        # the same decode step over two-plane weights (residual second plane)
+        two = DecodeStack(args.layers, args.batch, gen, dev, args.grouping, planes=2)
+        ms2, _, g2 = time_graph(two.step, max(3, args.steps // 2), 2)
+        del g2
+        ms2 /= max(3, args.steps // 2)
+        gb2, gms2, _ = two.gemv_times()
+        tb2 = two.packed_bytes()
+        extra["decode_two_plane"] = {"ms_per_step": round(ms2, 4), "packed_bytes_per_step": tb2,
+                                     "gbs_packed": round(tb2 / (ms2 * 1e-3) / 1e9, 1),
+                                     "gemv_gbs_algorithmic": round(gb2 / (gms2 * 1e-3) / 1e9, 1),
+                                     "gemv_frac_of_hbm_peak": round(gb2 / (gms2 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     "gemv_avg_launch_us": round(gms2 * 1e3, 3)}
+        log(f"decode two-plane: {ms2:.4f} ms/step, GEMV {extra['decode_two_plane']['gemv_gbs_algorithmic']} GB/s")
+        del two
         extra.update(extra_phases(gen, dev, args.quick))
 
     traffic = recorded_traffic()
@@ -544,7 +560,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None or args.batch != 1 else round(traffic),
-                     "kernel": "gemv_staged_kernel (one grouped launch per layer: QKV, O, gate/up, down)",
+                     "kernel": "gemv_staged_kernel (two grouped launches per layer: QKV + O + gate/up, then down)",
                      "bytes_per_launch": "sum over the 4 matrices of N*K/4 + N*K/64 + 2*B*K + 4*B*N"},
         "extra": extra,
     }

@@ -188,9 +188,10 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_
  * group and stores their signs (mhpq.cn §1.2).
  * TB_FMT_DENSE_MINERR (dense storage) chooses each group's threshold and
  * scale to minimise ||W' - s t||^2 (the threshold as the accuracy-critical
- * knob, xxqk.cn/news/652513 §4): over the group's magnitudes theta, the kept
- * set {|W'| >= theta} with the largest S^2 / j (S the sum of its magnitudes,
- * j its size), t = sign(W') on it, s = S / j; ties go to the larger theta.
+ * knob, xxqk.cn/news/652513 §3, its per-block threshold search): over the
+ * group's magnitudes theta, the kept set {|W'| >= theta} with the largest
+ * S^2 / j (S the sum of its magnitudes, j its size), t = sign(W') on it,
+ * s = S / j; ties go to the larger theta.
  * The 0.38-quantile threshold of dpshk.com §3.2 step 4 is one of the
  * candidates (it keeps the largest 79 of 128).
  * TB_FMT_DENSE_RESID adds a second ternary plane for what the first misses

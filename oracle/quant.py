@@ -14,7 +14,8 @@ Definitions followed (readings of the pages are listed in the design doc):
 * Error-minimising variant: for each group choose the threshold theta and
   scale s that minimise ||w' - s t||^2 with t = sign(w') [|w'| >= theta]
   (a threshold-shaped ternarisation, dpshk.com/news/5289456 §3.2 steps 4-5;
-  the threshold as the accuracy-critical choice, xxqk.cn/news/652513 §4).
+  the threshold as the accuracy-critical choice, xxqk.cn/news/652513 §3,
+  its per-block threshold search).
   For a kept set of j elements with magnitude sum S the best scale is S / j
   and the error is sum w'^2 - S^2 / j, so theta is the group magnitude that
   maximises S^2 / j over the kept sets {|w'| >= theta}.  The 0.38-quantile
