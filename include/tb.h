@@ -290,6 +290,35 @@ TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t*
 TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, void* y, int y_dtype, void* stream);
 
+/*
+ * Bytes of workspace tb_ternary_gemm_splitk uses for an [M][N] result with
+ * K-long rows: S * M * N * 4 for the S splits of K it chooses (about two
+ * workgroups per compute unit, at most 16 splits, at least one 128-group
+ * each), or 0 when one pass suffices (S = 1) or the sizes are invalid.
+ * Host-only.
+ */
+TB_API size_t tb_ternary_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
+
+/*
+ * tb_ternary_gemm for few rows of activations (M = 16-256, between decode and
+ * prefill), where one pass over K leaves too few output tiles to fill the
+ * GPU: K is cut into S splits at 128-group boundaries, each split's fp32
+ * partial product goes to `workspace` ([S][M][N] fp32), and a second kernel
+ * adds the partials in split order and writes y (bf16 rounded to nearest
+ * even, or fp32).  The same contraction and error rules as tb_ternary_gemm;
+ * the sums are grouped by split, so the fp32 result may differ from
+ * tb_ternary_gemm's in the last bits.
+ *   workspace  device memory of workspace_bytes bytes, caller-owned; S is
+ *              reduced to what fits (S <= workspace_bytes / (M*N*4)); with
+ *              room for fewer than two partials (or NULL) the call runs as
+ *              tb_ternary_gemm.  Must not overlap any other argument
+ *              (TB_ERR_ALIAS).  Calls sharing a workspace must be ordered on
+ *              one stream.
+ */
+TB_API tb_status tb_ternary_gemm_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                 int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

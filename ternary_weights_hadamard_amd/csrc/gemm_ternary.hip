@@ -19,6 +19,12 @@
 // buffered, rows padded to spread banks), two steps per scale group.  Each K
 // step reads the codes of 128 rows once (8 bytes per thread) and decodes them
 // once for all 128 activation rows of the tile.
+// Split K (few rows of activations, so few output tiles): workgroup z of S
+// takes the scale groups [G z / S, G (z + 1) / S) and writes its fp32 partial
+// result to a caller-provided workspace; a second kernel adds the S partials
+// in order (the result does not depend on timing) and converts.
+#include <algorithm>
+
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -45,7 +51,7 @@ template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                            const uint32_t* __restrict__ codes,
                                                            const uint16_t* __restrict__ scales, int64_t N,
-                                                           int64_t K, void* __restrict__ y) {
+                                                           int64_t K, void* __restrict__ y, int splits) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE_ELEMS];  // [stage][X | W][row][k]
   __shared__ uint16_t lds_s[2][BN];                                         // [stage][weight row] fp16 scale
   const int tid = threadIdx.x;
@@ -56,18 +62,20 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t G = K / kBlock;
-  const int nsteps = (int)(K / KT);  // even: K is a multiple of 128
+  // this workgroup's scale groups [gb, ge); output: y, or partial z of the workspace
+  const int64_t gb = G * blockIdx.z / splits, ge = G * (blockIdx.z + 1) / splits;
+  const int nsteps = (int)(2 * (ge - gb));  // two K steps per group
 
   // global -> register staging assignment
   // X: 128 rows x 64 k bf16 = 128 B per row; thread -> row tid/2, 32 k (64 B) at (tid&1)*32
   const int xr = tid >> 1, xk = (tid & 1) * 32;
   const bool xvalid = m0 + xr < M;
-  const uint16_t* xsrc = x + (m0 + xr) * K + xk;
+  const uint16_t* xsrc = x + (m0 + xr) * K + gb * kBlock + xk;
   // W: 128 rows x 64 k; thread -> row tid/2, the 32 columns of lane group
   // (k0 % 128) / 32 + (tid & 1) of the row's tile: two consecutive words
   const int wr = tid >> 1, wk = (tid & 1) * 32;
-  const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
-  const uint16_t* ssrc = scales + (n0 + wr) * G;
+  const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + gb * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
+  const uint16_t* ssrc = scales + (n0 + wr) * G + gb;
 
   u32x4 xs[4];
   u32x2 cs;
@@ -156,6 +164,7 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   }
 
   // lane holds acc[i][j][r] = 2 * y[m0 + wm + 16i + 4q + r][n0 + wn + 16j + li]
+  if (splits > 1) y = static_cast<float*>(y) + (size_t)blockIdx.z * M * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -174,17 +183,71 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
     }
 }
 
+// y = sum over s < S of part[s] (in order), rounded to bf16 or kept fp32;
+// MN is a multiple of 4.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t MN,
+                                                            void* __restrict__ y) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < MN; e += stride) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + e);
+    for (int s = 1; s < S; ++s) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] += b[r];
+    }
+    if constexpr (OUT_BF16) {
+      const uint32_t lo = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + e) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(y) + e) = a;
+    }
+  }
+}
+
+hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
+                       int64_t K, void* y, bool bf16_out, int splits, hipStream_t stream) {
+  const int64_t mt = (M + BM - 1) / BM;
+  if (mt > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(N / BN), (unsigned)mt, (unsigned)splits), block(256);
+  if (bf16_out)
+    hipLaunchKernelGGL((gemm_ternary_kernel<true>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits);
+  else
+    hipLaunchKernelGGL((gemm_ternary_kernel<false>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream) {
-  const int64_t mt = (M + BM - 1) / BM;
-  if (mt > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(N / BN), (unsigned)mt), block(256);
+  return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, 1, stream);
+}
+
+int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
+  // about two workgroups per compute unit (256 CUs), at least one scale group
+  // per split, at most 16 splits
+  const int64_t tiles = (N / BN) * ((M + BM - 1) / BM);
+  int64_t s = (512 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::min<int64_t>(K / kBlock, 16));
+  return (int)std::max<int64_t>(s, 1);
+}
+
+hipError_t launch_gemm_ternary_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                      int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  const size_t part = (size_t)M * (size_t)N * sizeof(float);
+  const int S = (int)std::min<size_t>((size_t)gemm_splitk_parts(M, N, K), workspace ? workspace_bytes / part : 0);
+  if (S <= 1) return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, 1, stream);
+  const hipError_t e = launch_gemm(x, M, codes, scales, N, K, workspace, false, S, stream);
+  if (e != hipSuccess) return e;
+  const int64_t MN = M * N;
+  const int64_t blocks = std::min<int64_t>((MN / 4 + 255) / 256, 4096);
   if (y_dtype == TB_BF16)
-    hipLaunchKernelGGL((gemm_ternary_kernel<true>), grid, block, 0, stream, x, M, codes, scales, N, K, y);
+    hipLaunchKernelGGL((splitk_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, workspace, S, MN, y);
   else
-    hipLaunchKernelGGL((gemm_ternary_kernel<false>), grid, block, 0, stream, x, M, codes, scales, N, K, y);
+    hipLaunchKernelGGL((splitk_reduce_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, workspace, S, MN, y);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ SIGNATURES = {
     "tb_act8_prep": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "tb_ternary_gemm": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]),
+    "tb_ternary_gemm_splitk_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "tb_ternary_gemm_splitk": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp, ctypes.c_size_t, _vp]),
 }
 
 
@@ -256,4 +258,27 @@ def tb_ternary_gemm(x, codes, scales, y=None, out_dtype=torch.bfloat16, stream=N
     _dev(y)
     _check(lib().tb_ternary_gemm(_p(x), m, _p(codes), _p(scales), n, k, _p(y), _dt(y), _stream(stream)),
            "tb_ternary_gemm")
+    return y
+
+
+def tb_ternary_gemm_splitk_workspace(m, n, k):
+    return int(lib().tb_ternary_gemm_splitk_workspace(int(m), int(n), int(k)))
+
+
+def tb_ternary_gemm_splitk(x, codes, scales, y=None, out_dtype=torch.bfloat16, workspace=None, stream=None):
+    """tb_ternary_gemm with K split across workgroups for few activation rows;
+    `workspace` is a device tensor of at least tb_ternary_gemm_splitk_workspace
+    bytes (allocated here when None)."""
+    _dev(x, codes, scales)
+    m, k = x.shape
+    n = scales.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        nbytes = tb_ternary_gemm_splitk_workspace(m, n, k)
+        workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=x.device)
+    _dev(y, workspace)
+    _check(lib().tb_ternary_gemm_splitk(_p(x), m, _p(codes), _p(scales), n, k, _p(y), _dt(y), _p(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tb_ternary_gemm_splitk")
     return y

@@ -186,6 +186,26 @@ def test_gemm_validation():
     assert L.tb_ternary_gemm(None, 0, None, None, 128, 128, None, 1, s) == 0
 
 
+def test_gemm_splitk_validation_and_workspace_size():
+    L = tb.lib()
+    s = None
+    # 40 tiles of 128 x 128 for M = 64, N = 5120: 13 splits of K = 5120 fill ~512 workgroups
+    assert tb.tb_ternary_gemm_splitk_workspace(64, 5120, 5120) == 13 * 64 * 5120 * 4
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 5120, 17408) == 13 * 16 * 5120 * 4
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 128, 256) == 2 * 16 * 128 * 4      # at most one split per group
+    assert tb.tb_ternary_gemm_splitk_workspace(2048, 17408, 5120) == 0                 # enough tiles already
+    assert tb.tb_ternary_gemm_splitk_workspace(0, 128, 128) == 0
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 100, 128) == 0
+    ws = 0x50000
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 9, _v(ws), 4096, s) == 4
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, _v(B), _v(C), 128, 200, _v(D), 1, _v(ws), 4096, s) == 2
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, None, _v(C), 128, 128, _v(D), 1, _v(ws), 4096, s) == 1
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 1, _v(MIS), 4096, s) == 3
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 1, _v(D + 16), 4096, s) == 8  # ws over y
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 1, _v(B + 16), 4096, s) == 8  # ws over codes
+    assert L.tb_ternary_gemm_splitk(None, 0, None, None, 128, 128, None, 1, None, 0, s) == 0
+
+
 def test_binding_raises_typed_error_on_cpu_tensors():
     import torch
 

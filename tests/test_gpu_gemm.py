@@ -88,3 +88,70 @@ def test_gemm_canaries_and_empty():
     assert_close(host_f64(y), oracle.matvec.gemm(x, codes, scales, k), "gemm canary run", out_bf16=True)
     e = tb.tb_ternary_gemm(torch.empty((0, k), dtype=torch.bfloat16, device=DEV), u32_dev(codes), f16_dev(scales))
     assert e.shape == (0, n)
+
+
+# ---------------------------------------------------------------- split K (few activation rows)
+
+@pytest.mark.parametrize("m,n,k", [(1, 256, 384), (17, 256, 640), (100, 384, 1280), (200, 128, 2176), (256, 256, 128)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_gemm_splitk_small_matches_oracle(m, n, k, out):
+    say(f"split-K gemm M={m} N={n} K={k} {out}")
+    codes = synth.random_code_words(n, k, seed=m + 3 * n)
+    scales = synth.random_scales_f16(n, k, seed=k + 1)
+    x = synth.gaussian_bf16((m, k), seed=m + 7)
+    ws_bytes = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+    assert ws_bytes % (m * n * 4) == 0 and ws_bytes // (m * n * 4) <= min(16, k // 128)
+    y = tb.tb_ternary_gemm_splitk(bf16_dev(x), u32_dev(codes), f16_dev(scales),
+                                  out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matvec.gemm(x, codes, scales, k)
+    assert_close(host_f64(y), ref, f"split-K gemm {m}x{n}x{k} {out}", out_bf16=out == "bf16")
+
+
+@pytest.mark.parametrize("m", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("n,k", [(5120, 5120), (17408, 5120), (5120, 17408)])
+def test_gemm_splitk_mid_batch_sampled(m, n, k):
+    say(f"split-K gemm mid-batch M={m} N={n} K={k}")
+    codes = synth.random_code_words(n, k, seed=60 + m)
+    scales = synth.random_scales_f16(n, k, seed=61)
+    x = synth.gaussian_bf16((m, k), seed=62 + m)
+    parts = tb.tb_ternary_gemm_splitk_workspace(m, n, k) // (m * n * 4)
+    y = host_f64(tb.tb_ternary_gemm_splitk(bf16_dev(x), u32_dev(codes), f16_dev(scales), out_dtype=torch.float32))
+    tiles = np.sort(np.random.default_rng(7).choice(n // 16, 6, replace=False))
+    cs = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+    ref = oracle.matvec.gemm(x, codes[tiles], scales[cs], k)
+    assert_close(y[:, cs], ref, f"split-K gemm {m}x{n}x{k} ({parts} splits, 6 tiles sampled)")
+
+
+def test_gemm_splitk_exact_and_fallbacks():
+    # small integers, power-of-two scales: every split's sum is exact, so the
+    # split result equals the oracle and the one-pass GEMM bit for bit
+    m, n, k = 48, 384, 2048
+    codes = u32_dev(synth.random_code_words(n, k, seed=63))
+    x_bits = synth.small_int_bf16((m, k), seed=64)
+    sc = (2.0 ** np.random.default_rng(65).integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    x, scales = bf16_dev(x_bits), f16_dev(sc)
+    ref = oracle.matvec.gemm(x_bits, synth.random_code_words(n, k, seed=63), sc, k)
+    parts = tb.tb_ternary_gemm_splitk_workspace(m, n, k) // (m * n * 4)
+    assert parts > 1
+    for out in (torch.float32, torch.bfloat16):
+        y1 = tb.tb_ternary_gemm(x, codes, scales, out_dtype=out)
+        ys = tb.tb_ternary_gemm_splitk(x, codes, scales, out_dtype=out)
+        # a workspace with room for one partial only, and none: one pass
+        small = torch.empty(m * n, dtype=torch.float32, device=DEV)
+        yf = tb.tb_ternary_gemm_splitk(x, codes, scales, out_dtype=out, workspace=small)
+        torch.cuda.synchronize()
+        assert torch.equal(ys, y1) and torch.equal(yf, y1)
+        if out == torch.float32:
+            assert np.array_equal(host_f64(ys), ref)
+    # canaries around y and the workspace
+    wsb = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+    wbuf = torch.full((wsb // 4 + 64,), 7.0, dtype=torch.float32, device=DEV)
+    ws = wbuf[32:32 + wsb // 4]
+    ybuf = torch.full((m * n + 64,), -5.0, dtype=torch.float32, device=DEV)
+    y = ybuf[32:32 + m * n].view(m, n)
+    tb.tb_ternary_gemm_splitk(x, codes, scales, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(wbuf[:32] == 7.0) and torch.all(wbuf[32 + wsb // 4:] == 7.0)
+    assert torch.all(ybuf[:32] == -5.0) and torch.all(ybuf[32 + m * n:] == -5.0)
+    assert np.array_equal(host_f64(y), ref)
