@@ -15,6 +15,17 @@
 // batch row i at two 8-wide K blocks; D[4q + r][i] returns in lane (i, q).
 // The 64-wide windows are mapped to actual K so that lane q of SMFMAC h covers
 // K 128g + 32q + 16h .. +15: one meta word and one sign word per lane and group.
+//
+// Staged path (batch <= 4): a wave owns one 16-row tile and a slice of at most
+// CH groups of K.  The format is row-major, so a row's meta, signs and scales
+// for the slice are contiguous: the wave fetches them, and its slice of x, with
+// a few whole-wave 16-, 8- and 2-byte loads issued before any use, copies them
+// into a private LDS area and reads each group's words back in the operand
+// layout.  That is about 8 loads per slice instead of 6 per group.  The K
+// slices of a tile are the waves of one workgroup, added through LDS in a
+// fixed order.
+#include <algorithm>
+
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -154,12 +165,159 @@ __global__ void __launch_bounds__(512) gemv_ternary24_kernel(const uint16_t* __r
   if (li < B) *reinterpret_cast<f32x4*>(y + (int64_t)li * N + nbase + 4 * q) = acc_y;
 }
 
+// bytes of one wave's staging area: meta [CH][16][16 B], signs [CH][16][8 B],
+// scales [CH][16] fp16 (padded to 16 B), x [B][CH][256 B]
+__host__ __device__ constexpr int stage24_bytes(int ch, int b) {
+  return ch * 256 + ch * 128 + (ch * 32 + 15) / 16 * 16 + b * ch * 256;
+}
+
+template <int CH>
+__global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __restrict__ x, int B,
+                                                             const uint32_t* __restrict__ meta,
+                                                             const uint32_t* __restrict__ signs,
+                                                             const uint16_t* __restrict__ scales, int64_t N,
+                                                             int64_t K, float* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int KS = (int)(blockDim.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, q = lane >> 4;
+  const int64_t nb = blockIdx.x;
+  const int G = (int)(K / kBlock);
+  const int gb = G * w / KS, ge = G * (w + 1) / KS;
+  const int n = ge - gb;  // 1 .. CH groups
+  unsigned char* st = smem + (size_t)w * stage24_bytes(CH, B);
+  unsigned char* st_meta = st;                         // [CH][16 rows][4 words]
+  unsigned char* st_sign = st + CH * 256;              // [CH][16 rows][2 words]
+  unsigned char* st_sc = st_sign + CH * 128;           // [CH][16 rows] fp16
+  unsigned char* st_x = st_sc + (CH * 32 + 15) / 16 * 16;  // [B][CH * 128] bf16
+  float* red = reinterpret_cast<float*>(smem + (size_t)KS * stage24_bytes(CH, B));
+
+  // 1. every load of the slice.  Item p = lane + 64 t is (row p / CH, group p % CH).
+  constexpr int kItems = (16 * CH + 63) / 64;
+  const int64_t row0 = 16 * nb;
+  u32x4 m_st[kItems];
+  u32x2 s_st[kItems];
+  uint32_t c_st[kItems];
+#pragma unroll
+  for (int t = 0; t < kItems; ++t) {
+    const int p = lane + 64 * t, r = p / CH, gi = p % CH;
+    if (r < 16 && gi < n) {
+      m_st[t] = *reinterpret_cast<const u32x4*>(meta + (row0 + r) * (K / 32) + 4 * (gb + gi));
+      s_st[t] = *reinterpret_cast<const u32x2*>(signs + (row0 + r) * (K / 64) + 2 * (gb + gi));
+      c_st[t] = scales[(row0 + r) * G + gb + gi];
+    }
+  }
+  // x slice of each batch row: 16 chunks of 16 bytes per group
+  constexpr int kXChunks = (16 * CH + 63) / 64;
+  u32x4 x_st[4][kXChunks];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int t = 0; t < kXChunks; ++t) {
+      const int c = lane + 64 * t;
+      if (b < B && c < 16 * n) x_st[b][t] = *reinterpret_cast<const u32x4*>(x + (int64_t)b * K + 128 * gb + 8 * c);
+    }
+  // 2. into this wave's LDS area (read back by the same wave only)
+#pragma unroll
+  for (int t = 0; t < kItems; ++t) {
+    const int p = lane + 64 * t, r = p / CH, gi = p % CH;
+    if (r < 16 && gi < n) {
+      *reinterpret_cast<u32x4*>(st_meta + (gi * 16 + r) * 16) = m_st[t];
+      *reinterpret_cast<u32x2*>(st_sign + (gi * 16 + r) * 8) = s_st[t];
+      *reinterpret_cast<uint16_t*>(st_sc + (gi * 16 + r) * 2) = (uint16_t)c_st[t];
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int t = 0; t < kXChunks; ++t) {
+      const int c = lane + 64 * t;
+      if (b < B && c < 16 * n) *reinterpret_cast<u32x4*>(st_x + (b * CH * 128 + 8 * c) * 2) = x_st[b][t];
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 3. the products.  Lanes of batch rows >= B read row B - 1 (their results
+  // are never stored).
+  const int sbit = 8 * (q & 1);
+  const int b0 = 4 * (q >> 1) + (q & 1);
+  const unsigned char* xrow = st_x + (size_t)min(li, B - 1) * CH * 128 * 2;
+  f32x4 acc_y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int jj = min(j, n - 1);  // slots past the slice repeat its last group
+    const uint32_t mw = *reinterpret_cast<const uint32_t*>(st_meta + (jj * 16 + li) * 16 + 4 * q);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(st_sign + (jj * 16 + li) * 8 + 4 * (q >> 1));
+    const u32x2 sc2 = *reinterpret_cast<const u32x2*>(st_sc + (jj * 16 + 4 * q) * 2);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 a;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int p_bit = sbit + 4 * h + d;
+        a[d] = ((sw << (15 - p_bit)) & 0x80008000u) | 0x3F803F80u;
+      }
+      const unsigned char* xb = xrow + jj * 256;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(xb + 16 * (b0 + 2 * h));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(xb + 16 * (b0 + 2 * h + 8));
+      const u32x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (h == 0)
+        acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, bx),
+                                                        acc, (int)mw, 0, 0);
+      else
+        acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, bx),
+                                                        acc, (int)mw, 0, 1);
+    }
+    const uint32_t sv[4] = {sc2[0] & 0xFFFFu, sc2[0] >> 16, sc2[1] & 0xFFFFu, sc2[1] >> 16};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = __builtin_fmaf(f16_bits_to_f32(sv[r]), acc[r], acc_y[r]);
+      acc_y[r] = j < n ? a : acc_y[r];
+    }
+  }
+
+  // 4. lane holds y[b = li][n = 16 nb + 4q + r]; slices added in order
+  if (KS > 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(w * 4 + r) * 64 + lane] = acc_y[r];
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      for (int u = 1; u < KS; ++u) acc_y[r] += red[(u * 4 + r) * 64 + lane];
+  }
+  if (li < B) *reinterpret_cast<f32x4*>(y + (int64_t)li * N + 16 * nb + 4 * q) = acc_y;
+}
+
 }  // namespace
 
 hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                                  const uint16_t* scales, int64_t N, int64_t K, float* y, hipStream_t stream) {
   const int64_t G = K / kBlock;
   const int64_t wg = N / 16;
+  {
+    // staged path: K slices of at most 9 groups, about 4096 waves or more
+    int ks = 1;
+    // (every slice keeps at least one group: 2 ks <= G before doubling)
+    while (ks < 16 && 2 * ks <= G && ((G + ks - 1) / ks > 9 || wg * ks < 4096)) ks *= 2;
+    const int64_t ch = (G + ks - 1) / ks;
+    if (B <= 4 && ch <= 9) {
+      const int CH = ch <= 5 ? 5 : 9;
+      const size_t lds = (size_t)ks * stage24_bytes(CH, (int)B) + (size_t)ks * 4 * 64 * sizeof(float);
+      if (lds <= 96 * 1024) {
+        const dim3 grid((unsigned)wg), block((unsigned)(64 * ks));
+        if (CH == 5)
+          hipLaunchKernelGGL((gemv24_staged_kernel<5>), grid, block, lds, stream, x, (int)B, meta, signs, scales, N,
+                             K, y);
+        else
+          hipLaunchKernelGGL((gemv24_staged_kernel<9>), grid, block, lds, stream, x, (int)B, meta, signs, scales, N,
+                             K, y);
+        return hipGetLastError();
+      }
+    }
+  }
   int ks = 1;
   while (ks < 8 && wg * ks < 2048 && G / (ks * 2) >= 4) ks *= 2;
   const size_t xbytes = (size_t)B * (K + 8) * 2;

@@ -175,7 +175,8 @@ def test_act8_from_fwht_equals_prep_of_rotated_bf16():
 
 # ---------------------------------------------------------------- 2:4
 
-@pytest.mark.parametrize("n,k,b", [(128, 128, 1), (256, 384, 1), (1024, 1024, 1), (256, 640, 4), (128, 256, 16)])
+@pytest.mark.parametrize("n,k,b", [(128, 128, 1), (256, 384, 1), (1024, 1024, 1), (256, 640, 4), (128, 256, 16),
+                                   (384, 2176, 2), (512, 17408, 1), (256, 1152, 3), (640, 5120, 4), (128, 5120, 6)])
 def test_gemv24_small_matches_oracle(n, k, b):
     say(f"gemv24 N={n} K={k} B={b}")
     meta, signs = synth.random_24(n, k, seed=n + k)
