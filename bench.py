@@ -237,6 +237,33 @@ def extra_phases(gen, dev, quick):
         del codes, scales, x, y
     out["prefill_gemm"] = {"workload": "M=2048, (K,N) = (5120,17408) and (17408,5120), bf16 out", "peak_tflops": PEAK_MFMA_TFLOPS, **gemm}
 
+    # mid-batch GEMM (split K), M = 16 and 256, the three layer shapes, rotated over weight copies
+    mid = {}
+    for k, n in ((D, D), (D, F), (F, D)):
+        copies = 8
+        ws = [(synth.torch_code_words(n, k, gen, dev), synth.torch_scales_f16(n, k, gen, dev)) for _ in range(copies)]
+        for m in (16, 256):
+            x = synth.torch_gaussian_bf16((m, k), gen, dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            wsb = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+            work = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev)
+
+            def runm():
+                for c, sc in ws:
+                    tb.tb_ternary_gemm_splitk(x, c, sc, y=y, workspace=work)
+
+            us = time_eager(runm, 2 if quick else 5) * 1e3 / copies
+            wbytes = n * k // 4 + n * k // 64
+            mid[f"M{m}_{k}x{n}"] = {"us": round(us, 2), "splits": wsb // (m * n * 4) if wsb else 1,
+                                    "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1),
+                                    "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)}
+            log(f"  mid-batch GEMM M={m} K={k} N={n}: {us:.1f} us")
+            del x, y, work
+        del ws
+    out["midbatch_gemm"] = {"workload": "tb_ternary_gemm_splitk, M = 16 and 256, (K, N) = (5120, 5120), (5120, 17408), "
+                                        "(17408, 5120), bf16 out, 8 weight copies rotated, eager launches",
+                            **mid}
+
     # 2:4 GEMV, 17408 x 5120, batch 1, rotated over >= 1 GB of weight copies
     n, k = F, D
     copies = 64
@@ -381,8 +408,8 @@ def summarize_kernel_stats(stats_csv, out_path, command):
 
     rows = [r for r in csv.DictReader(open(stats_csv)) if "tb::" in r["Name"]]
     total = sum(float(r["TotalDurationNs"]) for r in rows)
-    lines = ["# rocprofv3 kernel statistics of the decode-step benchmark on one MI355X (libtb kernels only;",
-             "# the input generation outside the timed region is left out)", f"#   {command}",
+    lines = ["# rocprofv3 kernel statistics of a bench.py run on one MI355X (libtb kernels only;",
+             "# the input generation outside the timed regions is left out)", f"#   {command}",
              "# kernel | calls | average us | total us | share of libtb kernel time", ""]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         short = r["Name"].replace("void tb::(anonymous namespace)::", "").split("(")[0]
@@ -447,11 +474,13 @@ def main():
                     help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--summarize-kernel-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
                     help="write a text summary of a rocprofv3 --stats kernel table")
+    ap.add_argument("--stats-command", default=None,
+                    help="the profiled command to record in the kernel-stats summary (default: the decode-step trace)")
     args = ap.parse_args()
 
     if args.summarize_kernel_stats:
-        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
-               "python3 bench.py --steps 5 --warmup 1 --no-extra --no-cpu-baseline")
+        cmd = args.stats_command or ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                                     "python3 bench.py --steps 5 --warmup 1 --no-extra --no-cpu-baseline")
         summarize_kernel_stats(args.summarize_kernel_stats[0], args.summarize_kernel_stats[1], cmd)
         return
 
