@@ -34,6 +34,7 @@ namespace {
 
 constexpr int BM = 128, BN = 128, KT = 64;
 constexpr int LDS_ROW = KT + 8;  // bf16 elements per LDS row (144 bytes)
+constexpr int kWRing = 2;        // groups of codes and scales in flight ahead
 constexpr int TILE_ELEMS = BM * LDS_ROW;
 
 // bf16 pairs (2t, 2t') of the 16 columns of a dense code word, in column order.
@@ -77,10 +78,14 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + gb * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
   const uint16_t* ssrc = scales + (n0 + wr) * G + gb;
 
+  // Activations come one K step ahead (from L2: every column tile reads
+  // them).  The codes and scales, read once from HBM, come kWRing groups ahead
+  // through a ring of registers, so their latency is hidden behind several
+  // steps of work rather than one.
   u32x4 xs[4];
-  u32x2 cs;
-  uint32_t ss;
-  auto gload = [&](int step) {
+  u32x2 cw[kWRing][2];  // [ring slot][step of the group]
+  uint32_t sw[kWRing];
+  auto gload_x = [&](int step) {
     const int64_t k0 = (int64_t)step * KT;
     if (xvalid) {
       const u32x4* s = reinterpret_cast<const u32x4*>(xsrc + k0);
@@ -90,10 +95,16 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < 4; ++i) xs[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    cs = *reinterpret_cast<const u32x2*>(wsrc + (k0 / kBlock) * 128 + 64 * ((k0 % kBlock) / 64));
-    ss = ssrc[k0 / kBlock];
   };
-  auto lstore = [&](int stage) {
+  // codes and scale of group gi (relative to gb) into ring slot `slot`; groups
+  // past the range reload the last one (never used)
+  auto gload_w = [&](int gi, int slot) {
+    const int64_t g = std::min<int64_t>(gi, ge - gb - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) cw[slot][h] = *reinterpret_cast<const u32x2*>(wsrc + g * 128 + 64 * h);
+    sw[slot] = ssrc[g];
+  };
+  auto lstore = [&](int stage, int slot, int h) {
     // X: 32 bf16 of row xr, as they are
     uint16_t* xd = &lds[stage][0][xr * LDS_ROW + xk];
 #pragma unroll
@@ -103,11 +114,11 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t bits[8];
-      decode_word_bf16(cs[j], bits);
+      decode_word_bf16(cw[slot][h][j], bits);
       *reinterpret_cast<u32x4*>(wd + 16 * j) = u32x4{bits[0], bits[1], bits[2], bits[3]};
       *reinterpret_cast<u32x4*>(wd + 16 * j + 8) = u32x4{bits[4], bits[5], bits[6], bits[7]};
     }
-    if ((tid & 1) == 0) lds_s[stage][wr] = (uint16_t)ss;
+    if ((tid & 1) == 0) lds_s[stage][wr] = (uint16_t)sw[slot];
   };
 
   // acc: the result; accg: the current scale group's products
@@ -138,17 +149,20 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
     }
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    // first step of the group: stage 0, while step + 1 comes in
-    gload(step + 1);
+  // one scale group: its two K steps from LDS stages 0 and 1; the group's
+  // codes are in ring slot `slot`, the next group's in slot `slot` + 1
+  const int ngroups = (int)(ge - gb);
+  auto group = [&](int gi, int slot) {
+    // first step of the group: stage 0, while step 2 gi + 1 comes in
+    gload_x(2 * gi + 1);
     mfma_step(0, true);
-    lstore(1);
+    lstore(1, slot, 1);
+    // the group's codes are all in LDS now: refill its slot kWRing groups ahead
+    gload_w(gi + kWRing, slot);
     __syncthreads();
     // second step: stage 1, while the next group's first step comes in
-    if (step + 2 < nsteps) gload(step + 2);
+    const bool more = gi + 1 < ngroups;
+    if (more) gload_x(2 * gi + 2);
     mfma_step(1, false);
     // fold the group: lane's column n = n0 + wn + 16 j + li
 #pragma unroll
@@ -159,8 +173,19 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(accg[i][j][r], sc, acc[i][j][r]);
     }
-    if (step + 2 < nsteps) lstore(0);
+    if (more) lstore(0, (slot + 1) % kWRing, 0);
     __syncthreads();
+  };
+
+#pragma unroll
+  for (int r = 0; r < kWRing; ++r) gload_w(r, r);
+  gload_x(0);
+  lstore(0, 0, 0);
+  __syncthreads();
+  for (int gi = 0; gi < ngroups; gi += kWRing) {
+#pragma unroll
+    for (int r = 0; r < kWRing; ++r)
+      if (gi + r < ngroups) group(gi + r, r);
   }
 
   // lane holds acc[i][j][r] = 2 * y[m0 + wm + 16i + 4q + r][n0 + wn + 16j + li]
