@@ -251,12 +251,26 @@ hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* cod
 }
 
 int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
-  // about two workgroups per compute unit (256 CUs), at least one scale group
-  // per split, at most 16 splits
-  const int64_t tiles = (N / BN) * ((M + BM - 1) / BM);
-  int64_t s = (512 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, std::min<int64_t>(K / kBlock, 16));
-  return (int)std::max<int64_t>(s, 1);
+  // Each workgroup is latency bound: about one K step (64) per microsecond,
+  // two per scale group.  Two workgroups fit a CU, so 512 run at once and a
+  // launch takes ceil(workgroups / 512) rounds of ceil(G / S) groups each.
+  // Each split beyond one adds M * N fp32 written and read back (about 5 TB/s)
+  // and a second launch.  Take the S in 1 .. min(16, G) with the lowest
+  // estimate (the smaller S on ties).
+  const int64_t tiles = (N / BN) * ((M + BM - 1) / BM), G = K / kBlock;
+  const int64_t smax = std::min<int64_t>(16, G);
+  int best = 1;
+  double best_us = 0.0;
+  for (int64_t s = 1; s <= smax; ++s) {
+    const int64_t rounds = (tiles * s + 511) / 512, groups = (G + s - 1) / s;
+    double us = 2.2 * (double)(rounds * groups);
+    if (s > 1) us += 2.0 + 8.0 * (double)s * (double)M * (double)N / 5.0e6;
+    if (s == 1 || us < best_us) {
+      best = (int)s;
+      best_us = us;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_gemm_ternary_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

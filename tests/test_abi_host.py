@@ -189,9 +189,11 @@ def test_gemm_validation():
 def test_gemm_splitk_validation_and_workspace_size():
     L = tb.lib()
     s = None
-    # 40 tiles of 128 x 128 for M = 64, N = 5120: 13 splits of K = 5120 fill ~512 workgroups
-    assert tb.tb_ternary_gemm_splitk_workspace(64, 5120, 5120) == 13 * 64 * 5120 * 4
-    assert tb.tb_ternary_gemm_splitk_workspace(16, 5120, 17408) == 13 * 16 * 5120 * 4
+    # 40 tiles of 128 x 128 for M = 64, N = 5120: 10 splits of K = 5120 (4 groups each)
+    # keep 400 workgroups, one round of the 512 that fit at once; 12 splits of
+    # K = 17408 likewise (12 groups each)
+    assert tb.tb_ternary_gemm_splitk_workspace(64, 5120, 5120) == 10 * 64 * 5120 * 4
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 5120, 17408) == 12 * 16 * 5120 * 4
     assert tb.tb_ternary_gemm_splitk_workspace(16, 128, 256) == 2 * 16 * 128 * 4      # at most one split per group
     assert tb.tb_ternary_gemm_splitk_workspace(2048, 17408, 5120) == 0                 # enough tiles already
     assert tb.tb_ternary_gemm_splitk_workspace(0, 128, 128) == 0
