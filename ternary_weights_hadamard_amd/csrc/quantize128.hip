@@ -72,7 +72,7 @@ __device__ __forceinline__ constexpr int field_pos(int r) { return 4 * (r & 7) +
 enum Rule { kAbsmean = 0, kTwoFour = 1, kMinError = 2, kResidual = 3 };
 
 template <int RULE>
-__global__ void __launch_bounds__(256) quantize128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+__global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                                            uint32_t* __restrict__ codes,
                                                            uint32_t* __restrict__ meta,
                                                            uint16_t* __restrict__ scales,
