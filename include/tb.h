@@ -319,6 +319,23 @@ TB_API tb_status tb_ternary_gemm_splitk(const uint16_t* x, int64_t M, const uint
                                  int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * The GEMM with the output rotated back to the unrotated basis in the same
+ * launch (the second transform of dpshk.com/news/5289456 §4.2, fused with the
+ * product instead of a separate tb_fwht128 along N):
+ *   y[m][128b + i] = (1/sqrt(128)) * sum_j H[i][j] * y'[m][128b + j],
+ *   y' = the product of tb_ternary_gemm.
+ * y' stays in fp32 and y is rounded once (bf16 nearest even, or fp32), so the
+ * result equals tb_ternary_gemm with fp32 output followed by tb_fwht128
+ * (fp32 in, y_dtype out).  Arguments and errors as tb_ternary_gemm_splitk:
+ * with a workspace of tb_ternary_gemm_splitk_workspace bytes K is split and
+ * the rotation runs in the reduction; with NULL the product is one pass and
+ * the rotation runs in its epilogue.
+ */
+TB_API tb_status tb_ternary_gemm_rotated(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                  int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

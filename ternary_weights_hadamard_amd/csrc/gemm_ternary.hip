@@ -19,12 +19,19 @@
 // buffered, rows padded to spread banks), two steps per scale group.  Each K
 // step reads the codes of 128 rows once (8 bytes per thread) and decodes them
 // once for all 128 activation rows of the tile.
+// Rotated output (ROT): the output tile is 128 columns wide, one 128-block of
+// N, so the back-rotation y = R_N y' (the second transform of
+// dpshk.com/news/5289456 §4.2, fused with the product) runs in the epilogue:
+// the tile goes to LDS in fp32, each 16-lane group transforms a row with the
+// in-register butterflies of the activation transform, and the result is
+// rounded once.
 // Split K (few rows of activations, so few output tiles): workgroup z of S
 // takes the scale groups [G z / S, G (z + 1) / S) and writes its fp32 partial
 // result to a caller-provided workspace; a second kernel adds the S partials
 // in order (the result does not depend on timing) and converts.
 #include <algorithm>
 
+#include "fwht_lanes.h"
 #include "tb_common.h"
 #include "tb_launch.h"
 
@@ -48,7 +55,7 @@ __device__ __forceinline__ void decode_word_bf16(uint32_t w, uint32_t (&out)[8])
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool ROT>
 __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                            const uint32_t* __restrict__ codes,
                                                            const uint16_t* __restrict__ scales, int64_t N,
@@ -65,7 +72,6 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const int64_t G = K / kBlock;
   // this workgroup's scale groups [gb, ge); output: y, or partial z of the workspace
   const int64_t gb = G * blockIdx.z / splits, ge = G * (blockIdx.z + 1) / splits;
-  const int nsteps = (int)(2 * (ge - gb));  // two K steps per group
 
   // global -> register staging assignment
   // X: 128 rows x 64 k bf16 = 128 B per row; thread -> row tid/2, 32 k (64 B) at (tid&1)*32
@@ -189,6 +195,46 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   }
 
   // lane holds acc[i][j][r] = 2 * y[m0 + wm + 16i + 4q + r][n0 + wn + 16j + li]
+  if constexpr (ROT) {
+    // the tile in fp32, rows padded (the main loop's last barrier has passed)
+    constexpr int TROW = BN + 4;
+    static_assert(BM * TROW * sizeof(float) <= sizeof(lds), "rotation tile exceeds LDS");
+    float* t = reinterpret_cast<float*>(&lds[0][0][0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[(wm + 16 * i + 4 * q + r) * TROW + wn + 16 * j + li] = acc[i][j][r] * 0.5f;
+    __syncthreads();
+    const int sub = tid & 15;
+    for (int row = tid >> 4; row < BM; row += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(t + row * TROW + 8 * sub);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(t + row * TROW + 8 * sub + 4);
+      float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      fwht128_lanes(v, sub);
+      const int64_t m = m0 + row;
+      if (m >= M) continue;
+      const int64_t base = m * N + n0 + 8 * sub;
+      if constexpr (OUT_BF16) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = f32_to_bf16_rne(v[2 * e] * kInvSqrt128) | (f32_to_bf16_rne(v[2 * e + 1] * kInvSqrt128) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
+      } else {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = v[e] * kInvSqrt128;
+          hi[e] = v[4 + e] * kInvSqrt128;
+        }
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base) = lo;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base + 4) = hi;
+      }
+    }
+    return;
+  }
   if (splits > 1) y = static_cast<float*>(y) + (size_t)blockIdx.z * M * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -231,15 +277,72 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The S partials summed in order, then each 128-block of a row rotated back
+// (R_N) by one 16-lane group, rounded once.  MN is a multiple of 128.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) splitk_reduce_rot_kernel(const float* __restrict__ part, int S, int64_t MN,
+                                                                void* __restrict__ y) {
+  const int sub = threadIdx.x & 15;
+  const int64_t nblk = MN / kBlock, stride = (int64_t)gridDim.x * 16;
+  for (int64_t bk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); bk - (threadIdx.x >> 4) < nblk; bk += stride) {
+    // every lane of the wave runs the cross-lane rounds; lanes past the end carry zeros
+    const bool live = bk < nblk;
+    const int64_t e = (live ? bk : 0) * kBlock + 8 * sub;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      a = *reinterpret_cast<const f32x4*>(part + e);
+      b = *reinterpret_cast<const f32x4*>(part + e + 4);
+      for (int s = 1; s < S; ++s) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e + 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a[r] += c[r];
+          b[r] += d[r];
+        }
+      }
+    }
+    float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    fwht128_lanes(v, sub);
+    if (!live) continue;
+    if constexpr (OUT_BF16) {
+      u32x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        w[r] = f32_to_bf16_rne(v[2 * r] * kInvSqrt128) | (f32_to_bf16_rne(v[2 * r + 1] * kInvSqrt128) << 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + e) = w;
+    } else {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lo[r] = v[r] * kInvSqrt128;
+        hi[r] = v[4 + r] * kInvSqrt128;
+      }
+      *reinterpret_cast<f32x4*>(static_cast<float*>(y) + e) = lo;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(y) + e + 4) = hi;
+    }
+  }
+}
+
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
-                       int64_t K, void* y, bool bf16_out, int splits, hipStream_t stream) {
+                       int64_t K, void* y, bool bf16_out, bool rot, int splits, hipStream_t stream) {
   const int64_t mt = (M + BM - 1) / BM;
   if (mt > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(N / BN), (unsigned)mt, (unsigned)splits), block(256);
-  if (bf16_out)
-    hipLaunchKernelGGL((gemm_ternary_kernel<true>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits);
-  else
-    hipLaunchKernelGGL((gemm_ternary_kernel<false>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits);
+#define TB_GEMM(B_, R_) \
+  hipLaunchKernelGGL((gemm_ternary_kernel<B_, R_>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits)
+  if (rot) {
+    if (bf16_out)
+      TB_GEMM(true, true);
+    else
+      TB_GEMM(false, true);
+  } else {
+    if (bf16_out)
+      TB_GEMM(true, false);
+    else
+      TB_GEMM(false, false);
+  }
+#undef TB_GEMM
   return hipGetLastError();
 }
 
@@ -247,7 +350,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, cons
 
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream) {
-  return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, 1, stream);
+  return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, false, 1, stream);
 }
 
 int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
@@ -275,13 +378,23 @@ int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_ternary_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                       int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+                                      size_t workspace_bytes, bool rotate, hipStream_t stream) {
   const size_t part = (size_t)M * (size_t)N * sizeof(float);
   const int S = (int)std::min<size_t>((size_t)gemm_splitk_parts(M, N, K), workspace ? workspace_bytes / part : 0);
-  if (S <= 1) return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, 1, stream);
-  const hipError_t e = launch_gemm(x, M, codes, scales, N, K, workspace, false, S, stream);
+  if (S <= 1) return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, rotate, 1, stream);
+  const hipError_t e = launch_gemm(x, M, codes, scales, N, K, workspace, false, false, S, stream);
   if (e != hipSuccess) return e;
   const int64_t MN = M * N;
+  if (rotate) {
+    const int64_t blocks = std::min<int64_t>((MN / kBlock + 15) / 16, 4096);
+    if (y_dtype == TB_BF16)
+      hipLaunchKernelGGL((splitk_reduce_rot_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, workspace, S,
+                         MN, y);
+    else
+      hipLaunchKernelGGL((splitk_reduce_rot_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, workspace, S,
+                         MN, y);
+    return hipGetLastError();
+  }
   const int64_t blocks = std::min<int64_t>((MN / 4 + 255) / 256, 4096);
   if (y_dtype == TB_BF16)
     hipLaunchKernelGGL((splitk_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, workspace, S, MN, y);

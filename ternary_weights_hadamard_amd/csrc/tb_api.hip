@@ -67,6 +67,25 @@ tb_status check_gemv(const tb_gemv_segment& g) {
 }
 
 
+// arguments of the GEMM entry points that take a workspace (NULL allowed)
+tb_status check_gemm_ws(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
+                        int64_t K, const void* y, int y_dtype, const float* workspace, size_t workspace_bytes) {
+  if (!dtype_ok(y_dtype)) return TB_ERR_DTYPE;
+  if (!dims_ok(N, K) || M < 0 || M > (int64_t)65535 * 128) return TB_ERR_SHAPE;
+  if (M == 0) return TB_OK;
+  if (!x || !codes || !scales || !y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || (workspace && !aligned16(workspace)))
+    return TB_ERR_ALIGN;
+  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)M * (size_t)N * dtype_bytes(y_dtype);
+  if (overlap(y, yb, x, (size_t)M * K * 2) || overlap(y, yb, codes, nk / 4) || overlap(y, yb, scales, nk / 64))
+    return TB_ERR_ALIAS;
+  const size_t wb = workspace ? workspace_bytes : 0;
+  if (overlap(workspace, wb, x, (size_t)M * K * 2) || overlap(workspace, wb, codes, nk / 4) ||
+      overlap(workspace, wb, scales, nk / 64) || overlap(workspace, wb, y, yb))
+    return TB_ERR_ALIAS;
+  return TB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,21 +262,19 @@ size_t tb_ternary_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {
 tb_status tb_ternary_gemm_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                  int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
                                  size_t workspace_bytes, void* stream) {
-  if (!dtype_ok(y_dtype)) return TB_ERR_DTYPE;
-  if (!dims_ok(N, K) || M < 0 || M > (int64_t)65535 * 128) return TB_ERR_SHAPE;
-  if (M == 0) return TB_OK;
-  if (!x || !codes || !scales || !y) return TB_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || (workspace && !aligned16(workspace)))
-    return TB_ERR_ALIGN;
-  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)M * (size_t)N * dtype_bytes(y_dtype);
-  if (overlap(y, yb, x, (size_t)M * K * 2) || overlap(y, yb, codes, nk / 4) || overlap(y, yb, scales, nk / 64))
-    return TB_ERR_ALIAS;
-  const size_t wb = workspace ? workspace_bytes : 0;
-  if (overlap(workspace, wb, x, (size_t)M * K * 2) || overlap(workspace, wb, codes, nk / 4) ||
-      overlap(workspace, wb, scales, nk / 64) || overlap(workspace, wb, y, yb))
-    return TB_ERR_ALIAS;
-  return launched(tb::launch_gemm_ternary_splitk(x, M, codes, scales, N, K, y, y_dtype, workspace, wb,
-                                                 as_stream(stream)));
+  const tb_status st = check_gemm_ws(x, M, codes, scales, N, K, y, y_dtype, workspace, workspace_bytes);
+  if (st != TB_OK || M == 0) return st;
+  return launched(tb::launch_gemm_ternary_splitk(x, M, codes, scales, N, K, y, y_dtype, workspace,
+                                                 workspace ? workspace_bytes : 0, false, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemm_rotated(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                  int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  const tb_status st = check_gemm_ws(x, M, codes, scales, N, K, y, y_dtype, workspace, workspace_bytes);
+  if (st != TB_OK || M == 0) return st;
+  return launched(tb::launch_gemm_ternary_splitk(x, M, codes, scales, N, K, y, y_dtype, workspace,
+                                                 workspace ? workspace_bytes : 0, true, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -27,8 +27,10 @@ hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* cod
                                int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream);
 // K splits the split-K GEMM uses for this shape (1: none)
 int gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
+// split K when the workspace allows (else one pass); `rotate` rotates the
+// result back along N (y = R_N y') before it is written
 hipError_t launch_gemm_ternary_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                       int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
-                                      size_t workspace_bytes, hipStream_t stream);
+                                      size_t workspace_bytes, bool rotate, hipStream_t stream);
 
 }  // namespace tb

@@ -61,6 +61,7 @@ SIGNATURES = {
     "tb_ternary_gemm": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]),
     "tb_ternary_gemm_splitk_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "tb_ternary_gemm_splitk": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp, ctypes.c_size_t, _vp]),
+    "tb_ternary_gemm_rotated": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp, ctypes.c_size_t, _vp]),
 }
 
 
@@ -281,4 +282,20 @@ def tb_ternary_gemm_splitk(x, codes, scales, y=None, out_dtype=torch.bfloat16, w
     _check(lib().tb_ternary_gemm_splitk(_p(x), m, _p(codes), _p(scales), n, k, _p(y), _dt(y), _p(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)),
            "tb_ternary_gemm_splitk")
+    return y
+
+
+def tb_ternary_gemm_rotated(x, codes, scales, y=None, out_dtype=torch.bfloat16, workspace=None, stream=None):
+    """The GEMM with its output rotated back along N (y = R_N y') in the same
+    launch; `workspace` (a device tensor, or None for one pass over K) as in
+    tb_ternary_gemm_splitk."""
+    _dev(x, codes, scales)
+    m, k = x.shape
+    n = scales.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _dev(y, workspace)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().tb_ternary_gemm_rotated(_p(x), m, _p(codes), _p(scales), n, k, _p(y), _dt(y), _p(workspace),
+                                         wbytes, _stream(stream)), "tb_ternary_gemm_rotated")
     return y

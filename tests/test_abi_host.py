@@ -208,6 +208,18 @@ def test_gemm_splitk_validation_and_workspace_size():
     assert L.tb_ternary_gemm_splitk(None, 0, None, None, 128, 128, None, 1, None, 0, s) == 0
 
 
+def test_gemm_rotated_validation():
+    L = tb.lib()
+    s = None
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 9, None, 0, s) == 4
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), _v(C), 100, 128, _v(D), 1, None, 0, s) == 2
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), None, 128, 128, _v(D), 1, None, 0, s) == 1
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), _v(C), 128, 128, _v(MIS), 1, None, 0, s) == 3
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), _v(C), 128, 128, _v(A), 0, None, 0, s) == 8    # y over x
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), _v(C), 128, 128, _v(D), 1, _v(C), 4096, s) == 8  # ws over scales
+    assert L.tb_ternary_gemm_rotated(None, 0, None, None, 128, 128, None, 1, None, 0, s) == 0
+
+
 def test_binding_raises_typed_error_on_cpu_tensors():
     import torch
 

@@ -155,3 +155,63 @@ def test_gemm_splitk_exact_and_fallbacks():
     assert torch.all(wbuf[:32] == 7.0) and torch.all(wbuf[32 + wsb // 4:] == 7.0)
     assert torch.all(ybuf[:32] == -5.0) and torch.all(ybuf[32 + m * n:] == -5.0)
     assert np.array_equal(host_f64(y), ref)
+
+
+# ---------------------------------------------------------------- output rotation fused
+
+def _rotate_rows(y):
+    return oracle.hadamard.fwht_dense(y)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (7, 256, 384), (300, 384, 640), (64, 512, 2176)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("split", [False, True])
+def test_gemm_rotated_matches_oracle(m, n, k, out, split):
+    say(f"rotated gemm M={m} N={n} K={k} {out} split={split}")
+    codes = synth.random_code_words(n, k, seed=m + 5 * n)
+    scales = synth.random_scales_f16(n, k, seed=k + 3)
+    x = synth.gaussian_bf16((m, k), seed=m + 11)
+    ws = None
+    if split:
+        wsb = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+        ws = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=DEV)
+    y = tb.tb_ternary_gemm_rotated(bf16_dev(x), u32_dev(codes), f16_dev(scales),
+                                   out_dtype=torch.bfloat16 if out == "bf16" else torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    ref = _rotate_rows(oracle.matvec.gemm(x, codes, scales, k))
+    assert_close(host_f64(y), ref, f"rotated gemm {m}x{n}x{k} {out}", out_bf16=out == "bf16")
+
+
+@pytest.mark.parametrize("m,n,k", [(40, 384, 1280), (256, 5120, 5120)])
+def test_gemm_rotated_equals_product_then_rotation(m, n, k):
+    # the fused rotation is the same fp32 product and the same butterflies,
+    # rounded once: bit for bit the two-call composition
+    codes = u32_dev(synth.random_code_words(n, k, seed=71))
+    scales = f16_dev(synth.random_scales_f16(n, k, seed=72))
+    x = bf16_dev(synth.gaussian_bf16((m, k), seed=73))
+    wsb = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+    ws = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=DEV)
+    for out in (torch.float32, torch.bfloat16):
+        y1 = tb.tb_fwht128(tb.tb_ternary_gemm(x, codes, scales, out_dtype=torch.float32), out_dtype=out)
+        yr = tb.tb_ternary_gemm_rotated(x, codes, scales, out_dtype=out)
+        y2 = tb.tb_fwht128(tb.tb_ternary_gemm_splitk(x, codes, scales, out_dtype=torch.float32, workspace=ws),
+                           out_dtype=out)
+        yrs = tb.tb_ternary_gemm_rotated(x, codes, scales, out_dtype=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(yr, y1), f"one pass, {out}"
+        assert torch.equal(yrs, y2), f"split K, {out}"
+
+
+def test_gemm_rotated_full_size_sampled():
+    m, k, n = 2048, 5120, 17408
+    say(f"rotated gemm full M={m} K={k} N={n}")
+    codes = synth.random_code_words(n, k, seed=74)
+    scales = synth.random_scales_f16(n, k, seed=75)
+    x = synth.gaussian_bf16((m, k), seed=76)
+    y = host_f64(tb.tb_ternary_gemm_rotated(bf16_dev(x), u32_dev(codes), f16_dev(scales)))
+    rs = np.sort(np.random.default_rng(8).choice(m, 48, replace=False))
+    blocks = np.sort(np.random.default_rng(9).choice(n // 128, 2, replace=False))
+    tiles = (8 * blocks[:, None] + np.arange(8)[None, :]).ravel()
+    cs = (128 * blocks[:, None] + np.arange(128)[None, :]).ravel()
+    ref = _rotate_rows(oracle.matvec.gemm(x[rs], codes[tiles], scales[cs], k))
+    assert_close(y[np.ix_(rs, cs)], ref, "rotated gemm (48 rows x 2 column blocks sampled)", out_bf16=True)
