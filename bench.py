@@ -237,6 +237,25 @@ def extra_phases(gen, dev, quick):
         del codes, scales, x, y
     out["prefill_gemm"] = {"workload": "M=2048, (K,N) = (5120,17408) and (17408,5120), bf16 out", "peak_tflops": PEAK_MFMA_TFLOPS, **gemm}
 
+    # the same GEMMs with the output rotated back in the epilogue, against the
+    # product followed by a separate rotation launch
+    rot = {}
+    for k, n in ((D, F), (F, D)):
+        codes = synth.torch_code_words(n, k, gen, dev)
+        scales = synth.torch_scales_f16(n, k, gen, dev)
+        x = synth.torch_gaussian_bf16((m, k), gen, dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        yf = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ms_f = time_eager(lambda: tb.tb_ternary_gemm_rotated(x, codes, scales, y=y), 3 if quick else 10)
+        ms_s = time_eager(lambda: (tb.tb_ternary_gemm(x, codes, scales, y=yf), tb.tb_fwht128(yf, y=y)),
+                          3 if quick else 10)
+        rot[f"{k}x{n}"] = {"fused_ms": round(ms_f, 4), "separate_ms": round(ms_s, 4),
+                           "fused_tflops": round(2.0 * m * n * k / (ms_f * 1e-3) / 1e12, 1)}
+        log(f"  rotated GEMM M={m} K={k} N={n}: fused {ms_f:.3f} ms, product + rotation {ms_s:.3f} ms")
+        del codes, scales, x, y, yf
+    out["prefill_gemm_rotated"] = {"workload": "M=2048, both shapes, y = R_N y' in bf16: fused (tb_ternary_gemm_rotated) "
+                                               "vs tb_ternary_gemm fp32 + tb_fwht128", **rot}
+
     # mid-batch GEMM (split K), M = 16 and 256, the three layer shapes, rotated over weight copies
     mid = {}
     for k, n in ((D, D), (D, F), (F, D)):
