@@ -90,8 +90,8 @@ typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_
  * Every bf16 activation is stored exactly as the sum of four e4m3 values on
  * four sub-rows (two magnitude levels x high and low significand halves) with
  * one E8M0 scale per 32 K-elements and sub-row:
- *   values  uint8 [B][K/128][4 sub-rows][4 q][32]: bytes 0-15 of q are
- *           K 128g + 16q + (0..15), bytes 16-31 are K 128g + 64 + 16q + (0..15);
+ *   values  uint8 [B][K/128][2 halves h][4 sub-rows][4 q][16]: the 16 bytes
+ *           of (h, q) are K 128g + 64h + 16q + (0..15);
  *   scales  uint8 at byte offset 4*B*K: [B][K/128][4 sub-rows][4 blocks],
  *           block q = K 128g + 32q .. +31; 0xFF marks a block holding a
  *           non-finite activation (the product rows then come out NaN).

@@ -22,9 +22,11 @@
 //
 // Layout for B activation rows of length K (G = K / 128 groups), one buffer of
 // 4 B K + B K / 8 bytes:
-//   values  [B][G][4 sub-rows][4 lane groups q][32 bytes]: bytes 0-15 of lane
-//           group q are K 128 g + 16 q + (0..15), bytes 16-31 are K 128 g + 64 +
-//           16 q + (0..15) - the fp8 A-operand order of the instruction.
+//   values  [B][G][2 halves h][4 sub-rows][4 lane groups q][16 bytes]: the 16
+//           bytes of (h, q) are K 128 g + 64 h + 16 q + (0..15).  Lane group q
+//           of the instruction's fp8 A operand takes (0, q) as its bytes 0-15
+//           and (1, q) as bytes 16-31, so the 16 lanes of one batch row read
+//           256 contiguous bytes per 16-byte load (whole cache lines).
 //   scales  at byte 4 B K: [B][G][4 sub-rows][4 blocks q] E8M0 codes, block q =
 //           K 128 g + 32 q .. + 31.  0xFF (NaN) marks a block that held a
 //           non-finite activation; its sub-row-0 element is then an e4m3 NaN.
@@ -117,11 +119,12 @@ __device__ __forceinline__ void act8_encode(const uint32_t (&h)[8], uint32_t (&w
   }
 }
 
-// Byte offset of lane `sub`'s 8 values inside a sub-row of 128 bytes: K
-// 128 g + 8 sub .. +7 is 16-chunk c = sub / 2, i.e. lane group c % 4, half c / 4.
+// Byte offset of lane `sub`'s 8 values of sub-row 0 inside a group's 512
+// value bytes (sub-row j is 64 bytes further on): K 128 g + 8 sub .. +7 is
+// 16-chunk c = sub / 2, i.e. half c / 4, lane group c % 4.
 __device__ __forceinline__ int act8_lane_offset(int sub) {
   const int c = sub >> 1;
-  return (c & 3) * 32 + (c >> 2) * 16 + (sub & 1) * 8;
+  return (c >> 2) * 256 + (c & 3) * 16 + (sub & 1) * 8;
 }
 
 // act8_encode, then store the group: `vals` points at its 512 value bytes,
@@ -135,7 +138,7 @@ __device__ __forceinline__ void act8_encode_store(const uint32_t (&h)[8], int su
   const int off = act8_lane_offset(sub);
 #pragma unroll
   for (int j = 0; j < kActSub; ++j)
-    *reinterpret_cast<u32x2*>(vals + j * 128 + off) = u32x2{word[j][0], word[j][1]};
+    *reinterpret_cast<u32x2*>(vals + j * 64 + off) = u32x2{word[j][0], word[j][1]};
   if ((sub & 3) == 0) {
     const int q = sub >> 2;  // 32-block of this quad
 #pragma unroll

@@ -16,12 +16,16 @@
 //   * Lane (i, q) holds output rows 4q .. 4q + 3 of column i: the four sub-rows
 //     of batch row 4m + q.  Their sum times f16(scale) / 2 is the group's
 //     contribution.
-// Work split: a wave owns one 16-row tile and a slice of at most CH groups of
-// K; it issues every load of its slice (activations, codes and scales, group
-// by group) before the first instruction that needs one, so all of them are in
-// flight at once and the in-order load counter never makes a far load wait for
-// a near one.  The KS slices of a tile are the waves of one workgroup and are
-// added through LDS in a fixed order (the result does not depend on timing).
+// Two kernels split the work:
+//   * batch 1 (staged): a wave owns one 16-row tile and a slice of K, stages its
+//     activation slice in LDS and issues every load of the slice before the
+//     first instruction that needs one;
+//   * batch 2-16, and batch 1 past the staged slices (wide): a wave owns T
+//     consecutive tiles and a slice of K, walked
+//     in chunks, and applies each activation fragment to all T tiles.
+// The K slices of a tile are waves of one workgroup and are added through LDS
+// in a fixed order, so a result does not depend on timing or on which
+// segments share its launch.
 #include <algorithm>
 
 #include "tb_common.h"
@@ -37,113 +41,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 constexpr int kMaxSlices = 16;  // waves per workgroup
 constexpr int kMaxSegs = TB_MAX_SEGMENTS;
 
-// groups per wave and chunk: a group costs 9 * NB4 + 3 registers, and a
-// workgroup of up to 16 waves leaves 128 per lane
-template <int NB4>
-struct Chunk {
-  static constexpr int value = NB4 == 1 ? 9 : NB4 == 2 ? 4 : NB4 == 3 ? 3 : 2;
-};
-
-template <int NB4, int CH>
-__global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint8_t* __restrict__ act, int B,
-                                                                        const uint32_t* __restrict__ codes,
-                                                                        const uint16_t* __restrict__ scales,
-                                                                        int64_t N, int64_t K, int P,
-                                                                        float* __restrict__ y, int KS) {
-  __shared__ float red[kMaxSlices][NB4][64];
-  const int lane = threadIdx.x & 63;
-  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i = lane & 15, q = lane >> 4;
-  const int64_t nb = blockIdx.x;
-  const int GA = (int)(K / kBlock);  // activation groups per row
-  const int G = GA * P;              // code and scale groups per row (P planes)
-  const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
-
-  // activation operand rows of this lane: batch 4m + i/4, sub-row i % 4
-  const uint8_t* av_base[NB4];
-  const uint8_t* as_base[NB4];
-  bool arow[NB4];
-#pragma unroll
-  for (int m = 0; m < NB4; ++m) {
-    const int b = 4 * m + (i >> 2);
-    arow[m] = b < B;
-    const size_t row = (size_t)(arow[m] ? b : 0) * GA;
-    av_base[m] = act + (row * 16 + (i & 3) * 4 + q) * 32;
-    as_base[m] = act + (size_t)4 * B * K + row * 16 + (i & 3) * 4 + q;
-  }
-  const uint32_t* cp = codes + (size_t)nb * G * 128 + 2 * lane;
-  const uint16_t* sp = scales + (size_t)(16 * nb + i) * G;
-
-  float acc[NB4];
-#pragma unroll
-  for (int m = 0; m < NB4; ++m) acc[m] = 0.f;
-
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int c = gb; c < ge; c += CH) {
-    const int n = min(CH, ge - c);
-    i32x8 av[CH][NB4];
-    int as[CH][NB4];
-    u32x2 cw[CH];
-    uint32_t sw[CH];
-    // every load of the chunk first (slots past the slice repeat its last group;
-    // the loops stay free of early exits so the arrays live in registers)
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int g = min(c + j, ge - 1);
-      const int ga = P == 1 ? g : g >> 1;  // the activation group of code group g
-      cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)g * 128);
-      sw[j] = sp[g];
-#pragma unroll
-      for (int m = 0; m < NB4; ++m) {
-        if (arow[m]) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(av_base[m] + (size_t)ga * 512);
-          const u32x4 lo = p[0], hi = p[1];
-          av[j][m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          as[j][m] = as_base[m][(size_t)ga * 16];
-        } else {
-          av[j][m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-          as[j][m] = 127;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const uint32_t w0 = cw[j][0], w1 = cw[j][1];
-      const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
-                        (int)((w1 << 2) & 0xCCCCCCCCu)};
-      const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
-      const float s = f16_bits_to_f32(sw[j]) * 0.5f;
-#pragma unroll
-      for (int m = 0; m < NB4; ++m) {
-        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[j][m], b8, zero, 0, 4, 0, as[j][m], 0, 127);
-        // the destination must not reuse the sources' registers (the
-        // instruction reads them over several passes)
-        keep_sources_past(d, av[j][m], bw);
-        const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc[m]);
-        acc[m] = j < n ? a : acc[m];  // slots past the slice (a repeated group) add nothing
-      }
-    }
-  }
-
-  if (KS > 1) {
-#pragma unroll
-    for (int m = 0; m < NB4; ++m) red[ks][m][lane] = acc[m];
-    __syncthreads();
-    if (ks != 0) return;
-#pragma unroll
-    for (int m = 0; m < NB4; ++m)
-      for (int w = 1; w < KS; ++w) acc[m] += red[w][m][lane];
-  }
-#pragma unroll
-  for (int m = 0; m < NB4; ++m) {
-    const int b = 4 * m + q;
-    if (b < B) y[(size_t)b * N + 16 * nb + i] = acc[m];
-  }
-}
-
-
-// Staged path (B <= 4, the activation slices of a workgroup fit in LDS).  Per
+// Staged path (batch 1, the activation slices of a workgroup fit in LDS).  Per
 // wave: the activation operand of its slice is copied into a private LDS area
 // with whole-wave 16-byte loads (one load moves two groups of one batch row),
 // the weight scales come in with one load per four groups (lane (i, q) fetches
@@ -158,12 +56,10 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_direct_kernel(const uint
 // workgroup of `waves` waves covers waves / ks tiles of it.
 constexpr int kStageBytes = 528;  // act8 bytes per group and batch row (512 values + 16 scales)
 constexpr size_t kStagedMaxLds = 96 * 1024;
-// groups per wave: 10 for one batch row, 8 when up to four rows are staged
-// (the staging registers grow with the rows).  A batch-1 group whose longest
-// K would need more than 8 waves per tile takes 18 groups per wave instead:
-// 8-wave workgroups of at most 76 KB LDS, two per CU, rather than 16-wave
-// ones that fit only once per CU.
-constexpr int staged_ch(int bmax) { return bmax == 1 ? 10 : 8; }
+// groups per wave: 10.  A group whose longest K would need more than 8 waves
+// per tile takes 18 groups per wave instead: 8-wave workgroups of at most 76 KB
+// LDS, two per CU, rather than 16-wave ones that fit only once per CU.
+constexpr int kStagedCH = 10;
 constexpr int kLongCH = 18;
 
 struct StagedSeg {
@@ -275,15 +171,15 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
     //    Rows of batches >= B only reach output rows that are never stored, so
     //    those lanes read the last batch row instead of branching.
     const int bp = min(i >> 2, B - 1);
-    const unsigned char* a_src = st + (size_t)bp * SG * 512 + ((i & 3) * 4 + q) * 32;
+    const unsigned char* a_src = st + (size_t)bp * SG * 512 + ((i & 3) * 4 + q) * 16;
     const unsigned char* a_sc = st_sc + (size_t)bp * SG * 16 + (i & 3) * 4 + q;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       // staged activation group of slot j (slots past the slice repeat the last one)
       const int aj = P == 1 ? j : (min(gb + j, ge - 1) >> 1) - ab;
-      const u32x4* p = reinterpret_cast<const u32x4*>(a_src + aj * 512);
-      const u32x4 lo = p[0], hi = p[1];
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(a_src + aj * 512);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(a_src + aj * 512 + 256);
       const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       const int as = a_sc[aj * 16];
       const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * (j & 3)) * 4, (int)sr[j >> 2]);
@@ -308,9 +204,193 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
   if (live && q < B) sg.y[(size_t)q * N + 16 * nb + i] = acc;
 }
 
-int slices(int64_t K, int ch) {
-  const int64_t G = K / kBlock;
-  return (int)std::min<int64_t>(kMaxSlices, (G + ch - 1) / ch);
+// Wide path (B > 4, or a K too long for the staged slices).  A batch quad's
+// activation operand is 8 registers (32 bytes) per lane and group, so at batch
+// 8 one group of activations is eight times the bytes of one 16-row code
+// tile; read once per tile, the activations would cost more cache-to-CU
+// traffic than the codes cost HBM traffic.  A wave here covers T consecutive
+// tiles of 16 output rows and applies each activation fragment to all of
+// them.  The slice of K is walked in chunks of CH groups, every load of a
+// chunk issued before its first product; per tile and chunk one scale load
+// brings CH groups (lane (i, q) fetches row i's scale of group c + q) and
+// ds_bpermute hands them to the other lanes.  Rows of batches >= B in the last
+// quad read batch row B - 1 instead: a row of the instruction's A operand
+// reaches only its own output row, which is never stored.  As in the staged
+// path one launch carries several segments, a segment splits K over ks waves
+// (a power of two) and the slices of a tile are added through LDS in a fixed
+// order.  N is a multiple of 128, so a tile count is a multiple of 8 and a
+// wave's T tiles (T divides 8) lie inside the segment or wholly past it.
+struct WideSeg {
+  const uint8_t* act;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  float* y;
+  int64_t N, K;
+  int B, P, ks, wg_begin;
+};
+
+struct WideSegs {
+  WideSeg s[kMaxSegs];
+  int count;
+};
+
+__device__ __forceinline__ WideSeg pick_wide_segment(const WideSegs& a) {
+  const int wg = (int)blockIdx.x;
+  WideSeg r = a.s[0];
+#pragma unroll
+  for (int t = 1; t < kMaxSegs; ++t) {
+    const bool take = t < a.count && wg >= a.s[t].wg_begin;
+    r.act = take ? a.s[t].act : r.act;
+    r.codes = take ? a.s[t].codes : r.codes;
+    r.scales = take ? a.s[t].scales : r.scales;
+    r.y = take ? a.s[t].y : r.y;
+    r.N = take ? a.s[t].N : r.N;
+    r.K = take ? a.s[t].K : r.K;
+    r.B = take ? a.s[t].B : r.B;
+    r.P = take ? a.s[t].P : r.P;
+    r.ks = take ? a.s[t].ks : r.ks;
+    r.wg_begin = take ? a.s[t].wg_begin : r.wg_begin;
+  }
+  return r;
+}
+
+template <int NB4, int T, int CH>
+__global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs segs) {
+  static_assert(8 % T == 0 && CH <= 4, "tile sets must divide 8 tiles; one scale load covers at most 4 groups");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const WideSeg sg = pick_wide_segment(segs);
+  const int B = sg.B, KS = sg.ks, P = sg.P;
+  const int64_t N = sg.N, K = sg.K;
+  const int waves = (int)(blockDim.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = w % KS;
+  const int i = lane & 15, q = lane >> 4;
+  const int64_t tiles = N / 16;
+  const int64_t t0 = ((int64_t)(blockIdx.x - sg.wg_begin) * (waves / KS) + w / KS) * T;  // first tile
+  const bool live = t0 < tiles;
+  const int GA = (int)(K / kBlock);  // activation groups per row
+  const int G = GA * P;              // code and scale groups per row
+  const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
+
+  float acc[T][NB4];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int m = 0; m < NB4; ++m) acc[t][m] = 0.f;
+
+  if (live) {
+    // Addresses are a uniform base plus a 32-bit per-lane byte offset.
+    // Activation operand rows of this lane: batch 4m + i / 4 (clamped to
+    // B - 1), sub-row i % 4, lane group q.
+    const unsigned char* act = sg.act;
+    const unsigned char* act_sc = sg.act + (size_t)4 * B * K;
+    uint32_t av_off[NB4], as_off[NB4];
+#pragma unroll
+    for (int m = 0; m < NB4; ++m) {
+      const int b = min(4 * m + (i >> 2), B - 1);
+      av_off[m] = (uint32_t)b * GA * 512 + ((i & 3) * 4 + q) * 16;
+      as_off[m] = (uint32_t)b * GA * 16 + (i & 3) * 4 + q;
+    }
+    const unsigned char* cbase = reinterpret_cast<const unsigned char*>(sg.codes + (size_t)t0 * G * 128);
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(sg.scales + (size_t)16 * t0 * G);
+    const uint32_t c_stride = (uint32_t)G * 512, s_stride = (uint32_t)G * 32;  // bytes per tile
+    const uint32_t c_lane = (uint32_t)lane * 8, s_lane = (uint32_t)i * G * 2;
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int c = gb; c < ge; c += CH) {
+      const int n = min(CH, ge - c);
+      i32x8 av[CH][NB4];
+      int as[CH][NB4];
+      u32x2 cw[CH][T];
+      uint32_t sr[T];
+      // every load of the chunk first (slots past the slice repeat its last group)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int g = min(c + j, ge - 1);
+        const uint32_t ga = P == 1 ? g : g >> 1;  // the activation group of code group g
+#pragma unroll
+        for (int m = 0; m < NB4; ++m) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(act + (av_off[m] + ga * 512));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(act + (av_off[m] + ga * 512 + 256));
+          av[j][m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          as[j][m] = act_sc[as_off[m] + ga * 16];
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          cw[j][t] = *reinterpret_cast<const u32x2*>(cbase + (t * c_stride + (uint32_t)g * 512 + c_lane));
+      }
+      const uint32_t gq = (uint32_t)min(c + q, ge - 1);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        sr[t] = *reinterpret_cast<const uint16_t*>(sbase + (t * s_stride + s_lane + gq * 2));
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t w0 = cw[j][t][0], w1 = cw[j][t][1];
+          const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
+                            (int)((w1 << 2) & 0xCCCCCCCCu)};
+          const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
+          const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * j) * 4, (int)sr[t]);
+          const float s = f16_bits_to_f32((uint32_t)sbits & 0xFFFFu) * 0.5f;
+#pragma unroll
+          for (int m = 0; m < NB4; ++m) {
+            const f32x4 d =
+                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[j][m], b8, zero, 0, 4, 0, as[j][m], 0, 127);
+            keep_sources_past(d, av[j][m], bw);  // the destination must not reuse the sources' registers
+            const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc[t][m]);
+            acc[t][m] = j < n ? a : acc[t][m];  // slots past the slice add nothing
+          }
+        }
+      }
+    }
+  }
+
+  if (KS > 1) {
+    float* red = reinterpret_cast<float*>(smem);  // [waves][T][NB4][64]
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int m = 0; m < NB4; ++m) red[((w * T + t) * NB4 + m) * 64 + lane] = acc[t][m];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int m = 0; m < NB4; ++m)
+        for (int u = 1; u < KS; ++u) acc[t][m] += red[(((w + u) * T + t) * NB4 + m) * 64 + lane];
+  }
+  if (live) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int m = 0; m < NB4; ++m) {
+        const int b = 4 * m + q;
+        if (b < B) sg.y[(size_t)b * N + 16 * (t0 + t) + i] = acc[t][m];
+      }
+    }
+  }
+}
+
+// Groups per chunk of the wide path: a group costs 9 * NB4 + 2 * T registers
+// per lane, and T * NB4 accumulators stay live
+template <int NB4, int T>
+struct WideChunk {
+  static constexpr int value = NB4 * 9 + 2 * T <= 26 ? 3 : 2;
+};
+
+// K slices of a wide segment: the smallest power of two leaving at most
+// kWideSlice groups per wave
+#ifndef TB_WIDE_SLICE
+#define TB_WIDE_SLICE 6
+#endif
+constexpr int kWideSlice = TB_WIDE_SLICE;
+int wide_slices(int64_t G) {
+  int ks = 1;
+  while (ks < kMaxSlices && G > (int64_t)ks * kWideSlice) ks *= 2;
+  return ks;
 }
 
 // K slices of a staged segment: the smallest power of two giving at most ch
@@ -324,34 +404,109 @@ int staged_slices(int64_t K, int ch) {
 
 }  // namespace
 
-// Groups per wave of one segment, a function of its own code length K (all
-// planes) and B only, so that a segment is cut into the same K slices (and
+// Groups per wave of one staged segment, a function of its own code length K
+// (all planes) only, so that a segment is cut into the same K slices (and
 // summed in the same order) whatever it is launched with.
-int segment_ch(int64_t K, int64_t B) {
-  if (B > 1) return staged_ch(4);
-  const int ks = staged_slices(K, staged_ch(1));
-  return ks != 0 && ks <= 8 ? staged_ch(1) : kLongCH;
+int segment_ch(int64_t K) {
+  const int ks = staged_slices(K, kStagedCH);
+  return ks != 0 && ks <= 8 ? kStagedCH : kLongCH;
+}
+
+// The staged path takes a batch-1 segment whose K fits the staged slices;
+// everything else takes the wide path (from batch 2 on it is the faster one:
+// 27 against 40 us at batch 2 on a 27B layer's QKV + O + gate/up).
+bool stageable(const GemvSegment& g) {
+  const int64_t kc = g.K * g.planes;  // code groups x 128
+  return g.B == 1 && staged_slices(kc, segment_ch(kc)) != 0;
+}
+
+// Wide launch geometry for T tiles per wave: workgroups, waves per workgroup
+// and the segment table
+int wide_plan(const GemvSegment* segs, int count, int T, WideSegs& ws, int& waves) {
+  waves = 1;
+  for (int c = 0; c < count; ++c) waves = std::max(waves, wide_slices(segs[c].K / kBlock * segs[c].planes));
+  int wg = 0;
+  for (int c = 0; c < count; ++c) {
+    const int ks = wide_slices(segs[c].K / kBlock * segs[c].planes);
+    const int64_t sets = segs[c].N / 16 / T, per_wg = waves / ks;
+    ws.s[c] = WideSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
+                      (int)segs[c].B, (int)segs[c].planes, ks, wg};
+    wg += (int)((sets + per_wg - 1) / per_wg);
+  }
+  ws.count = count;
+  return wg;
+}
+
+#ifndef TB_WIDE_TMAX
+#define TB_WIDE_TMAX 8
+#endif
+#ifndef TB_WIDE_MIN_WAVES
+#define TB_WIDE_MIN_WAVES 2048
+#endif
+
+template <int NB4, int T>
+hipError_t launch_wide_t(const WideSegs& ws, int wg, int waves, hipStream_t stream) {
+  const size_t lds = (size_t)waves * T * NB4 * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemv_wide_kernel<NB4, T, WideChunk<NB4, T>::value>), dim3((unsigned)wg), dim3(64 * waves), lds,
+                     stream, ws);
+  return hipGetLastError();
+}
+
+// Tiles per wave: the most (up to TB_WIDE_TMAX, 4 above batch 8 where the
+// accumulators crowd the registers) that still give the launch
+// TB_WIDE_MIN_WAVES waves, else one.  More tiles per wave means fewer
+// activation reads per tile; fewer waves leave CUs idle (the down projection,
+// 320 tiles, takes two per wave).  Measured on the 27B-shaped layers.
+template <int NB4>
+hipError_t launch_wide(const GemvSegment* segs, int count, hipStream_t stream) {
+  WideSegs ws{};
+  int waves = 1;
+  for (int T = NB4 <= 2 ? TB_WIDE_TMAX : std::min(TB_WIDE_TMAX, 4); T >= 1; T /= 2) {
+    const int wg = wide_plan(segs, count, T, ws, waves);
+    if (T > 1 && (int64_t)wg * waves < TB_WIDE_MIN_WAVES) continue;
+#if TB_WIDE_TMAX >= 8
+    if (T == 8) return launch_wide_t<NB4, 8>(ws, wg, waves, stream);
+#endif
+    if (T == 4) return launch_wide_t<NB4, 4>(ws, wg, waves, stream);
+    if (T == 2) return launch_wide_t<NB4, 2>(ws, wg, waves, stream);
+    return launch_wide_t<NB4, 1>(ws, wg, waves, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream) {
-  // one grouped launch when every segment fits the staged path together, else
-  // each segment on its own exactly as a single call would run it
+  // one grouped launch when every segment takes the same path alone and the
+  // group fits it, else each segment on its own exactly as a single call
+  // would run it (a segment's result never depends on its companions)
+  int n_staged = 0;
+  for (int c = 0; c < count; ++c) n_staged += stageable(segs[c]) ? 1 : 0;
+  if (count >= 1 && count <= kMaxSegs && n_staged == 0) {
+    int bmax = 1;
+    for (int c = 0; c < count; ++c) bmax = std::max(bmax, (int)segs[c].B);
+    switch ((bmax + 3) / 4) {
+      case 1:
+        return launch_wide<1>(segs, count, stream);
+      case 2:
+        return launch_wide<2>(segs, count, stream);
+      case 3:
+        return launch_wide<3>(segs, count, stream);
+      default:
+        return launch_wide<4>(segs, count, stream);
+    }
+  }
   StagedSegs st{};
-  bool staged = count <= kMaxSegs;
+  bool staged = count <= kMaxSegs && n_staged == count;
   int bmax = 1, ch = 1, waves = 1, wg = 0;
   const int64_t planes = count > 0 ? segs[0].planes : 1;
   for (int c = 0; c < count && staged; ++c) {
     const int64_t kc = segs[c].K * segs[c].planes;  // code groups x 128
-    const int sc = segment_ch(kc, segs[c].B);
+    const int sc = segment_ch(kc);
     const int ks = staged_slices(kc, sc);
-    if (segs[c].B > 4 || ks == 0) staged = false;
     bmax = std::max(bmax, (int)segs[c].B);
     ch = std::max(ch, sc);
     waves = std::max(waves, ks);
     if (segs[c].planes != planes) staged = false;  // one plane count per grouped launch
   }
-  // kernels exist for (10, 1), (18, 1) and (8, up to 4 rows)
-  if (bmax > 1 && ch != staged_ch(4)) staged = false;
   // a slice of at most ch code groups spans at most ch activation groups with
   // one plane, ch / 2 + 1 with two
   const int stage_groups = planes == 1 ? ch : ch / 2 + 1;
@@ -359,7 +514,7 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
   if (staged && lds <= kStagedMaxLds) {
     for (int c = 0; c < count; ++c) {
       const int64_t kc = segs[c].K * segs[c].planes;
-      const int ks = staged_slices(kc, segment_ch(kc, segs[c].B));
+      const int ks = staged_slices(kc, segment_ch(kc));
       const int64_t tiles = segs[c].N / 16, per_wg = waves / ks;
       st.s[c] = StagedSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
                           (int)segs[c].B, ks, wg, 0};
@@ -370,65 +525,30 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
     st.stage_groups = stage_groups;
     const dim3 grid((unsigned)wg), block(64 * waves);
 #define TB_STAGED(CH_, BMAX_, P_) hipLaunchKernelGGL((gemv_staged_kernel<CH_, BMAX_, P_>), grid, block, lds, stream, st)
+    // batch 1 only: kernels exist for 10 and 18 groups per wave
     if (planes == 1) {
-      if (bmax == 1 && ch == kLongCH)
+      if (ch == kLongCH)
         TB_STAGED(kLongCH, 1, 1);
-      else if (bmax == 1)
-        TB_STAGED(staged_ch(1), 1, 1);
       else
-        TB_STAGED(staged_ch(4), 4, 1);
+        TB_STAGED(kStagedCH, 1, 1);
     } else {
-      if (bmax == 1 && ch == kLongCH)
+      if (ch == kLongCH)
         TB_STAGED(kLongCH, 1, 2);
-      else if (bmax == 1)
-        TB_STAGED(staged_ch(1), 1, 2);
       else
-        TB_STAGED(staged_ch(4), 4, 2);
+        TB_STAGED(kStagedCH, 1, 2);
     }
 #undef TB_STAGED
     return hipGetLastError();
   }
-  if (count == 1)
-    return launch_gemv_direct(segs[0].act, segs[0].B, segs[0].codes, segs[0].scales, segs[0].N, segs[0].K,
-                              (int)segs[0].planes, segs[0].y, stream);
+  if (count == 1) {
+    // a stageable segment whose staging does not fit the LDS budget
+    return launch_wide<1>(segs, 1, stream);
+  }
   for (int c = 0; c < count; ++c) {
     const hipError_t e = launch_gemv_multi(segs + c, 1, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-hipError_t launch_gemv_direct(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                              int64_t N, int64_t K, int planes, float* y, hipStream_t stream) {
-  const dim3 grid((unsigned)(N / 16));
-  const int b = (int)B;
-  switch ((B + 3) / 4) {
-    case 1: {
-      const int ks = slices(K * planes, Chunk<1>::value);
-      hipLaunchKernelGGL((gemv_direct_kernel<1, Chunk<1>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, planes, y, ks);
-      break;
-    }
-    case 2: {
-      const int ks = slices(K * planes, Chunk<2>::value);
-      hipLaunchKernelGGL((gemv_direct_kernel<2, Chunk<2>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, planes, y, ks);
-      break;
-    }
-    case 3: {
-      const int ks = slices(K * planes, Chunk<3>::value);
-      hipLaunchKernelGGL((gemv_direct_kernel<3, Chunk<3>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, planes, y, ks);
-      break;
-    }
-    default: {
-      const int ks = slices(K * planes, Chunk<4>::value);
-      hipLaunchKernelGGL((gemv_direct_kernel<4, Chunk<4>::value>), grid, dim3(64 * ks), 0, stream, act, b, codes,
-                         scales, N, K, planes, y, ks);
-      break;
-    }
-  }
-  return hipGetLastError();
 }
 
 

@@ -18,8 +18,6 @@ hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uin
 hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream);
 typedef tb_gemv_segment GemvSegment;
 // segments' `planes` must be 1 or 2 (the API layer normalises it)
-hipError_t launch_gemv_direct(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                              int64_t N, int64_t K, int planes, float* y, hipStream_t stream);
 hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream);
 hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                                  const uint16_t* scales, int64_t N, int64_t K, float* y, hipStream_t stream);

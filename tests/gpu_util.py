@@ -105,13 +105,13 @@ def act8_decode(buf, b, k):
     """x[b, k] as the sum of the four sub-rows of an act8 buffer (float64)."""
     buf = np.asarray(buf, dtype=np.uint8)
     g = k // 128
-    vals = buf[:4 * b * k].reshape(b, g, 4, 4, 32).astype(np.int64)  # [b][g][sub][q][byte]
+    vals = buf[:4 * b * k].reshape(b, g, 2, 4, 4, 16).astype(np.int64)  # [b][g][half][sub][q][byte]
     scl = buf[4 * b * k:4 * b * k + b * k // 8].reshape(b, g, 4, 4).astype(np.int64)  # [b][g][sub][block]
     x = np.zeros((b, k))
     for q in range(4):
         for half in range(2):
             kl = 64 * half + 16 * q + np.arange(16)           # K within the group
-            v = e4m3_to_f64(vals[:, :, :, q, 16 * half:16 * half + 16])  # [b][g][sub][16]
+            v = e4m3_to_f64(vals[:, :, half, :, q, :])         # [b][g][sub][16]
             sc = scl[:, :, :, (kl // 32)]                       # [b][g][sub][16]
             fac = np.where(sc == 0xFF, np.nan, np.ldexp(1.0, (sc - 127)))
             part = np.sum(v * fac, axis=2)                      # [b][g][16]

@@ -218,7 +218,7 @@ def test_gemv24_exact_and_dense_equivalence():
 
 # ---------------------------------------------------------------- grouped launches
 
-@pytest.mark.parametrize("b", [1, 3])
+@pytest.mark.parametrize("b", [1, 3, 8])
 def test_grouped_fwht_and_gemv_equal_single_calls(b):
     # shapes with different K-slice counts in one launch (G = 40, 5, 17, 136)
     shapes = [(1920, 5120), (640, 640), (768, 2176), (128, 17408)]
@@ -243,6 +243,35 @@ def test_grouped_fwht_and_gemv_equal_single_calls(b):
         k = x.shape[1]
         xr = oracle.numerics.f64_to_bf16_bits(oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(x)))
         assert_close(y.cpu().numpy(), oracle.matvec.gemv(xr, codes, scales, k), f"grouped segment {c} vs oracle")
+
+
+@pytest.mark.parametrize("batches", [(2, 5, 8, 16), (1, 2, 5, 8)])
+def test_grouped_mixed_batches_equal_single_calls(batches):
+    # segments of different batch sizes in one call: one wide launch sized for
+    # the largest batch (tiles per wave chosen for the whole launch), or, with a
+    # batch-1 segment among them, one launch per segment; either way every
+    # segment equals its single call bit for bit and matches the oracle
+    shapes = [(1920, 5120), (640, 640), (768, 2176), (256, 17408)]
+    say(f"grouped gemv, batches {batches}")
+    segs, singles = [], []
+    for c, ((n, k), b) in enumerate(zip(shapes, batches)):
+        codes = synth.random_code_words(n, k, seed=270 + c)
+        scales = synth.random_scales_f16(n, k, seed=280 + c)
+        x = synth.gaussian_bf16((b, k), seed=290 + c)
+        act = tb.tb_act8_prep(bf16_dev(x))
+        cd, sc = u32_dev(codes), f16_dev(scales)
+        y = torch.empty((b, n), dtype=torch.float32, device=DEV)
+        segs.append((act, cd, sc, b, y))
+        singles.append((x, codes, scales, k))
+    tb.tb_ternary_gemv_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((act, cd, sc, b, y), (x, codes, scales, k)) in enumerate(zip(segs, singles)):
+        y1 = tb.tb_ternary_gemv(act, cd, sc, b)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y1), f"segment {c} (B={b}): grouped differs from the single call"
+        ref = oracle.matvec.gemv(x, codes, scales, k)
+        assert_close(y.cpu().numpy(), ref, f"mixed-batch segment {c} (B={b}) vs oracle")
+        assert np.max(np.abs(y.cpu().numpy() - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
 def test_grouped_output_rotation_f32():
