@@ -232,10 +232,21 @@ def extra_phases(gen, dev, quick):
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ms = time_eager(lambda: tb.tb_ternary_gemm(x, codes, scales, y=y), 3 if quick else 10)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-        gemm[f"{k}x{n}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS, 4)}
-        log(f"  prefill GEMM M={m} K={k} N={n}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
-        del codes, scales, x, y
-    out["prefill_gemm"] = {"workload": "M=2048, (K,N) = (5120,17408) and (17408,5120), bf16 out", "peak_tflops": PEAK_MFMA_TFLOPS, **gemm}
+        # the same product through the split-K entry point (the library picks
+        # the split count; one pass when splitting does not pay)
+        wsb = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+        work = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev)
+        ms_k = time_eager(lambda: tb.tb_ternary_gemm_splitk(x, codes, scales, y=y, workspace=work), 3 if quick else 10)
+        tf_k = 2.0 * m * n * k / (ms_k * 1e-3) / 1e12
+        gemm[f"{k}x{n}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS, 4),
+                            "splitk_ms": round(ms_k, 4), "splitk_splits": wsb // (m * n * 4) if wsb else 1,
+                            "splitk_tflops": round(tf_k, 1), "splitk_frac_of_peak": round(tf_k / PEAK_MFMA_TFLOPS, 4)}
+        log(f"  prefill GEMM M={m} K={k} N={n}: {ms:.3f} ms, {tf:.1f} TFLOP/s; split-K entry "
+            f"({gemm[f'{k}x{n}']['splitk_splits']} splits) {ms_k:.3f} ms, {tf_k:.1f} TFLOP/s")
+        del codes, scales, x, y, work
+    out["prefill_gemm"] = {"workload": "M=2048, (K,N) = (5120,17408) and (17408,5120), bf16 out; tb_ternary_gemm "
+                                       "(one pass) and tb_ternary_gemm_splitk (caller workspace)",
+                           "peak_tflops": PEAK_MFMA_TFLOPS, **gemm}
 
     # the same GEMMs with the output rotated back in the epilogue, against the
     # product followed by a separate rotation launch
