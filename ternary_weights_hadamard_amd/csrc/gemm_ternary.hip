@@ -75,9 +75,10 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
 
   // global -> register staging assignment
   // X: 128 rows x 64 k bf16 = 128 B per row; thread -> row tid/2, 32 k (64 B) at (tid&1)*32
+  // rows past M read row M - 1 instead: an activation row reaches only its own
+  // output row, and those are never stored
   const int xr = tid >> 1, xk = (tid & 1) * 32;
-  const bool xvalid = m0 + xr < M;
-  const uint16_t* xsrc = x + (m0 + xr) * K + gb * kBlock + xk;
+  const uint16_t* xsrc = x + std::min<int64_t>(m0 + xr, M - 1) * K + gb * kBlock + xk;
   // W: 128 rows x 64 k; thread -> row tid/2, the 32 columns of lane group
   // (k0 % 128) / 32 + (tid & 1) of the row's tile: two consecutive words
   const int wr = tid >> 1, wk = (tid & 1) * 32;
@@ -93,14 +94,9 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   uint32_t sw[kWRing];
   auto gload_x = [&](int step) {
     const int64_t k0 = (int64_t)step * KT;
-    if (xvalid) {
-      const u32x4* s = reinterpret_cast<const u32x4*>(xsrc + k0);
+    const u32x4* s = reinterpret_cast<const u32x4*>(xsrc + k0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[i] = s[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xs[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; ++i) xs[i] = s[i];
   };
   // codes and scale of group gi (relative to gb) into ring slot `slot`; groups
   // past the range reload the last one (never used)
