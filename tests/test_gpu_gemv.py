@@ -274,6 +274,41 @@ def test_grouped_mixed_batches_equal_single_calls(batches):
         assert np.max(np.abs(y.cpu().numpy() - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("b", [8, 12])
+def test_grouped_27b_layer_wide_batch(b):
+    # the d_model-input projections of a 27B layer in one launch (QKV 15360,
+    # O 5120, up 17408 rows; K = 5120): enough tiles that the launch takes
+    # the most tiles per wave (8 at batch 8, 4 at batch 12); each single call
+    # takes fewer.  Grouped and single results are equal bit for bit, and 16
+    # sampled tiles of each match the oracle.
+    shapes = [(15360, 5120), (5120, 5120), (17408, 5120)]
+    say(f"grouped 27B layer, B={b}")
+    rng = np.random.default_rng(b)
+    segs, singles = [], []
+    for c, (n, k) in enumerate(shapes):
+        codes = synth.random_code_words(n, k, seed=370 + c)
+        scales = synth.random_scales_f16(n, k, seed=380 + c)
+        x = synth.gaussian_bf16((b, k), seed=390 + c)
+        act = tb.tb_act8_prep(bf16_dev(x))
+        cd, sc = u32_dev(codes), f16_dev(scales)
+        y = torch.empty((b, n), dtype=torch.float32, device=DEV)
+        segs.append((act, cd, sc, b, y))
+        singles.append((x, codes, scales, k))
+    tb.tb_ternary_gemv_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((act, cd, sc, _, y), (x, codes, scales, k)) in enumerate(zip(segs, singles)):
+        y1 = tb.tb_ternary_gemv(act, cd, sc, b)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y1), f"segment {c}: grouped differs from the single call"
+        n = codes.shape[0] * 16
+        tiles = np.sort(rng.choice(n // 16, 16, replace=False))
+        rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+        ref = oracle.matvec.gemv(x, codes[tiles], scales[rows], k)
+        got = y.cpu().numpy().astype(np.float64)[:, rows]
+        assert_close(got, ref, f"27B segment {c} B={b} (16 sampled tiles)")
+        assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
 def test_grouped_output_rotation_f32():
     shapes = [(2, 384), (2, 17408), (2, 1024)]
     xs = [torch.randn(s, dtype=torch.float32, device=DEV) for s in shapes]
