@@ -56,7 +56,7 @@ __device__ __forceinline__ void decode_word_bf16(uint32_t w, uint32_t (&out)[8])
 }
 
 template <bool OUT_BF16, bool ROT>
-__global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __restrict__ x, int64_t M,
+__global__ void __launch_bounds__(256, 2) gemm_ternary_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                            const uint32_t* __restrict__ codes,
                                                            const uint16_t* __restrict__ scales, int64_t N,
                                                            int64_t K, void* __restrict__ y, int splits) {
@@ -85,18 +85,22 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + gb * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
   const uint16_t* ssrc = scales + (n0 + wr) * G + gb;
 
-  // Activations come one K step ahead (from L2: every column tile reads
-  // them).  The codes and scales, read once from HBM, come kWRing groups ahead
-  // through a ring of registers, so their latency is hidden behind several
-  // steps of work rather than one.
-  u32x4 xs[4];
+  // Activations come two K steps ahead through two register sets, one per
+  // step parity (from L2: every column tile reads them; one step of products
+  // is shorter than an L2 round trip).  The codes and scales, read once from
+  // HBM, come kWRing groups ahead through a ring of registers, so their
+  // latency is hidden behind several steps of work rather than one.  Every
+  // prefetch is issued, clamped to the last step or group past the range, so
+  // the wait counts are the same on every path.
+  u32x4 xs[2][4];       // [step parity]
   u32x2 cw[kWRing][2];  // [ring slot][step of the group]
   uint32_t sw[kWRing];
+  const int nsteps = 2 * (int)(ge - gb);
   auto gload_x = [&](int step) {
-    const int64_t k0 = (int64_t)step * KT;
+    const int64_t k0 = (int64_t)std::min(step, nsteps - 1) * KT;
     const u32x4* s = reinterpret_cast<const u32x4*>(xsrc + k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[i] = s[i];
+    for (int i = 0; i < 4; ++i) xs[step & 1][i] = s[i];
   };
   // codes and scale of group gi (relative to gb) into ring slot `slot`; groups
   // past the range reload the last one (never used)
@@ -106,11 +110,12 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
     for (int h = 0; h < 2; ++h) cw[slot][h] = *reinterpret_cast<const u32x2*>(wsrc + g * 128 + 64 * h);
     sw[slot] = ssrc[g];
   };
+  // the step in registers whose parity is `stage` into LDS stage `stage`
   auto lstore = [&](int stage, int slot, int h) {
     // X: 32 bf16 of row xr, as they are
     uint16_t* xd = &lds[stage][0][xr * LDS_ROW + xk];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xd + 8 * i) = xs[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xd + 8 * i) = xs[stage][i];
     // W: decode 32 k of row wr into bf16 2t, pairs (k, k+1)
     uint16_t* wd = &lds[stage][1][wr * LDS_ROW + wk];
 #pragma unroll
@@ -155,16 +160,17 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   // codes are in ring slot `slot`, the next group's in slot `slot` + 1
   const int ngroups = (int)(ge - gb);
   auto group = [&](int gi, int slot) {
-    // first step of the group: stage 0, while step 2 gi + 1 comes in
-    gload_x(2 * gi + 1);
+    // first step of the group from stage 0; step 2 gi + 1 goes to stage 1
+    // and its registers refill with step 2 gi + 3
     mfma_step(0, true);
     lstore(1, slot, 1);
+    gload_x(2 * gi + 3);
     // the group's codes are all in LDS now: refill its slot kWRing groups ahead
     gload_w(gi + kWRing, slot);
     __syncthreads();
-    // second step: stage 1, while the next group's first step comes in
+    // second step from stage 1; step 2 gi + 2 goes to stage 0 and its
+    // registers refill with step 2 gi + 4
     const bool more = gi + 1 < ngroups;
-    if (more) gload_x(2 * gi + 2);
     mfma_step(1, false);
     // fold the group: lane's column n = n0 + wn + 16 j + li
 #pragma unroll
@@ -176,6 +182,7 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
         for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(accg[i][j][r], sc, acc[i][j][r]);
     }
     if (more) lstore(0, (slot + 1) % kWRing, 0);
+    gload_x(2 * gi + 4);
     __syncthreads();
   };
 
@@ -183,6 +190,8 @@ __global__ void __launch_bounds__(256) gemm_ternary_kernel(const uint16_t* __res
   for (int r = 0; r < kWRing; ++r) gload_w(r, r);
   gload_x(0);
   lstore(0, 0, 0);
+  gload_x(1);
+  gload_x(2);
   __syncthreads();
   for (int gi = 0; gi < ngroups; gi += kWRing) {
 #pragma unroll
