@@ -200,11 +200,19 @@ def time_graph(fn, steps, warmup):
     return t0.elapsed_time(t1), wall, g
 
 
-def time_eager(fn, iters):
+def time_eager(fn, iters, warm_s=0.1):
+    """ms per call of fn over `iters` back-to-back calls, after calling it for at
+    least warm_s seconds (the first calls of a process run at lower clocks)."""
+    import time
+
     import torch
 
-    fn()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_s:
+            break
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()

@@ -143,11 +143,15 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
       if (b < B && lane < na)
         as_st[b] = *reinterpret_cast<const u32x4*>(act + (size_t)4 * B * K + ((size_t)b * GA + ab + lane) * 16);
     }
-    // 2. codes, one 8-byte load per lane and group (slots past the slice repeat its last group)
+    // 2. codes, one 8-byte load per lane and group (slots past the slice repeat
+    //    its last group).  Non-temporal: read once, they need not displace the
+    //    activations from the caches (batch 1 on a 27B layer's QKV + O +
+    //    gate/up: 20.1 -> 19.45 us; down 12.6 -> 12.4 us)
     const uint32_t* cp = sg.codes + (size_t)nb * G * 128 + 2 * lane;
     u32x2 cw[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) cw[j] = *reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128);
+    for (int j = 0; j < CH; ++j)
+      cw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128));
     // 3. weight scales: lane (i, q) holds row i's scale of groups gb + 4r + q
     const uint16_t* sp = sg.scales + (size_t)(16 * nb + i) * G;
     uint32_t sr[kScaleRegs];
