@@ -5,7 +5,10 @@
 // 1/sqrt(block size).  One 128-block lives in 16 consecutive lanes of a wave,
 // 8 contiguous elements per lane (one 16-byte bf16 load), and the butterflies
 // run in registers (fwht_lanes.h).  The kernel is HBM bound: 4 bytes per
-// element for bf16 in and out.
+// element for bf16 in and out.  Workgroups are one wave (four blocks): at
+// decode sizes (a few hundred blocks) a launch is latency bound, and spreading
+// it over more CUs took 0.2 us off each launch (3.9 -> 3.7 us for a 27B
+// layer's four input rotations); prefill sizes are unchanged.
 //
 // With the act8 output the rounded bf16 result is re-encoded in the same pass
 // as the dense GEMV's activation operand (act8.h); the same kernel without the
@@ -37,10 +40,10 @@ struct FwhtSegs {
 };
 
 template <bool IN_BF16, int OUT, bool XFORM>
-__global__ void __launch_bounds__(256) fwht128_kernel(FwhtSegs segs) {
+__global__ void __launch_bounds__(64) fwht128_kernel(FwhtSegs segs) {
   const int sub = threadIdx.x & 15;
-  for (int64_t bf = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); bf - (threadIdx.x >> 4) < segs.total;
-       bf += (int64_t)gridDim.x * 16) {
+  for (int64_t bf = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 4); bf - (threadIdx.x >> 4) < segs.total;
+       bf += (int64_t)gridDim.x * 4) {
     // every lane of the wave runs the cross-lane stages; lanes past the end carry zeros
     const bool live = bf < segs.total;
     const void* x = segs.s[0].x;
@@ -117,10 +120,10 @@ __global__ void __launch_bounds__(256) fwht128_kernel(FwhtSegs segs) {
 template <bool XFORM>
 hipError_t launch_segments(const FwhtSegs& segs, int x_dtype, int y_dtype, hipStream_t stream) {
   if (segs.total == 0) return hipSuccess;
-  int64_t groups = (segs.total + 15) / 16;
+  int64_t groups = (segs.total + 3) / 4;
   const int64_t cap = 1 << 20;
   const unsigned grid = (unsigned)(groups < cap ? groups : cap);
-  const dim3 g(grid), blk(256);
+  const dim3 g(grid), blk(64);
   const bool ib = x_dtype == TB_BF16;
   if (y_dtype == TB_ACT8) {
     if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutAct8, XFORM>), g, blk, 0, stream, segs);
