@@ -37,6 +37,28 @@ def test_ragged_block_grids(n, k, seed):
     check_dense_codes(codes, scales, oracle.quant.quantize_dense(w.astype(np.float64)), k, f"{n}x{k}")
 
 
+def test_full_layer_sampled_blocks():
+    # a 27B down projection, 5120 x 17408, with heavy-tailed outlier input
+    # channels (the stack recipe), quantised in one launch as the stack
+    # benchmark does; 16 sampled 128 x 128 blocks checked against the oracle
+    # run on each block alone (blocks are independent)
+    n, k = 5120, 17408
+    w = synth.stack_weights(n, k, seed=21)
+    say(f"quantize full layer {n}x{k}")
+    codes, _, scales = _quant(w)
+    rng = np.random.default_rng(22)
+    picks = list(zip(rng.integers(0, n // 128, 16), rng.integers(0, k // 128, 16)))
+    # an outlier column's block is among them
+    cols = np.nonzero(np.max(np.abs(w), axis=0) > 0.2)[0]
+    picks[0] = (0, int(cols[0]) // 128)
+    for a, b in picks:
+        wb = w[128 * a:128 * (a + 1), 128 * b:128 * (b + 1)]
+        ref = oracle.quant.quantize_dense(wb.astype(np.float64))
+        cb = codes[8 * a:8 * (a + 1), b:b + 1, :].contiguous()
+        sb = scales[128 * a:128 * (a + 1), b:b + 1].contiguous()
+        check_dense_codes(cb, sb, ref, 128, f"block ({a}, {b})")
+
+
 def test_closed_form_blocks():
     w = np.zeros((256, 512), dtype=np.float32)
     w[3, 9] = 4.0                    # spike in block (0,0): lossless, all codes +-1
@@ -108,6 +130,28 @@ def test_24_matches_oracle(n, k, seed):
     assert not bad.any()
     ulp = np.abs(host_u16(scales).astype(np.int64) - ref["scales"].astype(np.int64))
     assert ulp.max() <= 1
+
+
+def test_24_full_layer_sampled_blocks():
+    # the 2:4 shape of the 27B up projection, 17408 x 5120, stack recipe, one
+    # launch; 16 sampled 128 x 128 blocks against the oracle run on each block
+    n, k = 17408, 5120
+    w = synth.stack_weights(n, k, seed=23)
+    say(f"quantize 2:4 full layer {n}x{k}")
+    signs, meta, scales = _quant(w, fmt=tb.TB_FMT_24)
+    rng = np.random.default_rng(24)
+    for a, b in zip(rng.integers(0, n // 128, 16), rng.integers(0, k // 128, 16)):
+        rows = slice(128 * a, 128 * (a + 1))
+        ref = oracle.quant.quantize_24(w[rows, 128 * b:128 * (b + 1)].astype(np.float64))
+        mb = meta[rows, 4 * b:4 * (b + 1)].contiguous()
+        gb = signs[rows, 2 * b:2 * (b + 1)].contiguous()
+        i0, i1, n0, n1 = oracle.quant.unpack_24(host_u32(mb), host_u32(gb), 128)
+        tie = oracle.quant.near_tie_24(ref["wr"], ref["s"])
+        bad = ((i0 != ref["idx0"]) | (i1 != ref["idx1"]) | (n0 != ref["neg0"]) | (n1 != ref["neg1"])) & ~tie
+        say(f"  block ({a}, {b}): {int(tie.sum())} near-tie quads, {int(bad.sum())} mismatches outside them")
+        assert not bad.any()
+        ulp = np.abs(host_u16(scales[rows, b:b + 1].contiguous()).astype(np.int64) - ref["scales"].astype(np.int64))
+        assert ulp.max() <= 1
 
 
 # ---------------------------------------------------------------- error-minimising rule
