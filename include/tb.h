@@ -232,7 +232,9 @@ TB_API tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* 
 /*
  * tb_ternary_gemv over up to TB_MAX_SEGMENTS independent products in one
  * launch (e.g. the projections of a layer, so that small matrices do not leave
- * the GPU idle); each segment is validated and computed as tb_ternary_gemv.
+ * the GPU idle); each segment is validated and computed as tb_ternary_gemv,
+ * and its result is bit for bit that of the single call (how a segment's sum is
+ * split and ordered depends only on its own shape and batch).
  * `segs` is a host array read during the call; no segment's y may overlap any
  * segment's inputs or another y.  count == 0 is a no-op; count outside
  * [0, TB_MAX_SEGMENTS] returns TB_ERR_SHAPE.
