@@ -530,8 +530,9 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
-              "would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (the products would shard "
+              "by output rows, or by K with one all-reduce of the partial outputs); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,7 +1,8 @@
 """Offline quantiser: absmean group scale, ternarisation and packing, dense and
 2:4, in float64.
 
-Definitions followed (readings of the pages are listed in the design doc):
+Definitions followed (where the pages leave a step open, the reading taken is
+stated with the step):
 
 * Group scale: the mean absolute value of the 128 contiguous K-elements of one
   row of one rotated 128x128 block (mhpq.cn/news/1159370 §1.1: take the group's
