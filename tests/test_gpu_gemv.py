@@ -39,7 +39,7 @@ def test_gemv_small_matches_oracle(n, k, b):
 
 
 @pytest.mark.parametrize("n,k", [(5120, 5120), (17408, 5120), (5120, 17408), (15360, 5120)])
-@pytest.mark.parametrize("b", [1, 4, 8])
+@pytest.mark.parametrize("b", [1, 4, 8, 16])
 def test_gemv_full_size_sampled_tiles(n, k, b):
     say(f"gemv full N={n} K={k} B={b}")
     codes, scales, x = _dense_inputs(n, k, b, seed=20 + b)
