@@ -619,7 +619,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8xfp4,f32acc",
         "data": "synthetic",
         "config": {"workload": f"decode GEMV, {args.layers}-layer 27B-shaped stack (d_model 5120, d_ff 17408; fused QKV, O, "
                                f"gate/up, down), batch {args.batch}, FWHT128 in and out, HIP graph",
