@@ -25,8 +25,11 @@ namespace {
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutAct8 = 2 };
 
 // A launch covers up to TB_MAX_SEGMENTS independent arrays (segments); the
-// 128-blocks are numbered across them and each 16-lane group finds the
-// segment of its block.
+// 128-blocks are numbered across them, each segment starting at a multiple
+// of 4, so that the four blocks of a wave always lie in one segment.  The
+// segment is then found per wave (scalar compares and loads of the kernel
+// arguments); a per-lane choice kept all segments' pointers live and spilled
+// them through VGPR lanes.
 struct FwhtSeg {
   const void* x;
   void* y;
@@ -42,22 +45,18 @@ struct FwhtSegs {
 template <bool IN_BF16, int OUT, bool XFORM>
 __global__ void __launch_bounds__(64) fwht128_kernel(FwhtSegs segs) {
   const int sub = threadIdx.x & 15;
-  for (int64_t bf = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 4); bf - (threadIdx.x >> 4) < segs.total;
-       bf += (int64_t)gridDim.x * 4) {
-    // every lane of the wave runs the cross-lane stages; lanes past the end carry zeros
-    const bool live = bf < segs.total;
-    const void* x = segs.s[0].x;
-    void* y = segs.s[0].y;
-    int64_t nblocks = segs.s[0].nblocks, begin = 0;
+  for (int64_t bw = (int64_t)blockIdx.x * 4; bw < segs.total; bw += (int64_t)gridDim.x * 4) {
+    // the wave's segment: the last whose first block is at or before bw
+    int seg = 0;
 #pragma unroll
-    for (int t = 1; t < TB_MAX_SEGMENTS; ++t) {
-      const bool take = t < segs.count && bf >= segs.s[t].begin;
-      x = take ? segs.s[t].x : x;
-      y = take ? segs.s[t].y : y;
-      nblocks = take ? segs.s[t].nblocks : nblocks;
-      begin = take ? segs.s[t].begin : begin;
-    }
-    const int64_t b = bf - begin;  // block inside its segment
+    for (int t = 1; t < TB_MAX_SEGMENTS; ++t) seg += (t < segs.count && bw >= segs.s[t].begin) ? 1 : 0;
+    const void* x = segs.s[seg].x;
+    void* y = segs.s[seg].y;
+    const int64_t nblocks = segs.s[seg].nblocks;
+    const int64_t b = bw - segs.s[seg].begin + (threadIdx.x >> 4);  // block inside its segment
+    // every lane of the wave runs the cross-lane stages; lanes past the
+    // segment's end carry zeros
+    const bool live = b < nblocks;
     const int64_t base = b * kBlock + sub * 8;
     float v[8];
     if constexpr (IN_BF16) {
@@ -160,7 +159,7 @@ hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dt
   for (int c = 0; c < count; ++c) {
     const int64_t nb = segs[c].rows * (segs[c].K / kBlock);
     s.s[c] = FwhtSeg{segs[c].x, segs[c].y, nb, total};
-    total += nb;
+    total += (nb + 3) / 4 * 4;  // the next segment starts on a wave boundary
   }
   s.count = count;
   s.total = total;
