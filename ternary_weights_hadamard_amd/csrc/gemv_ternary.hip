@@ -79,26 +79,20 @@ struct StagedSegs {
   int stage_groups;  // activation groups staged per wave and batch row (two planes)
 };
 
-// the segment of this workgroup, selected field by field (the index is
-// uniform, so these are scalar selects on kernel arguments)
-__device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) {
+// the segment of this workgroup: its index from the workgroup starts, then
+// that one entry's fields (a uniform index, so scalar loads of the kernel
+// arguments; selecting every field across all entries kept them all live
+// and spilled scalar registers)
+template <class Segs>
+__device__ __forceinline__ int segment_index(const Segs& a) {
   const int wg = (int)blockIdx.x;
-  StagedSeg r = a.s[0];
+  int seg = 0;
 #pragma unroll
-  for (int t = 1; t < kMaxSegs; ++t) {
-    const bool take = t < a.count && wg >= a.s[t].wg_begin;
-    r.act = take ? a.s[t].act : r.act;
-    r.codes = take ? a.s[t].codes : r.codes;
-    r.scales = take ? a.s[t].scales : r.scales;
-    r.y = take ? a.s[t].y : r.y;
-    r.N = take ? a.s[t].N : r.N;
-    r.K = take ? a.s[t].K : r.K;
-    r.B = take ? a.s[t].B : r.B;
-    r.ks = take ? a.s[t].ks : r.ks;
-    r.wg_begin = take ? a.s[t].wg_begin : r.wg_begin;
-  }
-  return r;
+  for (int t = 1; t < kMaxSegs; ++t) seg += (t < a.count && wg >= a.s[t].wg_begin) ? 1 : 0;
+  return seg;
 }
+
+__device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) { return a.s[segment_index(a)]; }
 
 // P code planes per segment (1, or 2 with the planes' groups interleaved)
 template <int CH, int BMAX, int P>
@@ -111,13 +105,16 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
   const int waves = (int)(blockDim.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ks = w % KS;
+  // KS and waves are powers of two (waves the largest KS of the launch), so
+  // the slice arithmetic is shifts and masks: a wave starts its loads sooner
+  const int lg = __builtin_ctz((unsigned)KS);
+  const int ks = w & (KS - 1);
   const int i = lane & 15, q = lane >> 4;
-  const int64_t nb = (int64_t)(blockIdx.x - sg.wg_begin) * (waves / KS) + w / KS;
-  const bool live = nb < N / 16;
-  const int GA = (int)(K / kBlock);  // activation groups per row
-  const int G = GA * P;              // code and scale groups per row
-  const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
+  const int64_t nb = (int64_t)(blockIdx.x - sg.wg_begin) * (waves >> lg) + (w >> lg);
+  const bool live = nb < (int64_t)((uint64_t)N >> 4);
+  const int GA = (int)((uint64_t)K >> 7);  // activation groups per row
+  const int G = GA * P;                    // code and scale groups per row
+  const int gb = (G * ks) >> lg, ge = (G * (ks + 1)) >> lg;
   const int n = ge - gb;  // 1 .. CH code groups in this slice
   // activation groups of the slice: code group g multiplies activation group g / P
   const int ab = gb / P, na = (ge - 1) / P - ab + 1;
@@ -243,25 +240,7 @@ struct WideSegs {
   int count;
 };
 
-__device__ __forceinline__ WideSeg pick_wide_segment(const WideSegs& a) {
-  const int wg = (int)blockIdx.x;
-  WideSeg r = a.s[0];
-#pragma unroll
-  for (int t = 1; t < kMaxSegs; ++t) {
-    const bool take = t < a.count && wg >= a.s[t].wg_begin;
-    r.act = take ? a.s[t].act : r.act;
-    r.codes = take ? a.s[t].codes : r.codes;
-    r.scales = take ? a.s[t].scales : r.scales;
-    r.y = take ? a.s[t].y : r.y;
-    r.N = take ? a.s[t].N : r.N;
-    r.K = take ? a.s[t].K : r.K;
-    r.B = take ? a.s[t].B : r.B;
-    r.P = take ? a.s[t].P : r.P;
-    r.ks = take ? a.s[t].ks : r.ks;
-    r.wg_begin = take ? a.s[t].wg_begin : r.wg_begin;
-  }
-  return r;
-}
+__device__ __forceinline__ WideSeg pick_wide_segment(const WideSegs& a) { return a.s[segment_index(a)]; }
 
 template <int NB4, int T, int CH>
 __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs segs) {
@@ -273,14 +252,16 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs seg
   const int waves = (int)(blockDim.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ks = w % KS;
+  // KS and waves are powers of two: shifts and masks, as in the staged kernel
+  const int lg = __builtin_ctz((unsigned)KS);
+  const int ks = w & (KS - 1);
   const int i = lane & 15, q = lane >> 4;
-  const int64_t tiles = N / 16;
-  const int64_t t0 = ((int64_t)(blockIdx.x - sg.wg_begin) * (waves / KS) + w / KS) * T;  // first tile
+  const int64_t tiles = (int64_t)((uint64_t)N >> 4);
+  const int64_t t0 = ((int64_t)(blockIdx.x - sg.wg_begin) * (waves >> lg) + (w >> lg)) * T;  // first tile
   const bool live = t0 < tiles;
-  const int GA = (int)(K / kBlock);  // activation groups per row
-  const int G = GA * P;              // code and scale groups per row
-  const int gb = G * ks / KS, ge = G * (ks + 1) / KS;
+  const int GA = (int)((uint64_t)K >> 7);  // activation groups per row
+  const int G = GA * P;                    // code and scale groups per row
+  const int gb = (G * ks) >> lg, ge = (G * (ks + 1)) >> lg;
 
   float acc[T][NB4];
 #pragma unroll
