@@ -183,8 +183,11 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, q = lane >> 4;
   const int64_t nb = blockIdx.x;
-  const int G = (int)(K / kBlock);
-  const int gb = G * w / KS, ge = G * (w + 1) / KS;
+  const int G = (int)((uint64_t)K >> 7);
+  // KS is a power of two (the launch doubles it): shifts, not divisions, so
+  // that the wave reaches its first load sooner
+  const int lg = __builtin_ctz((unsigned)KS);
+  const int gb = (G * w) >> lg, ge = (G * (w + 1)) >> lg;
   const int n = ge - gb;  // 1 .. CH groups
   unsigned char* st = smem + (size_t)w * stage24_bytes(CH, B);
   unsigned char* st_meta = st;                         // [CH][16 rows][4 words]
