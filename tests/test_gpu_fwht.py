@@ -77,3 +77,39 @@ def test_fwht_empty_batch_is_noop():
     t = torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV)
     tb.tb_fwht128(t)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16"),
+                                      ("bf16", "act8"), ("f32", "act8")])
+def test_grouped_fwht_ragged_segments_equal_single_calls(din, dout):
+    # eight segments of 1-17 blocks: in a grouped launch each segment starts on a
+    # four-block boundary, so the lanes past a segment's end must write nothing
+    shapes = [(1, 128), (1, 256), (3, 128), (1, 640), (7, 128), (3, 384), (1, 1664), (1, 2176)]
+    say(f"grouped fwht {din}->{dout}, blocks {[r * k // 128 for r, k in shapes]}")
+    canary = 64  # bytes after each output
+    xs, ys, outs = [], [], []
+    for c, (rows, k) in enumerate(shapes):
+        if din == "bf16":
+            x = bf16_dev(synth.gaussian_bf16((rows, k), seed=300 + c))
+        else:
+            x = f32_dev(np.random.default_rng(300 + c).standard_normal((rows, k)).astype(np.float32))
+        nbytes = tb.tb_act8_bytes(rows, k) if dout == "act8" else rows * k * (2 if dout == "bf16" else 4)
+        buf = torch.full((nbytes + canary,), 0xA5, dtype=torch.uint8, device=DEV)
+        if dout == "act8":
+            y = buf[:nbytes]
+        else:
+            y = buf[:nbytes].view(torch.bfloat16 if dout == "bf16" else torch.float32).view(rows, k)
+        xs.append(x)
+        ys.append(y)
+        outs.append(buf)
+    tb.tb_fwht128_multi(list(zip(xs, ys)))
+    torch.cuda.synchronize()
+    for c, (x, y, buf) in enumerate(zip(xs, ys, outs)):
+        if dout == "act8":
+            single = tb.tb_fwht128(x, out_dtype=torch.uint8)
+        else:
+            single = tb.tb_fwht128(x, out_dtype=torch.bfloat16 if dout == "bf16" else torch.float32)
+        torch.cuda.synchronize()
+        nbytes = buf.numel() - canary
+        assert torch.equal(buf[:nbytes], single.contiguous().view(-1).view(torch.uint8)), f"segment {c} differs"
+        assert bool((buf[nbytes:] == 0xA5).all()), f"segment {c}: write past its end"
