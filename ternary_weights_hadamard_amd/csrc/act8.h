@@ -103,14 +103,12 @@ __device__ __forceinline__ void act8_encode(const uint32_t (&h)[8], uint32_t (&w
 #pragma unroll
   for (int e = 0; e < 8; ++e) in[e] = ex[e] > 0 && ex[e] < 255 && ex[e] + 10 >= m0;
   act8_level(f, in, m0, word[0], word[1], sc[0], sc[1]);
-  if (m1 != 0) {  // some element lies more than 10 binades below the block's largest
+  // level 1 without a branch, so that it can interleave with level 0: with
+  // m1 == 0 no element is in it (words 0) and its scales are 127 (2^0)
+  bool in1[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) in[e] = ex[e] > 0 && ex[e] + 10 < m0 && ex[e] + 10 >= m1;
-    act8_level(f, in, m1, word[2], word[3], sc[2], sc[3]);
-  } else {
-    word[2][0] = word[2][1] = word[3][0] = word[3][1] = 0u;
-    sc[2] = sc[3] = 127u;
-  }
+  for (int e = 0; e < 8; ++e) in1[e] = ex[e] > 0 && ex[e] + 10 < m0 && ex[e] + 10 >= m1;
+  act8_level(f, in1, m1, word[2], word[3], sc[2], sc[3]);
   if (nonfinite) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
