@@ -92,7 +92,14 @@ __device__ __forceinline__ int segment_index(const Segs& a) {
   return seg;
 }
 
-__device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) { return a.s[segment_index(a)]; }
+// Entry 0 is read alongside the workgroup starts, so that the workgroups of
+// the first segment (all of them in a one-segment launch) do not wait for a
+// second round of scalar loads.
+__device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) {
+  const StagedSeg r0 = a.s[0];
+  const int seg = segment_index(a);
+  return seg == 0 ? r0 : a.s[seg];
+}
 
 // P code planes per segment (1, or 2 with the planes' groups interleaved)
 template <int CH, int BMAX, int P>
@@ -240,7 +247,11 @@ struct WideSegs {
   int count;
 };
 
-__device__ __forceinline__ WideSeg pick_wide_segment(const WideSegs& a) { return a.s[segment_index(a)]; }
+__device__ __forceinline__ WideSeg pick_wide_segment(const WideSegs& a) {
+  const WideSeg r0 = a.s[0];
+  const int seg = segment_index(a);
+  return seg == 0 ? r0 : a.s[seg];
+}
 
 template <int NB4, int T, int CH>
 __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs segs) {
