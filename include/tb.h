@@ -70,7 +70,8 @@ typedef enum {
   TB_ERR_FORMAT = 5,      /* unknown format, or a plane given/missing for it    */
   TB_ERR_LAUNCH = 6,      /* the HIP runtime refused the launch                 */
   TB_ERR_UNSUPPORTED = 7, /* valid request this build does not implement        */
-  TB_ERR_ALIAS = 8        /* input and output overlap where that is not allowed */
+  TB_ERR_ALIAS = 8,       /* input and output overlap where that is not allowed */
+  TB_ERR_WORKSPACE = 9    /* workspace missing or smaller than the call needs   */
 } tb_status;
 
 typedef enum { TB_F32 = 0, TB_BF16 = 1, TB_ACT8 = 2 } tb_dtype;
@@ -85,11 +86,14 @@ typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_
 #define TB_EFLAG_SCALE_OVF 2u /* a group scale rounded to fp16 infinity (absmean >= 65520)      */
 
 /*
- * TB_ACT8 is the activation operand of tb_ternary_gemv, for B rows of K
- * activations, in one buffer of tb_act8_bytes(B, K) = 4*B*K + B*K/8 bytes.
- * Every bf16 activation is stored exactly as the sum of four e4m3 values on
- * four sub-rows (two magnitude levels x high and low significand halves) with
- * one E8M0 scale per 32 K-elements and sub-row:
+ * TB_ACT8 is the activation operand of the dense GEMV's matrix instruction,
+ * for B rows of K activations, in one buffer of tb_act8_bytes(B, K) =
+ * 4*B*K + B*K/8 bytes.  tb_ternary_gemv encodes bf16 activations into it
+ * itself (in a caller workspace), or takes it already encoded.  An activation
+ * is written as the sum of up to four e4m3 values on four sub-rows (two
+ * magnitude levels x high and low significand halves) with one E8M0 scale per
+ * 32 K-elements and sub-row; the sum is exact for every element the two levels
+ * cover (see below), the rest are read as zero:
  *   values  uint8 [B][K/128][2 halves h][4 sub-rows][4 q][16]: the 16 bytes
  *           of (h, q) are K 128g + 64h + 16q + (0..15);
  *   scales  uint8 at byte offset 4*B*K: [B][K/128][4 sub-rows][4 blocks],
@@ -202,8 +206,8 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_
  * with their groups interleaved, codes [N/16][2K/128][128] and scales
  * [N][2K/128], where group 2g + p is plane p's group g.
  *   W       fp32 [N][K]
- *   codes   dense: [N][K/16] code words; two-plane: [N][K/8]; 2:4: the sign
- *           plane [N][K/64]
+ *   codes   dense: [N/16][K/128][128] code words (the tile layout above);
+ *           two-plane: [N/16][2K/128][128]; 2:4: the sign plane [N][K/64]
  *   meta    2:4: [N][K/32]; must be NULL for the dense formats (else TB_ERR_FORMAT)
  *   scales  fp16 bits [N][K/128]; two-plane: [N][2K/128]
  *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
@@ -217,22 +221,37 @@ TB_API tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt,
  * Decode GEMV with dense ternary weights (mhpq.cn/news/1159370 §4.2: read the
  * weight bits, expand the signs, apply the scale, multiply):
  *   y[b][n] = sum_g fp16(scales[n][g]) * sum_{k in g} t[n][k] * x[b][k]
- *   act     the already rotated activations x [B][K] in the TB_ACT8 operand
- *           format (tb_act8_prep, or tb_fwht128 with y_dtype TB_ACT8)
+ *   x, x_dtype  the already rotated activations x' [B][K], either
+ *           TB_BF16: bf16 bits [B][K].  The call first encodes them as the
+ *             TB_ACT8 operand into `workspace` (one launch), then runs the
+ *             product (a second launch on the same stream);
+ *           TB_ACT8: the operand already encoded, tb_act8_bytes(B, K) bytes
+ *             for exactly these B rows (its scales start at byte 4*B*K, so
+ *             the operand of more rows cannot be passed with a smaller B);
+ *             made by tb_act8_prep or by tb_fwht128 with y_dtype TB_ACT8.
+ *             One launch; `workspace` is not used and may be NULL.
+ *           Other dtypes return TB_ERR_DTYPE.
  *   B       0 <= B <= TB_GEMV_MAX_BATCH (else TB_ERR_SHAPE)
  *   codes, scales  dense format, [N/16][K/128][128] and [N][K/128]
  *   y       fp32 [B][N]; must not overlap the inputs (TB_ERR_ALIAS)
+ *   workspace, workspace_bytes  for TB_BF16: caller-owned device memory of at
+ *           least tb_act8_bytes(B, K) bytes (else TB_ERR_WORKSPACE), 16-byte
+ *           aligned, overlapping no other argument (TB_ERR_ALIAS); it holds
+ *           the encoded operand when the call completes.  Calls sharing a
+ *           workspace must be ordered on one stream.
  * The products are exact; each 32-element block's products are summed
  * exactly inside the matrix instruction, blocks, sub-rows and groups are
- * accumulated in fp32.
+ * accumulated in fp32.  Activations more than 20 binades below their
+ * 32-block's largest, and bf16 subnormals, are read as zero (TB_ACT8 above).
  */
-TB_API tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                          int64_t N, int64_t K, float* y, void* stream);
+TB_API tb_status tb_ternary_gemv(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                          int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * tb_ternary_gemv over up to TB_MAX_SEGMENTS independent products in one
  * launch (e.g. the projections of a layer, so that small matrices do not leave
- * the GPU idle); each segment is validated and computed as tb_ternary_gemv,
+ * the GPU idle), each given its TB_ACT8 operand (`act`, as tb_ternary_gemv
+ * with x_dtype TB_ACT8); each segment is validated and computed as tb_ternary_gemv,
  * and its result is bit for bit that of the single call (how a segment's sum is
  * split and ordered depends only on its own shape and batch).
  * `segs` is a host array read during the call; no segment's y may overlap any
@@ -247,11 +266,13 @@ TB_API tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, v
  *   y[b][n] = sum_g sum_p fp16(s_p[n][g]) * sum_{k in g} t_p[n][k] * x[b][k]
  *   codes   [N/16][2K/128][128], scales [N][2K/128]: group 2g + p is plane
  *           p's group g (as tb_quantize_pack writes them)
- *   act, B, y and the error rules as tb_ternary_gemv; K is the activation
- *   length.  Both planes' products are exact and accumulated in fp32.
+ *   x, x_dtype, B, y, workspace and the error rules as tb_ternary_gemv; K is
+ *   the activation length.  Both planes' products are exact and accumulated
+ *   in fp32.
  */
-TB_API tb_status tb_ternary_gemv_resid(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                                int64_t N, int64_t K, float* y, void* stream);
+TB_API tb_status tb_ternary_gemv_resid(const void* x, int x_dtype, int64_t B, const uint32_t* codes,
+                                const uint16_t* scales, int64_t N, int64_t K, float* y, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of the TB_ACT8 activation operand for B rows of K activations:

@@ -176,8 +176,9 @@ def mse_threshold(a):
 
 def mse_objective_gap(a):
     """Relative gap between the best and the second-best objective S^2 / j over
-    distinct thresholds of each group (0 when the group has one distinct
-    magnitude)."""
+    distinct thresholds of each group.  A group with a single candidate (one
+    distinct magnitude) or an all-zero group gets inf: no other threshold can
+    come close, so float rounding cannot change its choice."""
     a = np.asarray(a, dtype=np.float64)
     d = -np.sort(-a, axis=-1)
     n = d.shape[-1]

@@ -66,6 +66,34 @@ tb_status check_gemv(const tb_gemv_segment& g) {
   return TB_OK;
 }
 
+// One dense GEMV call with its activations as bf16 x' (encoded as the act8
+// operand into `workspace`, then the product: two launches) or as the act8
+// operand itself (one launch; the workspace is not used).
+tb_status gemv_call(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
+                    int64_t K, float* y, void* workspace, size_t workspace_bytes, int64_t planes, hipStream_t stream) {
+  if (x_dtype != TB_BF16 && x_dtype != TB_ACT8) return TB_ERR_DTYPE;
+  const bool encode = x_dtype == TB_BF16;
+  const tb_gemv_segment g{static_cast<const uint8_t*>(encode ? workspace : x), B, codes, scales, N, K, y, planes};
+  if (encode) {
+    if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+    if (B == 0) return TB_OK;
+    if (!x) return TB_ERR_NULL;
+    if (!aligned16(x)) return TB_ERR_ALIGN;
+    if (!workspace || workspace_bytes < act8_bytes((size_t)B * (size_t)K)) return TB_ERR_WORKSPACE;
+  }
+  const tb_status st = check_gemv(g);
+  if (st != TB_OK || B == 0) return st;
+  if (encode) {
+    const size_t xb = (size_t)B * (size_t)K * 2, ab = act8_bytes((size_t)B * (size_t)K);
+    if (overlap(y, (size_t)B * (size_t)N * 4, x, xb) || overlap(workspace, ab, x, xb) ||
+        overlap(workspace, ab, codes, gemv_code_bytes(g)) || overlap(workspace, ab, scales, gemv_scale_bytes(g)))
+      return TB_ERR_ALIAS;
+    const hipError_t e = tb::launch_act8_prep(static_cast<const uint16_t*>(x), B, K, static_cast<uint8_t*>(workspace),
+                                              stream);
+    if (e != hipSuccess) return TB_ERR_LAUNCH;
+  }
+  return launched(tb::launch_gemv_multi(&g, 1, stream));
+}
 
 // arguments of the GEMM entry points that take a workspace (NULL allowed)
 tb_status check_gemm_ws(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
@@ -101,11 +129,12 @@ const char* tb_status_string(int status) {
     case TB_ERR_LAUNCH: return "TB_ERR_LAUNCH: the HIP runtime refused the launch";
     case TB_ERR_UNSUPPORTED: return "TB_ERR_UNSUPPORTED: not implemented";
     case TB_ERR_ALIAS: return "TB_ERR_ALIAS: output overlaps an input";
+    case TB_ERR_WORKSPACE: return "TB_ERR_WORKSPACE: the workspace is missing or smaller than the call needs";
     default: return "unknown tb_status";
   }
 }
 
-int tb_version(void) { return 102; }
+int tb_version(void) { return 200; }
 
 size_t tb_act8_bytes(int64_t B, int64_t K) {
   if (B < 0 || K <= 0 || K % kGroup) return 0;
@@ -183,20 +212,15 @@ tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, vo
   return launched(tb::launch_act8_prep(x, B, K, act, as_stream(stream)));
 }
 
-tb_status tb_ternary_gemv(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
-                          int64_t K, float* y, void* stream) {
-  const tb_gemv_segment g{act, B, codes, scales, N, K, y, 1};
-  const tb_status st = check_gemv(g);
-  if (st != TB_OK || B == 0) return st;
-  return launched(tb::launch_gemv_multi(&g, 1, as_stream(stream)));
+tb_status tb_ternary_gemv(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                          int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemv_call(x, x_dtype, B, codes, scales, N, K, y, workspace, workspace_bytes, 1, as_stream(stream));
 }
 
-tb_status tb_ternary_gemv_resid(const uint8_t* act, int64_t B, const uint32_t* codes, const uint16_t* scales,
-                                int64_t N, int64_t K, float* y, void* stream) {
-  const tb_gemv_segment g{act, B, codes, scales, N, K, y, 2};
-  const tb_status st = check_gemv(g);
-  if (st != TB_OK || B == 0) return st;
-  return launched(tb::launch_gemv_multi(&g, 1, as_stream(stream)));
+tb_status tb_ternary_gemv_resid(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                                int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return gemv_call(x, x_dtype, B, codes, scales, N, K, y, workspace, workspace_bytes, 2, as_stream(stream));
 }
 
 tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* stream) {

@@ -7,7 +7,7 @@ a call fails, these functions raise.
 
 Dtypes on the Python side (bit patterns are what matter):
   activations x      torch.bfloat16 (or int16/uint16 bit views)  [rows, K]
-  act8 operand       torch.uint8, flat, tb_act8_bytes(B, K) bytes
+  act8 operand       torch.uint8, flat, exactly tb_act8_bytes(B, K) bytes
   weights W          torch.float32 [N, K]
   codes              torch.int32 (uint32 bit patterns): dense [N/16, K/128, 128],
                      2:4 sign plane [N, K/64]
@@ -53,8 +53,8 @@ SIGNATURES = {
     "tb_fwht128_multi": (_int, [ctypes.POINTER(FwhtSegment), _int, _int, _int, _vp]),
     "tb_ternary_gemv_multi": (_int, [ctypes.POINTER(GemvSegment), _int, _vp]),
     "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
-    "tb_ternary_gemv": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
-    "tb_ternary_gemv_resid": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "tb_ternary_gemv": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tb_ternary_gemv_resid": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "tb_act8_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "tb_act8_prep": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
@@ -193,32 +193,56 @@ def tb_act8_prep(x, act=None, stream=None):
     return act
 
 
-def tb_ternary_gemv(act, codes, scales, batch, y=None, stream=None):
-    """y[b, n] (fp32) = sum_g scale[n, g] * sum_k t[n, k] x[b, k] for `batch`
-    rows of activations given as the act8 operand `act`."""
-    _dev(act, codes, scales)
-    n, g = scales.shape
-    k = g * 128
+def _act8_operand(act, batch, k, where):
+    """Check that `act` is the act8 operand of exactly `batch` rows of length k
+    (its scale part starts at byte 4 * batch * k, so the size must match)."""
+    if batch is None:
+        raise ValueError(f"{where}: an act8 operand needs its batch")
+    if batch == 0:
+        return  # a no-op call reads nothing
+    if act.dtype != torch.uint8 or act.numel() != tb_act8_bytes(batch, k):
+        raise ValueError(f"{where}: act8 operand of {batch} rows x {k} must be a uint8 buffer of "
+                         f"{tb_act8_bytes(batch, k)} bytes (got {act.dtype}, {act.numel()} elements)")
+
+
+def _gemv(fn, where, x, codes, scales, k, batch, y, workspace, stream):
+    _dev(x, codes, scales)
+    n = scales.shape[0]
+    if x.dtype == torch.uint8:
+        _act8_operand(x, batch, k, where)
+        b, dt, wbytes = int(batch), TB_ACT8, 0
+    else:
+        if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or x.dim() != 2 or x.shape[1] != k:
+            raise ValueError(f"{where}: x must be bf16 [B, {k}] (got {x.dtype} {tuple(x.shape)})")
+        b, dt = x.shape[0], TB_BF16
+        if batch is not None and int(batch) != b:
+            raise ValueError(f"{where}: batch {batch} but x has {b} rows")
+        if workspace is None:
+            workspace = torch.empty(max(tb_act8_bytes(b, k), 16), dtype=torch.uint8, device=x.device)
+        wbytes = workspace.numel() * workspace.element_size()
     if y is None:
-        y = torch.empty((batch, n), dtype=torch.float32, device=act.device)
-    _dev(y)
-    _check(lib().tb_ternary_gemv(_p(act), int(batch), _p(codes), _p(scales), n, k, _p(y), _stream(stream)),
-           "tb_ternary_gemv")
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _dev(y, workspace)
+    _check(fn(_p(x), dt, b, _p(codes), _p(scales), n, k, _p(y), _p(workspace) if dt == TB_BF16 else None,
+              wbytes, _stream(stream)), where)
     return y
 
 
-def tb_ternary_gemv_resid(act, codes, scales, batch, y=None, stream=None):
+def tb_ternary_gemv(x, codes, scales, batch=None, y=None, workspace=None, stream=None):
+    """y[b, n] (fp32) = sum_g scale[n, g] * sum_k t[n, k] x[b, k].  x is either
+    the rotated activations as bf16 [B, K] (encoded into `workspace`, a uint8
+    device tensor of at least tb_act8_bytes(B, K) bytes, allocated here when
+    None) or their act8 operand (uint8, exactly tb_act8_bytes(batch, K) bytes,
+    `batch` given)."""
+    return _gemv(lib().tb_ternary_gemv, "tb_ternary_gemv", x, codes, scales, scales.shape[1] * 128, batch, y,
+                 workspace, stream)
+
+
+def tb_ternary_gemv_resid(x, codes, scales, batch=None, y=None, workspace=None, stream=None):
     """tb_ternary_gemv over two-plane weights (TB_FMT_DENSE_RESID): codes
     [N/16, 2K/128, 128], scales [N, 2K/128], groups of the planes interleaved."""
-    _dev(act, codes, scales)
-    n, g2 = scales.shape
-    k = g2 // 2 * 128
-    if y is None:
-        y = torch.empty((batch, n), dtype=torch.float32, device=act.device)
-    _dev(y)
-    _check(lib().tb_ternary_gemv_resid(_p(act), int(batch), _p(codes), _p(scales), n, k, _p(y), _stream(stream)),
-           "tb_ternary_gemv_resid")
-    return y
+    return _gemv(lib().tb_ternary_gemv_resid, "tb_ternary_gemv_resid", x, codes, scales, scales.shape[1] // 2 * 128,
+                 batch, y, workspace, stream)
 
 
 def tb_ternary_gemv_multi(segments, stream=None):
@@ -232,8 +256,10 @@ def tb_ternary_gemv_multi(segments, stream=None):
         planes = int(seg[5]) if len(seg) > 5 else 1
         _dev(act, codes, scales, y)
         n, g = scales.shape
-        arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n,
-                             g // max(planes, 1) * 128, y.data_ptr(), planes)
+        k = g // max(planes, 1) * 128
+        _act8_operand(act, int(batch), k, "tb_ternary_gemv_multi")
+        arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n, k, y.data_ptr(),
+                             planes)
     _check(lib().tb_ternary_gemv_multi(arr, len(segments), _stream(stream)), "tb_ternary_gemv_multi")
 
 

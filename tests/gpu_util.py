@@ -74,11 +74,15 @@ def assert_close(got, ref, what, tol=FLOAT_TOL, out_bf16=False):
 
 
 def check_dense_codes(codes_gpu, scales_gpu, ref, k, what):
-    """Codes bit-exact except near-threshold elements; fp16 scales equal or 1 ulp."""
+    """Codes bit-exact except near-threshold elements, where the code must be 0
+    or sign(W'); fp16 scales equal or 1 ulp."""
     t_gpu = oracle.quant.unpack_dense(host_u32(codes_gpu), k)  # raises on an invalid field
     near = oracle.quant.near_threshold(ref["wr"], ref["s"])
     mism = t_gpu != ref["t"]
     outside = mism & ~near
+    # at the threshold the two valid answers are 0 and sign(W'): never the opposite sign
+    wrong_side = mism & near & (t_gpu != 0) & (t_gpu != np.sign(ref["wr"]))
+    assert not wrong_side.any(), f"{what}: {int(wrong_side.sum())} near-threshold codes of the wrong sign"
     sg = host_u16(scales_gpu).astype(np.int64)
     sr = ref["scales"].astype(np.int64)
     ulp = np.abs(sg - sr)
@@ -136,3 +140,36 @@ def act8_kept(x_bits):
     keep = keep | (e == 255)
     out[~keep.reshape(b, k)] = 0
     return out
+
+
+def check_24_planes(meta_gpu, signs_gpu, scales_gpu, ref, k, what):
+    """2:4 planes against the oracle (oracle.quant.quantize_24 output `ref`).
+    Outside near-tie quads (oracle.quant.near_tie_24) the kept pair and both
+    signs are bit-exact.  In a near-tie quad the GPU may keep another pair,
+    but each kept magnitude must be at least the quad's second largest (within
+    1e-5 relative), and each kept element's sign must be that of W' wherever
+    |W'| > 1e-5 s.  fp16 scales equal or 1 ulp.  Returns (near-tie quads,
+    near-tie quads where the GPU differs)."""
+    i0, i1, n0, n1 = oracle.quant.unpack_24(host_u32(meta_gpu), host_u32(signs_gpu), k)
+    wr = ref["wr"]
+    n = wr.shape[0]
+    quads = wr.reshape(n, k // 4, 4)
+    mag = np.abs(quads)
+    second = np.sort(mag, axis=2)[:, :, 2]
+    tie = oracle.quant.near_tie_24(wr, ref["s"])
+    differ = (i0 != ref["idx0"]) | (i1 != ref["idx1"]) | (n0 != ref["neg0"]) | (n1 != ref["neg1"])
+    outside = differ & ~tie
+    pick = lambda arr, idx: np.take_along_axis(arr, idx[:, :, None], axis=2)[:, :, 0]
+    w0, w1 = pick(quads, i0), pick(quads, i1)
+    top2 = (np.abs(w0) >= second * (1 - 1e-5)) & (np.abs(w1) >= second * (1 - 1e-5))
+    sq = np.repeat(ref["s"], 32, axis=1)
+    sign0 = (np.abs(w0) <= 1e-5 * sq) | (n0 == (w0 < 0))
+    sign1 = (np.abs(w1) <= 1e-5 * sq) | (n1 == (w1 < 0))
+    valid = top2 & sign0 & sign1
+    ulp = np.abs(host_u16(scales_gpu).astype(np.int64) - ref["scales"].astype(np.int64))
+    say(f"  {what}: {int(tie.sum())} near-tie quads, {int((differ & tie).sum())} of them differ; "
+        f"{int(outside.sum())} mismatches outside them; scale 1-ulp diffs {int((ulp == 1).sum())}")
+    assert not outside.any(), f"{what}: {int(outside.sum())} 2:4 mismatches outside the near-tie quads"
+    assert valid[tie].all(), f"{what}: {int((~valid & tie).sum())} near-tie quads with an invalid pick"
+    assert ulp.max(initial=0) <= 1, f"{what}: scale differs by {ulp.max()} ulp"
+    return int(tie.sum()), int((differ & tie).sum())

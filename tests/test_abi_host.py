@@ -39,8 +39,9 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings_and_version():
     L = tb.lib()
     assert L.tb_version() >= 100
-    for code in range(9):
+    for code in range(10):
         assert L.tb_status_string(code)
+    assert b"WORKSPACE" in L.tb_status_string(9)
     assert b"unknown" in L.tb_status_string(99)
 
 
@@ -110,17 +111,24 @@ def test_quantize_validation():
     assert L.tb_quantize_pack(_v(A), 128, 128, 0, _v(A + 1024), None, _v(C), None, s) == 8  # codes inside W
 
 
+ACT8, BF16 = tb.TB_ACT8, tb.TB_BF16
+
+
 def test_gemv_resid_validation():
     L = tb.lib()
     s = None
-    assert L.tb_ternary_gemv_resid(_v(A), 17, _v(B), _v(C), 128, 128, _v(D), s) == 2
-    assert L.tb_ternary_gemv_resid(_v(A), 1, None, _v(C), 128, 128, _v(D), s) == 1
-    assert L.tb_ternary_gemv_resid(_v(A), 1, _v(B), _v(C), 128, 128, _v(MIS), s) == 3
-    assert L.tb_ternary_gemv_resid(None, 0, None, None, 128, 128, None, s) == 0
+    R = L.tb_ternary_gemv_resid
+    assert R(_v(A), ACT8, 17, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 2
+    assert R(_v(A), ACT8, 1, None, _v(C), 128, 128, _v(D), None, 0, s) == 1
+    assert R(_v(A), ACT8, 1, _v(B), _v(C), 128, 128, _v(MIS), None, 0, s) == 3
+    assert R(None, ACT8, 0, None, None, 128, 128, None, None, 0, s) == 0
     # y right after one plane's codes (4 KB) overlaps the second plane; after
     # one plane's scales (256 B) overlaps the second plane's scales
-    assert L.tb_ternary_gemv_resid(_v(A), 1, _v(B), _v(C), 128, 128, _v(B + 4096), s) == 8
-    assert L.tb_ternary_gemv_resid(_v(A), 1, _v(B), _v(C), 128, 128, _v(C + 256), s) == 8
+    assert R(_v(A), ACT8, 1, _v(B), _v(C), 128, 128, _v(B + 4096), None, 0, s) == 8
+    assert R(_v(A), ACT8, 1, _v(B), _v(C), 128, 128, _v(C + 256), None, 0, s) == 8
+    # bf16 activations need a workspace of the act8 size
+    assert R(_v(A), BF16, 1, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 9
+    assert R(_v(A), BF16, 1, _v(B), _v(C), 128, 128, _v(D), _v(0x50000), 527, s) == 9
     Gs = tb.GemvSegment
     bad_planes = (Gs * 1)(Gs(A, 1, B, C, 128, 128, D, 3))
     assert L.tb_ternary_gemv_multi(bad_planes, 1, s) == 5
@@ -133,14 +141,32 @@ def test_gemv_resid_validation():
 def test_gemv_validation():
     L = tb.lib()
     s = None
-    assert L.tb_ternary_gemv(_v(A), 17, _v(B), _v(C), 128, 128, _v(D), s) == 2   # B > 16
-    assert L.tb_ternary_gemv(_v(A), -1, _v(B), _v(C), 128, 128, _v(D), s) == 2
-    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 100, 128, _v(D), s) == 2
-    assert L.tb_ternary_gemv(_v(A), 1, None, _v(C), 128, 128, _v(D), s) == 1
-    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(MIS), s) == 3
-    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(B), s) == 8     # y over codes
-    assert L.tb_ternary_gemv(_v(A), 1, _v(B), _v(C), 128, 128, _v(A + 512), s) == 8  # y over act8 (528 bytes)
-    assert L.tb_ternary_gemv(None, 0, None, None, 128, 128, None, s) == 0         # empty batch
+    G = L.tb_ternary_gemv
+    # the pre-encoded act8 operand
+    assert G(_v(A), ACT8, 17, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 2   # B > 16
+    assert G(_v(A), ACT8, -1, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 2
+    assert G(_v(A), ACT8, 1, _v(B), _v(C), 100, 128, _v(D), None, 0, s) == 2
+    assert G(_v(A), ACT8, 1, None, _v(C), 128, 128, _v(D), None, 0, s) == 1
+    assert G(_v(A), ACT8, 1, _v(B), _v(C), 128, 128, _v(MIS), None, 0, s) == 3
+    assert G(_v(A), ACT8, 1, _v(B), _v(C), 128, 128, _v(B), None, 0, s) == 8     # y over codes
+    assert G(_v(A), ACT8, 1, _v(B), _v(C), 128, 128, _v(A + 512), None, 0, s) == 8  # y over act8 (528 bytes)
+    assert G(None, ACT8, 0, None, None, 128, 128, None, None, 0, s) == 0         # empty batch
+    # dtypes: bf16 x' or the act8 operand only
+    assert G(_v(A), tb.TB_F32, 1, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 4
+    assert G(_v(A), 7, 1, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 4
+    # bf16 x': the workspace must hold tb_act8_bytes(B, K) (528 bytes per row of 128)
+    W = 0x50000
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(D), None, 0, s) == 9     # no workspace
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(D), _v(W), 1055, s) == 9  # one byte short
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(D), _v(W + 8), 1056, s) == 3  # misaligned workspace
+    assert G(_v(MIS), BF16, 2, _v(B), _v(C), 128, 128, _v(D), _v(W), 1056, s) == 3
+    assert G(None, BF16, 2, _v(B), _v(C), 128, 128, _v(D), _v(W), 1056, s) == 1
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 200, _v(D), _v(W), 1056, s) == 2
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(A + 256), _v(W), 1056, s) == 8   # y over x (512 B)
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(D), _v(A + 256), 1056, s) == 8   # workspace over x
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(D), _v(C), 1056, s) == 8         # workspace over scales
+    assert G(_v(A), BF16, 2, _v(B), _v(C), 128, 128, _v(W + 1024), _v(W), 1056, s) == 8  # y over workspace
+    assert G(None, BF16, 0, None, None, 128, 128, None, None, 0, s) == 0
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), None, _v(C), 128, 128, _v(D), s) == 1
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), _v(C), _v(D), 128, 384, _v(MIS), s) == 3
     assert L.tb_ternary24_gemv(_v(A), 20, _v(B), _v(C), _v(D), 128, 384, _v(A), s) == 2
@@ -225,3 +251,16 @@ def test_binding_raises_typed_error_on_cpu_tensors():
 
     with pytest.raises(ValueError):
         tb.tb_fwht128(torch.zeros(1, 128, dtype=torch.bfloat16))
+
+
+def test_binding_checks_the_act8_operand_size():
+    import torch
+
+    ok = torch.zeros(tb.tb_act8_bytes(3, 256), dtype=torch.uint8)
+    tb._act8_operand(ok, 3, 256, "t")
+    tb._act8_operand(ok, 0, 256, "t")  # an empty batch reads nothing
+    for bad, batch in ((ok, 2), (ok[:-1], 3), (ok.view(torch.int32), 3), (torch.zeros(0, dtype=torch.uint8), 1)):
+        with pytest.raises(ValueError):
+            tb._act8_operand(bad, batch, 256, "t")
+    with pytest.raises(ValueError):
+        tb._act8_operand(ok, None, 256, "t")

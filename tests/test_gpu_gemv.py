@@ -51,6 +51,40 @@ def test_gemv_full_size_sampled_tiles(n, k, b):
     assert np.max(np.abs(y[:, rows] - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("n,k,b", [(128, 128, 1), (384, 2176, 3), (1024, 5120, 16), (512, 17408, 2), (256, 1152, 7)])
+def test_gemv_bf16_entry_matches_oracle_and_the_act8_route(n, k, b):
+    # the rotated activations as bf16: the call encodes them into the caller's
+    # workspace and multiplies; the result is the act8 route's bit for bit
+    say(f"gemv bf16 entry N={n} K={k} B={b}")
+    codes, scales, x = _dense_inputs(n, k, b, seed=300 + n + b)
+    xd, cd, sc = bf16_dev(x), u32_dev(codes), f16_dev(scales)
+    ws = torch.full((tb.tb_act8_bytes(b, k) + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    y = tb.tb_ternary_gemv(xd, cd, sc, workspace=ws[:tb.tb_act8_bytes(b, k)])
+    act = tb.tb_act8_prep(xd)
+    y_act = tb.tb_ternary_gemv(act, cd, sc, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_act), "bf16 entry differs from the act8 route"
+    assert torch.equal(ws[:act.numel()], act), "workspace does not hold the encoded operand"
+    assert torch.all(ws[act.numel():] == 0x5A), "encoding wrote past the workspace it needs"
+    ref = oracle.matvec.gemv(x, codes, scales, k)
+    got = y.cpu().numpy().astype(np.float64)
+    assert_close(got, ref, f"gemv bf16 entry {n}x{k} B={b}")
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_gemv_resid_bf16_entry_equals_the_act8_route():
+    n, k, b = 768, 2176, 4
+    codes = synth.random_code_words(n, 2 * k, seed=321)
+    scales = synth.random_scales_f16(n, 2 * k, seed=322)
+    x = synth.gaussian_bf16((b, k), seed=323)
+    xd, cd, sc = bf16_dev(x), u32_dev(codes), f16_dev(scales)
+    y = tb.tb_ternary_gemv_resid(xd, cd, sc)
+    y_act = tb.tb_ternary_gemv_resid(tb.tb_act8_prep(xd), cd, sc, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_act)
+    assert_close(y.cpu().numpy(), oracle.matvec.gemv_residual(x, codes, scales, k), "two-plane bf16 entry")
+
+
 @pytest.mark.parametrize("b", [1, 3, 16])
 def test_gemv_exact_small_integers(b):
     # integer activations and power-of-two scales: the exact result is an fp32 value
@@ -146,6 +180,9 @@ def test_gemv_wide_range_activations_exact_on_kept_values():
     scales = synth.random_scales_f16(n, k, seed=42)
     x = _wide_range_bf16(b, k, seed=43, span=40)
     y = _gemv(x, codes, scales)
+    # the product of the activations as given, at the float bar
+    assert_close(y, oracle.matvec.gemv(x, codes, scales, k), "gemv wide-range activations")
+    # and, tighter, the exact product of what the operand format represents
     ref = oracle.matvec.gemv(act8_kept(x), codes, scales, k)
     assert_close(y, ref, "gemv wide-range activations (oracle on kept values)")
     assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))

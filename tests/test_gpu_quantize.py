@@ -6,7 +6,7 @@ import scipy.linalg
 import torch
 
 import oracle
-from gpu_util import DEV, check_dense_codes, f32_dev, host_u16, host_u32, say
+from gpu_util import DEV, check_24_planes, check_dense_codes, f32_dev, host_u16, host_u32, say
 from ternary_weights_hadamard_amd import synth, tb
 
 pytestmark = pytest.mark.gpu
@@ -123,13 +123,7 @@ def test_24_matches_oracle(n, k, seed):
     say(f"quantize 2:4 {n}x{k}")
     signs, meta, scales = _quant(w, fmt=tb.TB_FMT_24)
     ref = oracle.quant.quantize_24(w.astype(np.float64))
-    i0, i1, n0, n1 = oracle.quant.unpack_24(host_u32(meta), host_u32(signs), k)
-    tie = oracle.quant.near_tie_24(ref["wr"], ref["s"])
-    bad = ((i0 != ref["idx0"]) | (i1 != ref["idx1"]) | (n0 != ref["neg0"]) | (n1 != ref["neg1"])) & ~tie
-    say(f"  2:4 {n}x{k}: {int(tie.sum())} near-tie quads, {int(bad.sum())} mismatches outside them")
-    assert not bad.any()
-    ulp = np.abs(host_u16(scales).astype(np.int64) - ref["scales"].astype(np.int64))
-    assert ulp.max() <= 1
+    check_24_planes(meta, signs, scales, ref, k, f"2:4 {n}x{k}")
 
 
 def test_24_full_layer_sampled_blocks():
@@ -145,13 +139,7 @@ def test_24_full_layer_sampled_blocks():
         ref = oracle.quant.quantize_24(w[rows, 128 * b:128 * (b + 1)].astype(np.float64))
         mb = meta[rows, 4 * b:4 * (b + 1)].contiguous()
         gb = signs[rows, 2 * b:2 * (b + 1)].contiguous()
-        i0, i1, n0, n1 = oracle.quant.unpack_24(host_u32(mb), host_u32(gb), 128)
-        tie = oracle.quant.near_tie_24(ref["wr"], ref["s"])
-        bad = ((i0 != ref["idx0"]) | (i1 != ref["idx1"]) | (n0 != ref["neg0"]) | (n1 != ref["neg1"])) & ~tie
-        say(f"  block ({a}, {b}): {int(tie.sum())} near-tie quads, {int(bad.sum())} mismatches outside them")
-        assert not bad.any()
-        ulp = np.abs(host_u16(scales[rows, b:b + 1].contiguous()).astype(np.int64) - ref["scales"].astype(np.int64))
-        assert ulp.max() <= 1
+        check_24_planes(mb, gb, scales[rows, b:b + 1].contiguous(), ref, 128, f"block ({a}, {b})")
 
 
 # ---------------------------------------------------------------- error-minimising rule

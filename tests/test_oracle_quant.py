@@ -411,3 +411,68 @@ def test_residual_plane_lowers_the_error_and_keeps_plane_one():
     # the residual of a Gaussian group is again spread out: plane 2 keeps most
     # elements (|d| > mean |d| / 2)
     assert 0.5 < np.mean(r["t2"] != 0) < 0.9
+
+
+# ---------------------------------------------------------------- acceptance bands
+# The parity tests forgive a GPU/oracle difference only inside these bands, so
+# each band is pinned here by hand-built cases on both of its sides.
+
+def test_near_threshold_band_edges():
+    # one group with s = 1 (threshold 0.5): the band is |(|w'| - 0.5)| <= 0.5e-5
+    wr = np.zeros((1, 128))
+    wr[0, :6] = [0.5, -0.5, 0.5 + 0.25e-5, 0.5 - 0.25e-5, 0.5 + 1e-5, -(0.5 - 1e-5)]
+    s = np.array([[1.0]])
+    near = q.near_threshold(wr, s)
+    assert near[0, :6].tolist() == [True, True, True, True, False, False]
+    assert not near[0, 6:].any()           # zeros are 0.5 away from the threshold
+
+
+def test_near_tie_24_flags_equal_second_and_third_magnitudes():
+    s = np.array([[1.0]])
+    rows = {
+        "exact tie of 2nd and 3rd": ([3.0, 2.0, -2.0, 1.0], True),
+        "gap 0.5e-5 relative": ([3.0, 2.0, 2.0 * (1 - 0.5e-5), 1.0], True),
+        "gap 1e-4 relative": ([3.0, 2.0, 2.0 * (1 - 1e-4), 1.0], False),
+        "tie of 1st and 2nd only": ([2.0, 2.0, 1.0, 0.5], False),
+        "kept element at 1e-7 s": ([1.0, 1e-7, 0.0, 0.0], True),
+        "kept element at 2e-5 s": ([1.0, 2e-5, 0.0, 0.0], False),
+    }
+    for name, (quad, flagged) in rows.items():
+        wr = np.zeros((1, 128))
+        wr[0, 4:8] = quad           # second quad; the first quad is all zero
+        wr[0, 8:] = [1.0, 0.5, 0.0, 0.0] * 30
+        tie = q.near_tie_24(wr, s)
+        assert bool(tie[0, 1]) == flagged, name
+        assert not tie[0, 2:].any(), name   # quads 1.0, 0.5, 0, 0: a clear choice
+    # an all-zero quad: every pair is a tie (and its kept elements are zero)
+    assert q.near_tie_24(np.zeros((1, 128)), s).all()
+
+
+def test_mse_objective_gap_hand_worked():
+    # a = [2, 2, 1, 1, 0]: objectives 16/2 = 8 (theta 2), 36/4 = 9 (theta 1), 36/5 = 7.2 (theta 0)
+    assert q.mse_objective_gap(np.array([2.0, 1.0, 0.0, 2.0, 1.0])) == pytest.approx(1.0 / 9.0, rel=1e-15)
+    # a = [3, 1, 1, 1]: 9/1 and 36/4 tie exactly
+    assert q.mse_objective_gap(np.array([3.0, 1.0, 1.0, 1.0])) == 0.0
+    # one distinct magnitude, or all zero: no second candidate
+    assert q.mse_objective_gap(np.full(7, 0.25)) == np.inf
+    assert q.mse_objective_gap(np.zeros(5)) == np.inf
+
+
+def test_near_tie_mse_flags_groups_within_the_band():
+    # a group [x, 1, 1, 1, 0 x 124]: theta = x gives x^2, theta = 1 gives (x + 3)^2 / 4,
+    # equal at x = 3; at x = 3 + e the relative gap is about e / 3
+    def group(x):
+        g = np.zeros(128)
+        g[:4] = [x, -1.0, 1.0, -1.0]
+        return g
+    wr = np.stack([group(3.0), group(3.0 + 3e-6), group(3.0 + 3e-4), group(3.0 - 3e-6), group(5.0)])
+    assert q.near_tie_mse(wr)[:, 0].tolist() == [True, True, False, True, False]
+
+
+def test_near_threshold_mse_band_edges():
+    theta = np.array([[2.0]])
+    wr = np.zeros((1, 128))
+    wr[0, :5] = [2.0, -2.0 * (1 - 0.5e-5), 2.0 * (1 + 0.5e-5), 2.0 * (1 + 2e-5), 2.0 * (1 - 2e-5)]
+    near = q.near_threshold_mse(wr, theta)
+    assert near[0, :5].tolist() == [True, True, True, False, False]
+    assert not near[0, 5:].any()
