@@ -247,6 +247,29 @@ TB_API tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt,
 TB_API tb_status tb_ternary_gemv(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device array tb_ternary_gemv_noalloc encodes its activations
+ * into: it takes B and K with tb_act8_bytes(B, K) <= this (B = 16 with
+ * K <= 63488, B = 1 with K <= 1016704). */
+#define TB_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/*
+ * tb_ternary_gemv with bf16 activations for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation): the same product and the same kernels,
+ * but the act8 encoding of x goes to an array the library holds on each GPU
+ * (TB_NOALLOC_SCRATCH_BYTES, held until the process ends) instead of a
+ * caller workspace.  The call allocates and frees nothing.
+ *   x       bf16 bits [B][K], the already rotated activations
+ *   B, codes, scales, N, K, y and the error rules as tb_ternary_gemv;
+ *   tb_act8_bytes(B, K) > TB_NOALLOC_SCRATCH_BYTES returns TB_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (different streams, or different host threads without
+ * ordering) race and must be serialised by the caller.  The result is that of
+ * tb_ternary_gemv with TB_BF16 bit for bit.  Two launches on the stream.
+ */
+TB_API tb_status tb_ternary_gemv_noalloc(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                                  int64_t N, int64_t K, float* y, void* stream);
+
 /*
  * tb_ternary_gemv over up to TB_MAX_SEGMENTS independent products in one
  * launch (e.g. the projections of a layer, so that small matrices do not leave

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tb.h"
 #include "tb_launch.h"
 
@@ -66,33 +68,78 @@ tb_status check_gemv(const tb_gemv_segment& g) {
   return TB_OK;
 }
 
+// The checks of a GEMV call with bf16 activations x [B][K] other than those of
+// its act8 workspace (g.act is not looked at).
+tb_status check_gemv_bf16(const void* x, const tb_gemv_segment& g) {
+  if (gemv_planes(g) == 0) return TB_ERR_FORMAT;
+  if (!dims_ok(g.N, g.K) || g.B < 0 || g.B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+  if (g.B == 0) return TB_OK;
+  if (!x || !g.codes || !g.scales || !g.y) return TB_ERR_NULL;
+  if (!aligned16(x) || !aligned16(g.codes) || !aligned16(g.scales) || !aligned16(g.y)) return TB_ERR_ALIGN;
+  const size_t yb = (size_t)g.B * (size_t)g.N * 4;
+  if (overlap(g.y, yb, x, (size_t)g.B * (size_t)g.K * 2) || overlap(g.y, yb, g.codes, gemv_code_bytes(g)) ||
+      overlap(g.y, yb, g.scales, gemv_scale_bytes(g)))
+    return TB_ERR_ALIAS;
+  return TB_OK;
+}
+
+// Encode bf16 x' as the act8 operand into g.act, then the product: two
+// launches on the stream.
+tb_status encode_and_multiply(const void* x, const tb_gemv_segment& g, hipStream_t stream) {
+  const hipError_t e = tb::launch_act8_prep(static_cast<const uint16_t*>(x), g.B, g.K, const_cast<uint8_t*>(g.act),
+                                            stream);
+  if (e != hipSuccess) return TB_ERR_LAUNCH;
+  return launched(tb::launch_gemv_multi(&g, 1, stream));
+}
+
 // One dense GEMV call with its activations as bf16 x' (encoded as the act8
-// operand into `workspace`, then the product: two launches) or as the act8
-// operand itself (one launch; the workspace is not used).
+// operand into `workspace`, then the product) or as the act8 operand itself
+// (one launch; the workspace is not used).
 tb_status gemv_call(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales, int64_t N,
                     int64_t K, float* y, void* workspace, size_t workspace_bytes, int64_t planes, hipStream_t stream) {
   if (x_dtype != TB_BF16 && x_dtype != TB_ACT8) return TB_ERR_DTYPE;
-  const bool encode = x_dtype == TB_BF16;
-  const tb_gemv_segment g{static_cast<const uint8_t*>(encode ? workspace : x), B, codes, scales, N, K, y, planes};
-  if (encode) {
-    if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
-    if (B == 0) return TB_OK;
-    if (!x) return TB_ERR_NULL;
-    if (!aligned16(x)) return TB_ERR_ALIGN;
-    if (!workspace || workspace_bytes < act8_bytes((size_t)B * (size_t)K)) return TB_ERR_WORKSPACE;
+  if (x_dtype == TB_ACT8) {
+    const tb_gemv_segment g{static_cast<const uint8_t*>(x), B, codes, scales, N, K, y, planes};
+    const tb_status st = check_gemv(g);
+    if (st != TB_OK || B == 0) return st;
+    return launched(tb::launch_gemv_multi(&g, 1, stream));
   }
-  const tb_status st = check_gemv(g);
+  const tb_gemv_segment g{static_cast<const uint8_t*>(workspace), B, codes, scales, N, K, y, planes};
+  const tb_status st = check_gemv_bf16(x, g);
   if (st != TB_OK || B == 0) return st;
-  if (encode) {
-    const size_t xb = (size_t)B * (size_t)K * 2, ab = act8_bytes((size_t)B * (size_t)K);
-    if (overlap(y, (size_t)B * (size_t)N * 4, x, xb) || overlap(workspace, ab, x, xb) ||
-        overlap(workspace, ab, codes, gemv_code_bytes(g)) || overlap(workspace, ab, scales, gemv_scale_bytes(g)))
-      return TB_ERR_ALIAS;
-    const hipError_t e = tb::launch_act8_prep(static_cast<const uint16_t*>(x), B, K, static_cast<uint8_t*>(workspace),
-                                              stream);
-    if (e != hipSuccess) return TB_ERR_LAUNCH;
+  const size_t ab = act8_bytes((size_t)B * (size_t)K);
+  if (!workspace || workspace_bytes < ab) return TB_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TB_ERR_ALIGN;
+  if (overlap(workspace, ab, x, (size_t)B * (size_t)K * 2) || overlap(workspace, ab, codes, gemv_code_bytes(g)) ||
+      overlap(workspace, ab, scales, gemv_scale_bytes(g)) || overlap(workspace, ab, y, (size_t)B * (size_t)N * 4))
+    return TB_ERR_ALIAS;
+  return encode_and_multiply(x, g, stream);
+}
+
+// ---------------------------------------------------------------- no-alloc GEMV
+// tb_ternary_gemv_noalloc encodes its activations into this library-owned
+// array instead of a caller workspace.  Host code never passes `scratch`
+// itself to a kernel (on the host the name is a stand-in, not the device
+// address): the device address is looked up once per device, with that device
+// current, and kept here.
+static __device__ __align__(256) unsigned char scratch[TB_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null until looked up)
+
+// The device address of `scratch` on the current device.
+tb_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TB_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return TB_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
   }
-  return launched(tb::launch_gemv_multi(&g, 1, stream));
+  *out = scratch_ptr[dev];
+  return TB_OK;
 }
 
 // arguments of the GEMM entry points that take a workspace (NULL allowed)
@@ -215,6 +262,19 @@ tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* act, vo
 tb_status tb_ternary_gemv(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream) {
   return gemv_call(x, x_dtype, B, codes, scales, N, K, y, workspace, workspace_bytes, 1, as_stream(stream));
+}
+
+tb_status tb_ternary_gemv_noalloc(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales,
+                                  int64_t N, int64_t K, float* y, void* stream) {
+  tb_gemv_segment g{nullptr, B, codes, scales, N, K, y, 1};
+  tb_status st = check_gemv_bf16(x, g);
+  if (st != TB_OK || B == 0) return st;
+  if (act8_bytes((size_t)B * (size_t)K) > (size_t)TB_NOALLOC_SCRATCH_BYTES) return TB_ERR_WORKSPACE;
+  void* p = nullptr;
+  st = scratch_address(&p);
+  if (st != TB_OK) return st;
+  g.act = static_cast<const uint8_t*>(p);
+  return encode_and_multiply(x, g, as_stream(stream));
 }
 
 tb_status tb_ternary_gemv_resid(const void* x, int x_dtype, int64_t B, const uint32_t* codes, const uint16_t* scales,

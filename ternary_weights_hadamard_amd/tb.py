@@ -27,6 +27,7 @@ TB_FMT_DENSE, TB_FMT_24, TB_FMT_DENSE_MINERR, TB_FMT_DENSE_RESID = 0, 1, 2, 3
 TB_EFLAG_NONFINITE, TB_EFLAG_SCALE_OVF = 1, 2
 TB_GEMV_MAX_BATCH = 16
 TB_MAX_SEGMENTS = 8
+TB_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 
@@ -54,6 +55,7 @@ SIGNATURES = {
     "tb_ternary_gemv_multi": (_int, [ctypes.POINTER(GemvSegment), _int, _vp]),
     "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "tb_ternary_gemv": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "tb_ternary_gemv_noalloc": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp]),
     "tb_ternary_gemv_resid": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "tb_act8_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "tb_act8_prep": (_int, [_vp, _i64, _i64, _vp, _vp]),
@@ -236,6 +238,22 @@ def tb_ternary_gemv(x, codes, scales, batch=None, y=None, workspace=None, stream
     `batch` given)."""
     return _gemv(lib().tb_ternary_gemv, "tb_ternary_gemv", x, codes, scales, scales.shape[1] * 128, batch, y,
                  workspace, stream)
+
+
+def tb_ternary_gemv_noalloc(x, codes, scales, y, stream=None):
+    """tb_ternary_gemv of bf16 x [B, K] into the caller's fp32 y [B, N] with the
+    library's own device array for the encoded activations: nothing is
+    allocated (the caller passes y).  Calls that may overlap on one GPU race."""
+    _dev(x, codes, scales, y)
+    n, g = scales.shape
+    k = g * 128
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"tb_ternary_gemv_noalloc: x must be bf16 [B, {k}] (got {x.dtype} {tuple(x.shape)})")
+    if y.dtype != torch.float32 or tuple(y.shape) != (x.shape[0], n):
+        raise ValueError(f"tb_ternary_gemv_noalloc: y must be float32 [{x.shape[0]}, {n}]")
+    _check(lib().tb_ternary_gemv_noalloc(_p(x), x.shape[0], _p(codes), _p(scales), n, k, _p(y), _stream(stream)),
+           "tb_ternary_gemv_noalloc")
+    return y
 
 
 def tb_ternary_gemv_resid(x, codes, scales, batch=None, y=None, workspace=None, stream=None):
