@@ -14,9 +14,10 @@ value = packed weight bytes (codes + scales) streamed per step / step time.
 Also measured in the same run, each over its own synthetic input, and
 reported under "extra": the same decode step at batch 8, the 2:4 GEMV
 (17408x5120, batch 1), the prefill GEMM (M = 2048, both FFN shapes), the
-activation FWHT at prefill size, and the offline quantiser over one layer
-(absmean rule and the error-minimising rule).
-The CPU oracle is timed on a bounded sample of the decode workload.
+activation FWHT at prefill size, the offline quantiser streamed over a
+64-layer stack (absmean rule) and over one layer with the error-minimising
+rule.  The CPU oracle is timed on bounded samples of the decode GEMV, the 2:4
+GEMV, the GEMM and the quantiser, on one core and on all cores.
 """
 
 import argparse
@@ -332,38 +333,97 @@ def extra_phases(gen, dev, quick):
     log(f"  FWHT 2048x17408: {ms * 1e3:.1f} us, {out['fwht128']['gbs']} GB/s")
     del xa, ya
 
-    # offline quantiser over one 27B layer (7 matrices, 372M fp32 weights)
-    mats = [("q", D, D), ("k", D, D), ("v", D, D), ("o", D, D), ("up", F, D), ("gate", F, D), ("down", D, F)]
-    ws, outs = [], []
-    for _, n, k in mats:
-        w = torch.randn((n, k), generator=gen, device=dev) * 0.02
-        ws.append(w)
-        outs.append((torch.empty((n // 16, k // 128, 128), dtype=torch.int32, device=dev),
-                     torch.empty((n, k // 128), dtype=torch.float16, device=dev)))
+    # offline quantiser streamed over the 64-layer stack (its own function)
+    out["quantize_stack"] = quantize_stack(dev, 64)
 
-    def runq():
-        for w, (c, s) in zip(ws, outs):
-            tb.tb_quantize_pack(w, codes=c, scales=s)
-
-    ms = time_eager(runq, 2 if quick else 5)
-    nw = sum(n * k for _, n, k in mats)
-    qb = nw * 4 + nw // 4 + nw // 64
-    out["quantize"] = {"workload": "one 27B layer, 7 matrices, 372,244,480 fp32 weights", "ms_per_layer": round(ms, 3),
-                       "gbs": round(qb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(qb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                       "projected_64_layer_ms": round(64 * ms, 1)}
-    log(f"  quantise one layer: {ms:.3f} ms, {out['quantize']['gbs']} GB/s")
+    # the error-minimising rule on layer 0 of the same stack recipe
+    mats = synth.LAYER_MATRICES
+    g0 = torch.Generator(device=dev)
+    g0.manual_seed(5000)
+    ws = [synth.torch_stack_weights(n, k, g0, dev) for _, n, k in mats]
+    outs = [(torch.empty((n // 16, k // 128, 128), dtype=torch.int32, device=dev),
+             torch.empty((n, k // 128), dtype=torch.float16, device=dev)) for _, n, k in mats]
 
     def runq_minerr():
-        for w, (c, s) in zip(ws, outs):
-            tb.tb_quantize_pack(w, fmt=tb.TB_FMT_DENSE_MINERR, codes=c, scales=s)
+        for w, (c, sc) in zip(ws, outs):
+            tb.tb_quantize_pack(w, fmt=tb.TB_FMT_DENSE_MINERR, codes=c, scales=sc)
 
     ms = time_eager(runq_minerr, 1 if quick else 2)
-    out["quantize_minerr"] = {"workload": "one 27B layer, error-minimising threshold and scale per group",
+    nw = sum(n * k for _, n, k in mats)
+    qb = nw * 4 + nw // 4 + nw // 64
+    out["quantize_minerr"] = {"workload": "layer 0 of the stack recipe (7 matrices, 372,244,480 weights), "
+                                          "error-minimising threshold and scale per group",
                               "ms_per_layer": round(ms, 3), "gbs": round(qb / (ms * 1e-3) / 1e9, 1),
                               "note": "every group magnitude tried as the threshold (128 x 128 compares per group)"}
     log(f"  quantise one layer, min-error rule: {ms:.3f} ms")
     del ws, outs
     return out
+
+
+QUANT_BYTES_PER_WEIGHT = 4 + 1 / 4 + 1 / 64  # fp32 read, 2-bit codes and fp16 scales written
+
+
+def quantize_stack(dev, layers):
+    """The offline quantiser streamed over a 27B-shaped stack, layer by layer.
+    Each layer's 7 fp32 matrices (Q, K, V, O 5120x5120, up and gate
+    17408x5120, down 5120x17408) are drawn on the device with the stack recipe
+    (N(0, 0.02^2) with 1 % of the input columns 0.02 * Student-t(3); the
+    generator seeded 5000 + 8 * layer), quantised with the absmean rule and
+    packed (tb_quantize_pack), and the codes and scales copied to pinned host
+    memory.  The quantiser launches and the copies are timed apart with events
+    on the stream; drawing the weights is outside both."""
+    import torch
+
+    from ternary_weights_hadamard_amd import synth, tb
+
+    mats = synth.LAYER_MATRICES
+    codes = [torch.empty((n // 16, k // 128, 128), dtype=torch.int32, device=dev) for _, n, k in mats]
+    scales = [torch.empty((n, k // 128), dtype=torch.float16, device=dev) for _, n, k in mats]
+    codes_h = [torch.empty(c.shape, dtype=c.dtype, pin_memory=True) for c in codes]
+    scales_h = [torch.empty(x.shape, dtype=x.dtype, pin_memory=True) for x in scales]
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    q_ms, c_ms = [], []
+    w0 = time.perf_counter()
+    for layer in range(layers):
+        gen.manual_seed(5000 + 8 * layer)
+        ws = [synth.torch_stack_weights(n, k, gen, dev) for _, n, k in mats]
+        if layer == 0:  # first-touch and clocks: one untimed pass over layer 0
+            for w, c, sc in zip(ws, codes, scales):
+                tb.tb_quantize_pack(w, codes=c, scales=sc)
+        ev[0].record()
+        for w, c, sc in zip(ws, codes, scales):
+            tb.tb_quantize_pack(w, codes=c, scales=sc, err_flag=flag)
+        ev[1].record()
+        for j in range(len(mats)):
+            codes_h[j].copy_(codes[j], non_blocking=True)
+            scales_h[j].copy_(scales[j], non_blocking=True)
+        ev[2].record()
+        ev[2].synchronize()
+        q_ms.append(ev[0].elapsed_time(ev[1]))
+        c_ms.append(ev[1].elapsed_time(ev[2]))
+        del ws
+        if layer % 16 == 15:
+            log(f"  quantised {layer + 1}/{layers} layers")
+    wall = time.perf_counter() - w0
+    nw = layers * sum(n * k for _, n, k in mats)
+    packed = layers * sum(n * k // 4 + n * k // 64 for _, n, k in mats)
+    tq = sum(q_ms)
+    gbs = nw * QUANT_BYTES_PER_WEIGHT / (tq * 1e-3) / 1e9
+    qs = sorted(q_ms)
+    pct = lambda p: round(qs[min(len(qs) - 1, int(p * len(qs)))], 4)
+    res = {"workload": f"{layers}-layer 27B-shaped stack (7 matrices per layer), fp32 N(0, 0.02^2) with 1 % "
+                       "Student-t(3) outlier input columns drawn on the device per layer; absmean rule, 2-bit pack; "
+                       "codes and scales copied to pinned host memory",
+           "layers": layers, "weights": nw, "bytes_per_weight": QUANT_BYTES_PER_WEIGHT,
+           "quantize_ms_total": round(tq, 3), "ms_per_layer_median": pct(0.5), "ms_per_layer_p10": pct(0.1),
+           "ms_per_layer_p90": pct(0.9), "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "d2h_ms_total": round(sum(c_ms), 3), "d2h_gbs": round(packed / (sum(c_ms) * 1e-3) / 1e9, 1),
+           "wall_s_with_generation": round(wall, 2), "error_flag": int(flag.item())}
+    log(f"  quantise stack: {layers} layers, {tq:.2f} ms of quantiser kernels ({gbs:.1f} GB/s, "
+        f"{gbs / PEAK_HBM_GBS:.3f} of HBM), D2H {sum(c_ms):.1f} ms, wall {wall:.1f} s")
+    return res
 
 
 def profile_pass(dev):
@@ -458,41 +518,168 @@ def summarize_kernel_stats(stats_csv, out_path, command):
     print("\n".join(lines))
 
 
-def cpu_baseline(stack, max_seconds=30.0):
-    """Time the CPU oracle's GEMV on layer 0's fused matrices at batch 1, with one
-    BLAS thread, until about max_seconds of work; report packed-weight GB/s."""
+# ---------------------------------------------------------------- CPU oracle baseline
+# The oracle (plain float64 numpy, oracle/) timed on this host's cores on
+# bounded samples of the workloads.  A task runs one oracle call and returns
+# its elapsed seconds (and, for the quantiser, its near-threshold count); the
+# all-cores runs hand the row chunks of a sample to one spawned worker process
+# per core, each with one BLAS thread.
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def _oracle_task(task):
+    import numpy as np
+
+    import oracle
+
+    kind, args = task
+    t0 = time.perf_counter()
+    near = 0
+    if kind == "gemv":
+        oracle.matvec.gemv(*args)
+    elif kind == "gemv24":
+        oracle.matvec.gemv24(*args)
+    elif kind == "quant":
+        for blk in args:
+            r = oracle.quant.quantize_dense(blk.astype(np.float64))
+            near += int(oracle.quant.near_threshold(r["wr"], r["s"]).sum())
+    else:
+        raise ValueError(kind)
+    return time.perf_counter() - t0, near
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _chunks(n_rows, parts, align=16):
+    """[lo, hi) row ranges, multiples of `align`, splitting n_rows into about `parts` pieces."""
+    step = max(align, (n_rows // parts + align - 1) // align * align)
+    return [(lo, min(n_rows, lo + step)) for lo in range(0, n_rows, step)]
+
+
+def cpu_baseline(stack, dev, max_seconds=20.0):
+    """The CPU oracle on bounded samples of the decode GEMV (the headline,
+    value), the 2:4 GEMV, the prefill GEMM and the quantiser, each on one
+    core and on all of this host's cores (the worker count is what the
+    process may use, at most 16, the CPU share of one GPU here)."""
+    import multiprocessing as mp
+
     import numpy as np
     import torch
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+    from ternary_weights_hadamard_amd import synth
     import oracle
 
-    import contextlib
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    pool = ctx.Pool(workers, initializer=_one_blas_thread)
+    pool.map(_oracle_task, [("quant", [])] * workers)  # workers up and importing before any timing
 
-    x = stack.x  # same activation tensors the GPU used
-    done_bytes, t_total, names = 0, 0.0, []
-    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    with ctx:
-        for j, (codes, scales, n, k) in enumerate(stack.w[0]):
-            c = codes.cpu().numpy().view(np.uint32)
-            s = scales.cpu().view(torch.int16).numpy().view(np.uint16)
-            xb = x[j][:1].cpu().view(torch.int16).numpy().view(np.uint16)
-            xr = oracle.numerics.f64_to_bf16_bits(oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(xb)))
-            t0 = time.perf_counter()
-            oracle.matvec.gemv(xr, c, s, k)
-            dt = time.perf_counter() - t0
-            t_total += dt
-            done_bytes += packed_bytes(n, k)
-            names.append(FUSED[j][0])
-            log(f"  oracle GEMV {FUSED[j][0]} {n}x{k}: {dt:.2f} s")
-            if t_total > max_seconds:
-                break
-    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 numpy oracle GEMV (dequantise + matmul), batch 1, layer 0 matrices {'/'.join(names)} "
-                      f"({done_bytes / 1e6:.1f} MB packed), one thread, {t_total:.1f} s"}
+    def one_core(tasks):
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            return [_oracle_task(t) for t in tasks]
+
+    def all_cores(tasks):
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_task, tasks, chunksize=1)
+        return time.perf_counter() - t0, res
+
+    out = {}
+    # decode GEMV, batch 1, layer 0's fused matrices of the stack (the same bits the GPU used),
+    # x rotated by the oracle first (not timed); one core until max_seconds, all cores on the same matrices
+    t1, done, names, mats = 0.0, 0, [], []
+    for j, (codes, scales, n, k) in enumerate(stack.w[0]):
+        c = codes.cpu().numpy().view(np.uint32)
+        sc = scales.cpu().view(torch.int16).numpy().view(np.uint16)
+        xb = stack.x[j][:1].cpu().view(torch.int16).numpy().view(np.uint16)
+        xr = oracle.numerics.f64_to_bf16_bits(oracle.hadamard.fwht_dense(oracle.numerics.bf16_bits_to_f64(xb)))
+        dt, _ = one_core([("gemv", (xr, c, sc, k))])[0]
+        t1 += dt
+        done += packed_bytes(n, k)
+        names.append(FUSED[j][0])
+        mats.append((xr, c, sc, n, k))
+        log(f"  oracle GEMV {FUSED[j][0]} {n}x{k}, one core: {dt:.2f} s")
+        if t1 > max_seconds:
+            break
+    tasks = [("gemv", (xr, c[lo // 16:hi // 16], sc[lo:hi], k)) for xr, c, sc, n, k in mats for lo, hi in
+             _chunks(n, workers)]
+    ta, _ = all_cores(tasks)
+    log(f"  oracle GEMV, {workers} cores: {ta:.2f} s (one core {t1:.2f} s)")
+    gemv_sample = (f"float64 numpy oracle GEMV (dequantise + matmul), batch 1, layer 0's fused matrices "
+                   f"{'/'.join(names)} ({done / 1e6:.1f} MB packed)")
+
+    # 2:4 GEMV, 17408 x 5120, batch 1: a 2048-row slice
+    n24, k24 = 2048, D
+    meta, signs = synth.random_24(n24, k24, seed=30)
+    sc24 = synth.random_scales_f16(n24, k24, seed=31)
+    x24 = synth.gaussian_bf16((1, k24), seed=32)
+    b24 = n24 * k24 // 8 + n24 * k24 // 16 + n24 * k24 // 64
+    d1, _ = one_core([("gemv24", (x24, meta, signs, sc24, k24))])[0]
+    da, _ = all_cores([("gemv24", (x24, meta[lo:hi], signs[lo:hi], sc24[lo:hi], k24))
+                       for lo, hi in _chunks(n24, workers)])
+    out["gemv24"] = {"sample": "2:4 GEMV 2048 x 5120 rows of the 17408 x 5120 shape, batch 1", "unit": "GB/s",
+                     "one_core": round(b24 / d1 / 1e9, 4), "all_cores": round(b24 / da / 1e9, 4)}
+
+    # prefill GEMM, M = 2048, K = 5120: a 512-column slice of N (the dequantised fp64 matmul)
+    m, kg, ng = 2048, D, 512
+    cg = synth.random_code_words(ng, kg, seed=40)
+    sg = synth.random_scales_f16(ng, kg, seed=41)
+    xg = synth.gaussian_bf16((m, kg), seed=42)
+    fl = 2.0 * m * ng * kg
+    d1, _ = one_core([("gemv", (xg, cg, sg, kg))])[0]
+    da, _ = all_cores([("gemv", (xg, cg, sg, kg))] if workers == 1 else
+                      [("gemv", (xg[lo:hi], cg, sg, kg)) for lo, hi in _chunks(m, workers)])
+    out["gemm"] = {"sample": "prefill GEMM M = 2048, K = 5120, a 512-wide slice of N (dequantise + float64 matmul)",
+                   "unit": "GFLOP/s", "one_core": round(fl / d1 / 1e9, 2), "all_cores": round(fl / da / 1e9, 2)}
+
+    # quantiser: 1 % of the 128 x 128 blocks of layer 0 of the stack recipe, drawn on the
+    # device as the stack phase draws them; near-threshold elements counted on the way
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5000)
+    rng = np.random.default_rng(7000)
+    blocks, total_blocks = [], 0
+    for _, n, k in synth.LAYER_MATRICES:
+        w = synth.torch_stack_weights(n, k, gen, dev)
+        nb = (n // 128) * (k // 128)
+        total_blocks += nb
+        for b in rng.choice(nb, max(1, nb // 100), replace=False):
+            a, c = divmod(int(b), k // 128)
+            blocks.append(w[128 * a:128 * (a + 1), 128 * c:128 * (c + 1)].cpu().numpy())
+        del w
+    per = (len(blocks) + workers - 1) // workers
+    d1, near1 = one_core([("quant", blocks)])[0]
+    da, res = all_cores([("quant", blocks[i:i + per]) for i in range(0, len(blocks), per)])
+    qw = len(blocks) * 128 * 128
+    stack_weights = 64 * sum(n * k for _, n, k in synth.LAYER_MATRICES)
+    frac = len(blocks) / total_blocks
+    out["quantize"] = {"sample": f"{len(blocks)} random 128 x 128 blocks ({frac:.4f} of layer 0) of the stack recipe",
+                       "unit": "GB/s", "bytes_per_weight": QUANT_BYTES_PER_WEIGHT,
+                       "one_core": round(qw * QUANT_BYTES_PER_WEIGHT / d1 / 1e9, 5),
+                       "all_cores": round(qw * QUANT_BYTES_PER_WEIGHT / da / 1e9, 5),
+                       "near_threshold_in_sample": near1,
+                       "near_threshold_per_weight": near1 / qw,
+                       "near_threshold_projected_64_layers": round(near1 / qw * stack_weights)}
+    pool.close()
+    pool.join()
+    return {"value": round(done / ta / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": gemv_sample + f", {workers} worker processes with one BLAS thread each, {ta:.2f} s",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)),
+            "one_core": {"value": round(done / t1 / 1e9, 4), "unit": "GB/s", "seconds": round(t1, 2)},
+            "other_configs": out}
 
 
 def main():
@@ -634,7 +821,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(stack)
+        result["cpu_baseline"] = cpu_baseline(stack, dev)
     print(json.dumps(result), flush=True)
 
 

@@ -386,10 +386,7 @@ struct WideChunk {
 
 // K slices of a wide segment: the smallest power of two leaving at most
 // kWideSlice groups per wave
-#ifndef TB_WIDE_SLICE
-#define TB_WIDE_SLICE 6
-#endif
-constexpr int kWideSlice = TB_WIDE_SLICE;
+constexpr int kWideSlice = 6;
 int wide_slices(int64_t G) {
   int ks = 1;
   while (ks < kMaxSlices && G > (int64_t)ks * kWideSlice) ks *= 2;
@@ -440,12 +437,8 @@ int wide_plan(const GemvSegment* segs, int count, int T, WideSegs& ws, int& wave
   return wg;
 }
 
-#ifndef TB_WIDE_TMAX
-#define TB_WIDE_TMAX 8
-#endif
-#ifndef TB_WIDE_MIN_WAVES
-#define TB_WIDE_MIN_WAVES 2048
-#endif
+constexpr int kWideTMax = 8;         // tiles per wave, at most
+constexpr int kWideMinWaves = 2048;  // waves a launch should have before T is lowered
 
 template <int NB4, int T>
 hipError_t launch_wide_t(const WideSegs& ws, int wg, int waves, hipStream_t stream) {
@@ -455,23 +448,21 @@ hipError_t launch_wide_t(const WideSegs& ws, int wg, int waves, hipStream_t stre
   return hipGetLastError();
 }
 
-// Tiles per wave: the most (up to TB_WIDE_TMAX, 4 above batch 8 where the
+// Tiles per wave: the most (up to kWideTMax, 4 above batch 8 where the
 // accumulators crowd the registers) that still give the launch
-// TB_WIDE_MIN_WAVES waves, else one.  More tiles per wave means fewer
+// kWideMinWaves waves, else one.  More tiles per wave means fewer
 // activation reads per tile; fewer waves leave CUs idle (the down projection,
 // 320 tiles, takes two per wave).  Measured on the 27B-shaped layers.
 template <int NB4>
 hipError_t launch_wide(const GemvSegment* segs, int count, hipStream_t stream) {
   WideSegs ws{};
   int waves = 1;
-  for (int T = NB4 <= 2 ? TB_WIDE_TMAX : std::min(TB_WIDE_TMAX, 4); T >= 1; T /= 2) {
+  for (int T = NB4 <= 2 ? kWideTMax : std::min(kWideTMax, 4); T >= 1; T /= 2) {
     const int wg = wide_plan(segs, count, T, ws, waves);
-    if (T > 1 && (int64_t)wg * waves < TB_WIDE_MIN_WAVES) continue;
-#if TB_WIDE_TMAX >= 8
+    if (T > 1 && (int64_t)wg * waves < kWideMinWaves) continue;
     if constexpr (NB4 <= 2) {
       if (T == 8) return launch_wide_t<NB4, 8>(ws, wg, waves, stream);
     }
-#endif
     if (T == 4) return launch_wide_t<NB4, 4>(ws, wg, waves, stream);
     if (T == 2) return launch_wide_t<NB4, 2>(ws, wg, waves, stream);
     return launch_wide_t<NB4, 1>(ws, wg, waves, stream);

@@ -131,6 +131,22 @@ def torch_gaussian_bf16(shape, gen, device, scale=1.0):
     return (torch.randn(shape, generator=gen, device=device) * scale).to(torch.bfloat16)
 
 
+def torch_stack_weights(n, k, gen, device, sigma=0.02, outlier_col_frac=0.01, nu=3):
+    """The stack recipe of stack_weights drawn on the device: W ~ N(0, sigma^2)
+    fp32 [n, k], with round(outlier_col_frac * k) input columns replaced by
+    sigma * Student-t(nu) draws (a standard normal over the root of the mean of
+    nu squared standard normals; nu a positive integer)."""
+    import torch
+
+    w = torch.randn((n, k), generator=gen, device=device) * sigma
+    ncol = max(1, int(round(outlier_col_frac * k)))
+    cols = torch.randperm(k, generator=gen, device=device)[:ncol]
+    z = torch.randn((n, ncol), generator=gen, device=device)
+    chi2 = torch.randn((nu, n, ncol), generator=gen, device=device).square().sum(dim=0)
+    w[:, cols] = z / torch.sqrt(chi2 / nu) * sigma
+    return w
+
+
 def torch_24(n, k, gen, device):
     """2:4 planes (meta [n, k/32], signs [n, k/64]) as int32, uniform index pairs and signs."""
     import torch

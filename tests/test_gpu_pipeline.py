@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close, bf16_dev, check_dense_codes, f32_dev, host_f64, host_u16, say
+from gpu_util import assert_close, bf16_dev, check_dense_codes, f32_dev, host_f64, host_u16, host_u32, say
 from ternary_weights_hadamard_amd import synth, tb
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,16 @@ def test_single_layer_pipeline_1024():
     assert_close(host_f64(yr), yr_ref, "y' (rotated basis)")
     y_ref = oracle.hadamard.fwht_dense(yr_ref)
     assert_close(host_f64(y), y_ref, "y after back-rotation")
+    # weight NMSE of the GPU's codes and fp16 scales against W', and of the same
+    # absmean rule applied to the unrotated W (reported; the oracle test pins both)
+    t_gpu = oracle.quant.unpack_dense(host_u32(codes), k)
+    s_gpu = oracle.numerics.f16_bits_to_f64(host_u16(scales))
+    nmse_rot = np.sum((t_gpu * np.repeat(s_gpu, 128, axis=1) - ref["wr"]) ** 2) / np.sum(ref["wr"] ** 2)
+    w64 = w.astype(np.float64)
+    s_raw = oracle.quant.absmean_scales(w64)
+    nmse_raw = np.sum((oracle.quant.ternarize(w64, s_raw) * np.repeat(s_raw, 128, axis=1) - w64) ** 2) / np.sum(w64 ** 2)
+    say(f"  weight NMSE: rotated (GPU codes) {nmse_rot:.4f}, unrotated (same rule) {nmse_raw:.4f}")
+    assert nmse_rot < nmse_raw
     # the method's accuracy on this layer, reported (not gated): relative error vs W x
     wx = w.astype(np.float64) @ oracle.numerics.bf16_bits_to_f64(x)[0]
     rel = np.linalg.norm(host_f64(y)[0] - wx) / np.linalg.norm(wx)
