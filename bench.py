@@ -525,7 +525,14 @@ def summarize_kernel_stats(stats_csv, out_path, command):
 # all-cores runs hand the row chunks of a sample to one spawned worker process
 # per core, each with one BLAS thread.
 
+BLAS_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+
+
 def _one_blas_thread():
+    # the workers inherit BLAS_THREAD_VARS = 1 from the parent; numpy is loaded
+    # here, before any task, and its pools are held at one thread as well
+    import numpy  # noqa: F401
+
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(limits=1)
@@ -585,7 +592,16 @@ def cpu_baseline(stack, dev, max_seconds=20.0):
 
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     ctx = mp.get_context("spawn")
-    pool = ctx.Pool(workers, initializer=_one_blas_thread)
+    saved = {v: os.environ.get(v) for v in BLAS_THREAD_VARS}
+    os.environ.update({v: "1" for v in BLAS_THREAD_VARS})  # inherited by the spawned workers
+    try:
+        pool = ctx.Pool(workers, initializer=_one_blas_thread)
+    finally:
+        for v, old in saved.items():
+            if old is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = old
     pool.map(_oracle_task, [("quant", [])] * workers)  # workers up and importing before any timing
 
     def one_core(tasks):
@@ -641,8 +657,7 @@ def cpu_baseline(stack, dev, max_seconds=20.0):
     xg = synth.gaussian_bf16((m, kg), seed=42)
     fl = 2.0 * m * ng * kg
     d1, _ = one_core([("gemv", (xg, cg, sg, kg))])[0]
-    da, _ = all_cores([("gemv", (xg, cg, sg, kg))] if workers == 1 else
-                      [("gemv", (xg[lo:hi], cg, sg, kg)) for lo, hi in _chunks(m, workers)])
+    da, _ = all_cores([("gemv", (xg, cg[lo // 16:hi // 16], sg[lo:hi], kg)) for lo, hi in _chunks(ng, workers)])
     out["gemm"] = {"sample": "prefill GEMM M = 2048, K = 5120, a 512-wide slice of N (dequantise + float64 matmul)",
                    "unit": "GFLOP/s", "one_core": round(fl / d1 / 1e9, 2), "all_cores": round(fl / da / 1e9, 2)}
 
