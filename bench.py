@@ -657,7 +657,7 @@ def cpu_baseline(stack, dev, max_seconds=20.0):
     xg = synth.gaussian_bf16((m, kg), seed=42)
     fl = 2.0 * m * ng * kg
     d1, _ = one_core([("gemv", (xg, cg, sg, kg))])[0]
-    da, _ = all_cores([("gemv", (xg, cg[lo // 16:hi // 16], sg[lo:hi], kg)) for lo, hi in _chunks(ng, workers)])
+    da, _ = all_cores([("gemv", (xg[lo:hi], cg, sg, kg)) for lo, hi in _chunks(m, workers)])
     out["gemm"] = {"sample": "prefill GEMM M = 2048, K = 5120, a 512-wide slice of N (dequantise + float64 matmul)",
                    "unit": "GFLOP/s", "one_core": round(fl / d1 / 1e9, 2), "all_cores": round(fl / da / 1e9, 2)}
 
