@@ -306,7 +306,7 @@ def extra_phases(gen, dev, quick):
     # 2:4 GEMV, 17408 x 5120, batch 1, rotated over >= 1 GB of weight copies
     n, k = F, D
     copies = 64
-    planes = [synth.torch_24(n, k, gen, dev) + (synth.torch_scales_f16(n, k, gen, dev),) for _ in range(copies)]
+    planes = [synth.torch_24(n, k, gen, dev) + (synth.torch_scales24_f16(n, k, gen, dev),) for _ in range(copies)]
     x = synth.torch_gaussian_bf16((1, k), gen, dev)
     y = torch.empty((1, n), dtype=torch.float32, device=dev)
 
@@ -342,7 +342,7 @@ def extra_phases(gen, dev, quick):
     g0.manual_seed(5000)
     ws = [synth.torch_stack_weights(n, k, g0, dev) for _, n, k in mats]
     outs = [(torch.empty((n // 16, k // 128, 128), dtype=torch.int32, device=dev),
-             torch.empty((n, k // 128), dtype=torch.float16, device=dev)) for _, n, k in mats]
+             torch.empty((n // 16, k // 128, 16), dtype=torch.float16, device=dev)) for _, n, k in mats]
 
     def runq_minerr():
         for w, (c, sc) in zip(ws, outs):
@@ -378,7 +378,7 @@ def quantize_stack(dev, layers):
 
     mats = synth.LAYER_MATRICES
     codes = [torch.empty((n // 16, k // 128, 128), dtype=torch.int32, device=dev) for _, n, k in mats]
-    scales = [torch.empty((n, k // 128), dtype=torch.float16, device=dev) for _, n, k in mats]
+    scales = [torch.empty((n // 16, k // 128, 16), dtype=torch.float16, device=dev) for _, n, k in mats]
     codes_h = [torch.empty(c.shape, dtype=c.dtype, pin_memory=True) for c in codes]
     scales_h = [torch.empty(x.shape, dtype=x.dtype, pin_memory=True) for x in scales]
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -631,7 +631,7 @@ def cpu_baseline(stack, dev, max_seconds=20.0):
         log(f"  oracle GEMV {FUSED[j][0]} {n}x{k}, one core: {dt:.2f} s")
         if t1 > max_seconds:
             break
-    tasks = [("gemv", (xr, c[lo // 16:hi // 16], sc[lo:hi], k)) for xr, c, sc, n, k in mats for lo, hi in
+    tasks = [("gemv", (xr, c[lo // 16:hi // 16], sc[lo // 16:hi // 16], k)) for xr, c, sc, n, k in mats for lo, hi in
              _chunks(n, workers)]
     ta, _ = all_cores(tasks)
     log(f"  oracle GEMV, {workers} cores: {ta:.2f} s (one core {t1:.2f} s)")
@@ -641,7 +641,7 @@ def cpu_baseline(stack, dev, max_seconds=20.0):
     # 2:4 GEMV, 17408 x 5120, batch 1: a 2048-row slice
     n24, k24 = 2048, D
     meta, signs = synth.random_24(n24, k24, seed=30)
-    sc24 = synth.random_scales_f16(n24, k24, seed=31)
+    sc24 = synth.random_scales24_f16(n24, k24, seed=31)
     x24 = synth.gaussian_bf16((1, k24), seed=32)
     b24 = n24 * k24 // 8 + n24 * k24 // 16 + n24 * k24 // 64
     d1, _ = one_core([("gemv24", (x24, meta, signs, sc24, k24))])[0]

@@ -40,8 +40,12 @@
  *                the arrangement is this library's, chosen so that two AND
  *                masks turn a word into the fp4 operand of the gfx950
  *                block-scaled matrix instruction.)
- *   Scales       uint16 fp16 bits scales[N][K/128], the group's absmean,
- *                rounded to nearest even.
+ *   Scales       uint16 fp16 bits, one per row and 128-group: the group's
+ *                absmean, rounded to nearest even.  Dense formats store them
+ *                tile-major like the codes, scales[N/16][K/128][16]: the scale
+ *                of row n, group g at ((n/16)*(K/128) + g)*16 + n%16 (a 16-row
+ *                tile's scales for one group are 32 contiguous bytes).  The 2:4
+ *                format stores them by row, scales[N][K/128].
  *   2:4 meta     uint32 meta[N][K/32]: for quad q = k/4 the nibble at bits
  *                4*(q%8) holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1,
  *                the kept positions inside the quad.
@@ -204,12 +208,13 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_
  * scale, in the rotated basis) is ternarised by the same rule, giving
  * W' ~ fp16(s1) t1 + fp16(s2) t2.  Storage: the dense format of both planes
  * with their groups interleaved, codes [N/16][2K/128][128] and scales
- * [N][2K/128], where group 2g + p is plane p's group g.
+ * [N/16][2K/128][16], where group 2g + p is plane p's group g.
  *   W       fp32 [N][K]
  *   codes   dense: [N/16][K/128][128] code words (the tile layout above);
  *           two-plane: [N/16][2K/128][128]; 2:4: the sign plane [N][K/64]
  *   meta    2:4: [N][K/32]; must be NULL for the dense formats (else TB_ERR_FORMAT)
- *   scales  fp16 bits [N][K/128]; two-plane: [N][2K/128]
+ *   scales  fp16 bits; dense: [N/16][K/128][16] (tile-major, above);
+ *           two-plane: [N/16][2K/128][16]; 2:4: [N][K/128]
  *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
  *             (the caller zeroes it first).
  * Arithmetic is fp32; the absmean threshold uses the unrounded scale.
@@ -232,7 +237,7 @@ TB_API tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt,
  *             One launch; `workspace` is not used and may be NULL.
  *           Other dtypes return TB_ERR_DTYPE.
  *   B       0 <= B <= TB_GEMV_MAX_BATCH (else TB_ERR_SHAPE)
- *   codes, scales  dense format, [N/16][K/128][128] and [N][K/128]
+ *   codes, scales  dense format, [N/16][K/128][128] and [N/16][K/128][16]
  *   y       fp32 [B][N]; must not overlap the inputs (TB_ERR_ALIAS)
  *   workspace, workspace_bytes  for TB_BF16: caller-owned device memory of at
  *           least tb_act8_bytes(B, K) bytes (else TB_ERR_WORKSPACE), 16-byte
@@ -287,7 +292,7 @@ TB_API tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, v
  * Decode GEMV with two-plane dense ternary weights (TB_FMT_DENSE_RESID, the
  * residual calibration of xxqk.cn/news/652513 §3):
  *   y[b][n] = sum_g sum_p fp16(s_p[n][g]) * sum_{k in g} t_p[n][k] * x[b][k]
- *   codes   [N/16][2K/128][128], scales [N][2K/128]: group 2g + p is plane
+ *   codes   [N/16][2K/128][128], scales [N/16][2K/128][16]: group 2g + p is plane
  *           p's group g (as tb_quantize_pack writes them)
  *   x, x_dtype, B, y, workspace and the error rules as tb_ternary_gemv; K is
  *   the activation length.  Both planes' products are exact and accumulated
@@ -326,6 +331,7 @@ TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t*
  * tb_ternary_gemv for M rows of activations:
  *   y[m][n] = sum_g fp16(scales[n][g]) * sum_{k in g} t[n][k] * x[m][k]
  *   x       bf16 bits [M][K], M >= 0 (any M; ragged tails are handled)
+ *   codes, scales  dense format, [N/16][K/128][128] and [N/16][K/128][16]
  *   y       [M][N] in y_dtype: TB_BF16 (rounded to nearest even) or TB_F32;
  *           must not overlap the inputs.
  * The matrix cores take the activations as the bf16 values they are and each

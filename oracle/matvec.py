@@ -14,7 +14,7 @@ brute-force forms are explicit Python loops for tiny shapes.
 import numpy as np
 
 from .numerics import bf16_bits_to_f64, f16_bits_to_f64
-from .quant import GROUP, dense_from_24, split_planes, unpack_24, unpack_dense
+from .quant import GROUP, dense_from_24, split_planes, unpack_24, unpack_dense, untile_scales
 
 
 def _x(x_bf16_bits):
@@ -23,9 +23,10 @@ def _x(x_bf16_bits):
 
 
 def dequant_dense(codes, scales, k):
-    """W~[n, k] = f16(scale[n, k // 128]) * t[n, k]."""
+    """W~[n, k] = f16(scale[n, k // 128]) * t[n, k], scales in the dense storage
+    order [N/16, K/128, 16]."""
     t = unpack_dense(codes, k).astype(np.float64)
-    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    s = f16_bits_to_f64(untile_scales(np.asarray(scales, dtype=np.uint16)))
     return t * np.repeat(s, GROUP, axis=1)
 
 
@@ -68,7 +69,7 @@ def gemv_bruteforce(x_bf16_bits, codes, scales, k):
     """Loop form of gemv: decode each 2-bit field by hand and accumulate."""
     x = _x(x_bf16_bits)
     codes = np.asarray(codes, dtype=np.uint32)
-    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    st = np.asarray(scales, dtype=np.uint16)  # [N/16, G, 16]
     m_rows, n_rows = x.shape[0], codes.shape[0] * 16
     y = np.zeros((m_rows, n_rows))
     for m in range(m_rows):
@@ -88,7 +89,7 @@ def gemv_bruteforce(x_bf16_bits, codes, scales, k):
                         part -= x[m, kk]
                     elif field != 0:
                         raise ValueError("invalid code")
-                total += float(s[n, g]) * part
+                total += float(f16_bits_to_f64(st[n // 16, g, n % 16])) * part
             y[m, n] = total
     return y
 

@@ -43,16 +43,17 @@ Dense format (N a multiple of 16, K a multiple of 128):
   4 (r mod 8) + 2 - 2 floor(r / 8), so fields r < 8 sit in bits 2-3 of nibble r
   and fields r >= 8 in bits 0-1 of nibble r - 8.  Field value: 0b00 -> 0,
   0b01 -> +1, 0b11 -> -1 (bit 0 = nonzero, bit 1 = negative); 0b10 is invalid.
-  scales[n][k // 128] fp16 bits.
+  scales[N / 16][K / 128][16] fp16 bits, tile-major like the codes: the scale
+  of row n and group g at [n // 16, g, n % 16] (tile_scales).
 Residual (two-plane) format: the dense format of both planes with their
   groups interleaved along K (interleave_planes), codes [N/16][2 K/128][128] and
-  scales [N][2 K/128].
+  scales [N/16][2 K/128][16].
 2:4 format:
   meta[n][q // 8] uint32 for quad q = k // 4: the nibble at bits 4 * (q % 8)
   holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1 the kept positions.
   signs[n][q // 16] uint32: bit q % 16 is set when the element at idx0 is
   negative, bit 16 + q % 16 when the element at idx1 is.
-  scales as dense.
+  scales[n][k // 128] fp16 bits, by row.
 """
 
 import numpy as np
@@ -137,17 +138,35 @@ def unpack_dense(codes, k):
     return np.where(f == 0b01, 1, np.where(f == 0b11, -1, 0)).astype(np.int8)
 
 
+def tile_scales(s16):
+    """Scale bits by row, [N, G], into the dense storage order [N/16, G, 16]:
+    the scale of row n and group g goes to [n // 16, g, n % 16]."""
+    s16 = np.asarray(s16)
+    n, g = s16.shape
+    if n % 16:
+        raise ValueError("N must be a multiple of 16")
+    return np.ascontiguousarray(s16.reshape(n // 16, 16, g).transpose(0, 2, 1))
+
+
+def untile_scales(t):
+    """Inverse of tile_scales: [N/16, G, 16] -> [N, G]."""
+    t = np.asarray(t)
+    if t.ndim != 3 or t.shape[2] != 16:
+        raise ValueError("dense scales must be [N/16, G, 16]")
+    return np.ascontiguousarray(t.transpose(0, 2, 1).reshape(t.shape[0] * 16, t.shape[1]))
+
+
 def quantize_dense(w):
     """Rotate 128x128 blocks, take absmean group scales, ternarise, pack.
 
-    Returns a dict with codes (uint32 [N/16, K/128, 128]), scales (fp16 bits uint16
-    [N, K/128]) and the float64 intermediates wr (W'), s (unrounded scales) and
-    t (int8 ternary values)."""
+    Returns a dict with codes (uint32 [N/16, K/128, 128]), scales (fp16 bits
+    uint16 [N/16, K/128, 16], tile_scales) and the float64 intermediates wr
+    (W'), s (unrounded scales, [N, K/128]) and t (int8 ternary values)."""
     w = _check_w(w)
     wr = rotate_blocks(w)
     s = absmean_scales(wr)
     t = ternarize(wr, s)
-    return {"codes": pack_dense(t), "scales": f64_to_f16_bits(s), "wr": wr, "s": s, "t": t}
+    return {"codes": pack_dense(t), "scales": tile_scales(f64_to_f16_bits(s)), "wr": wr, "s": s, "t": t}
 
 
 # ---------------------------------------------------------------- error-minimising variant
@@ -205,7 +224,8 @@ def quantize_dense_mse(w):
     s = S / j
     keep = a >= theta[..., None]
     t = (np.sign(wr) * keep.reshape(n, k)).astype(np.int8)
-    return {"codes": pack_dense(t), "scales": f64_to_f16_bits(s), "wr": wr, "s": s, "theta": theta, "t": t}
+    return {"codes": pack_dense(t), "scales": tile_scales(f64_to_f16_bits(s)), "wr": wr, "s": s, "theta": theta,
+            "t": t}
 
 
 def near_threshold_mse(wr, theta, rel=NEAR_REL):
@@ -226,7 +246,7 @@ def near_tie_mse(wr, rel=NEAR_REL):
 def interleave_planes(a, b):
     """Per-group interleave of two planes along the group axis (axis 1): the
     result's group 2 g is a's group g and group 2 g + 1 is b's.  Works for
-    codes [N/16, G, 128] and for scales [N, G]."""
+    codes [N/16, G, 128] and for scales [N/16, G, 16] (or [N, G])."""
     a = np.asarray(a)
     b = np.asarray(b)
     if a.shape != b.shape:
@@ -254,7 +274,8 @@ def quantize_dense_residual(w):
     group, t2 = +-1 where |d| > s2 / 2, fp16 scale.
 
     Storage (interleave_planes): codes [N/16][2 K/128][128] and scales
-    [N][2 K/128], where group 2 g + p holds plane p's group g (p = 0 first).
+    [N/16][2 K/128][16], where group 2 g + p holds plane p's group g (p = 0
+    first).
 
     Returns codes, scales, and wr, s1, t1, d, s2, t2 (float64 / int8)."""
     w = _check_w(w)
@@ -266,7 +287,8 @@ def quantize_dense_residual(w):
     s2 = absmean_scales(d)
     t2 = ternarize(d, s2)
     sc2 = f64_to_f16_bits(s2)
-    return {"codes": interleave_planes(pack_dense(t1), pack_dense(t2)), "scales": interleave_planes(sc1, sc2),
+    return {"codes": interleave_planes(pack_dense(t1), pack_dense(t2)),
+            "scales": interleave_planes(tile_scales(sc1), tile_scales(sc2)),
             "wr": wr, "s1": s1, "t1": t1, "d": d, "s2": s2, "t2": t2}
 
 

@@ -100,7 +100,8 @@ __global__ void __launch_bounds__(256, 2) gemm_ternary_kernel(const uint16_t* __
   // (k0 % 128) / 32 + (tid & 1) of the row's tile: two consecutive words
   const int wr = tid >> 1, wk = (tid & 1) * 32;
   const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + gb * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
-  const uint16_t* ssrc = scales + (n0 + wr) * G + gb;
+  // scales [N/16][G][16]: row n's scale of group g at ((n / 16) G + g) 16 + n % 16
+  const uint16_t* ssrc = scales + ((n0 + wr) >> 4) * G * 16 + gb * 16 + ((n0 + wr) & 15);
 
   // Activations come two K steps ahead through two register sets, one per
   // step parity (from L2: every column tile reads them; one step of products
@@ -125,7 +126,7 @@ __global__ void __launch_bounds__(256, 2) gemm_ternary_kernel(const uint16_t* __
     const int64_t g = std::min<int64_t>(gi, ge - gb - 1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) cw[slot][h] = *reinterpret_cast<const u32x2*>(wsrc + g * 128 + 64 * h);
-    sw[slot] = ssrc[g];
+    sw[slot] = ssrc[g * 16];
   };
   // the step in registers whose parity is `stage` into LDS stage `stage`
   auto lstore = [&](int stage, int slot, int h) {

@@ -17,9 +17,9 @@
 //     of batch row 4m + q.  Their sum times f16(scale) / 2 is the group's
 //     contribution.
 // Two kernels split the work:
-//   * batch 1 (staged): a wave owns one 16-row tile and a slice of K, stages its
-//     activation slice in LDS and issues every load of the slice before the
-//     first instruction that needs one;
+//   * batch 1 (staged): a wave owns one or two 16-row tiles and a slice of K,
+//     stages its activation slice in LDS and issues every load of the slice
+//     before the first instruction that needs one;
 //   * batch 2-16, and batch 1 past the staged slices (wide): a wave owns T
 //     consecutive tiles and a slice of K, walked
 //     in chunks, and applies each activation fragment to all T tiles.
@@ -44,11 +44,12 @@ constexpr int kMaxSegs = TB_MAX_SEGMENTS;
 // Staged path (batch 1, the activation slices of a workgroup fit in LDS).  Per
 // wave: the activation operand of its slice is copied into a private LDS area
 // with whole-wave 16-byte loads (one load moves two groups of one batch row),
-// the weight scales come in with one load per four groups (lane (i, q) fetches
-// group 4r + q of row i) and are handed to the other lanes with ds_bpermute,
-// and the codes with one load per group.  That is about CH + CH/2 + CH/4 + 1
-// loads for CH groups instead of 5 CH, which matters because the number of
-// loads a wave can keep in flight, not their size, bounds this kernel.
+// the weight scales come in with one load per eight groups of its tile and
+// are handed to the other lanes with ds_bpermute, and the codes with one load
+// per group.  That is about CH + CH/2 + CH/8 + 1 loads for CH groups instead of
+// 5 CH, which matters because the number of loads a wave can keep in flight,
+// not their size, bounds this kernel.  A wave may take two consecutive tiles
+// at its K slice, which share the staged activations.
 //
 // One launch can carry up to kMaxSegs independent products (segments), e.g.
 // the projections of one layer: workgroups are numbered across segments and
@@ -63,6 +64,7 @@ constexpr size_t kStagedMaxLds = 96 * 1024;
 // (1.5 % faster than 18 on the 27B down projection).
 constexpr int kStagedCH = 10;
 constexpr int kLongCH = 17;
+constexpr int64_t kTwoTileMin = 2048;  // tiles in a launch before a wave takes two
 
 struct StagedSeg {
   const uint8_t* act;
@@ -101,8 +103,10 @@ __device__ __forceinline__ StagedSeg pick_segment(const StagedSegs& a) {
   return seg == 0 ? r0 : a.s[seg];
 }
 
-// P code planes per segment (1, or 2 with the planes' groups interleaved)
-template <int CH, int BMAX, int P>
+// P code planes per segment (1, or 2 with the planes' groups interleaved); T
+// consecutive tiles per wave at the same K slice, which share the staged
+// activation slice
+template <int CH, int BMAX, int P, int T>
 __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs segs) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const StagedSeg sg = pick_segment(segs);
@@ -117,8 +121,9 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
   const int lg = __builtin_ctz((unsigned)KS);
   const int ks = w & (KS - 1);
   const int i = lane & 15, q = lane >> 4;
-  const int64_t nb = (int64_t)(blockIdx.x - sg.wg_begin) * (waves >> lg) + (w >> lg);
-  const bool live = nb < (int64_t)((uint64_t)N >> 4);
+  const int64_t nb0 = ((int64_t)(blockIdx.x - sg.wg_begin) * (waves >> lg) + (w >> lg)) * T;
+  const int64_t ntiles = (int64_t)((uint64_t)N >> 4);
+  const bool live = nb0 < ntiles;
   const int GA = (int)((uint64_t)K >> 7);  // activation groups per row
   const int G = GA * P;                    // code and scale groups per row
   const int gb = (G * ks) >> lg, ge = (G * (ks + 1)) >> lg;
@@ -126,14 +131,15 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
   // activation groups of the slice: code group g multiplies activation group g / P
   const int ab = gb / P, na = (ge - 1) / P - ab + 1;
   constexpr int kPairs = (CH + 1) / 2;
-  constexpr int kScaleRegs = (CH + 3) / 4;
   const int SG = P == 1 ? CH : segs.stage_groups;  // >= na
   const size_t region = (size_t)segs.bmax * SG * kStageBytes;
   unsigned char* st = smem + (size_t)w * region;  // [B][SG][512] values, then [B][SG][16] scales
   unsigned char* st_sc = st + (size_t)B * SG * 512;
   float* red = reinterpret_cast<float*>(smem + (size_t)waves * region);
 
-  float acc = 0.f;
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.f;
   if (live) {
     // 1. activation slice (issued first: it is waited for first)
     u32x4 av_st[BMAX][kPairs];
@@ -151,21 +157,29 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
     }
     // 2. weight scales, issued before the codes so that each product waits
     //    only for its own code group (a 27B layer's down projection at batch
-    //    1: 12.2 -> 11.9 us); lane (i, q) holds row i's scale of groups
-    //    gb + 4r + q
-    const uint16_t* sp = sg.scales + (size_t)(16 * nb + i) * G;
-    uint32_t sr[kScaleRegs];
-#pragma unroll
-    for (int r = 0; r < kScaleRegs; ++r) sr[r] = sp[min(gb + 4 * r + q, ge - 1)];
+    //    1: 12.2 -> 11.9 us).  Scales are tile-major, [N/16][G][16], so one
+    //    dword load brings 8 groups of the tile (lane l: group gb + 8 r + l / 8,
+    //    rows 2 (l % 8) and 2 (l % 8) + 1) from 256 contiguous bytes; with
+    //    scales by row, each load of 16 rows touched 10-16 cache lines (a 27B
+    //    layer at batch 1: 17.9 -> 16.4 us and 10.7 -> 9.7 us per launch).
     // 3. codes, one 8-byte load per lane and group (slots past the slice repeat
     //    its last group).  Non-temporal: read once, they need not displace the
     //    activations from the caches (batch 1 on a 27B layer's QKV + O +
     //    gate/up: 20.1 -> 19.45 us; down 12.6 -> 12.4 us)
-    const uint32_t* cp = sg.codes + (size_t)nb * G * 128 + 2 * lane;
-    u32x2 cw[CH];
+    constexpr int kSR = (CH + 7) / 8;
+    uint32_t sr[T][kSR];
+    u32x2 cw[T][CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j)
-      cw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128));
+    for (int t = 0; t < T; ++t) {
+      const int64_t nb = min(nb0 + t, ntiles - 1);  // tiles past the end repeat the last (never stored)
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(sg.scales + (size_t)nb * G * 16);
+#pragma unroll
+      for (int r = 0; r < kSR; ++r) sr[t][r] = sp[min((gb + 8 * r) * 8 + lane, ge * 8 - 1)];
+      const uint32_t* cp = sg.codes + (size_t)nb * G * 128 + 2 * lane;
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        cw[t][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cp + (size_t)min(gb + j, ge - 1) * 128));
+    }
     // 4. activation slice into this wave's LDS area (read back by other lanes of
     //    the same wave only; LDS operations of a wave complete in order)
 #pragma unroll
@@ -182,39 +196,48 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
 
     // 5. the products: lane (i, q) feeds A rows of batch i / 4, sub-row i % 4.
     //    Rows of batches >= B only reach output rows that are never stored, so
-    //    those lanes read the last batch row instead of branching.
+    //    those lanes read the last batch row instead of branching.  The scale
+    //    of row i and group gb + j sits in lane 8 (j % 8) + i / 2, half i % 2.
     const int bp = min(i >> 2, B - 1);
     const unsigned char* a_src = st + (size_t)bp * SG * 512 + ((i & 3) * 4 + q) * 16;
     const unsigned char* a_sc = st_sc + (size_t)bp * SG * 16 + (i & 3) * 4 + q;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      // staged activation group of slot j (slots past the slice repeat the last one)
-      const int aj = P == 1 ? j : (min(gb + j, ge - 1) >> 1) - ab;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(a_src + aj * 512);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(a_src + aj * 512 + 256);
-      const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int as = a_sc[aj * 16];
-      const int sbits = __builtin_amdgcn_ds_bpermute((i + 16 * (j & 3)) * 4, (int)sr[j >> 2]);
-      const float s = f16_bits_to_f32((uint32_t)sbits & 0xFFFFu) * 0.5f;
-      const uint32_t w0 = cw[j][0], w1 = cw[j][1];
-      const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
-                        (int)((w1 << 2) & 0xCCCCCCCCu)};
-      const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
-      const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, zero, 0, 4, 0, as, 0, 127);
-      keep_sources_past(d, av, bw);  // the destination must not reuse the sources' registers
-      const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc);
-      acc = j < n ? a : acc;  // slots past the slice add nothing
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        // staged activation group of slot j (slots past the slice repeat the last one)
+        const int aj = P == 1 ? j : (min(gb + j, ge - 1) >> 1) - ab;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(a_src + aj * 512);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(a_src + aj * 512 + 256);
+        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const int as = a_sc[aj * 16];
+        const int sbits = __builtin_amdgcn_ds_bpermute(((j & 7) * 8 + (i >> 1)) * 4, (int)sr[t][j >> 3]);
+        const float s = f16_bits_to_f32(((uint32_t)sbits >> ((i & 1) * 16)) & 0xFFFFu) * 0.5f;
+        const uint32_t w0 = cw[t][j][0], w1 = cw[t][j][1];
+        const i32x4 bw = {(int)(w0 & 0xCCCCCCCCu), (int)((w0 << 2) & 0xCCCCCCCCu), (int)(w1 & 0xCCCCCCCCu),
+                          (int)((w1 << 2) & 0xCCCCCCCCu)};
+        const i32x8 b8 = {bw[0], bw[1], bw[2], bw[3], 0, 0, 0, 0};  // fp4 uses the low four registers
+        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b8, zero, 0, 4, 0, as, 0, 127);
+        keep_sources_past(d, av, bw);  // the destination must not reuse the sources' registers
+        const float a = __builtin_fmaf(s, (d[0] + d[1]) + (d[2] + d[3]), acc[t]);
+        acc[t] = j < n ? a : acc[t];  // slots past the slice add nothing
+      }
     }
   }
 
   if (KS > 1) {
-    red[w * 64 + lane] = acc;
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[(w * T + t) * 64 + lane] = acc[t];
     __syncthreads();
     if (ks != 0) return;
-    for (int u = 1; u < KS; ++u) acc += red[(w + u) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      for (int u = 1; u < KS; ++u) acc[t] += red[((w + u) * T + t) * 64 + lane];
   }
-  if (live && q < B) sg.y[(size_t)q * N + 16 * nb + i] = acc;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    if (nb0 + t < ntiles && q < B) sg.y[(size_t)q * N + 16 * (nb0 + t) + i] = acc[t];
 }
 
 // Wide path (B > 4, or a K too long for the staged slices).  A batch quad's
@@ -296,7 +319,8 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs seg
     const unsigned char* cbase = reinterpret_cast<const unsigned char*>(sg.codes + (size_t)t0 * G * 128);
     const unsigned char* sbase = reinterpret_cast<const unsigned char*>(sg.scales + (size_t)16 * t0 * G);
     const uint32_t c_stride = (uint32_t)G * 512, s_stride = (uint32_t)G * 32;  // bytes per tile
-    const uint32_t c_lane = (uint32_t)lane * 8, s_lane = (uint32_t)i * G * 2;
+    // scales [N/16][G][16]: lane (i, q) reads row i of group c + q, 32 bytes per group
+    const uint32_t c_lane = (uint32_t)lane * 8, s_lane = (uint32_t)i * 2;
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int c = gb; c < ge; c += CH) {
@@ -325,7 +349,7 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs seg
       const uint32_t gq = (uint32_t)min(c + q, ge - 1);
 #pragma unroll
       for (int t = 0; t < T; ++t)
-        sr[t] = *reinterpret_cast<const uint16_t*>(sbase + (t * s_stride + s_lane + gq * 2));
+        sr[t] = *reinterpret_cast<const uint16_t*>(sbase + (t * s_stride + s_lane + gq * 32));
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
 #pragma unroll
@@ -506,12 +530,19 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
   // a slice of at most ch code groups spans at most ch activation groups with
   // one plane, ch / 2 + 1 with two
   const int stage_groups = planes == 1 ? ch : ch / 2 + 1;
-  const size_t lds = (size_t)waves * bmax * stage_groups * kStageBytes + (size_t)waves * 64 * sizeof(float);
+  // Tiles per wave: 2 when every segment takes the short slices and the launch
+  // has many tiles (one staged activation slice then serves two tiles; a 27B
+  // layer's QKV + O + gate/up at batch 1: 16.4 -> 15.9 us), else 1.  A tile's
+  // sum does not depend on it.
+  int64_t all_tiles = 0;
+  for (int c = 0; c < count; ++c) all_tiles += segs[c].N / 16;
+  const int LT = ch == kStagedCH && all_tiles >= kTwoTileMin ? 2 : 1;
+  const size_t lds = (size_t)waves * bmax * stage_groups * kStageBytes + (size_t)waves * LT * 64 * sizeof(float);
   if (staged && lds <= kStagedMaxLds) {
     for (int c = 0; c < count; ++c) {
       const int64_t kc = segs[c].K * segs[c].planes;
       const int ks = staged_slices(kc, segment_ch(kc));
-      const int64_t tiles = segs[c].N / 16, per_wg = waves / ks;
+      const int64_t tiles = segs[c].N / 16, per_wg = waves / ks * LT;
       st.s[c] = StagedSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
                           (int)segs[c].B, ks, wg, 0};
       wg += (int)((tiles + per_wg - 1) / per_wg);
@@ -520,7 +551,13 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
     st.bmax = bmax;
     st.stage_groups = stage_groups;
     const dim3 grid((unsigned)wg), block(64 * waves);
-#define TB_STAGED(CH_, BMAX_, P_) hipLaunchKernelGGL((gemv_staged_kernel<CH_, BMAX_, P_>), grid, block, lds, stream, st)
+#define TB_STAGED(CH_, BMAX_, P_)                                                                \
+  do {                                                                                           \
+    if (LT == 2)                                                                                 \
+      hipLaunchKernelGGL((gemv_staged_kernel<CH_, BMAX_, P_, 2>), grid, block, lds, stream, st); \
+    else                                                                                         \
+      hipLaunchKernelGGL((gemv_staged_kernel<CH_, BMAX_, P_, 1>), grid, block, lds, stream, st); \
+  } while (0)
     // batch 1 only: kernels exist for 10 and 17 groups per wave
     if (planes == 1) {
       if (ch == kLongCH)

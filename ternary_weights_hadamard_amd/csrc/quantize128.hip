@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
       if (half == 0) {
         const uint32_t h16 = f32_to_f16_bits(s);
         if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
-        scales[grow * kblocks + bk] = (uint16_t)h16;
+        scales[((grow >> 4) * kblocks + bk) * 16 + (grow & 15)] = (uint16_t)h16;
       }
     } else if constexpr (RULE == kAbsmean || RULE == kResidual) {
       // one plane, or two with their groups interleaved (group 2 bk + p)
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
         const uint32_t h16 = f32_to_f16_bits(s);
         if (half == 0) {
           if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
-          scales[grow * kPlanes * kblocks + gcol] = (uint16_t)h16;
+          scales[((grow >> 4) * kPlanes * kblocks + gcol) * 16 + (grow & 15)] = (uint16_t)h16;
         }
         if (p + 1 < kPlanes) {
           // the residual against the stored scale, in units of T: T - 128 f16(s) t

@@ -82,7 +82,15 @@ def random_code_words(n, k, seed, p=(0.35, 0.30, 0.35)):
 
 
 def random_scales_f16(n, k, seed, lo=0.005, hi=0.05):
-    """fp16 bit patterns [n, k/128] of U(lo, hi) draws."""
+    """fp16 bit patterns of U(lo, hi) draws in the dense storage shape
+    [n/16, k/128, 16] (one scale per row and 128-group, tile-major; the draws
+    are i.i.d., so no assignment of draws to rows is assumed)."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(lo, hi, size=(n // 16, k // 128, 16)).astype(np.float16).view(np.uint16)
+
+
+def random_scales24_f16(n, k, seed, lo=0.005, hi=0.05):
+    """fp16 bit patterns [n, k/128] of U(lo, hi) draws (the 2:4 format's scales, by row)."""
     rng = np.random.default_rng(seed)
     return rng.uniform(lo, hi, size=(n, k // 128)).astype(np.float16).view(np.uint16)
 
@@ -120,6 +128,14 @@ def torch_code_words(n, k, gen, device, p=(0.35, 0.30, 0.35)):
 
 
 def torch_scales_f16(n, k, gen, device, lo=0.005, hi=0.05):
+    """U(lo, hi) fp16 scales in the dense storage shape [n/16, k/128, 16]."""
+    import torch
+
+    return (lo + (hi - lo) * torch.rand((n // 16, k // 128, 16), generator=gen, device=device)).to(torch.float16)
+
+
+def torch_scales24_f16(n, k, gen, device, lo=0.005, hi=0.05):
+    """U(lo, hi) fp16 scales [n, k/128] (the 2:4 format, by row)."""
     import torch
 
     return (lo + (hi - lo) * torch.rand((n, k // 128), generator=gen, device=device)).to(torch.float16)

@@ -12,7 +12,9 @@ Dtypes on the Python side (bit patterns are what matter):
   codes              torch.int32 (uint32 bit patterns): dense [N/16, K/128, 128],
                      2:4 sign plane [N, K/64]
   meta               torch.int32 [N, K/32]
-  scales             torch.float16 (fp16 bit patterns) [N, K/128]
+  scales             torch.float16 (fp16 bit patterns): dense formats
+                     [N/16, K/128, 16] (tile-major, two-plane [N/16, 2K/128, 16]),
+                     2:4 [N, K/128]
 """
 
 import ctypes
@@ -177,7 +179,8 @@ def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, er
     if meta is None and fmt == TB_FMT_24:
         meta = torch.empty((n, k // 32), dtype=torch.int32, device=dev)
     if scales is None:
-        scales = torch.empty((n, planes * k // 128), dtype=torch.float16, device=dev)
+        shape = (n // 16, planes * k // 128, 16) if fmt != TB_FMT_24 else (n, k // 128)
+        scales = torch.empty(shape, dtype=torch.float16, device=dev)
     _dev(codes, meta, scales, err_flag)
     _check(lib().tb_quantize_pack(_p(w), n, k, int(fmt), _p(codes), _p(meta), _p(scales), _p(err_flag),
                                   _stream(stream)), "tb_quantize_pack")
@@ -207,9 +210,16 @@ def _act8_operand(act, batch, k, where):
                          f"{tb_act8_bytes(batch, k)} bytes (got {act.dtype}, {act.numel()} elements)")
 
 
+def _dense_n(scales):
+    """Output rows of dense-format scales [N/16, G, 16]."""
+    if scales.dim() != 3 or scales.shape[2] != 16:
+        raise ValueError(f"dense scales must be [N/16, G, 16] (got {tuple(scales.shape)})")
+    return scales.shape[0] * 16
+
+
 def _gemv(fn, where, x, codes, scales, k, batch, y, workspace, stream):
     _dev(x, codes, scales)
-    n = scales.shape[0]
+    n = _dense_n(scales)
     if x.dtype == torch.uint8:
         _act8_operand(x, batch, k, where)
         b, dt, wbytes = int(batch), TB_ACT8, 0
@@ -245,8 +255,7 @@ def tb_ternary_gemv_noalloc(x, codes, scales, y, stream=None):
     library's own device array for the encoded activations: nothing is
     allocated (the caller passes y).  Calls that may overlap on one GPU race."""
     _dev(x, codes, scales, y)
-    n, g = scales.shape
-    k = g * 128
+    n, k = _dense_n(scales), scales.shape[1] * 128
     if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"tb_ternary_gemv_noalloc: x must be bf16 [B, {k}] (got {x.dtype} {tuple(x.shape)})")
     if y.dtype != torch.float32 or tuple(y.shape) != (x.shape[0], n):
@@ -273,7 +282,7 @@ def tb_ternary_gemv_multi(segments, stream=None):
         act, codes, scales, batch, y = seg[:5]
         planes = int(seg[5]) if len(seg) > 5 else 1
         _dev(act, codes, scales, y)
-        n, g = scales.shape
+        n, g = _dense_n(scales), scales.shape[1]
         k = g // max(planes, 1) * 128
         _act8_operand(act, int(batch), k, "tb_ternary_gemv_multi")
         arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n, k, y.data_ptr(),
@@ -297,7 +306,7 @@ def tb_ternary_gemm(x, codes, scales, y=None, out_dtype=torch.bfloat16, stream=N
     """Y[m, n] = sum_g scale[n, g] * sum_k t[n, k] x[m, k]; x bf16 [M, K], Y bf16 or fp32."""
     _dev(x, codes, scales)
     m, k = x.shape
-    n = scales.shape[0]
+    n = _dense_n(scales)
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
     _dev(y)
@@ -316,7 +325,7 @@ def tb_ternary_gemm_splitk(x, codes, scales, y=None, out_dtype=torch.bfloat16, w
     bytes (allocated here when None)."""
     _dev(x, codes, scales)
     m, k = x.shape
-    n = scales.shape[0]
+    n = _dense_n(scales)
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
     if workspace is None:
@@ -335,7 +344,7 @@ def tb_ternary_gemm_rotated(x, codes, scales, y=None, out_dtype=torch.bfloat16, 
     tb_ternary_gemm_splitk."""
     _dev(x, codes, scales)
     m, k = x.shape
-    n = scales.shape[0]
+    n = _dense_n(scales)
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
     _dev(y, workspace)

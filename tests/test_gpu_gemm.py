@@ -37,7 +37,7 @@ def test_gemm_full_size_sampled(k, n):
         rs = np.sort(np.random.default_rng(5).choice(m, 64, replace=False))
         tiles = np.sort(np.random.default_rng(6).choice(n // 16, 6, replace=False))
         cs = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
-        ref = oracle.matvec.gemm(x[rs], codes[tiles], scales[cs], k)
+        ref = oracle.matvec.gemm(x[rs], codes[tiles], scales[tiles], k)
         assert_close(y[np.ix_(rs, cs)], ref, f"gemm {m}x{n}x{k} {out} (64 rows x 6 tiles sampled)",
                      out_bf16=out == torch.bfloat16)
         del y
@@ -47,7 +47,7 @@ def test_gemm_exact_small_integers_and_gemv_agreement():
     m, n, k = 33, 256, 1024
     codes = synth.random_code_words(n, k, seed=50)
     x = synth.small_int_bf16((m, k), seed=51)
-    sc = (2.0 ** np.random.default_rng(52).integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    sc = (2.0 ** np.random.default_rng(52).integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
     y = tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(sc), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
@@ -69,7 +69,7 @@ def test_gemm_tiny_and_wide_range_activations_exact():
     xv = mant.astype(np.float64) * np.exp2(e.astype(np.float64))
     x = oracle.numerics.f64_to_bf16_bits(xv)
     assert np.array_equal(oracle.numerics.bf16_bits_to_f64(x), xv)
-    sc = (2.0 ** rng.integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    sc = (2.0 ** rng.integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
     y = tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(sc), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
@@ -119,7 +119,7 @@ def test_gemm_splitk_mid_batch_sampled(m, n, k):
     y = host_f64(tb.tb_ternary_gemm_splitk(bf16_dev(x), u32_dev(codes), f16_dev(scales), out_dtype=torch.float32))
     tiles = np.sort(np.random.default_rng(7).choice(n // 16, 6, replace=False))
     cs = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
-    ref = oracle.matvec.gemm(x, codes[tiles], scales[cs], k)
+    ref = oracle.matvec.gemm(x, codes[tiles], scales[tiles], k)
     assert_close(y[:, cs], ref, f"split-K gemm {m}x{n}x{k} ({parts} splits, 6 tiles sampled)")
 
 
@@ -129,7 +129,7 @@ def test_gemm_splitk_exact_and_fallbacks():
     m, n, k = 48, 384, 2048
     codes = u32_dev(synth.random_code_words(n, k, seed=63))
     x_bits = synth.small_int_bf16((m, k), seed=64)
-    sc = (2.0 ** np.random.default_rng(65).integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    sc = (2.0 ** np.random.default_rng(65).integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
     x, scales = bf16_dev(x_bits), f16_dev(sc)
     ref = oracle.matvec.gemm(x_bits, synth.random_code_words(n, k, seed=63), sc, k)
     parts = tb.tb_ternary_gemm_splitk_workspace(m, n, k) // (m * n * 4)
@@ -213,5 +213,5 @@ def test_gemm_rotated_full_size_sampled():
     blocks = np.sort(np.random.default_rng(9).choice(n // 128, 2, replace=False))
     tiles = (8 * blocks[:, None] + np.arange(8)[None, :]).ravel()
     cs = (128 * blocks[:, None] + np.arange(128)[None, :]).ravel()
-    ref = _rotate_rows(oracle.matvec.gemm(x[rs], codes[tiles], scales[cs], k))
+    ref = _rotate_rows(oracle.matvec.gemm(x[rs], codes[tiles], scales[tiles], k))
     assert_close(y[np.ix_(rs, cs)], ref, "rotated gemm (48 rows x 2 column blocks sampled)", out_bf16=True)

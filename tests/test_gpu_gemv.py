@@ -46,7 +46,7 @@ def test_gemv_full_size_sampled_tiles(n, k, b):
     y = _gemv(x, codes, scales)
     tiles = np.sort(np.random.default_rng(1).choice(n // 16, 16, replace=False))
     rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
-    ref = oracle.matvec.gemv(x, codes[tiles], scales[rows], k)
+    ref = oracle.matvec.gemv(x, codes[tiles], scales[tiles], k)
     assert_close(y[:, rows], ref, f"gemv {n}x{k} B={b} (16 sampled tiles)")
     assert np.max(np.abs(y[:, rows] - ref)) <= 1e-5 * np.max(np.abs(ref))
 
@@ -91,7 +91,7 @@ def test_gemv_exact_small_integers(b):
     n, k = 256, 1280
     codes = synth.random_code_words(n, k, seed=5)
     x = synth.small_int_bf16((b, k), seed=6)
-    sc = (2.0 ** np.random.default_rng(7).integers(-6, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    sc = (2.0 ** np.random.default_rng(7).integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
     y = _gemv(x, codes, sc)
     ref = oracle.matvec.gemv(x, codes, sc, k)
     assert np.array_equal(y, ref)
@@ -101,7 +101,7 @@ def test_gemv_special_patterns():
     n, k = 128, 256
     x = synth.gaussian_bf16((1, k), seed=9)
     xv = oracle.numerics.bf16_bits_to_f64(x)
-    ones_scale = np.full((n, k // 128), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+    ones_scale = np.full((n // 16, k // 128, 16), np.float16(1.0).view(np.uint16), dtype=np.uint16)
     t = np.ones((n, k), dtype=np.int8)
     y = _gemv(x, oracle.quant.pack_dense(t), ones_scale)
     assert np.allclose(y, xv.sum(), rtol=1e-5)
@@ -217,7 +217,7 @@ def test_act8_from_fwht_equals_prep_of_rotated_bf16():
 def test_gemv24_small_matches_oracle(n, k, b):
     say(f"gemv24 N={n} K={k} B={b}")
     meta, signs = synth.random_24(n, k, seed=n + k)
-    scales = synth.random_scales_f16(n, k, seed=3)
+    scales = synth.random_scales24_f16(n, k, seed=3)
     x = synth.gaussian_bf16((b, k), seed=4)
     y = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(scales))
     torch.cuda.synchronize()
@@ -230,7 +230,7 @@ def test_gemv24_full_size_sampled():
     n, k = 17408, 5120
     say("gemv24 full 17408x5120 B=1")
     meta, signs = synth.random_24(n, k, seed=30)
-    scales = synth.random_scales_f16(n, k, seed=31)
+    scales = synth.random_scales24_f16(n, k, seed=31)
     x = synth.gaussian_bf16((1, k), seed=32)
     y = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(scales)).cpu().numpy()
     rows = np.sort(np.random.default_rng(3).choice(n, 256, replace=False))
@@ -246,7 +246,7 @@ def test_gemv24_exact_and_dense_equivalence():
     y24 = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(sc))
     i0, i1, n0, n1 = oracle.quant.unpack_24(meta, signs, k)
     dense = oracle.quant.pack_dense(oracle.quant.dense_from_24(i0, i1, n0, n1))
-    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(sc), x.shape[0])
+    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(oracle.quant.tile_scales(sc)), x.shape[0])
     torch.cuda.synchronize()
     ref = oracle.matvec.gemv24(x, meta, signs, sc, k)
     assert np.array_equal(y24.cpu().numpy().astype(np.float64), ref)
@@ -340,7 +340,7 @@ def test_grouped_27b_layer_wide_batch(b):
         n = codes.shape[0] * 16
         tiles = np.sort(rng.choice(n // 16, 16, replace=False))
         rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
-        ref = oracle.matvec.gemv(x, codes[tiles], scales[rows], k)
+        ref = oracle.matvec.gemv(x, codes[tiles], scales[tiles], k)
         got = y.cpu().numpy().astype(np.float64)[:, rows]
         assert_close(got, ref, f"27B segment {c} B={b} (16 sampled tiles)")
         assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
@@ -392,7 +392,7 @@ def test_gemv_resid_full_size_sampled_tiles(n, k, b):
     y = _gemv_resid(x, codes, scales)
     tiles = np.sort(np.random.default_rng(2).choice(n // 16, 12, replace=False))
     rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
-    ref = oracle.matvec.gemv_residual(x, codes[tiles], scales[rows], k)
+    ref = oracle.matvec.gemv_residual(x, codes[tiles], scales[tiles], k)
     assert_close(y[:, rows], ref, f"two-plane gemv {n}x{k} B={b} (12 sampled tiles)")
     assert np.max(np.abs(y[:, rows] - ref)) <= 1e-5 * np.max(np.abs(ref))
 
@@ -402,7 +402,7 @@ def test_gemv_resid_exact_small_integers(b):
     n, k = 256, 1280
     codes = synth.random_code_words(n, 2 * k, seed=15)
     x = synth.small_int_bf16((b, k), seed=16)
-    sc = (2.0 ** np.random.default_rng(17).integers(-6, 2, size=(n, 2 * k // 128))).astype(np.float16).view(np.uint16)
+    sc = (2.0 ** np.random.default_rng(17).integers(-6, 2, size=(n // 16, 2 * k // 128, 16))).astype(np.float16).view(np.uint16)
     y = _gemv_resid(x, codes, sc)
     assert np.array_equal(y, oracle.matvec.gemv_residual(x, codes, sc, k))
 

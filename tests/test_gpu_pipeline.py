@@ -38,7 +38,7 @@ def test_single_layer_pipeline_1024():
     # weight NMSE of the GPU's codes and fp16 scales against W', and of the same
     # absmean rule applied to the unrotated W (reported; the oracle test pins both)
     t_gpu = oracle.quant.unpack_dense(host_u32(codes), k)
-    s_gpu = oracle.numerics.f16_bits_to_f64(host_u16(scales))
+    s_gpu = oracle.numerics.f16_bits_to_f64(oracle.quant.untile_scales(host_u16(scales)))
     nmse_rot = np.sum((t_gpu * np.repeat(s_gpu, 128, axis=1) - ref["wr"]) ** 2) / np.sum(ref["wr"] ** 2)
     w64 = w.astype(np.float64)
     s_raw = oracle.quant.absmean_scales(w64)

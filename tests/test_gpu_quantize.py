@@ -55,7 +55,7 @@ def test_full_layer_sampled_blocks():
         wb = w[128 * a:128 * (a + 1), 128 * b:128 * (b + 1)]
         ref = oracle.quant.quantize_dense(wb.astype(np.float64))
         cb = codes[8 * a:8 * (a + 1), b:b + 1, :].contiguous()
-        sb = scales[128 * a:128 * (a + 1), b:b + 1].contiguous()
+        sb = scales[8 * a:8 * (a + 1), b:b + 1].contiguous()
         check_dense_codes(cb, sb, ref, 128, f"block ({a}, {b})")
 
 
@@ -70,7 +70,7 @@ def test_closed_form_blocks():
     check_dense_codes(codes, scales, ref, 512, "closed forms")
     t = oracle.quant.unpack_dense(host_u32(codes), 512)
     assert np.array_equal(t, ref["t"])
-    s = host_u16(scales)
+    s = oracle.quant.untile_scales(host_u16(scales))
     assert np.all(s[:128, 0] == np.float16(4.0 / 128).view(np.uint16))
     assert np.all(s[128:, 1] == np.float16(1.0 / 128).view(np.uint16))
     assert s[0, 2] == np.float16(0.375).view(np.uint16) and np.all(s[1:128, 2] == 0)
@@ -85,7 +85,7 @@ def test_tie_at_half_scale():
     codes, _, scales = _quant(w)
     t = oracle.quant.unpack_dense(host_u32(codes), 128)
     assert np.all(t[0, :48] == 1) and np.all(t[0, 48:] == 0)
-    assert host_u16(scales)[0, 0] == np.float16(0.5).view(np.uint16)
+    assert host_u16(scales)[0, 0, 0] == np.float16(0.5).view(np.uint16)
 
 
 def test_error_flags():
@@ -109,7 +109,7 @@ def test_output_canaries():
     cb = torch.full((n * k // 16 + 8,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
     sb = torch.full((n * k // 128 + 16,), -3.0, dtype=torch.float16, device=DEV)
     codes = cb[4:4 + n * k // 16].view(n // 16, k // 128, 128)
-    scales = sb[8:8 + n * k // 128].view(n, k // 128)
+    scales = sb[8:8 + n * k // 128].view(n // 16, k // 128, 16)
     tb.tb_quantize_pack(f32_dev(w), codes=codes, scales=scales)
     torch.cuda.synchronize()
     assert torch.all(cb[:4] == 0x5A5A5A5A) and torch.all(cb[4 + n * k // 16:] == 0x5A5A5A5A)
@@ -172,8 +172,8 @@ def _check_minerr(codes, scales, w, what):
     hi_drop = np.where(~kept & (a > 0), a, 0).max(axis=2)
     shaped = lo_kept >= hi_drop * (1 - 1e-5)
     near_opt = obj >= best * (1 - 1e-5)
-    sg = host_u16(scales).astype(np.int64)
-    sr = ref["scales"].astype(np.int64)
+    sg = oracle.quant.untile_scales(host_u16(scales)).astype(np.int64)
+    sr = oracle.quant.untile_scales(ref["scales"]).astype(np.int64)
     s_ok = np.abs(sg - sr) <= 1
     # in near-tie groups the scale belongs to the GPU's own kept set
     own = oracle.numerics.f64_to_f16_bits(np.where(j > 0, S / np.maximum(j, 1), 0.0)).astype(np.int64)
@@ -202,13 +202,13 @@ def test_minerr_closed_forms_and_lower_error_than_absmean():
     w[5, 130] = 3.0                                       # a spike: lossless
     codes, _, scales = _quant(w, fmt=tb.TB_FMT_DENSE_MINERR)
     ref = _check_minerr(codes, scales, w, "min-error closed forms")
-    s = host_u16(scales)
+    s = oracle.quant.untile_scales(host_u16(scales))
     assert np.all(s[:128, 0] == 0) and np.all(host_u32(codes)[:8, 0] == 0)
     # reconstruction error in the rotated domain: never above the absmean rule's
     ca, _, sa = _quant(w)
     wr = ref["wr"]
     f16 = lambda b: b.view(np.float16).astype(np.float64)
-    err = lambda t, sc: np.sum((wr - np.repeat(f16(host_u16(sc)), 128, axis=1) * t) ** 2)
+    err = lambda t, sc: np.sum((wr - np.repeat(f16(oracle.quant.untile_scales(host_u16(sc))), 128, axis=1) * t) ** 2)
     e_min = err(oracle.quant.unpack_dense(host_u32(codes), 512), scales)
     e_abs = err(oracle.quant.unpack_dense(host_u32(ca), 512), sa)
     say(f"  squared error: min-error rule {e_min:.4e}, absmean rule {e_abs:.4e}")
@@ -231,8 +231,8 @@ def _check_resid(codes, scales, w, what):
     n, k = w.shape
     g = k // 128
     c1, c2 = oracle.quant.split_planes(host_u32(codes))
-    sc1, sc2 = (p.astype(np.int64) for p in oracle.quant.split_planes(host_u16(scales)))
-    r1, r2 = (p.astype(np.int64) for p in oracle.quant.split_planes(ref["scales"]))
+    sc1, sc2 = (oracle.quant.untile_scales(p).astype(np.int64) for p in oracle.quant.split_planes(host_u16(scales)))
+    r1, r2 = (oracle.quant.untile_scales(p).astype(np.int64) for p in oracle.quant.split_planes(ref["scales"]))
     t1 = oracle.quant.unpack_dense(c1, k)
     t2 = oracle.quant.unpack_dense(c2, k)
     wr = ref["wr"]
@@ -265,7 +265,7 @@ def test_resid_matches_oracle(n, k, seed):
     w = synth.single_layer_weights(n, k, seed=seed) if seed == 0 else synth.stack_weights(n, k, seed=seed)
     say(f"quantize two-plane {n}x{k} seed {seed}")
     codes, meta, scales = _quant(w, fmt=tb.TB_FMT_DENSE_RESID)
-    assert meta is None and tuple(codes.shape) == (n // 16, 2 * k // 128, 128) and tuple(scales.shape) == (n, 2 * k // 128)
+    assert meta is None and tuple(codes.shape) == (n // 16, 2 * k // 128, 128) and tuple(scales.shape) == (n // 16, 2 * k // 128, 16)
     _, t1, t2, sc1, sc2 = _check_resid(codes, scales, w, f"two-plane {n}x{k}")
     # plane 1 is the one-plane format, word for word
     c_one, _, s_one = _quant(w)

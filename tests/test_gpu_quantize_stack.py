@@ -40,7 +40,7 @@ def test_stack_layer0_in_full(j):
     near = differ = 0
     for r0 in range(0, n, SLAB):
         ref = oracle.quant.quantize_dense(w[r0:r0 + SLAB].astype(np.float64))
-        a, b = check_dense_codes(codes[r0 // 16:(r0 + SLAB) // 16], scales[r0:r0 + SLAB], ref, k,
+        a, b = check_dense_codes(codes[r0 // 16:(r0 + SLAB) // 16], scales[r0 // 16:(r0 + SLAB) // 16], ref, k,
                                  f"layer 0 {name} rows {r0}..{r0 + SLAB - 1}")
         near, differ = near + a, differ + b
     say(f"  layer 0 {name}: {near} near-threshold elements of {n * k} ({near / (n * k):.2e} per element), "
@@ -62,7 +62,7 @@ def test_stack_layer_sampled_blocks(layer):
             a, b = divmod(int(blk), gk)
             ref = oracle.quant.quantize_dense(w[128 * a:128 * (a + 1), 128 * b:128 * (b + 1)].astype(np.float64))
             cb = codes[8 * a:8 * (a + 1), b:b + 1, :].contiguous()
-            sb = scales[128 * a:128 * (a + 1), b:b + 1].contiguous()
+            sb = scales[8 * a:8 * (a + 1), b:b + 1].contiguous()
             x, y = check_dense_codes(cb, sb, ref, 128, f"layer {layer} {name} block ({a}, {b})")
             near, differ, blocks = near + x, differ + y, blocks + 1
     say(f"  layer {layer}: {blocks} sampled blocks, {near} near-threshold elements, {differ} of them differ")

@@ -49,7 +49,7 @@ def test_gemv_exact_integer_case():
     codes = synth.random_code_words(n, k, seed=1)
     x = synth.small_int_bf16((2, k), seed=2)
     sc_exp = np.random.default_rng(3).integers(-6, 1, size=(n, k // 128))
-    scales = (2.0 ** sc_exp).astype(np.float16).view(np.uint16)
+    scales = q.tile_scales((2.0 ** sc_exp).astype(np.float16).view(np.uint16))
     y = mv.gemv(x, codes, scales, k)
     t = _t_from_codes(codes, k)
     xi = nu.bf16_bits_to_f64(x).astype(np.int64)
@@ -67,7 +67,7 @@ def test_all_plus_one_is_row_sum_and_one_hot_is_gather():
     x = synth.gaussian_bf16((1, k), seed=5)
     xv = nu.bf16_bits_to_f64(x)
     one = np.float16(1.0).view(np.uint16)
-    ones = np.full((n, k // 128), one, dtype=np.uint16)
+    ones = np.full((n // 16, k // 128, 16), one, dtype=np.uint16)
     t = np.ones((n, k), dtype=np.int8)
     y = mv.gemv(x, q.pack_dense(t), ones, k)
     assert np.allclose(y, xv.sum(), rtol=1e-14, atol=1e-12)
@@ -94,14 +94,16 @@ def test_dequantised_matrix_matches_independent_decode():
     codes = synth.random_code_words(n, k, seed=12)
     scales = synth.random_scales_f16(n, k, seed=13)
     wq = mv.dequant_dense(codes, scales, k)
-    s = scales.view(np.float16).astype(np.float64)
+    # the scale of row r and group g sits at [r // 16, g, r % 16]
+    s = np.array([[scales[r // 16, g, r % 16] for g in range(k // 128)] for r in range(n)], dtype=np.uint16)
+    s = s.view(np.float16).astype(np.float64)
     assert np.array_equal(wq, _t_from_codes(codes, k) * np.repeat(s, 128, axis=1))
 
 
 @pytest.mark.parametrize("n,k,b", [(128, 128, 1), (128, 256, 2)])
 def test_gemv24_equals_bruteforce_and_dense_expansion(n, k, b):
     meta, signs = synth.random_24(n, k, seed=n + k)
-    scales = synth.random_scales_f16(n, k, seed=14)
+    scales = synth.random_scales24_f16(n, k, seed=14)
     x = synth.gaussian_bf16((b, k), seed=15)
     y = mv.gemv24(x, meta, signs, scales, k)
     yb = mv.gemv24_bruteforce(x, meta, signs, scales, k)
@@ -109,7 +111,7 @@ def test_gemv24_equals_bruteforce_and_dense_expansion(n, k, b):
     # the 2:4 encoding expanded to dense ternary codes gives the same product exactly
     idx0, idx1, neg0, neg1 = q.unpack_24(meta, signs, k)
     dense_codes = q.pack_dense(q.dense_from_24(idx0, idx1, neg0, neg1))
-    assert np.array_equal(mv.gemv(x, dense_codes, scales, k), y)
+    assert np.array_equal(mv.gemv(x, dense_codes, q.tile_scales(scales), k), y)
     # exactly two nonzeros per quad
     t = q.dense_from_24(idx0, idx1, neg0, neg1)
     assert np.all(np.count_nonzero(t.reshape(n, k // 4, 4), axis=2) == 2)
@@ -131,8 +133,8 @@ def test_gemv_residual_two_plane_cases():
     wr = np.where(rng.random((n, k)) < 0.5, 1.0, 0.5) * np.where(rng.random((n, 1)) < 0.5, 1.0, -1.0)
     t1 = np.sign(wr).astype(np.int8)
     t2 = np.where(np.abs(wr) == 1.0, 1, -1).astype(np.int8) * t1
-    s1 = np.full((n, k // 128), np.float16(0.75)).view(np.uint16)
-    s2 = np.full((n, k // 128), np.float16(0.25)).view(np.uint16)
+    s1 = np.full((n // 16, k // 128, 16), np.float16(0.75)).view(np.uint16)
+    s2 = np.full((n // 16, k // 128, 16), np.float16(0.25)).view(np.uint16)
     codes = q.interleave_planes(q.pack_dense(t1), q.pack_dense(t2))
     scales = q.interleave_planes(s1, s2)
     x = nu.f64_to_bf16_bits(rng.standard_normal((3, k)))
@@ -146,3 +148,17 @@ def test_gemv_residual_two_plane_cases():
     sw = q.interleave_planes(q.pack_dense(t2), q.pack_dense(t1))
     ss = q.interleave_planes(s2, s1)
     assert np.allclose(mv.gemv_residual(x, sw, ss, k), xf @ wr.T, rtol=0, atol=1e-12)
+
+
+def test_scale_tiling_places_each_row_and_group():
+    # tile_scales puts the scale of row r, group g at [r // 16, g, r % 16]
+    n, g = 48, 5
+    rows = np.arange(n * g, dtype=np.uint16).reshape(n, g)
+    t = q.tile_scales(rows)
+    assert t.shape == (3, 5, 16)
+    for r in range(n):
+        for j in range(g):
+            assert t[r // 16, j, r % 16] == rows[r, j]
+    assert np.array_equal(q.untile_scales(t), rows)
+    with pytest.raises(ValueError):
+        q.tile_scales(np.zeros((20, 2), dtype=np.uint16))

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 def _noalloc(x, cd, sc, y):
     L = tb.lib()
-    n, g = sc.shape
+    n, g = sc.shape[0] * 16, sc.shape[1]
     st = L.tb_ternary_gemv_noalloc(ctypes.c_void_p(x.data_ptr()), x.shape[0], ctypes.c_void_p(cd.data_ptr()),
                                    ctypes.c_void_p(sc.data_ptr()), n, g * 128, ctypes.c_void_p(y.data_ptr()),
                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
