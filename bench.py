@@ -6,9 +6,12 @@ Timed step (the value): one decode token through a 64-layer 27B-shaped stack
 projection (QKV 15360x5120, O 5120x5120, gate/up 34816x5120, down
 5120x17408) the activations are rotated and encoded as the GEMV operand
 (tb_fwht128 with the act8 output), multiplied by the packed ternary weights
-(tb_ternary_gemv) and the output is rotated back (tb_fwht128 along N).  All 6.33 GB of packed weights are resident in HBM and
-each is read once per step, far beyond the 256 MB last-level cache.  The step
-is captured once in a HIP graph and replayed.
+(grouped tb_ternary_gemv launches) and the output is rotated back (tb_fwht128
+along N); one rotation launch per layer boundary carries the previous
+layer's output rotations and this layer's input rotations.  All 6.33 GB of
+packed weights are resident in HBM and each is read once per step, far
+beyond the 256 MB last-level cache.  The step is captured once in a HIP
+graph and replayed.
 value = packed weight bytes (codes + scales) streamed per step / step time.
 
 Also measured in the same run, each over its own synthetic input, and
@@ -128,17 +131,26 @@ class DecodeStack:
             tb.tb_ternary_gemv_multi([s for s, (_, _, _, k) in zip(segs, layer) if k == D])
             tb.tb_ternary_gemv_multi([s for s, (_, _, _, k) in zip(segs, layer) if k != D])
 
-    def step(self):
-        """One decode step: per layer one launch rotating and encoding the four
-        projections' activations, the grouped GEMV launches, one launch
-        rotating the four outputs back."""
+    def step(self, merged=True):
+        """One decode step.  Per layer boundary one launch rotates the previous
+        layer's four outputs back (fp32) and rotates and encodes this layer's
+        four inputs (bf16 -> act8), the place where a model's inter-layer work
+        (residual add, norm) sits; then the grouped GEMV launches; after the
+        last layer one launch rotates its outputs back.  merged=False makes the
+        input and output rotations separate launches (two per layer)."""
         from ternary_weights_hadamard_amd import tb
 
         rot_in = list(zip(self.x, self.act))
         rot_out = list(zip(self.yr, self.y))
-        for layer in self.w:
-            tb.tb_fwht128_multi(rot_in)
+        for li, layer in enumerate(self.w):
+            if merged:
+                tb.tb_fwht128_multi((rot_out if li > 0 else []) + rot_in)
+            else:
+                tb.tb_fwht128_multi(rot_in)
             self.gemv_calls(layer)
+            if not merged:
+                tb.tb_fwht128_multi(rot_out)
+        if merged:
             tb.tb_fwht128_multi(rot_out)
 
     def step_sequential(self):
@@ -333,6 +345,8 @@ def extra_phases(gen, dev, quick):
     log(f"  FWHT 2048x17408: {ms * 1e3:.1f} us, {out['fwht128']['gbs']} GB/s")
     del xa, ya
 
+    out["ceilings"] = ceilings(dev)
+
     # offline quantiser streamed over the 64-layer stack (its own function)
     out["quantize_stack"] = quantize_stack(dev, 64)
 
@@ -426,28 +440,219 @@ def quantize_stack(dev, layers):
     return res
 
 
-def profile_pass(dev):
-    """Short run for the counter passes: a 4-layer stack (weights beyond the
-    256 MB last-level cache), every layer's grouped GEMV launches 3 times round
-    robin, then a plain copy of CALIB_BYTES for the counter calibration."""
+PROBE_LIB = os.path.join(ROOT, "ternary_weights_hadamard_amd", "libtb_probe.so")
+
+
+def probe_lib():
+    """The measurement probes of include/tb_probe.h (libtb_probe.so)."""
+    import ctypes
+
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.tbp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.tbp_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+def _cur_stream():
     import torch
 
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(31)
-    stack = DecodeStack(4, 1, gen, dev, "split")
-    stack.step()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def ceilings(dev):
+    """What this device achieves with the simplest kernels (tb_probe.h): a
+    streaming read of 1 GiB; reads of the byte counts of the decode step's two
+    grouped GEMV launches, each over its own buffer, rotated over >= 1 GB of
+    buffers and replayed in a HIP graph as the step is; and a register-only
+    loop of bf16 matrix instructions."""
+    import torch
+
+    lib = probe_lib()
+    sink = torch.empty(16384 * 256, dtype=torch.int32, device=dev)
+    out = {}
+    big = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(7)
+    best = 0.0
+    for grid in (2048, 4096, 8192):
+        ms, _, g = time_graph(lambda: lib.tbp_stream_read(big.data_ptr(), big.numel() * 4, sink.data_ptr(), grid,
+                                                         _cur_stream()), 10, 2)
+        del g
+        best = max(best, big.numel() * 4 * 10 / (ms * 1e-3) / 1e9)
+    out["read_1gib_gbs"] = round(best, 1)
+    del big
+    first = sum(gemv_bytes(n, k, 1) for _, n, k in FUSED[:3])
+    down = gemv_bytes(FUSED[3][1], FUSED[3][2], 1)
+    for label, nbytes in (("read_first_launch", first), ("read_down_launch", down)):
+        nbytes = nbytes // 4096 * 4096
+        copies = -(-(1 << 30) // nbytes)
+        bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7) for _ in range(copies)]
+        res = {}
+        for grid in (512, 2048):
+            def fn():
+                for b in bufs:
+                    lib.tbp_stream_read(b.data_ptr(), nbytes, sink.data_ptr(), grid, _cur_stream())
+            ms, _, g = time_graph(fn, 5, 2)
+            del g
+            us = ms * 1e3 / (5 * copies)
+            res[grid] = us
+        us = min(res.values())
+        out[label] = {"bytes": nbytes, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del bufs
+    fs = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    grid, iters = 2048, 4000
+    lib.tbp_mfma_bf16(fs.data_ptr(), 100, grid, _cur_stream())
     torch.cuda.synchronize()
-    for _ in range(3):
-        stack.gemv_only()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    lib.tbp_mfma_bf16(fs.data_ptr(), iters, grid, _cur_stream())
+    b.record()
+    torch.cuda.synchronize()
+    flops = grid * 4 * iters * 4 * 2.0 * 16 * 16 * 32
+    out["mfma_bf16_tflops"] = round(flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+    log(f"  ceilings: read 1 GiB {out['read_1gib_gbs']} GB/s; first-launch bytes {out['read_first_launch']['us']} us, "
+        f"down-launch bytes {out['read_down_launch']['us']} us; bf16 MFMA {out['mfma_bf16_tflops']} TFLOP/s")
+    return out
+
+
+def _calibration_copy(dev):
+    """A plain device copy of CALIB_BYTES, three times: the byte counters of
+    the same run are scaled by what they read for it."""
+    import torch
+
     src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    per_launch = sum(gemv_bytes(n, k, 1) for _, _, n, k in stack.w[0]) / 2
-    print(json.dumps({"profile_pass": True, "gemv_launches": 3 * 2 * 4, "algorithmic_bytes_per_launch": per_launch,
-                      "calibration_copy_bytes": CALIB_BYTES}), flush=True)
+
+
+PROFILE_KINDS = ("gemv", "gemm", "gemv24", "quant", "midbatch", "ceiling")
+
+
+def profile_pass(dev, kind):
+    """Short runs for rocprofv3 counter passes, one workload each, then the
+    calibration copy:
+      gemv      the decode step's grouped GEMV launches over a 4-layer stack
+                (weights beyond the 256 MB last-level cache), 3 times;
+      gemm      the prefill GEMM, M = 2048, both FFN shapes, twice each;
+      gemv24    the 2:4 GEMV, 17408 x 5120, batch 1, over 16 weight copies;
+      quant     the quantiser on one layer of the stack recipe, twice;
+      midbatch  the split-K GEMM at M = 16 on the three layer shapes, 4 copies;
+      ceiling   the streaming-read probe over 256 MiB, 3 times."""
+    import torch
+
+    from ternary_weights_hadamard_amd import synth, tb
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    info = {"profile_pass": kind}
+    if kind == "gemv":
+        stack = DecodeStack(4, 1, gen, dev, "split")
+        stack.step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            stack.gemv_only()
+        info["algorithmic_bytes_per_launch"] = sum(gemv_bytes(n, k, 1) for _, _, n, k in stack.w[0]) / 2
+    elif kind == "gemm":
+        for k, n in ((D, F), (F, D)):
+            codes = synth.torch_code_words(n, k, gen, dev)
+            scales = synth.torch_scales_f16(n, k, gen, dev)
+            x = synth.torch_gaussian_bf16((2048, k), gen, dev)
+            y = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
+            for _ in range(2):
+                tb.tb_ternary_gemm(x, codes, scales, y=y)
+            torch.cuda.synchronize()
+    elif kind == "gemv24":
+        n, k = F, D
+        planes = [synth.torch_24(n, k, gen, dev) + (synth.torch_scales24_f16(n, k, gen, dev),) for _ in range(16)]
+        x = synth.torch_gaussian_bf16((1, k), gen, dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        for meta, signs, sc in planes:
+            tb.tb_ternary24_gemv(x, meta, signs, sc, y=y)
+        info["algorithmic_bytes_per_launch"] = n * k // 8 + n * k // 16 + n * k // 64 + 2 * k + 4 * n
+    elif kind == "quant":
+        g0 = torch.Generator(device=dev)
+        g0.manual_seed(5000)
+        for _ in range(2):
+            for _, n, k in synth.LAYER_MATRICES:
+                w = synth.torch_stack_weights(n, k, g0, dev)
+                tb.tb_quantize_pack(w)
+                torch.cuda.synchronize()
+                del w
+        info["algorithmic_bytes_per_weight"] = QUANT_BYTES_PER_WEIGHT
+    elif kind == "midbatch":
+        for k, n in ((D, D), (D, F), (F, D)):
+            ws = [(synth.torch_code_words(n, k, gen, dev), synth.torch_scales_f16(n, k, gen, dev)) for _ in range(4)]
+            x = synth.torch_gaussian_bf16((16, k), gen, dev)
+            y = torch.empty((16, n), dtype=torch.bfloat16, device=dev)
+            wsb = tb.tb_ternary_gemm_splitk_workspace(16, n, k)
+            work = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev)
+            for c, sc in ws:
+                tb.tb_ternary_gemm_splitk(x, c, sc, y=y, workspace=work)
+            torch.cuda.synchronize()
+            del ws
+    elif kind == "ceiling":
+        lib = probe_lib()
+        buf = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device=dev).fill_(7)
+        sink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            lib.tbp_stream_read(buf.data_ptr(), CALIB_BYTES, sink.data_ptr(), 4096, _cur_stream())
+        info["read_bytes_per_launch"] = CALIB_BYTES
+    else:
+        raise SystemExit(f"unknown profile pass {kind}; one of {PROFILE_KINDS}")
+    torch.cuda.synchronize()
+    _calibration_copy(dev)
+    info["calibration_copy_bytes"] = CALIB_BYTES
+    print(json.dumps(info), flush=True)
+
+
+def summarize_pmc(out_path, dirs, command_lines, title):
+    """Per-kernel means per dispatch of every counter found in the rocprofv3
+    --pmc output folders `dirs` (libtb and probe kernels; FETCH_SIZE and
+    WRITE_SIZE also as bytes, scaled by what each reads for the calibration
+    copy of the same run)."""
+    import csv
+    import glob
+
+    per = {}  # (kernel, counter) -> [values]
+    calib = {}  # counter -> [values of the calibration copies]
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows = list(csv.DictReader(open(f)))
+            by = {}
+            for r in rows:
+                key = (r.get("Dispatch_Id"), r.get("Kernel_Name", ""), r.get("Counter_Name"))
+                by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+            for (_, name, counter), v in by.items():
+                if "tb::" in name or "stream_read_kernel" in name or "mfma_bf16_kernel" in name:
+                    short = name.replace("void ", "").replace("tb::(anonymous namespace)::", "")
+                    short = short.replace("(anonymous namespace)::", "").split("(")[0]
+                    per.setdefault((short, counter), []).append(v)
+                elif "copy" in name.lower():
+                    calib.setdefault(counter, []).append(v)
+    kib = 1024.0
+    scale = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = sorted(calib.get(counter, []))[-3:]
+        if vals:
+            scale[counter] = CALIB_BYTES / (sum(vals) / len(vals) * kib)
+    lines = [f"# {title}", "# rocprofv3 counter passes on one MI355X; commands (run from the repository root):"]
+    lines += [f"#   {c}" for c in command_lines]
+    lines += ["# Per kernel: the mean per dispatch.  FETCH_SIZE / WRITE_SIZE are KiB per dispatch; the bytes",
+              f"# column scales them by what the same counter reads for a {CALIB_BYTES >> 20} MiB device copy",
+              "# (read once, written once) in the same run.", ""]
+    for c, f in sorted(scale.items()):
+        lines.append(f"calibration {c}: x {f:.4f}")
+    lines.append("")
+    lines.append("kernel | counter | dispatches | mean per dispatch | bytes per dispatch")
+    for (kern, counter) in sorted(per):
+        v = per[(kern, counter)]
+        mean = sum(v) / len(v)
+        b = f"{mean * kib * scale[counter]:.0f}" if counter in scale else ""
+        lines.append(f"{kern} | {counter} | {len(v)} | {mean:.6g} | {b}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_counters(fetch_dir, write_dir, out_path, commands):
@@ -709,7 +914,12 @@ def main():
     ap.add_argument("--quick", action="store_true", help="fewer iterations in the extra phases")
     ap.add_argument("--grouping", choices=("layer", "split", "none"), default="split",
                     help="GEMV launches per layer: one over all four matrices, two (d_model-input ones, then down), or one per matrix")
-    ap.add_argument("--profile-pass", action="store_true", help="short run for rocprofv3 counter passes")
+    ap.add_argument("--profile-pass", nargs="?", const="gemv", choices=PROFILE_KINDS,
+                    help="short run of one workload for rocprofv3 counter passes (default: gemv)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar=("OUT", "DIR"),
+                    help="write a per-kernel summary of rocprofv3 --pmc output folders: OUT DIR [DIR ...]")
+    ap.add_argument("--pmc-title", default="counter summary", help="title line of --summarize-pmc")
+    ap.add_argument("--pmc-command", action="append", default=[], help="a command to record in --summarize-pmc")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--summarize-kernel-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
@@ -722,6 +932,10 @@ def main():
         cmd = args.stats_command or ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
                                      "python3 bench.py --steps 5 --warmup 1 --no-extra --no-cpu-baseline")
         summarize_kernel_stats(args.summarize_kernel_stats[0], args.summarize_kernel_stats[1], cmd)
+        return
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1:], args.pmc_command, args.pmc_title)
         return
 
     if args.summarize_counters:
@@ -746,7 +960,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.profile_pass:
-        profile_pass(dev)
+        profile_pass(dev, args.profile_pass)
         return
     gen = torch.Generator(device=dev)
     gen.manual_seed(29)
@@ -771,6 +985,15 @@ def main():
 
     extra = {"step_wall_ms": round(wall_ms / args.steps, 4),
              "gemv_avg_launch_us": round(gms * 1e3, 3), "gemv_launches_per_step": nl}
+    # the same step with the input and output rotations as separate launches
+    if not args.no_extra:
+        ms_apart, _, ga = time_graph(lambda: stack.step(merged=False), max(3, args.steps // 2), 2)
+        del ga
+        ms_apart /= max(3, args.steps // 2)
+        extra["decode_rotations_apart"] = {"ms_per_step": round(ms_apart, 4),
+                                           "gbs_packed": round(step_bytes / (ms_apart * 1e-3) / 1e9, 1),
+                                           "note": "input and output rotations as two launches per layer"}
+        log(f"decode step, rotations apart: {ms_apart:.4f} ms")
     # the same step with a decoder layer's ordering (no grouping across projections)
     if not args.no_extra:
         ms_seq, _, gs = time_graph(stack.step_sequential, max(3, args.steps // 2), 2)

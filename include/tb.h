@@ -115,12 +115,15 @@ typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_
 /* Most segments one grouped call (tb_fwht128_multi, tb_ternary_gemv_multi) takes. */
 #define TB_MAX_SEGMENTS 8
 
-/* One array of a grouped tb_fwht128_multi call: arguments as in tb_fwht128. */
+/* One array of a grouped tb_fwht128_multi call: arguments as in tb_fwht128,
+ * each segment with its own input and output dtypes. */
 typedef struct {
   const void* x;
   void* y;
   int64_t rows;
   int64_t K;
+  int x_dtype;
+  int y_dtype;
 } tb_fwht_segment;
 
 /* One product of a grouped tb_ternary_gemv_multi call: arguments as in
@@ -176,13 +179,15 @@ TB_API tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, in
 
 /*
  * tb_fwht128 over up to TB_MAX_SEGMENTS independent arrays in one launch (the
- * activations of several projections, or their outputs); same transform and
- * rules per segment, one x_dtype / y_dtype for all.  `segs` is a host array
- * read during the call.  Segments must not overlap one another except a
- * segment rotating in place.  count == 0 is a no-op; count outside
- * [0, TB_MAX_SEGMENTS] returns TB_ERR_SHAPE.
+ * activations of several projections, their outputs, or one layer's outputs
+ * together with the next layer's inputs); same transform and rules per
+ * segment, each with its own x_dtype / y_dtype (a segment's result does not
+ * depend on what it is grouped with).  `segs` is a host array read during
+ * the call.  Segments must not overlap one another except a segment rotating
+ * in place.  count == 0 is a no-op; count outside [0, TB_MAX_SEGMENTS]
+ * returns TB_ERR_SHAPE.
  */
-TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype, void* stream);
+TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, void* stream);
 
 /*
  * Offline quantise and pack (mhpq.cn/news/1159370 §1.1-§1.3, §3.1;

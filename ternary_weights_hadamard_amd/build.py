@@ -23,6 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtb.so")
+PROBE_LIB = os.path.join(PKG, "libtb_probe.so")  # measurement probes (include/tb_probe.h)
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
@@ -41,8 +42,8 @@ CFLAGS = [
 ]
 
 
-def _sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def _sources(d=CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 def _filter(stderr):
@@ -107,14 +108,8 @@ def _check_asm(src):
             return check_scaled_mfma_operands(f.read(), os.path.basename(src))
 
 
-def build(verbose=True):
-    objdir = os.path.join(PKG, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    srcs = _sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, objdir), srcs))
-        checked = sum(ex.map(_check_asm, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -125,9 +120,22 @@ def build(verbose=True):
     if missing:
         os.remove(tmp)
         raise RuntimeError("kernel launch stubs missing from the link: " + ", ".join(missing))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=True):
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = _sources()
+    probes = _sources(os.path.join(CSRC, "probe"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, objdir), srcs))
+        pobjs = list(ex.map(lambda s: _compile(s, objdir), probes))
+        checked = sum(ex.map(_check_asm, srcs))
+    _link(objs, LIB)
+    _link(pobjs, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources ({checked} scaled MFMAs checked)")
+        print(f"built {LIB} from {len(srcs)} sources ({checked} scaled MFMAs checked), {PROBE_LIB}")
     return LIB
 
 

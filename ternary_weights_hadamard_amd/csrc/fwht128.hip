@@ -29,11 +29,14 @@ enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutAct8 = 2 };
 // of 4, so that the four blocks of a wave always lie in one segment.  The
 // segment is then found per wave (scalar compares and loads of the kernel
 // arguments); a per-lane choice kept all segments' pointers live and spilled
-// them through VGPR lanes.
+// them through VGPR lanes.  Segments may differ in their input and output
+// dtypes (`kind`): a layer's outputs in fp32 rotated back and the next
+// layer's bf16 inputs rotated and encoded, in one launch.
 struct FwhtSeg {
   const void* x;
   void* y;
   int64_t nblocks, begin;
+  int kind, pad;  // 3 * (x bf16 ? 1 : 0) + OutKind
 };
 
 struct FwhtSegs {
@@ -42,87 +45,122 @@ struct FwhtSegs {
   int64_t total;
 };
 
+// One 128-block per 16 lanes: block b of a segment of nblocks blocks; lanes
+// past the end (b >= nblocks) run the cross-lane rounds on zeros and store
+// nothing.
+template <bool IN_BF16, int OUT, bool XFORM>
+__device__ __forceinline__ void fwht_block(const void* x, void* y, int64_t nblocks, int64_t b, int sub) {
+  const bool live = b < nblocks;
+  const int64_t base = b * kBlock + sub * 8;
+  float v[8];
+  if constexpr (IN_BF16) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (live) w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  } else {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + base);
+      a = p[0];
+      c = p[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = c[i];
+    }
+  }
+  float sc = 1.0f;
+  if constexpr (XFORM) {
+    fwht128_lanes(v, sub);
+    sc = kInvSqrt128;
+  }
+  if constexpr (OUT == kOutAct8) {
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e] * sc);
+    // act8 buffer: values of block b at b * 512, scales at 4 * elements + b * 16
+    uint8_t* act = static_cast<uint8_t*>(y);
+    const int64_t bb = live ? b : 0;
+    act8_encode_store(h, sub, act + bb * 512, act + nblocks * 512 + bb * 16, live);
+    return;
+  }
+  if (!live) return;
+  if constexpr (OUT == kOutBF16) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = f32_to_bf16_rne(v[2 * i] * sc) | (f32_to_bf16_rne(v[2 * i + 1] * sc) << 16);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
+  } else {
+    f32x4 a, c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = v[i] * sc;
+      c[i] = v[4 + i] * sc;
+    }
+    f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + base);
+    p[0] = a;
+    p[1] = c;
+  }
+}
+
+__device__ __forceinline__ int wave_segment(const FwhtSegs& segs, int64_t bw) {
+  // the wave's segment: the last whose first block is at or before bw
+  int seg = 0;
+#pragma unroll
+  for (int t = 1; t < TB_MAX_SEGMENTS; ++t) seg += (t < segs.count && bw >= segs.s[t].begin) ? 1 : 0;
+  return seg;
+}
+
+// every segment of the launch of one kind
 template <bool IN_BF16, int OUT, bool XFORM>
 __global__ void __launch_bounds__(64) fwht128_kernel(FwhtSegs segs) {
   const int sub = threadIdx.x & 15;
   for (int64_t bw = (int64_t)blockIdx.x * 4; bw < segs.total; bw += (int64_t)gridDim.x * 4) {
-    // the wave's segment: the last whose first block is at or before bw
-    int seg = 0;
-#pragma unroll
-    for (int t = 1; t < TB_MAX_SEGMENTS; ++t) seg += (t < segs.count && bw >= segs.s[t].begin) ? 1 : 0;
-    const void* x = segs.s[seg].x;
-    void* y = segs.s[seg].y;
-    const int64_t nblocks = segs.s[seg].nblocks;
+    const int seg = wave_segment(segs, bw);
     const int64_t b = bw - segs.s[seg].begin + (threadIdx.x >> 4);  // block inside its segment
-    // every lane of the wave runs the cross-lane stages; lanes past the
-    // segment's end carry zeros
-    const bool live = b < nblocks;
-    const int64_t base = b * kBlock + sub * 8;
-    float v[8];
-    if constexpr (IN_BF16) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (live) w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + base);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-      }
-    } else {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
-      if (live) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + base);
-        a = p[0];
-        c = p[1];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = a[i];
-        v[4 + i] = c[i];
-      }
-    }
-    float sc = 1.0f;
-    if constexpr (XFORM) {
-      fwht128_lanes(v, sub);
-      sc = kInvSqrt128;
-    }
-    if constexpr (OUT == kOutAct8) {
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e] * sc);
-      // act8 buffer: values of block b at b * 512, scales at 4 * elements + b * 16
-      uint8_t* act = static_cast<uint8_t*>(y);
-      const int64_t bb = live ? b : 0;
-      act8_encode_store(h, sub, act + bb * 512, act + nblocks * 512 + bb * 16, live);
-      continue;
-    }
-    if (!live) continue;
-    if constexpr (OUT == kOutBF16) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = f32_to_bf16_rne(v[2 * i] * sc) | (f32_to_bf16_rne(v[2 * i + 1] * sc) << 16);
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
-    } else {
-      f32x4 a, c;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = v[i] * sc;
-        c[i] = v[4 + i] * sc;
-      }
-      f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + base);
-      p[0] = a;
-      p[1] = c;
+    fwht_block<IN_BF16, OUT, XFORM>(segs.s[seg].x, segs.s[seg].y, segs.s[seg].nblocks, b, sub);
+  }
+}
+
+// segments of different kinds: the kind is uniform per wave, so the choice
+// is a scalar branch
+__global__ void __launch_bounds__(64) fwht128_mixed_kernel(FwhtSegs segs) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t bw = (int64_t)blockIdx.x * 4; bw < segs.total; bw += (int64_t)gridDim.x * 4) {
+    const int seg = wave_segment(segs, bw);
+    const FwhtSeg& sg = segs.s[seg];
+    const int64_t b = bw - sg.begin + (threadIdx.x >> 4);
+    switch (__builtin_amdgcn_readfirstlane(sg.kind)) {
+      case 0: fwht_block<false, kOutF32, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
+      case 1: fwht_block<false, kOutBF16, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
+      case 2: fwht_block<false, kOutAct8, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
+      case 3: fwht_block<true, kOutF32, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
+      case 4: fwht_block<true, kOutBF16, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
+      default: fwht_block<true, kOutAct8, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
     }
   }
+}
+
+int seg_kind(int x_dtype, int y_dtype) {
+  const int out = y_dtype == TB_ACT8 ? kOutAct8 : y_dtype == TB_BF16 ? kOutBF16 : kOutF32;
+  return 3 * (x_dtype == TB_BF16 ? 1 : 0) + out;
+}
+
+unsigned grid_of(int64_t total) {
+  const int64_t groups = (total + 3) / 4, cap = 1 << 20;
+  return (unsigned)(groups < cap ? groups : cap);
 }
 
 template <bool XFORM>
 hipError_t launch_segments(const FwhtSegs& segs, int x_dtype, int y_dtype, hipStream_t stream) {
   if (segs.total == 0) return hipSuccess;
-  int64_t groups = (segs.total + 3) / 4;
-  const int64_t cap = 1 << 20;
-  const unsigned grid = (unsigned)(groups < cap ? groups : cap);
-  const dim3 g(grid), blk(64);
+  const dim3 g(grid_of(segs.total)), blk(64);
   const bool ib = x_dtype == TB_BF16;
   if (y_dtype == TB_ACT8) {
     if (ib) hipLaunchKernelGGL((fwht128_kernel<true, kOutAct8, XFORM>), g, blk, 0, stream, segs);
@@ -139,7 +177,7 @@ hipError_t launch_segments(const FwhtSegs& segs, int x_dtype, int y_dtype, hipSt
 
 FwhtSegs one_segment(const void* x, void* y, int64_t nblocks) {
   FwhtSegs s{};
-  s.s[0] = FwhtSeg{x, y, nblocks, 0};
+  s.s[0] = FwhtSeg{x, y, nblocks, 0, 0, 0};
   s.count = 1;
   s.total = nblocks;
   return s;
@@ -152,18 +190,23 @@ hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int6
   return launch_segments<true>(one_segment(x, y, rows * (K / kBlock)), x_dtype, y_dtype, stream);
 }
 
-hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype,
-                                hipStream_t stream) {
+hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, hipStream_t stream) {
   FwhtSegs s{};
   int64_t total = 0;
+  bool same = true;
   for (int c = 0; c < count; ++c) {
     const int64_t nb = segs[c].rows * (segs[c].K / kBlock);
-    s.s[c] = FwhtSeg{segs[c].x, segs[c].y, nb, total};
+    s.s[c] = FwhtSeg{segs[c].x, segs[c].y, nb, total, seg_kind(segs[c].x_dtype, segs[c].y_dtype), 0};
     total += (nb + 3) / 4 * 4;  // the next segment starts on a wave boundary
+    same = same && s.s[c].kind == s.s[0].kind;
   }
   s.count = count;
   s.total = total;
-  return launch_segments<true>(s, x_dtype, y_dtype, stream);
+  if (count == 0) return hipSuccess;
+  if (same) return launch_segments<true>(s, segs[0].x_dtype, segs[0].y_dtype, stream);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(fwht128_mixed_kernel, dim3(grid_of(total)), dim3(64), 0, stream, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream) {

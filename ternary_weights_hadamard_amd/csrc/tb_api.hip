@@ -206,28 +206,27 @@ tb_status tb_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t r
   return launched(tb::launch_fwht128(x, x_dtype, y, y_dtype, rows, K, as_stream(stream)));
 }
 
-tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype, void* stream) {
+tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, void* stream) {
   if (count < 0 || count > TB_MAX_SEGMENTS) return TB_ERR_SHAPE;
-  if (!dtype_ok(x_dtype) || !(dtype_ok(y_dtype) || y_dtype == TB_ACT8)) return TB_ERR_DTYPE;
   if (count == 0) return TB_OK;
   if (!segs) return TB_ERR_NULL;
   tb_fwht_segment live[TB_MAX_SEGMENTS];
   int n = 0;
   for (int c = 0; c < count; ++c) {
     const tb_fwht_segment& a = segs[c];
-    const tb_status st = check_fwht(a.x, x_dtype, a.y, y_dtype, a.rows, a.K);
+    const tb_status st = check_fwht(a.x, a.x_dtype, a.y, a.y_dtype, a.rows, a.K);
     if (st != TB_OK) return st;
     for (int d = 0; d < c; ++d) {
       const tb_fwht_segment& b = segs[d];
       if (a.rows == 0 || b.rows == 0) continue;
-      const size_t ai = fwht_in_bytes(a.rows, a.K, x_dtype), ao = fwht_out_bytes(a.rows, a.K, y_dtype);
-      const size_t bi = fwht_in_bytes(b.rows, b.K, x_dtype), bo = fwht_out_bytes(b.rows, b.K, y_dtype);
+      const size_t ai = fwht_in_bytes(a.rows, a.K, a.x_dtype), ao = fwht_out_bytes(a.rows, a.K, a.y_dtype);
+      const size_t bi = fwht_in_bytes(b.rows, b.K, b.x_dtype), bo = fwht_out_bytes(b.rows, b.K, b.y_dtype);
       if (overlap(a.y, ao, b.y, bo) || overlap(a.y, ao, b.x, bi) || overlap(b.y, bo, a.x, ai)) return TB_ERR_ALIAS;
     }
     if (a.rows > 0) live[n++] = a;
   }
   if (n == 0) return TB_OK;
-  return launched(tb::launch_fwht128_multi(live, n, x_dtype, y_dtype, as_stream(stream)));
+  return launched(tb::launch_fwht128_multi(live, n, as_stream(stream)));
 }
 
 tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,

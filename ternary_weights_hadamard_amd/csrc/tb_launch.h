@@ -11,8 +11,7 @@ namespace tb {
 
 hipError_t launch_fwht128(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t K,
                           hipStream_t stream);
-hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, int x_dtype, int y_dtype,
-                                hipStream_t stream);
+hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, hipStream_t stream);
 hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
                               uint16_t* scales, int32_t* err_flag, hipStream_t stream);
 hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream);

@@ -38,7 +38,8 @@ _vp = ctypes.c_void_p
 _int = ctypes.c_int
 
 class FwhtSegment(ctypes.Structure):
-    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("rows", ctypes.c_int64), ("K", ctypes.c_int64)]
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("x_dtype", ctypes.c_int), ("y_dtype", ctypes.c_int)]
 
 
 class GemvSegment(ctypes.Structure):
@@ -53,7 +54,7 @@ SIGNATURES = {
     "tb_packed_bytes": (_int, [_int, _i64, _i64, ctypes.POINTER(ctypes.c_size_t),
                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "tb_fwht128": (_int, [_vp, _int, _vp, _int, _i64, _i64, _vp]),
-    "tb_fwht128_multi": (_int, [ctypes.POINTER(FwhtSegment), _int, _int, _int, _vp]),
+    "tb_fwht128_multi": (_int, [ctypes.POINTER(FwhtSegment), _int, _vp]),
     "tb_ternary_gemv_multi": (_int, [ctypes.POINTER(GemvSegment), _int, _vp]),
     "tb_quantize_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "tb_ternary_gemv": (_int, [_vp, _int, _i64, _vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -152,8 +153,8 @@ def tb_fwht128(x, y=None, out_dtype=None, stream=None):
 
 
 def tb_fwht128_multi(pairs, stream=None):
-    """One launch rotating several arrays: pairs = [(x, y), ...] with a common
-    input dtype and a common output dtype (a uint8 y means the act8 operand)."""
+    """One launch rotating several arrays: pairs = [(x, y), ...], each with its
+    own dtypes (a uint8 y means the act8 operand)."""
     if not pairs:
         return
     for x, y in pairs:
@@ -161,9 +162,8 @@ def tb_fwht128_multi(pairs, stream=None):
     arr = (FwhtSegment * len(pairs))()
     for c, (x, y) in enumerate(pairs):
         rows = x.numel() // x.shape[-1] if x.numel() else 0
-        arr[c] = FwhtSegment(x.data_ptr(), y.data_ptr(), rows, x.shape[-1])
-    _check(lib().tb_fwht128_multi(arr, len(pairs), _dt(pairs[0][0]), _dt(pairs[0][1]), _stream(stream)),
-           "tb_fwht128_multi")
+        arr[c] = FwhtSegment(x.data_ptr(), y.data_ptr(), rows, x.shape[-1], _dt(x), _dt(y))
+    _check(lib().tb_fwht128_multi(arr, len(pairs), _stream(stream)), "tb_fwht128_multi")
 
 
 def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, err_flag=None, stream=None):

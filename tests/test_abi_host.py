@@ -176,18 +176,26 @@ def test_grouped_validation():
     L = tb.lib()
     s = None
     F, Gs = tb.FwhtSegment, tb.GemvSegment
-    fw = (F * 2)(F(A, B, 1, 128), F(C, D, 1, 128))
-    assert L.tb_fwht128_multi(fw, 9, 1, 1, s) == 2                 # more than TB_MAX_SEGMENTS
-    assert L.tb_fwht128_multi(fw, -1, 1, 1, s) == 2
-    assert L.tb_fwht128_multi(fw, 0, 1, 1, s) == 0                 # empty group
-    assert L.tb_fwht128_multi(None, 2, 1, 1, s) == 1
-    assert L.tb_fwht128_multi(fw, 2, 7, 1, s) == 4
-    bad = (F * 2)(F(A, B, 1, 128), F(C, D, 1, 100))
-    assert L.tb_fwht128_multi(bad, 2, 1, 1, s) == 2                # one bad segment fails the call
-    clash = (F * 2)(F(A, B, 1, 128), F(C, B + 64, 1, 128))
-    assert L.tb_fwht128_multi(clash, 2, 1, 1, s) == 8              # outputs overlap each other
-    reads = (F * 2)(F(A, B, 1, 128), F(B, D, 1, 128))
-    assert L.tb_fwht128_multi(reads, 2, 1, 1, s) == 8              # one writes what another reads
+    bb = lambda x, y, rows, k: F(x, y, rows, k, tb.TB_BF16, tb.TB_BF16)
+    fw = (F * 2)(bb(A, B, 1, 128), bb(C, D, 1, 128))
+    assert L.tb_fwht128_multi(fw, 9, s) == 2                       # more than TB_MAX_SEGMENTS
+    assert L.tb_fwht128_multi(fw, -1, s) == 2
+    assert L.tb_fwht128_multi(fw, 0, s) == 0                       # empty group
+    assert L.tb_fwht128_multi(None, 2, s) == 1
+    bad_dtype = (F * 2)(bb(A, B, 1, 128), F(C, D, 1, 128, 7, tb.TB_BF16))
+    assert L.tb_fwht128_multi(bad_dtype, 2, s) == 4                # one segment's dtype
+    act_in = (F * 1)(F(A, B, 1, 128, tb.TB_ACT8, tb.TB_F32))
+    assert L.tb_fwht128_multi(act_in, 1, s) == 4                   # act8 is an output-only dtype
+    bad = (F * 2)(bb(A, B, 1, 128), bb(C, D, 1, 100))
+    assert L.tb_fwht128_multi(bad, 2, s) == 2                      # one bad segment fails the call
+    clash = (F * 2)(bb(A, B, 1, 128), bb(C, B + 64, 1, 128))
+    assert L.tb_fwht128_multi(clash, 2, s) == 8                    # outputs overlap each other
+    reads = (F * 2)(bb(A, B, 1, 128), bb(B, D, 1, 128))
+    assert L.tb_fwht128_multi(reads, 2, s) == 8                    # one writes what another reads
+    # sizes follow each segment's own dtypes: an fp32 output of 512 bytes at D,
+    # and another segment reading bf16 at D + 256 (inside it)
+    mixed = (F * 2)(F(A, D, 1, 128, tb.TB_F32, tb.TB_F32), bb(D + 256, C, 1, 128))
+    assert L.tb_fwht128_multi(mixed, 2, s) == 8
     gv = (Gs * 2)(Gs(A, 1, B, C, 128, 128, D), Gs(A, 1, B, C, 128, 128, D + 4096))
     assert L.tb_ternary_gemv_multi(gv, 9, s) == 2
     assert L.tb_ternary_gemv_multi(gv, 0, s) == 0

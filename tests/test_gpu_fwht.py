@@ -113,3 +113,33 @@ def test_grouped_fwht_ragged_segments_equal_single_calls(din, dout):
         nbytes = buf.numel() - canary
         assert torch.equal(buf[:nbytes], single.contiguous().view(-1).view(torch.uint8)), f"segment {c} differs"
         assert bool((buf[nbytes:] == 0xA5).all()), f"segment {c}: write past its end"
+
+
+def test_grouped_fwht_mixed_dtypes_equal_single_calls():
+    # one launch whose segments differ in dtypes (a layer's fp32 outputs rotated
+    # back next to the following layer's bf16 inputs rotated into act8), ragged
+    # block counts, canaries after each output; each segment equals its single call
+    specs = [("f32", "f32", 1, 15360), ("bf16", "act8", 1, 5120), ("f32", "f32", 3, 640), ("bf16", "act8", 2, 17408),
+             ("bf16", "bf16", 1, 384), ("f32", "bf16", 1, 1152), ("f32", "act8", 5, 128), ("bf16", "f32", 1, 2176)]
+    canary = 64
+    pairs, outs = [], []
+    for c, (din, dout, rows, k) in enumerate(specs):
+        if din == "bf16":
+            x = bf16_dev(synth.gaussian_bf16((rows, k), seed=500 + c))
+        else:
+            x = f32_dev(np.random.default_rng(500 + c).standard_normal((rows, k)).astype(np.float32))
+        nbytes = tb.tb_act8_bytes(rows, k) if dout == "act8" else rows * k * (2 if dout == "bf16" else 4)
+        buf = torch.full((nbytes + canary,), 0xA5, dtype=torch.uint8, device=DEV)
+        y = buf[:nbytes] if dout == "act8" else buf[:nbytes].view(torch.bfloat16 if dout == "bf16" else torch.float32).view(rows, k)
+        pairs.append((x, y))
+        outs.append((buf, dout))
+    say(f"grouped fwht, mixed dtypes: {[(a, b, r * k // 128) for a, b, r, k in specs]}")
+    tb.tb_fwht128_multi(pairs)
+    torch.cuda.synchronize()
+    for c, ((x, _), (buf, dout)) in enumerate(zip(pairs, outs)):
+        od = {"act8": torch.uint8, "bf16": torch.bfloat16, "f32": torch.float32}[dout]
+        single = tb.tb_fwht128(x, out_dtype=od)
+        torch.cuda.synchronize()
+        nbytes = buf.numel() - canary
+        assert torch.equal(buf[:nbytes], single.contiguous().view(-1).view(torch.uint8)), f"segment {c} differs"
+        assert bool((buf[nbytes:] == 0xA5).all()), f"segment {c}: write past its end"
