@@ -343,23 +343,29 @@ TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t*
  * weight as the exact bf16 value 2t; every product is exact.  Each 128-K
  * group's products are summed in fp32 and added to the result times the
  * group's scale; the result is halved on the way out.
+ * M <= 16 runs a kernel of its own (one pass over K for at most 16 rows,
+ * weights decoded in registers); a row's result depends on its activations,
+ * N and K only, not on M.
  */
 TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, void* y, int y_dtype, void* stream);
 
 /*
- * Bytes of workspace tb_ternary_gemm_splitk uses for an [M][N] result with
- * K-long rows: S * M * N * 4 for the S splits of K it chooses (about two
- * workgroups per compute unit, at most 16 splits, at least one 128-group
- * each), or 0 when one pass suffices (S = 1) or the sizes are invalid.
+ * Bytes of workspace tb_ternary_gemm_splitk and tb_ternary_gemm_rotated use
+ * for an [M][N] result with K-long rows: S * M * N * 4 for the S splits of K
+ * they choose (about two workgroups per compute unit, at most 16 splits, at
+ * least one 128-group each), or 0 when one pass suffices (S = 1) or the
+ * sizes are invalid.  For M <= 16 only the rotated GEMM splits K.
  * Host-only.
  */
 TB_API size_t tb_ternary_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
 
 /*
  * tb_ternary_gemm for few rows of activations (M = 16-256, between decode and
- * prefill), where one pass over K leaves too few output tiles to fill the
- * GPU: K is cut into S splits at 128-group boundaries, each split's fp32
+ * prefill).  M <= 16 runs tb_ternary_gemm's kernel for such M (one pass, the
+ * workspace unused, the same result bit for bit).  Above that one pass over K
+ * leaves too few output tiles to fill the GPU: K is cut into S splits at
+ * 128-group boundaries, each split's fp32
  * partial product goes to `workspace` ([S][M][N] fp32), and a second kernel
  * adds the partials in split order and writes y (bf16 rounded to nearest
  * even, or fp32).  The same contraction and error rules as tb_ternary_gemm;

@@ -1,0 +1,221 @@
+// Ternary GEMM for at most 16 rows of activations (the mid-batch case between
+// decode and prefill), the contraction of the prefill GEMM:
+//   y[m][n] = sum_g f16(scale[n][g]) * sum_{k in g} t[n][k] * x[m][k]
+//
+// With M <= 16 the 128 x 128 tiles of the prefill kernel are mostly padding
+// and too few to fill the GPU, and the run is bound by streaming the codes.
+// Here one v_mfma_f32_16x16x32_bf16 row block holds all M rows (rows past M
+// repeat row M - 1 and are never stored) and its 16 columns are the 16 weight
+// rows of one code tile, so the decoded weights never leave registers:
+//   * a lane (q = lane / 16, i = lane % 16) loads the two code words it owns
+//     in the tile layout (row i, columns 32q .. 32q + 31 of the group) and
+//     decodes them in place.  The sum over K does not care in which order the
+//     K positions enter, so the m-th product of the group takes, in lane q,
+//     columns 32q + 8m .. 32q + 8m + 7 of both operands.
+//   * decode: masking a word with 0xCCCCCCCC leaves in every nibble the field
+//     of one column as the 4-bit float 0, +2 or -2 (sign bit, lowest exponent
+//     bit); the word shifted left by 2 and masked gives the other eight
+//     columns.  v_cvt_scalef32_pk_bf16_fp4 turns one byte of it (two columns)
+//     into a bf16 pair, exactly.
+//   * the activations are read from global memory in full 128-byte lines
+//     (16 lanes per row), written to a per-wave LDS tile with 16-byte chunk c
+//     of row r at position c ^ r, and read back as matrix operands (16 lanes
+//     read one chunk of 16 rows: 16 distinct positions, distinct banks).
+//   * each group's products accumulate in fp32, then are added to the result
+//     times the group's fp16 scale; the result is halved on the way out.
+// Work split: a workgroup owns two code tiles (32 output columns) and the
+// whole of K; its W waves take consecutive slices of the scale groups, each
+// wave streams its slice for both tiles with the codes, scales and
+// activations of the next step already in flight, and the W partial results
+// are summed in LDS in wave order.  The slice boundaries depend only on K and
+// on W, which depends only on N and K, so a row's result does not depend on M
+// or on timing.  Waves of different workgroups start their slices at
+// different groups, which spreads the activation reads over the L2 channels.
+#include <algorithm>
+
+#include "tb_common.h"
+#include "tb_launch.h"
+
+namespace tb {
+
+namespace {
+
+constexpr int kTiles = 2;   // code tiles (16 weight rows each) per workgroup
+constexpr int kAhead = 2;   // steps (scale groups) in flight ahead of the one in use
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// the 16 fields of one dense code word as bf16 pairs (2t): out[0..3] hold
+// columns 0-7 of the word, out[4..7] columns 8-15, in column order
+__device__ __forceinline__ void decode_word(uint32_t w, uint32_t (&out)[8]) {
+  const uint32_t a = w & 0xCCCCCCCCu, b = (w << 2) & 0xCCCCCCCCu;
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, 1.0f, 0));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, 1.0f, 1));
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, 1.0f, 2));
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, 1.0f, 3));
+  out[4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 0));
+  out[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 1));
+  out[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 2));
+  out[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 3));
+}
+
+__device__ __forceinline__ bf16x8 pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
+}
+
+// M <= 16; K / 128 >= W; N a multiple of 32 (two tiles per workgroup).
+template <int W, bool OUT_BF16>
+__global__ void __launch_bounds__(64 * W) gemm_skinny_kernel(const uint16_t* __restrict__ x, int M,
+                                                            const uint32_t* __restrict__ codes,
+                                                            const uint16_t* __restrict__ scales, int64_t N,
+                                                            int64_t K, void* __restrict__ y) {
+  __shared__ f32x4 red[W][kTiles][64];                               // each wave's partial result
+  __shared__ __attribute__((aligned(16))) uint32_t xlds[W][16 * 64];  // per wave: [row][chunk ^ row][4]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane & 15, q = lane >> 4;
+  const int64_t G = K / kBlock;
+  const int64_t t0 = (int64_t)blockIdx.x * kTiles;
+  // this wave's scale groups [gb, gb + ng)
+  const int64_t gb = G * w / W;
+  const int ng = (int)(G * (w + 1) / W - gb);
+  // activation staging: load m brings rows 4m + q (clamped to M - 1), 16-byte chunk li
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) xsrc[m] = x + (int64_t)std::min(4 * m + q, M - 1) * K + gb * kBlock + 8 * li;
+  const uint32_t* csrc[kTiles];
+  const uint16_t* ssrc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    csrc[t] = codes + ((t0 + t) * G + gb) * 128 + 2 * lane;
+    // scales [N/16][G][16]: the lane's weight row li of tile t0 + t
+    ssrc[t] = scales + ((t0 + t) * G + gb) * 16 + li;
+  }
+  uint32_t* xl = xlds[w];
+
+  // a ring of kAhead register sets; step s (group (s + rot) % ng of the
+  // slice) lives in set s % kAhead.  Steps past the slice reload its last
+  // group and are not accumulated, so every set is loaded and waited for the
+  // same way on every path.
+  u32x2 cw[kAhead][kTiles];
+  uint16_t sw[kAhead][kTiles];
+  u32x4 xv[kAhead][4];
+  const int rot = (int)(blockIdx.x % (unsigned)ng);
+  auto load = [&](int s, int set) {
+    int g = std::min(s, ng - 1) + rot;
+    g = g >= ng ? g - ng : g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xv[set][m] = *reinterpret_cast<const u32x4*>(xsrc[m] + (int64_t)g * kBlock);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      cw[set][t] = *reinterpret_cast<const u32x2*>(csrc[t] + (int64_t)g * 128);
+      sw[set][t] = ssrc[t][(int64_t)g * 16];
+    }
+  };
+
+  f32x4 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int s, int set) {
+    const bool live = s < ng;
+    // the activations of the group through LDS: written as loaded, read as operands
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 4 * m + q;
+      *reinterpret_cast<u32x4*>(xl + row * 64 + 4 * (li ^ row)) = xv[set][m];
+    }
+    bf16x8 a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      a[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + li * 64 + 4 * ((4 * q + m) ^ li)));
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      uint32_t b0[8], b1[8];
+      decode_word(cw[set][t][0], b0);
+      decode_word(cw[set][t][1], b1);
+      f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], pack4(b0[0], b0[1], b0[2], b0[3]), zero, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], pack4(b0[4], b0[5], b0[6], b0[7]), p, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], pack4(b1[0], b1[1], b1[2], b1[3]), p, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], pack4(b1[4], b1[5], b1[6], b1[7]), p, 0, 0, 0);
+      const float sc = (float)__builtin_bit_cast(_Float16, sw[set][t]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] = live ? __builtin_fmaf(p[r], sc, acc[t][r]) : acc[t][r];
+    }
+  };
+
+  // The scheduling barriers keep each set's loads in issue order between the
+  // steps, so the wait before a step covers that set alone.
+#pragma unroll
+  for (int r = 0; r < kAhead; ++r) {
+    load(r, r);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int s = 0;
+  do {  // ng >= 1
+#pragma unroll
+    for (int r = 0; r < kAhead; ++r) {
+      step(s + r, r);
+      __builtin_amdgcn_sched_barrier(0);
+      load(s + r + kAhead, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s += kAhead;
+  } while (s < ng);
+
+  // lane holds acc[t][r] = 2 y[4q + r][16 (t0 + t) + li]
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) red[w][t][lane] = acc[t];
+  __syncthreads();
+  const float* rf = reinterpret_cast<const float*>(red);
+  for (int e = threadIdx.x; e < kTiles * 256; e += 64 * W) {
+    const int t = e >> 8, m = (e >> 4) & 15, n = e & 15;
+    if (m >= M) continue;
+    const int off = (t * 64 + (m >> 2) * 16 + n) * 4 + (m & 3);
+    float v = rf[off];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) v += rf[ww * kTiles * 256 + off];
+    v *= 0.5f;
+    const int64_t o = (int64_t)m * N + (t0 + t) * 16 + n;
+    if constexpr (OUT_BF16)
+      static_cast<uint16_t*>(y)[o] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      static_cast<float*>(y)[o] = v;
+  }
+}
+
+template <int W>
+hipError_t launch_w(const uint16_t* x, int M, const uint32_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                    void* y, bool bf16_out, hipStream_t stream) {
+  const dim3 grid((unsigned)(N / 16 / kTiles)), block(64 * W);
+  if (bf16_out)
+    hipLaunchKernelGGL((gemm_skinny_kernel<W, true>), grid, block, 0, stream, x, M, codes, scales, N, K, y);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<W, false>), grid, block, 0, stream, x, M, codes, scales, N, K, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_skinny_waves(int64_t N, int64_t K) {
+  // Eight waves per workgroup while the workgroups fit on the compute units
+  // at once (at most 256 of them), four beyond that (measured on the three
+  // layer shapes at M = 16); never more waves than scale groups.
+  const int64_t G = K / kBlock, wgs = N / 16 / kTiles;
+  int w = wgs <= 256 ? 8 : 4;
+  while (w > G) w /= 2;
+  return w;
+}
+
+hipError_t launch_gemm_skinny(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                              int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream) {
+  if (M < 1 || M > kSkinnyMaxRows || N % (16 * kTiles) != 0 || K % kBlock != 0) return hipErrorInvalidValue;
+  const bool bf16 = y_dtype == TB_BF16;
+  switch (gemm_skinny_waves(N, K)) {
+    case 8: return launch_w<8>(x, (int)M, codes, scales, N, K, y, bf16, stream);
+    case 4: return launch_w<4>(x, (int)M, codes, scales, N, K, y, bf16, stream);
+    case 2: return launch_w<2>(x, (int)M, codes, scales, N, K, y, bf16, stream);
+    default: return launch_w<1>(x, (int)M, codes, scales, N, K, y, bf16, stream);
+  }
+}
+
+}  // namespace tb

@@ -32,6 +32,8 @@
 // the tile goes to LDS in fp32, each 16-lane group transforms a row with the
 // in-register butterflies of the activation transform, and the result is
 // rounded once.
+// At most 16 rows of activations take the kernel of gemm_skinny.hip instead
+// (unrotated output; rotated output keeps the path below).
 // Split K (few rows of activations, so few output tiles): workgroup z of S
 // takes the scale groups [G z / S, G (z + 1) / S) and writes its fp32 partial
 // result to a caller-provided workspace; a second kernel adds the S partials
@@ -372,6 +374,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, cons
 
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream) {
+  if (M <= kSkinnyMaxRows) return launch_gemm_skinny(x, M, codes, scales, N, K, y, y_dtype, stream);
   return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, false, 1, stream);
 }
 
@@ -401,6 +404,7 @@ int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_ternary_splitk(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                       int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
                                       size_t workspace_bytes, bool rotate, hipStream_t stream) {
+  if (!rotate && M <= kSkinnyMaxRows) return launch_gemm_skinny(x, M, codes, scales, N, K, y, y_dtype, stream);
   const size_t part = (size_t)M * (size_t)N * sizeof(float);
   const int S = (int)std::min<size_t>((size_t)gemm_splitk_parts(M, N, K), workspace ? workspace_bytes / part : 0);
   if (S <= 1) return launch_gemm(x, M, codes, scales, N, K, y, y_dtype == TB_BF16, rotate, 1, stream);

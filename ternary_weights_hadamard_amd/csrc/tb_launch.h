@@ -22,6 +22,13 @@ hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* m
                                  const uint16_t* scales, int64_t N, int64_t K, float* y, hipStream_t stream);
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream);
+// at most this many activation rows take the mid-batch kernel (gemm_skinny.hip)
+constexpr int kSkinnyMaxRows = 16;
+// waves per workgroup of the mid-batch kernel for this shape
+int gemm_skinny_waves(int64_t N, int64_t K);
+// 1 <= M <= kSkinnyMaxRows; one pass, no workspace
+hipError_t launch_gemm_skinny(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                              int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream);
 // K splits the split-K GEMM uses for this shape (1: none)
 int gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
 // split K when the workspace allows (else one pass); `rotate` rotates the

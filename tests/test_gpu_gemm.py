@@ -108,7 +108,7 @@ def test_gemm_splitk_small_matches_oracle(m, n, k, out):
     assert_close(host_f64(y), ref, f"split-K gemm {m}x{n}x{k} {out}", out_bf16=out == "bf16")
 
 
-@pytest.mark.parametrize("m", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("m", [8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("n,k", [(5120, 5120), (17408, 5120), (5120, 17408)])
 def test_gemm_splitk_mid_batch_sampled(m, n, k):
     say(f"split-K gemm mid-batch M={m} N={n} K={k}")
@@ -155,6 +155,76 @@ def test_gemm_splitk_exact_and_fallbacks():
     assert torch.all(wbuf[:32] == 7.0) and torch.all(wbuf[32 + wsb // 4:] == 7.0)
     assert torch.all(ybuf[:32] == -5.0) and torch.all(ybuf[32 + m * n:] == -5.0)
     assert np.array_equal(host_f64(y), ref)
+
+
+# ---------------------------------------------------------------- mid-batch kernel (M <= 16)
+
+# (n, k) chosen so the kernel runs with 1, 2, 4 and 8 waves per workgroup
+# (K = 128, 384 -> G = 1, 3; N = 8448 -> more than 256 workgroups)
+MID_SHAPES = [(128, 128), (256, 384), (384, 1280), (8448, 512), (1024, 2176)]
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 15, 16])
+@pytest.mark.parametrize("n,k", MID_SHAPES)
+def test_gemm_mid_batch_matches_oracle(m, n, k):
+    say(f"mid-batch gemm M={m} N={n} K={k}")
+    codes = synth.random_code_words(n, k, seed=m + n + k)
+    scales = synth.random_scales_f16(n, k, seed=k + 5)
+    x = synth.gaussian_bf16((m, k), seed=m + 11)
+    ref = oracle.matvec.gemm(x, codes, scales, k)
+    cd, sd, xd = u32_dev(codes), f16_dev(scales), bf16_dev(x)
+    for out in (torch.float32, torch.bfloat16):
+        y = tb.tb_ternary_gemm(xd, cd, sd, out_dtype=out)
+        ys = tb.tb_ternary_gemm_splitk(xd, cd, sd, out_dtype=out)
+        torch.cuda.synchronize()
+        assert_close(host_f64(y), ref, f"mid-batch gemm {m}x{n}x{k} {out}", out_bf16=out == torch.bfloat16)
+        # the split-K entry point takes the same one-pass kernel for M <= 16
+        assert torch.equal(ys, y)
+
+
+def test_gemm_mid_batch_rows_independent_and_exact():
+    # a row's result does not depend on how many rows share the launch, and
+    # with small-integer activations and power-of-two scales every partial sum
+    # is exact, so the result equals the oracle bit for bit
+    n, k = 1024, 2176
+    codes = synth.random_code_words(n, k, seed=70)
+    sc = (2.0 ** np.random.default_rng(71).integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
+    cd, sd = u32_dev(codes), f16_dev(sc)
+    xi = synth.small_int_bf16((16, k), seed=72)
+    y16 = tb.tb_ternary_gemm(bf16_dev(xi), cd, sd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f64(y16), oracle.matvec.gemm(xi, codes, sc, k))
+    xg = synth.gaussian_bf16((16, k), seed=73)
+    yg = tb.tb_ternary_gemm(bf16_dev(xg), cd, sd, out_dtype=torch.float32)
+    for m, r0 in ((1, 0), (3, 5), (9, 7)):
+        ym = tb.tb_ternary_gemm(bf16_dev(xg[r0:r0 + m]), cd, sd, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(ym, yg[r0:r0 + m]), (m, r0)
+
+
+def test_gemm_mid_batch_wide_range_exact_and_canaries():
+    # activations from 2^-100 to 2^20 (one binade per row keeps every sum exact)
+    m, n, k = 16, 256, 1024
+    rng = np.random.default_rng(74)
+    codes = synth.random_code_words(n, k, seed=75)
+    e = rng.integers(-100, 20, size=(m, 1))
+    xv = rng.integers(-8, 9, size=(m, k)).astype(np.float64) * np.exp2(e.astype(np.float64))
+    x = oracle.numerics.f64_to_bf16_bits(xv)
+    sc = (2.0 ** rng.integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
+    ybuf = torch.full((m * n + 256,), -7.0, dtype=torch.float32, device=DEV)
+    y = ybuf[128:128 + m * n].view(m, n)
+    tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(sc), y=y)
+    torch.cuda.synchronize()
+    assert torch.all(ybuf[:128] == -7.0) and torch.all(ybuf[128 + m * n:] == -7.0)
+    assert np.array_equal(host_f64(y), oracle.matvec.gemm(x, codes, sc, k))
+    # M = 5 into a bf16 buffer: rows past M are never written
+    m5 = 5
+    bbuf = torch.full((16 * n + 256,), -3.0, dtype=torch.bfloat16, device=DEV)
+    yb = bbuf[128:128 + m5 * n].view(m5, n)
+    tb.tb_ternary_gemm(bf16_dev(x[:m5]), u32_dev(codes), f16_dev(sc), y=yb)
+    torch.cuda.synchronize()
+    assert torch.all(bbuf[:128] == -3.0) and torch.all(bbuf[128 + m5 * n:] == -3.0)
+    assert_close(host_f64(yb), oracle.matvec.gemm(x[:m5], codes, sc, k), "mid-batch M=5 bf16", out_bf16=True)
 
 
 # ---------------------------------------------------------------- output rotation fused
