@@ -288,7 +288,8 @@ def extra_phases(gen, dev, quick):
     out["prefill_gemm_rotated"] = {"workload": "M=2048, both shapes, y = R_N y' in bf16: fused (tb_ternary_gemm_rotated) "
                                                "vs tb_ternary_gemm fp32 + tb_fwht128", **rot}
 
-    # mid-batch GEMM (split K), M = 16 and 256, the three layer shapes, rotated over weight copies
+    # mid-batch GEMM, M = 16 (the one-pass kernel for M <= 16) and 256 (split K), the three layer
+    # shapes, rotated over weight copies
     mid = {}
     for k, n in ((D, D), (D, F), (F, D)):
         copies = 8
@@ -305,14 +306,18 @@ def extra_phases(gen, dev, quick):
 
             us = time_eager(runm, 2 if quick else 5) * 1e3 / copies
             wbytes = n * k // 4 + n * k // 64
-            mid[f"M{m}_{k}x{n}"] = {"us": round(us, 2), "splits": wsb // (m * n * 4) if wsb else 1,
+            mid[f"M{m}_{k}x{n}"] = {"us": round(us, 2),
+                                    "kernel": "gemm_skinny_kernel" if m <= 16 else "gemm_ternary_kernel + splitk_reduce_kernel",
+                                    "splits": 1 if m <= 16 else (wsb // (m * n * 4) if wsb else 1),
                                     "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1),
-                                    "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)}
+                                    "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                                    "weight_frac_of_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
             log(f"  mid-batch GEMM M={m} K={k} N={n}: {us:.1f} us")
             del x, y, work
         del ws
-    out["midbatch_gemm"] = {"workload": "tb_ternary_gemm_splitk, M = 16 and 256, (K, N) = (5120, 5120), (5120, 17408), "
-                                        "(17408, 5120), bf16 out, 8 weight copies rotated, eager launches",
+    out["midbatch_gemm"] = {"workload": "tb_ternary_gemm_splitk (M <= 16 runs the one-pass mid-batch kernel), M = 16 "
+                                        "and 256, (K, N) = (5120, 5120), (5120, 17408), (17408, 5120), bf16 out, 8 weight "
+                                        "copies rotated, eager launches",
                             **mid}
 
     # 2:4 GEMV, 17408 x 5120, batch 1, rotated over >= 1 GB of weight copies
@@ -537,7 +542,7 @@ def profile_pass(dev, kind):
       gemm      the prefill GEMM, M = 2048, both FFN shapes, twice each;
       gemv24    the 2:4 GEMV, 17408 x 5120, batch 1, over 16 weight copies;
       quant     the quantiser on one layer of the stack recipe, twice;
-      midbatch  the split-K GEMM at M = 16 on the three layer shapes, 4 copies;
+      midbatch  the mid-batch GEMM (M = 16) on the three layer shapes, 4 copies;
       ceiling   the streaming-read probe over 256 MiB, 3 times."""
     import torch
 
@@ -585,10 +590,8 @@ def profile_pass(dev, kind):
             ws = [(synth.torch_code_words(n, k, gen, dev), synth.torch_scales_f16(n, k, gen, dev)) for _ in range(4)]
             x = synth.torch_gaussian_bf16((16, k), gen, dev)
             y = torch.empty((16, n), dtype=torch.bfloat16, device=dev)
-            wsb = tb.tb_ternary_gemm_splitk_workspace(16, n, k)
-            work = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev)
             for c, sc in ws:
-                tb.tb_ternary_gemm_splitk(x, c, sc, y=y, workspace=work)
+                tb.tb_ternary_gemm(x, c, sc, y=y)
             torch.cuda.synchronize()
             del ws
     elif kind == "ceiling":
