@@ -718,7 +718,7 @@ def summarize_kernel_stats(stats_csv, out_path, command):
              "# the input generation outside the timed regions is left out)", f"#   {command}",
              "# kernel | calls | average us | total us | share of libtb kernel time", ""]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        short = r["Name"].replace("void tb::(anonymous namespace)::", "").split("(")[0]
+        short = r["Name"].replace("void ", "").replace("tb::(anonymous namespace)::", "").split("(")[0]
         lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / total * 100:.1f}%")
     with open(out_path, "w") as fh:
