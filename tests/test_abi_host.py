@@ -36,6 +36,30 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(tb.SIGNATURES), "binding and header disagree"
 
 
+PROBE_HEADER = os.path.join(ROOT, "include", "tb_probe.h")
+PROBE_LIB = os.path.join(os.path.dirname(tb.LIB_PATH), "libtb_probe.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBE_LIB), reason="libtb_probe.so not built")
+def test_probe_library_exports_and_validates():
+    names = sorted(set(re.findall(r"\b(tbp_[a-z0-9_]+)\s*\(", open(PROBE_HEADER).read())))
+    assert names == ["tbp_mfma_bf16", "tbp_stream_read"]
+    L = ctypes.CDLL(PROBE_LIB)
+    for n in names:
+        assert hasattr(L, n), n
+    L.tbp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.tbp_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    invalid = 1  # hipErrorInvalidValue, returned before any HIP call
+    assert L.tbp_stream_read(None, 4096, _v(B), 1, None) == invalid
+    assert L.tbp_stream_read(_v(A), 4096, None, 1, None) == invalid
+    assert L.tbp_stream_read(_v(A), 4000, _v(B), 1, None) == invalid      # not a multiple of 4096
+    assert L.tbp_stream_read(_v(MIS), 4096, _v(B), 1, None) == invalid    # not 16-byte aligned
+    assert L.tbp_stream_read(_v(A), 4096, _v(B), 0, None) == invalid
+    assert L.tbp_mfma_bf16(None, 10, 1, None) == invalid
+    assert L.tbp_mfma_bf16(_v(B), 0, 1, None) == invalid
+    assert L.tbp_mfma_bf16(_v(B), 10, 0, None) == invalid
+
+
 def test_status_strings_and_version():
     L = tb.lib()
     assert L.tb_version() >= 100
