@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_MFMA_TFLOPS = 2500.0    # dense fp16 / bf16 matrix cores
 D, F = 5120, 17408
+DOWN_PARTS = 4  # K parts of the batch-1 down projection (tb_gemv_segment.parts)
 FUSED = (("qkv", 3 * D, D), ("o", D, D), ("gate_up", 2 * F, D), ("down", D, F))
 
 
@@ -109,9 +110,14 @@ class DecodeStack:
         from ternary_weights_hadamard_amd import tb
 
         self.batch = batch
+        # At batch 1 the long-K down projection (320 tiles of 16 rows) splits its K
+        # over DOWN_PARTS workgroups per tile; the parts are added by the rotation
+        # launch that follows (tb_fwht_segment.x_parts), so the split costs no launch
+        self.parts = [DOWN_PARTS if batch == 1 and self.planes == 1 and k == F else 1 for _, n, k in FUSED]
         self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
         self.act = [torch.empty(tb.tb_act8_bytes(batch, k), dtype=torch.uint8, device=dev) for _, n, k in FUSED]
-        self.yr = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+        self.yr = [torch.empty((p, batch, n) if p > 1 else (batch, n), dtype=torch.float32, device=dev)
+                   for p, (_, n, k) in zip(self.parts, FUSED)]
         self.y = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
 
     def gemv_calls(self, layer):
@@ -120,7 +126,7 @@ class DecodeStack:
         projection on its own ("split")."""
         from ternary_weights_hadamard_amd import tb
 
-        segs = [(self.act[j], codes, scales, self.batch, self.yr[j], self.planes)
+        segs = [(self.act[j], codes, scales, self.batch, self.yr[j], self.planes, self.parts[j])
                 for j, (codes, scales, n, k) in enumerate(layer)]
         if self.grouping == "layer":
             tb.tb_ternary_gemv_multi(segs)
@@ -141,7 +147,7 @@ class DecodeStack:
         from ternary_weights_hadamard_amd import tb
 
         rot_in = list(zip(self.x, self.act))
-        rot_out = list(zip(self.yr, self.y))
+        rot_out = list(zip(self.yr, self.y, self.parts))
         for li, layer in enumerate(self.w):
             if merged:
                 tb.tb_fwht128_multi((rot_out if li > 0 else []) + rot_in)
@@ -160,9 +166,10 @@ class DecodeStack:
 
         for layer in self.w:
             for j, (codes, scales, n, k) in enumerate(layer):
+                yr = self.yr[j][0] if self.parts[j] > 1 else self.yr[j]  # one product, no parts
                 tb.tb_fwht128(self.x[j], y=self.act[j])
-                tb.tb_ternary_gemv(self.act[j], codes, scales, self.batch, y=self.yr[j])
-                tb.tb_fwht128(self.yr[j], y=self.y[j])
+                tb.tb_ternary_gemv(self.act[j], codes, scales, self.batch, y=yr)
+                tb.tb_fwht128(yr, y=self.y[j])
 
     def gemv_only(self):
         for layer in self.w:

@@ -115,8 +115,18 @@ typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_
 /* Most segments one grouped call (tb_fwht128_multi, tb_ternary_gemv_multi) takes. */
 #define TB_MAX_SEGMENTS 8
 
+/* Most K parts of one GEMV segment (tb_gemv_segment.parts) and most partial
+ * inputs of one rotation segment (tb_fwht_segment.x_parts). */
+#define TB_MAX_PARTS 8
+
 /* One array of a grouped tb_fwht128_multi call: arguments as in tb_fwht128,
- * each segment with its own input and output dtypes. */
+ * each segment with its own input and output dtypes.
+ * x_parts (0 or 1: x is [rows][K]) greater than 1 makes x the x_parts
+ * partial results [x_parts][rows][K] of a split product (tb_gemv_segment
+ * with parts = x_parts): they are added in part order, in fp32, and the sum
+ * is transformed, so the reduction of the split GEMV costs no launch of its
+ * own.  Only with x_dtype TB_F32, at most TB_MAX_PARTS, and y must not overlap
+ * any part (else TB_ERR_DTYPE, TB_ERR_SHAPE, TB_ERR_ALIAS). */
 typedef struct {
   const void* x;
   void* y;
@@ -124,12 +134,23 @@ typedef struct {
   int64_t K;
   int x_dtype;
   int y_dtype;
+  int x_parts;
+  int reserved;  /* must be 0 */
 } tb_fwht_segment;
 
 /* One product of a grouped tb_ternary_gemv_multi call: arguments as in
  * tb_ternary_gemv.  `planes` is 1 for the one-plane dense formats (0 is read
  * as 1) and 2 for two-plane codes and scales (TB_FMT_DENSE_RESID, as
- * tb_ternary_gemv_resid takes them); anything else returns TB_ERR_FORMAT. */
+ * tb_ternary_gemv_resid takes them); anything else returns TB_ERR_FORMAT.
+ * `parts` (0 or 1: y is [B][N]) of 2, 4 or 8 splits the product's K over
+ * that many workgroups per 16-row tile, for a long-K product with too few
+ * tiles to fill the GPU (a 27B layer's down projection: 320 tiles): y is
+ * then [parts][B][N], part p holding the sum over the scale groups
+ * [floor(G p / parts), floor(G (p + 1) / parts)) (G = K/128 per plane times
+ * planes), so the product is the sum of the parts in part order.
+ * tb_fwht128_multi adds them on the way into the output rotation
+ * (tb_fwht_segment.x_parts).  Batch 1 only, G >= parts (else
+ * TB_ERR_UNSUPPORTED, TB_ERR_SHAPE). */
 typedef struct {
   const uint8_t* act;
   int64_t B;
@@ -139,6 +160,7 @@ typedef struct {
   int64_t K;
   float* y;
   int64_t planes;
+  int64_t parts;
 } tb_gemv_segment;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -286,7 +308,9 @@ TB_API tb_status tb_ternary_gemv_noalloc(const uint16_t* x, int64_t B, const uin
  * the GPU idle), each given its TB_ACT8 operand (`act`, as tb_ternary_gemv
  * with x_dtype TB_ACT8); each segment is validated and computed as tb_ternary_gemv,
  * and its result is bit for bit that of the single call (how a segment's sum is
- * split and ordered depends only on its own shape and batch).
+ * split and ordered depends only on its own shape, batch and parts).
+ * A segment with parts > 1 writes its parts instead of the product (see
+ * tb_gemv_segment; y then spans parts * B * N floats).
  * `segs` is a host array read during the call; no segment's y may overlap any
  * segment's inputs or another y.  count == 0 is a no-op; count outside
  * [0, TB_MAX_SEGMENTS] returns TB_ERR_SHAPE.

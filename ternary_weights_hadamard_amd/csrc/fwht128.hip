@@ -36,7 +36,8 @@ struct FwhtSeg {
   const void* x;
   void* y;
   int64_t nblocks, begin;
-  int kind, pad;  // 3 * (x bf16 ? 1 : 0) + OutKind
+  int kind;   // 3 * (x bf16 ? 1 : 0) + OutKind
+  int parts;  // fp32 input only: x holds `parts` partial arrays, added in order first
 };
 
 struct FwhtSegs {
@@ -47,9 +48,11 @@ struct FwhtSegs {
 
 // One 128-block per 16 lanes: block b of a segment of nblocks blocks; lanes
 // past the end (b >= nblocks) run the cross-lane rounds on zeros and store
-// nothing.
+// nothing.  An fp32 input of `parts` > 1 partial arrays (nblocks blocks
+// apart) is their sum, taken in part order.
 template <bool IN_BF16, int OUT, bool XFORM>
-__device__ __forceinline__ void fwht_block(const void* x, void* y, int64_t nblocks, int64_t b, int sub) {
+__device__ __forceinline__ void fwht_block(const void* x, void* y, int64_t nblocks, int64_t b, int sub,
+                                           int parts = 1) {
   const bool live = b < nblocks;
   const int64_t base = b * kBlock + sub * 8;
   float v[8];
@@ -67,6 +70,15 @@ __device__ __forceinline__ void fwht_block(const void* x, void* y, int64_t nbloc
       const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + base);
       a = p[0];
       c = p[1];
+      for (int pp = 1; pp < parts; ++pp) {
+        const f32x4* pn = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + pp * nblocks * kBlock + base);
+        const f32x4 a2 = pn[0], c2 = pn[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] += a2[i];
+          c[i] += c2[i];
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,7 +136,7 @@ __global__ void __launch_bounds__(64) fwht128_kernel(FwhtSegs segs) {
   for (int64_t bw = (int64_t)blockIdx.x * 4; bw < segs.total; bw += (int64_t)gridDim.x * 4) {
     const int seg = wave_segment(segs, bw);
     const int64_t b = bw - segs.s[seg].begin + (threadIdx.x >> 4);  // block inside its segment
-    fwht_block<IN_BF16, OUT, XFORM>(segs.s[seg].x, segs.s[seg].y, segs.s[seg].nblocks, b, sub);
+    fwht_block<IN_BF16, OUT, XFORM>(segs.s[seg].x, segs.s[seg].y, segs.s[seg].nblocks, b, sub, segs.s[seg].parts);
   }
 }
 
@@ -137,9 +149,9 @@ __global__ void __launch_bounds__(64) fwht128_mixed_kernel(FwhtSegs segs) {
     const FwhtSeg& sg = segs.s[seg];
     const int64_t b = bw - sg.begin + (threadIdx.x >> 4);
     switch (__builtin_amdgcn_readfirstlane(sg.kind)) {
-      case 0: fwht_block<false, kOutF32, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
-      case 1: fwht_block<false, kOutBF16, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
-      case 2: fwht_block<false, kOutAct8, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
+      case 0: fwht_block<false, kOutF32, true>(sg.x, sg.y, sg.nblocks, b, sub, sg.parts); break;
+      case 1: fwht_block<false, kOutBF16, true>(sg.x, sg.y, sg.nblocks, b, sub, sg.parts); break;
+      case 2: fwht_block<false, kOutAct8, true>(sg.x, sg.y, sg.nblocks, b, sub, sg.parts); break;
       case 3: fwht_block<true, kOutF32, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
       case 4: fwht_block<true, kOutBF16, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
       default: fwht_block<true, kOutAct8, true>(sg.x, sg.y, sg.nblocks, b, sub); break;
@@ -177,7 +189,7 @@ hipError_t launch_segments(const FwhtSegs& segs, int x_dtype, int y_dtype, hipSt
 
 FwhtSegs one_segment(const void* x, void* y, int64_t nblocks) {
   FwhtSegs s{};
-  s.s[0] = FwhtSeg{x, y, nblocks, 0, 0, 0};
+  s.s[0] = FwhtSeg{x, y, nblocks, 0, 0, 1};
   s.count = 1;
   s.total = nblocks;
   return s;
@@ -196,7 +208,8 @@ hipError_t launch_fwht128_multi(const tb_fwht_segment* segs, int count, hipStrea
   bool same = true;
   for (int c = 0; c < count; ++c) {
     const int64_t nb = segs[c].rows * (segs[c].K / kBlock);
-    s.s[c] = FwhtSeg{segs[c].x, segs[c].y, nb, total, seg_kind(segs[c].x_dtype, segs[c].y_dtype), 0};
+    s.s[c] = FwhtSeg{segs[c].x, segs[c].y, nb, total, seg_kind(segs[c].x_dtype, segs[c].y_dtype),
+                     segs[c].x_parts > 1 ? segs[c].x_parts : 1};
     total += (nb + 3) / 4 * 4;  // the next segment starts on a wave boundary
     same = same && s.s[c].kind == s.s[0].kind;
   }

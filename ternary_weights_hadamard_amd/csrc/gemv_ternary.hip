@@ -72,7 +72,8 @@ struct StagedSeg {
   const uint16_t* scales;
   float* y;
   int64_t N, K;
-  int B, ks, wg_begin, pad;
+  int B, ks, wg_begin;
+  int lgp;  // log2 of the segment's K parts: workgroups per tile, each writing its part of y
 };
 
 struct StagedSegs {
@@ -111,17 +112,23 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const StagedSeg sg = pick_segment(segs);
   const uint8_t* __restrict__ act = sg.act;
-  const int B = sg.B, KS = sg.ks;
+  const int B = sg.B, KS = sg.ks;  // K slices of a tile, over all its parts
   const int64_t N = sg.N, K = sg.K;
   const int waves = (int)(blockDim.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // KS and waves are powers of two (waves the largest KS of the launch), so
-  // the slice arithmetic is shifts and masks: a wave starts its loads sooner
+  // KS, the parts and waves are powers of two (waves the largest slices per
+  // part of the launch), so the slice arithmetic is shifts and masks: a wave
+  // starts its loads sooner.  A tile's parts are consecutive workgroups; part
+  // p adds slices [p KSW, (p + 1) KSW), KSW = KS / parts, one per wave.
   const int lg = __builtin_ctz((unsigned)KS);
-  const int ks = w & (KS - 1);
+  const int lgp = sg.lgp, lgw = lg - lgp;
+  const int64_t wgl = (int64_t)(blockIdx.x - sg.wg_begin);
+  const int part = (int)(wgl & ((1 << lgp) - 1));
+  const int ksw = w & ((1 << lgw) - 1);
+  const int ks = (part << lgw) + ksw;
   const int i = lane & 15, q = lane >> 4;
-  const int64_t nb0 = ((int64_t)(blockIdx.x - sg.wg_begin) * (waves >> lg) + (w >> lg)) * T;
+  const int64_t nb0 = ((wgl >> lgp) * (waves >> lgw) + (w >> lgw)) * T;
   const int64_t ntiles = (int64_t)((uint64_t)N >> 4);
   const bool live = nb0 < ntiles;
   const int GA = (int)((uint64_t)K >> 7);  // activation groups per row
@@ -266,18 +273,18 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_staged_kernel(StagedSegs
     }
   }
 
-  if (KS > 1) {
+  if (lgw > 0) {
 #pragma unroll
     for (int t = 0; t < T; ++t) red[(w * T + t) * 64 + lane] = acc[t];
     __syncthreads();
-    if (ks != 0) return;
+    if (ksw != 0) return;
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      for (int u = 1; u < KS; ++u) acc[t] += red[((w + u) * T + t) * 64 + lane];
+      for (int u = 1; u < (1 << lgw); ++u) acc[t] += red[((w + u) * T + t) * 64 + lane];
   }
 #pragma unroll
   for (int t = 0; t < T; ++t)
-    if (nb0 + t < ntiles && q < B) sg.y[(size_t)q * N + 16 * (nb0 + t) + i] = acc[t];
+    if (nb0 + t < ntiles && q < B) sg.y[((size_t)part * B + q) * N + 16 * (nb0 + t) + i] = acc[t];
 }
 
 // Wide path (B > 4, or a K too long for the staged slices).  A batch quad's
@@ -476,6 +483,24 @@ int segment_ch(int64_t K) {
   return ks != 0 && ks <= 8 ? kStagedCH : kLongCH;
 }
 
+// K slices of a staged segment's tiles (over all its parts) and its groups per
+// wave.  A segment split into parts takes the short slices (at most
+// kStagedCH groups) and at least one slice per part.
+void staged_geometry(const GemvSegment& g, int& ks, int& ch) {
+  const int64_t kc = g.K * g.planes;  // code groups x 128
+  if (g.parts > 1) {
+    ch = kStagedCH;
+    ks = std::max(staged_slices(kc, ch), (int)g.parts);
+  } else {
+    ch = segment_ch(kc);
+    ks = staged_slices(kc, ch);
+  }
+}
+
+bool gemv_parts_supported(const GemvSegment& g) {
+  return g.B == 1 && staged_slices(g.K * g.planes, kStagedCH) != 0 && g.parts <= kMaxSlices;
+}
+
 // The staged path takes a batch-1 segment whose K fits the staged slices;
 // everything else takes the wide path (from batch 2 on it is the faster one:
 // 27 against 40 us at batch 2 on a 27B layer's QKV + O + gate/up).
@@ -559,12 +584,11 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
   int bmax = 1, ch = 1, waves = 1, wg = 0;
   const int64_t planes = count > 0 ? segs[0].planes : 1;
   for (int c = 0; c < count && staged; ++c) {
-    const int64_t kc = segs[c].K * segs[c].planes;  // code groups x 128
-    const int sc = segment_ch(kc);
-    const int ks = staged_slices(kc, sc);
+    int ks = 0, sc = 0;
+    staged_geometry(segs[c], ks, sc);
     bmax = std::max(bmax, (int)segs[c].B);
     ch = std::max(ch, sc);
-    waves = std::max(waves, ks);
+    waves = std::max(waves, ks / (int)segs[c].parts);
     if (segs[c].planes != planes) staged = false;  // one plane count per grouped launch
   }
   // a slice of at most ch code groups spans at most ch activation groups with
@@ -580,12 +604,13 @@ hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t str
   const size_t lds = (size_t)waves * bmax * stage_groups * kStageBytes + (size_t)waves * LT * 64 * sizeof(float);
   if (staged && lds <= kStagedMaxLds) {
     for (int c = 0; c < count; ++c) {
-      const int64_t kc = segs[c].K * segs[c].planes;
-      const int ks = staged_slices(kc, segment_ch(kc));
-      const int64_t tiles = segs[c].N / 16, per_wg = waves / ks * LT;
+      int ks = 0, sc = 0;
+      staged_geometry(segs[c], ks, sc);
+      const int parts = (int)segs[c].parts;
+      const int64_t tiles = segs[c].N / 16, per_wg = waves / (ks / parts) * LT;
       st.s[c] = StagedSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
-                          (int)segs[c].B, ks, wg, 0};
-      wg += (int)((tiles + per_wg - 1) / per_wg);
+                          (int)segs[c].B, ks, wg, __builtin_ctz((unsigned)parts)};
+      wg += (int)((tiles + per_wg - 1) / per_wg * parts);
     }
     st.count = count;
     st.bmax = bmax;

@@ -51,17 +51,32 @@ tb_status check_fwht(const void* x, int x_dtype, const void* y, int y_dtype, int
 // code planes of a GEMV segment (0 is read as 1), or 0 when invalid
 int64_t gemv_planes(const tb_gemv_segment& g) { return g.planes == 0 ? 1 : (g.planes == 1 || g.planes == 2) ? g.planes : 0; }
 
+// K parts of a GEMV segment (0 is read as 1), or 0 when invalid
+int64_t gemv_parts(const tb_gemv_segment& g) {
+  return g.parts == 0 || g.parts == 1 ? 1 : (g.parts == 2 || g.parts == 4 || g.parts == 8) ? g.parts : 0;
+}
+
+// bytes of a GEMV segment's output: its parts of [B][N] fp32
+size_t gemv_y_bytes(const tb_gemv_segment& g) { return (size_t)gemv_parts(g) * (size_t)g.B * (size_t)g.N * 4; }
+
 // bytes of a GEMV segment's codes and scales (all planes)
 size_t gemv_code_bytes(const tb_gemv_segment& g) { return (size_t)gemv_planes(g) * (size_t)g.N * (size_t)g.K / 4; }
 size_t gemv_scale_bytes(const tb_gemv_segment& g) { return (size_t)gemv_planes(g) * (size_t)g.N * (size_t)g.K / 64; }
 
 tb_status check_gemv(const tb_gemv_segment& g) {
   if (gemv_planes(g) == 0) return TB_ERR_FORMAT;
-  if (!dims_ok(g.N, g.K) || g.B < 0 || g.B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+  if (!dims_ok(g.N, g.K) || g.B < 0 || g.B > TB_GEMV_MAX_BATCH || gemv_parts(g) == 0) return TB_ERR_SHAPE;
+  if (gemv_parts(g) > 1) {
+    if (g.K / kGroup * gemv_planes(g) < gemv_parts(g)) return TB_ERR_SHAPE;  // every part at least one group
+    tb_gemv_segment n = g;
+    n.planes = gemv_planes(g);
+    n.parts = gemv_parts(g);
+    if (g.B > 1 || (g.B == 1 && !tb::gemv_parts_supported(n))) return TB_ERR_UNSUPPORTED;
+  }
   if (g.B == 0) return TB_OK;
   if (!g.act || !g.codes || !g.scales || !g.y) return TB_ERR_NULL;
   if (!aligned16(g.act) || !aligned16(g.codes) || !aligned16(g.scales) || !aligned16(g.y)) return TB_ERR_ALIGN;
-  const size_t yb = (size_t)g.B * (size_t)g.N * 4;
+  const size_t yb = gemv_y_bytes(g);
   if (overlap(g.y, yb, g.act, act8_bytes((size_t)g.B * g.K)) || overlap(g.y, yb, g.codes, gemv_code_bytes(g)) ||
       overlap(g.y, yb, g.scales, gemv_scale_bytes(g)))
     return TB_ERR_ALIAS;
@@ -99,12 +114,12 @@ tb_status gemv_call(const void* x, int x_dtype, int64_t B, const uint32_t* codes
                     int64_t K, float* y, void* workspace, size_t workspace_bytes, int64_t planes, hipStream_t stream) {
   if (x_dtype != TB_BF16 && x_dtype != TB_ACT8) return TB_ERR_DTYPE;
   if (x_dtype == TB_ACT8) {
-    const tb_gemv_segment g{static_cast<const uint8_t*>(x), B, codes, scales, N, K, y, planes};
+    const tb_gemv_segment g{static_cast<const uint8_t*>(x), B, codes, scales, N, K, y, planes, 1};
     const tb_status st = check_gemv(g);
     if (st != TB_OK || B == 0) return st;
     return launched(tb::launch_gemv_multi(&g, 1, stream));
   }
-  const tb_gemv_segment g{static_cast<const uint8_t*>(workspace), B, codes, scales, N, K, y, planes};
+  const tb_gemv_segment g{static_cast<const uint8_t*>(workspace), B, codes, scales, N, K, y, planes, 1};
   const tb_status st = check_gemv_bf16(x, g);
   if (st != TB_OK || B == 0) return st;
   const size_t ab = act8_bytes((size_t)B * (size_t)K);
@@ -181,7 +196,7 @@ const char* tb_status_string(int status) {
   }
 }
 
-int tb_version(void) { return 200; }
+int tb_version(void) { return 300; }
 
 size_t tb_act8_bytes(int64_t B, int64_t K) {
   if (B < 0 || K <= 0 || K % kGroup) return 0;
@@ -214,13 +229,21 @@ tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, void* stream)
   int n = 0;
   for (int c = 0; c < count; ++c) {
     const tb_fwht_segment& a = segs[c];
+    if (a.reserved != 0 || a.x_parts < 0 || a.x_parts > TB_MAX_PARTS) return TB_ERR_SHAPE;
+    const int ap = a.x_parts > 1 ? a.x_parts : 1;
+    if (ap > 1 && a.x_dtype != TB_F32) return TB_ERR_DTYPE;
     const tb_status st = check_fwht(a.x, a.x_dtype, a.y, a.y_dtype, a.rows, a.K);
     if (st != TB_OK) return st;
+    // the partial inputs may not be overwritten while other lanes still read them
+    if (ap > 1 && a.rows > 0 &&
+        overlap(a.x, ap * fwht_in_bytes(a.rows, a.K, a.x_dtype), a.y, fwht_out_bytes(a.rows, a.K, a.y_dtype)))
+      return TB_ERR_ALIAS;
     for (int d = 0; d < c; ++d) {
       const tb_fwht_segment& b = segs[d];
       if (a.rows == 0 || b.rows == 0) continue;
-      const size_t ai = fwht_in_bytes(a.rows, a.K, a.x_dtype), ao = fwht_out_bytes(a.rows, a.K, a.y_dtype);
-      const size_t bi = fwht_in_bytes(b.rows, b.K, b.x_dtype), bo = fwht_out_bytes(b.rows, b.K, b.y_dtype);
+      const int bp = b.x_parts > 1 ? b.x_parts : 1;
+      const size_t ai = ap * fwht_in_bytes(a.rows, a.K, a.x_dtype), ao = fwht_out_bytes(a.rows, a.K, a.y_dtype);
+      const size_t bi = bp * fwht_in_bytes(b.rows, b.K, b.x_dtype), bo = fwht_out_bytes(b.rows, b.K, b.y_dtype);
       if (overlap(a.y, ao, b.y, bo) || overlap(a.y, ao, b.x, bi) || overlap(b.y, bo, a.x, ai)) return TB_ERR_ALIAS;
     }
     if (a.rows > 0) live[n++] = a;
@@ -265,7 +288,7 @@ tb_status tb_ternary_gemv(const void* x, int x_dtype, int64_t B, const uint32_t*
 
 tb_status tb_ternary_gemv_noalloc(const uint16_t* x, int64_t B, const uint32_t* codes, const uint16_t* scales,
                                   int64_t N, int64_t K, float* y, void* stream) {
-  tb_gemv_segment g{nullptr, B, codes, scales, N, K, y, 1};
+  tb_gemv_segment g{nullptr, B, codes, scales, N, K, y, 1, 1};
   tb_status st = check_gemv_bf16(x, g);
   if (st != TB_OK || B == 0) return st;
   if (act8_bytes((size_t)B * (size_t)K) > (size_t)TB_NOALLOC_SCRATCH_BYTES) return TB_ERR_WORKSPACE;
@@ -293,17 +316,17 @@ tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* st
     const tb_status st = check_gemv(a);
     if (st != TB_OK) return st;
     if (a.B == 0) continue;
-    const size_t ay = (size_t)a.B * (size_t)a.N * 4;
+    const size_t ay = gemv_y_bytes(a);
     for (int d = 0; d < count; ++d) {
       const tb_gemv_segment& b = segs[d];
       if (d == c || b.B == 0) continue;
       if (overlap(a.y, ay, b.act, act8_bytes((size_t)b.B * b.K)) || overlap(a.y, ay, b.codes, gemv_code_bytes(b)) ||
-          overlap(a.y, ay, b.scales, gemv_scale_bytes(b)) ||
-          (d < c && overlap(a.y, ay, b.y, (size_t)b.B * (size_t)b.N * 4)))
+          overlap(a.y, ay, b.scales, gemv_scale_bytes(b)) || (d < c && overlap(a.y, ay, b.y, gemv_y_bytes(b))))
         return TB_ERR_ALIAS;
     }
     live[n] = a;
-    live[n++].planes = gemv_planes(a);
+    live[n].planes = gemv_planes(a);
+    live[n++].parts = gemv_parts(a);
   }
   if (n == 0) return TB_OK;
   return launched(tb::launch_gemv_multi(live, n, as_stream(stream)));

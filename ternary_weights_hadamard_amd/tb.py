@@ -39,13 +39,14 @@ _int = ctypes.c_int
 
 class FwhtSegment(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("x_dtype", ctypes.c_int), ("y_dtype", ctypes.c_int)]
+                ("x_dtype", ctypes.c_int), ("y_dtype", ctypes.c_int), ("x_parts", ctypes.c_int),
+                ("reserved", ctypes.c_int)]
 
 
 class GemvSegment(ctypes.Structure):
     _fields_ = [("act", ctypes.c_void_p), ("B", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p),
-                ("planes", ctypes.c_int64)]
+                ("planes", ctypes.c_int64), ("parts", ctypes.c_int64)]
 
 
 SIGNATURES = {
@@ -153,16 +154,26 @@ def tb_fwht128(x, y=None, out_dtype=None, stream=None):
 
 
 def tb_fwht128_multi(pairs, stream=None):
-    """One launch rotating several arrays: pairs = [(x, y), ...], each with its
-    own dtypes (a uint8 y means the act8 operand)."""
+    """One launch rotating several arrays: pairs = [(x, y), ...] or
+    [(x, y, x_parts), ...], each with its own dtypes (a uint8 y means the act8
+    operand).  With x_parts > 1, x is [x_parts, rows, K] fp32 partial results
+    added in order before the transform (y is [rows, K])."""
     if not pairs:
         return
-    for x, y in pairs:
-        _dev(x, y)
+    for p in pairs:
+        _dev(p[0], p[1])
     arr = (FwhtSegment * len(pairs))()
-    for c, (x, y) in enumerate(pairs):
-        rows = x.numel() // x.shape[-1] if x.numel() else 0
-        arr[c] = FwhtSegment(x.data_ptr(), y.data_ptr(), rows, x.shape[-1], _dt(x), _dt(y))
+    for c, p in enumerate(pairs):
+        x, y = p[0], p[1]
+        parts = int(p[2]) if len(p) > 2 else 1
+        if parts > 1:
+            if x.dim() < 2 or x.shape[0] != parts:
+                raise TBError(f"tb_fwht128_multi: x_parts={parts} needs x of shape [{parts}, rows, K], got {tuple(x.shape)}")
+            inner = x[0]
+        else:
+            inner = x
+        rows = inner.numel() // inner.shape[-1] if inner.numel() else 0
+        arr[c] = FwhtSegment(x.data_ptr(), y.data_ptr(), rows, x.shape[-1], _dt(x), _dt(y), parts, 0)
     _check(lib().tb_fwht128_multi(arr, len(pairs), _stream(stream)), "tb_fwht128_multi")
 
 
@@ -273,20 +284,24 @@ def tb_ternary_gemv_resid(x, codes, scales, batch=None, y=None, workspace=None, 
 
 
 def tb_ternary_gemv_multi(segments, stream=None):
-    """One launch of several GEMVs: segments = [(act, codes, scales, batch, y[, planes]), ...];
-    planes is 1 (default) or 2 for two-plane weights."""
+    """One launch of several GEMVs: segments = [(act, codes, scales, batch, y[, planes[, parts]]), ...];
+    planes is 1 (default) or 2 for two-plane weights; parts > 1 (batch 1) splits K over that many
+    workgroups per tile and y receives the parts, [parts, batch, N], whose sum is the product."""
     if not segments:
         return
     arr = (GemvSegment * len(segments))()
     for c, seg in enumerate(segments):
         act, codes, scales, batch, y = seg[:5]
         planes = int(seg[5]) if len(seg) > 5 else 1
+        parts = int(seg[6]) if len(seg) > 6 else 1
         _dev(act, codes, scales, y)
         n, g = _dense_n(scales), scales.shape[1]
         k = g // max(planes, 1) * 128
         _act8_operand(act, int(batch), k, "tb_ternary_gemv_multi")
+        if y.numel() < max(parts, 1) * int(batch) * n:
+            raise TBError(f"tb_ternary_gemv_multi: y holds {y.numel()} floats, needs {max(parts, 1)} x {batch} x {n}")
         arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n, k, y.data_ptr(),
-                             planes)
+                             planes, parts)
     _check(lib().tb_ternary_gemv_multi(arr, len(segments), _stream(stream)), "tb_ternary_gemv_multi")
 
 

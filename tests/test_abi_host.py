@@ -232,6 +232,37 @@ def test_grouped_validation():
     assert L.tb_ternary_gemv_multi(shape, 1, s) == 2
 
 
+def test_split_gemv_and_summing_rotation_validation():
+    # tb_gemv_segment.parts: K split over workgroups, y holding the parts
+    L = tb.lib()
+    s = None
+    F, Gs = tb.FwhtSegment, tb.GemvSegment
+    one = lambda *seg: (Gs * 1)(Gs(*seg))
+    assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 1024, D, 1, 3), 1, s) == 2       # parts not 1, 2, 4, 8
+    assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 1024, D, 1, 16), 1, s) == 2
+    assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 384, D, 1, 4), 1, s) == 2        # 3 groups < 4 parts
+    assert L.tb_ternary_gemv_multi(one(A, 2, B, C, 128, 1024, D, 1, 2), 1, s) == 7       # batch 1 only
+    assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 128 * 161, D, 1, 2), 1, s) == 7  # K past the short slices
+    assert L.tb_ternary_gemv_multi(one(A, 0, B, C, 128, 1024, D, 1, 2), 1, s) == 0       # empty batch: no-op
+    # two parts of [1][128] fp32 span 1 KB: a second y 512 bytes on overlaps them
+    two = (Gs * 2)(Gs(A, 1, B, C, 128, 1024, D, 1, 2), Gs(A, 1, B, C, 128, 1024, D + 512, 1, 1))
+    assert L.tb_ternary_gemv_multi(two, 2, s) == 8
+    ok = (Gs * 2)(Gs(A, 1, B, C, 128, 1024, D, 1, 2), Gs(A, 1, B, C, 128, 1024, D + 1024, 1, 1))
+    assert L.tb_ternary_gemv_multi(ok, 0, s) == 0
+    # tb_fwht_segment.x_parts: fp32 partial inputs summed before the transform
+    f32 = lambda x, y, rows, k, parts, res=0: F(x, y, rows, k, tb.TB_F32, tb.TB_F32, parts, res)
+    assert L.tb_fwht128_multi((F * 1)(F(A, B, 1, 128, tb.TB_BF16, tb.TB_F32, 2, 0)), 1, s) == 4  # bf16 parts
+    assert L.tb_fwht128_multi((F * 1)(f32(A, B, 1, 128, 9)), 1, s) == 2              # more than TB_MAX_PARTS
+    assert L.tb_fwht128_multi((F * 1)(f32(A, B, 1, 128, -1)), 1, s) == 2
+    assert L.tb_fwht128_multi((F * 1)(f32(A, B, 1, 128, 2, 1)), 1, s) == 2           # reserved must be 0
+    assert L.tb_fwht128_multi((F * 1)(f32(A, A, 1, 128, 2)), 1, s) == 8              # in place over parts
+    # four parts of one fp32 row (2 KB): an output 1.5 KB on overlaps the last part
+    assert L.tb_fwht128_multi((F * 1)(f32(A, A + 1536, 1, 128, 4)), 1, s) == 8
+    # another segment reading where this one's parts lie
+    clash = (F * 2)(f32(A, B, 1, 128, 4), F(C, A + 1536, 1, 128, tb.TB_F32, tb.TB_F32, 1, 0))
+    assert L.tb_fwht128_multi(clash, 2, s) == 8
+
+
 def test_gemm_validation():
     L = tb.lib()
     s = None

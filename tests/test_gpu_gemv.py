@@ -356,6 +356,105 @@ def test_grouped_output_rotation_f32():
         assert torch.equal(y, tb.tb_fwht128(x))
 
 
+# ---------------------------------------------------------------- K split into parts
+
+def _parts_of(g, parts):
+    # scale groups [floor(G p / parts), floor(G (p + 1) / parts)) of part p
+    return [(g * p // parts, g * (p + 1) // parts) for p in range(parts)]
+
+
+@pytest.mark.parametrize("n,k,parts", [(128, 1024, 2), (256, 17408, 4), (384, 5120, 8), (1024, 2176, 4),
+                                       (128, 512, 4), (512, 20480, 8)])
+def test_gemv_parts_are_the_oracle_over_their_k_ranges(n, k, parts):
+    say(f"gemv parts N={n} K={k} parts={parts}")
+    codes, scales, x = _dense_inputs(n, k, 1, seed=n + k + parts)
+    act = tb.tb_act8_prep(bf16_dev(x))
+    cd, sd = u32_dev(codes), f16_dev(scales)
+    yp = torch.full((parts, 1, n), float("nan"), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv_multi([(act, cd, sd, 1, yp, 1, parts)])
+    torch.cuda.synchronize()
+    got = yp.cpu().numpy().astype(np.float64)
+    for p, (g0, g1) in enumerate(_parts_of(k // 128, parts)):
+        ref = oracle.matvec.gemv(x[:, 128 * g0:128 * g1], codes[:, g0:g1], scales[:, g0:g1], 128 * (g1 - g0))
+        assert_close(got[p], ref, f"part {p} of {parts} (groups {g0}..{g1})")
+        assert np.max(np.abs(got[p] - ref)) <= 1e-5 * np.max(np.abs(ref))
+    full = oracle.matvec.gemv(x, codes, scales, k)
+    assert_close(got.sum(axis=0), full, f"sum of {parts} parts")
+    # grouped with an unsplit product, each is bit for bit what it is alone
+    codes2, scales2, x2 = _dense_inputs(256, 1024, 1, seed=5)
+    act2 = tb.tb_act8_prep(bf16_dev(x2))
+    y2 = torch.empty((1, 256), dtype=torch.float32, device=DEV)
+    yp_g = torch.empty_like(yp)
+    tb.tb_ternary_gemv_multi([(act2, u32_dev(codes2), f16_dev(scales2), 1, y2, 1), (act, cd, sd, 1, yp_g, 1, parts)])
+    y2_alone = tb.tb_ternary_gemv(act2, u32_dev(codes2), f16_dev(scales2), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(yp_g, yp) and torch.equal(y2, y2_alone)
+
+
+def test_gemv_parts_two_planes_and_explicit_one():
+    n, k, parts = 256, 5120, 4
+    codes = synth.random_code_words(n, 2 * k, seed=91)
+    scales = synth.random_scales_f16(n, 2 * k, seed=92)
+    x = synth.gaussian_bf16((1, k), seed=93)
+    act = tb.tb_act8_prep(bf16_dev(x))
+    cd, sd = u32_dev(codes), f16_dev(scales)
+    yp = torch.empty((parts, 1, n), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv_multi([(act, cd, sd, 1, yp, 2, parts)])
+    torch.cuda.synchronize()
+    ref = oracle.matvec.gemv_residual(x, codes, scales, k)
+    assert_close(yp.cpu().numpy().astype(np.float64).sum(axis=0), ref, "two-plane parts summed")
+    # parts = 1 given explicitly is the unsplit product
+    codes1, scales1, x1 = _dense_inputs(256, 17408, 1, seed=94)
+    act1 = tb.tb_act8_prep(bf16_dev(x1))
+    y1 = torch.empty((1, 256), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv_multi([(act1, u32_dev(codes1), f16_dev(scales1), 1, y1, 1, 1)])
+    y0 = tb.tb_ternary_gemv(act1, u32_dev(codes1), f16_dev(scales1), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0)
+
+
+@pytest.mark.parametrize("parts", [2, 4, 8])
+def test_rotation_sums_partial_inputs_in_order(parts):
+    rows, k = 3, 5120
+    xs = torch.randn((parts, rows, k), dtype=torch.float32, device=DEV)
+    y = torch.empty((rows, k), dtype=torch.float32, device=DEV)
+    yb = torch.empty((rows, k), dtype=torch.bfloat16, device=DEV)
+    other = torch.randn((2, 1024), dtype=torch.float32, device=DEV)
+    other_y = torch.empty_like(other)
+    tb.tb_fwht128_multi([(xs, y, parts), (other, other_y), (xs, yb, parts)])
+    # the parts added in part order in fp32, then the plain transform
+    s = xs[0].clone()
+    for p in range(1, parts):
+        s = s + xs[p]
+    torch.cuda.synchronize()
+    assert torch.equal(y, tb.tb_fwht128(s))
+    assert torch.equal(yb, tb.tb_fwht128(s, out_dtype=torch.bfloat16))
+    assert torch.equal(other_y, tb.tb_fwht128(other))
+    ref = oracle.hadamard.fwht_dense(xs.double().sum(dim=0).cpu().numpy())
+    assert_close(y.cpu().numpy().astype(np.float64), ref, f"rotation of {parts} parts")
+
+
+def test_split_down_projection_fused_with_its_rotation():
+    # the decode step's use: the down projection split into 4 parts, its output
+    # rotated back while the parts are added; against the oracle's product
+    # followed by the transform
+    n, k, parts = 5120, 17408, 4
+    codes, scales, x = _dense_inputs(n, k, 1, seed=77)
+    act = tb.tb_act8_prep(bf16_dev(x))
+    yp = torch.empty((parts, 1, n), dtype=torch.float32, device=DEV)
+    y = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv_multi([(act, u32_dev(codes), f16_dev(scales), 1, yp, 1, parts)])
+    tb.tb_fwht128_multi([(yp, y, parts)])
+    torch.cuda.synchronize()
+    tiles = np.sort(np.random.default_rng(78).choice(n // 16, 16, replace=False))
+    blocks = np.unique(tiles // 8)  # the 128-blocks of N these tiles fall in
+    cs = (128 * blocks[:, None] + np.arange(128)[None, :]).ravel()
+    ts = np.unique(cs // 16)
+    yprime = oracle.matvec.gemv(x, codes[ts], scales[ts], k)
+    ref = oracle.hadamard.fwht_dense(yprime)
+    assert_close(y.cpu().numpy().astype(np.float64)[:, cs], ref, "split down projection + rotation (sampled blocks)")
+
+
 # ---------------------------------------------------------------- two-plane weights
 
 def _gemv_resid(x_bits, codes, scales):
