@@ -310,6 +310,7 @@ struct WideSeg {
   float* y;
   int64_t N, K;
   int B, P, ks, wg_begin;
+  int lgp;  // log2 of the segment's K parts (as in the staged kernel)
 };
 
 struct WideSegs {
@@ -333,12 +334,17 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs seg
   const int waves = (int)(blockDim.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // KS and waves are powers of two: shifts and masks, as in the staged kernel
+  // KS, the parts and waves are powers of two: shifts and masks, and a tile
+  // set's parts are consecutive workgroups, as in the staged kernel
   const int lg = __builtin_ctz((unsigned)KS);
-  const int ks = w & (KS - 1);
+  const int lgp = sg.lgp, lgw = lg - lgp;
+  const int64_t wgl = (int64_t)(blockIdx.x - sg.wg_begin);
+  const int part = (int)(wgl & ((1 << lgp) - 1));
+  const int ksw = w & ((1 << lgw) - 1);
+  const int ks = (part << lgw) + ksw;
   const int i = lane & 15, q = lane >> 4;
   const int64_t tiles = (int64_t)((uint64_t)N >> 4);
-  const int64_t t0 = ((int64_t)(blockIdx.x - sg.wg_begin) * (waves >> lg) + (w >> lg)) * T;  // first tile
+  const int64_t t0 = ((wgl >> lgp) * (waves >> lgw) + (w >> lgw)) * T;  // first tile
   const bool live = t0 < tiles;
   const int GA = (int)((uint64_t)K >> 7);  // activation groups per row
   const int G = GA * P;                    // code and scale groups per row
@@ -420,27 +426,28 @@ __global__ void __launch_bounds__(64 * kMaxSlices) gemv_wide_kernel(WideSegs seg
     }
   }
 
-  if (KS > 1) {
+  if (lgw > 0) {
     float* red = reinterpret_cast<float*>(smem);  // [waves][T][NB4][64]
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int m = 0; m < NB4; ++m) red[((w * T + t) * NB4 + m) * 64 + lane] = acc[t][m];
     __syncthreads();
-    if (ks != 0) return;
+    if (ksw != 0) return;
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int m = 0; m < NB4; ++m)
-        for (int u = 1; u < KS; ++u) acc[t][m] += red[(((w + u) * T + t) * NB4 + m) * 64 + lane];
+        for (int u = 1; u < (1 << lgw); ++u) acc[t][m] += red[(((w + u) * T + t) * NB4 + m) * 64 + lane];
   }
   if (live) {
+    float* yp = sg.y + (size_t)part * B * N;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
 #pragma unroll
       for (int m = 0; m < NB4; ++m) {
         const int b = 4 * m + q;
-        if (b < B) sg.y[(size_t)b * N + 16 * (t0 + t) + i] = acc[t][m];
+        if (b < B) yp[(size_t)b * N + 16 * (t0 + t) + i] = acc[t][m];
       }
     }
   }
@@ -498,7 +505,9 @@ void staged_geometry(const GemvSegment& g, int& ks, int& ch) {
 }
 
 bool gemv_parts_supported(const GemvSegment& g) {
-  return g.B == 1 && staged_slices(g.K * g.planes, kStagedCH) != 0 && g.parts <= kMaxSlices;
+  // batch 1 takes the staged path, which needs the short slices; larger
+  // batches take the wide path, which walks slices of any length
+  return g.parts <= kMaxSlices && (g.B > 1 || staged_slices(g.K * g.planes, kStagedCH) != 0);
 }
 
 // The staged path takes a batch-1 segment whose K fits the staged slices;
@@ -511,16 +520,21 @@ bool stageable(const GemvSegment& g) {
 
 // Wide launch geometry for T tiles per wave: workgroups, waves per workgroup
 // and the segment table
+// K slices of a wide segment's tiles over all its parts: at least one per part
+int wide_segment_slices(const GemvSegment& g) {
+  return std::max(wide_slices(g.K / kBlock * g.planes), (int)g.parts);
+}
+
 int wide_plan(const GemvSegment* segs, int count, int T, WideSegs& ws, int& waves) {
   waves = 1;
-  for (int c = 0; c < count; ++c) waves = std::max(waves, wide_slices(segs[c].K / kBlock * segs[c].planes));
+  for (int c = 0; c < count; ++c) waves = std::max(waves, wide_segment_slices(segs[c]) / (int)segs[c].parts);
   int wg = 0;
   for (int c = 0; c < count; ++c) {
-    const int ks = wide_slices(segs[c].K / kBlock * segs[c].planes);
-    const int64_t sets = segs[c].N / 16 / T, per_wg = waves / ks;
+    const int ks = wide_segment_slices(segs[c]), parts = (int)segs[c].parts;
+    const int64_t sets = segs[c].N / 16 / T, per_wg = waves / (ks / parts);
     ws.s[c] = WideSeg{segs[c].act, segs[c].codes, segs[c].scales, segs[c].y, segs[c].N, segs[c].K,
-                      (int)segs[c].B, (int)segs[c].planes, ks, wg};
-    wg += (int)((sets + per_wg - 1) / per_wg);
+                      (int)segs[c].B, (int)segs[c].planes, ks, wg, __builtin_ctz((unsigned)parts)};
+    wg += (int)((sets + per_wg - 1) / per_wg * parts);
   }
   ws.count = count;
   return wg;

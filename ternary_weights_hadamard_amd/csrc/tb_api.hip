@@ -71,7 +71,7 @@ tb_status check_gemv(const tb_gemv_segment& g) {
     tb_gemv_segment n = g;
     n.planes = gemv_planes(g);
     n.parts = gemv_parts(g);
-    if (g.B > 1 || (g.B == 1 && !tb::gemv_parts_supported(n))) return TB_ERR_UNSUPPORTED;
+    if (g.B > 0 && !tb::gemv_parts_supported(n)) return TB_ERR_UNSUPPORTED;
   }
   if (g.B == 0) return TB_OK;
   if (!g.act || !g.codes || !g.scales || !g.y) return TB_ERR_NULL;

@@ -391,6 +391,22 @@ def test_gemv_parts_are_the_oracle_over_their_k_ranges(n, k, parts):
     assert torch.equal(yp_g, yp) and torch.equal(y2, y2_alone)
 
 
+@pytest.mark.parametrize("n,k,b,parts", [(256, 1024, 2, 2), (384, 5120, 8, 4), (128, 17408, 5, 8), (1024, 2176, 16, 4),
+                                         (256, 768, 8, 4), (128, 1024, 3, 8)])
+def test_gemv_parts_batched_are_the_oracle_over_their_k_ranges(n, k, b, parts):
+    say(f"gemv parts N={n} K={k} B={b} parts={parts}")
+    codes, scales, x = _dense_inputs(n, k, b, seed=n + k + b + parts)
+    act = tb.tb_act8_prep(bf16_dev(x))
+    yp = torch.full((parts, b, n), float("nan"), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv_multi([(act, u32_dev(codes), f16_dev(scales), b, yp, 1, parts)])
+    torch.cuda.synchronize()
+    got = yp.cpu().numpy().astype(np.float64)
+    for p, (g0, g1) in enumerate(_parts_of(k // 128, parts)):
+        ref = oracle.matvec.gemv(x[:, 128 * g0:128 * g1], codes[:, g0:g1], scales[:, g0:g1], 128 * (g1 - g0))
+        assert_close(got[p], ref, f"part {p} of {parts} (groups {g0}..{g1}), batch {b}")
+        assert np.max(np.abs(got[p] - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
 def test_gemv_parts_two_planes_and_explicit_one():
     n, k, parts = 256, 5120, 4
     codes = synth.random_code_words(n, 2 * k, seed=91)
