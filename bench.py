@@ -36,7 +36,19 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_MFMA_TFLOPS = 2500.0    # dense fp16 / bf16 matrix cores
 D, F = 5120, 17408
-GEMV_PARTS = 4  # K parts of the batch-1 products (tb_gemv_segment.parts); --gemv-parts
+GEMV_PARTS = None  # K parts per tile of the decode GEMVs (tb_gemv_segment.parts); --gemv-parts
+
+
+def gemv_parts(batch, k_groups):
+    """K parts of one decode product: 4 at batch 1 (where the batch-1 kernel's
+    slices allow it: at most 160 code groups), 8 above, unless --gemv-parts
+    fixes it.  Measured on the 27B-shaped layers (per launch, QKV + O + gate/up
+    and down): batch 1 15.9 / 9.4 us unsplit, 15.0 / 7.8 us with 4 parts;
+    batch 8 33.5 / 22.5 us unsplit, 27.8 / 15.2 us with 8 parts."""
+    p = GEMV_PARTS if GEMV_PARTS is not None else (4 if batch == 1 else 8)
+    if batch == 1 and k_groups > 160:
+        return 1
+    return p
 FUSED = (("qkv", 3 * D, D), ("o", D, D), ("gate_up", 2 * F, D), ("down", D, F))
 
 
@@ -110,10 +122,10 @@ class DecodeStack:
         from ternary_weights_hadamard_amd import tb
 
         self.batch = batch
-        # At batch 1 every product splits its K over GEMV_PARTS workgroups per
-        # tile; the parts are added by the rotation launch that follows
-        # (tb_fwht_segment.x_parts), so the split costs no launch of its own
-        self.parts = [GEMV_PARTS if batch == 1 and self.planes == 1 else 1 for _, n, k in FUSED]
+        # Every product splits its K over several workgroups per tile; the parts
+        # are added by the rotation launch that follows (tb_fwht_segment.x_parts),
+        # so the split costs no launch of its own
+        self.parts = [gemv_parts(batch, self.planes * k // 128) for _, n, k in FUSED]
         self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
         self.act = [torch.empty(tb.tb_act8_bytes(batch, k), dtype=torch.uint8, device=dev) for _, n, k in FUSED]
         self.yr = [torch.empty((p, batch, n) if p > 1 else (batch, n), dtype=torch.float32, device=dev)
@@ -918,8 +930,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=64)
-    ap.add_argument("--gemv-parts", type=int, default=4, choices=(1, 2, 4, 8),
-                    help="K parts per tile of the batch-1 decode GEMVs, added by the output rotation")
+    ap.add_argument("--gemv-parts", type=int, default=None, choices=(1, 2, 4, 8),
+                    help="K parts per tile of the decode GEMVs, added by the output rotation "
+                         "(default: 4 at batch 1, 8 above)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-extra", action="store_true", help="skip the extra phases")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1062,14 +1075,14 @@ def main():
         "config": {"workload": f"decode GEMV, {args.layers}-layer 27B-shaped stack (d_model 5120, d_ff 17408; fused QKV, O, "
                                f"gate/up, down), batch {args.batch}, FWHT128 in and out, HIP graph",
                    "layers": args.layers, "batch": args.batch, "packed_bytes_per_step": step_bytes,
-                   "gemv_k_parts": GEMV_PARTS if args.batch == 1 else 1,
+                   "gemv_k_parts": gemv_parts(args.batch, D // 128),
                    "code_distribution": "P(-1,0,+1) = (0.35, 0.30, 0.35)", "scales": "U(0.005, 0.05) fp16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None or args.batch != 1 else round(traffic),
                      "kernel": "gemv_staged_kernel (two grouped launches per layer: QKV + O + gate/up, then down; "
-                               f"at batch 1 each product's K in {GEMV_PARTS} parts per tile, added by the next rotation "
-                               "launch)",
+                               f"each product's K in {gemv_parts(args.batch, D // 128)} parts per tile, added by the next "
+                               "rotation launch)",
                      "bytes_per_launch": "sum over the 4 matrices of N*K/4 + N*K/64 + 2*B*K + 4*B*N"},
         "extra": extra,
     }
