@@ -40,16 +40,36 @@ GEMV_PARTS = None  # K parts per tile of the decode GEMVs (tb_gemv_segment.parts
 
 
 def gemv_parts(batch, k_groups):
-    """K parts of one decode product: 4 at batch 1 (where the batch-1 kernel's
-    slices allow it: at most 160 code groups), 8 above, unless --gemv-parts
-    fixes it.  Measured on the 27B-shaped layers (per launch, QKV + O + gate/up
-    and down): batch 1 15.9 / 9.4 us unsplit, 15.0 / 7.8 us with 4 parts;
-    batch 8 33.5 / 22.5 us unsplit, 27.8 / 15.2 us with 8 parts."""
-    p = GEMV_PARTS if GEMV_PARTS is not None else (4 if batch == 1 else 8)
+    """K parts of one decode product (k_groups: its code groups per row): 4,
+    or 8 above batch 1 for the long-K down projection, unless --gemv-parts
+    fixes it; at batch 1 only where the batch-1 kernel's slices allow it (at
+    most 160 code groups).  Measured on the 64-layer 27B-shaped step with all
+    four products in one launch per layer: batch 1 1.53 ms with 4 parts
+    everywhere (1.56 ms with 8 for down, whose eight parts the next rotation
+    then reads); batch 8 2.66 ms with 4 / 8 parts, 2.74 ms with 8 / 8."""
+    if GEMV_PARTS is not None:
+        p = GEMV_PARTS
+    else:
+        p = 8 if batch > 1 and k_groups > 80 else 4
     if batch == 1 and k_groups > 160:
         return 1
     return p
 FUSED = (("qkv", 3 * D, D), ("o", D, D), ("gate_up", 2 * F, D), ("down", D, F))
+
+
+def auto_grouping(batch, planes=1):
+    """All four products of a layer in one GEMV launch ("layer") when each is
+    split into K parts (every segment then takes the short K slices), else
+    the long-K down projection in a launch of its own ("split"): a shared
+    launch would give every segment its long slices."""
+    parts = [gemv_parts(batch, planes * k // 128) for _, n, k in FUSED]
+    return "layer" if min(parts) > 1 else "split"
+
+
+GROUP_TEXT = {"layer": "all four products of a layer [QKV 15360x5120, O 5120x5120, gate/up 34816x5120, "
+                       "down 5120x17408] in one launch",
+              "split": "[QKV 15360x5120, O 5120x5120, gate/up 34816x5120] and [down 5120x17408] per layer",
+              "none": "one launch per product"}
 
 
 def log(msg):
@@ -71,9 +91,10 @@ def gemv_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
+def recorded_traffic(grouping):
     """HBM bytes per GEMV launch from the committed counter summary, or None when
-    it is missing or was taken on other GEMV sources than the current ones."""
+    it is missing, was taken on other GEMV sources than the current ones or
+    with launches grouped otherwise."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -81,7 +102,7 @@ def recorded_traffic():
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("gemv_source_hash") != gemv_source_hash():
+    if vals.get("gemv_source_hash") != gemv_source_hash() or vals.get("gemv_grouping") != grouping:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -99,12 +120,13 @@ def packed_bytes(n, k):
 
 
 class DecodeStack:
-    def __init__(self, layers, batch, gen, dev, grouping="split", planes=1):
+    def __init__(self, layers, batch, gen, dev, grouping="auto", planes=1):
         import torch
 
         from ternary_weights_hadamard_amd import synth
 
-        self.layers, self.batch, self.grouping, self.planes = layers, batch, grouping, planes
+        self.layers, self.batch, self.planes = layers, batch, planes
+        self.grouping_arg = grouping
         self.w = []
         # two-plane weights are the dense format of [n, 2k] (the planes' groups interleaved)
         for li in range(layers):
@@ -126,6 +148,9 @@ class DecodeStack:
         # are added by the rotation launch that follows (tb_fwht_segment.x_parts),
         # so the split costs no launch of its own
         self.parts = [gemv_parts(batch, self.planes * k // 128) for _, n, k in FUSED]
+        self.grouping = self.grouping_arg
+        if self.grouping == "auto":
+            self.grouping = auto_grouping(batch, self.planes)
         self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
         self.act = [torch.empty(tb.tb_act8_bytes(batch, k), dtype=torch.uint8, device=dev) for _, n, k in FUSED]
         self.yr = [torch.empty((p, batch, n) if p > 1 else (batch, n), dtype=torch.float32, device=dev)
@@ -571,12 +596,14 @@ def profile_pass(dev, kind):
     gen.manual_seed(31)
     info = {"profile_pass": kind}
     if kind == "gemv":
-        stack = DecodeStack(4, 1, gen, dev, "split")
+        stack = DecodeStack(4, 1, gen, dev)
         stack.step()
         torch.cuda.synchronize()
         for _ in range(3):
             stack.gemv_only()
-        info["algorithmic_bytes_per_launch"] = sum(gemv_bytes(n, k, 1) for _, _, n, k in stack.w[0]) / 2
+        per_layer = {"layer": 1, "split": 2, "none": 4}[stack.grouping]
+        info["grouping"] = stack.grouping
+        info["algorithmic_bytes_per_launch"] = sum(gemv_bytes(n, k, 1) for _, _, n, k in stack.w[0]) / per_layer
     elif kind == "gemm":
         for k, n in ((D, F), (F, D)):
             codes = synth.torch_code_words(n, k, gen, dev)
@@ -710,8 +737,9 @@ def summarize_counters(fetch_dir, write_dir, out_path, commands):
     w_scale = CALIB_BYTES / (sum(wc) / len(wc) * kib)
     fetch = sum(fg) / len(fg) * kib * f_scale
     write = sum(wg) / len(wg) * kib * w_scale
-    lines = ["# HBM traffic of the grouped decode GEMV (batch 1, 27B-shaped layers, split grouping:",
-             "# [QKV 15360x5120, O 5120x5120, gate/up 34816x5120] and [down 5120x17408] per layer)",
+    grouping = auto_grouping(1)  # what the profile pass runs
+    lines = ["# HBM traffic of the grouped decode GEMV (batch 1, 27B-shaped layers,",
+             f"# {GROUP_TEXT[grouping]}, K in {gemv_parts(1, D // 128)} parts per tile)",
              "# from two rocprofv3 counter passes over `python3 bench.py --profile-pass`:"]
     lines += [f"#   {c}" for c in commands]
     lines += ["# Counters are KiB per dispatch; each is scaled by what it reads for a plain",
@@ -720,6 +748,7 @@ def summarize_counters(fetch_dir, write_dir, out_path, commands):
               f"fetch_calibration_factor = {f_scale:.4f}", f"write_calibration_factor = {w_scale:.4f}",
               f"fetch_bytes_per_launch = {fetch:.0f}", f"write_bytes_per_launch = {write:.0f}",
               f"hbm_bytes_per_launch = {fetch + write:.0f}",
+              f"gemv_grouping = {grouping}",
               f"gemv_source_hash = {gemv_source_hash()}"]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -937,8 +966,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the extra phases")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="fewer iterations in the extra phases")
-    ap.add_argument("--grouping", choices=("layer", "split", "none"), default="split",
-                    help="GEMV launches per layer: one over all four matrices, two (d_model-input ones, then down), or one per matrix")
+    ap.add_argument("--grouping", choices=("auto", "layer", "split", "none"), default="auto",
+                    help="GEMV launches per layer: one over all four matrices, two (d_model-input ones, then down), "
+                         "or one per matrix; auto: one when every product is split into K parts, else two")
     ap.add_argument("--profile-pass", nargs="?", const="gemv", choices=PROFILE_KINDS,
                     help="short run of one workload for rocprofv3 counter passes (default: gemv)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar=("OUT", "DIR"),
@@ -1058,7 +1088,7 @@ def main():
         del two
         extra.update(extra_phases(gen, dev, args.quick))
 
-    traffic = recorded_traffic()
+    traffic = recorded_traffic(stack.grouping)
     result = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)",
         "value": round(value, 2),
@@ -1075,15 +1105,16 @@ def main():
         "config": {"workload": f"decode GEMV, {args.layers}-layer 27B-shaped stack (d_model 5120, d_ff 17408; fused QKV, O, "
                                f"gate/up, down), batch {args.batch}, FWHT128 in and out, HIP graph",
                    "layers": args.layers, "batch": args.batch, "packed_bytes_per_step": step_bytes,
-                   "gemv_k_parts": gemv_parts(args.batch, D // 128),
+                   "gemv_k_parts": [gemv_parts(args.batch, k // 128) for _, n, k in FUSED],
+                   "gemv_grouping": GROUP_TEXT[stack.grouping],
                    "code_distribution": "P(-1,0,+1) = (0.35, 0.30, 0.35)", "scales": "U(0.005, 0.05) fp16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None if traffic is None or args.batch != 1 else round(traffic),
-                     "kernel": "gemv_staged_kernel (two grouped launches per layer: QKV + O + gate/up, then down; "
-                               f"each product's K in {gemv_parts(args.batch, D // 128)} parts per tile, added by the next "
-                               "rotation launch)",
-                     "bytes_per_launch": "sum over the 4 matrices of N*K/4 + N*K/64 + 2*B*K + 4*B*N"},
+                     "kernel": f"{'gemv_staged_kernel' if args.batch == 1 else 'gemv_wide_kernel'} "
+                               f"({GROUP_TEXT[stack.grouping]}; each product's K split into parts per tile, "
+                               "added by the next rotation launch)",
+                     "bytes_per_launch": "sum over the launch's matrices of N*K/4 + N*K/64 + 2*B*K + 4*B*N"},
         "extra": extra,
     }
     if not args.no_cpu_baseline:
