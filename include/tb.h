@@ -308,7 +308,9 @@ TB_API tb_status tb_ternary_gemv_noalloc(const uint16_t* x, int64_t B, const uin
  * the GPU idle), each given its TB_ACT8 operand (`act`, as tb_ternary_gemv
  * with x_dtype TB_ACT8); each segment is validated and computed as tb_ternary_gemv,
  * and its result is bit for bit that of the single call (how a segment's sum is
- * split and ordered depends only on its own shape, batch and parts).
+ * split and ordered depends only on its own shape, batch and parts).  The
+ * launch schedules the longest-K segments first; the order of `segs` does not
+ * change any result.
  * A segment with parts > 1 writes its parts instead of the product (see
  * tb_gemv_segment; y then spans parts * B * N floats).
  * `segs` is a host array read during the call; no segment's y may overlap any

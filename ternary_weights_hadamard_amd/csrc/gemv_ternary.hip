@@ -573,10 +573,28 @@ hipError_t launch_wide(const GemvSegment* segs, int count, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream) {
+hipError_t launch_gemv_multi(const GemvSegment* segs_in, int count, hipStream_t stream) {
   // one grouped launch when every segment takes the same path alone and the
   // group fits it, else each segment on its own exactly as a single call
-  // would run it (a segment's result never depends on its companions)
+  // would run it (a segment's result never depends on its companions, nor
+  // on its place in the launch)
+  //
+  // The longest-K segments take the first workgroups: their workgroups carry
+  // the most work (more K slices per tile), and dispatched last they would
+  // set the launch's tail.  A 27B layer's four products in one launch at
+  // batch 1: 20.2 -> 19.7 us, step 1.50 -> 1.48 ms; batch 8 34.7 -> 32.4 us.
+  GemvSegment segs[kMaxSegs];
+  if (count > kMaxSegs) {
+    for (int c = 0; c < count; ++c) {
+      const hipError_t e = launch_gemv_multi(segs_in + c, 1, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  std::copy(segs_in, segs_in + count, segs);
+  std::stable_sort(segs, segs + count, [](const GemvSegment& a, const GemvSegment& b) {
+    return a.K * a.planes > b.K * b.planes;
+  });
   int n_staged = 0;
   for (int c = 0; c < count; ++c) n_staged += stageable(segs[c]) ? 1 : 0;
   if (count >= 1 && count <= kMaxSegs && n_staged == 0) {

@@ -346,6 +346,41 @@ def test_grouped_27b_layer_wide_batch(b):
         assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("b,parts", [(1, (4, 4, 4, 4)), (8, (4, 4, 4, 8)), (3, (2, 1, 8, 4))])
+def test_grouped_layer_with_parts_in_any_order(b, parts):
+    # a layer's four products (K = 5120 three times, then 17408) in one launch,
+    # each split into K parts, the way the decode step groups them: the launch
+    # schedules the long-K product first, so the order of the segments must
+    # change nothing; each segment equals its own single-segment call bit for
+    # bit, and its parts add up to the oracle's product
+    shapes = [(1920, 5120), (640, 5120), (2176, 5120), (640, 17408)]
+    say(f"grouped layer with parts {parts}, B={b}")
+    ins = []
+    for c, (n, k) in enumerate(shapes):
+        codes = synth.random_code_words(n, k, seed=470 + c)
+        scales = synth.random_scales_f16(n, k, seed=480 + c)
+        x = synth.gaussian_bf16((b, k), seed=490 + c)
+        ins.append((tb.tb_act8_prep(bf16_dev(x)), u32_dev(codes), f16_dev(scales), x, codes, scales))
+
+    def run(order):
+        ys = [torch.full((p, b, n), float("nan"), dtype=torch.float32, device=DEV) for p, (n, _) in zip(parts, shapes)]
+        tb.tb_ternary_gemv_multi([(ins[j][0], ins[j][1], ins[j][2], b, ys[j], 1, parts[j]) for j in order])
+        torch.cuda.synchronize()
+        return ys
+
+    base = run([0, 1, 2, 3])
+    for order in ([3, 2, 1, 0], [1, 3, 0, 2]):
+        for c, (y0, y1) in enumerate(zip(base, run(order))):
+            assert torch.equal(y0, y1), f"segment {c}: result depends on the segment order {order}"
+    for c, ((act, cd, sc, x, codes, scales), p, (n, k)) in enumerate(zip(ins, parts, shapes)):
+        y1 = torch.empty((p, b, n), dtype=torch.float32, device=DEV)
+        tb.tb_ternary_gemv_multi([(act, cd, sc, b, y1, 1, p)])
+        torch.cuda.synchronize()
+        assert torch.equal(base[c], y1), f"segment {c}: grouped differs from the single call"
+        got = base[c].cpu().numpy().astype(np.float64).sum(axis=0)
+        assert_close(got, oracle.matvec.gemv(x, codes, scales, k), f"segment {c} parts summed vs oracle")
+
+
 def test_grouped_output_rotation_f32():
     shapes = [(2, 384), (2, 17408), (2, 1024)]
     xs = [torch.randn(s, dtype=torch.float32, device=DEV) for s in shapes]
