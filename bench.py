@@ -40,20 +40,22 @@ GEMV_PARTS = None  # K parts per tile of the decode GEMVs (tb_gemv_segment.parts
 
 
 def gemv_parts(batch, k_groups):
-    """K parts of one decode product (k_groups: its code groups per row): 4,
-    or 8 above batch 1 for the long-K down projection, unless --gemv-parts
+    """K parts of one decode product (k_groups: its code groups per row): 8
+    for the long-K down projection, 4 for the others, unless --gemv-parts
     fixes it; at batch 1 only where the batch-1 kernel's slices allow it (at
     most 160 code groups).  Measured on the 64-layer 27B-shaped step with all
-    four products in one launch per layer: batch 1 1.53 ms with 4 parts
-    everywhere (1.56 ms with 8 for down, whose eight parts the next rotation
-    then reads); batch 8 2.66 ms with 4 / 8 parts, 2.74 ms with 8 / 8."""
+    four products in one launch per layer (K = 5120 / 17408 parts): batch 1
+    1.460 ms with 4 / 8, 1.467 ms with 4 / 4, 1.478 ms with 2 / 8, 1.535 ms
+    with 4 / 2; batch 8 2.495 ms with 4 / 8, 2.506 ms with 4 / 4."""
     if GEMV_PARTS is not None:
         p = GEMV_PARTS
     else:
-        p = 8 if batch > 1 and k_groups > 80 else 4
+        p = 8 if k_groups > 80 else 4
     if batch == 1 and k_groups > 160:
         return 1
     return p
+
+
 FUSED = (("qkv", 3 * D, D), ("o", D, D), ("gate_up", 2 * F, D), ("down", D, F))
 
 
@@ -961,7 +963,7 @@ def main():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--gemv-parts", type=int, default=None, choices=(1, 2, 4, 8),
                     help="K parts per tile of the decode GEMVs, added by the output rotation "
-                         "(default: 4 at batch 1, 8 above)")
+                         "(default: 8 for the down projection, 4 for the others)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-extra", action="store_true", help="skip the extra phases")
     ap.add_argument("--no-cpu-baseline", action="store_true")
