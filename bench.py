@@ -42,18 +42,13 @@ GEMV_PARTS = None  # K parts per tile of the decode GEMVs (tb_gemv_segment.parts
 def gemv_parts(batch, k_groups):
     """K parts of one decode product (k_groups: its code groups per row): 8
     for the long-K down projection, 4 for the others, unless --gemv-parts
-    fixes it; at batch 1 only where the batch-1 kernel's slices allow it (at
-    most 160 code groups).  Measured on the 64-layer 27B-shaped step with all
-    four products in one launch per layer (K = 5120 / 17408 parts): batch 1
-    1.460 ms with 4 / 8, 1.467 ms with 4 / 4, 1.478 ms with 2 / 8, 1.535 ms
-    with 4 / 2; batch 8 2.495 ms with 4 / 8, 2.506 ms with 4 / 4."""
+    fixes it.  Measured on the 64-layer 27B-shaped step with all four
+    products in one launch per layer (K = 5120 / 17408 parts): batch 1 1.460
+    ms with 4 / 8, 1.467 ms with 4 / 4, 1.478 ms with 2 / 8, 1.535 ms with
+    4 / 2; batch 8 2.495 ms with 4 / 8, 2.506 ms with 4 / 4."""
     if GEMV_PARTS is not None:
-        p = GEMV_PARTS
-    else:
-        p = 8 if k_groups > 80 else 4
-    if batch == 1 and k_groups > 160:
-        return 1
-    return p
+        return GEMV_PARTS
+    return 8 if k_groups > 80 else 4
 
 
 FUSED = (("qkv", 3 * D, D), ("o", D, D), ("gate_up", 2 * F, D), ("down", D, F))

@@ -149,8 +149,7 @@ typedef struct {
  * [floor(G p / parts), floor(G (p + 1) / parts)) (G = K/128 per plane times
  * planes), so the product is the sum of the parts in part order.
  * tb_fwht128_multi adds them on the way into the output rotation
- * (tb_fwht_segment.x_parts).  G >= parts (else TB_ERR_SHAPE); at batch 1
- * also G <= 160 (else TB_ERR_UNSUPPORTED). */
+ * (tb_fwht_segment.x_parts).  G >= parts (else TB_ERR_SHAPE). */
 typedef struct {
   const uint8_t* act;
   int64_t B;

@@ -472,10 +472,11 @@ int wide_slices(int64_t G) {
 }
 
 // K slices of a staged segment: the smallest power of two giving at most ch
-// groups per wave, or 0 when even kMaxSlices waves are too few
-int staged_slices(int64_t K, int ch) {
+// groups per wave, or 0 when even max_ks slices are too few (a tile's slices
+// are the waves of one workgroup, or of `parts` workgroups)
+int staged_slices(int64_t K, int ch, int max_ks = kMaxSlices) {
   const int64_t G = K / kBlock;
-  for (int ks = 1; ks <= kMaxSlices; ks *= 2)
+  for (int ks = 1; ks <= max_ks; ks *= 2)
     if (G <= (int64_t)ks * ch) return ks;
   return 0;
 }
@@ -492,22 +493,17 @@ int segment_ch(int64_t K) {
 
 // K slices of a staged segment's tiles (over all its parts) and its groups per
 // wave.  A segment split into parts takes the short slices (at most
-// kStagedCH groups) and at least one slice per part.
+// kStagedCH groups), at least one slice per part and at most kMaxSlices per
+// part (the waves of one workgroup).
 void staged_geometry(const GemvSegment& g, int& ks, int& ch) {
   const int64_t kc = g.K * g.planes;  // code groups x 128
   if (g.parts > 1) {
     ch = kStagedCH;
-    ks = std::max(staged_slices(kc, ch), (int)g.parts);
+    ks = std::max(staged_slices(kc, ch, kMaxSlices * (int)g.parts), (int)g.parts);
   } else {
     ch = segment_ch(kc);
     ks = staged_slices(kc, ch);
   }
-}
-
-bool gemv_parts_supported(const GemvSegment& g) {
-  // batch 1 takes the staged path, which needs the short slices; larger
-  // batches take the wide path, which walks slices of any length
-  return g.parts <= kMaxSlices && (g.B > 1 || staged_slices(g.K * g.planes, kStagedCH) != 0);
 }
 
 // The staged path takes a batch-1 segment whose K fits the staged slices;

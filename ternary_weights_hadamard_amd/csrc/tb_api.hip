@@ -68,10 +68,6 @@ tb_status check_gemv(const tb_gemv_segment& g) {
   if (!dims_ok(g.N, g.K) || g.B < 0 || g.B > TB_GEMV_MAX_BATCH || gemv_parts(g) == 0) return TB_ERR_SHAPE;
   if (gemv_parts(g) > 1) {
     if (g.K / kGroup * gemv_planes(g) < gemv_parts(g)) return TB_ERR_SHAPE;  // every part at least one group
-    tb_gemv_segment n = g;
-    n.planes = gemv_planes(g);
-    n.parts = gemv_parts(g);
-    if (g.B > 0 && !tb::gemv_parts_supported(n)) return TB_ERR_UNSUPPORTED;
   }
   if (g.B == 0) return TB_OK;
   if (!g.act || !g.codes || !g.scales || !g.y) return TB_ERR_NULL;

@@ -17,10 +17,8 @@ hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uin
 hipError_t launch_act8_prep(const uint16_t* x, int64_t rows, int64_t K, uint8_t* act, hipStream_t stream);
 typedef tb_gemv_segment GemvSegment;
 // segments' `planes` must be 1 or 2 and `parts` 1, 2, 4 or 8 (the API layer
-// normalises both; parts > 1 only where gemv_parts_supported)
+// normalises both)
 hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream);
-// whether a batch-1 segment (planes and parts normalised) can be split into its parts
-bool gemv_parts_supported(const GemvSegment& g);
 hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                                  const uint16_t* scales, int64_t N, int64_t K, float* y, hipStream_t stream);
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

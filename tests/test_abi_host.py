@@ -242,7 +242,6 @@ def test_split_gemv_and_summing_rotation_validation():
     assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 1024, D, 1, 16), 1, s) == 2
     assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 384, D, 1, 4), 1, s) == 2        # 3 groups < 4 parts
     assert L.tb_ternary_gemv_multi(one(A, 2, B, C, 128, 384, D, 1, 4), 1, s) == 2        # any batch: G >= parts
-    assert L.tb_ternary_gemv_multi(one(A, 1, B, C, 128, 128 * 161, D, 1, 2), 1, s) == 7  # K past the short slices
     assert L.tb_ternary_gemv_multi(one(A, 0, B, C, 128, 1024, D, 1, 2), 1, s) == 0       # empty batch: no-op
     # two parts of [1][128] fp32 span 1 KB: a second y 512 bytes on overlaps them
     two = (Gs * 2)(Gs(A, 1, B, C, 128, 1024, D, 1, 2), Gs(A, 1, B, C, 128, 1024, D + 512, 1, 1))

@@ -399,7 +399,11 @@ def _parts_of(g, parts):
 
 
 @pytest.mark.parametrize("n,k,parts", [(128, 1024, 2), (256, 17408, 4), (384, 5120, 8), (1024, 2176, 4),
-                                       (128, 512, 4), (512, 20480, 8)])
+                                       (128, 512, 4), (512, 20480, 8),
+                                       # 272 groups: 32 short slices, 16 or 4 waves per part
+                                       (256, 34816, 2), (128, 34816, 8),
+                                       # 320 groups: past the batch-1 kernel's slices (batched kernel)
+                                       (128, 40960, 4)])
 def test_gemv_parts_are_the_oracle_over_their_k_ranges(n, k, parts):
     say(f"gemv parts N={n} K={k} parts={parts}")
     codes, scales, x = _dense_inputs(n, k, 1, seed=n + k + parts)
@@ -440,6 +444,26 @@ def test_gemv_parts_batched_are_the_oracle_over_their_k_ranges(n, k, b, parts):
         ref = oracle.matvec.gemv(x[:, 128 * g0:128 * g1], codes[:, g0:g1], scales[:, g0:g1], 128 * (g1 - g0))
         assert_close(got[p], ref, f"part {p} of {parts} (groups {g0}..{g1}), batch {b}")
         assert np.max(np.abs(got[p] - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("parts", [2, 4, 8])
+def test_gemv_parts_two_plane_down_projection(parts):
+    # a 27B down projection's two planes at batch 1 (K = 17408: 272 code
+    # groups, more than one workgroup's short slices): its parts add up to
+    # the oracle's product
+    n, k = 640, 17408
+    say(f"two-plane gemv parts N={n} K={k} parts={parts}")
+    codes = synth.random_code_words(n, 2 * k, seed=95 + parts)
+    scales = synth.random_scales_f16(n, 2 * k, seed=96 + parts)
+    x = synth.gaussian_bf16((1, k), seed=97 + parts)
+    act = tb.tb_act8_prep(bf16_dev(x))
+    yp = torch.full((parts, 1, n), float("nan"), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemv_multi([(act, u32_dev(codes), f16_dev(scales), 1, yp, 2, parts)])
+    torch.cuda.synchronize()
+    ref = oracle.matvec.gemv_residual(x, codes, scales, k)
+    got = yp.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert_close(got.sum(axis=0), ref, f"two-plane down projection, {parts} parts summed")
 
 
 def test_gemv_parts_two_planes_and_explicit_one():
