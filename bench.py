@@ -507,10 +507,11 @@ def _cur_stream():
 
 def ceilings(dev):
     """What this device achieves with the simplest kernels (tb_probe.h): a
-    streaming read of 1 GiB; reads of the byte counts of the decode step's two
-    grouped GEMV launches, each over its own buffer, rotated over >= 1 GB of
-    buffers and replayed in a HIP graph as the step is; and a register-only
-    loop of bf16 matrix instructions."""
+    streaming read of 1 GiB; reads of the byte counts of a layer's grouped
+    GEMV launch (all four products) and of its two parts when split (QKV + O +
+    gate/up, down), each over its own buffer, rotated over >= 1 GB of buffers
+    and replayed in a HIP graph as the step is; and a register-only loop of
+    bf16 matrix instructions."""
     import torch
 
     lib = probe_lib()
@@ -527,7 +528,8 @@ def ceilings(dev):
     del big
     first = sum(gemv_bytes(n, k, 1) for _, n, k in FUSED[:3])
     down = gemv_bytes(FUSED[3][1], FUSED[3][2], 1)
-    for label, nbytes in (("read_first_launch", first), ("read_down_launch", down)):
+    for label, nbytes in (("read_layer_launch", first + down), ("read_first_launch", first),
+                          ("read_down_launch", down)):
         nbytes = nbytes // 4096 * 4096
         copies = -(-(1 << 30) // nbytes)
         bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7) for _ in range(copies)]
@@ -554,7 +556,8 @@ def ceilings(dev):
     torch.cuda.synchronize()
     flops = grid * 4 * iters * 4 * 2.0 * 16 * 16 * 32
     out["mfma_bf16_tflops"] = round(flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
-    log(f"  ceilings: read 1 GiB {out['read_1gib_gbs']} GB/s; first-launch bytes {out['read_first_launch']['us']} us, "
+    log(f"  ceilings: read 1 GiB {out['read_1gib_gbs']} GB/s; layer-launch bytes {out['read_layer_launch']['us']} us, "
+        f"first-launch bytes {out['read_first_launch']['us']} us, "
         f"down-launch bytes {out['read_down_launch']['us']} us; bf16 MFMA {out['mfma_bf16_tflops']} TFLOP/s")
     return out
 
@@ -736,7 +739,8 @@ def summarize_counters(fetch_dir, write_dir, out_path, commands):
     write = sum(wg) / len(wg) * kib * w_scale
     grouping = auto_grouping(1)  # what the profile pass runs
     lines = ["# HBM traffic of the grouped decode GEMV (batch 1, 27B-shaped layers,",
-             f"# {GROUP_TEXT[grouping]}, K in {gemv_parts(1, D // 128)} parts per tile)",
+             f"# {GROUP_TEXT[grouping]}, K parts per tile "
+             f"{'/'.join(str(gemv_parts(1, k // 128)) for _, n, k in FUSED)})",
              "# from two rocprofv3 counter passes over `python3 bench.py --profile-pass`:"]
     lines += [f"#   {c}" for c in commands]
     lines += ["# Counters are KiB per dispatch; each is scaled by what it reads for a plain",
