@@ -348,7 +348,7 @@ def extra_phases(gen, dev, quick):
             us = time_eager(runm, 2 if quick else 5) * 1e3 / copies
             wbytes = n * k // 4 + n * k // 64
             mid[f"M{m}_{k}x{n}"] = {"us": round(us, 2),
-                                    "kernel": "gemm_skinny_kernel" if m <= 16 else "gemm_ternary_kernel + splitk_reduce_kernel",
+                                    "kernel": "gemm_skinny_kernel" if m <= 16 else "gemm_rw_kernel + splitk_reduce_kernel",
                                     "splits": 1 if m <= 16 else (wsb // (m * n * 4) if wsb else 1),
                                     "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1),
                                     "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),

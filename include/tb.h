@@ -365,9 +365,12 @@ TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t*
  *   y       [M][N] in y_dtype: TB_BF16 (rounded to nearest even) or TB_F32;
  *           must not overlap the inputs.
  * The matrix cores take the activations as the bf16 values they are and each
- * weight as the exact bf16 value 2t; every product is exact.  Each 128-K
- * group's products are summed in fp32 and added to the result times the
- * group's scale; the result is halved on the way out.
+ * weight as the exact bf16 value 2t; every product is exact and sums are
+ * fp32.  Per output column the running sum is kept in units of the last
+ * nonzero group scale: a group with scale s rescales it by (previous unit) /
+ * s, rounded to fp32 (exact when the scales are powers of two), and then
+ * adds its products; a zero-scale group adds nothing.  The result is
+ * multiplied by the last unit and halved on the way out.
  * M <= 16 runs a kernel of its own (one pass over K for at most 16 rows,
  * weights decoded in registers); a row's result depends on its activations,
  * N and K only, not on M.
@@ -378,9 +381,9 @@ TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* c
 /*
  * Bytes of workspace tb_ternary_gemm_splitk and tb_ternary_gemm_rotated use
  * for an [M][N] result with K-long rows: S * M * N * 4 for the S splits of K
- * they choose (about two workgroups per compute unit, at most 16 splits, at
- * least one 128-group each), or 0 when one pass suffices (S = 1) or the
- * sizes are invalid.  For M <= 16 only the rotated GEMM splits K.
+ * they choose (from a time model of the kernel: at most 16 splits, at least
+ * one 128-group each), or 0 when one pass suffices (S = 1) or the sizes are
+ * invalid.  For M <= 16 only the rotated GEMM splits K.
  * Host-only.
  */
 TB_API size_t tb_ternary_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);

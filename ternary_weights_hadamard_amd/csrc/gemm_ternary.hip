@@ -1,37 +1,32 @@
 // Prefill GEMM with dense ternary weights, the decode contraction for M rows:
 //   y[m][n] = sum_g f16(scale[n][g]) * sum_{k in g} t[n][k] * x[m][k]
 //
-// The one dense contraction of the path, so it runs on the matrix cores, with
-// bf16 operands: the activations go to LDS as they are (no conversion) and
-// each weight enters as the bf16 value 2t (exact).  A 128-K group's products
-// accumulate in fp32 registers of their own; at the end of the group they are
-// added to the result accumulators times the group's fp16 scale (one FMA per
-// accumulator, the scale taken straight from fp16).  The result is halved on
-// the way out.
-// Decode: a dense code word holds column c's field in nibble c % 8, bits 2-3
-// for c < 8 and bits 0-1 for c >= 8.  Shifting the word left by 4, 6 and 2
-// puts the fields of columns 2p, 8 + 2p and 9 + 2p at bits 6-7 of byte p (the
-// field of column 2p + 1 is there already); one v_perm_b32 moves two such
-// bytes to bytes 1 and 3 and the mask 0xC000C000 leaves the bf16 pair
-// (2t, 2t') - bit 14 alone is the exponent of 2.0.
-// Tiling: 128 x 128 output tile per workgroup of 4 waves, each wave 64 x 64
-// with v_mfma_f32_16x16x32_bf16; K steps of 64 staged through LDS (double
-// buffered), two steps per scale group.  An LDS row is 128 bytes, eight
-// 16-byte chunks; chunk c of row r is stored at c ^ F(r), F(r) = (r ^ (((r >> 2)
-// ^ (r >> 3)) & 1)) & 7.  With it the matrix-operand reads (16 lanes read one
-// chunk of 16 consecutive rows) and the tile writes (16 lanes write chunks i
-// and 4 + i of 8 consecutive rows) touch distinct banks, whether the LDS
-// serves 8 lanes from 32 banks or 16 lanes from 64 (checked by enumeration);
-// against padded 144-byte rows it is about 2 % faster and 10 KB smaller.
-// Each K
-// step reads the codes of 128 rows once (8 bytes per thread) and decodes them
-// once for all 128 activation rows of the tile.
-// Rotated output (ROT): the output tile is 128 columns wide, one 128-block of
-// N, so the back-rotation y = R_N y' (the second transform of
+// The one dense contraction of the path, so it runs on the matrix cores
+// (v_mfma_f32_16x16x32_bf16) with bf16 operands: the activations as they are,
+// each weight as the bf16 value 2t (exact; the result is halved on the way
+// out).
+// Tiling: 64 x 256 output tile per workgroup of 4 waves; wave w owns columns
+// 64 w .. 64 w + 63 (four 16-column code tiles) for all 64 rows.  Only the
+// activations are staged in LDS (double-buffered K steps of 64); each wave
+// loads its own code words and decodes them straight into matrix operands
+// with v_cvt_scalef32_pk_bf16_fp4 (a code field masked into bits 2-3 of a
+// nibble is the e2m1 value of 2t), so no weight passes through LDS.  An LDS
+// row is 128 bytes, eight 16-byte chunks; chunk c of row r is stored at
+// c ^ F(r), F(r) = (r ^ (((r >> 2) ^ (r >> 3)) & 1)) & 7: the operand reads
+// (16 lanes read one chunk of 16 consecutive rows) touch distinct banks
+// whether the LDS serves 8 lanes from 32 banks or 16 lanes from 64, and the
+// tile writes at most two lanes per bank (checked by enumeration).
+// Scales: the accumulators hold the sum so far in units of the column's last
+// nonzero group scale; a group with scale s first rescales them by
+// unit / s, then adds its products, and a zero-scale group's code fields are
+// masked to zero.  With one set of accumulators a wave needs about 156
+// registers, so three workgroups share a CU.  The rescale factor is rounded
+// (exact for power-of-two scales), about 2^-23 relative per group.
+// Rotated output (ROT): the back-rotation y = R_N y' (the second transform of
 // dpshk.com/news/5289456 §4.2, fused with the product) runs in the epilogue:
-// the tile goes to LDS in fp32, each 16-lane group transforms a row with the
-// in-register butterflies of the activation transform, and the result is
-// rounded once.
+// the tile goes to LDS in fp32, each 16-lane group transforms one 128-column
+// block of a row with the in-register butterflies of the activation
+// transform, and the result is rounded once.
 // At most 16 rows of activations take the kernel of gemm_skinny.hip instead
 // (unrotated output; rotated output keeps the path below).
 // Split K (few rows of activations, so few output tiles): workgroup z of S
@@ -48,13 +43,9 @@ namespace tb {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, KT = 64;
+constexpr int KT = 64;       // K per step
+constexpr int kMaxSplits = 16;  // split-K parts, at most
 constexpr int LDS_ROW = KT;  // bf16 elements per LDS row (128 bytes, chunks swizzled)
-constexpr int kWRing = 2;        // groups of codes and scales in flight ahead
-constexpr int TILE_ELEMS = BM * LDS_ROW;
-constexpr int TROW = BN + 4;  // fp32 elements per row of the rotation epilogue's tile
-// LDS of the main loop ([stage][X | W][row][k], 64 KB) or of the epilogue tile
-constexpr int kLdsElems = 2 * 2 * TILE_ELEMS > BM * TROW * 2 ? 2 * 2 * TILE_ELEMS : BM * TROW * 2;
 
 // element offset of (row r, element k) in a swizzled LDS tile
 __device__ __forceinline__ int lds_off(int r, int k) {
@@ -62,184 +53,206 @@ __device__ __forceinline__ int lds_off(int r, int k) {
   return r * LDS_ROW + ((((k >> 3) ^ f) & 7) << 3) + (k & 7);
 }
 
-// bf16 pairs (2t, 2t') of the 16 columns of a dense code word, in column order.
-__device__ __forceinline__ void decode_word_bf16(uint32_t w, uint32_t (&out)[8]) {
-  const uint32_t t4 = w << 4, t6 = w << 6, t2 = w << 2;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t sel = 0x0Cu | ((uint32_t)p << 8) | (0x0Cu << 16) | ((uint32_t)(4 + p) << 24);
-    out[p] = __builtin_amdgcn_perm(w, t4, sel) & 0xC000C000u;       // columns 2p, 2p + 1
-    out[4 + p] = __builtin_amdgcn_perm(t2, t6, sel) & 0xC000C000u;   // columns 8 + 2p, 9 + 2p
-  }
-}
+// K order: in a 64-K step, lane (i, q) takes one whole code word per tile -
+// K 16 q .. 16 q + 15 of the step, the word of half q / 2 and slot q % 2 - and
+// feeds its first eight K to the step's first instruction and the other eight
+// to the second; the activation operand reads the same K (LDS chunk 2 q + kk
+// of its row).  The two instructions of a step thus split its 64 K
+// differently from a plain order; a group's four cover the same 128 K.
+// Against the previous design (128 x 128 tiles, weights decoded once per
+// workgroup into LDS and read back by every wave, LDS bound), M = 2048 on the
+// 27B FFN shapes: 905 -> 1210 TFLOP/s at K = 5120, 876 -> 1179 at K = 17408.
+constexpr int RBM = 64, RBN = 256;
+constexpr int kRCodeRing = 4;  // steps of code words in flight (two groups)
+constexpr int RTROW = RBN + 4;  // fp32 elements per row of the rotation epilogue's tile
 
 template <bool OUT_BF16, bool ROT>
-__global__ void __launch_bounds__(256, 2) gemm_ternary_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                           const uint32_t* __restrict__ codes,
-                                                           const uint16_t* __restrict__ scales, int64_t N,
-                                                           int64_t K, void* __restrict__ y, int splits) {
+__global__ void __launch_bounds__(256, ROT ? 2 : 3) gemm_rw_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                      const uint32_t* __restrict__ codes,
+                                                      const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                      void* __restrict__ y, int splits) {
+  constexpr int kXStage = RBM * LDS_ROW;  // bf16 elements of one activation stage
+  constexpr int kLdsElems = ROT && RBM * RTROW * 2 > 2 * kXStage ? RBM * RTROW * 2 : 2 * kXStage;
   __shared__ __attribute__((aligned(16))) uint16_t lds_mem[kLdsElems];
-  uint16_t(*lds)[2][TILE_ELEMS] = reinterpret_cast<uint16_t(*)[2][TILE_ELEMS]>(lds_mem);  // [stage][X | W]
-  __shared__ uint16_t lds_s[2][BN];                                         // [stage][weight row] fp16 scale
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;  // wave's sub-tile
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, q = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int64_t m0 = (int64_t)blockIdx.y * RBM;
+  const int64_t n0 = (int64_t)blockIdx.x * RBN;
   const int64_t G = K / kBlock;
-  // this workgroup's scale groups [gb, ge); output: y, or partial z of the workspace
   const int64_t gb = G * blockIdx.z / splits, ge = G * (blockIdx.z + 1) / splits;
+  const int ngroups = (int)(ge - gb), nsteps = 2 * ngroups;
 
-  // global -> register staging assignment
-  // X: 128 rows x 64 k bf16 = 128 B per row; thread -> row tid/2, 32 k (64 B) at (tid&1)*32
-  // rows past M read row M - 1 instead: an activation row reaches only its own
-  // output row, and those are never stored
-  const int xr = tid >> 1, xk = (tid & 1) * 32;
-  const uint16_t* xsrc = x + std::min<int64_t>(m0 + xr, M - 1) * K + gb * kBlock + xk;
-  // W: 128 rows x 64 k; thread -> row tid/2, the 32 columns of lane group
-  // (k0 % 128) / 32 + (tid & 1) of the row's tile: two consecutive words
-  const int wr = tid >> 1, wk = (tid & 1) * 32;
-  const uint32_t* wsrc = codes + ((n0 + wr) >> 4) * G * 128 + gb * 128 + 2 * (16 * (tid & 1) + ((n0 + wr) & 15));
-  // scales [N/16][G][16]: row n's scale of group g at ((n / 16) G + g) 16 + n % 16
-  const uint16_t* ssrc = scales + ((n0 + wr) >> 4) * G * 16 + gb * 16 + ((n0 + wr) & 15);
+  // this wave's four code tiles.  N is a multiple of 128, so in the last
+  // workgroup a wave's tiles are all inside N or all past it; a wave past N
+  // reads the last four tiles instead (its results are never stored).
+  const int64_t ntiles = N >> 4;
+  const int64_t ct0 = std::min<int64_t>((n0 >> 4) + 4 * wv, ntiles - 4);
+  // Addresses are a wave-uniform pointer (scalar registers) plus a 32-bit
+  // lane offset fixed for the whole loop, so a load needs no 64-bit vector
+  // address arithmetic.  Code word of (tile ct0 + j, group gb + g, step h of
+  // the group) for this lane: cbase + j ctile + 128 g + 64 h + coff.
+  const uint32_t* cbase = codes + (ct0 * G + gb) * 128;
+  const int coff = 32 * (q >> 1) + 2 * li + (q & 1);
+  const int64_t ctile = G * 128;  // words between consecutive tiles
+  const _Float16* sbase = reinterpret_cast<const _Float16*>(scales) + (ct0 * G + gb) * 16;
 
-  // Activations come two K steps ahead through two register sets, one per
-  // step parity (from L2: every column tile reads them; one step of products
-  // is shorter than an L2 round trip).  The codes and scales, read once from
-  // HBM, come kWRing groups ahead through a ring of registers, so their
-  // latency is hidden behind several steps of work rather than one.  Every
-  // prefetch is issued, clamped to the last step or group past the range, so
-  // the wait counts are the same on every path.
-  u32x4 xs[2][4];       // [step parity]
-  u32x2 cw[kWRing][2];  // [ring slot][step of the group]
-  uint32_t sw[kWRing];
-  const int nsteps = 2 * (int)(ge - gb);
-  auto gload_x = [&](int step) {
-    const int64_t k0 = (int64_t)std::min(step, nsteps - 1) * KT;
-    const u32x4* s = reinterpret_cast<const u32x4*>(xsrc + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xs[step & 1][i] = s[i];
+  // activation staging: thread -> row tid / 4, 16 consecutive K at 16 (tid % 4);
+  // rows past M read row M - 1 (they reach only output rows never stored)
+  const int xr = tid >> 2, xk = (tid & 3) * 16;
+  const uint16_t* xbase = x + m0 * K + gb * kBlock;  // wave-uniform
+  const int xoff = (int)std::min<int64_t>(xr, M - 1 - m0) * (int)K + xk;  // < 64 K elements
+
+  // Register rings, indexed by compile-time slots (the caller passes the
+  // step's place in a four-step trip): with an index the compiler cannot
+  // resolve, it copies loaded values between registers and waits for loads
+  // just issued.
+  u32x4 xs[2][2];             // [step parity] 16 bf16 of row xr
+  uint32_t cw[kRCodeRing][4];  // [step % kRCodeRing] one code word per tile
+  _Float16 sw[2][4];          // [group parity] scale per tile
+  auto gload_x = [&](int step, int par) {
+    const uint16_t* src = xbase + (int64_t)std::min(step, nsteps - 1) * KT;
+    xs[par][0] = *reinterpret_cast<const u32x4*>(src + xoff);
+    xs[par][1] = *reinterpret_cast<const u32x4*>(src + xoff + 8);
   };
-  // codes and scale of group gi (relative to gb) into ring slot `slot`; groups
-  // past the range reload the last one (never used)
-  auto gload_w = [&](int gi, int slot) {
-    const int64_t g = std::min<int64_t>(gi, ge - gb - 1);
+  auto gload_w = [&](int step, int slot) {  // steps past the range reload the last (never used)
+    const int st = std::min(step, nsteps - 1);
+    const uint32_t* src = cbase + (int64_t)(st >> 1) * 128 + 64 * (st & 1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) cw[slot][h] = *reinterpret_cast<const u32x2*>(wsrc + g * 128 + 64 * h);
-    sw[slot] = ssrc[g * 16];
+    for (int j = 0; j < 4; ++j) cw[slot][j] = (src + j * ctile)[coff];
   };
-  // the step in registers whose parity is `stage` into LDS stage `stage`
-  auto lstore = [&](int stage, int slot, int h) {
-    // X: 32 bf16 of row xr, as they are
-    uint16_t* xd = lds[stage][0];
+  auto gload_s = [&](int g, int par) {
+    const _Float16* src = sbase + (int64_t)std::min(g, ngroups - 1) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xd + lds_off(xr, xk + 8 * i)) = xs[stage][i];
-    // W: decode 32 k of row wr into bf16 2t, pairs (k, k+1)
-    uint16_t* wd = lds[stage][1];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t bits[8];
-      decode_word_bf16(cw[slot][h][j], bits);
-      *reinterpret_cast<u32x4*>(wd + lds_off(wr, wk + 16 * j)) = u32x4{bits[0], bits[1], bits[2], bits[3]};
-      *reinterpret_cast<u32x4*>(wd + lds_off(wr, wk + 16 * j + 8)) = u32x4{bits[4], bits[5], bits[6], bits[7]};
-    }
-    if ((tid & 1) == 0) lds_s[stage][wr] = (uint16_t)sw[slot];
+    for (int j = 0; j < 4; ++j) sw[par][j] = (src + j * G * 16)[li];
+  };
+  auto lstore = [&](int par) {
+    uint16_t* d = lds_mem + par * kXStage;
+    *reinterpret_cast<u32x4*>(d + lds_off(xr, xk)) = xs[par][0];
+    *reinterpret_cast<u32x4*>(d + lds_off(xr, xk + 8)) = xs[par][1];
   };
 
-  // acc: the result; accg: the current scale group's products
-  f32x4 acc[4][4], accg[4][4];
+  // acc holds the sum so far in units of `unit` (per column: the last
+  // nonzero group scale); a group with scale s rescales it by unit / s
+  // before its products are added, and a zero-scale group adds nothing (its
+  // code fields are masked to zero)
+  f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  float unit[4] = {1.f, 1.f, 1.f, 1.f};
+  uint32_t fmask[4];  // 0xCCCCCCCC, or 0 for a zero-scale group
 
-  // the MFMAs of one K step from LDS stage `st`; FIRST starts the group
-  auto mfma_step = [&](int st, bool first) {
+  // the products of one step (c: its place in the trip) from activation stage
+  // c & 1 and the code words of ring slot c
+  auto mfma_step = [&](int c) {
+    const uint16_t* xa = lds_mem + (c & 1) * kXStage;
 #pragma unroll
-    for (int kk = 0; kk < KT; kk += 32) {
+    for (int kk = 0; kk < 2; ++kk) {
       bf16x8 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&lds[st][0][lds_off(wm + 16 * i + li, kk + 8 * q)]);
+        a[i] = *reinterpret_cast<const bf16x8*>(xa + lds_off(16 * i + li, 16 * q + 8 * kk));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&lds[st][1][lds_off(wn + 16 * j + li, kk + 8 * q)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], (first && kk == 0) ? zero : accg[i][j], 0,
-                                                                 0, 0);
-    }
-  };
-
-  // one scale group: its two K steps from LDS stages 0 and 1; the group's
-  // codes are in ring slot `slot`, the next group's in slot `slot` + 1
-  const int ngroups = (int)(ge - gb);
-  auto group = [&](int gi, int slot) {
-    // first step of the group from stage 0; step 2 gi + 1 goes to stage 1
-    // and its registers refill with step 2 gi + 3
-    mfma_step(0, true);
-    lstore(1, slot, 1);
-    gload_x(2 * gi + 3);
-    // the group's codes are all in LDS now: refill its slot kWRing groups ahead
-    gload_w(gi + kWRing, slot);
-    __syncthreads();
-    // second step from stage 1; step 2 gi + 2 goes to stage 0 and its
-    // registers refill with step 2 gi + 4
-    const bool more = gi + 1 < ngroups;
-    mfma_step(1, false);
-    // fold the group: lane's column n = n0 + wn + 16 j + li
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sc = (float)__builtin_bit_cast(_Float16, lds_s[1][wn + 16 * j + li]);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = cw[c][j];
+        const uint32_t f = (kk == 0 ? w : w << 2) & fmask[j];  // e2m1 fields of 2t
+        b[j] = __builtin_bit_cast(
+            bf16x8, u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 1.0f, 0)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 1.0f, 1)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 1.0f, 2)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 1.0f, 3))});
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(accg[i][j][r], sc, acc[i][j][r]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) lstore(0, (slot + 1) % kWRing, 0);
-    gload_x(2 * gi + 4);
+  };
+
+  // one K step (step = 4 trip + c): at the start of a group the rescale; its
+  // products; the code words of step + kRCodeRing into the freed ring slot;
+  // at the end of a group the scales two groups on; the next step's
+  // activations into the other stage and the step after that into the freed
+  // registers; one barrier.  Steps past the range (an odd last trip) load
+  // as the others but add nothing.
+  auto step_body = [&](int step, int c) {
+    const int par = c >> 1;  // group parity
+    if (step < nsteps) {
+      if ((c & 1) == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sg = (float)sw[par][j];
+          const bool nz = sg != 0.f;
+          const float r = nz ? unit[j] * __builtin_amdgcn_rcpf(sg) : 1.f;
+          unit[j] = nz ? sg : unit[j];
+          fmask[j] = nz ? 0xCCCCCCCCu : 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] *= r;
+        }
+      }
+      mfma_step(c);
+    }
+    gload_w(step + kRCodeRing, c);
+    if (c & 1) gload_s((step >> 1) + 2, par);
+    if (step + 1 < nsteps) lstore((c + 1) & 1);
+    gload_x(step + 3, (c + 1) & 1);
     __syncthreads();
   };
 
 #pragma unroll
-  for (int r = 0; r < kWRing; ++r) gload_w(r, r);
-  gload_x(0);
-  lstore(0, 0, 0);
-  gload_x(1);
-  gload_x(2);
+  for (int c = 0; c < kRCodeRing; ++c) gload_w(c, c);
+  gload_s(0, 0);
+  gload_s(1, 1);
+  gload_x(0, 0);
+  lstore(0);
+  gload_x(1, 1);
+  gload_x(2, 0);
   __syncthreads();
-  for (int gi = 0; gi < ngroups; gi += kWRing) {
-#pragma unroll
-    for (int r = 0; r < kWRing; ++r)
-      if (gi + r < ngroups) group(gi + r, r);
+  // two groups (four steps) per trip, every load unconditional: a branch
+  // around the second group made the compiler merge the rings' registers
+  // with copies that waited for loads it had just issued
+  for (int t = 0; 2 * t < ngroups; ++t) {
+    step_body(4 * t, 0);
+    step_body(4 * t + 1, 1);
+    step_body(4 * t + 2, 2);
+    step_body(4 * t + 3, 3);
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] *= unit[j];
 
-  // lane holds acc[i][j][r] = 2 * y[m0 + wm + 16i + 4q + r][n0 + wn + 16j + li]
+  // lane holds acc[i][j][r] = 2 * y[m0 + 16i + 4q + r][n0 + 64 wv + 16j + li]
+  const bool wave_live = (n0 >> 4) + 4 * wv < ntiles;
   if constexpr (ROT) {
     // the tile in fp32, rows padded (the main loop's last barrier has passed)
-    static_assert(BM * TROW * sizeof(float) <= sizeof(lds_mem), "rotation tile exceeds LDS");
     float* t = reinterpret_cast<float*>(lds_mem);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) t[(wm + 16 * i + 4 * q + r) * TROW + wn + 16 * j + li] = acc[i][j][r] * 0.5f;
+        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * q + r) * RTROW + 64 * wv + 16 * j + li] = acc[i][j][r] * 0.5f;
     __syncthreads();
     const int sub = tid & 15;
-    for (int row = tid >> 4; row < BM; row += 16) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(t + row * TROW + 8 * sub);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(t + row * TROW + 8 * sub + 4);
+    // (row, 128-column block) pairs, 16 lanes each; every wave runs 8 rounds
+    for (int p = tid >> 4; p < 2 * RBM; p += 16) {
+      const int row = p >> 1, blk = p & 1;
+      const float* src = t + row * RTROW + 128 * blk + 8 * sub;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
       float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       fwht128_lanes(v, sub);
       const int64_t m = m0 + row;
-      if (m >= M) continue;
-      const int64_t base = m * N + n0 + 8 * sub;
+      if (m >= M || n0 + 128 * blk >= N) continue;
+      const int64_t base = m * N + n0 + 128 * blk + 8 * sub;
       if constexpr (OUT_BF16) {
         u32x4 w;
 #pragma unroll
@@ -259,16 +272,17 @@ __global__ void __launch_bounds__(256, 2) gemm_ternary_kernel(const uint16_t* __
     }
     return;
   }
+  if (!wave_live) return;
   if (splits > 1) y = static_cast<float*>(y) + (size_t)blockIdx.z * M * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t m = m0 + wm + 16 * i + 4 * q + r;
+      const int64_t m = m0 + 16 * i + 4 * q + r;
       if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + wn + 16 * j + li;
+        const int64_t n = n0 + 64 * wv + 16 * j + li;
         const float v = acc[i][j][r] * 0.5f;
         if constexpr (OUT_BF16)
           static_cast<uint16_t*>(y)[m * N + n] = (uint16_t)f32_to_bf16_rne(v);
@@ -285,12 +299,18 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
                                                             void* __restrict__ y) {
   const int64_t stride = (int64_t)gridDim.x * 256 * 4;
   for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < MN; e += stride) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(part + e);
-    for (int s = 1; s < S; ++s) {
-      const f32x4 b = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e);
+    // every partial's load is issued before the first add (S <= kMaxSplits)
+    f32x4 p[kMaxSplits];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] += b[r];
-    }
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < S) p[s] = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e);
+    f32x4 a = p[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplits; ++s)
+      if (s < S) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] += p[s][r];
+      }
     if constexpr (OUT_BF16) {
       const uint32_t lo = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
       const uint32_t hi = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
@@ -314,17 +334,25 @@ __global__ void __launch_bounds__(256) splitk_reduce_rot_kernel(const float* __r
     const int64_t e = (live ? bk : 0) * kBlock + 8 * sub;
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
     if (live) {
-      a = *reinterpret_cast<const f32x4*>(part + e);
-      b = *reinterpret_cast<const f32x4*>(part + e + 4);
-      for (int s = 1; s < S; ++s) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e + 4);
+      // every partial's loads are issued before the first add (S <= kMaxSplits)
+      f32x4 pa[kMaxSplits], pb[kMaxSplits];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          a[r] += c[r];
-          b[r] += d[r];
+      for (int s = 0; s < kMaxSplits; ++s)
+        if (s < S) {
+          pa[s] = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e);
+          pb[s] = *reinterpret_cast<const f32x4*>(part + (size_t)s * MN + e + 4);
         }
-      }
+      a = pa[0];
+      b = pb[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplits; ++s)
+        if (s < S) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            a[r] += pa[s][r];
+            b[r] += pb[s][r];
+          }
+        }
     }
     float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     fwht128_lanes(v, sub);
@@ -350,11 +378,11 @@ __global__ void __launch_bounds__(256) splitk_reduce_rot_kernel(const float* __r
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
                        int64_t K, void* y, bool bf16_out, bool rot, int splits, hipStream_t stream) {
-  const int64_t mt = (M + BM - 1) / BM;
+  const int64_t mt = (M + RBM - 1) / RBM;
   if (mt > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(N / BN), (unsigned)mt, (unsigned)splits), block(256);
+  const dim3 grid((unsigned)((N + RBN - 1) / RBN), (unsigned)mt, (unsigned)splits), block(256);
 #define TB_GEMM(B_, R_) \
-  hipLaunchKernelGGL((gemm_ternary_kernel<B_, R_>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits)
+  hipLaunchKernelGGL((gemm_rw_kernel<B_, R_>), grid, block, 0, stream, x, M, codes, scales, N, K, y, splits)
   if (rot) {
     if (bf16_out)
       TB_GEMM(true, true);
@@ -379,20 +407,21 @@ hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* cod
 }
 
 int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
-  // Each workgroup is latency bound: about one K step (64) per microsecond,
-  // two per scale group.  Two workgroups fit a CU, so 512 run at once and a
-  // launch takes ceil(workgroups / 512) rounds of ceil(G / S) groups each.
-  // Each split beyond one adds M * N fp32 written and read back (about 5 TB/s)
-  // and a second launch.  Take the S in 1 .. min(16, G) with the lowest
-  // estimate (the smaller S on ties).
-  const int64_t tiles = (N / BN) * ((M + BM - 1) / BM), G = K / kBlock;
+  // Time model of S splits (us), fitted to the 64 x 256 kernel on the
+  // 27B-shaped layers (M = 17 .. 2048): a workgroup costs about 8 us of
+  // launch, prologue and epilogue, then its ceil(G / S) scale groups take at
+  // least 1.25 us each (one workgroup alone on a CU), or 0.83 us each per
+  // workgroup sharing a CU; S > 1 adds the reduction launch, which reads the
+  // S fp32 partials (about 6 TB/s) and pays about 0.5 us per partial.  Take
+  // the S in 1 .. min(16, G) with the lowest estimate (the smaller on ties).
+  const int64_t tiles = ((N + RBN - 1) / RBN) * ((M + RBM - 1) / RBM), G = K / kBlock;
   const int64_t smax = std::min<int64_t>(16, G);
   int best = 1;
   double best_us = 0.0;
   for (int64_t s = 1; s <= smax; ++s) {
-    const int64_t rounds = (tiles * s + 511) / 512, groups = (G + s - 1) / s;
-    double us = 2.2 * (double)(rounds * groups);
-    if (s > 1) us += 2.0 + 8.0 * (double)s * (double)M * (double)N / 5.0e6;
+    const double groups = (double)((G + s - 1) / s), per_cu = (double)((tiles * s + 255) / 256);
+    double us = 8.0 + std::max(1.25 * groups, 0.83 * per_cu * groups);
+    if (s > 1) us += 2.0 + 4.0 * (double)s * (double)M * (double)N / 6.0e6 + 0.5 * (double)s;
     if (s == 1 || us < best_us) {
       best = (int)s;
       best_us = us;

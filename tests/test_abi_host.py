@@ -277,13 +277,15 @@ def test_gemm_validation():
 def test_gemm_splitk_validation_and_workspace_size():
     L = tb.lib()
     s = None
-    # 40 tiles of 128 x 128 for M = 64, N = 5120: 10 splits of K = 5120 (4 groups each)
-    # keep 400 workgroups, one round of the 512 that fit at once; 12 splits of
-    # K = 17408 likewise (12 groups each)
-    assert tb.tb_ternary_gemm_splitk_workspace(64, 5120, 5120) == 10 * 64 * 5120 * 4
+    # the split count of the time model: 20 tiles of 64 x 256 for M = 64, N =
+    # 5120 take 8 splits of K = 5120 (5 groups each) and 12 of K = 17408
+    assert tb.tb_ternary_gemm_splitk_workspace(64, 5120, 5120) == 8 * 64 * 5120 * 4
     assert tb.tb_ternary_gemm_splitk_workspace(16, 5120, 17408) == 12 * 16 * 5120 * 4
-    assert tb.tb_ternary_gemm_splitk_workspace(16, 128, 256) == 2 * 16 * 128 * 4      # at most one split per group
     assert tb.tb_ternary_gemm_splitk_workspace(2048, 17408, 5120) == 0                 # enough tiles already
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 128, 256) == 0                      # too little work to split
+    for m, n, k in ((1, 128, 256), (17, 256, 640), (32, 5120, 17408), (256, 17408, 5120), (64, 128, 1024)):
+        ws = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
+        assert ws % (m * n * 4) == 0 and ws // (m * n * 4) <= min(16, k // 128)    # at most one split per group
     assert tb.tb_ternary_gemm_splitk_workspace(0, 128, 128) == 0
     assert tb.tb_ternary_gemm_splitk_workspace(16, 100, 128) == 0
     ws = 0x50000

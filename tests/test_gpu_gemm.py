@@ -75,6 +75,31 @@ def test_gemm_tiny_and_wide_range_activations_exact():
     assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_gemm_zero_scale_groups(split):
+    # scale groups with a zero scale add nothing: about a third of them at
+    # random, every group of some columns, and the first or the last group of
+    # others; N = 384 (half of the last 256-column tile) and 9 groups (an odd
+    # count); the oracle's values, and exact zeros where every scale is zero
+    m, n, k = 70, 384, 1152
+    codes = synth.random_code_words(n, k, seed=90)
+    sc = synth.random_scales_f16(n, k, seed=91).copy()  # [n / 16][groups][16]
+    rng = np.random.default_rng(92)
+    sc[rng.random(sc.shape) < 0.33] = 0
+    sc[3, :, 5] = 0                              # column 53: every group
+    sc[20, 0, :] = 0                             # columns 320..335: the first group
+    sc[21, -1, :] = 0                            # columns 336..351: the last group
+    x = synth.gaussian_bf16((m, k), seed=93)
+    if split:
+        y = tb.tb_ternary_gemm_splitk(bf16_dev(x), u32_dev(codes), f16_dev(sc), out_dtype=torch.float32)
+    else:
+        y = tb.tb_ternary_gemm(bf16_dev(x), u32_dev(codes), f16_dev(sc), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = host_f64(y)
+    assert_close(got, oracle.matvec.gemm(x, codes, sc, k), f"gemm with zero-scale groups (split {split})")
+    assert np.all(got[:, 53] == 0.0)
+
+
 def test_gemm_canaries_and_empty():
     m, n, k = 130, 128, 256
     codes = synth.random_code_words(n, k, seed=60)
