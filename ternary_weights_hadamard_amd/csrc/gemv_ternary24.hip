@@ -301,15 +301,20 @@ hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* m
   const int64_t G = K / kBlock;
   const int64_t wg = N / 16;
   {
-    // staged path: K slices of at most 9 groups, about 4096 waves or more
+    // staged path: the fewest K slices (a power of two, at most 16) that leave
+    // at most 5 groups per slice, or 9 when 16 slices are not enough.  Per
+    // launch, batch 1 (graph-replayed): 17408 x 5120 10.8 us with 8 slices of
+    // 5 groups (11.0 with 4 of 10); 5120 x 5120 6.2 us with 8 (8.4 with 16);
+    // 5120 x 17408 17.7 us with 16 slices of 9 groups, which need 113 KB of
+    // LDS (38.2 us on the unstaged kernel the former 96 KB limit left it to).
     int ks = 1;
     // (every slice keeps at least one group: 2 ks <= G before doubling)
-    while (ks < 16 && 2 * ks <= G && ((G + ks - 1) / ks > 9 || wg * ks < 4096)) ks *= 2;
+    while (ks < 16 && 2 * ks <= G && (G + ks - 1) / ks > 5) ks *= 2;
     const int64_t ch = (G + ks - 1) / ks;
     if (B <= 4 && ch <= 9) {
       const int CH = ch <= 5 ? 5 : 9;
       const size_t lds = (size_t)ks * stage24_bytes(CH, (int)B) + (size_t)ks * 4 * 64 * sizeof(float);
-      if (lds <= 96 * 1024) {
+      if (lds <= 128 * 1024) {
         const dim3 grid((unsigned)wg), block((unsigned)(64 * ks));
         if (CH == 5)
           hipLaunchKernelGGL((gemv24_staged_kernel<5>), grid, block, lds, stream, x, (int)B, meta, signs, scales, N,

@@ -226,16 +226,16 @@ def test_gemv24_small_matches_oracle(n, k, b):
     assert np.max(np.abs(y.cpu().numpy() - ref)) <= 1e-5 * np.max(np.abs(ref))
 
 
-def test_gemv24_full_size_sampled():
-    n, k = 17408, 5120
-    say("gemv24 full 17408x5120 B=1")
+@pytest.mark.parametrize("n,k", [(17408, 5120), (5120, 17408)])
+def test_gemv24_full_size_sampled(n, k):
+    say(f"gemv24 full {n}x{k} B=1")
     meta, signs = synth.random_24(n, k, seed=30)
     scales = synth.random_scales24_f16(n, k, seed=31)
     x = synth.gaussian_bf16((1, k), seed=32)
     y = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(scales)).cpu().numpy()
     rows = np.sort(np.random.default_rng(3).choice(n, 256, replace=False))
     ref = oracle.matvec.gemv24(x, meta[rows], signs[rows], scales[rows], k)
-    assert_close(y[:, rows], ref, "gemv24 17408x5120 (256 sampled rows)")
+    assert_close(y[:, rows], ref, f"gemv24 {n}x{k} (256 sampled rows)")
 
 
 def test_gemv24_exact_and_dense_equivalence():
