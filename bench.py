@@ -902,8 +902,8 @@ def cpu_baseline(stack, dev, max_seconds=20.0):
     x24 = synth.gaussian_bf16((1, k24), seed=32)
     b24 = n24 * k24 // 8 + n24 * k24 // 16 + n24 * k24 // 64
     d1, _ = one_core([("gemv24", (x24, meta, signs, sc24, k24))])[0]
-    da, _ = all_cores([("gemv24", (x24, meta[lo:hi], signs[lo:hi], sc24[lo:hi], k24))
-                       for lo, hi in _chunks(n24, workers)])
+    da, _ = all_cores([("gemv24", (x24, meta[lo // 16:hi // 16], signs[lo // 16:hi // 16], sc24[lo // 16:hi // 16],
+                                   k24)) for lo, hi in _chunks(n24, workers)])
     out["gemv24"] = {"sample": "2:4 GEMV 2048 x 5120 rows of the 17408 x 5120 shape, batch 1", "unit": "GB/s",
                      "one_core": round(b24 / d1 / 1e9, 4), "all_cores": round(b24 / da / 1e9, 4)}
 

@@ -45,12 +45,21 @@
  *                tile-major like the codes, scales[N/16][K/128][16]: the scale
  *                of row n, group g at ((n/16)*(K/128) + g)*16 + n%16 (a 16-row
  *                tile's scales for one group are 32 contiguous bytes).  The 2:4
- *                format stores them by row, scales[N][K/128].
- *   2:4 meta     uint32 meta[N][K/32]: for quad q = k/4 the nibble at bits
- *                4*(q%8) holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1,
- *                the kept positions inside the quad.
- *   2:4 signs    uint32 signs[N][K/64]: bit q%16 set when the element kept at
- *                idx0 of quad q is negative, bit 16 + q%16 for idx1.
+ *                format stores them the same way.
+ *   2:4 meta     uint32 meta[N/16][K/128][4][16]: [n/16][g][w][n%16] is meta
+ *                word w of row n in group g, covering quads q = 32g + 8w ..
+ *                32g + 8w + 7 (q = k/4): the nibble at bits 4*(q%8) holds idx0
+ *                (bits 0-1) and idx1 (bits 2-3), idx0 < idx1, the kept
+ *                positions inside the quad.
+ *   2:4 signs    uint32 signs[N/16][K/128][2][16]: [n/16][g][w][n%16] is sign
+ *                word w of row n in group g, covering quads 32g + 16w .. +15:
+ *                bit q%16 set when the element kept at idx0 of quad q is
+ *                negative, bit 16 + q%16 for idx1.
+ *                Tile-major like the dense format, with row i's word w of a
+ *                tile-group at position 16w + i: a tile-group's meta (256
+ *                bytes), signs (128) and scales (32) are each contiguous, and
+ *                lane 16w + i of a wave reads word w of row i with one
+ *                dword load.
  */
 #ifndef TB_H
 #define TB_H
@@ -237,10 +246,10 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, void* 
  * [N/16][2K/128][16], where group 2g + p is plane p's group g.
  *   W       fp32 [N][K]
  *   codes   dense: [N/16][K/128][128] code words (the tile layout above);
- *           two-plane: [N/16][2K/128][128]; 2:4: the sign plane [N][K/64]
- *   meta    2:4: [N][K/32]; must be NULL for the dense formats (else TB_ERR_FORMAT)
+ *           two-plane: [N/16][2K/128][128]; 2:4: the sign plane [N/16][K/128][2][16]
+ *   meta    2:4: [N/16][K/128][4][16]; must be NULL for the dense formats (else TB_ERR_FORMAT)
  *   scales  fp16 bits; dense: [N/16][K/128][16] (tile-major, above);
- *           two-plane: [N/16][2K/128][16]; 2:4: [N][K/128]
+ *           two-plane: [N/16][2K/128][16]; 2:4: [N/16][K/128][16]
  *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
  *             (the caller zeroes it first).
  * Arithmetic is fp32; the absmean threshold uses the unrounded scale.
@@ -350,7 +359,8 @@ TB_API tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* 
  * Decode GEMV with 2:4 ternary weights (mhpq.cn/news/1159370 §1.2):
  *   y[b][n] = sum_g fp16(scales[n][g]) * sum_q (+-x[b][4q + idx0] +- x[b][4q + idx1])
  *   x       bf16 bits [B][K], the already rotated activations
- *   meta [N][K/32], signs [N][K/64], scales [N][K/128] in the 2:4 format;
+ *   meta [N/16][K/128][4][16], signs [N/16][K/128][2][16], scales
+ *   [N/16][K/128][16] in the (tile-major) 2:4 format;
  *   B and y as tb_ternary_gemv.  Products are exact, accumulation is fp32.
  */
 TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,

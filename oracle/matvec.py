@@ -14,7 +14,7 @@ brute-force forms are explicit Python loops for tiny shapes.
 import numpy as np
 
 from .numerics import bf16_bits_to_f64, f16_bits_to_f64
-from .quant import GROUP, dense_from_24, split_planes, unpack_24, unpack_dense, untile_scales
+from .quant import GROUP, dense_from_24, load_24, split_planes, unpack_24, unpack_dense, untile_scales
 
 
 def _x(x_bf16_bits):
@@ -54,9 +54,11 @@ def gemv_residual(x_bf16_bits, codes, scales, k):
 
 
 def dequant_24(meta, signs, scales, k):
-    idx0, idx1, neg0, neg1 = unpack_24(meta, signs, k)
+    """The stored 2:4 planes (tile-major) as a dense float64 matrix [N, K]."""
+    meta_r, signs_r, scales_r = load_24(meta, signs, scales)
+    idx0, idx1, neg0, neg1 = unpack_24(meta_r, signs_r, k)
     t = dense_from_24(idx0, idx1, neg0, neg1).astype(np.float64)
-    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
+    s = f16_bits_to_f64(np.asarray(scales_r, dtype=np.uint16))
     return t * np.repeat(s, GROUP, axis=1)
 
 
@@ -95,25 +97,27 @@ def gemv_bruteforce(x_bf16_bits, codes, scales, k):
 
 
 def gemv24_bruteforce(x_bf16_bits, meta, signs, scales, k):
-    """Loop form of gemv24: gather the two kept activations of every quad."""
+    """Loop form of gemv24 on the stored tile-major planes: find each quad's
+    words by hand and gather the two kept activations."""
     x = _x(x_bf16_bits)
-    meta = np.asarray(meta, dtype=np.uint32)
-    signs = np.asarray(signs, dtype=np.uint32)
-    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))
-    y = np.zeros((x.shape[0], meta.shape[0]))
+    meta = np.asarray(meta, dtype=np.uint32)  # [N/16, G, 4, 16]
+    signs = np.asarray(signs, dtype=np.uint32)  # [N/16, G, 2, 16]
+    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))  # [N/16, G, 16]
+    y = np.zeros((x.shape[0], meta.shape[0] * 16))
     for m in range(x.shape[0]):
-        for n in range(meta.shape[0]):
+        for n in range(meta.shape[0] * 16):
             total = 0.0
             for g in range(k // GROUP):
                 part = 0.0
                 for q in range(g * GROUP // 4, (g + 1) * GROUP // 4):
-                    nib = (int(meta[n, q // 8]) >> (4 * (q % 8))) & 0xF
+                    qg = q - g * GROUP // 4  # quad within the group, 0..31
+                    nib = (int(meta[n // 16, g, qg // 8, n % 16]) >> (4 * (q % 8))) & 0xF
                     i0, i1 = nib & 3, nib >> 2
-                    sw = int(signs[n, q // 16])
+                    sw = int(signs[n // 16, g, qg // 16, n % 16])
                     n0 = (sw >> (q % 16)) & 1
                     n1 = (sw >> (16 + q % 16)) & 1
                     part += (-1.0 if n0 else 1.0) * x[m, 4 * q + i0]
                     part += (-1.0 if n1 else 1.0) * x[m, 4 * q + i1]
-                total += float(s[n, g]) * part
+                total += float(s[n // 16, g, n % 16]) * part
             y[m, n] = total
     return y

@@ -48,12 +48,20 @@ Dense format (N a multiple of 16, K a multiple of 128):
 Residual (two-plane) format: the dense format of both planes with their
   groups interleaved along K (interleave_planes), codes [N/16][2 K/128][128] and
   scales [N/16][2 K/128][16].
-2:4 format:
-  meta[n][q // 8] uint32 for quad q = k // 4: the nibble at bits 4 * (q % 8)
-  holds idx0 (bits 0-1) and idx1 (bits 2-3), idx0 < idx1 the kept positions.
-  signs[n][q // 16] uint32: bit q % 16 is set when the element at idx0 is
-  negative, bit 16 + q % 16 when the element at idx1 is.
-  scales[n][k // 128] fp16 bits, by row.
+2:4 format.  The words of a row (pack_24, unpack_24):
+  meta word j of row n covers quads q = 8 j .. 8 j + 7 (q = k // 4): the
+  nibble at bits 4 * (q % 8) holds idx0 (bits 0-1) and idx1 (bits 2-3),
+  idx0 < idx1 the kept positions.  Sign word j covers quads 16 j .. 16 j + 15:
+  bit q % 16 is set when the element at idx0 is negative, bit 16 + q % 16
+  when the element at idx1 is.
+  Stored tile-major, like the dense format (store_24, load_24): a 16-row tile
+  and a 128-column group together, word-index-major within the tile-group,
+  so that row i's word w sits at position 16 w + i:
+    meta[N / 16][K / 128][4][16] uint32: [nb, g, w, i] = meta word 4 g + w of
+      row 16 nb + i;
+    signs[N / 16][K / 128][2][16] uint32: [nb, g, w, i] = sign word 2 g + w of
+      row 16 nb + i;
+    scales[N / 16][K / 128][16] fp16 bits (tile_scales).
 """
 
 import numpy as np
@@ -319,8 +327,8 @@ def near_tie_24(wr, s, rel=NEAR_REL):
 def quantize_24(w):
     """Rotate, keep 2 of every 4 along K, absmean over the kept elements, pack.
 
-    Returns meta, signs, scales plus wr, s, idx0, idx1, neg0, neg1 and the
-    dense ternary equivalent t."""
+    Returns meta, signs, scales (stored, tile-major) plus wr, s, idx0, idx1,
+    neg0, neg1 and the dense ternary equivalent t."""
     w = _check_w(w)
     wr = rotate_blocks(w)
     n, k = wr.shape
@@ -332,9 +340,9 @@ def quantize_24(w):
     s = kept_abs.sum(axis=2) / (GROUP // 2)
     neg0 = v0 < 0
     neg1 = v1 < 0
-    meta, signs = pack_24(idx0, idx1, neg0, neg1)
+    meta, signs, scales = store_24(*pack_24(idx0, idx1, neg0, neg1), f64_to_f16_bits(s))
     t = dense_from_24(idx0, idx1, neg0, neg1)
-    return {"meta": meta, "signs": signs, "scales": f64_to_f16_bits(s), "wr": wr, "s": s,
+    return {"meta": meta, "signs": signs, "scales": scales, "wr": wr, "s": s,
             "idx0": idx0, "idx1": idx1, "neg0": neg0, "neg1": neg1, "t": t}
 
 
@@ -357,6 +365,34 @@ def pack_24(idx0, idx1, neg0, neg1):
         signs |= n0[:, j::16] << np.uint64(j)
         signs |= n1[:, j::16] << np.uint64(16 + j)
     return meta.astype(np.uint32), signs.astype(np.uint32)
+
+
+def store_24(meta, signs, scales):
+    """Row words and scales ([N, K/32], [N, K/64], [N, K/128]) into the stored
+    tile-major arrays: row i of tile nb, word 4 g + w (meta) or 2 g + w (signs)
+    of its row, to [nb, g, w, i]; scales as tile_scales."""
+    meta = np.asarray(meta, dtype=np.uint32)
+    signs = np.asarray(signs, dtype=np.uint32)
+    n, nw = meta.shape
+    if n % 16 or nw % 4 or signs.shape != (n, nw // 2):
+        raise ValueError("2:4 rows must be [N, K/32] and [N, K/64] with N a multiple of 16")
+    g = nw // 4
+    m = meta.reshape(n // 16, 16, g, 4).transpose(0, 2, 3, 1)
+    sg = signs.reshape(n // 16, 16, g, 2).transpose(0, 2, 3, 1)
+    return np.ascontiguousarray(m), np.ascontiguousarray(sg), tile_scales(scales)
+
+
+def load_24(meta, signs, scales):
+    """Inverse of store_24: the row words [N, K/32], [N, K/64] and the
+    scales [N, K/128]."""
+    meta = np.asarray(meta, dtype=np.uint32)
+    signs = np.asarray(signs, dtype=np.uint32)
+    if meta.ndim != 4 or meta.shape[2:] != (4, 16) or signs.shape != meta.shape[:2] + (2, 16):
+        raise ValueError("stored 2:4 planes must be [N/16, G, 4, 16] and [N/16, G, 2, 16]")
+    nb, g = meta.shape[:2]
+    m = meta.transpose(0, 3, 1, 2).reshape(nb * 16, g * 4)
+    sg = signs.transpose(0, 3, 1, 2).reshape(nb * 16, g * 2)
+    return np.ascontiguousarray(m), np.ascontiguousarray(sg), untile_scales(scales)
 
 
 def unpack_24(meta, signs, k):

@@ -16,14 +16,18 @@
 // The 64-wide windows are mapped to actual K so that lane q of SMFMAC h covers
 // K 128g + 32q + 16h .. +15: one meta word and one sign word per lane and group.
 //
+// The planes are tile-major (a 16-row tile and a 128-group together, row i's
+// word w at position 16 w + i), so the operand words of a lane are where a
+// whole-wave load puts them: meta word q of row i is lane (i, q)'s dword of
+// the tile-group's 256 bytes.
 // Staged path (batch <= 4): a wave owns one 16-row tile and a slice of at most
-// CH groups of K.  The format is row-major, so a row's meta, signs and scales
-// for the slice are contiguous: the wave fetches them, and its slice of x, with
-// a few whole-wave 16-, 8- and 2-byte loads issued before any use, copies them
-// into a private LDS area and reads each group's words back in the operand
-// layout.  That is about 8 loads per slice instead of 6 per group.  The K
-// slices of a tile are the waves of one workgroup, added through LDS in a
-// fixed order.
+// CH groups of K.  It loads its slice of x first (staged through a private LDS
+// area, then read in the operand layout), then per group one meta dword, one
+// sign dword and one pair of scales straight into registers, all before the
+// first product.  With the row-major planes this kernel started from, a
+// slice was 16 short pieces per plane, staged through LDS (17408 x 5120:
+// 10.8 us).  The K slices of a tile are the waves of one workgroup, added
+// through LDS in a fixed order.
 #include <algorithm>
 
 #include "tb_common.h"
@@ -51,17 +55,21 @@ __global__ void __launch_bounds__(512) gemv_ternary24_kernel(const uint16_t* __r
   const int64_t nbase = (int64_t)blockIdx.x * 16;
   const int64_t gb = G * wv / KS, ge = G * (wv + 1) / KS;
   const int sbit = 8 * (q & 1);  // first sign bit of this lane's quads in its sign word
-  const uint32_t* mp = meta + (nbase + li) * (K / 32) + q;
-  const uint32_t* gp = signs + (nbase + li) * (K / 64) + (q >> 1);
-  const uint16_t* sp = scales + (nbase + 4 * q) * G;  // rows 4q .. 4q+3 of the tile
+  // tile-major planes: group g of this tile at tile-group nb G + g; meta word q
+  // of row li at 16 q + li (the lane), sign word q / 2 at 16 (q / 2) + li,
+  // the scales of rows 4q .. 4q+3 at 4q
+  const int64_t nb = (int64_t)blockIdx.x;
+  const uint32_t* mp = meta + nb * G * 64 + lane;
+  const uint32_t* gp = signs + nb * G * 32 + (q >> 1) * 16 + li;
+  const uint16_t* sp = scales + nb * G * 16 + 4 * q;
 
   u32x2 mbuf[kPrefetch];  // (meta word, sign word) of row li
   uint32_t sbuf[kPrefetch][4];
   auto load_w = [&](int64_t g, int p) {
-    mbuf[p][0] = __builtin_nontemporal_load(mp + 4 * g);
-    mbuf[p][1] = __builtin_nontemporal_load(gp + 2 * g);
+    mbuf[p][0] = __builtin_nontemporal_load(mp + 64 * g);
+    mbuf[p][1] = __builtin_nontemporal_load(gp + 32 * g);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sbuf[p][r] = sp[r * G + g];
+    for (int r = 0; r < 4; ++r) sbuf[p][r] = sp[16 * g + r];
   };
 #pragma unroll
   for (int p = 0; p < kPrefetch; ++p) {
@@ -165,11 +173,8 @@ __global__ void __launch_bounds__(512) gemv_ternary24_kernel(const uint16_t* __r
   if (li < B) *reinterpret_cast<f32x4*>(y + (int64_t)li * N + nbase + 4 * q) = acc_y;
 }
 
-// bytes of one wave's staging area: meta [CH][16][16 B], signs [CH][16][8 B],
-// scales [CH][16] fp16 (padded to 16 B), x [B][CH][256 B]
-__host__ __device__ constexpr int stage24_bytes(int ch, int b) {
-  return ch * 256 + ch * 128 + (ch * 32 + 15) / 16 * 16 + b * ch * 256;
-}
+// bytes of one wave's activation staging area: x [B][CH][256 B]
+__host__ __device__ constexpr int stage24_bytes(int ch, int b) { return b * ch * 256; }
 
 template <int CH>
 __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __restrict__ x, int B,
@@ -189,29 +194,11 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
   const int lg = __builtin_ctz((unsigned)KS);
   const int gb = (G * w) >> lg, ge = (G * (w + 1)) >> lg;
   const int n = ge - gb;  // 1 .. CH groups
-  unsigned char* st = smem + (size_t)w * stage24_bytes(CH, B);
-  unsigned char* st_meta = st;                         // [CH][16 rows][4 words]
-  unsigned char* st_sign = st + CH * 256;              // [CH][16 rows][2 words]
-  unsigned char* st_sc = st_sign + CH * 128;           // [CH][16 rows] fp16
-  unsigned char* st_x = st_sc + (CH * 32 + 15) / 16 * 16;  // [B][CH * 128] bf16
+  unsigned char* st_x = smem + (size_t)w * stage24_bytes(CH, B);  // [B][CH * 128] bf16
   float* red = reinterpret_cast<float*>(smem + (size_t)KS * stage24_bytes(CH, B));
 
-  // 1. every load of the slice.  Item p = lane + 64 t is (row p / CH, group p % CH).
-  constexpr int kItems = (16 * CH + 63) / 64;
-  const int64_t row0 = 16 * nb;
-  u32x4 m_st[kItems];
-  u32x2 s_st[kItems];
-  uint32_t c_st[kItems];
-#pragma unroll
-  for (int t = 0; t < kItems; ++t) {
-    const int p = lane + 64 * t, r = p / CH, gi = p % CH;
-    if (r < 16 && gi < n) {
-      m_st[t] = *reinterpret_cast<const u32x4*>(meta + (row0 + r) * (K / 32) + 4 * (gb + gi));
-      s_st[t] = *reinterpret_cast<const u32x2*>(signs + (row0 + r) * (K / 64) + 2 * (gb + gi));
-      c_st[t] = scales[(row0 + r) * G + gb + gi];
-    }
-  }
-  // x slice of each batch row: 16 chunks of 16 bytes per group
+  // 1. the x slice of each batch row first (every product needs it): 16
+  //    chunks of 16 bytes per group
   constexpr int kXChunks = (16 * CH + 63) / 64;
   u32x4 x_st[4][kXChunks];
 #pragma unroll
@@ -221,16 +208,22 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
       const int c = lane + 64 * t;
       if (b < B && c < 16 * n) x_st[b][t] = *reinterpret_cast<const u32x4*>(x + (int64_t)b * K + 128 * gb + 8 * c);
     }
-  // 2. into this wave's LDS area (read back by the same wave only)
+  // 2. each group's operand words straight from the tile-major planes, in
+  //    group order (a product then waits only for its own group): meta word q
+  //    of row li is the lane's dword of the tile-group's 256 bytes, sign word
+  //    q / 2 of row li, and the scales of rows 4q .. 4q+3.  Slots past the
+  //    slice repeat its last group.
+  const int64_t tg0 = nb * G + gb;  // first tile-group of the slice
+  uint32_t mw[CH], sw[CH];
+  u32x2 sc[CH];
 #pragma unroll
-  for (int t = 0; t < kItems; ++t) {
-    const int p = lane + 64 * t, r = p / CH, gi = p % CH;
-    if (r < 16 && gi < n) {
-      *reinterpret_cast<u32x4*>(st_meta + (gi * 16 + r) * 16) = m_st[t];
-      *reinterpret_cast<u32x2*>(st_sign + (gi * 16 + r) * 8) = s_st[t];
-      *reinterpret_cast<uint16_t*>(st_sc + (gi * 16 + r) * 2) = (uint16_t)c_st[t];
-    }
+  for (int j = 0; j < CH; ++j) {
+    const int64_t tg = tg0 + min(j, n - 1);
+    mw[j] = __builtin_nontemporal_load(meta + tg * 64 + lane);
+    sw[j] = __builtin_nontemporal_load(signs + tg * 32 + (q >> 1) * 16 + li);
+    sc[j] = *reinterpret_cast<const u32x2*>(scales + tg * 16 + 4 * q);
   }
+  // 3. the x slice into this wave's LDS area (read back by the same wave only)
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -241,7 +234,7 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 3. the products.  Lanes of batch rows >= B read row B - 1 (their results
+  // 4. the products.  Lanes of batch rows >= B read row B - 1 (their results
   // are never stored).
   const int sbit = 8 * (q & 1);
   const int b0 = 4 * (q >> 1) + (q & 1);
@@ -249,10 +242,7 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
   f32x4 acc_y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const int jj = min(j, n - 1);  // slots past the slice repeat its last group
-    const uint32_t mw = *reinterpret_cast<const uint32_t*>(st_meta + (jj * 16 + li) * 16 + 4 * q);
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(st_sign + (jj * 16 + li) * 8 + 4 * (q >> 1));
-    const u32x2 sc2 = *reinterpret_cast<const u32x2*>(st_sc + (jj * 16 + 4 * q) * 2);
+    const int jj = min(j, n - 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -260,7 +250,7 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int p_bit = sbit + 4 * h + d;
-        a[d] = ((sw << (15 - p_bit)) & 0x80008000u) | 0x3F803F80u;
+        a[d] = ((sw[j] << (15 - p_bit)) & 0x80008000u) | 0x3F803F80u;
       }
       const unsigned char* xb = xrow + jj * 256;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(xb + 16 * (b0 + 2 * h));
@@ -268,20 +258,20 @@ __global__ void __launch_bounds__(1024) gemv24_staged_kernel(const uint16_t* __r
       const u32x8 bx = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       if (h == 0)
         acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, bx),
-                                                        acc, (int)mw, 0, 0);
+                                                        acc, (int)mw[j], 0, 0);
       else
         acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, bx),
-                                                        acc, (int)mw, 0, 1);
+                                                        acc, (int)mw[j], 0, 1);
     }
-    const uint32_t sv[4] = {sc2[0] & 0xFFFFu, sc2[0] >> 16, sc2[1] & 0xFFFFu, sc2[1] >> 16};
+    const uint32_t sv[4] = {sc[j][0] & 0xFFFFu, sc[j][0] >> 16, sc[j][1] & 0xFFFFu, sc[j][1] >> 16};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float a = __builtin_fmaf(f16_bits_to_f32(sv[r]), acc[r], acc_y[r]);
-      acc_y[r] = j < n ? a : acc_y[r];
+      const float v = __builtin_fmaf(f16_bits_to_f32(sv[r]), acc[r], acc_y[r]);
+      acc_y[r] = j < n ? v : acc_y[r];
     }
   }
 
-  // 4. lane holds y[b = li][n = 16 nb + 4q + r]; slices added in order
+  // 5. lane holds y[b = li][n = 16 nb + 4q + r]; slices added in order
   if (KS > 1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[(w * 4 + r) * 64 + lane] = acc_y[r];

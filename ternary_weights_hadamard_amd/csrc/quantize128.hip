@@ -259,12 +259,17 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
       u32x2 mw = {0u, 0u};
 #pragma unroll
       for (int qd = 0; qd < 16; ++qd) mw[qd >> 3] |= nib[qd] << (4 * (qd & 7));
-      *reinterpret_cast<u32x2*>(meta + grow * (K / 32) + k0 / 32 + 2 * half) = mw;
-      codes[grow * (K / 64) + k0 / 64 + half] = sbits;
+      // tile-major: a 16-row tile's words of group bk, word w of row i at 16 w + i
+      // (meta words 2 half and 2 half + 1, sign word half)
+      const int64_t tg = (grow >> 4) * kblocks + bk;
+      const int64_t ri = grow & 15;
+      meta[(tg * 4 + 2 * half) * 16 + ri] = mw[0];
+      meta[(tg * 4 + 2 * half + 1) * 16 + ri] = mw[1];
+      codes[(tg * 2 + half) * 16 + ri] = sbits;
       if (half == 0) {
         const uint32_t h16 = f32_to_f16_bits(s);
         if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
-        scales[grow * kblocks + bk] = (uint16_t)h16;
+        scales[tg * 16 + ri] = (uint16_t)h16;
       }
     }
     wave_flag_or(err_flag, flags);

@@ -90,18 +90,21 @@ def random_scales_f16(n, k, seed, lo=0.005, hi=0.05):
 
 
 def random_scales24_f16(n, k, seed, lo=0.005, hi=0.05):
-    """fp16 bit patterns [n, k/128] of U(lo, hi) draws (the 2:4 format's scales, by row)."""
+    """fp16 bit patterns of U(lo, hi) draws in the 2:4 format's stored scale
+    shape [n/16, k/128, 16] (independent draws, so any order is the same
+    distribution)."""
     rng = np.random.default_rng(seed)
-    return rng.uniform(lo, hi, size=(n, k // 128)).astype(np.float16).view(np.uint16)
+    return rng.uniform(lo, hi, size=(n // 16, k // 128, 16)).astype(np.float16).view(np.uint16)
 
 
 def random_24(n, k, seed):
-    """2:4 planes: meta [n, k/32] with a uniform choice of the 6 index pairs per
-    quad, signs [n, k/64] with fair random bits."""
+    """2:4 planes in the stored shapes, meta [n/16, k/128, 4, 16] with a
+    uniform choice of the 6 index pairs per quad and signs [n/16, k/128, 2, 16]
+    with fair random bits (every word an independent draw)."""
     rng = np.random.default_rng(seed)
-    nib = rng.choice(np.array(NIBBLES_24, dtype=np.uint32), size=(n, k // 32, 8))
-    meta = np.bitwise_or.reduce(nib << (4 * np.arange(8, dtype=np.uint32)), axis=2).astype(np.uint32)
-    signs = rng.integers(0, 2 ** 32, size=(n, k // 64), dtype=np.uint64).astype(np.uint32)
+    nib = rng.choice(np.array(NIBBLES_24, dtype=np.uint32), size=(n // 16, k // 128, 4, 16, 8))
+    meta = np.bitwise_or.reduce(nib << (4 * np.arange(8, dtype=np.uint32)), axis=4).astype(np.uint32)
+    signs = rng.integers(0, 2 ** 32, size=(n // 16, k // 128, 2, 16), dtype=np.uint64).astype(np.uint32)
     return meta, signs
 
 
@@ -135,10 +138,10 @@ def torch_scales_f16(n, k, gen, device, lo=0.005, hi=0.05):
 
 
 def torch_scales24_f16(n, k, gen, device, lo=0.005, hi=0.05):
-    """U(lo, hi) fp16 scales [n, k/128] (the 2:4 format, by row)."""
+    """U(lo, hi) fp16 scales in the 2:4 stored shape [n/16, k/128, 16]."""
     import torch
 
-    return (lo + (hi - lo) * torch.rand((n, k // 128), generator=gen, device=device)).to(torch.float16)
+    return (lo + (hi - lo) * torch.rand((n // 16, k // 128, 16), generator=gen, device=device)).to(torch.float16)
 
 
 def torch_gaussian_bf16(shape, gen, device, scale=1.0):
@@ -164,11 +167,13 @@ def torch_stack_weights(n, k, gen, device, sigma=0.02, outlier_col_frac=0.01, nu
 
 
 def torch_24(n, k, gen, device):
-    """2:4 planes (meta [n, k/32], signs [n, k/64]) as int32, uniform index pairs and signs."""
+    """2:4 planes in the stored shapes (meta [n/16, k/128, 4, 16], signs
+    [n/16, k/128, 2, 16]) as int32, uniform index pairs and signs."""
     import torch
 
     nib = torch.tensor(NIBBLES_24, dtype=torch.int64, device=device)
-    sel = torch.randint(0, 6, (n, k // 32, 8), generator=gen, device=device)
+    sel = torch.randint(0, 6, (n // 16, k // 128, 4, 16, 8), generator=gen, device=device)
     meta = (nib[sel] << (4 * torch.arange(8, device=device, dtype=torch.int64))).sum(-1).to(torch.int32)
-    signs = torch.randint(-2 ** 31, 2 ** 31, (n, k // 64), generator=gen, device=device, dtype=torch.int64)
+    signs = torch.randint(-2 ** 31, 2 ** 31, (n // 16, k // 128, 2, 16), generator=gen, device=device,
+                          dtype=torch.int64)
     return meta, signs.to(torch.int32)

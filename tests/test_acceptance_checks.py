@@ -63,8 +63,9 @@ def _24_case():
 
 
 def _planes(ref, idx0, idx1, neg0, neg1):
-    meta, signs = oracle.quant.pack_24(idx0, idx1, neg0, neg1)
-    return _t(meta), _t(signs), _t(ref["scales"])
+    meta, signs, scales = oracle.quant.store_24(*oracle.quant.pack_24(idx0, idx1, neg0, neg1),
+                                                oracle.quant.untile_scales(ref["scales"]))
+    return _t(meta), _t(signs), _t(scales)
 
 
 def test_24_check_accepts_the_oracle_and_the_other_tied_pair():

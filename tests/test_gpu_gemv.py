@@ -233,20 +233,23 @@ def test_gemv24_full_size_sampled(n, k):
     scales = synth.random_scales24_f16(n, k, seed=31)
     x = synth.gaussian_bf16((1, k), seed=32)
     y = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(scales)).cpu().numpy()
-    rows = np.sort(np.random.default_rng(3).choice(n, 256, replace=False))
-    ref = oracle.matvec.gemv24(x, meta[rows], signs[rows], scales[rows], k)
-    assert_close(y[:, rows], ref, f"gemv24 {n}x{k} (256 sampled rows)")
+    tiles = np.sort(np.random.default_rng(3).choice(n // 16, 16, replace=False))
+    rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+    ref = oracle.matvec.gemv24(x, meta[tiles], signs[tiles], scales[tiles], k)
+    assert_close(y[:, rows], ref, f"gemv24 {n}x{k} (16 sampled tiles)")
 
 
 def test_gemv24_exact_and_dense_equivalence():
     n, k = 256, 1024
     meta, signs = synth.random_24(n, k, seed=40)
     x = synth.small_int_bf16((2, k), seed=41)
-    sc = (2.0 ** np.random.default_rng(42).integers(-5, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    sc = (2.0 ** np.random.default_rng(42).integers(-5, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
     y24 = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(sc))
-    i0, i1, n0, n1 = oracle.quant.unpack_24(meta, signs, k)
+    meta_r, signs_r, _ = oracle.quant.load_24(meta, signs, sc)
+    i0, i1, n0, n1 = oracle.quant.unpack_24(meta_r, signs_r, k)
     dense = oracle.quant.pack_dense(oracle.quant.dense_from_24(i0, i1, n0, n1))
-    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(oracle.quant.tile_scales(sc)), x.shape[0])
+    # both formats store the scales tile-major, [N/16, K/128, 16]
+    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(sc), x.shape[0])
     torch.cuda.synchronize()
     ref = oracle.matvec.gemv24(x, meta, signs, sc, k)
     assert np.array_equal(y24.cpu().numpy().astype(np.float64), ref)

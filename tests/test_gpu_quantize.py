@@ -137,9 +137,10 @@ def test_24_full_layer_sampled_blocks():
     for a, b in zip(rng.integers(0, n // 128, 16), rng.integers(0, k // 128, 16)):
         rows = slice(128 * a, 128 * (a + 1))
         ref = oracle.quant.quantize_24(w[rows, 128 * b:128 * (b + 1)].astype(np.float64))
-        mb = meta[rows, 4 * b:4 * (b + 1)].contiguous()
-        gb = signs[rows, 2 * b:2 * (b + 1)].contiguous()
-        check_24_planes(mb, gb, scales[rows, b:b + 1].contiguous(), ref, 128, f"block ({a}, {b})")
+        tiles = slice(8 * a, 8 * (a + 1))  # the block's eight 16-row tiles, group b
+        mb = meta[tiles, b:b + 1].contiguous()
+        gb = signs[tiles, b:b + 1].contiguous()
+        check_24_planes(mb, gb, scales[tiles, b:b + 1].contiguous(), ref, 128, f"block ({a}, {b})")
 
 
 # ---------------------------------------------------------------- error-minimising rule

@@ -230,6 +230,34 @@ def test_24_packing_hand_worked(golden_dir):
     assert all(np.array_equal(a, b) for a, b in zip(back, (idx0, idx1, neg0, neg1)))
 
 
+def test_24_stored_layout_places_every_word():
+    # tile-major storage: row i of tile nb, word 4 g + w (meta) or 2 g + w
+    # (signs) of its row goes to [nb, g, w, i]; scales as tile_scales.  Words
+    # numbered by (row, word) land where the layout says, and load_24 undoes it.
+    n, k = 48, 384
+    g = k // 128
+    rows = np.arange(n, dtype=np.uint32)[:, None]
+    meta = rows * 1000 + np.arange(4 * g, dtype=np.uint32)[None, :]
+    signs = rows * 1000 + 500 + np.arange(2 * g, dtype=np.uint32)[None, :]
+    scales = (rows * 10 + np.arange(g, dtype=np.uint32)[None, :]).astype(np.uint16)
+    m, sg, sc = q.store_24(meta, signs, scales)
+    assert m.shape == (n // 16, g, 4, 16) and sg.shape == (n // 16, g, 2, 16) and sc.shape == (n // 16, g, 16)
+    for nb in range(n // 16):
+        for gg in range(g):
+            for i in range(16):
+                r = 16 * nb + i
+                for w in range(4):
+                    assert m[nb, gg, w, i] == r * 1000 + 4 * gg + w
+                for w in range(2):
+                    assert sg[nb, gg, w, i] == r * 1000 + 500 + 2 * gg + w
+                assert sc[nb, gg, i] == r * 10 + gg
+    # flat order: a tile-group's meta words are 64 consecutive words, word w of row i at 16 w + i
+    flat = m.reshape(-1)
+    assert flat[(1 * g + 2) * 64 + 16 * 3 + 5] == (16 + 5) * 1000 + 4 * 2 + 3
+    back = q.load_24(m, sg, sc)
+    assert all(np.array_equal(a, b) for a, b in zip(back, (meta, signs, scales)))
+
+
 def test_24_all_patterns_and_signs_brute_force():
     # every quad pattern (6 index pairs x 4 sign pairs) with kept magnitudes 3, 2 and
     # pruned 1, 0.5, laid out as a rotated block; quantize_24 must keep exactly them
