@@ -11,7 +11,7 @@
 // weight); dpshk.com/news/5289456 §2.1 and §3.2 (transform per 128x128 block,
 // then sign(w) * (|w| > thr)).
 //
-// One workgroup of 256 threads owns one block at a time:
+// One workgroup of 256 threads owns one block:
 //   phase A  thread (column c, row half h) loads 64 rows of one column with
 //            coalesced 128-byte row segments and runs the column transform:
 //            6 butterfly rounds in registers, the 7th across lane ^ 32 with
@@ -87,25 +87,30 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
   const int64_t kblocks = K / kBlock;
   const int64_t nblk = (N / kBlock) * kblocks;
 
-  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+  // one block per workgroup (a loop over blocks made the compiler keep the
+  // 64 load addresses across it, spilled to scratch)
+  {
+    const int64_t blk = blockIdx.x;
+    if (blk >= nblk) return;
     const int64_t n0 = (blk / kblocks) * kBlock;
     const int64_t bk = blk % kblocks;
     const int64_t k0 = bk * kBlock;
     uint32_t flags = 0;
 
     // ---- phase A: column transform (along N) ----
+    // addresses: the block's row i (wave-uniform) plus a 32-bit lane offset
     float v[64];
     {
-      const float* src = W + (n0 + 64 * half) * K + k0 + col;
+      const float* base = W + n0 * K + k0;
+      const int lane_off = 64 * half * (int)K + col;  // < 64 K + 128 floats
 #pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = __builtin_nontemporal_load(src + (int64_t)i * K);
+      for (int i = 0; i < 64; ++i) v[i] = __builtin_nontemporal_load(base + (int64_t)i * K + lane_off);
     }
 #pragma unroll
     for (int i = 0; i < 64; ++i)
       if (!__builtin_isfinite(v[i])) flags |= TB_EFLAG_NONFINITE;
     fwht64_regs(v);
     fwht_cross_halves(v, sgn);
-    __syncthreads();  // previous block's phase B reads are done
     {
       // row r = 64*half + i; XOR-swizzle the column by row bit 6 to spread banks
       const int pc = col ^ (half << 5);
@@ -281,8 +286,9 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
 hipError_t launch_quantize128(const float* W, int64_t N, int64_t K, int fmt, uint32_t* codes, uint32_t* meta,
                               uint16_t* scales, int32_t* err_flag, hipStream_t stream) {
   const int64_t nblk = (N / kBlock) * (K / kBlock);
-  const int64_t cap = 1 << 20;
-  const unsigned grid = (unsigned)(nblk < cap ? nblk : cap);
+  // one workgroup per 128 x 128 block
+  if (nblk * 256 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)nblk;
   if (fmt == TB_FMT_24)
     hipLaunchKernelGGL((quantize128_kernel<kTwoFour>), dim3(grid), dim3(256), 0, stream, W, N, K, codes, meta,
                        scales, err_flag);
