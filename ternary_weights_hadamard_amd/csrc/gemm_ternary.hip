@@ -64,15 +64,16 @@ __device__ __forceinline__ int lds_off(int r, int k) {
 // 27B FFN shapes: 905 -> 1210 TFLOP/s at K = 5120, 876 -> 1179 at K = 17408.
 constexpr int RBM = 64, RBN = 256;
 constexpr int kRCodeRing = 4;  // steps of code words in flight (two groups)
-constexpr int RTROW = RBN + 4;  // fp32 elements per row of the rotation epilogue's tile
+constexpr int RTROW = 128 + 4;  // fp32 elements per row of the rotation epilogue's tile (one 128-block)
 
 template <bool OUT_BF16, bool ROT>
-__global__ void __launch_bounds__(256, ROT ? 2 : 3) gemm_rw_kernel(const uint16_t* __restrict__ x, int64_t M,
+__global__ void __launch_bounds__(256, 3) gemm_rw_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                       const uint32_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales, int64_t N, int64_t K,
                                                       void* __restrict__ y, int splits) {
   constexpr int kXStage = RBM * LDS_ROW;  // bf16 elements of one activation stage
   constexpr int kLdsElems = ROT && RBM * RTROW * 2 > 2 * kXStage ? RBM * RTROW * 2 : 2 * kXStage;
+  static_assert(RBN == 256, "the rotation epilogue takes the tile's two 128-column blocks in turn");
   __shared__ __attribute__((aligned(16))) uint16_t lds_mem[kLdsElems];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,43 +233,53 @@ __global__ void __launch_bounds__(256, ROT ? 2 : 3) gemm_rw_kernel(const uint16_
   // lane holds acc[i][j][r] = 2 * y[m0 + 16i + 4q + r][n0 + 64 wv + 16j + li]
   const bool wave_live = (n0 >> 4) + 4 * wv < ntiles;
   if constexpr (ROT) {
-    // the tile in fp32, rows padded (the main loop's last barrier has passed)
+    // The tile's two 128-column blocks in turn (waves 2 blk and 2 blk + 1 own
+    // block blk), each through LDS in fp32 with padded rows; each 16-lane
+    // group rotates one row of the block.  One block at a time keeps the
+    // epilogue's LDS at 33.8 KB, so three workgroups share a CU (the whole
+    // tile at once, 66.5 KB, allowed two).  The main loop's last barrier has
+    // passed.
     float* t = reinterpret_cast<float*>(lds_mem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[(16 * i + 4 * q + r) * RTROW + 64 * wv + 16 * j + li] = acc[i][j][r] * 0.5f;
-    __syncthreads();
     const int sub = tid & 15;
-    // (row, 128-column block) pairs, 16 lanes each; every wave runs 8 rounds
-    for (int p = tid >> 4; p < 2 * RBM; p += 16) {
-      const int row = p >> 1, blk = p & 1;
-      const float* src = t + row * RTROW + 128 * blk + 8 * sub;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-      float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      fwht128_lanes(v, sub);
-      const int64_t m = m0 + row;
-      if (m >= M || n0 + 128 * blk >= N) continue;
-      const int64_t base = m * N + n0 + 128 * blk + 8 * sub;
-      if constexpr (OUT_BF16) {
-        u32x4 w;
+    for (int blk = 0; blk < 2; ++blk) {
+      if ((wv >> 1) == blk) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = f32_to_bf16_rne(v[2 * e] * kInvSqrt128) | (f32_to_bf16_rne(v[2 * e + 1] * kInvSqrt128) << 16);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
-      } else {
-        f32x4 lo, hi;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = v[e] * kInvSqrt128;
-          hi[e] = v[4 + e] * kInvSqrt128;
-        }
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base) = lo;
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base + 4) = hi;
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              t[(16 * i + 4 * q + r) * RTROW + 64 * (wv & 1) + 16 * j + li] = acc[i][j][r] * 0.5f;
       }
+      __syncthreads();
+      // 64 rows, 16 per round of the workgroup's 16 groups: every wave runs 4 rounds
+      for (int row = tid >> 4; row < RBM; row += 16) {
+        const float* src = t + row * RTROW + 8 * sub;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+        float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        fwht128_lanes(v, sub);
+        const int64_t m = m0 + row;
+        if (m >= M || n0 + 128 * blk >= N) continue;
+        const int64_t base = m * N + n0 + 128 * blk + 8 * sub;
+        if constexpr (OUT_BF16) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = f32_to_bf16_rne(v[2 * e] * kInvSqrt128) | (f32_to_bf16_rne(v[2 * e + 1] * kInvSqrt128) << 16);
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + base) = w;
+        } else {
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = v[e] * kInvSqrt128;
+            hi[e] = v[4 + e] * kInvSqrt128;
+          }
+          *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base) = lo;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base + 4) = hi;
+        }
+      }
+      __syncthreads();  // the block's reads are done before the next block's writes
     }
     return;
   }
