@@ -44,22 +44,26 @@
  *                absmean, rounded to nearest even.  Dense formats store them
  *                tile-major like the codes, scales[N/16][K/128][16]: the scale
  *                of row n, group g at ((n/16)*(K/128) + g)*16 + n%16 (a 16-row
- *                tile's scales for one group are 32 contiguous bytes).  The 2:4
- *                format stores them the same way.
- *   2:4 meta     uint32 meta[N/16][K/128][4][16]: [n/16][g][w][n%16] is meta
- *                word w of row n in group g, covering quads q = 32g + 8w ..
- *                32g + 8w + 7 (q = k/4): the nibble at bits 4*(q%8) holds idx0
- *                (bits 0-1) and idx1 (bits 2-3), idx0 < idx1, the kept
- *                positions inside the quad.
- *   2:4 signs    uint32 signs[N/16][K/128][2][16]: [n/16][g][w][n%16] is sign
- *                word w of row n in group g, covering quads 32g + 16w .. +15:
- *                bit q%16 set when the element kept at idx0 of quad q is
- *                negative, bit 16 + q%16 for idx1.
- *                Tile-major like the dense format, with row i's word w of a
- *                tile-group at position 16w + i: a tile-group's meta (256
- *                bytes), signs (128) and scales (32) are each contiguous, and
- *                lane 16w + i of a wave reads word w of row i with one
- *                dword load.
+ *                tile's scales for one group are 32 contiguous bytes).
+ *   2:4 format   Lane-major in blocks of four 128-groups: a 16-row tile nb
+ *                and block b (groups 4b .. 4b+3; G4 = ceil(K/512) blocks, the
+ *                groups of the last block past K/128 stored as zeros) hold,
+ *                for lane l = 16w + i (row i of the tile, w = 0..3), what
+ *                lane l of a wave needs for the quads 32g + 8w .. 32g + 8w + 7
+ *                (q = k/4) of each group g of the block:
+ *   2:4 meta     uint32 meta[N/16][G4][64][4]: [nb][b][l][j] is the meta word
+ *                of row 16nb + i for those quads of group g = 4b + j: the
+ *                nibble at bits 4*(q%8) holds idx0 (bits 0-1) and idx1 (bits
+ *                2-3), idx0 < idx1, the kept positions inside the quad.
+ *   2:4 signs    uint32 signs[N/16][G4][64][2]: the 16-bit sign field of lane
+ *                l and group g = 4b + 2p + h in half h (bits 16h .. 16h+15) of
+ *                [nb][b][l][p]: bit q%8 set when the element kept at idx0 of
+ *                quad q is negative, bit 8 + q%8 for idx1.
+ *   2:4 scales   uint16 fp16 bits scales[N/16][G4][4][4][4]: [nb][b][w][j][r]
+ *                is the scale of row 16nb + 4w + r in group 4b + j.
+ *                A lane reads its four meta words with one 16-byte load, its
+ *                eight sign bytes with one 8-byte load, and the scales of its
+ *                output rows from a 128-byte block record.
  */
 #ifndef TB_H
 #define TB_H
@@ -179,10 +183,12 @@ TB_API int tb_version(void);
 
 /*
  * Sizes in bytes of the packed planes of an [N][K] matrix in format `fmt`
- * (tb_format).  Dense (both rules): code_bytes = N*K/4, meta_bytes = 0.  2:4: code_bytes
- * (the sign plane) = N*K/16, meta_bytes = N*K/8.  scale_bytes = N*K/64 for
- * both.  Two-plane (TB_FMT_DENSE_RESID): code_bytes = N*K/2, meta_bytes = 0,
- * scale_bytes = N*K/32.  Any output pointer may be NULL.  Host-only.
+ * (tb_format).  Dense (both rules): code_bytes = N*K/4, meta_bytes = 0,
+ * scale_bytes = N*K/64.  2:4, with K' = K rounded up to a multiple of 512
+ * (whole blocks of four groups): code_bytes (the sign plane) = N*K'/16,
+ * meta_bytes = N*K'/8, scale_bytes = N*K'/64.  Two-plane
+ * (TB_FMT_DENSE_RESID): code_bytes = N*K/2, meta_bytes = 0, scale_bytes =
+ * N*K/32.  Any output pointer may be NULL.  Host-only.
  * Cites the 2-bit storage of mhpq.cn/news/1159370 §3.1 and the bit ledger of §1.3.
  */
 TB_API tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
@@ -246,10 +252,12 @@ TB_API tb_status tb_fwht128_multi(const tb_fwht_segment* segs, int count, void* 
  * [N/16][2K/128][16], where group 2g + p is plane p's group g.
  *   W       fp32 [N][K]
  *   codes   dense: [N/16][K/128][128] code words (the tile layout above);
- *           two-plane: [N/16][2K/128][128]; 2:4: the sign plane [N/16][K/128][2][16]
- *   meta    2:4: [N/16][K/128][4][16]; must be NULL for the dense formats (else TB_ERR_FORMAT)
+ *           two-plane: [N/16][2K/128][128]; 2:4: the sign plane [N/16][G4][64][2]
+ *   meta    2:4: [N/16][G4][64][4] (G4 = ceil(K/512)); must be NULL for the
+ *           dense formats (else TB_ERR_FORMAT)
  *   scales  fp16 bits; dense: [N/16][K/128][16] (tile-major, above);
- *           two-plane: [N/16][2K/128][16]; 2:4: [N/16][K/128][16]
+ *           two-plane: [N/16][2K/128][16]; 2:4: [N/16][G4][4][4][4]
+ *           (2:4 groups past K/128 in the last block are written as zeros)
  *   err_flag  NULL, or a device int32 the kernels OR TB_EFLAG_* bits into
  *             (the caller zeroes it first).
  * Arithmetic is fp32; the absmean threshold uses the unrounded scale.
@@ -359,8 +367,9 @@ TB_API tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* 
  * Decode GEMV with 2:4 ternary weights (mhpq.cn/news/1159370 §1.2):
  *   y[b][n] = sum_g fp16(scales[n][g]) * sum_q (+-x[b][4q + idx0] +- x[b][4q + idx1])
  *   x       bf16 bits [B][K], the already rotated activations
- *   meta [N/16][K/128][4][16], signs [N/16][K/128][2][16], scales
- *   [N/16][K/128][16] in the (tile-major) 2:4 format;
+ *   meta [N/16][G4][64][4], signs [N/16][G4][64][2], scales
+ *   [N/16][G4][4][4][4] in the (lane-major) 2:4 format, G4 = ceil(K/512);
+ *   the padded groups of the last block are never read;
  *   B and y as tb_ternary_gemv.  Products are exact, accumulation is fp32.
  */
 TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,

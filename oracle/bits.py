@@ -28,15 +28,17 @@ def storage24_bits():
 def packed_bytes(fmt, n, k):
     """(code_bytes, meta_bytes, scale_bytes) of the packed planes of an [n, k] matrix.
 
-    dense: codes n*k/4 bytes, no meta; "24": signs n*k/16 bytes, meta n*k/8 bytes.
-    Scales are n*(k/128) fp16 values in both formats."""
+    dense: codes n*k/4 bytes, no meta, n*(k/128) fp16 scales.  "24": signs
+    n*k'/16 bytes, meta n*k'/8 bytes and n*(k'/128) fp16 scales for k' = k
+    rounded up to a multiple of 512 (the stored format keeps four 128-groups
+    per block and pads the last block with zero groups)."""
     if n <= 0 or k <= 0 or n % 128 or k % 128:
         raise ValueError("n and k must be positive multiples of 128")
-    scales = n * (k // 128) * 2
     if fmt == "dense":
-        return n * k // 4, 0, scales
+        return n * k // 4, 0, n * (k // 128) * 2
     if fmt == "24":
-        return n * k // 16, n * k // 8, scales
+        kp = -(-k // 512) * 512
+        return n * kp // 16, n * kp // 8, n * (kp // 128) * 2
     raise ValueError(f"unknown format {fmt!r}")
 
 

@@ -54,8 +54,8 @@ def gemv_residual(x_bf16_bits, codes, scales, k):
 
 
 def dequant_24(meta, signs, scales, k):
-    """The stored 2:4 planes (tile-major) as a dense float64 matrix [N, K]."""
-    meta_r, signs_r, scales_r = load_24(meta, signs, scales)
+    """The stored 2:4 planes (lane-major) as a dense float64 matrix [N, K]."""
+    meta_r, signs_r, scales_r = load_24(meta, signs, scales, k)
     idx0, idx1, neg0, neg1 = unpack_24(meta_r, signs_r, k)
     t = dense_from_24(idx0, idx1, neg0, neg1).astype(np.float64)
     s = f16_bits_to_f64(np.asarray(scales_r, dtype=np.uint16))
@@ -97,27 +97,32 @@ def gemv_bruteforce(x_bf16_bits, codes, scales, k):
 
 
 def gemv24_bruteforce(x_bf16_bits, meta, signs, scales, k):
-    """Loop form of gemv24 on the stored tile-major planes: find each quad's
-    words by hand and gather the two kept activations."""
+    """Loop form of gemv24 on the stored lane-major planes: find each quad's
+    words by hand and gather the two kept activations.  Quad qd of row n lies
+    in group g = qd // 32 and lane column q = (qd % 32) // 8, at position
+    e = qd % 8 of that lane's meta word and sign field."""
     x = _x(x_bf16_bits)
-    meta = np.asarray(meta, dtype=np.uint32)  # [N/16, G, 4, 16]
-    signs = np.asarray(signs, dtype=np.uint32)  # [N/16, G, 2, 16]
-    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))  # [N/16, G, 16]
+    meta = np.asarray(meta, dtype=np.uint32)  # [N/16, G4, 64, 4]
+    signs = np.asarray(signs, dtype=np.uint32)  # [N/16, G4, 64, 2]
+    s = f16_bits_to_f64(np.asarray(scales, dtype=np.uint16))  # [N/16, G4, 4, 4, 4]
     y = np.zeros((x.shape[0], meta.shape[0] * 16))
     for m in range(x.shape[0]):
         for n in range(meta.shape[0] * 16):
+            nb, i = n // 16, n % 16
             total = 0.0
             for g in range(k // GROUP):
+                b, j = g // 4, g % 4
                 part = 0.0
-                for q in range(g * GROUP // 4, (g + 1) * GROUP // 4):
-                    qg = q - g * GROUP // 4  # quad within the group, 0..31
-                    nib = (int(meta[n // 16, g, qg // 8, n % 16]) >> (4 * (q % 8))) & 0xF
+                for qd in range(g * GROUP // 4, (g + 1) * GROUP // 4):
+                    q, e = (qd % 32) // 8, qd % 8
+                    lane = 16 * q + i
+                    nib = (int(meta[nb, b, lane, j]) >> (4 * e)) & 0xF
                     i0, i1 = nib & 3, nib >> 2
-                    sw = int(signs[n // 16, g, qg // 16, n % 16])
-                    n0 = (sw >> (q % 16)) & 1
-                    n1 = (sw >> (16 + q % 16)) & 1
-                    part += (-1.0 if n0 else 1.0) * x[m, 4 * q + i0]
-                    part += (-1.0 if n1 else 1.0) * x[m, 4 * q + i1]
-                total += float(s[n // 16, g, n % 16]) * part
+                    field = (int(signs[nb, b, lane, j // 2]) >> (16 * (j % 2))) & 0xFFFF
+                    n0 = (field >> e) & 1
+                    n1 = (field >> (8 + e)) & 1
+                    part += (-1.0 if n0 else 1.0) * x[m, 4 * qd + i0]
+                    part += (-1.0 if n1 else 1.0) * x[m, 4 * qd + i1]
+                total += float(s[nb, b, i // 4, j, i % 4]) * part
             y[m, n] = total
     return y

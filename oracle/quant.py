@@ -54,14 +54,22 @@ Residual (two-plane) format: the dense format of both planes with their
   idx0 < idx1 the kept positions.  Sign word j covers quads 16 j .. 16 j + 15:
   bit q % 16 is set when the element at idx0 is negative, bit 16 + q % 16
   when the element at idx1 is.
-  Stored tile-major, like the dense format (store_24, load_24): a 16-row tile
-  and a 128-column group together, word-index-major within the tile-group,
-  so that row i's word w sits at position 16 w + i:
-    meta[N / 16][K / 128][4][16] uint32: [nb, g, w, i] = meta word 4 g + w of
-      row 16 nb + i;
-    signs[N / 16][K / 128][2][16] uint32: [nb, g, w, i] = sign word 2 g + w of
-      row 16 nb + i;
-    scales[N / 16][K / 128][16] fp16 bits (tile_scales).
+  Stored lane-major (store_24, load_24): a 16-row tile and a block of four
+  128-column groups together, G4 = ceil(G / 4) blocks per tile (G = K / 128;
+  the groups of the last block past G are zero).  Lane l = 16 q + i stands
+  for row i of the tile and the quads 32 g + 8 q .. 32 g + 8 q + 7 of each
+  group g (its meta word 4 g + q), so that one lane finds its words for the
+  four groups of a block side by side:
+    meta[N / 16][G4][64][4] uint32: [nb, b, 16 q + i, j] = meta word
+      4 g + q of row 16 nb + i, g = 4 b + j;
+    signs[N / 16][G4][64][2] uint32: the 16-bit sign field of lane (i, q)
+      and group g in the low half of [nb, b, 16 q + i, p] for g = 4 b + 2 p,
+      in the high half for g = 4 b + 2 p + 1.  The field holds the lane's
+      quads 32 g + 8 q + e, e = 0..7: bit e the idx0 sign, bit 8 + e the
+      idx1 sign (bits 8 (q % 2) + e and 16 + 8 (q % 2) + e of sign word
+      2 g + q // 2 of the row);
+    scales[N / 16][G4][4][4][4] fp16 bits: [nb, b, q, j, r] = the scale of
+      row 16 nb + 4 q + r and group 4 b + j.
 """
 
 import numpy as np
@@ -327,7 +335,7 @@ def near_tie_24(wr, s, rel=NEAR_REL):
 def quantize_24(w):
     """Rotate, keep 2 of every 4 along K, absmean over the kept elements, pack.
 
-    Returns meta, signs, scales (stored, tile-major) plus wr, s, idx0, idx1,
+    Returns meta, signs, scales (stored, lane-major) plus wr, s, idx0, idx1,
     neg0, neg1 and the dense ternary equivalent t."""
     w = _check_w(w)
     wr = rotate_blocks(w)
@@ -369,30 +377,66 @@ def pack_24(idx0, idx1, neg0, neg1):
 
 def store_24(meta, signs, scales):
     """Row words and scales ([N, K/32], [N, K/64], [N, K/128]) into the stored
-    tile-major arrays: row i of tile nb, word 4 g + w (meta) or 2 g + w (signs)
-    of its row, to [nb, g, w, i]; scales as tile_scales."""
+    lane-major arrays (module docstring): meta [N/16, G4, 64, 4], signs
+    [N/16, G4, 64, 2], scales [N/16, G4, 4, 4, 4], groups past G zero."""
     meta = np.asarray(meta, dtype=np.uint32)
     signs = np.asarray(signs, dtype=np.uint32)
+    scales = np.asarray(scales, dtype=np.uint16)
     n, nw = meta.shape
-    if n % 16 or nw % 4 or signs.shape != (n, nw // 2):
-        raise ValueError("2:4 rows must be [N, K/32] and [N, K/64] with N a multiple of 16")
+    if n % 16 or nw % 4 or signs.shape != (n, nw // 2) or scales.shape != (n, nw // 4):
+        raise ValueError("2:4 rows must be [N, K/32], [N, K/64], [N, K/128] with N a multiple of 16")
     g = nw // 4
-    m = meta.reshape(n // 16, 16, g, 4).transpose(0, 2, 3, 1)
-    sg = signs.reshape(n // 16, 16, g, 2).transpose(0, 2, 3, 1)
-    return np.ascontiguousarray(m), np.ascontiguousarray(sg), tile_scales(scales)
+    g4 = -(-g // 4)
+    # per row, group and lane column q: the meta word 4 g + q
+    mw = np.zeros((n, 4 * g4, 4), dtype=np.uint32)
+    mw[:, :g, :] = meta.reshape(n, g, 4)
+    # the 16-bit sign field of (row, g, q) from sign word 2 g + q // 2
+    sw = signs.reshape(n, g, 2).astype(np.uint64)
+    field = np.zeros((n, 4 * g4, 4), dtype=np.uint64)
+    for q in range(4):
+        word = sw[:, :, q // 2]
+        sh = np.uint64(8 * (q % 2))
+        field[:, :g, q] = ((word >> sh) & np.uint64(0xFF)) | (((word >> (np.uint64(16) + sh)) & np.uint64(0xFF)) << np.uint64(8))
+    sc = np.zeros((n, 4 * g4), dtype=np.uint16)
+    sc[:, :g] = scales
+    nb = n // 16
+    # meta: (nb, i, b, j, q) -> (nb, b, q, i, j)
+    m = mw.reshape(nb, 16, g4, 4, 4).transpose(0, 2, 4, 1, 3).reshape(nb, g4, 64, 4)
+    # signs: pairs of groups in one word, (nb, i, b, p, e, q) -> (nb, b, q, i, p)
+    f = field.reshape(nb, 16, g4, 2, 2, 4)
+    pair = f[:, :, :, :, 0, :] | (f[:, :, :, :, 1, :] << np.uint64(16))
+    sg = pair.transpose(0, 2, 4, 1, 3).reshape(nb, g4, 64, 2).astype(np.uint32)
+    # scales: row 16 nb + 4 q + r, group 4 b + j -> [nb, b, q, j, r]
+    st = sc.reshape(nb, 4, 4, g4, 4).transpose(0, 3, 1, 4, 2)
+    return np.ascontiguousarray(m), np.ascontiguousarray(sg), np.ascontiguousarray(st)
 
 
-def load_24(meta, signs, scales):
-    """Inverse of store_24: the row words [N, K/32], [N, K/64] and the
-    scales [N, K/128]."""
+def load_24(meta, signs, scales, k):
+    """Inverse of store_24 for K-long rows: the row words [N, K/32],
+    [N, K/64] and the scales [N, K/128]."""
     meta = np.asarray(meta, dtype=np.uint32)
     signs = np.asarray(signs, dtype=np.uint32)
-    if meta.ndim != 4 or meta.shape[2:] != (4, 16) or signs.shape != meta.shape[:2] + (2, 16):
-        raise ValueError("stored 2:4 planes must be [N/16, G, 4, 16] and [N/16, G, 2, 16]")
-    nb, g = meta.shape[:2]
-    m = meta.transpose(0, 3, 1, 2).reshape(nb * 16, g * 4)
-    sg = signs.transpose(0, 3, 1, 2).reshape(nb * 16, g * 2)
-    return np.ascontiguousarray(m), np.ascontiguousarray(sg), untile_scales(scales)
+    scales = np.asarray(scales, dtype=np.uint16)
+    g = k // GROUP
+    g4 = -(-g // 4)
+    if k % GROUP or meta.ndim != 4 or meta.shape[1:] != (g4, 64, 4) or signs.shape != meta.shape[:2] + (64, 2) \
+            or scales.shape != meta.shape[:2] + (4, 4, 4):
+        raise ValueError("stored 2:4 planes must be [N/16, G4, 64, 4], [N/16, G4, 64, 2] and [N/16, G4, 4, 4, 4]")
+    nb = meta.shape[0]
+    n = 16 * nb
+    m = meta.reshape(nb, g4, 4, 16, 4).transpose(0, 3, 1, 4, 2).reshape(n, 4 * g4, 4)[:, :g, :]
+    pair = signs.reshape(nb, g4, 4, 16, 2).astype(np.uint64)
+    field = np.stack([pair & np.uint64(0xFFFF), pair >> np.uint64(16)], axis=-1)  # (nb, b, q, i, p, e)
+    field = field.transpose(0, 3, 1, 4, 5, 2).reshape(n, 4 * g4, 4)[:, :g, :]  # (row, g, q)
+    sw = np.zeros((n, g, 2), dtype=np.uint64)
+    for q in range(4):
+        sh = np.uint64(8 * (q % 2))
+        lo = field[:, :, q] & np.uint64(0xFF)
+        hi = field[:, :, q] >> np.uint64(8)
+        sw[:, :, q // 2] |= (lo << sh) | (hi << (np.uint64(16) + sh))
+    sc = scales.transpose(0, 2, 4, 1, 3).reshape(n, 4 * g4)[:, :g]
+    return (np.ascontiguousarray(m.reshape(n, 4 * g)), np.ascontiguousarray(sw.reshape(n, 2 * g).astype(np.uint32)),
+            np.ascontiguousarray(sc))
 
 
 def unpack_24(meta, signs, k):

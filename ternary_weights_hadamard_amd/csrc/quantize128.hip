@@ -264,17 +264,36 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
       u32x2 mw = {0u, 0u};
 #pragma unroll
       for (int qd = 0; qd < 16; ++qd) mw[qd >> 3] |= nib[qd] << (4 * (qd & 7));
-      // tile-major: a 16-row tile's words of group bk, word w of row i at 16 w + i
-      // (meta words 2 half and 2 half + 1, sign word half)
-      const int64_t tg = (grow >> 4) * kblocks + bk;
-      const int64_t ri = grow & 15;
-      meta[(tg * 4 + 2 * half) * 16 + ri] = mw[0];
-      meta[(tg * 4 + 2 * half + 1) * 16 + ri] = mw[1];
-      codes[(tg * 2 + half) * 16 + ri] = sbits;
+      // lane-major blocks of four groups: this thread holds lanes 16 q + i for
+      // q = 2 half, 2 half + 1 (row i of the tile) of group bk = 4 b + j: meta
+      // word j of each lane, its 16-bit sign field (the byte pair of sbits at
+      // bits 8 (q % 2) and 16 + 8 (q % 2)) in half j % 2 of sign word j / 2,
+      // and the row's scale at [b][i / 4][j][i % 4].  The last group of K also
+      // zeroes the padded groups of its block.
+      const int64_t g4 = (kblocks + 3) >> 2;
+      const int64_t tb = (grow >> 4) * g4 + (bk >> 2);
+      const int ri = (int)(grow & 15), j = (int)(bk & 3);
+      uint16_t* sfield = reinterpret_cast<uint16_t*>(codes);
+      const uint32_t f0 = (sbits & 0xFFu) | (((sbits >> 16) & 0xFFu) << 8);
+      const uint32_t f1 = ((sbits >> 8) & 0xFFu) | (((sbits >> 24) & 0xFFu) << 8);
+      const int64_t l0 = tb * 64 + 16 * (2 * half) + ri, l1 = l0 + 16;
+      meta[l0 * 4 + j] = mw[0];
+      meta[l1 * 4 + j] = mw[1];
+      sfield[l0 * 4 + j] = (uint16_t)f0;
+      sfield[l1 * 4 + j] = (uint16_t)f1;
+      const uint32_t h16 = f32_to_f16_bits(s);
       if (half == 0) {
-        const uint32_t h16 = f32_to_f16_bits(s);
         if ((h16 & 0x7fffu) == 0x7c00u) flags |= TB_EFLAG_SCALE_OVF;
-        scales[tg * 16 + ri] = (uint16_t)h16;
+        scales[tb * 64 + ((ri >> 2) * 4 + j) * 4 + (ri & 3)] = (uint16_t)h16;
+      }
+      if (bk == kblocks - 1) {
+        for (int jj = j + 1; jj < 4; ++jj) {
+          meta[l0 * 4 + jj] = 0u;
+          meta[l1 * 4 + jj] = 0u;
+          sfield[l0 * 4 + jj] = 0;
+          sfield[l1 * 4 + jj] = 0;
+          if (half == 0) scales[tb * 64 + ((ri >> 2) * 4 + jj) * 4 + (ri & 3)] = 0;
+        }
       }
     }
     wave_flag_or(err_flag, flags);

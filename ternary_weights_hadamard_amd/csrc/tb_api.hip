@@ -199,12 +199,17 @@ size_t tb_act8_bytes(int64_t B, int64_t K) {
   return act8_bytes((size_t)B * (size_t)K);
 }
 
+// The 2:4 format stores whole blocks of four 128-groups: N * K' elements'
+// worth of planes for K' = K rounded up to a multiple of 512.
+static size_t nk24(int64_t N, int64_t K) { return (size_t)N * (size_t)((K + 511) / 512 * 512); }
+
 tb_status tb_packed_bytes(int fmt, int64_t N, int64_t K, size_t* code_bytes, size_t* meta_bytes,
                           size_t* scale_bytes) {
   if (fmt != TB_FMT_DENSE && fmt != TB_FMT_24 && fmt != TB_FMT_DENSE_MINERR && fmt != TB_FMT_DENSE_RESID)
     return TB_ERR_FORMAT;
   if (!dims_ok(N, K)) return TB_ERR_SHAPE;
-  const size_t nk = (size_t)N * (size_t)K, planes = fmt == TB_FMT_DENSE_RESID ? 2 : 1;
+  const size_t nk = fmt == TB_FMT_24 ? nk24(N, K) : (size_t)N * (size_t)K;
+  const size_t planes = fmt == TB_FMT_DENSE_RESID ? 2 : 1;
   if (code_bytes) *code_bytes = fmt == TB_FMT_24 ? nk / 16 : planes * nk / 4;
   if (meta_bytes) *meta_bytes = fmt == TB_FMT_24 ? nk / 8 : 0;
   if (scale_bytes) *scale_bytes = planes * nk / 64;
@@ -257,10 +262,11 @@ tb_status tb_quantize_pack(const float* W, int64_t N, int64_t K, int fmt, uint32
   if (!W || !codes || !scales || (fmt == TB_FMT_24 && !meta)) return TB_ERR_NULL;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(scales) || (meta && !aligned16(meta))) return TB_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(err_flag) & 3u) != 0) return TB_ERR_ALIGN;
-  const size_t nk = (size_t)N * (size_t)K;
+  const size_t nk = (size_t)N * (size_t)K, nkp = nk24(N, K);
   const bool dense = fmt != TB_FMT_24;
   const size_t planes = fmt == TB_FMT_DENSE_RESID ? 2 : 1;
-  const size_t cb = dense ? planes * nk / 4 : nk / 16, mb = dense ? 0 : nk / 8, sb = planes * nk / 64;
+  const size_t cb = dense ? planes * nk / 4 : nkp / 16, mb = dense ? 0 : nkp / 8,
+               sb = dense ? planes * nk / 64 : nkp / 64;
   if (overlap(W, nk * 4, codes, cb) || overlap(W, nk * 4, scales, sb) || overlap(codes, cb, scales, sb) ||
       (meta && (overlap(W, nk * 4, meta, mb) || overlap(meta, mb, codes, cb) || overlap(meta, mb, scales, sb))))
     return TB_ERR_ALIAS;
@@ -335,7 +341,7 @@ tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, 
   if (!x || !meta || !signs || !scales || !y) return TB_ERR_NULL;
   if (!aligned16(x) || !aligned16(meta) || !aligned16(signs) || !aligned16(scales) || !aligned16(y))
     return TB_ERR_ALIGN;
-  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)B * (size_t)N * 4;
+  const size_t nk = nk24(N, K), yb = (size_t)B * (size_t)N * 4;
   if (overlap(y, yb, x, (size_t)B * K * 2) || overlap(y, yb, meta, nk / 8) || overlap(y, yb, signs, nk / 16) ||
       overlap(y, yb, scales, nk / 64))
     return TB_ERR_ALIAS;

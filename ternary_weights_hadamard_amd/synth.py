@@ -89,22 +89,40 @@ def random_scales_f16(n, k, seed, lo=0.005, hi=0.05):
     return rng.uniform(lo, hi, size=(n // 16, k // 128, 16)).astype(np.float16).view(np.uint16)
 
 
+def _blocks24(k):
+    """Blocks of four 128-groups per 16-row tile in the stored 2:4 format, and
+    the [blocks, 4] mask of the groups that exist (the last block of a K that
+    is not a multiple of 512 is padded with zero groups)."""
+    g = k // 128
+    g4 = -(-g // 4)
+    return g4, (np.arange(4 * g4).reshape(g4, 4) < g)
+
+
 def random_scales24_f16(n, k, seed, lo=0.005, hi=0.05):
     """fp16 bit patterns of U(lo, hi) draws in the 2:4 format's stored scale
-    shape [n/16, k/128, 16] (independent draws, so any order is the same
-    distribution)."""
+    shape [n/16, G4, 4, 4, 4] (G4 = ceil(k/512); [.., b, q, j, r] is group
+    4 b + j; padded groups zero).  Independent draws, so any order is the
+    same distribution."""
     rng = np.random.default_rng(seed)
-    return rng.uniform(lo, hi, size=(n // 16, k // 128, 16)).astype(np.float16).view(np.uint16)
+    g4, valid = _blocks24(k)
+    s = rng.uniform(lo, hi, size=(n // 16, g4, 4, 4, 4)).astype(np.float16).view(np.uint16)
+    return s * valid[None, :, None, :, None].astype(np.uint16)
 
 
 def random_24(n, k, seed):
-    """2:4 planes in the stored shapes, meta [n/16, k/128, 4, 16] with a
-    uniform choice of the 6 index pairs per quad and signs [n/16, k/128, 2, 16]
-    with fair random bits (every word an independent draw)."""
+    """2:4 planes in the stored shapes, meta [n/16, G4, 64, 4] (word [.., b, l, j]
+    of group 4 b + j) with a uniform choice of the 6 index pairs per quad, and
+    signs [n/16, G4, 64, 2] (two 16-bit fields per word, group 4 b + 2 p in
+    the low half of word p) with fair random bits.  Padded groups are zero."""
     rng = np.random.default_rng(seed)
-    nib = rng.choice(np.array(NIBBLES_24, dtype=np.uint32), size=(n // 16, k // 128, 4, 16, 8))
+    g4, valid = _blocks24(k)
+    nib = rng.choice(np.array(NIBBLES_24, dtype=np.uint32), size=(n // 16, g4, 64, 4, 8))
     meta = np.bitwise_or.reduce(nib << (4 * np.arange(8, dtype=np.uint32)), axis=4).astype(np.uint32)
-    signs = rng.integers(0, 2 ** 32, size=(n // 16, k // 128, 2, 16), dtype=np.uint64).astype(np.uint32)
+    meta *= valid[None, :, None, :].astype(np.uint32)
+    signs = rng.integers(0, 2 ** 32, size=(n // 16, g4, 64, 2), dtype=np.uint64).astype(np.uint32)
+    half = valid.reshape(g4, 2, 2)  # [b, p, half]
+    keep = (half[:, :, 0] * np.uint32(0xFFFF)) | (half[:, :, 1] * np.uint32(0xFFFF0000))
+    signs &= keep[None, :, None, :].astype(np.uint32)
     return meta, signs
 
 
@@ -138,10 +156,14 @@ def torch_scales_f16(n, k, gen, device, lo=0.005, hi=0.05):
 
 
 def torch_scales24_f16(n, k, gen, device, lo=0.005, hi=0.05):
-    """U(lo, hi) fp16 scales in the 2:4 stored shape [n/16, k/128, 16]."""
+    """U(lo, hi) fp16 scales in the 2:4 stored shape [n/16, G4, 4, 4, 4]
+    (padded groups zero, as random_scales24_f16)."""
     import torch
 
-    return (lo + (hi - lo) * torch.rand((n // 16, k // 128, 16), generator=gen, device=device)).to(torch.float16)
+    g4, valid = _blocks24(k)
+    s = lo + (hi - lo) * torch.rand((n // 16, g4, 4, 4, 4), generator=gen, device=device)
+    mask = torch.as_tensor(valid, device=device).view(1, g4, 1, 4, 1)
+    return (s * mask).to(torch.float16)
 
 
 def torch_gaussian_bf16(shape, gen, device, scale=1.0):
@@ -167,13 +189,20 @@ def torch_stack_weights(n, k, gen, device, sigma=0.02, outlier_col_frac=0.01, nu
 
 
 def torch_24(n, k, gen, device):
-    """2:4 planes in the stored shapes (meta [n/16, k/128, 4, 16], signs
-    [n/16, k/128, 2, 16]) as int32, uniform index pairs and signs."""
+    """2:4 planes in the stored shapes (meta [n/16, G4, 64, 4], signs
+    [n/16, G4, 64, 2]) as int32, uniform index pairs and signs, padded groups
+    zero (as random_24)."""
     import torch
 
+    g4, valid = _blocks24(k)
     nib = torch.tensor(NIBBLES_24, dtype=torch.int64, device=device)
-    sel = torch.randint(0, 6, (n // 16, k // 128, 4, 16, 8), generator=gen, device=device)
-    meta = (nib[sel] << (4 * torch.arange(8, device=device, dtype=torch.int64))).sum(-1).to(torch.int32)
-    signs = torch.randint(-2 ** 31, 2 ** 31, (n // 16, k // 128, 2, 16), generator=gen, device=device,
-                          dtype=torch.int64)
-    return meta, signs.to(torch.int32)
+    sel = torch.randint(0, 6, (n // 16, g4, 64, 4, 8), generator=gen, device=device)
+    meta = (nib[sel] << (4 * torch.arange(8, device=device, dtype=torch.int64))).sum(-1)
+    meta = meta * torch.as_tensor(valid, device=device).view(1, g4, 1, 4)
+    signs = torch.randint(0, 2 ** 32, (n // 16, g4, 64, 2), generator=gen, device=device, dtype=torch.int64)
+    half = valid.reshape(g4, 2, 2).astype(np.int64)
+    keep = torch.as_tensor(half[:, :, 0] * 0xFFFF | half[:, :, 1] * 0xFFFF0000, device=device).view(1, g4, 1, 2)
+    signs = signs & keep
+    # two's complement view of the uint32 words
+    return (torch.where(meta >= 2 ** 31, meta - 2 ** 32, meta).to(torch.int32),
+            torch.where(signs >= 2 ** 31, signs - 2 ** 32, signs).to(torch.int32))

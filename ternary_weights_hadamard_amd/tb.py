@@ -10,10 +10,10 @@ Dtypes on the Python side (bit patterns are what matter):
   act8 operand       torch.uint8, flat, exactly tb_act8_bytes(B, K) bytes
   weights W          torch.float32 [N, K]
   codes              torch.int32 (uint32 bit patterns): dense [N/16, K/128, 128],
-                     2:4 sign plane [N/16, K/128, 2, 16]
-  meta               torch.int32, 2:4 only: [N/16, K/128, 4, 16]
+                     2:4 sign plane [N/16, G4, 64, 2] (G4 = ceil(K/512))
+  meta               torch.int32, 2:4 only: [N/16, G4, 64, 4]
   scales             torch.float16 (fp16 bit patterns), tile-major: [N/16, K/128, 16]
-                     (two-plane [N/16, 2K/128, 16])
+                     (two-plane [N/16, 2K/128, 16]; 2:4 [N/16, G4, 4, 4, 4])
 """
 
 import ctypes
@@ -183,13 +183,15 @@ def tb_quantize_pack(w, fmt=TB_FMT_DENSE, codes=None, meta=None, scales=None, er
     n, k = w.shape
     dev = w.device
     planes = 2 if fmt == TB_FMT_DENSE_RESID else 1
+    g4 = -(-k // 512)  # 2:4 blocks of four groups per tile
     if codes is None:
-        shape = (n // 16, planes * k // 128, 128) if fmt != TB_FMT_24 else (n // 16, k // 128, 2, 16)
+        shape = (n // 16, planes * k // 128, 128) if fmt != TB_FMT_24 else (n // 16, g4, 64, 2)
         codes = torch.empty(shape, dtype=torch.int32, device=dev)
     if meta is None and fmt == TB_FMT_24:
-        meta = torch.empty((n // 16, k // 128, 4, 16), dtype=torch.int32, device=dev)
+        meta = torch.empty((n // 16, g4, 64, 4), dtype=torch.int32, device=dev)
     if scales is None:
-        scales = torch.empty((n // 16, planes * k // 128, 16), dtype=torch.float16, device=dev)
+        shape = (n // 16, planes * k // 128, 16) if fmt != TB_FMT_24 else (n // 16, g4, 4, 4, 4)
+        scales = torch.empty(shape, dtype=torch.float16, device=dev)
     _dev(codes, meta, scales, err_flag)
     _check(lib().tb_quantize_pack(_p(w), n, k, int(fmt), _p(codes), _p(meta), _p(scales), _p(err_flag),
                                   _stream(stream)), "tb_quantize_pack")
@@ -304,13 +306,14 @@ def tb_ternary_gemv_multi(segments, stream=None):
 
 
 def tb_ternary24_gemv(x, meta, signs, scales, y=None, stream=None):
-    """x bf16 [B, K]; meta [N/16, K/128, 4, 16], signs [N/16, K/128, 2, 16],
-    scales [N/16, K/128, 16] (the stored 2:4 format)."""
+    """x bf16 [B, K]; meta [N/16, G4, 64, 4], signs [N/16, G4, 64, 2], scales
+    [N/16, G4, 4, 4, 4] (the stored 2:4 format, G4 = ceil(K/512))."""
     _dev(x, meta, signs, scales)
     b, k = x.shape
     n = meta.shape[0] * 16
-    if tuple(meta.shape) != (n // 16, k // 128, 4, 16) or tuple(signs.shape) != (n // 16, k // 128, 2, 16) \
-            or scales.numel() != n * (k // 128):
+    g4 = -(-k // 512)
+    if tuple(meta.shape) != (n // 16, g4, 64, 4) or tuple(signs.shape) != (n // 16, g4, 64, 2) \
+            or scales.numel() != n * g4 * 4:
         raise ValueError(f"2:4 planes {tuple(meta.shape)}, {tuple(signs.shape)} do not match K = {k}")
     if y is None:
         y = torch.empty((b, n), dtype=torch.float32, device=x.device)

@@ -150,7 +150,7 @@ def check_24_planes(meta_gpu, signs_gpu, scales_gpu, ref, k, what):
     1e-5 relative), and each kept element's sign must be that of W' wherever
     |W'| > 1e-5 s.  fp16 scales equal or 1 ulp.  Returns (near-tie quads,
     near-tie quads where the GPU differs)."""
-    meta_r, signs_r, _ = oracle.quant.load_24(host_u32(meta_gpu), host_u32(signs_gpu), host_u16(scales_gpu))
+    meta_r, signs_r, _ = oracle.quant.load_24(host_u32(meta_gpu), host_u32(signs_gpu), host_u16(scales_gpu), k)
     i0, i1, n0, n1 = oracle.quant.unpack_24(meta_r, signs_r, k)
     wr = ref["wr"]
     n = wr.shape[0]

@@ -72,6 +72,8 @@ def test_status_strings_and_version():
 def test_packed_bytes():
     assert tb.tb_packed_bytes(tb.TB_FMT_DENSE, 5120, 17408) == (5120 * 17408 // 4, 0, 5120 * 17408 // 64)
     assert tb.tb_packed_bytes(tb.TB_FMT_24, 17408, 5120) == (17408 * 5120 // 16, 17408 * 5120 // 8, 17408 * 5120 // 64)
+    # 2:4 stores whole blocks of four 128-groups: K = 384 takes the room of 512
+    assert tb.tb_packed_bytes(tb.TB_FMT_24, 256, 384) == (256 * 512 // 16, 256 * 512 // 8, 256 * 512 // 64)
     assert tb.tb_packed_bytes(tb.TB_FMT_DENSE_MINERR, 256, 384) == tb.tb_packed_bytes(tb.TB_FMT_DENSE, 256, 384)
     assert tb.tb_packed_bytes(tb.TB_FMT_DENSE_RESID, 5120, 5120) == (5120 * 5120 // 2, 0, 5120 * 5120 // 32)
     L = tb.lib()

@@ -63,8 +63,8 @@ def _24_case():
 
 
 def _planes(ref, idx0, idx1, neg0, neg1):
-    meta, signs, scales = oracle.quant.store_24(*oracle.quant.pack_24(idx0, idx1, neg0, neg1),
-                                                oracle.quant.untile_scales(ref["scales"]))
+    rows_scales = oracle.quant.load_24(ref["meta"], ref["signs"], ref["scales"], 128)[2]
+    meta, signs, scales = oracle.quant.store_24(*oracle.quant.pack_24(idx0, idx1, neg0, neg1), rows_scales)
     return _t(meta), _t(signs), _t(scales)
 
 

@@ -243,13 +243,15 @@ def test_gemv24_exact_and_dense_equivalence():
     n, k = 256, 1024
     meta, signs = synth.random_24(n, k, seed=40)
     x = synth.small_int_bf16((2, k), seed=41)
-    sc = (2.0 ** np.random.default_rng(42).integers(-5, 2, size=(n // 16, k // 128, 16))).astype(np.float16).view(np.uint16)
+    # power-of-two scales by row and group, in each format's stored order
+    sc_rows = (2.0 ** np.random.default_rng(42).integers(-5, 2, size=(n, k // 128))).astype(np.float16).view(np.uint16)
+    meta_r, signs_r, _ = oracle.quant.load_24(meta, signs, synth.random_scales24_f16(n, k, seed=43), k)
+    meta, signs, sc = oracle.quant.store_24(meta_r, signs_r, sc_rows)
     y24 = tb.tb_ternary24_gemv(bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(sc))
-    meta_r, signs_r, _ = oracle.quant.load_24(meta, signs, sc)
     i0, i1, n0, n1 = oracle.quant.unpack_24(meta_r, signs_r, k)
     dense = oracle.quant.pack_dense(oracle.quant.dense_from_24(i0, i1, n0, n1))
-    # both formats store the scales tile-major, [N/16, K/128, 16]
-    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(sc), x.shape[0])
+    yd = tb.tb_ternary_gemv(tb.tb_act8_prep(bf16_dev(x)), u32_dev(dense), f16_dev(oracle.quant.tile_scales(sc_rows)),
+                            x.shape[0])
     torch.cuda.synchronize()
     ref = oracle.matvec.gemv24(x, meta, signs, sc, k)
     assert np.array_equal(y24.cpu().numpy().astype(np.float64), ref)

@@ -117,13 +117,30 @@ def test_output_canaries():
     check_dense_codes(codes, scales, oracle.quant.quantize_dense(w.astype(np.float64)), k, "canary run")
 
 
-@pytest.mark.parametrize("n,k,seed", [(128, 128, 11), (256, 512, 12), (1024, 1024, 0)])
+@pytest.mark.parametrize("n,k,seed", [(128, 128, 11), (256, 512, 12), (1024, 1024, 0), (256, 384, 13),
+                                      (128, 1664, 14)])
 def test_24_matches_oracle(n, k, seed):
+    # K = 128, 384 and 1664 leave the last block of four groups 3, 1 and 3
+    # groups short: those stored groups must come back zero (the buffers start
+    # filled with another pattern)
     w = synth.single_layer_weights(n, k, seed=seed) if seed == 0 else synth.stack_weights(n, k, seed=seed)
     say(f"quantize 2:4 {n}x{k}")
-    signs, meta, scales = _quant(w, fmt=tb.TB_FMT_24)
+    g4 = -(-k // 512)
+    signs = torch.full((n // 16, g4, 64, 2), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    meta = torch.full((n // 16, g4, 64, 4), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    scales = torch.full((n // 16, g4, 4, 4, 4), -3.0, dtype=torch.float16, device=DEV)
+    tb.tb_quantize_pack(f32_dev(w), fmt=tb.TB_FMT_24, codes=signs, meta=meta, scales=scales)
+    torch.cuda.synchronize()
     ref = oracle.quant.quantize_24(w.astype(np.float64))
     check_24_planes(meta, signs, scales, ref, k, f"2:4 {n}x{k}")
+    pad = 4 * g4 - k // 128
+    if pad:
+        first = 4 - pad  # first padded group of the last block
+        assert torch.all(meta[:, -1, :, first:] == 0)
+        assert np.all(host_u16(scales[:, -1, :, first:, :]) == 0)
+        halves = torch.from_numpy(host_u32(signs[:, -1]).astype(np.int64)).view(n // 16, 64, 2)
+        fields = torch.stack([halves & 0xFFFF, halves >> 16], dim=-1).view(n // 16, 64, 4)
+        assert torch.all(fields[:, :, first:] == 0)
 
 
 def test_24_full_layer_sampled_blocks():
@@ -137,10 +154,12 @@ def test_24_full_layer_sampled_blocks():
     for a, b in zip(rng.integers(0, n // 128, 16), rng.integers(0, k // 128, 16)):
         rows = slice(128 * a, 128 * (a + 1))
         ref = oracle.quant.quantize_24(w[rows, 128 * b:128 * (b + 1)].astype(np.float64))
-        tiles = slice(8 * a, 8 * (a + 1))  # the block's eight 16-row tiles, group b
-        mb = meta[tiles, b:b + 1].contiguous()
-        gb = signs[tiles, b:b + 1].contiguous()
-        check_24_planes(mb, gb, scales[tiles, b:b + 1].contiguous(), ref, 128, f"block ({a}, {b})")
+        tiles = slice(8 * a, 8 * (a + 1))  # the block's eight 16-row tiles
+        # group b of those tiles as the stored planes of a K = 128 matrix (through the oracle's layout)
+        m_r, s_r, sc_r = oracle.quant.load_24(host_u32(meta[tiles]), host_u32(signs[tiles]), host_u16(scales[tiles]), k)
+        mb, gb, sb = oracle.quant.store_24(m_r[:, 4 * b:4 * b + 4], s_r[:, 2 * b:2 * b + 2], sc_r[:, b:b + 1])
+        check_24_planes(torch.from_numpy(mb.view(np.int32)), torch.from_numpy(gb.view(np.int32)),
+                        torch.from_numpy(sb.view(np.int16)).view(torch.float16), ref, 128, f"block ({a}, {b})")
 
 
 # ---------------------------------------------------------------- error-minimising rule

@@ -36,7 +36,9 @@ def test_packed_bytes_formula(n, k):
     c, m, s = bits.packed_bytes("dense", n, k)
     assert (c * 8 + s * 8) / (n * k) == bits.dense_storage_bits()
     c, m, s = bits.packed_bytes("24", n, k)
-    assert ((c + m + s) * 8) / (n * k) == bits.storage24_bits()
+    kp = -(-k // 512) * 512  # the 2:4 format pads K to whole blocks of four groups
+    assert ((c + m + s) * 8) / (n * kp) == bits.storage24_bits()
+    assert (kp == k) == (k % 512 == 0)
 
 
 def test_buffers_have_formula_sizes():

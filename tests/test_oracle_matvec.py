@@ -109,7 +109,7 @@ def test_gemv24_equals_bruteforce_and_dense_expansion(n, k, b):
     yb = mv.gemv24_bruteforce(x, meta, signs, scales, k)
     assert np.max(np.abs(y - yb)) <= 1e-12 * max(1.0, np.max(np.abs(yb)))
     # the 2:4 encoding expanded to dense ternary codes gives the same product exactly
-    meta_r, signs_r, scales_r = q.load_24(meta, signs, scales)
+    meta_r, signs_r, scales_r = q.load_24(meta, signs, scales, k)
     idx0, idx1, neg0, neg1 = q.unpack_24(meta_r, signs_r, k)
     dense_codes = q.pack_dense(q.dense_from_24(idx0, idx1, neg0, neg1))
     assert np.array_equal(mv.gemv(x, dense_codes, q.tile_scales(scales_r), k), y)

@@ -230,31 +230,49 @@ def test_24_packing_hand_worked(golden_dir):
     assert all(np.array_equal(a, b) for a, b in zip(back, (idx0, idx1, neg0, neg1)))
 
 
-def test_24_stored_layout_places_every_word():
-    # tile-major storage: row i of tile nb, word 4 g + w (meta) or 2 g + w
-    # (signs) of its row goes to [nb, g, w, i]; scales as tile_scales.  Words
-    # numbered by (row, word) land where the layout says, and load_24 undoes it.
-    n, k = 48, 384
+@pytest.mark.parametrize("k", [384, 1024])
+def test_24_stored_layout_places_every_word(k):
+    # lane-major storage, blocks of four groups: lane 16 q + i of block b holds
+    # row i's meta word 4 g + q for g = 4 b + j at [nb, b, lane, j]; its sign
+    # field (sign word 2 g + q // 2, the byte pair at bits 8 (q % 2) and
+    # 16 + 8 (q % 2)) in half g % 2 of [nb, b, lane, (g % 4) // 2]; the scale of
+    # row 4 q + r and group 4 b + j at [nb, b, q, j, r].  K = 384 leaves the last
+    # block one group short, which stays zero.  Words numbered by (row, word)
+    # land where the layout says, and load_24 undoes it.
+    n = 48
     g = k // 128
+    g4 = -(-g // 4)
     rows = np.arange(n, dtype=np.uint32)[:, None]
     meta = rows * 1000 + np.arange(4 * g, dtype=np.uint32)[None, :]
-    signs = rows * 1000 + 500 + np.arange(2 * g, dtype=np.uint32)[None, :]
+    rng = np.random.default_rng(5)
+    signs = rng.integers(0, 2 ** 32, size=(n, 2 * g), dtype=np.uint64).astype(np.uint32)
     scales = (rows * 10 + np.arange(g, dtype=np.uint32)[None, :]).astype(np.uint16)
     m, sg, sc = q.store_24(meta, signs, scales)
-    assert m.shape == (n // 16, g, 4, 16) and sg.shape == (n // 16, g, 2, 16) and sc.shape == (n // 16, g, 16)
+    assert m.shape == (n // 16, g4, 64, 4) and sg.shape == (n // 16, g4, 64, 2) and sc.shape == (n // 16, g4, 4, 4, 4)
     for nb in range(n // 16):
-        for gg in range(g):
-            for i in range(16):
-                r = 16 * nb + i
-                for w in range(4):
-                    assert m[nb, gg, w, i] == r * 1000 + 4 * gg + w
-                for w in range(2):
-                    assert sg[nb, gg, w, i] == r * 1000 + 500 + 2 * gg + w
-                assert sc[nb, gg, i] == r * 10 + gg
-    # flat order: a tile-group's meta words are 64 consecutive words, word w of row i at 16 w + i
+        for b in range(g4):
+            for j in range(4):
+                gg = 4 * b + j
+                for qq in range(4):
+                    for i in range(16):
+                        r = 16 * nb + i
+                        lane = 16 * qq + i
+                        half = (int(sg[nb, b, lane, j // 2]) >> (16 * (j % 2))) & 0xFFFF
+                        if gg >= g:
+                            assert m[nb, b, lane, j] == 0 and half == 0
+                            continue
+                        assert m[nb, b, lane, j] == r * 1000 + 4 * gg + qq
+                        word = int(signs[r, 2 * gg + qq // 2])
+                        lo = (word >> (8 * (qq % 2))) & 0xFF
+                        hi = (word >> (16 + 8 * (qq % 2))) & 0xFF
+                        assert half == lo | (hi << 8)
+                    for rr in range(4):
+                        want = (16 * nb + 4 * qq + rr) * 10 + gg if gg < g else 0
+                        assert sc[nb, b, qq, j, rr] == want
+    # flat order: a tile-block's meta is 256 consecutive words, lane l's four at 4 l .. 4 l + 3
     flat = m.reshape(-1)
-    assert flat[(1 * g + 2) * 64 + 16 * 3 + 5] == (16 + 5) * 1000 + 4 * 2 + 3
-    back = q.load_24(m, sg, sc)
+    assert flat[(1 * g4 + 0) * 256 + 4 * (16 * 3 + 5) + 2] == (16 + 5) * 1000 + 4 * 2 + 3
+    back = q.load_24(m, sg, sc, k)
     assert all(np.array_equal(a, b) for a, b in zip(back, (meta, signs, scales)))
 
 
