@@ -225,6 +225,67 @@ class DecodeStack:
         return per_launch_bytes, ms / (replays * nl), nl
 
 
+def gemv24_bytes(n, k, b=1):
+    """Algorithmic bytes of one 2:4 GEMV: meta N K/8, signs N K/16, scales N K/64,
+    bf16 x and fp32 y."""
+    return n * k // 8 + n * k // 16 + n * k // 64 + 2 * b * k + 4 * b * n
+
+
+class Decode24Stack:
+    """The decode step of DecodeStack over 2:4 weights: per layer one launch
+    rotates the previous layer's outputs back (fp32) and this layer's inputs
+    (bf16), then one grouped 2:4 GEMV launch covers the layer's four
+    products."""
+
+    def __init__(self, layers, batch, gen, dev):
+        import torch
+
+        from ternary_weights_hadamard_amd import synth
+
+        self.batch = batch
+        self.w = []
+        for li in range(layers):
+            self.w.append([synth.torch_24(n, k, gen, dev) + (synth.torch_scales24_f16(n, k, gen, dev), n, k)
+                           for _, n, k in FUSED])
+            if li % 16 == 15:
+                log(f"  generated {li + 1}/{layers} 2:4 layers")
+        self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
+        self.xr = [torch.empty((batch, k), dtype=torch.bfloat16, device=dev) for _, n, k in FUSED]
+        self.y = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+        self.yo = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+
+    def gemv_call(self, layer):
+        from ternary_weights_hadamard_amd import tb
+
+        tb.tb_ternary24_gemv_multi([(self.xr[j], meta, signs, sc, self.y[j])
+                                    for j, (meta, signs, sc, n, k) in enumerate(layer)])
+
+    def step(self):
+        from ternary_weights_hadamard_amd import tb
+
+        rot_in = list(zip(self.x, self.xr))
+        rot_out = list(zip(self.y, self.yo))
+        for li, layer in enumerate(self.w):
+            tb.tb_fwht128_multi((rot_out if li > 0 else []) + rot_in)
+            self.gemv_call(layer)
+        tb.tb_fwht128_multi(rot_out)
+
+    def gemv_only(self):
+        for layer in self.w:
+            self.gemv_call(layer)
+
+    def packed_bytes(self):
+        return sum(gemv24_bytes(n, k, 0) for layer in self.w for *_, n, k in layer)
+
+    def gemv_times(self, replays=5):
+        """(algorithmic bytes per launch, ms per launch, launches per step) of
+        the grouped 2:4 launches, graph-replayed on their own stream."""
+        ms, _, g = time_graph(self.gemv_only, replays, 1)
+        del g
+        per_launch = sum(gemv24_bytes(n, k, self.batch) for *_, n, k in self.w[0])
+        return per_launch, ms / (replays * len(self.w)), len(self.w)
+
+
 def time_graph(fn, steps, warmup):
     """Capture fn() in a HIP graph, replay `warmup` times untimed, then time
     exactly `steps` replays bracketed by synchronisations; returns ms total."""
@@ -1087,6 +1148,25 @@ def main():
                                      "gemv_avg_launch_us": round(gms2 * 1e3, 3)}
         log(f"decode two-plane: {ms2:.4f} ms/step, GEMV {extra['decode_two_plane']['gemv_gbs_algorithmic']} GB/s")
         del two
+        torch.cuda.empty_cache()
+        # the same decode step over 2:4 weights (one grouped 2:4 launch per layer)
+        d24 = Decode24Stack(args.layers, args.batch, gen, dev)
+        ms24, _, g24 = time_graph(d24.step, max(3, args.steps // 2), 2)
+        del g24
+        ms24 /= max(3, args.steps // 2)
+        gb24, gms24, _ = d24.gemv_times()
+        tb24 = d24.packed_bytes()
+        extra["decode_24"] = {"ms_per_step": round(ms24, 4), "packed_bytes_per_step": tb24,
+                              "gbs_packed": round(tb24 / (ms24 * 1e-3) / 1e9, 1),
+                              "gemv_bytes_per_launch": gb24,
+                              "gemv_gbs_algorithmic": round(gb24 / (gms24 * 1e-3) / 1e9, 1),
+                              "gemv_frac_of_hbm_peak": round(gb24 / (gms24 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "gemv_avg_launch_us": round(gms24 * 1e3, 3),
+                              "note": "2:4 weights (1.625 bit), one grouped 2:4 GEMV launch per layer"}
+        log(f"decode 2:4: {ms24:.4f} ms/step, GEMV {gms24 * 1e3:.2f} us per layer launch, "
+            f"{extra['decode_24']['gemv_gbs_algorithmic']} GB/s")
+        del d24
+        torch.cuda.empty_cache()
         extra.update(extra_phases(gen, dev, args.quick))
 
     traffic = recorded_traffic(stack.grouping)

@@ -175,6 +175,19 @@ typedef struct {
   int64_t parts;
 } tb_gemv_segment;
 
+/* One product of a grouped tb_ternary24_gemv_multi call: arguments as in
+ * tb_ternary24_gemv. */
+typedef struct {
+  const uint16_t* x;
+  const uint32_t* meta;
+  const uint32_t* signs;
+  const uint16_t* scales;
+  float* y;
+  int64_t B;
+  int64_t N;
+  int64_t K;
+} tb_gemv24_segment;
+
 /* Human-readable name of a status code (static storage, never NULL). */
 TB_API const char* tb_status_string(int status);
 
@@ -374,6 +387,20 @@ TB_API tb_status tb_act8_prep(const uint16_t* x, int64_t B, int64_t K, uint8_t* 
  */
 TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                             const uint16_t* scales, int64_t N, int64_t K, float* y, void* stream);
+
+/*
+ * tb_ternary24_gemv over up to TB_MAX_SEGMENTS independent products in one
+ * launch (a decoder layer's projections: the launch is long enough to keep
+ * HBM streaming, where a single product leaves it idle while the launch
+ * fills and drains).  Same contraction, rules and accuracy per segment; how
+ * a product's K is split over waves (and so the fp32 summation order)
+ * depends on the segments it is grouped with.  Segments with B > 4 make the
+ * call launch each product on its own.  `segs` is a host array read during
+ * the call; no segment's y may overlap any segment's inputs or another y.
+ * count == 0 is a no-op; count outside [0, TB_MAX_SEGMENTS] returns
+ * TB_ERR_SHAPE.
+ */
+TB_API tb_status tb_ternary24_gemv_multi(const tb_gemv24_segment* segs, int count, void* stream);
 
 /*
  * Prefill GEMM with dense ternary weights, the same contraction as

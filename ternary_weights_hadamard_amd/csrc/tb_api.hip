@@ -334,18 +334,49 @@ tb_status tb_ternary_gemv_multi(const tb_gemv_segment* segs, int count, void* st
   return launched(tb::launch_gemv_multi(live, n, as_stream(stream)));
 }
 
+// the arguments of one 2:4 product, without the launch
+static tb_status check_gemv24(const tb_gemv24_segment& a) {
+  if (!dims_ok(a.N, a.K) || a.B < 0 || a.B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
+  if (a.B == 0) return TB_OK;
+  if (!a.x || !a.meta || !a.signs || !a.scales || !a.y) return TB_ERR_NULL;
+  if (!aligned16(a.x) || !aligned16(a.meta) || !aligned16(a.signs) || !aligned16(a.scales) || !aligned16(a.y))
+    return TB_ERR_ALIGN;
+  return TB_OK;
+}
+
+// does y of segment a overlap any input (or, with with_y, the output) of b
+static bool gemv24_y_overlaps(const tb_gemv24_segment& a, const tb_gemv24_segment& b, bool with_y) {
+  const size_t yb = (size_t)a.B * (size_t)a.N * 4, nk = nk24(b.N, b.K);
+  return overlap(a.y, yb, b.x, (size_t)b.B * b.K * 2) || overlap(a.y, yb, b.meta, nk / 8) ||
+         overlap(a.y, yb, b.signs, nk / 16) || overlap(a.y, yb, b.scales, nk / 64) ||
+         (with_y && overlap(a.y, yb, b.y, (size_t)b.B * (size_t)b.N * 4));
+}
+
 tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                             const uint16_t* scales, int64_t N, int64_t K, float* y, void* stream) {
-  if (!dims_ok(N, K) || B < 0 || B > TB_GEMV_MAX_BATCH) return TB_ERR_SHAPE;
-  if (B == 0) return TB_OK;
-  if (!x || !meta || !signs || !scales || !y) return TB_ERR_NULL;
-  if (!aligned16(x) || !aligned16(meta) || !aligned16(signs) || !aligned16(scales) || !aligned16(y))
-    return TB_ERR_ALIGN;
-  const size_t nk = nk24(N, K), yb = (size_t)B * (size_t)N * 4;
-  if (overlap(y, yb, x, (size_t)B * K * 2) || overlap(y, yb, meta, nk / 8) || overlap(y, yb, signs, nk / 16) ||
-      overlap(y, yb, scales, nk / 64))
-    return TB_ERR_ALIAS;
+  const tb_gemv24_segment a{x, meta, signs, scales, y, B, N, K};
+  const tb_status st = check_gemv24(a);
+  if (st != TB_OK || B == 0) return st;
+  if (gemv24_y_overlaps(a, a, false)) return TB_ERR_ALIAS;
   return launched(tb::launch_gemv_ternary24(x, B, meta, signs, scales, N, K, y, as_stream(stream)));
+}
+
+tb_status tb_ternary24_gemv_multi(const tb_gemv24_segment* segs, int count, void* stream) {
+  if (count < 0 || count > TB_MAX_SEGMENTS) return TB_ERR_SHAPE;
+  if (count == 0) return TB_OK;
+  if (!segs) return TB_ERR_NULL;
+  tb_gemv24_segment live[TB_MAX_SEGMENTS];
+  int n = 0;
+  for (int c = 0; c < count; ++c) {
+    const tb_status st = check_gemv24(segs[c]);
+    if (st != TB_OK) return st;
+    if (segs[c].B == 0) continue;
+    for (int d = 0; d < count; ++d)
+      if (segs[d].B != 0 && gemv24_y_overlaps(segs[c], segs[d], d != c)) return TB_ERR_ALIAS;
+    live[n++] = segs[c];
+  }
+  if (n == 0) return TB_OK;
+  return launched(tb::launch_gemv24_multi(live, n, as_stream(stream)));
 }
 
 tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,

@@ -21,6 +21,8 @@ typedef tb_gemv_segment GemvSegment;
 hipError_t launch_gemv_multi(const GemvSegment* segs, int count, hipStream_t stream);
 hipError_t launch_gemv_ternary24(const uint16_t* x, int64_t B, const uint32_t* meta, const uint32_t* signs,
                                  const uint16_t* scales, int64_t N, int64_t K, float* y, hipStream_t stream);
+// segments with B == 0 removed by the API layer
+hipError_t launch_gemv24_multi(const tb_gemv24_segment* segs, int count, hipStream_t stream);
 hipError_t launch_gemm_ternary(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream);
 // at most this many activation rows take the mid-batch kernel (gemm_skinny.hip)

@@ -42,6 +42,12 @@ class FwhtSegment(ctypes.Structure):
                 ("reserved", ctypes.c_int)]
 
 
+class Gemv24Segment(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p), ("B", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64)]
+
+
 class GemvSegment(ctypes.Structure):
     _fields_ = [("act", ctypes.c_void_p), ("B", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p),
@@ -63,6 +69,7 @@ SIGNATURES = {
     "tb_act8_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "tb_act8_prep": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "tb_ternary24_gemv_multi": (_int, [ctypes.POINTER(Gemv24Segment), _int, _vp]),
     "tb_ternary_gemm": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]),
     "tb_ternary_gemm_splitk_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "tb_ternary_gemm_splitk": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp, ctypes.c_size_t, _vp]),
@@ -167,7 +174,8 @@ def tb_fwht128_multi(pairs, stream=None):
         parts = int(p[2]) if len(p) > 2 else 1
         if parts > 1:
             if x.dim() < 2 or x.shape[0] != parts:
-                raise TBError(f"tb_fwht128_multi: x_parts={parts} needs x of shape [{parts}, rows, K], got {tuple(x.shape)}")
+                raise ValueError(f"tb_fwht128_multi: x_parts={parts} needs x of shape [{parts}, rows, K], "
+                                 f"got {tuple(x.shape)}")
             inner = x[0]
         else:
             inner = x
@@ -299,28 +307,50 @@ def tb_ternary_gemv_multi(segments, stream=None):
         k = g // max(planes, 1) * 128
         _act8_operand(act, int(batch), k, "tb_ternary_gemv_multi")
         if y.numel() < max(parts, 1) * int(batch) * n:
-            raise TBError(f"tb_ternary_gemv_multi: y holds {y.numel()} floats, needs {max(parts, 1)} x {batch} x {n}")
+            raise ValueError(f"tb_ternary_gemv_multi: y holds {y.numel()} floats, needs {max(parts, 1)} x {batch} x {n}")
         arr[c] = GemvSegment(act.data_ptr(), int(batch), codes.data_ptr(), scales.data_ptr(), n, k, y.data_ptr(),
                              planes, parts)
     _check(lib().tb_ternary_gemv_multi(arr, len(segments), _stream(stream)), "tb_ternary_gemv_multi")
+
+
+def _planes24(x, meta, signs, scales, where):
+    """(B, N, K) of a 2:4 product, its planes checked against x."""
+    b, k = x.shape
+    n = meta.shape[0] * 16
+    g4 = -(-k // 512)
+    if tuple(meta.shape) != (n // 16, g4, 64, 4) or tuple(signs.shape) != (n // 16, g4, 64, 2) \
+            or scales.numel() != n * g4 * 4:
+        raise ValueError(f"{where}: 2:4 planes {tuple(meta.shape)}, {tuple(signs.shape)} do not match K = {k}")
+    return b, n, k
 
 
 def tb_ternary24_gemv(x, meta, signs, scales, y=None, stream=None):
     """x bf16 [B, K]; meta [N/16, G4, 64, 4], signs [N/16, G4, 64, 2], scales
     [N/16, G4, 4, 4, 4] (the stored 2:4 format, G4 = ceil(K/512))."""
     _dev(x, meta, signs, scales)
-    b, k = x.shape
-    n = meta.shape[0] * 16
-    g4 = -(-k // 512)
-    if tuple(meta.shape) != (n // 16, g4, 64, 4) or tuple(signs.shape) != (n // 16, g4, 64, 2) \
-            or scales.numel() != n * g4 * 4:
-        raise ValueError(f"2:4 planes {tuple(meta.shape)}, {tuple(signs.shape)} do not match K = {k}")
+    b, n, k = _planes24(x, meta, signs, scales, "tb_ternary24_gemv")
     if y is None:
         y = torch.empty((b, n), dtype=torch.float32, device=x.device)
     _dev(y)
     _check(lib().tb_ternary24_gemv(_p(x), b, _p(meta), _p(signs), _p(scales), n, k, _p(y), _stream(stream)),
            "tb_ternary24_gemv")
     return y
+
+
+def tb_ternary24_gemv_multi(segments, stream=None):
+    """One launch of several 2:4 GEMVs: segments = [(x, meta, signs, scales, y), ...]
+    with the shapes of tb_ternary24_gemv; y fp32 [B, N] each."""
+    if not segments:
+        return
+    arr = (Gemv24Segment * len(segments))()
+    for c, (x, meta, signs, scales, y) in enumerate(segments):
+        _dev(x, meta, signs, scales, y)
+        b, n, k = _planes24(x, meta, signs, scales, "tb_ternary24_gemv_multi")
+        if y.numel() < b * n:
+            raise ValueError(f"tb_ternary24_gemv_multi: y holds {y.numel()} floats, needs {b} x {n}")
+        arr[c] = Gemv24Segment(x.data_ptr(), meta.data_ptr(), signs.data_ptr(), scales.data_ptr(), y.data_ptr(),
+                               b, n, k)
+    _check(lib().tb_ternary24_gemv_multi(arr, len(segments), _stream(stream)), "tb_ternary24_gemv_multi")
 
 
 def tb_ternary_gemm(x, codes, scales, y=None, out_dtype=torch.bfloat16, stream=None):

@@ -196,6 +196,30 @@ def test_gemv_validation():
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), None, _v(C), 128, 128, _v(D), s) == 1
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), _v(C), _v(D), 128, 384, _v(MIS), s) == 3
     assert L.tb_ternary24_gemv(_v(A), 20, _v(B), _v(C), _v(D), 128, 384, _v(A), s) == 2
+    # y over the meta plane: 128 x 384 stores whole blocks, 128 x 512 / 8 = 8192 bytes of meta at B
+    assert L.tb_ternary24_gemv(_v(A), 1, _v(B), _v(C), _v(D), 128, 384, _v(B + 8192 - 256), s) == 8
+
+
+def test_grouped_24_validation():
+    L = tb.lib()
+    s = None
+    S = tb.Gemv24Segment
+    # x, meta, signs, scales, y, B, N, K
+    two = (S * 2)(S(A, B, C, D, 0x60000, 1, 128, 128), S(A, B, C, D, 0x61000, 1, 128, 128))
+    assert L.tb_ternary24_gemv_multi(two, 9, s) == 2               # more than TB_MAX_SEGMENTS
+    assert L.tb_ternary24_gemv_multi(two, -1, s) == 2
+    assert L.tb_ternary24_gemv_multi(two, 0, s) == 0
+    assert L.tb_ternary24_gemv_multi(None, 1, s) == 1
+    same_y = (S * 2)(S(A, B, C, D, 0x60000, 1, 128, 128), S(A, B, C, D, 0x60000, 1, 128, 128))
+    assert L.tb_ternary24_gemv_multi(same_y, 2, s) == 8            # two products into one y
+    y_over_in = (S * 2)(S(A, B, C, D, 0x60000, 1, 128, 128), S(0x60000, B, C, D, 0x61000, 1, 128, 128))
+    assert L.tb_ternary24_gemv_multi(y_over_in, 2, s) == 8         # a y is another's x
+    bad = (S * 2)(S(A, B, C, D, 0x60000, 1, 128, 128), S(A, B, C, D, 0x61000, 17, 128, 128))
+    assert L.tb_ternary24_gemv_multi(bad, 2, s) == 2               # one bad batch fails the call
+    mis = (S * 1)(S(A, B, C, D, MIS, 1, 128, 128))
+    assert L.tb_ternary24_gemv_multi(mis, 1, s) == 3
+    empty = (S * 1)(S(None, None, None, None, None, 0, 128, 128))
+    assert L.tb_ternary24_gemv_multi(empty, 1, s) == 0             # B = 0: nothing to do
 
 
 def test_grouped_validation():

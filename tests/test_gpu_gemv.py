@@ -632,3 +632,78 @@ def test_grouped_two_plane_and_mixed_equal_single_calls(b):
             assert torch.equal(y, y1), f"{case} segment {c}: grouped differs from the single call"
             ref = (oracle.matvec.gemv_residual if p == 2 else oracle.matvec.gemv)(x, codes, scales, k)
             assert_close(y.cpu().numpy(), ref, f"{case} segment {c} vs oracle")
+
+
+# ---------------------------------------------------------------- grouped 2:4
+
+@pytest.mark.parametrize("batches", [(1, 1, 1, 1), (2, 1, 4, 3), (1, 6, 2, 1)])
+def test_grouped_24_matches_oracle(batches):
+    # products of different K (G = 40, 5, 17, 3 and 136 groups: ragged blocks
+    # included) and batches in one call; a batch past 4 makes the call launch
+    # each product on its own
+    shapes = [(1920, 5120), (640, 640), (768, 2176), (256, 17408)]
+    if batches == (1, 1, 1, 1):
+        shapes[1] = (512, 384)
+    say(f"grouped gemv24, batches {batches}")
+    segs, refs = [], []
+    for c, ((n, k), b) in enumerate(zip(shapes, batches)):
+        meta, signs = synth.random_24(n, k, seed=300 + c)
+        scales = synth.random_scales24_f16(n, k, seed=310 + c)
+        x = synth.gaussian_bf16((b, k), seed=320 + c)
+        y = torch.full((b, n), float("nan"), dtype=torch.float32, device=DEV)
+        segs.append((bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(scales), y))
+        refs.append(oracle.matvec.gemv24(x, meta, signs, scales, k))
+    tb.tb_ternary24_gemv_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((*_, y), ref) in enumerate(zip(segs, refs)):
+        assert_close(y.cpu().numpy(), ref, f"grouped 2:4 segment {c} vs oracle")
+        assert np.max(np.abs(y.cpu().numpy() - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_grouped_24_exact_equals_single_calls():
+    # integer activations and power-of-two scales make every sum exact, so the
+    # grouped launch (whatever K split it picks) equals the single calls and
+    # the oracle bit for bit
+    shapes = [(896, 5120), (384, 5120), (1152, 5120), (256, 17408)]
+    segs, singles = [], []
+    for c, (n, k) in enumerate(shapes):
+        meta, signs = synth.random_24(n, k, seed=330 + c)
+        rows = (2.0 ** np.random.default_rng(340 + c).integers(-6, 2, size=(n, k // 128))).astype(np.float16)
+        m_r, s_r, _ = oracle.quant.load_24(meta, signs, synth.random_scales24_f16(n, k, seed=1), k)
+        meta, signs, sc = oracle.quant.store_24(m_r, s_r, rows.view(np.uint16))
+        x = synth.small_int_bf16((1, k), seed=350 + c)
+        y = torch.empty((1, n), dtype=torch.float32, device=DEV)
+        segs.append((bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(sc), y))
+        singles.append((x, meta, signs, sc, k))
+    say("grouped gemv24, exact sums")
+    tb.tb_ternary24_gemv_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((xd, md, sd, cd, y), (x, meta, signs, sc, k)) in enumerate(zip(segs, singles)):
+        y1 = tb.tb_ternary24_gemv(xd, md, sd, cd)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y1), f"segment {c}: grouped differs from the single call"
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemv24(x, meta, signs, sc, k))
+
+
+def test_grouped_24_27b_layer_sampled():
+    # a 27B layer's four products (QKV 15360, O 5120, gate/up 34816 rows on
+    # K = 5120; down 5120 rows on K = 17408) in one launch, batch 1, as the
+    # 2:4 decode step runs them; 8 sampled tiles per product against the oracle
+    shapes = [(15360, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]
+    say("grouped gemv24, 27B layer")
+    segs, host = [], []
+    for c, (n, k) in enumerate(shapes):
+        meta, signs = synth.random_24(n, k, seed=360 + c)
+        scales = synth.random_scales24_f16(n, k, seed=370 + c)
+        x = synth.gaussian_bf16((1, k), seed=380 + c)
+        segs.append((bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(scales),
+                     torch.empty((1, n), dtype=torch.float32, device=DEV)))
+        host.append((x, meta, signs, scales, k))
+    tb.tb_ternary24_gemv_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((*_, y), (x, meta, signs, scales, k)) in enumerate(zip(segs, host)):
+        n = meta.shape[0] * 16
+        tiles = np.sort(np.random.default_rng(390 + c).choice(n // 16, 8, replace=False))
+        rows = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+        ref = oracle.matvec.gemv24(x, meta[tiles], signs[tiles], scales[tiles], k)
+        assert_close(y.cpu().numpy()[:, rows], ref, f"27B layer product {c} (8 sampled tiles)")
