@@ -645,7 +645,8 @@ def profile_pass(dev, kind):
       gemv      the decode step's grouped GEMV launches over a 4-layer stack
                 (weights beyond the 256 MB last-level cache), 3 times;
       gemm      the prefill GEMM, M = 2048, both FFN shapes, twice each;
-      gemv24    the 2:4 GEMV, 17408 x 5120, batch 1, over 16 weight copies;
+      gemv24    the 2:4 GEMV, 17408 x 5120, batch 1, over 16 weight copies, then
+                the grouped 2:4 launches of a 4-layer 2:4 stack, 3 times;
       quant     the quantiser on one layer of the stack recipe, twice;
       midbatch  the mid-batch GEMM (M = 16) on the three layer shapes, 4 copies;
       ceiling   the streaming-read probe over 256 MiB, 3 times."""
@@ -681,7 +682,14 @@ def profile_pass(dev, kind):
         y = torch.empty((1, n), dtype=torch.float32, device=dev)
         for meta, signs, sc in planes:
             tb.tb_ternary24_gemv(x, meta, signs, sc, y=y)
-        info["algorithmic_bytes_per_launch"] = n * k // 8 + n * k // 16 + n * k // 64 + 2 * k + 4 * n
+        torch.cuda.synchronize()
+        info["algorithmic_bytes_per_launch"] = gemv24_bytes(n, k, 1)
+        del planes
+        stack24 = Decode24Stack(4, 1, gen, dev)
+        for _ in range(3):
+            stack24.gemv_only()
+        torch.cuda.synchronize()
+        info["grouped_algorithmic_bytes_per_launch"] = sum(gemv24_bytes(n, k, 1) for *_, n, k in stack24.w[0])
     elif kind == "quant":
         g0 = torch.Generator(device=dev)
         g0.manual_seed(5000)
