@@ -451,6 +451,8 @@ G24Geometry grouped_geometry(const tb_gemv24_segment* segs, int count, int bm, i
 }  // namespace
 
 hipError_t launch_gemv24_multi(const tb_gemv24_segment* segs, int count, hipStream_t stream) {
+  // (segments stay in the caller's order: longest K first measured the same
+  // on a 27B layer, 25.4-25.9 against 25.1-25.5 us)
   bool staged = count <= TB_MAX_SEGMENTS;
   int bm = 1;
   for (int c = 0; c < count; ++c) {
