@@ -99,7 +99,9 @@ typedef enum { TB_F32 = 0, TB_BF16 = 1, TB_ACT8 = 2 } tb_dtype;
 typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_DENSE_RESID = 3 } tb_format;
 
 /* Bits OR-ed into the optional device error flag of tb_quantize_pack. */
-#define TB_EFLAG_NONFINITE 1u /* a non-finite weight was seen; its block's codes are unspecified */
+/* TB_EFLAG_NONFINITE: a non-finite weight was seen (or a block's transform
+ * overflowed fp32); that block's codes are unspecified. */
+#define TB_EFLAG_NONFINITE 1u
 #define TB_EFLAG_SCALE_OVF 2u /* a group scale rounded to fp16 infinity (absmean >= 65520)      */
 
 /*

@@ -106,9 +106,6 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
 #pragma unroll
       for (int i = 0; i < 64; ++i) v[i] = __builtin_nontemporal_load(base + (int64_t)i * K + lane_off);
     }
-#pragma unroll
-    for (int i = 0; i < 64; ++i)
-      if (!__builtin_isfinite(v[i])) flags |= TB_EFLAG_NONFINITE;
     fwht64_regs(v);
     fwht_cross_halves(v, sgn);
     {
@@ -135,9 +132,20 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
     }
     fwht64_regs(v);
     fwht_cross_halves(v, sgn);
-    // v[j] = T[row][64*half + j] with T = H B H^T (unnormalised: W' = T / 128)
+    // v[j] = T[row][64*half + j] with T = H B H^T (unnormalised: W' = T / 128).
+    // Every element of T is a +- sum over a whole row and column of the block,
+    // so one non-finite weight makes every element non-finite: one test per
+    // thread on a sum of its values replaces a test per loaded weight (three
+    // instructions per weight, a tenth of the kernel's).  A finite block
+    // whose transform overflows fp32 is flagged the same way.
 
     const int64_t grow = n0 + row;
+    if constexpr (RULE == kMinError || RULE == kTwoFour) {
+      float chk = 0.f;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) chk += __builtin_fabsf(v[j]);
+      if (!__builtin_isfinite(chk)) flags |= TB_EFLAG_NONFINITE;
+    }
     if constexpr (RULE == kMinError) {
       // every magnitude of the group is a candidate threshold; per step each
       // lane of the pair offers one, both lanes count and sum their own
@@ -197,6 +205,7 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(const float* __rest
         float asum = 0.f;
 #pragma unroll
         for (int j = 0; j < 64; ++j) asum += __builtin_fabsf(v[j]);
+        if (p == 0 && !__builtin_isfinite(asum)) flags |= TB_EFLAG_NONFINITE;
         float lo, hi;
         swap_halves(asum, lo, hi);
         const float tsum = lo + hi;               // sum over the 128-group of |T|

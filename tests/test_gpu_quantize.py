@@ -94,6 +94,14 @@ def test_error_flags():
     w[5, 200] = np.nan
     _quant(w, flag=flag)
     assert int(flag.item()) & tb.TB_EFLAG_NONFINITE
+    # every rule, NaN and both infinities, in a block of otherwise ordinary weights
+    for fmt in (tb.TB_FMT_DENSE, tb.TB_FMT_24, tb.TB_FMT_DENSE_MINERR, tb.TB_FMT_DENSE_RESID):
+        for bad in (np.nan, np.inf, -np.inf):
+            w = synth.stack_weights(128, 256, seed=7)
+            w[77, 3] = bad
+            flag.zero_()
+            _quant(w, fmt=fmt, flag=flag)
+            assert int(flag.item()) & tb.TB_EFLAG_NONFINITE, (fmt, bad)
     flag.zero_()
     w = np.full((128, 128), 1.0e5, dtype=np.float32)  # row 0 scale = 1e5 > fp16 max
     _quant(w, flag=flag)
