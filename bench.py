@@ -315,6 +315,26 @@ def time_graph(fn, steps, warmup):
     return t0.elapsed_time(t1), wall, g
 
 
+def gpu_state():
+    """Clocks and power of the GPU from `rocm-smi --json` (a child process,
+    10 s limit): the card's entries whose names mention a clock or power, or
+    the error text when the tool is unavailable."""
+    import json
+    import subprocess
+
+    try:
+        r = subprocess.run(["/opt/rocm/bin/rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=10)
+        data = json.loads(r.stdout)
+    except Exception as e:  # missing tool, timeout, no JSON
+        return {"error": str(e)[:200]}
+    out = {}
+    for card, vals in data.items():
+        if isinstance(vals, dict):
+            out[card] = {k: v for k, v in vals.items() if "clk" in k.lower() or "power" in k.lower()}
+    return out
+
+
 def time_graph_replays(fn, replays, warmup=2):
     """fn() captured in a HIP graph, replayed `warmup` times untimed, then
     `replays` times with HIP events around each replay; returns the ms of
@@ -1122,7 +1142,9 @@ def main():
     log(f"packed weights per step: {step_bytes / 1e9:.3f} GB")
 
     torch.cuda.synchronize()
+    state_before = gpu_state()
     ms_total, wall_ms, graph = time_graph(stack.step, args.steps, args.warmup)
+    state_after = gpu_state()
     ms_step = ms_total / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"decode step: {ms_step:.4f} ms ({value:.1f} GB/s packed); wall {wall_ms / args.steps:.4f} ms/step")
@@ -1135,7 +1157,9 @@ def main():
     log(f"GEMV: {nl} launches per step, avg {gms * 1e3:.2f} us per launch, {achieved:.1f} GB/s algorithmic")
 
     extra = {"step_wall_ms": round(wall_ms / args.steps, 4),
-             "gemv_avg_launch_us": round(gms * 1e3, 3), "gemv_launches_per_step": nl}
+             "gemv_avg_launch_us": round(gms * 1e3, 3), "gemv_launches_per_step": nl,
+             "gpu_state": {"note": "rocm-smi clocks and power just before and after the timed decode steps",
+                           "before": state_before, "after": state_after}}
     # the same step with the input and output rotations as separate launches
     if not args.no_extra:
         ms_apart, _, ga = time_graph(lambda: stack.step(merged=False), max(3, args.steps // 2), 2)
@@ -1166,6 +1190,19 @@ def main():
                                   "gemv_gbs_algorithmic": round(gb8 / (gms8 * 1e-3) / 1e9, 1),
                                   "gemv_frac_of_hbm_peak": round(gb8 / (gms8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"decode batch 8: {ms8:.4f} ms/step, GEMV {extra['decode_batch8']['gemv_gbs_algorithmic']} GB/s")
+        # batch 16: sixteen activation rows (the mid-batch M = 16 case) through the
+        # same layer-grouped decode step
+        stack.make_acts(16, gen, dev)
+        ms16, _, g16 = time_graph(stack.step, max(3, args.steps // 2), 2)
+        del g16
+        ms16 /= max(3, args.steps // 2)
+        gb16, gms16, _ = stack.gemv_times()
+        extra["decode_batch16"] = {"ms_per_step": round(ms16, 4),
+                                   "gbs_packed": round(step_bytes / (ms16 * 1e-3) / 1e9, 1),
+                                   "gemv_gbs_algorithmic": round(gb16 / (gms16 * 1e-3) / 1e9, 1),
+                                   "gemv_frac_of_hbm_peak": round(gb16 / (gms16 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "note": "16 rows per step: the M = 16 products of a layer in one grouped launch"}
+        log(f"decode batch 16: {ms16:.4f} ms/step, GEMV {extra['decode_batch16']['gemv_gbs_algorithmic']} GB/s")
         stack.make_acts(args.batch, gen, dev)
         # the same decode step over two-plane weights (residual second plane)
         two = DecodeStack(args.layers, args.batch, gen, dev, args.grouping, planes=2)
