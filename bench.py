@@ -225,6 +225,51 @@ class DecodeStack:
         return per_launch_bytes, ms / (replays * nl), nl
 
 
+class DecodeMidBatch:
+    """The decode step of a DecodeStack's weights for a small batch (M <= 16)
+    on the mid-batch GEMM: per layer one rotation launch (the previous
+    outputs back, fp32; this layer's inputs in, bf16) and one grouped launch
+    of the layer's four products (tb_ternary_gemm_multi, fp32 out)."""
+
+    def __init__(self, stack, batch, gen, dev):
+        import torch
+
+        from ternary_weights_hadamard_amd import synth
+
+        self.stack, self.batch = stack, batch
+        self.x = [synth.torch_gaussian_bf16((batch, k), gen, dev) for _, n, k in FUSED]
+        self.xr = [torch.empty((batch, k), dtype=torch.bfloat16, device=dev) for _, n, k in FUSED]
+        self.y = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+        self.yo = [torch.empty((batch, n), dtype=torch.float32, device=dev) for _, n, k in FUSED]
+
+    def gemm_call(self, layer):
+        from ternary_weights_hadamard_amd import tb
+
+        tb.tb_ternary_gemm_multi([(self.xr[j], codes, scales, self.y[j])
+                                  for j, (codes, scales, n, k) in enumerate(layer)])
+
+    def step(self):
+        from ternary_weights_hadamard_amd import tb
+
+        rot_in = list(zip(self.x, self.xr))
+        rot_out = list(zip(self.y, self.yo))
+        for li, layer in enumerate(self.stack.w):
+            tb.tb_fwht128_multi((rot_out if li > 0 else []) + rot_in)
+            self.gemm_call(layer)
+        tb.tb_fwht128_multi(rot_out)
+
+    def gemm_only(self):
+        for layer in self.stack.w:
+            self.gemm_call(layer)
+
+    def gemm_times(self, replays=5):
+        """(algorithmic bytes per launch, ms per launch) of the grouped launches."""
+        ms, _, g = time_graph(self.gemm_only, replays, 1)
+        del g
+        per_launch = sum(packed_bytes(n, k) + 2 * self.batch * k + 4 * self.batch * n for *_, n, k in self.stack.w[0])
+        return per_launch, ms / (replays * len(self.stack.w))
+
+
 def gemv24_bytes(n, k, b=1):
     """Algorithmic bytes of one 2:4 GEMV: meta N K/8, signs N K/16, scales N K/64,
     bf16 x and fp32 y."""
@@ -1204,6 +1249,21 @@ def main():
                                    "note": "16 rows per step: the M = 16 products of a layer in one grouped launch"}
         log(f"decode batch 16: {ms16:.4f} ms/step, GEMV {extra['decode_batch16']['gemv_gbs_algorithmic']} GB/s")
         stack.make_acts(args.batch, gen, dev)
+        # the same batch-16 step on the mid-batch GEMM, one grouped launch per layer
+        mid = DecodeMidBatch(stack, 16, gen, dev)
+        msm, _, gm = time_graph(mid.step, max(3, args.steps // 2), 2)
+        del gm
+        msm /= max(3, args.steps // 2)
+        gbm, gmsm = mid.gemm_times()
+        extra["decode_batch16_midbatch_gemm"] = {
+            "ms_per_step": round(msm, 4), "gbs_packed": round(step_bytes / (msm * 1e-3) / 1e9, 1),
+            "gemm_us_per_layer_launch": round(gmsm * 1e3, 2),
+            "gemm_gbs_algorithmic": round(gbm / (gmsm * 1e-3) / 1e9, 1),
+            "gemm_frac_of_hbm_peak": round(gbm / (gmsm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": "16 rows per step on the mid-batch kernel (tb_ternary_gemm_multi), bf16 activations"}
+        log(f"decode batch 16, mid-batch GEMM: {msm:.4f} ms/step, {gmsm * 1e3:.2f} us per layer launch, "
+            f"{extra['decode_batch16_midbatch_gemm']['gemm_gbs_algorithmic']} GB/s")
+        del mid
         # the same decode step over two-plane weights (residual second plane)
         two = DecodeStack(args.layers, args.batch, gen, dev, args.grouping, planes=2)
         ms2, _, g2 = time_graph(two.step, max(3, args.steps // 2), 2)

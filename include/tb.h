@@ -190,6 +190,20 @@ typedef struct {
   int64_t K;
 } tb_gemv24_segment;
 
+/* One product of a grouped tb_ternary_gemm_multi call: arguments as in
+ * tb_ternary_gemm. */
+typedef struct {
+  const uint16_t* x;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  void* y;
+  int64_t M;
+  int64_t N;
+  int64_t K;
+  int y_dtype;
+  int reserved; /* must be 0 */
+} tb_gemm_segment;
+
 /* Human-readable name of a status code (static storage, never NULL). */
 TB_API const char* tb_status_string(int status);
 
@@ -425,6 +439,20 @@ TB_API tb_status tb_ternary24_gemv_multi(const tb_gemv24_segment* segs, int coun
  */
 TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, void* y, int y_dtype, void* stream);
+
+/*
+ * tb_ternary_gemm over up to TB_MAX_SEGMENTS independent products.  When
+ * every segment has M <= 16 they run as one launch of the mid-batch kernel
+ * (a decoder layer's products at a small batch: the launch is long enough to
+ * keep HBM streaming); otherwise each product is launched on its own.  Same
+ * contraction and accuracy per segment; in the one launch a product's K
+ * slices (and so its fp32 summation order) follow from the whole group's
+ * size.  `segs` is a host array read during the call; no segment's y may
+ * overlap any segment's inputs or another y; `reserved` must be 0 (else
+ * TB_ERR_SHAPE).  count == 0 is a no-op; count outside [0, TB_MAX_SEGMENTS]
+ * returns TB_ERR_SHAPE.
+ */
+TB_API tb_status tb_ternary_gemm_multi(const tb_gemm_segment* segs, int count, void* stream);
 
 /*
  * Bytes of workspace tb_ternary_gemm_splitk and tb_ternary_gemm_rotated use

@@ -32,6 +32,7 @@
 // or on timing.  Waves of different workgroups start their slices at
 // different groups, which spreads the activation reads over the L2 channels.
 #include <algorithm>
+#include <cstdint>
 
 #include "tb_common.h"
 #include "tb_launch.h"
@@ -40,7 +41,12 @@ namespace tb {
 
 namespace {
 
-constexpr int kTiles = 2;   // code tiles (16 weight rows each) per workgroup
+constexpr int kTiles = 2;   // code tiles (16 weight rows each) per workgroup, one product per launch
+// ... and in a grouped launch, where there are workgroups enough: each
+// activation load then serves four tiles (a 27B layer's four products at
+// M = 16: 55-57 us with two tiles, 43.5-45 us with four, 50-52 us with eight;
+// a single 17408 x 5120 product: 13.3 us with two, 19.7 with four)
+constexpr int kGroupedTiles = 4;
 constexpr int kAhead = 2;   // steps (scale groups) in flight ahead of the one in use
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -63,18 +69,28 @@ __device__ __forceinline__ bf16x8 pack4(uint32_t a, uint32_t b, uint32_t c, uint
   return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
-// M <= 16; K / 128 >= W; N a multiple of 32 (two tiles per workgroup).
-template <int W, bool OUT_BF16>
-__global__ void __launch_bounds__(64 * W) gemm_skinny_kernel(const uint16_t* __restrict__ x, int M,
-                                                            const uint32_t* __restrict__ codes,
-                                                            const uint16_t* __restrict__ scales, int64_t N,
-                                                            int64_t K, void* __restrict__ y) {
-  __shared__ f32x4 red[W][kTiles][64];                               // each wave's partial result
-  __shared__ __attribute__((aligned(16))) uint32_t xlds[W][16 * 64];  // per wave: [row][chunk ^ row][4]
+// LDS of one workgroup of W waves over TL tiles
+template <int W, int TL>
+struct SkinnyLds {
+  f32x4 red[W][TL][64];                                    // each wave's partial result
+  __attribute__((aligned(16))) uint32_t xlds[W][16 * 64];  // per wave: [row][chunk ^ row][4]
+};
+
+// Workgroup `wg` of one product: code tiles TL wg .. TL wg + TL - 1.
+// M <= 16; K / 128 >= W; N a multiple of 16 TL.
+template <int W, int TL>
+__device__ __forceinline__ void skinny_product(const uint16_t* __restrict__ x, int M,
+                                               const uint32_t* __restrict__ codes,
+                                               const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                               void* __restrict__ y, bool out_bf16, int64_t wg,
+                                               SkinnyLds<W, TL>& sm) {
+  constexpr int kTiles = TL;
+  auto& red = sm.red;
+  auto& xlds = sm.xlds;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane & 15, q = lane >> 4;
   const int64_t G = K / kBlock;
-  const int64_t t0 = (int64_t)blockIdx.x * kTiles;
+  const int64_t t0 = wg * kTiles;
   // this wave's scale groups [gb, gb + ng)
   const int64_t gb = G * w / W;
   const int ng = (int)(G * (w + 1) / W - gb);
@@ -99,7 +115,7 @@ __global__ void __launch_bounds__(64 * W) gemm_skinny_kernel(const uint16_t* __r
   u32x2 cw[kAhead][kTiles];
   uint16_t sw[kAhead][kTiles];
   u32x4 xv[kAhead][4];
-  const int rot = (int)(blockIdx.x % (unsigned)ng);
+  const int rot = (int)(wg % ng);
   auto load = [&](int s, int set) {
     int g = std::min(s, ng - 1) + rot;
     g = g >= ng ? g - ng : g;
@@ -176,11 +192,49 @@ __global__ void __launch_bounds__(64 * W) gemm_skinny_kernel(const uint16_t* __r
     for (int ww = 1; ww < W; ++ww) v += rf[ww * kTiles * 256 + off];
     v *= 0.5f;
     const int64_t o = (int64_t)m * N + (t0 + t) * 16 + n;
-    if constexpr (OUT_BF16)
+    if (out_bf16)
       static_cast<uint16_t*>(y)[o] = (uint16_t)f32_to_bf16_rne(v);
     else
       static_cast<float*>(y)[o] = v;
   }
+}
+
+template <int W, bool OUT_BF16>
+__global__ void __launch_bounds__(64 * W) gemm_skinny_kernel(const uint16_t* __restrict__ x, int M,
+                                                            const uint32_t* __restrict__ codes,
+                                                            const uint16_t* __restrict__ scales, int64_t N,
+                                                            int64_t K, void* __restrict__ y) {
+  __shared__ SkinnyLds<W, kTiles> sm;
+  skinny_product<W, kTiles>(x, M, codes, scales, N, K, y, OUT_BF16, blockIdx.x, sm);
+}
+
+// Several products in one launch: segment c owns workgroups [wg_begin,
+// next segment's wg_begin).  The segment is found per workgroup from the
+// kernel arguments (scalar compares).
+struct SkinnySeg {
+  const uint16_t* x;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  void* y;
+  int64_t N, K;
+  int M, out_bf16, wg_begin, reserved;
+};
+
+struct SkinnySegs {
+  SkinnySeg s[TB_MAX_SEGMENTS];
+  int count;
+};
+
+template <int W>
+__global__ void __launch_bounds__(64 * W) gemm_skinny_multi_kernel(SkinnySegs segs) {
+  __shared__ SkinnyLds<W, kGroupedTiles> sm;
+  int seg = 0;
+#pragma unroll
+  for (int t = 1; t < TB_MAX_SEGMENTS; ++t)
+    seg += (t < segs.count && (int)blockIdx.x >= segs.s[t].wg_begin) ? 1 : 0;
+  const SkinnySeg& sg = segs.s[seg];
+  skinny_product<W, kGroupedTiles>(sg.x, sg.M, sg.codes, sg.scales, sg.N, sg.K, sg.y, sg.out_bf16 != 0,
+                                   (int)blockIdx.x - sg.wg_begin, sm);
 }
 
 template <int W>
@@ -195,6 +249,12 @@ hipError_t launch_w(const uint16_t* x, int M, const uint32_t* codes, const uint1
 }
 
 }  // namespace
+
+template <int W>
+hipError_t launch_multi_w(const SkinnySegs& segs, unsigned wgs, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_skinny_multi_kernel<W>), dim3(wgs), dim3(64 * W), 0, stream, segs);
+  return hipGetLastError();
+}
 
 int gemm_skinny_waves(int64_t N, int64_t K) {
   // Eight waves per workgroup while the workgroups fit on the compute units
@@ -215,6 +275,41 @@ hipError_t launch_gemm_skinny(const uint16_t* x, int64_t M, const uint32_t* code
     case 4: return launch_w<4>(x, (int)M, codes, scales, N, K, y, bf16, stream);
     case 2: return launch_w<2>(x, (int)M, codes, scales, N, K, y, bf16, stream);
     default: return launch_w<1>(x, (int)M, codes, scales, N, K, y, bf16, stream);
+  }
+}
+
+int gemm_skinny_multi_waves(const tb_gemm_segment* segs, int count) {
+  // the single-product rule over the launch's workgroups; never more waves
+  // than the shortest product's scale groups
+  int64_t wgs = 0, gmin = INT64_MAX;
+  for (int c = 0; c < count; ++c) {
+    wgs += segs[c].N / 16 / kGroupedTiles;
+    gmin = std::min<int64_t>(gmin, segs[c].K / kBlock);
+  }
+  int w = wgs <= 256 ? 8 : 4;
+  while (w > gmin) w /= 2;
+  return w;
+}
+
+hipError_t launch_gemm_skinny_multi(const tb_gemm_segment* segs, int count, hipStream_t stream) {
+  if (count < 1 || count > TB_MAX_SEGMENTS) return hipErrorInvalidValue;
+  SkinnySegs ss{};
+  int64_t wgs = 0;
+  for (int c = 0; c < count; ++c) {
+    const tb_gemm_segment& a = segs[c];
+    if (a.M < 1 || a.M > kSkinnyMaxRows || a.N % (16 * kGroupedTiles) != 0 || a.K % kBlock != 0)
+      return hipErrorInvalidValue;
+    ss.s[c] = SkinnySeg{static_cast<const uint16_t*>(a.x), a.codes, a.scales, a.y, a.N, a.K, (int)a.M,
+                        a.y_dtype == TB_BF16 ? 1 : 0, (int)wgs, 0};
+    wgs += a.N / 16 / kGroupedTiles;
+  }
+  ss.count = count;
+  if (wgs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  switch (gemm_skinny_multi_waves(segs, count)) {
+    case 8: return launch_multi_w<8>(ss, (unsigned)wgs, stream);
+    case 4: return launch_multi_w<4>(ss, (unsigned)wgs, stream);
+    case 2: return launch_multi_w<2>(ss, (unsigned)wgs, stream);
+    default: return launch_multi_w<1>(ss, (unsigned)wgs, stream);
   }
 }
 

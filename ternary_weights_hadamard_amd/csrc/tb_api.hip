@@ -379,17 +379,59 @@ tb_status tb_ternary24_gemv_multi(const tb_gemv24_segment* segs, int count, void
   return launched(tb::launch_gemv24_multi(live, n, as_stream(stream)));
 }
 
+// the arguments of one GEMM product, without the launch
+static tb_status check_gemm(const tb_gemm_segment& a) {
+  if (!dtype_ok(a.y_dtype)) return TB_ERR_DTYPE;
+  if (!dims_ok(a.N, a.K) || a.M < 0 || a.M > (int64_t)65535 * 128 || a.reserved != 0) return TB_ERR_SHAPE;
+  if (a.M == 0) return TB_OK;
+  if (!a.x || !a.codes || !a.scales || !a.y) return TB_ERR_NULL;
+  if (!aligned16(a.x) || !aligned16(a.codes) || !aligned16(a.scales) || !aligned16(a.y)) return TB_ERR_ALIGN;
+  return TB_OK;
+}
+
+// does y of product a overlap any input (or, with with_y, the output) of b
+static bool gemm_y_overlaps(const tb_gemm_segment& a, const tb_gemm_segment& b, bool with_y) {
+  const size_t yb = (size_t)a.M * (size_t)a.N * dtype_bytes(a.y_dtype), nk = (size_t)b.N * (size_t)b.K;
+  return overlap(a.y, yb, b.x, (size_t)b.M * b.K * 2) || overlap(a.y, yb, b.codes, nk / 4) ||
+         overlap(a.y, yb, b.scales, nk / 64) ||
+         (with_y && overlap(a.y, yb, b.y, (size_t)b.M * (size_t)b.N * dtype_bytes(b.y_dtype)));
+}
+
 tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
                           int64_t K, void* y, int y_dtype, void* stream) {
-  if (!dtype_ok(y_dtype)) return TB_ERR_DTYPE;
-  if (!dims_ok(N, K) || M < 0 || M > (int64_t)65535 * 128) return TB_ERR_SHAPE;
-  if (M == 0) return TB_OK;
-  if (!x || !codes || !scales || !y) return TB_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return TB_ERR_ALIGN;
-  const size_t nk = (size_t)N * (size_t)K, yb = (size_t)M * (size_t)N * dtype_bytes(y_dtype);
-  if (overlap(y, yb, x, (size_t)M * K * 2) || overlap(y, yb, codes, nk / 4) || overlap(y, yb, scales, nk / 64))
-    return TB_ERR_ALIAS;
+  const tb_gemm_segment a{x, codes, scales, y, M, N, K, y_dtype, 0};
+  const tb_status st = check_gemm(a);
+  if (st != TB_OK || M == 0) return st;
+  if (gemm_y_overlaps(a, a, false)) return TB_ERR_ALIAS;
   return launched(tb::launch_gemm_ternary(x, M, codes, scales, N, K, y, y_dtype, as_stream(stream)));
+}
+
+tb_status tb_ternary_gemm_multi(const tb_gemm_segment* segs, int count, void* stream) {
+  if (count < 0 || count > TB_MAX_SEGMENTS) return TB_ERR_SHAPE;
+  if (count == 0) return TB_OK;
+  if (!segs) return TB_ERR_NULL;
+  tb_gemm_segment live[TB_MAX_SEGMENTS];
+  int n = 0;
+  bool skinny = true;
+  for (int c = 0; c < count; ++c) {
+    const tb_status st = check_gemm(segs[c]);
+    if (st != TB_OK) return st;
+    if (segs[c].M == 0) continue;
+    for (int d = 0; d < count; ++d)
+      if (segs[d].M != 0 && gemm_y_overlaps(segs[c], segs[d], d != c)) return TB_ERR_ALIAS;
+    skinny = skinny && segs[c].M <= tb::kSkinnyMaxRows;
+    live[n++] = segs[c];
+  }
+  if (n == 0) return TB_OK;
+  const hipStream_t st = as_stream(stream);
+  if (skinny) return launched(tb::launch_gemm_skinny_multi(live, n, st));
+  for (int c = 0; c < n; ++c) {
+    const tb_gemm_segment& a = live[c];
+    const tb_status r = launched(tb::launch_gemm_ternary(static_cast<const uint16_t*>(a.x), a.M, a.codes, a.scales,
+                                                         a.N, a.K, a.y, a.y_dtype, st));
+    if (r != TB_OK) return r;
+  }
+  return TB_OK;
 }
 
 size_t tb_ternary_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {

@@ -32,6 +32,8 @@ int gemm_skinny_waves(int64_t N, int64_t K);
 // 1 <= M <= kSkinnyMaxRows; one pass, no workspace
 hipError_t launch_gemm_skinny(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                               int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream);
+// one launch of the mid-batch kernel over several products, every M <= kSkinnyMaxRows
+hipError_t launch_gemm_skinny_multi(const tb_gemm_segment* segs, int count, hipStream_t stream);
 // K splits the split-K GEMM uses for this shape (1: none)
 int gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
 // split K when the workspace allows (else one pass); `rotate` rotates the

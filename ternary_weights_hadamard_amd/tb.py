@@ -48,6 +48,12 @@ class Gemv24Segment(ctypes.Structure):
                 ("K", ctypes.c_int64)]
 
 
+class GemmSegment(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("y_dtype", ctypes.c_int), ("reserved", ctypes.c_int)]
+
+
 class GemvSegment(ctypes.Structure):
     _fields_ = [("act", ctypes.c_void_p), ("B", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("y", ctypes.c_void_p),
@@ -71,6 +77,7 @@ SIGNATURES = {
     "tb_ternary24_gemv": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "tb_ternary24_gemv_multi": (_int, [ctypes.POINTER(Gemv24Segment), _int, _vp]),
     "tb_ternary_gemm": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp]),
+    "tb_ternary_gemm_multi": (_int, [ctypes.POINTER(GemmSegment), _int, _vp]),
     "tb_ternary_gemm_splitk_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "tb_ternary_gemm_splitk": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp, ctypes.c_size_t, _vp]),
     "tb_ternary_gemm_rotated": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _vp, ctypes.c_size_t, _vp]),
@@ -364,6 +371,22 @@ def tb_ternary_gemm(x, codes, scales, y=None, out_dtype=torch.bfloat16, stream=N
     _check(lib().tb_ternary_gemm(_p(x), m, _p(codes), _p(scales), n, k, _p(y), _dt(y), _stream(stream)),
            "tb_ternary_gemm")
     return y
+
+
+def tb_ternary_gemm_multi(segments, stream=None):
+    """Several GEMMs: segments = [(x, codes, scales, y), ...], x bf16 [M, K], y bf16 or fp32 [M, N];
+    one launch when every M <= 16, else one launch per product."""
+    if not segments:
+        return
+    arr = (GemmSegment * len(segments))()
+    for c, (x, codes, scales, y) in enumerate(segments):
+        _dev(x, codes, scales, y)
+        m, k = x.shape
+        n = _dense_n(scales)
+        if y.numel() < m * n:
+            raise ValueError(f"tb_ternary_gemm_multi: y holds {y.numel()} elements, needs {m} x {n}")
+        arr[c] = GemmSegment(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), y.data_ptr(), m, n, k, _dt(y), 0)
+    _check(lib().tb_ternary_gemm_multi(arr, len(segments), _stream(stream)), "tb_ternary_gemm_multi")
 
 
 def tb_ternary_gemm_splitk_workspace(m, n, k):

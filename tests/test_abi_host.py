@@ -200,6 +200,31 @@ def test_gemv_validation():
     assert L.tb_ternary24_gemv(_v(A), 1, _v(B), _v(C), _v(D), 128, 384, _v(B + 8192 - 256), s) == 8
 
 
+def test_grouped_gemm_validation():
+    L = tb.lib()
+    s = None
+    S = tb.GemmSegment
+    # x, codes, scales, y, M, N, K, y_dtype, reserved
+    two = (S * 2)(S(A, B, C, 0x60000, 16, 128, 128, tb.TB_F32, 0), S(A, B, C, 0x70000, 16, 128, 128, tb.TB_F32, 0))
+    assert L.tb_ternary_gemm_multi(two, 9, s) == 2                 # more than TB_MAX_SEGMENTS
+    assert L.tb_ternary_gemm_multi(two, -1, s) == 2
+    assert L.tb_ternary_gemm_multi(two, 0, s) == 0
+    assert L.tb_ternary_gemm_multi(None, 1, s) == 1
+    same_y = (S * 2)(S(A, B, C, 0x60000, 16, 128, 128, tb.TB_F32, 0), S(A, B, C, 0x60000, 16, 128, 128, tb.TB_F32, 0))
+    assert L.tb_ternary_gemm_multi(same_y, 2, s) == 8              # two products into one y
+    y_over_in = (S * 2)(S(A, B, C, 0x60000, 16, 128, 128, tb.TB_F32, 0),
+                        S(0x60000, B, C, 0x70000, 16, 128, 128, tb.TB_F32, 0))
+    assert L.tb_ternary_gemm_multi(y_over_in, 2, s) == 8           # a y is another's x
+    dt = (S * 1)(S(A, B, C, 0x60000, 16, 128, 128, 7, 0))
+    assert L.tb_ternary_gemm_multi(dt, 1, s) == 4
+    res = (S * 1)(S(A, B, C, 0x60000, 16, 128, 128, tb.TB_F32, 1))
+    assert L.tb_ternary_gemm_multi(res, 1, s) == 2                 # reserved must be 0
+    mis = (S * 1)(S(A, B, C, MIS, 16, 128, 128, tb.TB_F32, 0))
+    assert L.tb_ternary_gemm_multi(mis, 1, s) == 3
+    empty = (S * 1)(S(None, None, None, None, 0, 128, 128, tb.TB_F32, 0))
+    assert L.tb_ternary_gemm_multi(empty, 1, s) == 0               # M = 0: nothing to do
+
+
 def test_grouped_24_validation():
     L = tb.lib()
     s = None

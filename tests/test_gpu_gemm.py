@@ -310,3 +310,80 @@ def test_gemm_rotated_full_size_sampled():
     cs = (128 * blocks[:, None] + np.arange(128)[None, :]).ravel()
     ref = _rotate_rows(oracle.matvec.gemm(x[rs], codes[tiles], scales[tiles], k))
     assert_close(y[np.ix_(rs, cs)], ref, "rotated gemm (48 rows x 2 column blocks sampled)", out_bf16=True)
+
+
+# ---------------------------------------------------------------- grouped products (tb_ternary_gemm_multi)
+
+@pytest.mark.parametrize("ms", [(16, 16, 16, 16), (1, 7, 16, 3), (16, 40, 2, 5)])
+def test_gemm_multi_matches_oracle(ms):
+    # products of different K (G = 40, 5, 17, 136 groups) and row counts in one
+    # call, bf16 and fp32 outputs; an M past 16 makes the call launch each
+    # product on its own
+    shapes = [(1920, 5120), (640, 640), (768, 2176), (256, 17408)]
+    say(f"gemm multi, M = {ms}")
+    segs, refs = [], []
+    for c, ((n, k), m) in enumerate(zip(shapes, ms)):
+        codes = synth.random_code_words(n, k, seed=500 + c)
+        scales = synth.random_scales_f16(n, k, seed=510 + c)
+        x = synth.gaussian_bf16((m, k), seed=520 + c)
+        out = torch.bfloat16 if c % 2 else torch.float32
+        y = torch.full((m, n), float("nan"), dtype=out, device=DEV)
+        segs.append((bf16_dev(x), u32_dev(codes), f16_dev(scales), y))
+        refs.append(oracle.matvec.gemm(x, codes, scales, k))
+    tb.tb_ternary_gemm_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((*_, y), ref) in enumerate(zip(segs, refs)):
+        assert_close(host_f64(y), ref, f"gemm multi segment {c}", out_bf16=y.dtype == torch.bfloat16)
+
+
+def test_gemm_multi_single_segment_and_exact_sums():
+    # integer activations and power-of-two scales make every sum exact, so a
+    # grouped launch (four tiles per workgroup, its own K slices and starting
+    # groups) equals the single calls and the oracle bit for bit, alone or
+    # with other products
+    shapes = [(1536, 5120), (512, 5120), (3456, 5120), (512, 17408)]
+    segs, host = [], []
+    for c, (n, k) in enumerate(shapes):
+        codes = synth.random_code_words(n, k, seed=530 + c)
+        sc = (2.0 ** np.random.default_rng(540 + c).integers(-6, 2, size=(n // 16, k // 128, 16))).astype(np.float16)
+        sc = sc.view(np.uint16)
+        x = synth.small_int_bf16((16, k), seed=550 + c)
+        segs.append((bf16_dev(x), u32_dev(codes), f16_dev(sc), torch.empty((16, n), dtype=torch.float32, device=DEV)))
+        host.append((x, codes, sc, k))
+    say("gemm multi, single segment and exact sums")
+    xd, cd, sd, y = segs[0]
+    tb.tb_ternary_gemm_multi([segs[0]])
+    y1 = tb.tb_ternary_gemm(xd, cd, sd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1)
+    tb.tb_ternary_gemm_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((xd, cd, sd, y), (x, codes, sc, k)) in enumerate(zip(segs, host)):
+        y1 = tb.tb_ternary_gemm(xd, cd, sd, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y1), f"segment {c}: grouped differs from the single call"
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.matvec.gemm(x, codes, sc, k))
+
+
+def test_gemm_multi_27b_layer_m16_sampled():
+    # a 27B layer's four products at M = 16 in one launch (QKV 15360, O 5120,
+    # gate/up 34816 rows on K = 5120; down 5120 rows on K = 17408), as the
+    # batch-16 decode step runs them; 6 sampled tiles per product
+    shapes = [(15360, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]
+    say("gemm multi, 27B layer at M = 16")
+    segs, host = [], []
+    for c, (n, k) in enumerate(shapes):
+        codes = synth.random_code_words(n, k, seed=560 + c)
+        scales = synth.random_scales_f16(n, k, seed=570 + c)
+        x = synth.gaussian_bf16((16, k), seed=580 + c)
+        segs.append((bf16_dev(x), u32_dev(codes), f16_dev(scales),
+                     torch.empty((16, n), dtype=torch.float32, device=DEV)))
+        host.append((x, codes, scales, k))
+    tb.tb_ternary_gemm_multi(segs)
+    torch.cuda.synchronize()
+    for c, ((*_, y), (x, codes, scales, k)) in enumerate(zip(segs, host)):
+        n = codes.shape[0] * 16
+        tiles = np.sort(np.random.default_rng(590 + c).choice(n // 16, 6, replace=False))
+        cols = (16 * tiles[:, None] + np.arange(16)[None, :]).ravel()
+        ref = oracle.matvec.gemm(x, codes[tiles], scales[tiles], k)
+        assert_close(host_f64(y)[:, cols], ref, f"27B layer product {c} at M = 16 (6 sampled tiles)")
