@@ -75,11 +75,17 @@ __device__ __forceinline__ uint32_t sign_word(const u32x2& sw, int j) {
 // bf16 +1 in both halves, in a VGPR: the kept-value build is then one
 // shift and one and-or per dword (with the constant as an immediate the
 // compiler split the and-or in two, as a VOP3 instruction here takes no
-// literal and reads at most one SGPR)
+// literal and reads at most one SGPR).  The asm exists only in the device
+// pass, like keep_sources_past: the host pass cannot parse the "v"
+// constraint.
 __device__ __forceinline__ uint32_t bf16_one_pair() {
+#if defined(__HIP_DEVICE_COMPILE__)
   uint32_t v;
   asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(v));
   return v;
+#else
+  return 0x3F803F80u;
+#endif
 }
 
 // SMFMAC h (0, 1) of a group for a lane: kept values of its quads 4h ..
