@@ -410,8 +410,9 @@ TB_API tb_status tb_ternary24_gemv(const uint16_t* x, int64_t B, const uint32_t*
  * HBM streaming, where a single product leaves it idle while the launch
  * fills and drains).  Same contraction, rules and accuracy per segment; how
  * a product's K is split over waves (and so the fp32 summation order)
- * depends on the segments it is grouped with.  Segments with B > 4 make the
- * call launch each product on its own.  `segs` is a host array read during
+ * depends on the segments it is grouped with; a single segment is the
+ * single call.  Segments with B > 4 make the call launch each product on its
+ * own.  `segs` is a host array read during
  * the call; no segment's y may overlap any segment's inputs or another y.
  * count == 0 is a no-op; count outside [0, TB_MAX_SEGMENTS] returns
  * TB_ERR_SHAPE.

@@ -459,6 +459,12 @@ G24Geometry grouped_geometry(const tb_gemv24_segment* segs, int count, int bm, i
 hipError_t launch_gemv24_multi(const tb_gemv24_segment* segs, int count, hipStream_t stream) {
   // (segments stay in the caller's order: longest K first measured the same
   // on a 27B layer, 25.4-25.9 against 25.1-25.5 us)
+  // one product: its own launch geometry (many small workgroups; the grouped
+  // geometry's large ones measured 5120 x 5120 8.0 against 4.4 us, 17408 x
+  // 5120 11.7 against 7.9 us), and the single call's result bit for bit
+  if (count == 1)
+    return launch_gemv_ternary24(segs[0].x, segs[0].B, segs[0].meta, segs[0].signs, segs[0].scales, segs[0].N,
+                                 segs[0].K, segs[0].y, stream);
   bool staged = count <= TB_MAX_SEGMENTS;
   int bm = 1;
   for (int c = 0; c < count; ++c) {

@@ -676,6 +676,13 @@ def test_grouped_24_exact_equals_single_calls():
         segs.append((bf16_dev(x), u32_dev(meta), u32_dev(signs), f16_dev(sc), y))
         singles.append((x, meta, signs, sc, k))
     say("grouped gemv24, exact sums")
+    # a single segment is the single call bit for bit, whatever the sums
+    xg = bf16_dev(synth.gaussian_bf16((1, 5120), seed=333))
+    mg, sg_ = (u32_dev(a) for a in synth.random_24(896, 5120, seed=334))
+    cg = f16_dev(synth.random_scales24_f16(896, 5120, seed=335))
+    ya = torch.empty((1, 896), dtype=torch.float32, device=DEV)
+    tb.tb_ternary24_gemv_multi([(xg, mg, sg_, cg, ya)])
+    assert torch.equal(ya, tb.tb_ternary24_gemv(xg, mg, sg_, cg))
     tb.tb_ternary24_gemv_multi(segs)
     torch.cuda.synchronize()
     for c, ((xd, md, sd, cd, y), (x, meta, signs, sc, k)) in enumerate(zip(segs, singles)):
