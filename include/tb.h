@@ -448,7 +448,7 @@ TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* c
  * keep HBM streaming); otherwise each product is launched on its own.  Same
  * contraction and accuracy per segment; in the one launch a product's K
  * slices (and so its fp32 summation order) follow from the whole group's
- * size.  `segs` is a host array read during the call; no segment's y may
+ * size, and a single segment is the single call.  `segs` is a host array read during the call; no segment's y may
  * overlap any segment's inputs or another y; `reserved` must be 0 (else
  * TB_ERR_SHAPE).  count == 0 is a no-op; count outside [0, TB_MAX_SEGMENTS]
  * returns TB_ERR_SHAPE.

@@ -293,6 +293,11 @@ int gemm_skinny_multi_waves(const tb_gemm_segment* segs, int count) {
 
 hipError_t launch_gemm_skinny_multi(const tb_gemm_segment* segs, int count, hipStream_t stream) {
   if (count < 1 || count > TB_MAX_SEGMENTS) return hipErrorInvalidValue;
+  // one product: the single launch (two tiles per workgroup is faster there)
+  // and its result bit for bit
+  if (count == 1)
+    return launch_gemm_skinny(static_cast<const uint16_t*>(segs[0].x), segs[0].M, segs[0].codes, segs[0].scales,
+                              segs[0].N, segs[0].K, segs[0].y, segs[0].y_dtype, stream);
   SkinnySegs ss{};
   int64_t wgs = 0;
   for (int c = 0; c < count; ++c) {

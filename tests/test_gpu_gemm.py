@@ -339,8 +339,7 @@ def test_gemm_multi_matches_oracle(ms):
 def test_gemm_multi_single_segment_and_exact_sums():
     # integer activations and power-of-two scales make every sum exact, so a
     # grouped launch (four tiles per workgroup, its own K slices and starting
-    # groups) equals the single calls and the oracle bit for bit, alone or
-    # with other products
+    # groups) equals the single calls and the oracle bit for bit
     shapes = [(1536, 5120), (512, 5120), (3456, 5120), (512, 17408)]
     segs, host = [], []
     for c, (n, k) in enumerate(shapes):
@@ -351,11 +350,13 @@ def test_gemm_multi_single_segment_and_exact_sums():
         segs.append((bf16_dev(x), u32_dev(codes), f16_dev(sc), torch.empty((16, n), dtype=torch.float32, device=DEV)))
         host.append((x, codes, sc, k))
     say("gemm multi, single segment and exact sums")
-    xd, cd, sd, y = segs[0]
-    tb.tb_ternary_gemm_multi([segs[0]])
-    y1 = tb.tb_ternary_gemm(xd, cd, sd, out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y1)
+    # a single segment is the single call bit for bit, whatever the sums
+    xg = bf16_dev(synth.gaussian_bf16((16, 5120), seed=536))
+    cg = u32_dev(synth.random_code_words(1024, 5120, seed=537))
+    sg_ = f16_dev(synth.random_scales_f16(1024, 5120, seed=538))
+    ya = torch.empty((16, 1024), dtype=torch.float32, device=DEV)
+    tb.tb_ternary_gemm_multi([(xg, cg, sg_, ya)])
+    assert torch.equal(ya, tb.tb_ternary_gemm(xg, cg, sg_, out_dtype=torch.float32))
     tb.tb_ternary_gemm_multi(segs)
     torch.cuda.synchronize()
     for c, ((xd, cd, sd, y), (x, codes, sc, k)) in enumerate(zip(segs, host)):
