@@ -399,6 +399,14 @@ def time_graph_replays(fn, replays, warmup=2):
     return out
 
 
+def replay_stats(fn, replays, calls=1):
+    """fn() in a HIP graph replayed `replays` times (time_graph_replays):
+    (median, p10, p90) ms per call when fn makes `calls` calls."""
+    reps = sorted(time_graph_replays(fn, replays))
+    pick = lambda f: reps[min(len(reps) - 1, int(f * len(reps)))] / calls
+    return pick(0.5), pick(0.1), pick(0.9)
+
+
 def time_eager(fn, iters, warm_s=0.1):
     """ms per call of fn over `iters` back-to-back calls, after calling it for at
     least warm_s seconds (the first calls of a process run at lower clocks)."""
@@ -437,22 +445,27 @@ def extra_phases(gen, dev, quick):
         scales = synth.torch_scales_f16(n, k, gen, dev)
         x = synth.torch_gaussian_bf16((m, k), gen, dev)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ms = time_eager(lambda: tb.tb_ternary_gemm(x, codes, scales, y=y), 3 if quick else 10)
+        reps = 3 if quick else 12
+        ms, ms10, ms90 = replay_stats(lambda: [tb.tb_ternary_gemm(x, codes, scales, y=y) for _ in range(8)], reps, 8)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         # the same product through the split-K entry point (the library picks
         # the split count; one pass when splitting does not pay)
         wsb = tb.tb_ternary_gemm_splitk_workspace(m, n, k)
         work = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev)
-        ms_k = time_eager(lambda: tb.tb_ternary_gemm_splitk(x, codes, scales, y=y, workspace=work), 3 if quick else 10)
+        ms_k, mk10, mk90 = replay_stats(
+            lambda: [tb.tb_ternary_gemm_splitk(x, codes, scales, y=y, workspace=work) for _ in range(8)], reps, 8)
         tf_k = 2.0 * m * n * k / (ms_k * 1e-3) / 1e12
-        gemm[f"{k}x{n}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS, 4),
-                            "splitk_ms": round(ms_k, 4), "splitk_splits": wsb // (m * n * 4) if wsb else 1,
+        gemm[f"{k}x{n}"] = {"ms": round(ms, 4), "ms_p10_p90": [round(ms10, 4), round(ms90, 4)],
+                            "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_MFMA_TFLOPS, 4),
+                            "splitk_ms": round(ms_k, 4), "splitk_ms_p10_p90": [round(mk10, 4), round(mk90, 4)],
+                            "splitk_splits": wsb // (m * n * 4) if wsb else 1,
                             "splitk_tflops": round(tf_k, 1), "splitk_frac_of_peak": round(tf_k / PEAK_MFMA_TFLOPS, 4)}
         log(f"  prefill GEMM M={m} K={k} N={n}: {ms:.3f} ms, {tf:.1f} TFLOP/s; split-K entry "
             f"({gemm[f'{k}x{n}']['splitk_splits']} splits) {ms_k:.3f} ms, {tf_k:.1f} TFLOP/s")
         del codes, scales, x, y, work
     out["prefill_gemm"] = {"workload": "M=2048, (K,N) = (5120,17408) and (17408,5120), bf16 out; tb_ternary_gemm "
-                                       "(one pass) and tb_ternary_gemm_splitk (caller workspace)",
+                                       "(one pass) and tb_ternary_gemm_splitk (caller workspace); median (p10, p90) "
+                                       "over graph replays of 8 calls back to back",
                            "peak_tflops": PEAK_MFMA_TFLOPS, **gemm}
 
     # the same GEMMs with the output rotated back in the epilogue, against the
@@ -464,9 +477,10 @@ def extra_phases(gen, dev, quick):
         x = synth.torch_gaussian_bf16((m, k), gen, dev)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         yf = torch.empty((m, n), dtype=torch.float32, device=dev)
-        ms_f = time_eager(lambda: tb.tb_ternary_gemm_rotated(x, codes, scales, y=y), 3 if quick else 10)
-        ms_s = time_eager(lambda: (tb.tb_ternary_gemm(x, codes, scales, y=yf), tb.tb_fwht128(yf, y=y)),
-                          3 if quick else 10)
+        reps = 3 if quick else 10
+        ms_f = replay_stats(lambda: [tb.tb_ternary_gemm_rotated(x, codes, scales, y=y) for _ in range(8)], reps, 8)[0]
+        ms_s = replay_stats(lambda: [(tb.tb_ternary_gemm(x, codes, scales, y=yf), tb.tb_fwht128(yf, y=y))
+                                     for _ in range(8)], reps, 8)[0]
         rot[f"{k}x{n}"] = {"fused_ms": round(ms_f, 4), "separate_ms": round(ms_s, 4),
                            "fused_tflops": round(2.0 * m * n * k / (ms_f * 1e-3) / 1e12, 1)}
         log(f"  rotated GEMM M={m} K={k} N={n}: fused {ms_f:.3f} ms, product + rotation {ms_s:.3f} ms")
@@ -490,9 +504,9 @@ def extra_phases(gen, dev, quick):
                 for c, sc in ws:
                     tb.tb_ternary_gemm_splitk(x, c, sc, y=y, workspace=work)
 
-            us = time_eager(runm, 2 if quick else 5) * 1e3 / copies
+            us, us10, us90 = (v * 1e3 for v in replay_stats(runm, 8 if quick else 40, copies))
             wbytes = n * k // 4 + n * k // 64
-            mid[f"M{m}_{k}x{n}"] = {"us": round(us, 2),
+            mid[f"M{m}_{k}x{n}"] = {"us": round(us, 2), "us_p10_p90": [round(us10, 2), round(us90, 2)],
                                     "kernel": "gemm_skinny_kernel" if m <= 16 else "gemm_rw_kernel + splitk_reduce_kernel",
                                     "splits": 1 if m <= 16 else (wsb // (m * n * 4) if wsb else 1),
                                     "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1),
@@ -503,7 +517,7 @@ def extra_phases(gen, dev, quick):
         del ws
     out["midbatch_gemm"] = {"workload": "tb_ternary_gemm_splitk (M <= 16 runs the one-pass mid-batch kernel), M = 16 "
                                         "and 256, (K, N) = (5120, 5120), (5120, 17408), (17408, 5120), bf16 out, 8 weight "
-                                        "copies rotated, eager launches",
+                                        "copies rotated; median (p10, p90) over graph replays of the 8 launches",
                             **mid}
 
     # 2:4 GEMV, 17408 x 5120, batch 1, rotated over >= 1 GB of weight copies
@@ -519,22 +533,22 @@ def extra_phases(gen, dev, quick):
 
     # one replay = the 64 launches back to back in a HIP graph; per-launch
     # figures from the median (and p10 / p90) over the replays
-    reps = sorted(time_graph_replays(run24, 10 if quick else 60))
-    pick = lambda f: reps[min(len(reps) - 1, int(f * len(reps)))] / copies
-    ms = pick(0.5)
+    ms, ms10, ms90 = replay_stats(run24, 10 if quick else 60, copies)
     b24 = gemv24_bytes(n, k, 1)
     out["gemv24"] = {"workload": "17408x5120 2:4, batch 1, 64 weight copies (1.16 GB) rotated",
                      "us_per_launch": round(ms * 1e3, 2), "gbs": round(b24 / (ms * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(b24 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "us_per_launch_p10_p90": [round(pick(0.1) * 1e3, 2), round(pick(0.9) * 1e3, 2)],
-                     "note": f"median over {len(reps)} graph replays of the 64 launches"}
-    log(f"  2:4 GEMV: {ms * 1e3:.2f} us/launch (p10 {pick(0.1) * 1e3:.2f}, p90 {pick(0.9) * 1e3:.2f}), "
+                     "us_per_launch_p10_p90": [round(ms10 * 1e3, 2), round(ms90 * 1e3, 2)],
+                     "note": "median over graph replays of the 64 launches"}
+    log(f"  2:4 GEMV: {ms * 1e3:.2f} us/launch (p10 {ms10 * 1e3:.2f}, p90 {ms90 * 1e3:.2f}), "
         f"{out['gemv24']['gbs']} GB/s")
     del planes
 
     # activation FWHT at prefill size: 2048 x 17408 bf16 -> bf16
     xa = synth.torch_gaussian_bf16((2048, F), gen, dev)
     ya = torch.empty_like(xa)
+    # eager back-to-back calls: graph replays of this one-kernel call read 8 %
+    # slower (25.3-26.2 against 23.6 us), the GEMM's agree with eager within 2 %
     ms = time_eager(lambda: tb.tb_fwht128(xa, y=ya), 5 if quick else 20)
     fb = 2 * 2 * 2048 * F
     out["fwht128"] = {"workload": "2048x17408 bf16 -> bf16", "us": round(ms * 1e3, 2),
@@ -738,7 +752,8 @@ def profile_pass(dev, kind):
       gemv24    the 2:4 GEMV, 17408 x 5120, batch 1, over 16 weight copies, then
                 the grouped 2:4 launches of a 4-layer 2:4 stack, 3 times;
       quant     the quantiser on one layer of the stack recipe, twice;
-      midbatch  the mid-batch GEMM (M = 16) on the three layer shapes, 4 copies;
+      midbatch  the mid-batch GEMM (M = 16) on the three layer shapes, 4 copies,
+                then the grouped M = 16 launches of a 4-layer stack, 3 times;
       ceiling   the streaming-read probe over 256 MiB, 3 times."""
     import torch
 
@@ -799,6 +814,14 @@ def profile_pass(dev, kind):
                 tb.tb_ternary_gemm(x, c, sc, y=y)
             torch.cuda.synchronize()
             del ws
+        # then a 4-layer stack's grouped M = 16 launches (one per layer), 3 times
+        stack = DecodeStack(4, 1, gen, dev)
+        mid = DecodeMidBatch(stack, 16, gen, dev)
+        for _ in range(3):
+            mid.gemm_only()
+        torch.cuda.synchronize()
+        info["grouped_algorithmic_bytes_per_launch"] = sum(packed_bytes(n, k) + 2 * 16 * k + 4 * 16 * n
+                                                           for *_, n, k in stack.w[0])
     elif kind == "ceiling":
         lib = probe_lib()
         buf = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device=dev).fill_(7)
