@@ -740,7 +740,7 @@ def _calibration_copy(dev):
     torch.cuda.synchronize()
 
 
-PROFILE_KINDS = ("gemv", "gemm", "gemv24", "quant", "midbatch", "ceiling")
+PROFILE_KINDS = ("gemv", "gemv8", "gemm", "gemv24", "quant", "midbatch", "ceiling")
 
 
 def profile_pass(dev, kind):
@@ -748,6 +748,7 @@ def profile_pass(dev, kind):
     calibration copy:
       gemv      the decode step's grouped GEMV launches over a 4-layer stack
                 (weights beyond the 256 MB last-level cache), 3 times;
+      gemv8     the same at batch 8;
       gemm      the prefill GEMM, M = 2048, both FFN shapes, twice each;
       gemv24    the 2:4 GEMV, 17408 x 5120, batch 1, over 16 weight copies, then
                 the grouped 2:4 launches of a 4-layer 2:4 stack, 3 times;
@@ -762,15 +763,15 @@ def profile_pass(dev, kind):
     gen = torch.Generator(device=dev)
     gen.manual_seed(31)
     info = {"profile_pass": kind}
-    if kind == "gemv":
-        stack = DecodeStack(4, 1, gen, dev)
+    if kind in ("gemv", "gemv8"):
+        stack = DecodeStack(4, 8 if kind == "gemv8" else 1, gen, dev)
         stack.step()
         torch.cuda.synchronize()
         for _ in range(3):
             stack.gemv_only()
         per_layer = {"layer": 1, "split": 2, "none": 4}[stack.grouping]
         info["grouping"] = stack.grouping
-        info["algorithmic_bytes_per_launch"] = sum(gemv_bytes(n, k, 1) for _, _, n, k in stack.w[0]) / per_layer
+        info["algorithmic_bytes_per_launch"] = sum(gemv_bytes(n, k, stack.batch) for _, _, n, k in stack.w[0]) / per_layer
     elif kind == "gemm":
         for k, n in ((D, F), (F, D)):
             codes = synth.torch_code_words(n, k, gen, dev)
