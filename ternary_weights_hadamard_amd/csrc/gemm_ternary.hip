@@ -148,6 +148,7 @@ __global__ void __launch_bounds__(256, 3) gemm_rw_kernel(const uint16_t* __restr
 
   // the products of one step (c: its place in the trip) from activation stage
   // c & 1 and the code words of ring slot c
+  float rs[4];  // per tile: the rescale factor of the group that starts at this step
   auto mfma_step = [&](int c) {
     const uint16_t* xa = lds_mem + (c & 1) * kXStage;
 #pragma unroll
@@ -166,15 +167,25 @@ __global__ void __launch_bounds__(256, 3) gemm_rw_kernel(const uint16_t* __restr
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 1.0f, 2)),
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 1.0f, 3))});
       }
+      // at a group's first step each accumulator is rescaled just before its
+      // first product, so the multiplies interleave with the products of the
+      // others instead of holding the matrix cores (27B FFN shapes at M =
+      // 2048: about 1 % faster than rescaling all sixteen first)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if ((c & 1) == 0 && kk == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] *= rs[j];
+          }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
     }
   };
 
-  // one K step (step = 4 trip + c): at the start of a group the rescale; its
-  // products; the code words of step + kRCodeRing into the freed ring slot;
+  // one K step (step = 4 trip + c): at the start of a group the rescale
+  // factors; its products; the code words of step + kRCodeRing into the freed ring slot;
   // at the end of a group the scales two groups on; the next step's
   // activations into the other stage and the step after that into the freed
   // registers; one barrier.  Steps past the range (an odd last trip) load
@@ -187,13 +198,9 @@ __global__ void __launch_bounds__(256, 3) gemm_rw_kernel(const uint16_t* __restr
         for (int j = 0; j < 4; ++j) {
           const float sg = (float)sw[par][j];
           const bool nz = sg != 0.f;
-          const float r = nz ? unit[j] * __builtin_amdgcn_rcpf(sg) : 1.f;
+          rs[j] = nz ? unit[j] * __builtin_amdgcn_rcpf(sg) : 1.f;
           unit[j] = nz ? sg : unit[j];
           fmask[j] = nz ? 0xCCCCCCCCu : 0u;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] *= r;
         }
       }
       mfma_step(c);
