@@ -130,6 +130,11 @@ typedef enum { TB_FMT_DENSE = 0, TB_FMT_24 = 1, TB_FMT_DENSE_MINERR = 2, TB_FMT_
 /* Most segments one grouped call (tb_fwht128_multi, tb_ternary_gemv_multi) takes. */
 #define TB_MAX_SEGMENTS 8
 
+/* Longest K the GEMM entry points take (tb_ternary_gemm and its variants;
+ * longer K returns TB_ERR_SHAPE): their kernels address a workgroup's
+ * activation rows with 32-bit offsets. */
+#define TB_GEMM_MAX_K ((int64_t)1 << 24)
+
 /* Most K parts of one GEMV segment (tb_gemv_segment.parts) and most partial
  * inputs of one rotation segment (tb_fwht_segment.x_parts). */
 #define TB_MAX_PARTS 8
@@ -436,7 +441,7 @@ TB_API tb_status tb_ternary24_gemv_multi(const tb_gemv24_segment* segs, int coun
  * multiplied by the last unit and halved on the way out.
  * M <= 16 runs a kernel of its own (one pass over K for at most 16 rows,
  * weights decoded in registers); a row's result depends on its activations,
- * N and K only, not on M.
+ * N and K only, not on M.  K at most TB_GEMM_MAX_K (else TB_ERR_SHAPE).
  */
 TB_API tb_status tb_ternary_gemm(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                           int64_t N, int64_t K, void* y, int y_dtype, void* stream);

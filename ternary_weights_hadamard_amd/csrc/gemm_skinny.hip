@@ -48,6 +48,9 @@ constexpr int kTiles = 2;   // code tiles (16 weight rows each) per workgroup, o
 // a single 17408 x 5120 product: 13.3 us with two, 19.7 with four)
 constexpr int kGroupedTiles = 4;
 constexpr int kAhead = 2;   // steps (scale groups) in flight ahead of the one in use
+// longest K: every buffer offset (at most 32 K bytes of activations, 16 K of
+// code words) stays below 2^31
+constexpr int64_t kSkinnyMaxK = (int64_t)1 << 26;
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
@@ -63,6 +66,18 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t (&out)[8]) {
   out[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 1));
   out[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 2));
   out[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, 3));
+}
+
+// Word 3 of a buffer resource: the 32-bit data format raw loads need (with
+// the format left invalid every load returns zero).  A buffer load takes a
+// wave-uniform resource and step offset in scalar registers and a 32-bit lane
+// offset, so a step's addresses cost no vector arithmetic; an offset past the
+// resource's size reads zero instead of memory.
+constexpr int kBufferWord3 = 0x00020000;
+
+// a resource over [base, base + bytes); base wave-uniform
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, kBufferWord3);
 }
 
 __device__ __forceinline__ bf16x8 pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -87,31 +102,31 @@ __device__ __forceinline__ void skinny_product(const uint16_t* __restrict__ x, i
   constexpr int kTiles = TL;
   auto& red = sm.red;
   auto& xlds = sm.xlds;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: slice bounds and bases in scalars
   const int li = lane & 15, q = lane >> 4;
   const int64_t G = K / kBlock;
   const int64_t t0 = wg * kTiles;
   // this wave's scale groups [gb, gb + ng)
   const int64_t gb = G * w / W;
   const int ng = (int)(G * (w + 1) / W - gb);
-  // activation staging: load m brings rows 4m + q (clamped to M - 1), 16-byte chunk li
-  const uint16_t* xsrc[4];
+  // Loads through buffer resources based at group gb (the launchers keep
+  // every offset below 2^31 bytes).  Activations: load m brings rows 4m + q
+  // (clamped to M - 1), 16-byte chunk li of group gb + g, at byte
+  // x_lane[m] + 256 g.  Code words of tile t0 + t, group gb + g: byte
+  // 512 (t G + g) + 8 lane; scales [N/16][G][16], the lane's weight row li:
+  // byte 32 (t G + g) + 2 li.
+  const __amdgpu_buffer_rsrc_t xrs = buffer_over(x + gb * kBlock, ((int64_t)M * K - gb * kBlock) * 2);
+  const __amdgpu_buffer_rsrc_t crs = buffer_over(codes + (t0 * G + gb) * 128, (kTiles * G - gb) * 512);
+  const __amdgpu_buffer_rsrc_t srs = buffer_over(scales + (t0 * G + gb) * 16, (kTiles * G - gb) * 32);
+  int x_lane[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) xsrc[m] = x + (int64_t)std::min(4 * m + q, M - 1) * K + gb * kBlock + 8 * li;
-  const uint32_t* csrc[kTiles];
-  const uint16_t* ssrc[kTiles];
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    csrc[t] = codes + ((t0 + t) * G + gb) * 128 + 2 * lane;
-    // scales [N/16][G][16]: the lane's weight row li of tile t0 + t
-    ssrc[t] = scales + ((t0 + t) * G + gb) * 16 + li;
-  }
+  for (int m = 0; m < 4; ++m) x_lane[m] = (int)((std::min(4 * m + q, M - 1) * K + 8 * li) * 2);
   uint32_t* xl = xlds[w];
 
   // a ring of kAhead register sets; step s (group (s + rot) % ng of the
-  // slice) lives in set s % kAhead.  Steps past the slice reload its last
-  // group and are not accumulated, so every set is loaded and waited for the
-  // same way on every path.
+  // slice) lives in set s % kAhead.  Loads for steps past the slice reload
+  // its last group and are never used.
   u32x2 cw[kAhead][kTiles];
   uint16_t sw[kAhead][kTiles];
   u32x4 xv[kAhead][4];
@@ -120,11 +135,13 @@ __device__ __forceinline__ void skinny_product(const uint16_t* __restrict__ x, i
     int g = std::min(s, ng - 1) + rot;
     g = g >= ng ? g - ng : g;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) xv[set][m] = *reinterpret_cast<const u32x4*>(xsrc[m] + (int64_t)g * kBlock);
+    for (int m = 0; m < 4; ++m)
+      xv[set][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_lane[m], 256 * g, 0));
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      cw[set][t] = *reinterpret_cast<const u32x2*>(csrc[t] + (int64_t)g * 128);
-      sw[set][t] = ssrc[t][(int64_t)g * 16];
+      const int tg = t * (int)G + g;
+      cw[set][t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(crs, 8 * lane, 512 * tg, 0));
+      sw[set][t] = __builtin_amdgcn_raw_buffer_load_b16(srs, 2 * li, 32 * tg, 0);
     }
   };
 
@@ -132,8 +149,7 @@ __device__ __forceinline__ void skinny_product(const uint16_t* __restrict__ x, i
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  auto step = [&](int s, int set) {
-    const bool live = s < ng;
+  auto step = [&](int set) {
     // the activations of the group through LDS: written as loaded, read as operands
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -155,28 +171,31 @@ __device__ __forceinline__ void skinny_product(const uint16_t* __restrict__ x, i
       p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], pack4(b1[4], b1[5], b1[6], b1[7]), p, 0, 0, 0);
       const float sc = (float)__builtin_bit_cast(_Float16, sw[set][t]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] = live ? __builtin_fmaf(p[r], sc, acc[t][r]) : acc[t][r];
+      for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(p[r], sc, acc[t][r]);
     }
   };
 
   // The scheduling barriers keep each set's loads in issue order between the
-  // steps, so the wait before a step covers that set alone.
+  // steps, so the wait before a step covers that set alone.  Whole trips of
+  // kAhead steps, then the one step an odd slice has left (set 0), so that
+  // every step taken is accumulated.
+  static_assert(kAhead == 2, "the loop below leaves at most one step after its trips");
 #pragma unroll
   for (int r = 0; r < kAhead; ++r) {
     load(r, r);
     __builtin_amdgcn_sched_barrier(0);
   }
   int s = 0;
-  do {  // ng >= 1
+  for (; s + kAhead <= ng; s += kAhead) {
 #pragma unroll
     for (int r = 0; r < kAhead; ++r) {
-      step(s + r, r);
+      step(r);
       __builtin_amdgcn_sched_barrier(0);
       load(s + r + kAhead, r);
       __builtin_amdgcn_sched_barrier(0);
     }
-    s += kAhead;
-  } while (s < ng);
+  }
+  if (s < ng) step(0);
 
   // lane holds acc[t][r] = 2 y[4q + r][16 (t0 + t) + li]
 #pragma unroll
@@ -268,7 +287,8 @@ int gemm_skinny_waves(int64_t N, int64_t K) {
 
 hipError_t launch_gemm_skinny(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                               int64_t N, int64_t K, void* y, int y_dtype, hipStream_t stream) {
-  if (M < 1 || M > kSkinnyMaxRows || N % (16 * kTiles) != 0 || K % kBlock != 0) return hipErrorInvalidValue;
+  if (M < 1 || M > kSkinnyMaxRows || N % (16 * kTiles) != 0 || K % kBlock != 0 || K > kSkinnyMaxK)
+    return hipErrorInvalidValue;
   const bool bf16 = y_dtype == TB_BF16;
   switch (gemm_skinny_waves(N, K)) {
     case 8: return launch_w<8>(x, (int)M, codes, scales, N, K, y, bf16, stream);
@@ -312,7 +332,8 @@ hipError_t launch_gemm_skinny_multi(const tb_gemm_segment* segs, int count, hipS
   int64_t wgs = 0;
   for (int c = 0; c < count; ++c) {
     const tb_gemm_segment& a = segs[ord[c]];
-    if (a.M < 1 || a.M > kSkinnyMaxRows || a.N % (16 * kGroupedTiles) != 0 || a.K % kBlock != 0)
+    if (a.M < 1 || a.M > kSkinnyMaxRows || a.N % (16 * kGroupedTiles) != 0 || a.K % kBlock != 0 ||
+        a.K > kSkinnyMaxK)
       return hipErrorInvalidValue;
     ss.s[c] = SkinnySeg{static_cast<const uint16_t*>(a.x), a.codes, a.scales, a.y, a.N, a.K, (int)a.M,
                         a.y_dtype == TB_BF16 ? 1 : 0, (int)wgs, 0};

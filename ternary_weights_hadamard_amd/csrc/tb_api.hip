@@ -157,7 +157,7 @@ tb_status scratch_address(void** out) {
 tb_status check_gemm_ws(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, int64_t N,
                         int64_t K, const void* y, int y_dtype, const float* workspace, size_t workspace_bytes) {
   if (!dtype_ok(y_dtype)) return TB_ERR_DTYPE;
-  if (!dims_ok(N, K) || M < 0 || M > (int64_t)65535 * 128) return TB_ERR_SHAPE;
+  if (!dims_ok(N, K) || K > TB_GEMM_MAX_K || M < 0 || M > (int64_t)65535 * 128) return TB_ERR_SHAPE;
   if (M == 0) return TB_OK;
   if (!x || !codes || !scales || !y) return TB_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || (workspace && !aligned16(workspace)))
@@ -382,7 +382,8 @@ tb_status tb_ternary24_gemv_multi(const tb_gemv24_segment* segs, int count, void
 // the arguments of one GEMM product, without the launch
 static tb_status check_gemm(const tb_gemm_segment& a) {
   if (!dtype_ok(a.y_dtype)) return TB_ERR_DTYPE;
-  if (!dims_ok(a.N, a.K) || a.M < 0 || a.M > (int64_t)65535 * 128 || a.reserved != 0) return TB_ERR_SHAPE;
+  if (!dims_ok(a.N, a.K) || a.K > TB_GEMM_MAX_K || a.M < 0 || a.M > (int64_t)65535 * 128 || a.reserved != 0)
+    return TB_ERR_SHAPE;
   if (a.M == 0) return TB_OK;
   if (!a.x || !a.codes || !a.scales || !a.y) return TB_ERR_NULL;
   if (!aligned16(a.x) || !aligned16(a.codes) || !aligned16(a.scales) || !aligned16(a.y)) return TB_ERR_ALIGN;
@@ -435,7 +436,7 @@ tb_status tb_ternary_gemm_multi(const tb_gemm_segment* segs, int count, void* st
 }
 
 size_t tb_ternary_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {
-  if (!dims_ok(N, K) || M <= 0 || M > (int64_t)65535 * 128) return 0;
+  if (!dims_ok(N, K) || K > TB_GEMM_MAX_K || M <= 0 || M > (int64_t)65535 * 128) return 0;
   const int S = tb::gemm_splitk_parts(M, N, K);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }

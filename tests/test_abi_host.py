@@ -323,6 +323,15 @@ def test_gemm_validation():
     assert L.tb_ternary_gemm(_v(MIS), 4, _v(B), _v(C), 128, 128, _v(D), 1, s) == 3
     assert L.tb_ternary_gemm(_v(A), 4, _v(B), _v(C), 128, 128, _v(A), 0, s) == 8
     assert L.tb_ternary_gemm(None, 0, None, None, 128, 128, None, 1, s) == 0
+    kmax = 1 << 24                                                                  # TB_GEMM_MAX_K
+    assert L.tb_ternary_gemm(_v(A), 4, _v(B), _v(C), 128, kmax + 128, _v(D), 1, s) == 2
+    assert L.tb_ternary_gemm_splitk(_v(A), 4, _v(B), _v(C), 128, kmax + 128, _v(D), 1, None, 0, s) == 2
+    assert L.tb_ternary_gemm_rotated(_v(A), 4, _v(B), _v(C), 128, kmax + 128, _v(D), 1, None, 0, s) == 2
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 5120, kmax + 128) == 0
+    assert tb.tb_ternary_gemm_splitk_workspace(16, 5120, kmax) > 0                  # the limit itself is taken
+    S = tb.GemmSegment
+    long_k = (S * 1)(S(A, B, C, 0x60000, 16, 128, kmax + 128, tb.TB_F32, 0))
+    assert L.tb_ternary_gemm_multi(long_k, 1, s) == 2
 
 
 def test_gemm_splitk_validation_and_workspace_size():
